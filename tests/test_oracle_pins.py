@@ -1,0 +1,429 @@
+"""Pins of the fp64 CPU oracle against facts fixed outside the oracle itself.
+
+Every check here is a closed form, an invariant of the mathematics, a special
+case that reduces to a library routine (numpy/scipy/torch), a finite-difference
+or autograd check of a hand-written backward, or a brute-force evaluation.  The
+pages give no worked numeric examples for this path, so no printed values exist
+to compare against; the pins are chosen so that a dropped term, a sign error, a
+transposed operand, a wrong segment layout or a swapped row/column order in
+the oracle fails at least one of them.
+"""
+import numpy as np
+import pytest
+import scipy.optimize
+import scipy.special
+import torch
+
+import oracle as O
+
+RNG = np.random.default_rng(12345)
+
+
+def rnd(*shape, std=1.0):
+    return RNG.standard_normal(shape) * std
+
+
+# ---------------------------------------------------------------- conversions
+def test_bf16_rounding_matches_torch_rne():
+    # values exactly representable in fp32: torch's fp32 -> bf16 cast is RNE
+    v = (RNG.standard_normal(200000) * np.exp(RNG.uniform(-30, 30, 200000))).astype(np.float32)
+    # explicit ties: low 16 bits exactly 0x8000, with even and odd kept lsb
+    u = RNG.integers(0, 2**31, 2000, dtype=np.uint64).astype(np.uint32) & np.uint32(0x7F7F0000)
+    ties = (u | np.uint32(0x8000)).view(np.float32)
+    v = np.concatenate([v, ties, -ties, np.float32([0.0, -0.0, 1.0, 3.0e38, 1e-40])])
+    want = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = O.round_f64_to_bf16_bits(v.astype(np.float64))
+    np.testing.assert_array_equal(got, want)
+
+
+def test_bf16_rounding_direct_from_f64_no_double_rounding():
+    # 1 + 2^-8 + 2^-30: RNE to 8 bits must round up (above the tie); rounding to
+    # fp32 first would land exactly on the tie 1 + 2^-8 and round to even (down).
+    v = np.float64(1.0 + 2.0**-8 + 2.0**-30)
+    assert O.round_f64_to_bf16(np.array([v]))[0] == 1.0 + 2.0**-7
+
+
+def test_bf16_roundtrip_exact():
+    bits = RNG.integers(0, 2**16, 100000).astype(np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]  # drop Inf/NaN patterns
+    f = O.bf16_bits_to_f64(bits)
+    np.testing.assert_array_equal(O.round_f64_to_bf16_bits(f), bits)
+
+
+# ---------------------------------------------------------------- F1 projection
+def test_proj_matches_library_matmul_and_norm():
+    N, n, C = 5, 4, 24
+    X = rnd(N, n, C); W = rnd(n * C, 24, std=0.02)
+    p = O.proj_rms_h(X, W, eps_rms=1e-6)
+    Xf = X.reshape(N, -1)
+    q = np.linalg.norm(Xf, axis=1) / np.sqrt(n * C)
+    np.testing.assert_allclose(p.q, q, rtol=1e-14)
+    np.testing.assert_allclose(p.r, 1.0 / (q + 1e-6), rtol=1e-14)
+    np.testing.assert_allclose(p.z, (Xf @ W) * p.r[:, None], rtol=1e-12, atol=1e-15)
+    zh = p.z
+    np.testing.assert_allclose(p.H_pre, scipy.special.expit(zh[:, :4]), rtol=1e-14)
+    np.testing.assert_allclose(p.H_post, 2 * scipy.special.expit(zh[:, 4:8]), rtol=1e-14)
+    np.testing.assert_allclose(p.L.reshape(N, 16), zh[:, 8:], rtol=1e-14)
+
+
+def test_proj_segment_layout_one_hot_columns():
+    # W[k, j] = [k == perm[j]]: output j reads exactly x[perm[j]] * r, which
+    # pins PRE | POST | RES order and the row-major layout of the RES block.
+    N, n, C = 3, 4, 8
+    X = rnd(N, n, C)
+    perm = RNG.permutation(n * C)[:24]
+    W = np.zeros((n * C, 24)); W[perm, np.arange(24)] = 1.0
+    p = O.proj_rms_h(X, W, eps_rms=0.0)
+    xs = X.reshape(N, -1)[:, perm] * p.r[:, None]
+    np.testing.assert_allclose(p.H_pre, 1 / (1 + np.exp(-xs[:, 0:4])), rtol=1e-14)
+    np.testing.assert_allclose(p.H_post, 2 / (1 + np.exp(-xs[:, 4:8])), rtol=1e-14)
+    for a in range(4):
+        for b in range(4):
+            np.testing.assert_allclose(p.L[:, a, b], xs[:, 8 + 4 * a + b], rtol=1e-14)
+
+
+@pytest.mark.parametrize("c", [0.37, -2.5, 11.0])
+def test_rmsnorm_constant_row_is_pm_one(c):
+    # a constant row normalises to +-1 per element (up to eps): z = x_k * r
+    N, n, C = 2, 4, 16
+    X = np.full((N, n, C), c); X[1] *= -1
+    W = np.zeros((n * C, 24)); W[np.arange(24) * 2, np.arange(24)] = 1.0
+    eps = 1e-6
+    p = O.proj_rms_h(X, W, eps_rms=eps)
+    np.testing.assert_allclose(p.z[0], np.sign(c) * abs(c) / (abs(c) + eps), rtol=1e-15)
+    np.testing.assert_allclose(p.z[1], -np.sign(c) * abs(c) / (abs(c) + eps), rtol=1e-15)
+    assert np.all(np.abs(np.abs(p.z) - 1) <= eps / abs(c) * 1.0000001)
+
+
+def test_zero_row_forward_is_finite():
+    N, n, C = 2, 4, 8
+    X = rnd(N, n, C); X[0] = 0.0
+    hb = rnd(24)
+    p = O.proj_rms_h(X, rnd(n * C, 24), hbias=hb, eps_rms=1e-6)
+    assert p.q[0] == 0.0 and p.r[0] == 1e6
+    np.testing.assert_array_equal(p.z[0], 0.0)
+    np.testing.assert_allclose(p.H_pre[0], scipy.special.expit(hb[:4]), rtol=1e-15)
+    np.testing.assert_allclose(p.L[0].ravel(), hb[8:], rtol=0)
+    assert all(np.isfinite(a).all() for a in (p.H_pre, p.H_post, p.L, p.z))
+
+
+def test_proj_scale_invariance_and_ranges():
+    N, n, C = 6, 4, 32
+    X = rnd(N, n, C); W = rnd(n * C, 24, std=0.05)
+    base = O.proj_rms_h(X, W, eps_rms=1e-6)
+    for lam in (1e-3, 7.0, 1e4):
+        s = O.proj_rms_h(lam * X, W, eps_rms=1e-6)
+        # z(lam X) = p / (q + eps/lam) against p / (q + eps): the relative
+        # change is eps |1 - 1/lam| / (q + eps/lam) <= eps |1 - 1/lam| / q
+        bound = 1e-6 * abs(1 - 1 / lam) / base.q * 1.0001 + 1e-13
+        rel = np.abs(s.z - base.z) / np.abs(base.z)
+        assert np.all(rel <= bound[:, None])
+    assert np.all((base.H_pre > 0) & (base.H_pre < 1))
+    assert np.all((base.H_post > 0) & (base.H_post < 2))
+
+
+def test_proj_gains_and_bias_are_affine_per_segment():
+    N, n, C = 4, 4, 16
+    X = rnd(N, n, C); W = rnd(n * C, 24, std=0.05)
+    alpha = np.array([1.7, -0.4, 2.3]); hb = rnd(24)
+    a = O.proj_rms_h(X, W, alpha=alpha, hbias=hb)
+    b = O.proj_rms_h(X, W)
+    np.testing.assert_allclose(a.z, b.z, rtol=1e-15)
+    np.testing.assert_allclose(a.L.reshape(N, 16), alpha[2] * b.L.reshape(N, 16) + hb[8:], rtol=1e-13)
+    logit = lambda h: np.log(h / (1 - h))
+    np.testing.assert_allclose(logit(a.H_pre), alpha[0] * b.z[:, :4] + hb[:4], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(logit(a.H_post / 2), alpha[1] * b.z[:, 4:8] + hb[4:8], rtol=1e-9, atol=1e-12)
+
+
+# ---------------------------------------------------------------- F2 Sinkhorn
+@pytest.mark.parametrize("iters,eps", [(1, 1e-6), (20, 1e-6), (3, 0.3), (20, 0.0)])
+def test_sinkhorn_cross_ratio_invariant(iters, eps):
+    # every half-step rescales rows or columns, so H = D1 exp(L) D2 and all
+    # cross ratios keep their value, whatever the iteration count and eps.
+    L = rnd(50, 4, 4, std=2.0)
+    H = O.sinkhorn_fwd(L, iters, eps)
+    for (a, c) in [(0, 1), (1, 3), (2, 3)]:
+        for (b, d) in [(0, 2), (1, 3), (0, 3)]:
+            lhs = np.log(H[:, a, b]) + np.log(H[:, c, d]) - np.log(H[:, a, d]) - np.log(H[:, c, b])
+            rhs = L[:, a, b] + L[:, c, d] - L[:, a, d] - L[:, c, b]
+            np.testing.assert_allclose(lhs, rhs, atol=1e-12)
+
+
+def test_sinkhorn_rank_one_logits_give_uniform():
+    u = rnd(20, 4, 1); v = rnd(20, 1, 4)
+    H = O.sinkhorn_fwd(u + v, 20, 1e-6)
+    np.testing.assert_allclose(H, 0.25, atol=2e-5)
+    H0 = O.sinkhorn_fwd(u + v, 5, 0.0)
+    np.testing.assert_allclose(H0, 0.25, atol=1e-15)
+
+
+def test_sinkhorn_permutation_equivariant():
+    L = rnd(30, 4, 4)
+    P = np.eye(4)[RNG.permutation(4)]; Q = np.eye(4)[RNG.permutation(4)]
+    H = O.sinkhorn_fwd(L, 20, 1e-6)
+    Hp = O.sinkhorn_fwd(P @ L @ Q, 20, 1e-6)
+    np.testing.assert_allclose(Hp, P @ H @ Q, rtol=1e-13)
+
+
+def test_sinkhorn_last_pass_column_sums():
+    L = rnd(200, 4, 4, std=3.0)
+    for eps in (1e-6, 1e-2):
+        H = O.sinkhorn_fwd(L, 7, eps)
+        cs = H.sum(axis=1)
+        # after the final column pass each column sums to s/(s+eps), s = the pre-pass sum
+        assert np.all(cs <= 1 + 1e-15) and np.all(cs >= 1 - eps / (1 - eps) * 4)
+
+
+def test_sinkhorn_zero_iterations_is_exp():
+    L = rnd(10, 4, 4)
+    np.testing.assert_allclose(O.sinkhorn_fwd(L, 0, 1e-6), np.exp(L), rtol=1e-15)
+
+
+def test_sinkhorn_converged_matches_independent_solver():
+    # Sinkhorn's theorem: the doubly stochastic D1 A D2 is unique.  Find it by
+    # minimising the convex dual sum(exp(L + u_a + v_b)) - sum(u) - sum(v).
+    for trial in range(5):
+        L = rnd(4, 4, std=1.0 + trial)
+        H = O.sinkhorn_fwd(L[None], 2000, 0.0)[0]
+
+        def f(w):
+            u, v = w[:4], w[4:]
+            E = np.exp(L + u[:, None] + v[None, :])
+            return E.sum() - u.sum() - v.sum(), np.concatenate([E.sum(1) - 1, E.sum(0) - 1])
+
+        res = scipy.optimize.minimize(f, np.zeros(8), jac=True, method="BFGS",
+                                      options=dict(gtol=1e-14, maxiter=10000))
+        u, v = res.x[:4], res.x[4:]
+        Hs = np.exp(L + u[:, None] + v[None, :])
+        np.testing.assert_allclose(H, Hs, atol=1e-9)
+        np.testing.assert_allclose(H.sum(0), 1, atol=1e-12)
+        np.testing.assert_allclose(H.sum(1), 1, atol=1e-12)
+
+
+def test_sinkhorn_2x2_closed_form():
+    # a 2x2 doubly stochastic matrix is [[p, 1-p], [1-p, p]] and keeps the
+    # cross ratio: p^2/(1-p)^2 = exp(L00 + L11 - L01 - L10).
+    L = rnd(40, 2, 2, std=2.0)
+    H = O.sinkhorn_fwd(L, 3000, 0.0)
+    s = np.sqrt(np.exp(L[:, 0, 0] + L[:, 1, 1] - L[:, 0, 1] - L[:, 1, 0]))
+    p = s / (1 + s)
+    np.testing.assert_allclose(H[:, 0, 0], p, rtol=1e-10)
+    np.testing.assert_allclose(H[:, 0, 1], 1 - p, rtol=1e-10)
+
+
+def test_sinkhorn_converges_doubly_stochastic_at_1e5():
+    L = rnd(2000, 4, 4)
+    H = O.sinkhorn_fwd(L, 200, 1e-6)
+    np.testing.assert_allclose(H.sum(2), 1, atol=1e-5)
+    np.testing.assert_allclose(H.sum(1), 1, atol=1e-5)
+
+
+# ---------------------------------------------------------------- B2 Sinkhorn backward
+def _fd(f, x, h=1e-6):
+    g = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        hh = h * max(1.0, abs(x[i]))
+        xp = x.copy(); xp[i] += hh
+        xm = x.copy(); xm[i] -= hh
+        g[i] = (f(xp) - f(xm)) / (2 * hh)
+    return g
+
+
+@pytest.mark.parametrize("iters,eps,std", [(1, 1e-6, 1.0), (20, 1e-6, 1.0), (20, 1e-6, 3.4), (4, 0.05, 1.0)])
+def test_sinkhorn_bwd_finite_difference(iters, eps, std):
+    L = rnd(3, 4, 4, std=std); dH = rnd(3, 4, 4)
+    dL = O.sinkhorn_bwd(dH, L, iters, eps)
+    fd = _fd(lambda l: float((dH * O.sinkhorn_fwd(l, iters, eps)).sum()), L)
+    assert np.linalg.norm(dL - fd) <= 1e-6 * max(1.0, np.linalg.norm(fd))
+
+
+def test_sinkhorn_bwd_matches_torch_autograd():
+    L = rnd(64, 4, 4, std=2.0); dH = rnd(64, 4, 4)
+    Lt = torch.tensor(L, dtype=torch.float64, requires_grad=True)
+    M = torch.exp(Lt)
+    for _ in range(20):
+        M = M / (M.sum(dim=2, keepdim=True) + 1e-6)
+        M = M / (M.sum(dim=1, keepdim=True) + 1e-6)
+    (M * torch.tensor(dH)).sum().backward()
+    np.testing.assert_allclose(O.sinkhorn_bwd(dH, L, 20, 1e-6), Lt.grad.numpy(), rtol=1e-9, atol=1e-12)
+
+
+def test_sinkhorn_bwd_row_sums_vanish_and_pin_row_first():
+    # adding a constant to a logit row is undone by the first (row) pass when
+    # eps = 0, so every row of dL sums to zero; columns do not, which pins the
+    # row-then-column order.
+    L = rnd(100, 4, 4); dH = rnd(100, 4, 4)
+    dL = O.sinkhorn_bwd(dH, L, 2, 0.0)
+    scale = np.abs(dL).max()
+    assert np.abs(dL.sum(2)).max() <= 1e-12 * scale
+    assert np.abs(dL.sum(1)).max() >= 1e-3 * scale
+    dL6 = O.sinkhorn_bwd(dH, L, 20, 1e-6)
+    assert np.abs(dL6.sum(2)).max() <= 1e-5 * np.abs(dL6).max()
+
+
+# ---------------------------------------------------------------- F3/B3 aggregate
+def test_aggregate_one_hot_and_uniform():
+    N, n, C = 7, 4, 40
+    X = rnd(N, n, C)
+    sel = RNG.integers(0, n, N)
+    Hp = np.eye(n)[sel]
+    np.testing.assert_array_equal(O.h_aggregate_fwd(X, Hp), X[np.arange(N), sel])
+    np.testing.assert_allclose(O.h_aggregate_fwd(X, np.full((N, n), 1 / n)), X.mean(1), rtol=1e-14, atol=1e-15)
+
+
+def test_aggregate_adjoint_identities():
+    N, n, C = 5, 4, 33
+    X = rnd(N, n, C); Hp = rnd(N, n); g = rnd(N, C)
+    agg = O.h_aggregate_fwd(X, Hp)
+    dX, dH = O.h_aggregate_bwd(g, X, Hp)
+    lhs = (g * agg).sum()
+    np.testing.assert_allclose(lhs, (dX * X).sum(), rtol=1e-12)
+    np.testing.assert_allclose(lhs, (dH * Hp).sum(), rtol=1e-12)
+    np.testing.assert_allclose(dX, Hp[:, :, None] * g[:, None, :], rtol=1e-15)
+
+
+# ---------------------------------------------------------------- F4/B4 post
+def test_post_identity_and_permutation():
+    N, n, C = 6, 4, 24
+    X = rnd(N, n, C); Hp = rnd(N, n); x = rnd(N, C); b = rnd(C)
+    out = O.h_post_bda_fwd(X, np.broadcast_to(np.eye(n), (N, n, n)), Hp, x, b)
+    np.testing.assert_allclose(out, X + Hp[:, :, None] * (x + b)[:, None, :], rtol=1e-15, atol=1e-15)
+    perm = RNG.permutation(n)
+    P = np.eye(n)[perm]            # P[j, i] = [perm[j] == i]; out_i = X_{perm^-1(i)}
+    out = O.h_post_bda_fwd(X, np.broadcast_to(P, (N, n, n)), np.zeros((N, n)), x, None)
+    inv = np.argsort(perm)
+    np.testing.assert_array_equal(out, X[:, inv, :])
+
+
+def test_post_uses_transpose_of_h_res():
+    # H_res = e_0 e_1^T (only entry [0][1] set): transpose means out_1 = X_0, out_0 = 0
+    N, n, C = 2, 4, 8
+    X = rnd(N, n, C)
+    H = np.zeros((N, n, n)); H[:, 0, 1] = 1.0
+    out = O.h_post_bda_fwd(X, H, np.zeros((N, n)), np.zeros((N, C)))
+    np.testing.assert_array_equal(out[:, 1], X[:, 0])
+    np.testing.assert_array_equal(out[:, 0], 0.0)
+
+
+def test_post_stream_sum_conservation():
+    N, n, C = 5, 4, 16
+    X = rnd(N, n, C); Hr = np.abs(rnd(N, n, n)); Hp = rnd(N, n); x = rnd(N, C); b = rnd(C)
+    out = O.h_post_bda_fwd(X, Hr, Hp, x, b)
+    want = (Hr.sum(2)[:, :, None] * X).sum(1) + Hp.sum(1)[:, None] * (x + b)
+    np.testing.assert_allclose(out.sum(1), want, rtol=1e-12, atol=1e-12)
+
+
+def test_post_bwd_adjoints_and_dbias():
+    N, n, C = 5, 4, 20
+    X = rnd(N, n, C); Hr = rnd(N, n, n); Hp = rnd(N, n); x = rnd(N, C); b = rnd(C); G = rnd(N, n, C)
+    out = O.h_post_bda_fwd(X, Hr, Hp, x, b)
+    dX, dHr, dHp, dx, db = O.h_post_bda_bwd(G, X, Hr, Hp, x, b)
+    total = (G * out).sum()
+    mix = (G * O.h_post_bda_fwd(X, Hr, np.zeros((N, n)), np.zeros((N, C)))).sum()
+    dist = total - mix
+    np.testing.assert_allclose(mix, (dX * X).sum(), rtol=1e-12)
+    np.testing.assert_allclose(mix, (dHr * Hr).sum(), rtol=1e-12)
+    np.testing.assert_allclose(dist, (dHp * Hp).sum(), rtol=1e-12)
+    np.testing.assert_allclose(dist, (dx * (x + b)).sum(), rtol=1e-12)
+    np.testing.assert_allclose(db, dx.sum(0), rtol=1e-13, atol=1e-13)
+    _, _, _, _, none = O.h_post_bda_bwd(G, X, Hr, Hp, x, None)
+    assert none is None
+
+
+# ---------------------------------------------------------------- B1 projection backward
+def _proj_loss(X, W, alpha, hb, dHp, dHq, dL, eps):
+    p = O.proj_rms_h(X, W, alpha, hb, eps)
+    return float((dHp * p.H_pre).sum() + (dHq * p.H_post).sum() + (dL * p.L).sum())
+
+
+def test_proj_bwd_finite_difference_all_parameters():
+    N, n, C = 2, 4, 4
+    X = rnd(N, n, C); W = rnd(n * C, 24, std=0.3); alpha = np.array([0.9, 1.3, 0.7]); hb = rnd(24, std=0.2)
+    dHp = rnd(N, n); dHq = rnd(N, n); dL = rnd(N, n, n)
+    eps = 1e-3
+    dX, dW, da, db = O.proj_rms_h_bwd(X, W, dHp, dHq, dL, alpha, hb, eps)
+    f = lambda **kw: _proj_loss(kw.get("X", X), kw.get("W", W), kw.get("alpha", alpha), kw.get("hb", hb),
+                                dHp, dHq, dL, eps)
+    for name, val, grad in (("X", X, dX), ("W", W, dW), ("alpha", alpha, da), ("hb", hb, db)):
+        fd = _fd(lambda v: f(**{name: v}), val)
+        assert np.linalg.norm(grad - fd) <= 1e-6 * max(1.0, np.linalg.norm(fd)), name
+
+
+def test_proj_bwd_matches_torch_autograd():
+    N, n, C = 6, 4, 16
+    X = rnd(N, n, C); W = rnd(n * C, 24, std=0.05); alpha = np.array([1.1, 0.6, 1.4]); hb = rnd(24, std=0.1)
+    dHp = rnd(N, n); dHq = rnd(N, n); dL = rnd(N, n, n); eps = 1e-6
+    t = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+    Xt, Wt, at, bt = t(X), t(W), t(alpha), t(hb)
+    xf = Xt.reshape(N, -1)
+    q = torch.sqrt((xf * xf).sum(1) / (n * C))
+    r = 1 / (q + eps)
+    z = (xf @ Wt) * r[:, None]
+    gains = torch.cat([at[0].repeat(4), at[1].repeat(4), at[2].repeat(16)])
+    zh = z * gains + bt
+    loss = ((torch.tensor(dHp) * torch.sigmoid(zh[:, :4])).sum() + (torch.tensor(dHq) * 2 * torch.sigmoid(zh[:, 4:8])).sum()
+            + (torch.tensor(dL).reshape(N, 16) * zh[:, 8:]).sum())
+    loss.backward()
+    dX, dW, da, db = O.proj_rms_h_bwd(X, W, dHp, dHq, dL, alpha, hb, eps)
+    np.testing.assert_allclose(dX, Xt.grad.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(dW, Wt.grad.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(da, at.grad.numpy(), rtol=1e-10)
+    np.testing.assert_allclose(db, bt.grad.numpy(), rtol=1e-10)
+
+
+def test_proj_bwd_zero_row_is_finite_and_rms_leg_vanishes():
+    N, n, C = 3, 4, 8
+    X = rnd(N, n, C); X[1] = 0.0
+    W = rnd(n * C, 24, std=0.1)
+    dHp = rnd(N, n); dHq = rnd(N, n); dL = rnd(N, n, n)
+    dX, dW, da, db = O.proj_rms_h_bwd(X, W, dHp, dHq, dL, eps_rms=1e-6)
+    assert np.isfinite(dX).all() and np.isfinite(dW).all()
+    # zero row: only the GEMM leg remains, dX = r * (dzh) @ W^T with r = 1/eps
+    p = O.proj_rms_h(X, W, eps_rms=1e-6)
+    s_pre = p.H_pre[1]; s_post = p.H_post[1] / 2
+    dzh = np.concatenate([dHp[1] * s_pre * (1 - s_pre), dHq[1] * 2 * s_post * (1 - s_post), dL[1].ravel()])
+    np.testing.assert_allclose(dX[1].ravel(), 1e6 * (W @ dzh), rtol=1e-12)
+
+
+# ---------------------------------------------------------------- the whole chain
+def _chain_loss(X, W, x_scale, G, bias, iters=20, eps=1e-6):
+    f = O.pre_fwd(X, W, iters=iters, eps=eps)
+    x = f["agg"] * x_scale
+    out = O.h_post_bda_fwd(X, f["H_res"], f["H_post"], x, bias)
+    return float((G * out).sum())
+
+
+def test_chain_backward_finite_difference():
+    # full mHC layer with a per-channel scale as the layer function:
+    # dX = post-bwd dX + pre-bwd dX, with the layer backward d_agg = dx * scale
+    N, n, C = 2, 4, 4
+    X = rnd(N, n, C); W = rnd(n * C, 24, std=0.3); s = RNG.uniform(0.5, 1.5, C); b = rnd(C, std=0.1)
+    G = rnd(N, n, C)
+    f = O.pre_fwd(X, W)
+    x = f["agg"] * s
+    dXp, dHr, dHq, dx, _ = O.h_post_bda_bwd(G, X, f["H_res"], f["H_post"], x, b)
+    pb = O.pre_bwd(dx * s, dHq, dHr, X, W)
+    dX = dXp + pb["dX"]
+    fdX = _fd(lambda v: _chain_loss(v, W, s, G, b), X)
+    fdW = _fd(lambda v: _chain_loss(X, v, s, G, b), W)
+    assert np.linalg.norm(dX - fdX) <= 1e-6 * np.linalg.norm(fdX)
+    assert np.linalg.norm(pb["dW"] - fdW) <= 1e-6 * max(1.0, np.linalg.norm(fdW))
+
+
+def test_tiny_chain_workload_brute_force_consistency():
+    # the 64-token fp32 forward chain: pre_fwd composes exactly the single ops
+    from mhc_hyper_connection_proj_amd import synth
+    w = synth.WORKLOADS["tiny_chain"]
+    X = synth.tensor(w, "X").astype(np.float64); W = synth.tensor(w, "W").astype(np.float64)
+    f = O.pre_fwd(X, W)
+    # brute force: every token independently through plain numpy
+    Xf = X.reshape(64, -1)
+    r = 1 / (np.sqrt((Xf ** 2).mean(1)) + 1e-6)
+    z = (Xf @ W) * r[:, None]
+    np.testing.assert_allclose(f["H_pre"], 1 / (1 + np.exp(-z[:, :4])), rtol=1e-12)
+    np.testing.assert_allclose(f["agg"], np.einsum("ti,tic->tc", f["H_pre"], X), rtol=1e-12, atol=1e-14)
+    H = f["H_res"]
+    # row sums of the returned matrix: close to 1 at the tiny chain's logit spread
+    assert np.abs(H.sum(2) - 1).max() < 1e-5 and np.abs(H.sum(1) - 1).max() < 1e-5
