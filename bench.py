@@ -1,0 +1,243 @@
+"""Benchmark of the per-token mHC path on one MI355X.
+
+Default workload (one GPU): B=4, T=4096 (16384 tokens), n=4, C=7168, bf16
+residual; the layer between h_aggregate and h_post_bda is a fixed per-channel
+bf16 scale.  One step = pre pass forward (projection + RMS + compute_h +
+Sinkhorn + h_aggregate) -> layer -> h_post_bda forward -> h_post_bda backward
+-> layer backward -> pre pass backward (accumulated onto the h_post_bda dX).
+
+Timing: W untimed warmup steps, then K timed steps between synchronisations.
+HIP events on the launch stream bracket every phase; the mHC time of a step
+is the sum of its four mHC phases (the layer stand-in is not part of the
+path and is reported separately).  value = tokens / mHC time.
+
+Prints one JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "tokens/s and achieved HBM GB/s (% of peak), mHC pre+post fwd+bwd, n=4"
+
+
+def ledger_bytes_per_token(C: int, N: int) -> dict:
+    """Algorithmic HBM bytes per token: every boundary tensor read or written once per phase."""
+    K = 4 * C
+    w_amort = K * 24 * 4 / N  # W read (fwd), W read + dW write (bwd), amortised over the tokens
+    phases = {
+        "pre_fwd": 8 * C + 2 * C + 16 + 16 + 64 + 64 + 128 + w_amort,
+        "post_fwd": 8 * C + 2 * C + 64 + 16 + 8 * C,
+        "post_bwd": 8 * C + 8 * C + 2 * C + 64 + 16 + 8 * C + 2 * C + 64 + 16,
+        "pre_bwd": 2 * C + 8 * C + 8 * C + 16 + 64 + 128 + 16 + 16 + 64 + 8 * C + 2 * w_amort,
+    }
+    phases["total"] = sum(phases.values())
+    return phases
+
+
+def src_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(w, X, W, s, G, budget_s: float) -> dict:
+    """Time the fp64 oracle (single thread, as written) on the first tokens of the workload."""
+    import oracle as O
+
+    O._lib()
+    C = w.C
+    n_done, t_used, chunk = 0, 0.0, 16
+    Wd = W.astype(np.float64)
+    sd = O.bf16_bits_to_f64(s)
+    while t_used < budget_s and n_done + chunk <= X.shape[0]:
+        sl = slice(n_done, n_done + chunk)
+        Xc = O.bf16_bits_to_f64(X[sl]); Gc = O.bf16_bits_to_f64(G[sl])
+        t0 = time.perf_counter()
+        f = O.pre_fwd(Xc, Wd, eps_rms=w.rms_eps, iters=w.iters, eps=w.eps)
+        x = O.round_f64_to_bf16(O.round_f64_to_bf16(f["agg"]) * sd)
+        O.h_post_bda_fwd(Xc, f["H_res"], f["H_post"], x, None)
+        dX, dHr, dHp, dx, _ = O.h_post_bda_bwd(Gc, Xc, f["H_res"], f["H_post"], x, None)
+        g = O.round_f64_to_bf16(O.round_f64_to_bf16(dx) * sd)
+        O.pre_bwd(g, dHp, dHr, Xc, Wd, eps_rms=w.rms_eps, iters=w.iters, eps=w.eps)
+        t_used += time.perf_counter() - t0
+        n_done += chunk
+    return {"value": n_done / t_used, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n_done} tokens of the workload (C={C}), full mHC fwd+bwd chain incl. "
+                      f"layer scale, fp64, {t_used:.1f} s single-threaded"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--tokens", type=int, default=None, help="override token count (testing only)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a 1 GiB device copy (for HBM counter calibration under rocprofv3 --pmc)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards over tokens with no exchange; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from mhc_hyper_connection_proj_amd import _lib, synth
+    from mhc_hyper_connection_proj_amd._lib import MHC_BF16
+
+    lib = _lib.lib()
+    w = synth.WORKLOADS["full_layer"]
+    N = args.tokens or w.tokens
+    C, n, K = w.C, w.n, 4 * w.C
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    X = synth.tensor(w, "X", tokens=N)
+    W = synth.tensor(w, "W")
+    s = synth.tensor(w, "scale")
+    G = synth.tensor(w, "G", tokens=N)
+    Xd, Wd, sd, Gd = to_dev(X), to_dev(W), to_dev(s), to_dev(G)
+
+    f32 = torch.float32
+    e = lambda *shape, dt=f32: torch.empty(*shape, dtype=dt, device=dev)
+    bf = torch.bfloat16
+    H_pre, H_post, H_res, L, saved = e(N, 4), e(N, 4), e(N, 4, 4), e(N, 4, 4), e(N, 32)
+    agg, x, out, dx, g = e(N, C, dt=bf), e(N, C, dt=bf), e(N, 4, C, dt=bf), e(N, C, dt=bf), e(N, C, dt=bf)
+    dX, dHr, dHp = e(N, 4, C, dt=bf), e(N, 4, 4), e(N, 4)
+    dW, da, db = e(K, 24), e(3), e(24)
+    ws_f = lib.mhc_pre_fwd_workspace_size(N, n, C, MHC_BF16)
+    ws_b = lib.mhc_pre_bwd_workspace_size(N, n, C, MHC_BF16)
+    ws_p = lib.mhc_h_post_bda_bwd_workspace_size(N, n, C, MHC_BF16, 0)
+    wsf, wsb = e(max(ws_f, 16), dt=torch.uint8), e(max(ws_b, 16), dt=torch.uint8)
+    wsp = e(max(ws_p, 16), dt=torch.uint8)
+    P = lambda t: t.data_ptr()
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def pre_fwd():
+        _lib.check(lib.mhc_pre_fwd(sp, N, n, C, MHC_BF16, P(Xd), P(Wd), None, None, w.rms_eps, w.iters, w.eps,
+                                   P(H_pre), P(H_post), P(H_res), P(L), P(saved), P(agg), P(wsf), ws_f))
+
+    def post_fwd():
+        _lib.check(lib.mhc_h_post_bda_fwd(sp, N, n, C, MHC_BF16, P(Xd), P(H_res), P(H_post), P(x), None, P(out)))
+
+    def post_bwd():
+        _lib.check(lib.mhc_h_post_bda_bwd(sp, N, n, C, MHC_BF16, P(Gd), P(Xd), P(H_res), P(H_post), P(x), None,
+                                          P(dX), P(dHr), P(dHp), P(dx), None, P(wsp), ws_p))
+
+    def pre_bwd():
+        _lib.check(lib.mhc_pre_bwd(sp, N, n, C, MHC_BF16, P(g), P(dHp), P(dHr), P(Xd), P(Wd), None, P(saved),
+                                   P(H_pre), P(H_post), P(L), w.iters, w.eps, P(dX), 1, P(dW), P(da), P(db),
+                                   None, None, P(wsb), ws_b))
+
+    def layer_fwd():
+        torch.mul(agg, sd, out=x)
+
+    def layer_bwd():
+        torch.mul(dx, sd, out=g)
+
+    seq = [("pre_fwd", pre_fwd, True), ("layer_fwd", layer_fwd, False), ("post_fwd", post_fwd, True),
+           ("post_bwd", post_bwd, True), ("layer_bwd", layer_bwd, False), ("pre_bwd", pre_bwd, True)]
+
+    if args.copy_calib:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    for _ in range(args.warmup):
+        for _, fn, _ in seq:
+            fn()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for st in range(args.steps):
+        evs[st][0].record(stream)
+        for i, (_, fn, _) in enumerate(seq):
+            fn()
+            evs[st][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    phase_ms = {name: [] for name, _, _ in seq}
+    for st in range(args.steps):
+        for i, (name, _, _) in enumerate(seq):
+            phase_ms[name].append(evs[st][i].elapsed_time(evs[st][i + 1]))
+    mean = {k: float(np.mean(v)) for k, v in phase_ms.items()}
+    mhc_ms = sum(mean[k] for k, _, m in seq if m)
+    step_ms = sum(mean.values())
+
+    led = ledger_bytes_per_token(C, N)
+    tot_bytes = led["total"] * N
+    gbs = tot_bytes / (mhc_ms * 1e-3) / 1e9
+
+    # dominant kernel: h_post_bda backward is one kernel (no bias) and the largest byte mover
+    kname = "h_post_bda_bwd_kernel"
+    k_ms = mean["post_bwd"]
+    k_bytes = led["post_bwd"] * N
+    k_gbs = k_bytes / (k_ms * 1e-3) / 1e9
+    traffic = None
+    pmc = os.path.join(ROOT, "profiles", "h_post_bda_bwd_full_layer_pmc.json")
+    if os.path.exists(pmc):
+        rec = json.load(open(pmc))
+        if rec.get("src_hash") == src_hash(["mhc_hyper_connection_proj_amd/csrc/streams.hip",
+                                            "mhc_hyper_connection_proj_amd/csrc/device.h"]):
+            traffic = rec.get("hbm_bytes_per_launch")
+
+    res = {
+        "metric": METRIC,
+        "value": N / (mhc_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": mhc_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "full_layer: B=4 T=4096 n=4 C=7168 bf16 residual, fp32 W [28672,24], "
+                               "Sinkhorn 20 iters eps=1e-6, layer = per-channel bf16 scale, no bias",
+                   "tokens": N, "n": n, "C": C, "parallelism": "single GPU"},
+        "achieved_gbs": gbs,
+        "hbm_frac": gbs / HBM_PEAK_GBS,
+        "ledger_bytes_per_token": led["total"],
+        "phases_ms": mean,
+        "ms_per_step_incl_layer": step_ms,
+        "wall_ms_per_step": wall * 1e3 / args.steps,
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": k_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": k_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": k_bytes, "avg_launch_ms": k_ms},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, X, W, s, G, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,231 @@
+/*
+ * mhc.h -- C ABI of libmhc: the per-token mHC (Manifold-Constrained
+ * Hyper-Connections) residual-mixing path on AMD Instinct MI355X (gfx950).
+ *
+ * Notation (per token): n residual streams of C channels; K = n*C; the
+ * flattened stream index is k = i*C + c; J = n*n + 2n controller outputs,
+ * ordered PRE [0,n) | POST [n,2n) | RES [2n, 2n+n*n) with RES row-major.
+ * This build supports n == 4 (J = 24) on the GPU.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls only enqueue work on it and return; results are ready when the
+ *    stream has reached the call.
+ *  - Every tensor pointer is caller-owned DEVICE memory, dense, row-major,
+ *    16-byte aligned.  The library allocates nothing and keeps no state
+ *    between calls; scratch for cross-token reductions comes from the
+ *    caller's `workspace` (sized by the matching *_workspace_size query,
+ *    256-byte aligned).  Calls on different streams with disjoint buffers
+ *    may run concurrently.
+ *  - Activation tensors (residual X and its gradients, the layer input/output
+ *    x, bias, the aggregated stream) are stored as `act` (bf16 or fp32) and
+ *    computed in fp32; H tensors, logits, W, alpha, hbias and all of their
+ *    gradients are fp32.  bf16 outputs are rounded once, to nearest even.
+ *  - Every output is fully overwritten; `accumulate_dX = 1` is the only
+ *    read-modify-write (dX += this op's gradient, for summing the residual
+ *    gradient contributions).  No float atomics: results are bitwise
+ *    deterministic from run to run.
+ *  - Fail-closed validation BEFORE anything is enqueued: a bad argument
+ *    returns an error and leaves every output untouched.  MHC_ERR_NULL for a
+ *    missing required pointer, MHC_ERR_SHAPE for negative/zero sizes,
+ *    MHC_ERR_UNSUPPORTED for n != 4, C % 8 != 0, C > 16384 or iters > 4096,
+ *    MHC_ERR_ALIGN for pointers not 16-byte aligned, MHC_ERR_ALIAS when an
+ *    output overlaps an input or another output, MHC_ERR_WORKSPACE when the
+ *    workspace is missing or too small, MHC_ERR_ARG for eps < 0, a
+ *    non-finite eps or an unknown dtype, MHC_ERR_HIP when a launch fails.
+ *    tokens == 0 (or count == 0) is a successful no-op.  mhc_last_error()
+ *    describes the most recent failure on the calling thread.
+ */
+#ifndef MHC_H_
+#define MHC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mhc_status {
+  MHC_OK = 0,
+  MHC_ERR_NULL = 1,
+  MHC_ERR_SHAPE = 2,
+  MHC_ERR_UNSUPPORTED = 3,
+  MHC_ERR_ALIGN = 4,
+  MHC_ERR_ALIAS = 5,
+  MHC_ERR_WORKSPACE = 6,
+  MHC_ERR_ARG = 7,
+  MHC_ERR_HIP = 8
+} mhc_status;
+
+typedef enum mhc_dtype { MHC_BF16 = 0, MHC_F32 = 1 } mhc_dtype;
+
+/* Per-token record written by the projection forward and read by its
+ * backward: fp32 [tokens][MHC_SAVED_STRIDE] = { r, q, z[0..J), 0 ... } with
+ * q = sqrt(sum x^2 / K), r = 1/(q + rms_eps) and z = r * (x @ W) (pre-gain). */
+#define MHC_SAVED_STRIDE 32
+
+const char *mhc_status_string(mhc_status s);
+const char *mhc_last_error(void);
+const char *mhc_version(void);
+
+/* -------------------------------------------------------------------------
+ * Projection + RMS + compute_h, forward.
+ * Megatron Core "core.fusions.fused_mhc_kernels", operation
+ * proj_rms_compute_h (`_torch_proj_rms_compute_h(x, weight, alpha_pre,
+ * alpha_post, alpha_res, bias, n, eps)`); RL-Kernel PR #383 review of the RMS
+ * leg (r = 1/(q + eps)) and the commit making alpha three segment gains.
+ *
+ *   q = sqrt(sum_k x_k^2 / K), r = 1/(q + rms_eps), z = r * (x @ W)
+ *   zh_j = alpha[seg(j)] * z_j + hbias[j]
+ *   H_pre = sigmoid(zh_PRE), H_post = 2 sigmoid(zh_POST), logits = zh_RES
+ *
+ * X [tokens][n][C] (act); W [K][J] fp32; alpha [3] fp32 (pre, post, res) or
+ * NULL for ones; hbias [J] fp32 or NULL for zeros.  Outputs (fp32): H_pre
+ * [tokens][n], H_post [tokens][n], H_res_logits [tokens][n][n], saved
+ * [tokens][MHC_SAVED_STRIDE].  `saved` may be NULL when no backward follows.
+ * ---------------------------------------------------------------------- */
+size_t mhc_proj_rms_h_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act);
+mhc_status mhc_proj_rms_h(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                          const void *X, const float *W, const float *alpha, const float *hbias,
+                          float rms_eps, float *H_pre, float *H_post, float *H_res_logits,
+                          float *saved, void *workspace, size_t workspace_bytes);
+
+/* -------------------------------------------------------------------------
+ * Projection + RMS + compute_h, backward (RL-Kernel PR #383: the RMS
+ * backward is the GEMM leg plus the RMS leg, with the RMS leg zero for an
+ * all-zero row; d_alpha is three scalars).
+ *
+ *   dzh_PRE = dH_pre * H_pre (1 - H_pre), dzh_POST = dH_post * H_post (1 -
+ *   H_post/2), dzh_RES = dH_res_logits; dz = alpha * dzh; dr = sum_j dz_j z_j / r;
+ *   dX (+)= r dz @ W^T - dr r^2 x / (K q)     (RMS term 0 when q == 0)
+ *   dW = sum_t r x^T dz, dalpha[s] = sum_t sum_{j in s} dzh_j z_j,
+ *   dhbias = sum_t dzh
+ *
+ * Inputs: X, W, alpha (NULL = ones), saved/H_pre/H_post from the forward,
+ * upstream gradients dH_pre [tokens][n], dH_post [tokens][n], dH_res_logits
+ * [tokens][n][n] (fp32).  Outputs: dX [tokens][n][C] (act; overwritten, or
+ * accumulated into when accumulate_dX != 0); dW [K][J], dalpha [3], dhbias
+ * [J] (fp32; each may be NULL to skip it).
+ * ---------------------------------------------------------------------- */
+size_t mhc_proj_rms_h_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act);
+mhc_status mhc_proj_rms_h_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                              const void *X, const float *W, const float *alpha, const float *saved,
+                              const float *H_pre, const float *H_post, const float *dH_pre,
+                              const float *dH_post, const float *dH_res_logits, void *dX,
+                              int32_t accumulate_dX, float *dW, float *dalpha, float *dhbias,
+                              void *workspace, size_t workspace_bytes);
+
+/* -------------------------------------------------------------------------
+ * Sinkhorn-Knopp projection of each n x n logit matrix (Megatron Core
+ * fused_mhc_kernels, operation sinkhorn / `fused_sinkhorn`: project logits to
+ * a doubly stochastic matrix; rwkv-ops mhu_ffi.cu, "Sinkhorn Knopp FFI",
+ * attributes num_iters and eps).
+ *
+ *   M = exp(logits); iters times: each row /= (row sum + eps), then each
+ *   column /= (column sum + eps).   H_res = M.
+ *
+ * logits, H_res: fp32 [count][n][n].  iters in [0, 4096], eps >= 0.
+ * ---------------------------------------------------------------------- */
+mhc_status mhc_sinkhorn_fwd(void *stream, int64_t count, int32_t n, const float *logits,
+                            float *H_res, int32_t iters, float eps);
+
+/* Exact reverse mode of the unrolled forward map (every half-step, eps
+ * included), replayed from the logits (rwkv-ops "Sinkhorn Knopp FFI"
+ * backward takes the forward input, iters and eps).  dH_res, logits,
+ * dlogits: fp32 [count][n][n]. */
+mhc_status mhc_sinkhorn_bwd(void *stream, int64_t count, int32_t n, const float *dH_res,
+                            const float *logits, float *dlogits, int32_t iters, float eps);
+
+/* -------------------------------------------------------------------------
+ * h_aggregate: weighted n-stream -> 1-stream aggregation (Megatron Core
+ * fused_mhc_kernels `fused_h_aggregate` / `FusedHAggregate`; rwkv-ops
+ * "Stream Aggregate FFI", per-token weights).
+ *
+ *   out[t][c] = sum_i H_pre[t][i] X[t][i][c]
+ *
+ * X [tokens][n][C] (act), H_pre [tokens][n] fp32, out [tokens][C] (act).
+ * ---------------------------------------------------------------------- */
+mhc_status mhc_h_aggregate_fwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                               const void *X, const float *H_pre, void *out);
+
+/* Backward (`_torch_h_aggregate_bwd(grad_output, x, h_pre)`):
+ *   dX[t][i][c] (+)= H_pre[t][i] g[t][c],   dH_pre[t][i] = sum_c g[t][c] X[t][i][c]
+ * g [tokens][C] (act); dX (act, overwritten or accumulated); dH_pre fp32. */
+mhc_status mhc_h_aggregate_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                               const void *g, const void *X, const float *H_pre, void *dX,
+                               int32_t accumulate_dX, float *dH_pre);
+
+/* -------------------------------------------------------------------------
+ * h_post_bda: H_res^T @ residual + H_post * (x + bias) (Megatron Core
+ * fused_mhc_kernels `fused_h_post_bda` / `FusedHPostBDA`; rwkv-ops "MHC
+ * Post-Op FFI", which has no bias).
+ *
+ *   out[t][i][c] = sum_j H_res[t][j][i] X[t][j][c] + H_post[t][i] (x[t][c] + bias[c])
+ *
+ * X [tokens][n][C] (act), H_res [tokens][n][n] fp32, H_post [tokens][n] fp32,
+ * x [tokens][C] (act), bias [C] (act) or NULL, out [tokens][n][C] (act).
+ * ---------------------------------------------------------------------- */
+mhc_status mhc_h_post_bda_fwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                              const void *X, const float *H_res, const float *H_post, const void *x,
+                              const void *bias, void *out);
+
+/* Backward (`_torch_h_post_bda_bwd(grad_output, h_res, original_residual,
+ * h_post, x, bias)` -> five gradients, the last optional):
+ *   dX[j][c] = sum_i H_res[j][i] G[i][c]          (act, overwritten)
+ *   dH_res[j][i] = sum_c X[j][c] G[i][c]          (fp32)
+ *   dH_post[i] = sum_c G[i][c] (x[c] + bias[c])   (fp32)
+ *   dx[c] = sum_i H_post[i] G[i][c]               (act)
+ *   dbias[c] = sum_t dx_t[c]                      (act; only if dbias != NULL,
+ *                                                  which requires bias != NULL)
+ * G [tokens][n][C] (act). */
+size_t mhc_h_post_bda_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                                         int32_t with_dbias);
+mhc_status mhc_h_post_bda_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                              const void *G, const void *X, const float *H_res,
+                              const float *H_post, const void *x, const void *bias, void *dX,
+                              float *dH_res, float *dH_post, void *dx, void *dbias,
+                              void *workspace, size_t workspace_bytes);
+
+/* -------------------------------------------------------------------------
+ * Fused pre pass (rwkv-ops "MHC Pre-Op FFI" fuses aggregate + sigmoid +
+ * Sinkhorn; here the projection is fused in as well):
+ *   forward  = proj_rms_h -> sinkhorn(H_res_logits) -> h_aggregate(X, H_pre)
+ * Outputs: H_pre, H_post, H_res (Sinkhorn output), H_res_logits, saved (as
+ * mhc_proj_rms_h) and agg [tokens][C] (act).
+ * ---------------------------------------------------------------------- */
+size_t mhc_pre_fwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act);
+mhc_status mhc_pre_fwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                       const void *X, const float *W, const float *alpha, const float *hbias,
+                       float rms_eps, int32_t iters, float eps, float *H_pre, float *H_post,
+                       float *H_res, float *H_res_logits, float *saved, void *agg,
+                       void *workspace, size_t workspace_bytes);
+
+/* Fused pre pass backward: h_aggregate backward (dH_pre and the H_pre * g
+ * residual term) + Sinkhorn backward (dH_res -> logits) + projection
+ * backward, with the residual gradient terms summed into dX (Megatron Core
+ * `fused_add_3` sums the three residual-gradient contributions).
+ *
+ * g [tokens][C] (act) is the gradient of the aggregated stream; dH_post
+ * [tokens][n] and dH_res [tokens][n][n] (fp32) come from the h_post_bda
+ * backward.  dX (act): overwritten, or accumulated into when
+ * accumulate_dX != 0 (pass the h_post_bda dX to get the layer's full
+ * residual gradient).  dW/dalpha/dhbias as mhc_proj_rms_h_bwd.  dH_pre_out
+ * [tokens][n] and dlogits_out [tokens][n][n] (fp32) optionally receive the
+ * intermediate gradients; pass NULL to skip them.
+ * ---------------------------------------------------------------------- */
+size_t mhc_pre_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act);
+mhc_status mhc_pre_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                       const void *g, const float *dH_post, const float *dH_res, const void *X,
+                       const float *W, const float *alpha, const float *saved, const float *H_pre,
+                       const float *H_post, const float *H_res_logits, int32_t iters, float eps,
+                       void *dX, int32_t accumulate_dX, float *dW, float *dalpha, float *dhbias,
+                       float *dH_pre_out, float *dlogits_out, void *workspace,
+                       size_t workspace_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHC_H_ */

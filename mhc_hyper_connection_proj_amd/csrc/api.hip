@@ -1,0 +1,474 @@
+// api.hip -- the extern "C" boundary of libmhc (declared in include/mhc.h).
+//
+// Every entry point validates all of its arguments on the host before it
+// enqueues anything (fail closed), then launches on the caller's stream.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/mhc.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+struct Span {
+  const char *name;
+  uintptr_t lo, hi;
+};
+
+// Collects the buffers of one call and checks them.
+class Validator {
+ public:
+  explicit Validator(const char *fn) : fn_(fn) {}
+
+  bool ok() const { return st_ == MHC_OK; }
+  mhc_status status() const { return st_; }
+
+  void fail(mhc_status s, const std::string &msg) {
+    if (st_ != MHC_OK) return;
+    st_ = s;
+    g_last_error = std::string(fn_) + ": " + msg;
+  }
+
+  void dims(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
+    if (tokens < 0) fail(MHC_ERR_SHAPE, "tokens must be >= 0");
+    if (n <= 0) fail(MHC_ERR_SHAPE, "n must be > 0");
+    if (C <= 0) fail(MHC_ERR_SHAPE, "C must be > 0");
+    if (n > 0 && n != mhc::kN) fail(MHC_ERR_UNSUPPORTED, "only n == 4 is supported");
+    if (C > 0 && C % 8 != 0) fail(MHC_ERR_UNSUPPORTED, "C must be a multiple of 8");
+    if (C > mhc::kMaxC) fail(MHC_ERR_UNSUPPORTED, "C must be <= 16384");
+    if (act != MHC_BF16 && act != MHC_F32) fail(MHC_ERR_ARG, "unknown activation dtype");
+  }
+
+  void eps(float e, const char *what) {
+    if (!std::isfinite(e) || e < 0.f) fail(MHC_ERR_ARG, std::string(what) + " must be finite and >= 0");
+  }
+
+  void iters(int32_t it) {
+    if (it < 0) fail(MHC_ERR_ARG, "iters must be >= 0");
+    if (it > 4096) fail(MHC_ERR_UNSUPPORTED, "iters must be <= 4096");
+  }
+
+  // A device buffer of `bytes` bytes.  Optional buffers may be NULL.
+  void in(const void *p, size_t bytes, const char *name, bool optional = false) {
+    add(p, bytes, name, optional, ins_);
+  }
+  void out(const void *p, size_t bytes, const char *name, bool optional = false) {
+    add(p, bytes, name, optional, outs_);
+  }
+
+  void workspace(const void *ws, size_t have, size_t need) {
+    if (need == 0) return;
+    if (!ws) { fail(MHC_ERR_WORKSPACE, "workspace is NULL but " + std::to_string(need) + " bytes are needed"); return; }
+    if (have < need) {
+      fail(MHC_ERR_WORKSPACE, "workspace too small: " + std::to_string(have) + " < " + std::to_string(need));
+      return;
+    }
+    if (reinterpret_cast<uintptr_t>(ws) % 16) { fail(MHC_ERR_ALIGN, "workspace not 16-byte aligned"); return; }
+    outs_.push_back({"workspace", reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + need});
+  }
+
+  // Outputs must not overlap inputs or each other.
+  mhc_status finish() {
+    if (st_ != MHC_OK) return st_;
+    for (size_t a = 0; a < outs_.size(); ++a) {
+      for (const Span &b : ins_)
+        if (overlap(outs_[a], b)) {
+          fail(MHC_ERR_ALIAS, std::string(outs_[a].name) + " overlaps input " + b.name);
+          return st_;
+        }
+      for (size_t b = a + 1; b < outs_.size(); ++b)
+        if (overlap(outs_[a], outs_[b])) {
+          fail(MHC_ERR_ALIAS, std::string(outs_[a].name) + " overlaps output " + outs_[b].name);
+          return st_;
+        }
+    }
+    return st_;
+  }
+
+ private:
+  static bool overlap(const Span &a, const Span &b) { return a.lo < b.hi && b.lo < a.hi; }
+
+  void add(const void *p, size_t bytes, const char *name, bool optional, std::vector<Span> &v) {
+    if (!p) {
+      if (!optional) fail(MHC_ERR_NULL, std::string(name) + " is NULL");
+      return;
+    }
+    if (reinterpret_cast<uintptr_t>(p) % 16) {
+      fail(MHC_ERR_ALIGN, std::string(name) + " is not 16-byte aligned");
+      return;
+    }
+    if (bytes) v.push_back({name, reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + bytes});
+  }
+
+  const char *fn_;
+  mhc_status st_ = MHC_OK;
+  std::vector<Span> ins_, outs_;
+};
+
+inline size_t esz(mhc_dtype act) { return act == MHC_F32 ? 4 : 2; }
+
+mhc_status launched(const char *fn) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_last_error = std::string(fn) + ": launch failed: " + hipGetErrorString(e);
+    return MHC_ERR_HIP;
+  }
+  return MHC_OK;
+}
+
+__global__ void fill_zero_kernel(float *p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+__global__ void fill_zero_u16_kernel(uint16_t *p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// Zero-fill kernels (not hipMemsetAsync, so callers may capture the call in
+// a HIP graph).  Return whether anything was launched.
+bool zero_f32(hipStream_t s, float *p, int64_t n) {
+  if (!p || n <= 0) return false;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
+  return true;
+}
+
+bool zero_act(hipStream_t s, void *p, int64_t n, mhc_dtype act) {
+  if (!p || n <= 0) return false;
+  if (act == MHC_F32) return zero_f32(s, (float *)p, n);
+  hipLaunchKernelGGL(fill_zero_u16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (uint16_t *)p, n);
+  return true;
+}
+
+constexpr int64_t J = mhc::kJ;
+
+}  // namespace
+
+extern "C" {
+
+const char *mhc_status_string(mhc_status s) {
+  switch (s) {
+    case MHC_OK: return "MHC_OK";
+    case MHC_ERR_NULL: return "MHC_ERR_NULL";
+    case MHC_ERR_SHAPE: return "MHC_ERR_SHAPE";
+    case MHC_ERR_UNSUPPORTED: return "MHC_ERR_UNSUPPORTED";
+    case MHC_ERR_ALIGN: return "MHC_ERR_ALIGN";
+    case MHC_ERR_ALIAS: return "MHC_ERR_ALIAS";
+    case MHC_ERR_WORKSPACE: return "MHC_ERR_WORKSPACE";
+    case MHC_ERR_ARG: return "MHC_ERR_ARG";
+    case MHC_ERR_HIP: return "MHC_ERR_HIP";
+  }
+  return "MHC_ERR_UNKNOWN";
+}
+
+const char *mhc_last_error(void) { return g_last_error.c_str(); }
+
+const char *mhc_version(void) { return "libmhc 0.1 gfx950"; }
+
+// ------------------------------------------------------------------ projection fwd
+size_t mhc_proj_rms_h_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
+  if (tokens <= 0 || n != 4 || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
+  return mhc::proj_fwd_ws(tokens, C, act == MHC_F32);
+}
+
+mhc_status mhc_proj_rms_h(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                          const void *X, const float *W, const float *alpha, const float *hbias,
+                          float rms_eps, float *H_pre, float *H_post, float *H_res_logits,
+                          float *saved, void *workspace, size_t workspace_bytes) {
+  Validator v("mhc_proj_rms_h");
+  v.dims(tokens, n, C, act);
+  v.eps(rms_eps, "rms_eps");
+  if (!v.ok()) return v.status();
+  if (tokens == 0) return MHC_OK;
+  const int64_t K = 4 * C;
+  v.in(X, tokens * K * esz(act), "X");
+  v.in(W, K * J * 4, "W");
+  v.in(alpha, 3 * 4, "alpha", true);
+  v.in(hbias, J * 4, "hbias", true);
+  v.out(H_pre, tokens * 16, "H_pre");
+  v.out(H_post, tokens * 16, "H_post");
+  v.out(H_res_logits, tokens * 64, "H_res_logits");
+  v.out(saved, tokens * MHC_SAVED_STRIDE * 4, "saved", true);
+  v.workspace(workspace, workspace_bytes, mhc::proj_fwd_ws(tokens, C, act == MHC_F32));
+  if (v.finish() != MHC_OK) return v.status();
+  mhc::launch_proj_fwd((hipStream_t)stream, act == MHC_F32, tokens, C, X, W, alpha, hbias, rms_eps,
+                       H_pre, H_post, H_res_logits, saved, nullptr, 0, 0.f, workspace);
+  return launched("mhc_proj_rms_h");
+}
+
+// ------------------------------------------------------------------ projection bwd
+size_t mhc_proj_rms_h_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
+  if (tokens <= 0 || n != 4 || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
+  return mhc::proj_bwd_ws(tokens, C, act == MHC_F32);
+}
+
+mhc_status mhc_proj_rms_h_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                              const void *X, const float *W, const float *alpha, const float *saved,
+                              const float *H_pre, const float *H_post, const float *dH_pre,
+                              const float *dH_post, const float *dH_res_logits, void *dX,
+                              int32_t accumulate_dX, float *dW, float *dalpha, float *dhbias,
+                              void *workspace, size_t workspace_bytes) {
+  Validator v("mhc_proj_rms_h_bwd");
+  v.dims(tokens, n, C, act);
+  if (!v.ok()) return v.status();
+  const int64_t K = 4 * C;
+  const hipStream_t s = (hipStream_t)stream;
+  if (tokens == 0) {
+    v.out(dW, K * J * 4, "dW", true);
+    v.out(dalpha, 12, "dalpha", true);
+    v.out(dhbias, J * 4, "dhbias", true);
+    if (v.finish() != MHC_OK) return v.status();
+    const bool any = zero_f32(s, dW, K * J) | zero_f32(s, dalpha, 3) | zero_f32(s, dhbias, J);
+    return any ? launched("mhc_proj_rms_h_bwd") : MHC_OK;
+  }
+  v.in(X, tokens * K * esz(act), "X");
+  v.in(W, K * J * 4, "W");
+  v.in(alpha, 12, "alpha", true);
+  v.in(saved, tokens * MHC_SAVED_STRIDE * 4, "saved");
+  v.in(H_pre, tokens * 16, "H_pre");
+  v.in(H_post, tokens * 16, "H_post");
+  v.in(dH_pre, tokens * 16, "dH_pre");
+  v.in(dH_post, tokens * 16, "dH_post");
+  v.in(dH_res_logits, tokens * 64, "dH_res_logits");
+  v.out(dX, tokens * K * esz(act), "dX");
+  v.out(dW, K * J * 4, "dW", true);
+  v.out(dalpha, 12, "dalpha", true);
+  v.out(dhbias, J * 4, "dhbias", true);
+  v.workspace(workspace, workspace_bytes, mhc::proj_bwd_ws(tokens, C, act == MHC_F32));
+  if (v.finish() != MHC_OK) return v.status();
+  mhc::ProjBwdArgs a{};
+  a.f32 = act == MHC_F32; a.N = tokens; a.C = C; a.X = X; a.W = W; a.alpha = alpha; a.saved = saved;
+  a.H_pre = H_pre; a.H_post = H_post; a.dH_pre = dH_pre; a.dH_post = dH_post; a.dL = dH_res_logits;
+  a.dH_res = nullptr; a.logits = nullptr; a.iters = 0; a.eps = 0.f; a.g = nullptr; a.dX = dX;
+  a.accumulate = accumulate_dX != 0; a.dW = dW; a.dalpha = dalpha; a.dhbias = dhbias;
+  a.dH_pre_out = nullptr; a.dL_out = nullptr; a.ws = workspace;
+  mhc::launch_proj_bwd(s, a);
+  return launched("mhc_proj_rms_h_bwd");
+}
+
+// ------------------------------------------------------------------ Sinkhorn
+mhc_status mhc_sinkhorn_fwd(void *stream, int64_t count, int32_t n, const float *logits,
+                            float *H_res, int32_t iters, float eps) {
+  Validator v("mhc_sinkhorn_fwd");
+  if (count < 0) v.fail(MHC_ERR_SHAPE, "count must be >= 0");
+  if (n <= 0) v.fail(MHC_ERR_SHAPE, "n must be > 0");
+  else if (n != 4) v.fail(MHC_ERR_UNSUPPORTED, "only n == 4 is supported");
+  v.iters(iters);
+  v.eps(eps, "eps");
+  if (!v.ok()) return v.status();
+  if (count == 0) return MHC_OK;
+  v.in(logits, count * 64, "logits");
+  v.out(H_res, count * 64, "H_res");
+  if (v.finish() != MHC_OK) return v.status();
+  mhc::launch_sinkhorn_fwd((hipStream_t)stream, count, logits, H_res, iters, eps);
+  return launched("mhc_sinkhorn_fwd");
+}
+
+mhc_status mhc_sinkhorn_bwd(void *stream, int64_t count, int32_t n, const float *dH_res,
+                            const float *logits, float *dlogits, int32_t iters, float eps) {
+  Validator v("mhc_sinkhorn_bwd");
+  if (count < 0) v.fail(MHC_ERR_SHAPE, "count must be >= 0");
+  if (n <= 0) v.fail(MHC_ERR_SHAPE, "n must be > 0");
+  else if (n != 4) v.fail(MHC_ERR_UNSUPPORTED, "only n == 4 is supported");
+  v.iters(iters);
+  v.eps(eps, "eps");
+  if (!v.ok()) return v.status();
+  if (count == 0) return MHC_OK;
+  v.in(dH_res, count * 64, "dH_res");
+  v.in(logits, count * 64, "logits");
+  v.out(dlogits, count * 64, "dlogits");
+  if (v.finish() != MHC_OK) return v.status();
+  mhc::launch_sinkhorn_bwd((hipStream_t)stream, count, dH_res, logits, dlogits, iters, eps);
+  return launched("mhc_sinkhorn_bwd");
+}
+
+// ------------------------------------------------------------------ h_aggregate
+mhc_status mhc_h_aggregate_fwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                               const void *X, const float *H_pre, void *out) {
+  Validator v("mhc_h_aggregate_fwd");
+  v.dims(tokens, n, C, act);
+  if (!v.ok()) return v.status();
+  if (tokens == 0) return MHC_OK;
+  v.in(X, tokens * 4 * C * esz(act), "X");
+  v.in(H_pre, tokens * 16, "H_pre");
+  v.out(out, tokens * C * esz(act), "out");
+  if (v.finish() != MHC_OK) return v.status();
+  mhc::launch_h_aggregate_fwd((hipStream_t)stream, act == MHC_F32, tokens, C, X, H_pre, out);
+  return launched("mhc_h_aggregate_fwd");
+}
+
+mhc_status mhc_h_aggregate_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                               const void *g, const void *X, const float *H_pre, void *dX,
+                               int32_t accumulate_dX, float *dH_pre) {
+  Validator v("mhc_h_aggregate_bwd");
+  v.dims(tokens, n, C, act);
+  if (!v.ok()) return v.status();
+  if (tokens == 0) return MHC_OK;
+  v.in(g, tokens * C * esz(act), "g");
+  v.in(X, tokens * 4 * C * esz(act), "X");
+  v.in(H_pre, tokens * 16, "H_pre");
+  v.out(dX, tokens * 4 * C * esz(act), "dX");
+  v.out(dH_pre, tokens * 16, "dH_pre");
+  if (v.finish() != MHC_OK) return v.status();
+  mhc::launch_h_aggregate_bwd((hipStream_t)stream, act == MHC_F32, tokens, C, g, X, H_pre, dX,
+                              accumulate_dX != 0, dH_pre);
+  return launched("mhc_h_aggregate_bwd");
+}
+
+// ------------------------------------------------------------------ h_post_bda
+mhc_status mhc_h_post_bda_fwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                              const void *X, const float *H_res, const float *H_post, const void *x,
+                              const void *bias, void *out) {
+  Validator v("mhc_h_post_bda_fwd");
+  v.dims(tokens, n, C, act);
+  if (!v.ok()) return v.status();
+  if (tokens == 0) return MHC_OK;
+  v.in(X, tokens * 4 * C * esz(act), "X");
+  v.in(H_res, tokens * 64, "H_res");
+  v.in(H_post, tokens * 16, "H_post");
+  v.in(x, tokens * C * esz(act), "x");
+  v.in(bias, C * esz(act), "bias", true);
+  v.out(out, tokens * 4 * C * esz(act), "out");
+  if (v.finish() != MHC_OK) return v.status();
+  mhc::launch_h_post_bda_fwd((hipStream_t)stream, act == MHC_F32, tokens, C, X, H_res, H_post, x, bias, out);
+  return launched("mhc_h_post_bda_fwd");
+}
+
+size_t mhc_h_post_bda_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                                         int32_t with_dbias) {
+  (void)act;
+  if (tokens <= 0 || n != 4 || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
+  return mhc::h_post_bda_bwd_ws(tokens, C, with_dbias != 0);
+}
+
+mhc_status mhc_h_post_bda_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                              const void *G, const void *X, const float *H_res,
+                              const float *H_post, const void *x, const void *bias, void *dX,
+                              float *dH_res, float *dH_post, void *dx, void *dbias,
+                              void *workspace, size_t workspace_bytes) {
+  Validator v("mhc_h_post_bda_bwd");
+  v.dims(tokens, n, C, act);
+  if (dbias && !bias) v.fail(MHC_ERR_ARG, "dbias requested without bias");
+  if (!v.ok()) return v.status();
+  const hipStream_t s = (hipStream_t)stream;
+  if (tokens == 0) {
+    v.out(dbias, C * esz(act), "dbias", true);
+    if (v.finish() != MHC_OK) return v.status();
+    return zero_act(s, dbias, C, act) ? launched("mhc_h_post_bda_bwd") : MHC_OK;
+  }
+  v.in(G, tokens * 4 * C * esz(act), "G");
+  v.in(X, tokens * 4 * C * esz(act), "X");
+  v.in(H_res, tokens * 64, "H_res");
+  v.in(H_post, tokens * 16, "H_post");
+  v.in(x, tokens * C * esz(act), "x");
+  v.in(bias, C * esz(act), "bias", true);
+  v.out(dX, tokens * 4 * C * esz(act), "dX");
+  v.out(dH_res, tokens * 64, "dH_res");
+  v.out(dH_post, tokens * 16, "dH_post");
+  v.out(dx, tokens * C * esz(act), "dx");
+  v.out(dbias, C * esz(act), "dbias", true);
+  v.workspace(workspace, workspace_bytes, mhc::h_post_bda_bwd_ws(tokens, C, dbias != nullptr));
+  if (v.finish() != MHC_OK) return v.status();
+  mhc::launch_h_post_bda_bwd(s, act == MHC_F32, tokens, C, G, X, H_res, H_post, x, bias, dX, dH_res,
+                             dH_post, dx, dbias, workspace);
+  return launched("mhc_h_post_bda_bwd");
+}
+
+// ------------------------------------------------------------------ fused pre pass
+size_t mhc_pre_fwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
+  return mhc_proj_rms_h_workspace_size(tokens, n, C, act);
+}
+
+mhc_status mhc_pre_fwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                       const void *X, const float *W, const float *alpha, const float *hbias,
+                       float rms_eps, int32_t iters, float eps, float *H_pre, float *H_post,
+                       float *H_res, float *H_res_logits, float *saved, void *agg,
+                       void *workspace, size_t workspace_bytes) {
+  Validator v("mhc_pre_fwd");
+  v.dims(tokens, n, C, act);
+  v.eps(rms_eps, "rms_eps");
+  v.eps(eps, "eps");
+  v.iters(iters);
+  if (!v.ok()) return v.status();
+  if (tokens == 0) return MHC_OK;
+  const int64_t K = 4 * C;
+  v.in(X, tokens * K * esz(act), "X");
+  v.in(W, K * J * 4, "W");
+  v.in(alpha, 12, "alpha", true);
+  v.in(hbias, J * 4, "hbias", true);
+  v.out(H_pre, tokens * 16, "H_pre");
+  v.out(H_post, tokens * 16, "H_post");
+  v.out(H_res, tokens * 64, "H_res");
+  v.out(H_res_logits, tokens * 64, "H_res_logits");
+  v.out(saved, tokens * MHC_SAVED_STRIDE * 4, "saved", true);
+  v.out(agg, tokens * C * esz(act), "agg");
+  v.workspace(workspace, workspace_bytes, mhc::proj_fwd_ws(tokens, C, act == MHC_F32));
+  if (v.finish() != MHC_OK) return v.status();
+  const hipStream_t s = (hipStream_t)stream;
+  mhc::launch_proj_fwd(s, act == MHC_F32, tokens, C, X, W, alpha, hbias, rms_eps, H_pre, H_post,
+                       H_res_logits, saved, H_res, iters, eps, workspace);
+  mhc::launch_h_aggregate_fwd(s, act == MHC_F32, tokens, C, X, H_pre, agg);
+  return launched("mhc_pre_fwd");
+}
+
+size_t mhc_pre_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
+  return mhc_proj_rms_h_bwd_workspace_size(tokens, n, C, act);
+}
+
+mhc_status mhc_pre_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                       const void *g, const float *dH_post, const float *dH_res, const void *X,
+                       const float *W, const float *alpha, const float *saved, const float *H_pre,
+                       const float *H_post, const float *H_res_logits, int32_t iters, float eps,
+                       void *dX, int32_t accumulate_dX, float *dW, float *dalpha, float *dhbias,
+                       float *dH_pre_out, float *dlogits_out, void *workspace,
+                       size_t workspace_bytes) {
+  Validator v("mhc_pre_bwd");
+  v.dims(tokens, n, C, act);
+  v.eps(eps, "eps");
+  v.iters(iters);
+  if (!v.ok()) return v.status();
+  const int64_t K = 4 * C;
+  const hipStream_t s = (hipStream_t)stream;
+  if (tokens == 0) {
+    v.out(dW, K * J * 4, "dW", true);
+    v.out(dalpha, 12, "dalpha", true);
+    v.out(dhbias, J * 4, "dhbias", true);
+    if (v.finish() != MHC_OK) return v.status();
+    const bool any = zero_f32(s, dW, K * J) | zero_f32(s, dalpha, 3) | zero_f32(s, dhbias, J);
+    return any ? launched("mhc_pre_bwd") : MHC_OK;
+  }
+  v.in(g, tokens * C * esz(act), "g");
+  v.in(dH_post, tokens * 16, "dH_post");
+  v.in(dH_res, tokens * 64, "dH_res");
+  v.in(X, tokens * K * esz(act), "X");
+  v.in(W, K * J * 4, "W");
+  v.in(alpha, 12, "alpha", true);
+  v.in(saved, tokens * MHC_SAVED_STRIDE * 4, "saved");
+  v.in(H_pre, tokens * 16, "H_pre");
+  v.in(H_post, tokens * 16, "H_post");
+  v.in(H_res_logits, tokens * 64, "H_res_logits");
+  v.out(dX, tokens * K * esz(act), "dX");
+  v.out(dW, K * J * 4, "dW", true);
+  v.out(dalpha, 12, "dalpha", true);
+  v.out(dhbias, J * 4, "dhbias", true);
+  v.out(dH_pre_out, tokens * 16, "dH_pre_out", true);
+  v.out(dlogits_out, tokens * 64, "dlogits_out", true);
+  v.workspace(workspace, workspace_bytes, mhc::proj_bwd_ws(tokens, C, act == MHC_F32));
+  if (v.finish() != MHC_OK) return v.status();
+  mhc::ProjBwdArgs a{};
+  a.f32 = act == MHC_F32; a.N = tokens; a.C = C; a.X = X; a.W = W; a.alpha = alpha; a.saved = saved;
+  a.H_pre = H_pre; a.H_post = H_post; a.dH_pre = nullptr; a.dH_post = dH_post; a.dL = nullptr;
+  a.dH_res = dH_res; a.logits = H_res_logits; a.iters = iters; a.eps = eps; a.g = g; a.dX = dX;
+  a.accumulate = accumulate_dX != 0; a.dW = dW; a.dalpha = dalpha; a.dhbias = dhbias;
+  a.dH_pre_out = dH_pre_out; a.dL_out = dlogits_out; a.ws = workspace;
+  mhc::launch_proj_bwd(s, a);
+  return launched("mhc_pre_bwd");
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// device.h -- shared gfx950 device helpers for libmhc kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mhc {
+
+typedef uint16_t bf16_t;  // bf16 storage: the upper half of an fp32 bit pattern
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> two bf16 (round to nearest even) packed low|high: v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const __bf16 ha = (__bf16)a;
+  const __bf16 hb = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+// ---------------------------------------------------------------- 8-wide activation I/O
+// Activations move in groups of 8 channels: one 128-bit access for bf16,
+// two for fp32.  Callers guarantee 16-byte alignment (C % 8 == 0 and
+// 16-byte aligned base pointers are checked on the host).
+template <typename T> struct Io8;
+
+template <> struct Io8<bf16_t> {
+  static __device__ __forceinline__ void load(const bf16_t *p, float v[8]) {
+    const uint4 w = *reinterpret_cast<const uint4 *>(p);
+    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+    v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+    v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+    v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+  }
+  static __device__ __forceinline__ void store(bf16_t *p, const float v[8]) {
+    uint4 w;
+    w.x = pack_bf16x2(v[0], v[1]);
+    w.y = pack_bf16x2(v[2], v[3]);
+    w.z = pack_bf16x2(v[4], v[5]);
+    w.w = pack_bf16x2(v[6], v[7]);
+    *reinterpret_cast<uint4 *>(p) = w;
+  }
+};
+
+template <> struct Io8<float> {
+  static __device__ __forceinline__ void load(const float *p, float v[8]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  static __device__ __forceinline__ void store(float *p, const float v[8]) {
+    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4 *>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+};
+
+// ---------------------------------------------------------------- wave64 reductions
+// DPP control words (GFX9 encoding).
+enum : int {
+  DPP_QUAD_1032 = 0xb1,  // quad_perm [1,0,3,2]
+  DPP_QUAD_2301 = 0x4e,  // quad_perm [2,3,0,1]
+  DPP_ROW_ROR4 = 0x124,
+  DPP_ROW_ROR8 = 0x128,
+  DPP_ROW_BCAST15 = 0x142,
+  DPP_ROW_BCAST31 = 0x143,
+};
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+
+// Sum over the 64 lanes of a wave; the total is returned to every lane.
+// Fixed association order, so the result is deterministic.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp<DPP_QUAD_1032>(v);
+  v += dpp<DPP_QUAD_2301>(v);
+  v += dpp<DPP_ROW_ROR4>(v);
+  v += dpp<DPP_ROW_ROR8>(v);           // every lane holds its 16-lane row sum
+  v += dpp<DPP_ROW_BCAST15, 0xa>(v);   // rows 1, 3 += rows 0, 2
+  v += dpp<DPP_ROW_BCAST31, 0xc>(v);   // rows 2, 3 += row 1 (now rows 0+1)
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+}  // namespace mhc

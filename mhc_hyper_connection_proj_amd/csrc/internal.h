@@ -1,0 +1,77 @@
+// internal.h -- launchers shared between the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mhc {
+
+constexpr int kN = 4;            // residual streams supported on the GPU
+constexpr int kJ = kN * kN + 2 * kN;  // 24 controller outputs
+constexpr int kSavedStride = 32;
+
+// ---- launch geometry for per-token streaming kernels
+struct StreamGeom {
+  int tpb;  // threads per block (64, 128 or 256)
+  int gpt;  // 8-channel groups per thread (1, 2, 4 or 8): C <= 16384
+};
+constexpr int64_t kMaxC = 16384;
+StreamGeom stream_geom(int64_t C);
+
+// ---- Sinkhorn
+void launch_sinkhorn_fwd(hipStream_t s, int64_t count, const float *L, float *H, int iters, float eps);
+void launch_sinkhorn_bwd(hipStream_t s, int64_t count, const float *dH, const float *L, float *dL,
+                         int iters, float eps);
+
+// ---- streaming ops; `f32` selects fp32 activations, else bf16
+void launch_h_aggregate_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *X,
+                            const float *H_pre, void *out);
+// dX may be NULL (only dH_pre is produced).
+void launch_h_aggregate_bwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *g,
+                            const void *X, const float *H_pre, void *dX, bool accumulate,
+                            float *dH_pre);
+void launch_h_post_bda_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *X,
+                           const float *H_res, const float *H_post, const void *x,
+                           const void *bias, void *out);
+size_t h_post_bda_bwd_ws(int64_t N, int64_t C, bool with_dbias);
+void launch_h_post_bda_bwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *G,
+                           const void *X, const float *H_res, const float *H_post, const void *x,
+                           const void *bias, void *dX, float *dH_res, float *dH_post, void *dx,
+                           void *dbias, void *ws);
+
+// ---- projection (forward)
+size_t proj_fwd_ws(int64_t N, int64_t C, bool f32);
+// Writes H_pre, H_post, logits, saved (may be NULL); if H_res != NULL also
+// runs Sinkhorn on the logits.
+void launch_proj_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *X, const float *W,
+                     const float *alpha, const float *hbias, float rms_eps, float *H_pre,
+                     float *H_post, float *logits, float *saved, float *H_res, int iters,
+                     float eps, void *ws);
+
+// ---- projection (backward).  Two front ends share the dX / dW kernels:
+//  - proj_rms_h_bwd: dL given directly (dH_res_logits)
+//  - pre_bwd: dH_pre from g.X, dL from the Sinkhorn backward of dH_res, and
+//    the aggregate term H_pre * g added into dX.
+size_t proj_bwd_ws(int64_t N, int64_t C, bool f32);
+struct ProjBwdArgs {
+  bool f32;
+  int64_t N, C;
+  const void *X;
+  const float *W, *alpha, *saved, *H_pre, *H_post;
+  const float *dH_pre;   // NULL in the fused pre backward (computed from g)
+  const float *dH_post;
+  const float *dL;       // logits gradient, or NULL when dH_res + logits are given
+  const float *dH_res, *logits;
+  int iters;
+  float eps;
+  const void *g;         // gradient of the aggregated stream (fused pre backward) or NULL
+  void *dX;
+  bool accumulate;
+  float *dW, *dalpha, *dhbias;
+  float *dH_pre_out, *dL_out;
+  void *ws;
+};
+void launch_proj_bwd(hipStream_t s, const ProjBwdArgs &a);
+
+}  // namespace mhc

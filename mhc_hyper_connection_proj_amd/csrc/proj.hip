@@ -1,0 +1,601 @@
+// proj.hip -- projection + RMS + compute_h (forward and backward).
+//
+// Forward (Megatron Core fused_mhc_kernels, proj_rms_compute_h; RL-Kernel
+// PR #383 for r = 1/(q + eps) and the three segment gains), per token:
+//   q = sqrt(sum x^2 / K), r = 1/(q + rms_eps), p = x @ W, z = r p,
+//   zh = alpha[seg] z + hbias, H_pre = sigmoid, H_post = 2 sigmoid, logits = zh_RES.
+//
+// The contraction x @ W ([K] x [K, 24] per token, K = 4C up to 64K) is the
+// only dense work on the path.  It runs on MFMA:
+//  * W (fp32) is split exactly into three bf16 terms hi + mid + lo (8 + 8 + 8
+//    significant bits cover fp32's 24), and bf16 x times each term is exact in
+//    the fp32 accumulator, so 3 bf16 MFMAs reproduce the fp32 product.  For
+//    fp32 activations the fp32 MFMA is used on W directly.
+//  * A 32x32x16 MFMA takes 32 tokens x 16 k from X and 16 k x 32 columns
+//    (24 used) from W.  The k order inside one MFMA is free as long as A and
+//    B agree, so lane (row, h) loads 32 consecutive k of its token (64 bytes)
+//    per 64-k chunk and feeds them to four MFMAs; W is packed so the matching
+//    B fragment is one 16-byte load.
+//  * Split-K: the k range is cut into kSplitK slices and workgroup b works on
+//    slice b % 8.  Workgroups are dispatched round-robin over the 8 XCDs, so
+//    each XCD streams one slice and its L2 only holds that slice of W.
+//  * Accuracy: each 64-k chunk accumulates in a fresh MFMA accumulator and is
+//    then added into an fp32 running sum (two-level blocking), the 4 waves of a
+//    workgroup and the 8 slices are summed in a fixed order; sum x^2 uses
+//    v_dot2_f32_bf16 with the same blocking.
+#include "device.h"
+#include "internal.h"
+#include "sinkhorn.h"
+
+namespace mhc {
+
+constexpr int kSplitK = 8;   // one k slice per XCD
+constexpr int kTPW = 2;      // 32-token MFMA tiles per wave
+constexpr int kTB = 32 * kTPW;  // tokens per workgroup
+constexpr int kPartStride = 32;  // partial record: p[24], sumsq, pad
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+static inline int64_t kpad64(int64_t K) { return (K + 63) / 64 * 64; }
+
+static inline size_t wpack_bytes(int64_t C, bool f32) {
+  const int64_t Kp = kpad64(4 * C);
+  return (size_t)(f32 ? Kp * kJ * 4 : Kp * kJ * 3 * 2);
+}
+
+static inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+size_t proj_fwd_ws(int64_t N, int64_t C, bool f32) {
+  return align256(wpack_bytes(C, f32)) + align256((size_t)kSplitK * N * kPartStride * 4);
+}
+
+// ------------------------------------------------------------------ W pack
+// bf16: Wp[kg][term][j][8] (kg = k/8), term 0,1,2 = hi, mid, lo.
+// fp32: Wf[kg][j][8].  Rows k >= K (padding to a multiple of 64) are zero.
+__device__ __forceinline__ float bf16_round(float v) {
+  const __bf16 h = (__bf16)v;
+  return (float)h;
+}
+
+template <bool F32>
+__global__ __launch_bounds__(256) void pack_w_kernel(const float *__restrict__ W, void *__restrict__ out,
+                                                     int64_t K, int64_t Kp) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over Kp * 24
+  if (idx >= Kp * kJ) return;
+  const int64_t k = idx / kJ;
+  const int j = (int)(idx % kJ);
+  const float w = k < K ? W[k * kJ + j] : 0.f;
+  const int64_t kg = k >> 3;
+  const int e = (int)(k & 7);
+  if (F32) {
+    reinterpret_cast<float *>(out)[(kg * kJ + j) * 8 + e] = w;
+  } else {
+    const float hi = bf16_round(w);
+    const float r1 = w - hi;
+    const float mid = bf16_round(r1);
+    const float lo = bf16_round(r1 - mid);
+    bf16_t *o = reinterpret_cast<bf16_t *>(out);
+    o[((kg * 3 + 0) * kJ + j) * 8 + e] = __builtin_bit_cast(uint16_t, (__bf16)hi);
+    o[((kg * 3 + 1) * kJ + j) * 8 + e] = __builtin_bit_cast(uint16_t, (__bf16)mid);
+    o[((kg * 3 + 2) * kJ + j) * 8 + e] = __builtin_bit_cast(uint16_t, (__bf16)lo);
+  }
+}
+
+// ------------------------------------------------------------------ partial projection
+// Grid: ceil(N / kTB) * kSplitK workgroups of 256 threads; workgroup b handles
+// token block b / kSplitK and k slice b % kSplitK.  Wave w takes the slice's
+// 64-k chunks w, w+4, ...  Output: part[slice][t][0..24) = partial x @ W,
+// part[slice][t][24] = partial sum x^2.
+template <bool F32>
+__global__ __launch_bounds__(256) void proj_partial_kernel(const void *__restrict__ Xv,
+                                                           const void *__restrict__ Wpk,
+                                                           float *__restrict__ part, int64_t N,
+                                                           int64_t K) {
+  __shared__ float red_p[4][kTB][kJ + 1];
+  __shared__ float red_s[4][kTB][2];
+  const int slice = blockIdx.x % kSplitK;
+  const int64_t tb = blockIdx.x / kSplitK;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = lane & 31, h = lane >> 5;
+  const int64_t nch = (K + 63) / 64;
+  const int64_t cps = (nch + kSplitK - 1) / kSplitK;
+  const int64_t c_begin = slice * cps;
+  const int64_t c_end = min(nch, c_begin + cps);
+
+  f32x16 outer[kTPW];
+  float ss[kTPW];
+#pragma unroll
+  for (int u = 0; u < kTPW; ++u) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) outer[u][r] = 0.f;
+    ss[u] = 0.f;
+  }
+  int64_t trow[kTPW];
+  bool tvalid[kTPW];
+#pragma unroll
+  for (int u = 0; u < kTPW; ++u) {
+    trow[u] = tb * kTB + 32 * u + row;
+    tvalid[u] = trow[u] < N;
+  }
+  const bool bcol = row < kJ;  // B lanes with a real W column
+
+  for (int64_t c = c_begin + wave; c < c_end; c += 4) {
+    const int64_t k0 = c * 64;
+    const bool kvalid = (k0 + 32 * h) < K;
+    f32x16 acc[kTPW];
+#pragma unroll
+    for (int u = 0; u < kTPW; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[u][r] = 0.f;
+    if constexpr (!F32) {
+      const bf16_t *X = reinterpret_cast<const bf16_t *>(Xv);
+      const bf16_t *Wp = reinterpret_cast<const bf16_t *>(Wpk);
+      u32x4 a[kTPW][4];
+#pragma unroll
+      for (int u = 0; u < kTPW; ++u) {
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(X + trow[u] * K + k0 + 32 * h);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) a[u][m] = (tvalid[u] && kvalid) ? src[m] : u32x4{0u, 0u, 0u, 0u};
+      }
+      u32x4 b[4][3];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int64_t kg = k0 / 8 + 4 * h + m;
+#pragma unroll
+        for (int tm = 0; tm < 3; ++tm)
+          b[m][tm] = bcol ? *reinterpret_cast<const u32x4 *>(Wp + ((kg * 3 + tm) * kJ + row) * 8)
+                          : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int tm = 0; tm < 3; ++tm)
+#pragma unroll
+          for (int u = 0; u < kTPW; ++u)
+            acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, a[u][m]), __builtin_bit_cast(bf16x8, b[m][tm]), acc[u], 0, 0, 0);
+      // sum of squares of this lane's 32 elements of each token row.  The
+      // dwords are pulled out by name: bit-casting an indexed ext-vector
+      // element (a[u][m][q]) makes hipcc reuse dword 0 for every q.
+#pragma unroll
+      for (int u = 0; u < kTPW; ++u) {
+        float s = 0.f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const unsigned w4[4] = {a[u][m].x, a[u][m].y, a[u][m].z, a[u][m].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+            const bf16x2 v = __builtin_bit_cast(bf16x2, w4[q]);
+            s = __builtin_amdgcn_fdot2_f32_bf16(v, v, s, false);
+          }
+        }
+        ss[u] += s;
+      }
+    } else {
+      const float *X = reinterpret_cast<const float *>(Xv);
+      const float *Wf = reinterpret_cast<const float *>(Wpk);
+      float a[kTPW][32];
+#pragma unroll
+      for (int u = 0; u < kTPW; ++u) {
+        const float4 *src = reinterpret_cast<const float4 *>(X + trow[u] * K + k0 + 32 * h);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float4 v = (tvalid[u] && kvalid) ? src[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+          a[u][4 * q] = v.x; a[u][4 * q + 1] = v.y; a[u][4 * q + 2] = v.z; a[u][4 * q + 3] = v.w;
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int64_t kg = k0 / 8 + 4 * h + m;
+        float b[8];
+        const float4 *src = reinterpret_cast<const float4 *>(Wf + (kg * kJ + row) * 8);
+        const float4 b0 = bcol ? src[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 b1 = bcol ? src[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+        b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w;
+        b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+          for (int u = 0; u < kTPW; ++u)
+            acc[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u][8 * m + e], b[e], acc[u], 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kTPW; ++u) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) s = fmaf(a[u][e], a[u][e], s);
+        ss[u] += s;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kTPW; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) outer[u][r] += acc[u][r];
+  }
+
+  // accumulator layout of a 32x32 MFMA: lane (col, h), register r holds
+  // row 8*(r/4) + 4*h + (r%4), column col.
+#pragma unroll
+  for (int u = 0; u < kTPW; ++u) {
+    if (bcol) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red_p[wave][32 * u + 8 * (r >> 2) + 4 * h + (r & 3)][row] = outer[u][r];
+    }
+    red_s[wave][32 * u + row][h] = ss[u];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < kTB * (kJ + 1); idx += 256) {
+    const int tt = idx / (kJ + 1), j = idx % (kJ + 1);
+    const int64_t t = tb * kTB + tt;
+    if (t >= N) continue;
+    float v;
+    if (j < kJ)
+      v = (red_p[0][tt][j] + red_p[1][tt][j]) + (red_p[2][tt][j] + red_p[3][tt][j]);
+    else
+      v = ((red_s[0][tt][0] + red_s[0][tt][1]) + (red_s[1][tt][0] + red_s[1][tt][1])) +
+          ((red_s[2][tt][0] + red_s[2][tt][1]) + (red_s[3][tt][0] + red_s[3][tt][1]));
+    part[((int64_t)slice * N + t) * kPartStride + j] = v;
+  }
+}
+
+// ------------------------------------------------------------------ finalize
+// One thread per token: fixed-order sum of the kSplitK partials, RMS,
+// compute_h, and (when H_res != NULL) the Sinkhorn projection of the logits.
+__global__ __launch_bounds__(256) void proj_finalize_kernel(
+    const float *__restrict__ part, const float *__restrict__ alpha, const float *__restrict__ hbias,
+    float rms_eps, float *__restrict__ Hpre, float *__restrict__ Hpost, float *__restrict__ logits,
+    float *__restrict__ saved, float *__restrict__ Hres, int iters, float eps, int64_t N, int64_t K) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= N) return;
+  float p[kJ + 1];
+#pragma unroll
+  for (int j = 0; j < kJ + 1; ++j) {
+    float v[kSplitK];
+#pragma unroll
+    for (int s = 0; s < kSplitK; ++s) v[s] = part[((int64_t)s * N + t) * kPartStride + j];
+    p[j] = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+  }
+  const float q = sqrtf(p[kJ] / (float)K);
+  const float r = 1.0f / (q + rms_eps);
+  float z[kJ], zh[kJ];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    z[j] = r * p[j];
+    const int seg = j < 4 ? 0 : (j < 8 ? 1 : 2);
+    const float a = alpha ? alpha[seg] : 1.f;
+    const float b = hbias ? hbias[j] : 0.f;
+    zh[j] = a * z[j] + b;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    Hpre[t * 4 + i] = 1.0f / (1.0f + expf(-zh[i]));
+    Hpost[t * 4 + i] = 2.0f / (1.0f + expf(-zh[4 + i]));
+  }
+  store16(logits + t * 16, zh + 8);
+  if (saved) {
+    float sv[kSavedStride];
+    sv[0] = r;
+    sv[1] = q;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) sv[2 + j] = z[j];
+#pragma unroll
+    for (int j = 2 + kJ; j < kSavedStride; ++j) sv[j] = 0.f;
+#pragma unroll
+    for (int qd = 0; qd < kSavedStride / 4; ++qd)
+      reinterpret_cast<float4 *>(saved + t * kSavedStride)[qd] =
+          make_float4(sv[4 * qd], sv[4 * qd + 1], sv[4 * qd + 2], sv[4 * qd + 3]);
+  }
+  if (Hres) {
+    float M[16];
+    sk_exp(zh + 8, M);
+    sk_forward(M, iters, eps);
+    store16(Hres + t * 16, M);
+  }
+}
+
+void launch_proj_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *X, const float *W,
+                     const float *alpha, const float *hbias, float rms_eps, float *H_pre,
+                     float *H_post, float *logits, float *saved, float *H_res, int iters, float eps,
+                     void *ws) {
+  const int64_t K = 4 * C;
+  const int64_t Kp = kpad64(K);
+  char *base = (char *)ws;
+  void *wpk = base;
+  float *part = (float *)(base + align256(wpack_bytes(C, f32)));
+  const unsigned pack_blocks = (unsigned)((Kp * kJ + 255) / 256);
+  const unsigned pblocks = (unsigned)(((N + kTB - 1) / kTB) * kSplitK);
+  if (f32) {
+    hipLaunchKernelGGL((pack_w_kernel<true>), dim3(pack_blocks), dim3(256), 0, s, W, wpk, K, Kp);
+    hipLaunchKernelGGL((proj_partial_kernel<true>), dim3(pblocks), dim3(256), 0, s, X, wpk, part, N, K);
+  } else {
+    hipLaunchKernelGGL((pack_w_kernel<false>), dim3(pack_blocks), dim3(256), 0, s, W, wpk, K, Kp);
+    hipLaunchKernelGGL((proj_partial_kernel<false>), dim3(pblocks), dim3(256), 0, s, X, wpk, part, N, K);
+  }
+  hipLaunchKernelGGL(proj_finalize_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, part,
+                     alpha, hbias, rms_eps, H_pre, H_post, logits, saved, H_res, iters, eps, N, K);
+}
+
+// ================================================================== backward
+// Per-token record written by proj_bwd_token_kernel (fp32, stride kRec):
+//   [0,24) dp = r * alpha * dzh     [24] c_rms = -dr r^2 / (K q) (0 if q == 0)
+//   [25,28) per-token d_alpha terms [32,56) dzh (per-token d_hbias terms)
+constexpr int kRec = 64;
+constexpr int kDxK = 4;               // consecutive k per thread in the dX/dW kernel
+constexpr int kDxKT = 256 * kDxK;     // k per workgroup
+
+static int64_t bwd_token_block(int64_t N, int64_t K) {
+  // aim for ~1024 workgroups; token blocks of at least 64
+  const int64_t nkt = (K + kDxKT - 1) / kDxKT;
+  int64_t tb = (N * nkt + 1023) / 1024;
+  tb = tb < 64 ? 64 : tb;
+  return (tb + 63) / 64 * 64;
+}
+
+size_t proj_bwd_ws(int64_t N, int64_t C, bool) {
+  const int64_t K = 4 * C;
+  const int64_t tb = bwd_token_block(N, K);
+  const int64_t ntb = (N + tb - 1) / tb;
+  return align256((size_t)N * kRec * 4) + align256((size_t)N * 4 * 4) +
+         align256((size_t)ntb * K * kJ * 4);
+}
+
+__global__ __launch_bounds__(256) void proj_bwd_token_kernel(
+    const float *__restrict__ alpha, const float *__restrict__ saved, const float *__restrict__ Hpre,
+    const float *__restrict__ Hpost, const float *__restrict__ dHpre, const float *__restrict__ dHpost,
+    const float *__restrict__ dL_in, const float *__restrict__ dHres, const float *__restrict__ logits,
+    int iters, float eps, float *__restrict__ rec, float *__restrict__ dL_out,
+    float *__restrict__ dHpre_out, int64_t N, int64_t K) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= N) return;
+  float dl[16];
+  if (dL_in) {
+    load16(dL_in + t * 16, dl);
+  } else {
+    float lg[16];
+    load16(logits + t * 16, lg);
+    load16(dHres + t * 16, dl);
+    sk_backward(lg, dl, iters, eps);
+  }
+  if (dL_out) store16(dL_out + t * 16, dl);
+  const float r = saved[t * kSavedStride + 0];
+  const float q = saved[t * kSavedStride + 1];
+  float z[kJ], dzh[kJ];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) z[j] = saved[t * kSavedStride + 2 + j];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float hp = Hpre[t * 4 + i];
+    const float dhp = dHpre[t * 4 + i];
+    if (dHpre_out) dHpre_out[t * 4 + i] = dhp;
+    dzh[i] = dhp * (hp * (1.f - hp));
+    const float hq = Hpost[t * 4 + i];
+    dzh[4 + i] = dHpost[t * 4 + i] * (hq * (1.f - 0.5f * hq));
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) dzh[8 + e] = dl[e];
+  float a3[3] = {1.f, 1.f, 1.f};
+  if (alpha) { a3[0] = alpha[0]; a3[1] = alpha[1]; a3[2] = alpha[2]; }
+  float da[3] = {0.f, 0.f, 0.f};
+  float S = 0.f;
+  float out[kRec];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const int seg = j < 4 ? 0 : (j < 8 ? 1 : 2);
+    da[seg] += dzh[j] * z[j];
+    const float dz = a3[seg] * dzh[j];
+    S += dz * z[j];
+    out[j] = r * dz;
+    out[32 + j] = dzh[j];
+  }
+  // dr = sum_j dz_j p_j with p_j = z_j / r, and r (q + rms_eps) = 1, so the
+  // RMS coefficient -dr r^2 / (K q) equals -S r / (K q) with S = sum_j dz_j z_j.
+  out[24] = q > 0.f ? -S * r / ((float)K * q) : 0.f;
+  out[25] = da[0]; out[26] = da[1]; out[27] = da[2];
+  out[28] = out[29] = out[30] = out[31] = 0.f;
+#pragma unroll
+  for (int j = 56; j < kRec; ++j) out[j] = 0.f;
+#pragma unroll
+  for (int qd = 0; qd < kRec / 4; ++qd)
+    reinterpret_cast<float4 *>(rec + t * kRec)[qd] =
+        make_float4(out[4 * qd], out[4 * qd + 1], out[4 * qd + 2], out[4 * qd + 3]);
+}
+
+// dX[t][k] = (acc ? dX[t][k] : 0) + H_pre[t][i] g[t][c] + c_rms[t] x[t][k] + sum_j dp[t][j] W[k][j]
+// dW partial[tb][k][j] = sum_{t in tb} x[t][k] dp[t][j]
+template <typename T, bool ACCUM, bool HAS_G, bool DW>
+__global__ __launch_bounds__(256) void proj_bwd_dx_kernel(
+    const T *__restrict__ X, const float *__restrict__ W, const float *__restrict__ rec,
+    const float *__restrict__ Hpre, const T *__restrict__ gr, T *__restrict__ dX,
+    float *__restrict__ dWpart, int64_t N, int64_t C, int64_t tbsz) {
+  const int64_t K = 4 * C;
+  const int64_t nkt = (K + kDxKT - 1) / kDxKT;
+  const int64_t kt = blockIdx.x % nkt;
+  const int64_t tb = blockIdx.x / nkt;
+  const int64_t k = kt * kDxKT + kDxK * threadIdx.x;
+  const bool kv = k < K;
+  const int si = (int)(k / C);
+  const int64_t c = k - si * C;
+  float w[kDxK][kJ];
+  float dw[kDxK][kJ];
+#pragma unroll
+  for (int e = 0; e < kDxK; ++e)
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      w[e][j] = kv ? W[(k + e) * kJ + j] : 0.f;
+      dw[e][j] = 0.f;
+    }
+  const int64_t t_end = min(N, (tb + 1) * tbsz);
+  for (int64_t t = tb * tbsz; t < t_end; ++t) {
+    const float *rt = rec + t * kRec;
+    float dp[kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) dp[j] = rt[j];
+    const float crms = rt[24];
+    if (kv) {
+      float xv[kDxK], o[kDxK];
+      if constexpr (sizeof(T) == 2) {
+        const uint2 w2 = *reinterpret_cast<const uint2 *>(X + t * K + k);
+        xv[0] = bf16_lo(w2.x); xv[1] = bf16_hi(w2.x); xv[2] = bf16_lo(w2.y); xv[3] = bf16_hi(w2.y);
+        if (ACCUM) {
+          const uint2 d2 = *reinterpret_cast<const uint2 *>(dX + t * K + k);
+          o[0] = bf16_lo(d2.x); o[1] = bf16_hi(d2.x); o[2] = bf16_lo(d2.y); o[3] = bf16_hi(d2.y);
+        }
+        if (HAS_G) {
+          const float hpi = Hpre[t * 4 + si];
+          const uint2 g2 = *reinterpret_cast<const uint2 *>(gr + t * C + c);
+          const float gv[4] = {bf16_lo(g2.x), bf16_hi(g2.x), bf16_lo(g2.y), bf16_hi(g2.y)};
+#pragma unroll
+          for (int e = 0; e < kDxK; ++e) o[e] = ACCUM ? o[e] + hpi * gv[e] : hpi * gv[e];
+        } else if (!ACCUM) {
+#pragma unroll
+          for (int e = 0; e < kDxK; ++e) o[e] = 0.f;
+        }
+      } else {
+        const float4 x4 = *reinterpret_cast<const float4 *>(X + t * K + k);
+        xv[0] = x4.x; xv[1] = x4.y; xv[2] = x4.z; xv[3] = x4.w;
+        if (ACCUM) {
+          const float4 d4 = *reinterpret_cast<const float4 *>(dX + t * K + k);
+          o[0] = d4.x; o[1] = d4.y; o[2] = d4.z; o[3] = d4.w;
+        }
+        if (HAS_G) {
+          const float hpi = Hpre[t * 4 + si];
+          const float4 g4 = *reinterpret_cast<const float4 *>(gr + t * C + c);
+          const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+          for (int e = 0; e < kDxK; ++e) o[e] = ACCUM ? o[e] + hpi * gv[e] : hpi * gv[e];
+        } else if (!ACCUM) {
+#pragma unroll
+          for (int e = 0; e < kDxK; ++e) o[e] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < kDxK; ++e) {
+        float acc = crms * xv[e];
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) acc = fmaf(dp[j], w[e][j], acc);
+        o[e] += acc;
+      }
+      if (DW) {
+#pragma unroll
+        for (int e = 0; e < kDxK; ++e)
+#pragma unroll
+          for (int j = 0; j < kJ; ++j) dw[e][j] = fmaf(xv[e], dp[j], dw[e][j]);
+      }
+      if constexpr (sizeof(T) == 2) {
+        uint2 o2;
+        o2.x = pack_bf16x2(o[0], o[1]);
+        o2.y = pack_bf16x2(o[2], o[3]);
+        *reinterpret_cast<uint2 *>(dX + t * K + k) = o2;
+      } else {
+        *reinterpret_cast<float4 *>(dX + t * K + k) = make_float4(o[0], o[1], o[2], o[3]);
+      }
+    }
+  }
+  if (DW && kv) {
+    float *dst = dWpart + (tb * K + k) * kJ;
+#pragma unroll
+    for (int e = 0; e < kDxK; ++e)
+#pragma unroll
+      for (int jq = 0; jq < kJ / 4; ++jq)
+        reinterpret_cast<float4 *>(dst + e * kJ)[jq] =
+            make_float4(dw[e][4 * jq], dw[e][4 * jq + 1], dw[e][4 * jq + 2], dw[e][4 * jq + 3]);
+  }
+}
+
+// dW[k][j] = sum over token blocks of the partials, in block order.
+__global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict__ part,
+                                                        float *__restrict__ dW, int64_t ntb,
+                                                        int64_t KJ) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= KJ) return;
+  float s = 0.f;
+  for (int64_t b = 0; b < ntb; ++b) s += part[b * KJ + idx];
+  dW[idx] = s;
+}
+
+// d_alpha[3] and d_hbias[24]: one workgroup; thread i sums tokens i, i+256, ...
+// in order, then a fixed pairwise tree over the 256 threads.
+__global__ __launch_bounds__(256) void param_reduce_kernel(const float *__restrict__ rec,
+                                                           float *__restrict__ dalpha,
+                                                           float *__restrict__ dhbias, int64_t N) {
+  __shared__ float red[256][28];
+  float acc[27];
+#pragma unroll
+  for (int e = 0; e < 27; ++e) acc[e] = 0.f;
+  for (int64_t t = threadIdx.x; t < N; t += 256) {
+    const float *rt = rec + t * kRec;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) acc[j] += rt[32 + j];
+#pragma unroll
+    for (int s = 0; s < 3; ++s) acc[kJ + s] += rt[25 + s];
+  }
+#pragma unroll
+  for (int e = 0; e < 27; ++e) red[threadIdx.x][e] = acc[e];
+  __syncthreads();
+  for (int stride = 128; stride > 0; stride >>= 1) {
+    if (threadIdx.x < stride)
+      for (int e = 0; e < 27; ++e) red[threadIdx.x][e] += red[threadIdx.x + stride][e];
+    __syncthreads();
+  }
+  if (threadIdx.x < kJ && dhbias) dhbias[threadIdx.x] = red[0][threadIdx.x];
+  if (threadIdx.x < 3 && dalpha) dalpha[threadIdx.x] = red[0][kJ + threadIdx.x];
+}
+
+template <typename T, bool ACCUM, bool HAS_G>
+static void launch_dx(hipStream_t s, const ProjBwdArgs &a, const float *rec, float *dwp, int64_t tbsz,
+                      int64_t ntb) {
+  const int64_t K = 4 * a.C;
+  const int64_t nkt = (K + kDxKT - 1) / kDxKT;
+  const unsigned blocks = (unsigned)(nkt * ntb);
+  if (a.dW)
+    hipLaunchKernelGGL((proj_bwd_dx_kernel<T, ACCUM, HAS_G, true>), dim3(blocks), dim3(256), 0, s,
+                       (const T *)a.X, a.W, rec, a.H_pre, (const T *)a.g, (T *)a.dX, dwp, a.N, a.C, tbsz);
+  else
+    hipLaunchKernelGGL((proj_bwd_dx_kernel<T, ACCUM, HAS_G, false>), dim3(blocks), dim3(256), 0, s,
+                       (const T *)a.X, a.W, rec, a.H_pre, (const T *)a.g, (T *)a.dX, dwp, a.N, a.C, tbsz);
+}
+
+template <typename T>
+static void launch_dx_any(hipStream_t s, const ProjBwdArgs &a, const float *rec, float *dwp,
+                          int64_t tbsz, int64_t ntb) {
+  const bool hg = a.g != nullptr;
+  if (a.accumulate) {
+    if (hg) launch_dx<T, true, true>(s, a, rec, dwp, tbsz, ntb);
+    else launch_dx<T, true, false>(s, a, rec, dwp, tbsz, ntb);
+  } else {
+    if (hg) launch_dx<T, false, true>(s, a, rec, dwp, tbsz, ntb);
+    else launch_dx<T, false, false>(s, a, rec, dwp, tbsz, ntb);
+  }
+}
+
+void launch_proj_bwd(hipStream_t s, const ProjBwdArgs &a) {
+  const int64_t N = a.N, K = 4 * a.C;
+  const int64_t tbsz = bwd_token_block(N, K);
+  const int64_t ntb = (N + tbsz - 1) / tbsz;
+  char *base = (char *)a.ws;
+  float *rec = (float *)base;
+  float *dhpre_ws = (float *)(base + align256((size_t)N * kRec * 4));
+  float *dwp = (float *)(base + align256((size_t)N * kRec * 4) + align256((size_t)N * 16));
+  const float *dHpre = a.dH_pre;
+  if (a.g) {  // fused pre backward: dH_pre = g . X per stream
+    launch_h_aggregate_bwd(s, a.f32, N, a.C, a.g, a.X, a.H_pre, nullptr, false, dhpre_ws);
+    dHpre = dhpre_ws;
+  }
+  hipLaunchKernelGGL(proj_bwd_token_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s,
+                     a.alpha, a.saved, a.H_pre, a.H_post, dHpre, a.dH_post, a.dL, a.dH_res, a.logits,
+                     a.iters, a.eps, rec, a.dL_out, a.dH_pre_out, N, K);
+  if (a.f32)
+    launch_dx_any<float>(s, a, rec, dwp, tbsz, ntb);
+  else
+    launch_dx_any<bf16_t>(s, a, rec, dwp, tbsz, ntb);
+  if (a.dW)
+    hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((K * kJ + 255) / 256)), dim3(256), 0, s, dwp,
+                       a.dW, ntb, K * kJ);
+  if (a.dalpha || a.dhbias)
+    hipLaunchKernelGGL(param_reduce_kernel, dim3(1), dim3(256), 0, s, rec, a.dalpha, a.dhbias, N);
+}
+
+}  // namespace mhc

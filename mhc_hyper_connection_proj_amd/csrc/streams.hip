@@ -1,0 +1,438 @@
+// streams.hip -- HBM-streaming kernels: h_aggregate and h_post_bda, fwd + bwd.
+//
+// Layout: X/G/dX [tokens][4][C], x/agg/dx [tokens][C], bias [C] (activation
+// type), H_pre/H_post [tokens][4], H_res [tokens][4][4] (fp32).
+//
+// Each workgroup owns whole tokens.  A thread owns 8-channel groups
+// g = tid + j*TPB (j < GPT) and touches every stream of those channels, so
+// each tensor element is read exactly once with a 128-bit (bf16) access and
+// the 4x4 mix stays in registers.  The per-token H values are wave-uniform
+// (scalar loads).  Per-token reductions over C go lane -> wave (DPP) ->
+// workgroup (LDS, fixed wave order); cross-token sums (dbias) go through
+// per-workgroup partials reduced in a fixed order by a second kernel.
+#include "device.h"
+#include "internal.h"
+
+namespace mhc {
+
+StreamGeom stream_geom(int64_t C) {
+  const int64_t G = C / 8;
+  if (G <= 64) return {64, 1};
+  if (G <= 128) return {128, 1};
+  const int64_t per = (G + 255) / 256;
+  return {256, per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8};
+}
+
+// ============================================================ h_aggregate fwd
+template <typename T, int GPT>
+__global__ __launch_bounds__(256) void h_aggregate_fwd_kernel(const T *__restrict__ X,
+                                                               const float *__restrict__ Hpre,
+                                                               T *__restrict__ out, int64_t C) {
+  const int64_t t = blockIdx.x;
+  const int G = (int)(C / 8);
+  const float h0 = Hpre[t * 4 + 0], h1 = Hpre[t * 4 + 1], h2 = Hpre[t * 4 + 2], h3 = Hpre[t * 4 + 3];
+  const T *xt = X + t * 4 * C;
+  float v[GPT][4][8];
+#pragma unroll
+  for (int j = 0; j < GPT; ++j) {
+    const int g = threadIdx.x + j * blockDim.x;
+    if (g < G) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Io8<T>::load(xt + i * C + 8 * g, v[j][i]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < GPT; ++j) {
+    const int g = threadIdx.x + j * blockDim.x;
+    if (g < G) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = h0 * v[j][0][e] + h1 * v[j][1][e] + h2 * v[j][2][e] + h3 * v[j][3][e];
+      Io8<T>::store(out + t * C + 8 * g, o);
+    }
+  }
+}
+
+// ============================================================ h_aggregate bwd
+// dH_pre[t][i] = sum_c g[t][c] X[t][i][c];  optionally dX (+)= H_pre[i] g.
+template <typename T, int GPT, bool WRITE_DX, bool ACCUM>
+__global__ __launch_bounds__(256) void h_aggregate_bwd_kernel(
+    const T *__restrict__ gr, const T *__restrict__ X, const float *__restrict__ Hpre,
+    T *__restrict__ dX, float *__restrict__ dHpre, int64_t C) {
+  __shared__ float red[4][4];
+  const int64_t t = blockIdx.x;
+  const int G = (int)(C / 8);
+  const T *xt = X + t * 4 * C;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float h[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) h[i] = Hpre[t * 4 + i];
+#pragma unroll
+  for (int j = 0; j < GPT; ++j) {
+    const int g = threadIdx.x + j * blockDim.x;
+    if (g < G) {
+      float gv[8], xv[4][8];
+      Io8<T>::load(gr + t * C + 8 * g, gv);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Io8<T>::load(xt + i * C + 8 * g, xv[i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += gv[e] * xv[i][e];
+        acc[i] += s;
+      }
+      if (WRITE_DX) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          T *p = dX + (t * 4 + i) * C + 8 * g;
+          float d[8];
+          if (ACCUM) {
+            Io8<T>::load(p, d);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d[e] += h[i] * gv[e];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d[e] = h[i] * gv[e];
+          }
+          Io8<T>::store(p, d);
+        }
+      }
+    }
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float s = wave_sum(acc[i]);
+    if (lane == 0) red[wave][i] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x < 4) {
+    const int nw = blockDim.x >> 6;
+    float s = 0.f;
+    for (int w = 0; w < nw; ++w) s += red[w][threadIdx.x];
+    dHpre[t * 4 + threadIdx.x] = s;
+  }
+}
+
+// ============================================================ h_post_bda fwd
+template <typename T, int GPT, bool HAS_BIAS>
+__global__ __launch_bounds__(256) void h_post_bda_fwd_kernel(
+    const T *__restrict__ X, const float *__restrict__ Hres, const float *__restrict__ Hpost,
+    const T *__restrict__ x, const T *__restrict__ bias, T *__restrict__ out, int64_t C) {
+  const int64_t t = blockIdx.x;
+  const int G = (int)(C / 8);
+  float hr[16], hp[4];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) hr[e] = Hres[t * 16 + e];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hp[i] = Hpost[t * 4 + i];
+  const T *xt = X + t * 4 * C;
+  T *ot = out + t * 4 * C;
+#pragma unroll
+  for (int j = 0; j < GPT; ++j) {
+    const int g = threadIdx.x + j * blockDim.x;
+    if (g < G) {
+      float xv[4][8], lv[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Io8<T>::load(xt + i * C + 8 * g, xv[i]);
+      Io8<T>::load(x + t * C + 8 * g, lv);
+      if (HAS_BIAS) {
+        float bv[8];
+        Io8<T>::load(bias + 8 * g, bv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lv[e] += bv[e];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          o[e] = (hr[0 * 4 + i] * xv[0][e] + hr[1 * 4 + i] * xv[1][e]) +
+                 (hr[2 * 4 + i] * xv[2][e] + hr[3 * 4 + i] * xv[3][e]) + hp[i] * lv[e];
+        Io8<T>::store(ot + i * C + 8 * g, o);
+      }
+    }
+  }
+}
+
+// ============================================================ h_post_bda bwd
+// Workgroup b owns tokens [b*TG, b*TG + TG).  Per token: dX, dx streamed out;
+// 16 dH_res + 4 dH_post dot products reduced to LDS; after the token loop
+// one barrier and the per-token sums are written.  With DBIAS, each thread
+// keeps the fp32 dx sums of its channels over the workgroup's tokens and
+// writes them as one partial row.
+constexpr int kPostTG = 16;
+
+template <typename T, int GPT, bool HAS_BIAS, bool DBIAS>
+__global__ __launch_bounds__(256) void h_post_bda_bwd_kernel(
+    const T *__restrict__ Gr, const T *__restrict__ X, const float *__restrict__ Hres,
+    const float *__restrict__ Hpost, const T *__restrict__ x, const T *__restrict__ bias,
+    T *__restrict__ dX, float *__restrict__ dHres, float *__restrict__ dHpost, T *__restrict__ dx,
+    float *__restrict__ dbias_part, int64_t N, int64_t C, int TG) {
+  extern __shared__ float red[];  // [nwaves][TG][20]
+  const int G = (int)(C / 8);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float dbp[GPT][8];
+  if (DBIAS) {
+#pragma unroll
+    for (int j = 0; j < GPT; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dbp[j][e] = 0.f;
+  }
+  const int64_t t0 = (int64_t)blockIdx.x * TG;
+  const int ntok = (int)min((int64_t)TG, N - t0);
+  for (int tt = 0; tt < ntok; ++tt) {
+    const int64_t t = t0 + tt;
+    float hr[16], hp[4];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) hr[e] = Hres[t * 16 + e];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hp[i] = Hpost[t * 4 + i];
+    float acc[20];
+#pragma unroll
+    for (int e = 0; e < 20; ++e) acc[e] = 0.f;
+    const T *gt = Gr + t * 4 * C;
+    const T *xt = X + t * 4 * C;
+#pragma unroll
+    for (int j = 0; j < GPT; ++j) {
+      const int g = threadIdx.x + j * blockDim.x;
+      if (g < G) {
+        float gv[4][8], xv[4][8], lv[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Io8<T>::load(gt + i * C + 8 * g, gv[i]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Io8<T>::load(xt + i * C + 8 * g, xv[i]);
+        Io8<T>::load(x + t * C + 8 * g, lv);
+        if (HAS_BIAS) {
+          float bv[8];
+          Io8<T>::load(bias + 8 * g, bv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) lv[e] += bv[e];
+        }
+        // dX[j] = sum_i H_res[j][i] G[i]
+#pragma unroll
+        for (int js = 0; js < 4; ++js) {
+          float o[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            o[e] = (hr[js * 4 + 0] * gv[0][e] + hr[js * 4 + 1] * gv[1][e]) +
+                   (hr[js * 4 + 2] * gv[2][e] + hr[js * 4 + 3] * gv[3][e]);
+          Io8<T>::store(dX + (t * 4 + js) * C + 8 * g, o);
+        }
+        // dx = sum_i H_post[i] G[i]
+        {
+          float o[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            o[e] = (hp[0] * gv[0][e] + hp[1] * gv[1][e]) + (hp[2] * gv[2][e] + hp[3] * gv[3][e]);
+          Io8<T>::store(dx + t * C + 8 * g, o);
+          if (DBIAS) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dbp[j][e] += o[e];
+          }
+        }
+        // dH_res[js][i] += X[js] . G[i];  dH_post[i] += G[i] . (x + bias)
+#pragma unroll
+        for (int js = 0; js < 4; ++js)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s += xv[js][e] * gv[i][e];
+            acc[js * 4 + i] += s;
+          }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float s = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s += gv[i][e] * lv[e];
+          acc[16 + i] += s;
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 20; ++e) {
+      const float s = wave_sum(acc[e]);
+      if (lane == 0) red[(wave * TG + tt) * 20 + e] = s;
+    }
+  }
+  __syncthreads();
+  const int nw = blockDim.x >> 6;
+  for (int k = threadIdx.x; k < ntok * 20; k += blockDim.x) {
+    const int tt = k / 20, e = k % 20;
+    float s = 0.f;
+    for (int w = 0; w < nw; ++w) s += red[(w * TG + tt) * 20 + e];
+    const int64_t t = t0 + tt;
+    if (e < 16)
+      dHres[t * 16 + e] = s;
+    else
+      dHpost[t * 4 + (e - 16)] = s;
+  }
+  if (DBIAS) {
+#pragma unroll
+    for (int j = 0; j < GPT; ++j) {
+      const int g = threadIdx.x + j * blockDim.x;
+      if (g < G) {
+        float *p = dbias_part + (int64_t)blockIdx.x * C + 8 * g;
+        *reinterpret_cast<float4 *>(p) = make_float4(dbp[j][0], dbp[j][1], dbp[j][2], dbp[j][3]);
+        *reinterpret_cast<float4 *>(p + 4) = make_float4(dbp[j][4], dbp[j][5], dbp[j][6], dbp[j][7]);
+      }
+    }
+  }
+}
+
+// dbias[c] = sum over partial rows, fixed order: 4 waves stride the rows,
+// then the 4 wave sums are added in wave order.  Block = 64 channels.
+template <typename T>
+__global__ __launch_bounds__(256) void dbias_reduce_kernel(const float *__restrict__ part,
+                                                           T *__restrict__ dbias, int64_t rows,
+                                                           int64_t C) {
+  __shared__ float red[4][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
+  float s = 0.f;
+  if (c < C)
+    for (int64_t r = wave; r < rows; r += 4) s += part[r * C + c];
+  red[wave][lane] = s;
+  __syncthreads();
+  if (wave == 0 && c < C) {
+    const float tot = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+    if constexpr (sizeof(T) == 2) {
+      const __bf16 h = (__bf16)tot;
+      dbias[c] = __builtin_bit_cast(uint16_t, h);
+    } else {
+      dbias[c] = tot;
+    }
+  }
+}
+
+// ============================================================ launchers
+#define MHC_GPT_DISPATCH(GPT_VAL, ...)                       \
+  switch (GPT_VAL) {                                         \
+    case 1: { constexpr int GPT = 1; __VA_ARGS__; } break;   \
+    case 2: { constexpr int GPT = 2; __VA_ARGS__; } break;   \
+    case 4: { constexpr int GPT = 4; __VA_ARGS__; } break;   \
+    default: { constexpr int GPT = 8; __VA_ARGS__; } break;  \
+  }
+
+template <typename T>
+static void agg_fwd(hipStream_t s, int64_t N, int64_t C, const void *X, const float *H, void *out) {
+  const StreamGeom g = stream_geom(C);
+  MHC_GPT_DISPATCH(g.gpt, hipLaunchKernelGGL((h_aggregate_fwd_kernel<T, GPT>), dim3((unsigned)N),
+                                              dim3(g.tpb), 0, s, (const T *)X, H, (T *)out, C));
+}
+
+void launch_h_aggregate_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *X,
+                            const float *H_pre, void *out) {
+  if (f32)
+    agg_fwd<float>(s, N, C, X, H_pre, out);
+  else
+    agg_fwd<bf16_t>(s, N, C, X, H_pre, out);
+}
+
+template <typename T, bool WRITE_DX, bool ACCUM>
+static void agg_bwd3(hipStream_t s, int64_t N, int64_t C, const void *g, const void *X,
+                     const float *H, void *dX, float *dH) {
+  const StreamGeom geo = stream_geom(C);
+  MHC_GPT_DISPATCH(geo.gpt,
+                   hipLaunchKernelGGL((h_aggregate_bwd_kernel<T, GPT, WRITE_DX, ACCUM>),
+                                      dim3((unsigned)N), dim3(geo.tpb), 0, s, (const T *)g,
+                                      (const T *)X, H, (T *)dX, dH, C));
+}
+
+template <typename T>
+static void agg_bwd(hipStream_t s, int64_t N, int64_t C, const void *g, const void *X,
+                    const float *H, void *dX, bool acc, float *dH) {
+  if (!dX)
+    agg_bwd3<T, false, false>(s, N, C, g, X, H, dX, dH);
+  else if (acc)
+    agg_bwd3<T, true, true>(s, N, C, g, X, H, dX, dH);
+  else
+    agg_bwd3<T, true, false>(s, N, C, g, X, H, dX, dH);
+}
+
+void launch_h_aggregate_bwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *g,
+                            const void *X, const float *H_pre, void *dX, bool accumulate,
+                            float *dH_pre) {
+  if (f32)
+    agg_bwd<float>(s, N, C, g, X, H_pre, dX, accumulate, dH_pre);
+  else
+    agg_bwd<bf16_t>(s, N, C, g, X, H_pre, dX, accumulate, dH_pre);
+}
+
+template <typename T>
+static void post_fwd(hipStream_t s, int64_t N, int64_t C, const void *X, const float *Hr,
+                     const float *Hp, const void *x, const void *b, void *out) {
+  const StreamGeom geo = stream_geom(C);
+  if (b) {
+    MHC_GPT_DISPATCH(geo.gpt, hipLaunchKernelGGL((h_post_bda_fwd_kernel<T, GPT, true>),
+                                                  dim3((unsigned)N), dim3(geo.tpb), 0, s,
+                                                  (const T *)X, Hr, Hp, (const T *)x,
+                                                  (const T *)b, (T *)out, C));
+  } else {
+    MHC_GPT_DISPATCH(geo.gpt, hipLaunchKernelGGL((h_post_bda_fwd_kernel<T, GPT, false>),
+                                                  dim3((unsigned)N), dim3(geo.tpb), 0, s,
+                                                  (const T *)X, Hr, Hp, (const T *)x,
+                                                  (const T *)nullptr, (T *)out, C));
+  }
+}
+
+void launch_h_post_bda_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *X,
+                           const float *H_res, const float *H_post, const void *x,
+                           const void *bias, void *out) {
+  if (f32)
+    post_fwd<float>(s, N, C, X, H_res, H_post, x, bias, out);
+  else
+    post_fwd<bf16_t>(s, N, C, X, H_res, H_post, x, bias, out);
+}
+
+size_t h_post_bda_bwd_ws(int64_t N, int64_t C, bool with_dbias) {
+  if (!with_dbias) return 0;
+  const int64_t rows = (N + kPostTG - 1) / kPostTG;
+  return (size_t)(rows * C) * sizeof(float);
+}
+
+template <typename T, bool HAS_BIAS, bool DBIAS>
+static void post_bwd3(hipStream_t s, int64_t N, int64_t C, const void *G, const void *X,
+                      const float *Hr, const float *Hp, const void *x, const void *b, void *dX,
+                      float *dHr, float *dHp, void *dx, float *part) {
+  const StreamGeom geo = stream_geom(C);
+  const int TG = DBIAS ? kPostTG : 1;
+  const unsigned blocks = (unsigned)((N + TG - 1) / TG);
+  const size_t lds = (size_t)(geo.tpb / 64) * TG * 20 * sizeof(float);
+  MHC_GPT_DISPATCH(geo.gpt,
+                   hipLaunchKernelGGL((h_post_bda_bwd_kernel<T, GPT, HAS_BIAS, DBIAS>),
+                                      dim3(blocks), dim3(geo.tpb), lds, s, (const T *)G,
+                                      (const T *)X, Hr, Hp, (const T *)x, (const T *)b, (T *)dX,
+                                      dHr, dHp, (T *)dx, part, N, C, TG));
+}
+
+template <typename T>
+static void post_bwd(hipStream_t s, int64_t N, int64_t C, const void *G, const void *X,
+                     const float *Hr, const float *Hp, const void *x, const void *b, void *dX,
+                     float *dHr, float *dHp, void *dx, void *db, void *ws) {
+  if (b && db) {
+    float *part = (float *)ws;
+    post_bwd3<T, true, true>(s, N, C, G, X, Hr, Hp, x, b, dX, dHr, dHp, dx, part);
+    const int64_t rows = (N + kPostTG - 1) / kPostTG;
+    hipLaunchKernelGGL((dbias_reduce_kernel<T>), dim3((unsigned)((C + 63) / 64)), dim3(256), 0, s,
+                       part, (T *)db, rows, C);
+  } else if (b) {
+    post_bwd3<T, true, false>(s, N, C, G, X, Hr, Hp, x, b, dX, dHr, dHp, dx, nullptr);
+  } else {
+    post_bwd3<T, false, false>(s, N, C, G, X, Hr, Hp, x, b, dX, dHr, dHp, dx, nullptr);
+  }
+}
+
+void launch_h_post_bda_bwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *G,
+                           const void *X, const float *H_res, const float *H_post, const void *x,
+                           const void *bias, void *dX, float *dH_res, float *dH_post, void *dx,
+                           void *dbias, void *ws) {
+  if (f32)
+    post_bwd<float>(s, N, C, G, X, H_res, H_post, x, bias, dX, dH_res, dH_post, dx, dbias, ws);
+  else
+    post_bwd<bf16_t>(s, N, C, G, X, H_res, H_post, x, bias, dX, dH_res, dH_post, dx, dbias, ws);
+}
+
+}  // namespace mhc

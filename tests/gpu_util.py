@@ -1,0 +1,75 @@
+"""Helpers for the GPU parity tests: host<->device transfer and tolerance rules.
+
+Tolerances (stated by the benchmark spec for this path, applied element by element):
+  * fp32 H tensors (H_pre, H_post, H_res, r): |g - o| <= 1e-5 |o|
+  * fp32 quantities that cross zero (logits, z, gradients, dW, ...):
+    |g - o| <= 1e-5 (|o| + rms(o)), i.e. 1e-5 relative to the tensor's scale
+  * bf16 tensors: |g - o| <= 8e-3 |o| + 1e-5 rms(o), o being the oracle's fp64
+    result rounded once to bf16 (8e-3 is one bf16 ulp; the small absolute
+    term absorbs fp32 accumulation on cancelling sums).
+"""
+import sys
+
+import numpy as np
+import torch
+
+import oracle as O
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a: np.ndarray, act: str | None = None) -> torch.Tensor:
+    """Host storage array -> CUDA tensor (uint16 bit patterns become bfloat16)."""
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def h64(a) -> np.ndarray:
+    """Storage array (bf16 bits or float) or tensor -> exact float64 numpy."""
+    if isinstance(a, torch.Tensor):
+        return a.detach().float().cpu().double().numpy()
+    if a.dtype == np.uint16:
+        return O.bf16_bits_to_f64(a)
+    return np.asarray(a, dtype=np.float64)
+
+
+def _report(name, g, o, bound):
+    err = np.abs(g - o)
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(
+            f"{name}: {bad.sum()} of {bad.size} elements out of tolerance; worst at {i}: "
+            f"gpu={g[i]!r} oracle={o[i]!r} err={err[i]:.3e} bound={bound[i] if np.ndim(bound) else bound:.3e}")
+
+
+def assert_rel(name, g, o, rtol=1e-5):
+    g = h64(g); o = np.asarray(o, np.float64)
+    assert g.shape == o.shape, (name, g.shape, o.shape)
+    assert np.isfinite(g).all(), f"{name}: non-finite GPU values"
+    _report(name, g, o, rtol * np.abs(o))
+
+
+def assert_mixed(name, g, o, rtol=1e-5):
+    g = h64(g); o = np.asarray(o, np.float64)
+    assert g.shape == o.shape, (name, g.shape, o.shape)
+    assert np.isfinite(g).all(), f"{name}: non-finite GPU values"
+    rms = np.sqrt(np.mean(o * o)) if o.size else 0.0
+    _report(name, g, o, rtol * (np.abs(o) + rms))
+
+
+def assert_act(name, g, o, act):
+    """Activation-typed output: bf16 rule against the oracle rounded to bf16, fp32 mixed rule."""
+    g = h64(g); o = np.asarray(o, np.float64)
+    assert g.shape == o.shape, (name, g.shape, o.shape)
+    assert np.isfinite(g).all(), f"{name}: non-finite GPU values"
+    if act == "bf16":
+        ob = O.round_f64_to_bf16(o)
+        rms = np.sqrt(np.mean(o * o)) if o.size else 0.0
+        _report(name, g, ob, 8e-3 * np.abs(ob) + 1e-5 * rms)
+    else:
+        assert_mixed(name, g, o)

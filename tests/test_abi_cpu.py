@@ -1,0 +1,166 @@
+"""CPU tests of the C ABI boundary: symbols, status strings, fail-closed validation.
+
+No kernel is launched: every call here fails validation on the host, before
+any HIP runtime call, so the pointers are plain integers that are never
+dereferenced.
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+import torch
+
+from mhc_hyper_connection_proj_amd import _lib as L
+
+# The fake pointers below must never reach a kernel: with a GPU visible, a call
+# that slipped through validation would launch on invalid addresses.
+pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                reason="host-only validation tests use fake device pointers")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, WS, ARG = range(8)
+A = 0x7f0000000000  # fake, 16-byte aligned device addresses, far apart
+MB = 1 << 20
+
+
+def p(i):
+    return A + i * 64 * MB
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from mhc_hyper_connection_proj_amd import build
+        build.build()
+    return L.lib()
+
+
+def test_exports_every_header_symbol(lib):
+    declared = L.header_functions()
+    assert len(declared) >= 18
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [f for f in declared if f not in exported]
+    assert not missing, missing
+    for f in declared:
+        assert hasattr(lib, f)
+    assert set(declared) == set(L.SIGNATURES)
+
+
+def test_status_strings_and_version(lib):
+    for i, name in enumerate(L.STATUS):
+        assert lib.mhc_status_string(i).decode() == name
+    assert b"gfx950" in lib.mhc_version()
+
+
+def _last(lib):
+    return lib.mhc_last_error().decode()
+
+
+def test_sinkhorn_validation(lib):
+    f = lib.mhc_sinkhorn_fwd
+    assert f(None, -1, 4, p(0), p(1), 20, 1e-6) == SHAPE
+    assert f(None, 10, 3, p(0), p(1), 20, 1e-6) == UNSUP
+    assert f(None, 10, 0, p(0), p(1), 20, 1e-6) == SHAPE
+    assert f(None, 10, 4, p(0), p(1), -1, 1e-6) == ARG
+    assert f(None, 10, 4, p(0), p(1), 5000, 1e-6) == UNSUP
+    assert f(None, 10, 4, p(0), p(1), 20, -1e-6) == ARG
+    assert f(None, 10, 4, p(0), p(1), 20, float("nan")) == ARG
+    assert f(None, 10, 4, None, p(1), 20, 1e-6) == NULL and "logits" in _last(lib)
+    assert f(None, 10, 4, p(0) + 4, p(1), 20, 1e-6) == ALIGN
+    assert f(None, 10, 4, p(0), p(0) + 320, 20, 1e-6) == ALIAS   # 10*64 bytes: overlaps
+    assert f(None, 0, 4, None, None, 20, 1e-6) == OK              # empty: no-op
+    g = lib.mhc_sinkhorn_bwd
+    assert g(None, 10, 4, p(0), p(1), p(1), 20, 1e-6) == ALIAS
+    assert g(None, 10, 4, p(0), None, p(2), 20, 1e-6) == NULL
+
+
+def test_dims_validation(lib):
+    f = lib.mhc_h_aggregate_fwd
+    assert f(None, 4, 4, 63, 0, p(0), p(1), p(2)) == UNSUP       # C % 8
+    assert f(None, 4, 4, 0, 0, p(0), p(1), p(2)) == SHAPE
+    assert f(None, 4, 4, 16392, 0, p(0), p(1), p(2)) == UNSUP    # C > 16384
+    assert f(None, 4, 5, 64, 0, p(0), p(1), p(2)) == UNSUP       # n != 4
+    assert f(None, 4, 4, 64, 7, p(0), p(1), p(2)) == ARG         # dtype
+    assert f(None, -2, 4, 64, 0, p(0), p(1), p(2)) == SHAPE
+    assert f(None, 0, 4, 64, 0, None, None, None) == OK
+    assert f(None, 4, 4, 64, 0, p(0), p(1), p(0) + 1024) == ALIAS  # out inside X (4*4*64*2 bytes)
+
+
+def test_post_bwd_validation(lib):
+    f = lib.mhc_h_post_bda_bwd
+    # stream, tokens, n, C, act, G, X, H_res, H_post, x, bias, dX, dH_res, dH_post, dx, dbias, ws, ws_bytes
+    args = [None, 8, 4, 64, 0, p(0), p(1), p(2), p(3), p(4), None, p(5), p(6), p(7), p(8), None, None, 0]
+    # dbias without bias
+    a = list(args); a[15] = p(9)
+    assert f(*a) == ARG
+    # dbias with bias but no workspace
+    a = list(args); a[10] = p(10); a[15] = p(9)
+    assert f(*a) == WS
+    need = lib.mhc_h_post_bda_bwd_workspace_size(8, 4, 64, 0, 1)
+    assert need > 0
+    a[16] = p(11); a[17] = need - 1
+    assert f(*a) == WS
+    a[17] = need; a[16] = p(11) + 8
+    assert f(*a) == ALIGN
+    # outputs overlapping each other
+    a = list(args); a[12] = p(5)
+    assert f(*a) == ALIAS
+    assert lib.mhc_h_post_bda_bwd_workspace_size(8, 4, 64, 0, 0) == 0
+
+
+def test_proj_validation(lib):
+    f = lib.mhc_proj_rms_h
+    need = lib.mhc_proj_rms_h_workspace_size(70, 4, 4096, 0)
+    assert need > 0
+    base = [None, 70, 4, 4096, 0, p(0), p(1), None, None, 1e-6, p(2), p(3), p(4), p(5), p(6), need]
+    a = list(base); a[9] = -1.0
+    assert f(*a) == ARG
+    a = list(base); a[14] = None
+    assert f(*a) == WS
+    a = list(base); a[6] = None
+    assert f(*a) == NULL
+    a = list(base); a[12] = p(0) + 4096
+    assert f(*a) == ALIAS
+    a = list(base); a[13] = p(6)                                  # saved == workspace
+    assert f(*a) == ALIAS
+    g = lib.mhc_proj_rms_h_bwd
+    nb = lib.mhc_proj_rms_h_bwd_workspace_size(70, 4, 4096, 0)
+    b = [None, 70, 4, 4096, 0, p(0), p(1), None, p(2), p(3), p(4), p(5), p(6), p(7), p(0), 1, p(9), None, None,
+         p(10), nb]
+    assert g(*b) == ALIAS                                          # dX aliases X
+    b[14] = p(8)
+    b[19] = None
+    assert g(*b) == WS
+    assert g(None, 0, 4, 64, 0, None, None, None, None, None, None, None, None, None, None, 0, None, None, None,
+             None, 0) == OK
+
+
+def test_pre_validation(lib):
+    f = lib.mhc_pre_fwd
+    ws = lib.mhc_pre_fwd_workspace_size(16, 4, 256, 1)
+    base = [None, 16, 4, 256, 1, p(0), p(1), None, None, 1e-6, 20, 1e-6, p(2), p(3), p(4), p(5), None, p(6),
+            p(7), ws]
+    a = list(base); a[10] = -3
+    assert f(*a) == ARG
+    a = list(base); a[11] = float("inf")
+    assert f(*a) == ARG
+    a = list(base); a[17] = p(4)
+    assert f(*a) == ALIAS
+    g = lib.mhc_pre_bwd
+    wb = lib.mhc_pre_bwd_workspace_size(16, 4, 256, 1)
+    b = [None, 16, 4, 256, 1, p(0), p(1), p(2), p(3), p(4), None, p(5), p(6), p(7), p(8), 20, 1e-6, p(9), 1, p(10),
+         None, None, None, None, p(11), wb]
+    b2 = list(b); b2[5] = None
+    assert g(*b2) == NULL
+    b2 = list(b); b2[17] = p(3)                                    # dX aliases X
+    assert g(*b2) == ALIAS
+    b2 = list(b); b2[25] = wb - 16
+    assert g(*b2) == WS
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        L.lib()

@@ -1,0 +1,261 @@
+"""GPU parity: each libmhc entry point against the fp64 oracle, element by element.
+
+Inputs are seeded synthetic arrays (mhc_hyper_connection_proj_amd.synth) or
+oracle outputs rounded to their storage type; nothing fed to the oracle comes
+from the GPU.  Sizes span several MFMA/workgroup tiles and ragged tails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_util import assert_act, assert_mixed, assert_rel, dev, h64, log
+from mhc_hyper_connection_proj_amd import binding as B
+from mhc_hyper_connection_proj_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+RNG = np.random.default_rng(7)
+
+
+def f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def store(a64, act):
+    """float64 -> storage array (bf16 bits or float32), rounding once."""
+    return O.round_f64_to_bf16_bits(a64) if act == "bf16" else f32(a64)
+
+
+# ----------------------------------------------------------------- Sinkhorn
+@pytest.mark.parametrize("count,iters,eps,std", [
+    (1, 20, 1e-6, 1.0), (5000, 20, 1e-6, 1.0), (777, 20, 1e-6, 3.4), (300, 0, 1e-6, 1.0),
+    (300, 1, 1e-6, 1.0), (300, 45, 1e-6, 1.0), (300, 7, 0.25, 1.0), (300, 20, 0.0, 1.0)])
+def test_sinkhorn_fwd_bwd(count, iters, eps, std):
+    log(f"sinkhorn count={count} iters={iters} eps={eps} std={std}")
+    L = f32(RNG.standard_normal((count, 4, 4)) * std)
+    dH = f32(RNG.standard_normal((count, 4, 4)))
+    H = B.mhc_sinkhorn_fwd(dev(L), iters, eps)
+    dL = B.mhc_sinkhorn_bwd(dev(dH), dev(L), iters, eps)
+    torch.cuda.synchronize()
+    assert_rel("H_res", H, O.sinkhorn_fwd(h64(L), iters, eps))
+    assert_mixed("dlogits", dL, O.sinkhorn_bwd(h64(dH), h64(L), iters, eps))
+
+
+def test_sinkhorn_batched_workload_full():
+    w = synth.WORKLOADS["sinkhorn_batched"]
+    log(f"sinkhorn full workload count={w.tokens}")
+    L = synth.tensor(w, "L")
+    dH = synth.tensor(w, "dH")
+    H = B.mhc_sinkhorn_fwd(dev(L), w.iters, w.eps)
+    dL = B.mhc_sinkhorn_bwd(dev(dH), dev(L), w.iters, w.eps)
+    torch.cuda.synchronize()
+    assert_rel("H_res", H, O.sinkhorn_fwd(h64(L), w.iters, w.eps))
+    assert_mixed("dlogits", dL, O.sinkhorn_bwd(h64(dH), h64(L), w.iters, w.eps))
+
+
+# ----------------------------------------------------------------- h_aggregate
+SHAPES = [("bf16", 1, 256), ("bf16", 37, 296), ("bf16", 9, 4096), ("bf16", 5, 7168),
+          ("f32", 64, 256), ("f32", 11, 1032), ("bf16", 3, 8), ("bf16", 2, 16384), ("f32", 2, 12288)]
+
+
+@pytest.mark.parametrize("act,N,C", SHAPES)
+def test_h_aggregate(act, N, C):
+    log(f"h_aggregate act={act} N={N} C={C}")
+    X = store(RNG.standard_normal((N, 4, C)), act)
+    Hp = f32(1 / (1 + np.exp(-RNG.standard_normal((N, 4)))))
+    g = store(RNG.standard_normal((N, C)), act)
+    dX0 = store(RNG.standard_normal((N, 4, C)), act)
+    Xd = dev(X)
+    out = B.mhc_h_aggregate_fwd(Xd, dev(Hp))
+    dX, dH = B.mhc_h_aggregate_bwd(dev(g), Xd, dev(Hp))
+    dXa, _ = B.mhc_h_aggregate_bwd(dev(g), Xd, dev(Hp), dX=dev(dX0), accumulate_dX=True)
+    torch.cuda.synchronize()
+    assert_act("agg", out, O.h_aggregate_fwd(h64(X), h64(Hp)), act)
+    odX, odH = O.h_aggregate_bwd(h64(g), h64(X), h64(Hp))
+    assert_act("dX", dX, odX, act)
+    assert_act("dX accumulated", dXa, h64(dX0) + odX, act)
+    assert_mixed("dH_pre", dH, odH)
+
+
+def test_h_aggregate_one_hot_exact():
+    N, C = 40, 7168
+    X = synth.f32_to_bf16_bits(RNG.standard_normal((N, 4, C)).astype(np.float32))
+    sel = RNG.integers(0, 4, N)
+    Hp = f32(np.eye(4)[sel])
+    out = B.mhc_h_aggregate_fwd(dev(X), dev(Hp))
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, X[np.arange(N), sel])
+
+
+# ----------------------------------------------------------------- h_post_bda
+@pytest.mark.parametrize("act,N,C,bias", [
+    ("bf16", 1, 256, True), ("bf16", 37, 296, True), ("bf16", 50, 4096, True), ("bf16", 21, 7168, False),
+    ("f32", 64, 256, True), ("f32", 17, 1032, False), ("bf16", 33, 8, True), ("bf16", 3, 16384, True)])
+def test_h_post_bda(act, N, C, bias):
+    log(f"h_post_bda act={act} N={N} C={C} bias={bias}")
+    X = store(RNG.standard_normal((N, 4, C)), act)
+    G = store(RNG.standard_normal((N, 4, C)), act)
+    x = store(RNG.standard_normal((N, C)), act)
+    b = store(RNG.standard_normal(C) * 0.1, act) if bias else None
+    Hr = f32(O.sinkhorn_fwd(RNG.standard_normal((N, 4, 4)), 20, 1e-6))
+    Hp = f32(2 / (1 + np.exp(-RNG.standard_normal((N, 4)))))
+    out = B.mhc_h_post_bda_fwd(dev(X), dev(Hr), dev(Hp), dev(x), dev(b) if bias else None)
+    dX, dHr, dHp, dx, db = B.mhc_h_post_bda_bwd(dev(G), dev(X), dev(Hr), dev(Hp), dev(x),
+                                                dev(b) if bias else None)
+    torch.cuda.synchronize()
+    bb = h64(b) if bias else None
+    assert_act("out", out, O.h_post_bda_fwd(h64(X), h64(Hr), h64(Hp), h64(x), bb), act)
+    odX, odHr, odHp, odx, odb = O.h_post_bda_bwd(h64(G), h64(X), h64(Hr), h64(Hp), h64(x), bb)
+    assert_act("dX", dX, odX, act)
+    assert_mixed("dH_res", dHr, odHr)
+    assert_mixed("dH_post", dHp, odHp)
+    assert_act("dx", dx, odx, act)
+    if bias:
+        assert_act("dbias", db, odb, act)
+    else:
+        assert db is None
+
+
+def test_h_post_bda_identity_h_res_exact_bf16():
+    # H_res = I and H_post = 0: out must reproduce the residual bit for bit
+    N, C = 19, 4096
+    X = synth.f32_to_bf16_bits(RNG.standard_normal((N, 4, C)).astype(np.float32))
+    x = synth.f32_to_bf16_bits(RNG.standard_normal((N, C)).astype(np.float32))
+    Hr = f32(np.broadcast_to(np.eye(4), (N, 4, 4)))
+    out = B.mhc_h_post_bda_fwd(dev(X), dev(Hr), dev(np.zeros((N, 4), np.float32)), dev(x))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), X)
+
+
+# ----------------------------------------------------------------- projection
+PROJ = [("f32", 64, 256), ("bf16", 37, 296), ("bf16", 70, 4096), ("bf16", 67, 7168),
+        ("bf16", 5, 8), ("f32", 33, 1032), ("bf16", 129, 1024)]
+
+
+def _proj_inputs(act, N, C, zero_row=True):
+    X = store(RNG.standard_normal((N, 4, C)), act)
+    if zero_row and N > 3:
+        X[2] = 0
+    W = f32(RNG.standard_normal((4 * C, 24)) * 0.02)
+    alpha = f32([1.3, 0.7, 1.1])
+    hb = f32(RNG.standard_normal(24) * 0.1)
+    return X, W, alpha, hb
+
+
+@pytest.mark.parametrize("act,N,C", PROJ)
+def test_proj_rms_h_fwd(act, N, C):
+    log(f"proj_rms_h fwd act={act} N={N} C={C}")
+    X, W, alpha, hb = _proj_inputs(act, N, C)
+    Hp, Hq, L, saved = B.mhc_proj_rms_h(dev(X), dev(W), dev(alpha), dev(hb), 1e-6)
+    torch.cuda.synchronize()
+    p = O.proj_rms_h(h64(X), h64(W), h64(alpha), h64(hb), 1e-6)
+    # upstream quantities first, so a failure names the first diverging value
+    s = h64(saved)
+    assert_rel("q", s[:, 1], p.q)
+    assert_rel("r", s[:, 0], p.r)
+    assert_mixed("z", s[:, 2:26], p.z)
+    np.testing.assert_array_equal(s[:, 26:], 0.0)
+    assert_mixed("logits", L, p.L)
+    assert_rel("H_pre", Hp, p.H_pre)
+    assert_rel("H_post", Hq, p.H_post)
+
+
+@pytest.mark.parametrize("act,N,C", PROJ)
+def test_proj_rms_h_bwd(act, N, C):
+    log(f"proj_rms_h bwd act={act} N={N} C={C}")
+    X, W, alpha, hb = _proj_inputs(act, N, C)
+    p = O.proj_rms_h(h64(X), h64(W), h64(alpha), h64(hb), 1e-6)
+    saved = np.zeros((N, 32), np.float32)
+    saved[:, 0] = p.r; saved[:, 1] = p.q; saved[:, 2:26] = p.z
+    Hp, Hq = f32(p.H_pre), f32(p.H_post)
+    dHp = f32(RNG.standard_normal((N, 4))); dHq = f32(RNG.standard_normal((N, 4)))
+    dL = f32(RNG.standard_normal((N, 4, 4)))
+    dX0 = store(RNG.standard_normal((N, 4, C)), act)
+    args = (dev(X), dev(W), dev(saved), dev(Hp), dev(Hq), dev(dHp), dev(dHq), dev(dL))
+    dX, dW, da, db = B.mhc_proj_rms_h_bwd(*args, alpha=dev(alpha))
+    dXa, _, _, _ = B.mhc_proj_rms_h_bwd(*args, alpha=dev(alpha), dX=dev(dX0), accumulate_dX=True,
+                                        want_dW=False, want_dalpha=False, want_dhbias=False)
+    torch.cuda.synchronize()
+    odX, odW, oda, odb = O.proj_rms_h_bwd(h64(X), h64(W), h64(dHp), h64(dHq), h64(dL), h64(alpha), h64(hb), 1e-6)
+    assert_act("dX", dX, odX, act)
+    assert_act("dX accumulated", dXa, h64(dX0) + odX, act)
+    assert_mixed("dW", dW, odW)
+    assert_mixed("dalpha", da, oda)
+    assert_mixed("dhbias", db, odb)
+
+
+# ----------------------------------------------------------------- fused pre pass
+@pytest.mark.parametrize("act,N,C", [("f32", 64, 256), ("bf16", 37, 296), ("bf16", 66, 7168), ("bf16", 130, 4096)])
+def test_pre_fwd_bwd(act, N, C):
+    log(f"pre fwd/bwd act={act} N={N} C={C}")
+    X, W, alpha, hb = _proj_inputs(act, N, C)
+    o = B.mhc_pre_fwd(dev(X), dev(W), dev(alpha), dev(hb), 1e-6, 20, 1e-6)
+    torch.cuda.synchronize()
+    ref = O.pre_fwd(h64(X), h64(W), h64(alpha), h64(hb), 1e-6, 20, 1e-6)
+    assert_rel("H_pre", o["H_pre"], ref["H_pre"])
+    assert_rel("H_post", o["H_post"], ref["H_post"])
+    assert_mixed("logits", o["H_res_logits"], ref["L"])
+    # Sinkhorn of the GPU's own logits is checked by the Sinkhorn tests; here
+    # H_res is compared end to end, where logit rounding enters through exp.
+    assert_rel("H_res", o["H_res"], ref["H_res"], rtol=2e-5)
+    assert_act("agg", o["agg"], ref["agg"], act)
+    # backward from oracle-produced forward state
+    saved = np.zeros((N, 32), np.float32)
+    saved[:, 0] = ref["r"]; saved[:, 1] = ref["q"]; saved[:, 2:26] = ref["z"]
+    g = store(RNG.standard_normal((N, C)), act)
+    dHq = f32(RNG.standard_normal((N, 4)))
+    dHr = f32(RNG.standard_normal((N, 4, 4)))
+    dX0 = store(RNG.standard_normal((N, 4, C)), act)
+    ob = B.mhc_pre_bwd(dev(g), dev(dHq), dev(dHr), dev(X), dev(W), dev(saved), dev(f32(ref["H_pre"])),
+                       dev(f32(ref["H_post"])), dev(f32(ref["L"])), alpha=dev(alpha), iters=20, eps=1e-6,
+                       dX=dev(dX0), accumulate_dX=True, want_intermediates=True)
+    torch.cuda.synchronize()
+    rb = O.pre_bwd(h64(g), h64(dHq), h64(dHr), h64(X), h64(W), h64(alpha), h64(hb), 1e-6, 20, 1e-6)
+    assert_mixed("dH_pre", ob["dH_pre"], rb["dH_pre"])
+    assert_mixed("dlogits", ob["dlogits"], rb["dL"])
+    assert_act("dX", ob["dX"], h64(dX0) + rb["dX"], act)
+    assert_mixed("dW", ob["dW"], rb["dW"])
+    assert_mixed("dalpha", ob["dalpha"], rb["dalpha"])
+    assert_mixed("dhbias", ob["dhbias"], rb["dhbias"])
+
+
+# ----------------------------------------------------------------- edge cases
+def test_zero_tokens_is_noop_and_zero_param_grads():
+    C = 64
+    X = torch.empty(0, 4, C, dtype=torch.bfloat16, device="cuda")
+    W = torch.randn(4 * C, 24, device="cuda")
+    e = torch.empty(0, 4, device="cuda")
+    o = B.mhc_pre_bwd(torch.empty(0, C, dtype=torch.bfloat16, device="cuda"), e, torch.empty(0, 4, 4, device="cuda"),
+                      X, W, torch.empty(0, 32, device="cuda"), e, e, torch.empty(0, 4, 4, device="cuda"))
+    torch.cuda.synchronize()
+    assert o["dW"].abs().max().item() == 0.0
+    assert o["dalpha"].abs().max().item() == 0.0 and o["dhbias"].abs().max().item() == 0.0
+    assert B.mhc_sinkhorn_fwd(torch.empty(0, 4, 4, device="cuda")).numel() == 0
+
+
+def test_deterministic_bitwise():
+    act, N, C = "bf16", 96, 4096
+    X, W, alpha, hb = _proj_inputs(act, N, C)
+    G = store(RNG.standard_normal((N, 4, C)), act)
+    x = store(RNG.standard_normal((N, C)), act)
+    b = store(RNG.standard_normal(C) * 0.1, act)
+    outs = []
+    for _ in range(2):
+        o = B.mhc_pre_fwd(dev(X), dev(W), dev(alpha), dev(hb))
+        pb = B.mhc_h_post_bda_bwd(dev(G), dev(X), o["H_res"], o["H_post"], dev(x), dev(b))
+        bw = B.mhc_pre_bwd(o["agg"], pb[2], pb[1], dev(X), dev(W), o["saved"], o["H_pre"], o["H_post"],
+                           o["H_res_logits"], alpha=dev(alpha))
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in (*o.values(), *[p for p in pb if p is not None], *bw.values())])
+    for a, b2 in zip(*outs):
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a, b2.view(torch.uint8)
+                           if b2.dtype == torch.bfloat16 else b2)
+
+
+def test_invalid_arguments_raise():
+    X = torch.zeros(4, 3, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(B._lib.MhcError) as e:
+        B.mhc_h_aggregate_fwd(X, torch.zeros(4, 3, device="cuda"))
+    assert e.value.name == "MHC_ERR_UNSUPPORTED"
