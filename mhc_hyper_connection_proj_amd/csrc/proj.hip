@@ -319,96 +319,359 @@ void launch_proj_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *
 }
 
 // ================================================================== backward
-// Per-token record written by proj_bwd_token_kernel (fp32, stride kRec):
-//   [0,24) dp = r * alpha * dzh     [24] c_rms = -dr r^2 / (K q) (0 if q == 0)
-//   [25,28) per-token d_alpha terms [32,56) dzh (per-token d_hbias terms)
-constexpr int kRec = 64;
-constexpr int kDxK = 4;               // consecutive k per thread in the dX/dW kernel
-constexpr int kDxKT = 256 * kDxK;     // k per workgroup
+// Per token (proj_bwd_token_kernel): the sigmoid / Sinkhorn backward gives
+// dzh; dp = r alpha dzh and c_rms = -S r / (K q) with S = sum_j alpha dzh_j z_j
+// (the RMS leg -dr r^2 x / (K q) of the reference backward, using
+// dr = S / r and r (q + eps) = 1).  Then, over all tokens and k,
+//   dX[t][k] (+)= H_pre[t][i] g[t][c] + c_rms[t] x[t][k] + sum_j dp[t][j] W[k][j]
+//   dW[k][j]    = sum_t x[t][k] dp[t][j]
+// Both contractions run on MFMA for bf16 activations:
+//  * dX: fp32 MFMA (32x32x2) on dp and W as they are.  A bf16 split of dp
+//    and W is not accurate enough here: for an all-zero residual row
+//    r = 1/eps amplifies dp to ~1e5 while dX entries cancel to O(1).
+//  * dW: bf16 MFMA.  The contraction runs over tokens, so each wave stages its 32x64 X
+//    tile in LDS and reads 8-token columns as A fragments; dp comes split
+//    exactly into hi + mid + lo bf16 terms, stored token-contiguous per (term,
+//    j) so each B fragment is one 16-byte load.
+// fp32 activations use a VALU kernel for both contractions.
+constexpr int kDpf = 32;     // fp32 per-token record: dp[24], c_rms, pad
+constexpr int kBwKW = 64;    // k per wave in the MFMA kernel
+constexpr int kBwKT = 4 * kBwKW;
+constexpr int kDxK = 4;      // k per thread in the fp32 VALU kernel
+constexpr int kDxKT = 256 * kDxK;
 
-static int64_t bwd_token_block(int64_t N, int64_t K) {
-  // aim for ~1024 workgroups; token blocks of at least 64
-  const int64_t nkt = (K + kDxKT - 1) / kDxKT;
-  int64_t tb = (N * nkt + 1023) / 1024;
-  tb = tb < 64 ? 64 : tb;
-  return (tb + 63) / 64 * 64;
+static int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+// Token block of the dX/dW kernels: about 2048 workgroups, multiple of 32.
+static int64_t bwd_token_block(int64_t N, int64_t K, bool f32) {
+  const int64_t nkt = f32 ? (K + kDxKT - 1) / kDxKT : (K + kBwKT - 1) / kBwKT;
+  int64_t tb = (N * nkt + 2047) / 2048;
+  return round_up(tb < 32 ? 32 : tb, 32);
 }
 
-size_t proj_bwd_ws(int64_t N, int64_t C, bool) {
+struct BwdWs {
+  float *dpf, *dhpre, *ppart, *dwpart;
+  bf16_t *dpB;
+  int64_t npad, nblk, tbsz, ntb;
+};
+
+static BwdWs bwd_layout(void *ws, int64_t N, int64_t C, bool f32) {
   const int64_t K = 4 * C;
-  const int64_t tb = bwd_token_block(N, K);
-  const int64_t ntb = (N + tb - 1) / tb;
-  return align256((size_t)N * kRec * 4) + align256((size_t)N * 4 * 4) +
-         align256((size_t)ntb * K * kJ * 4);
+  BwdWs L{};
+  L.npad = round_up(N, 32);
+  L.nblk = (L.npad + 255) / 256;
+  L.tbsz = bwd_token_block(N, K, f32);
+  L.ntb = (N + L.tbsz - 1) / L.tbsz;
+  size_t off = 0;
+  char *b = (char *)ws;
+  auto take = [&](size_t bytes) { char *p = b ? b + off : nullptr; off += align256(bytes); return p; };
+  L.dpf = (float *)take((size_t)N * kDpf * 4);
+  L.dhpre = (float *)take((size_t)N * 16);
+  L.ppart = (float *)take((size_t)L.nblk * 32 * 4);
+  if (!f32) L.dpB = (bf16_t *)take((size_t)3 * kJ * L.npad * 2);
+  L.dwpart = (float *)take((size_t)L.ntb * K * kJ * 4);
+  return L;
 }
 
+size_t proj_bwd_ws(int64_t N, int64_t C, bool f32) {
+  const int64_t K = 4 * C;
+  BwdWs L = bwd_layout(nullptr, N, C, f32);
+  size_t total = align256((size_t)N * kDpf * 4) + align256((size_t)N * 16) + align256((size_t)L.nblk * 128);
+  if (!f32) total += align256((size_t)3 * kJ * L.npad * 2);
+  return total + align256((size_t)L.ntb * K * kJ * 4);
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+
+// One thread per token (grid covers npad tokens; tokens >= N only zero their
+// dpB column).  Block partial sums of dhbias (24) and dalpha (3) go to ppart.
+template <bool MFMA_OUT>
 __global__ __launch_bounds__(256) void proj_bwd_token_kernel(
     const float *__restrict__ alpha, const float *__restrict__ saved, const float *__restrict__ Hpre,
     const float *__restrict__ Hpost, const float *__restrict__ dHpre, const float *__restrict__ dHpost,
     const float *__restrict__ dL_in, const float *__restrict__ dHres, const float *__restrict__ logits,
-    int iters, float eps, float *__restrict__ rec, float *__restrict__ dL_out,
-    float *__restrict__ dHpre_out, int64_t N, int64_t K) {
+    int iters, float eps, float *__restrict__ dpf, bf16_t *__restrict__ dpB,
+    float *__restrict__ ppart, float *__restrict__ dL_out, float *__restrict__ dHpre_out, int64_t N,
+    int64_t npad, int64_t K) {
+  __shared__ float red[4][28];
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= N) return;
-  float dl[16];
-  if (dL_in) {
-    load16(dL_in + t * 16, dl);
-  } else {
-    float lg[16];
-    load16(logits + t * 16, lg);
-    load16(dHres + t * 16, dl);
-    sk_backward(lg, dl, iters, eps);
+  float contrib[27];
+#pragma unroll
+  for (int e = 0; e < 27; ++e) contrib[e] = 0.f;
+  if (t < N) {
+    float dl[16];
+    if (dL_in) {
+      load16(dL_in + t * 16, dl);
+    } else {
+      float lg[16];
+      load16(logits + t * 16, lg);
+      load16(dHres + t * 16, dl);
+      sk_backward(lg, dl, iters, eps);
+    }
+    if (dL_out) store16(dL_out + t * 16, dl);
+    const float r = saved[t * kSavedStride + 0];
+    const float q = saved[t * kSavedStride + 1];
+    float z[kJ], dzh[kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) z[j] = saved[t * kSavedStride + 2 + j];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float hp = Hpre[t * 4 + i];
+      const float dhp = dHpre[t * 4 + i];
+      if (dHpre_out) dHpre_out[t * 4 + i] = dhp;
+      dzh[i] = dhp * (hp * (1.f - hp));
+      const float hq = Hpost[t * 4 + i];
+      dzh[4 + i] = dHpost[t * 4 + i] * (hq * (1.f - 0.5f * hq));
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dzh[8 + e] = dl[e];
+    float a3[3] = {1.f, 1.f, 1.f};
+    if (alpha) { a3[0] = alpha[0]; a3[1] = alpha[1]; a3[2] = alpha[2]; }
+    float S = 0.f;
+    float dp[kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int seg = j < 4 ? 0 : (j < 8 ? 1 : 2);
+      contrib[j] = dzh[j];
+      contrib[kJ + seg] += dzh[j] * z[j];
+      const float dz = a3[seg] * dzh[j];
+      S += dz * z[j];
+      dp[j] = r * dz;
+    }
+    const float crms = q > 0.f ? -S * r / ((float)K * q) : 0.f;
+    float rowf[kDpf];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) rowf[j] = dp[j];
+    rowf[kJ] = crms;
+#pragma unroll
+    for (int j = kJ + 1; j < kDpf; ++j) rowf[j] = 0.f;
+#pragma unroll
+    for (int qd = 0; qd < kDpf / 4; ++qd)
+      reinterpret_cast<float4 *>(dpf + t * kDpf)[qd] =
+          make_float4(rowf[4 * qd], rowf[4 * qd + 1], rowf[4 * qd + 2], rowf[4 * qd + 3]);
+    if (MFMA_OUT) {
+      uint16_t hi[kJ], mid[kJ], lo[kJ];
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        const float h = bf16_round(dp[j]);
+        const float r1 = dp[j] - h;
+        const float m = bf16_round(r1);
+        hi[j] = bf16_bits(h);
+        mid[j] = bf16_bits(m);
+        lo[j] = bf16_bits(r1 - m);
+      }
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        dpB[(0 * kJ + j) * npad + t] = hi[j];
+        dpB[(1 * kJ + j) * npad + t] = mid[j];
+        dpB[(2 * kJ + j) * npad + t] = lo[j];
+      }
+    }
+  } else if (MFMA_OUT && t < npad) {
+#pragma unroll
+    for (int j = 0; j < 3 * kJ; ++j) dpB[(int64_t)j * npad + t] = 0;
   }
-  if (dL_out) store16(dL_out + t * 16, dl);
-  const float r = saved[t * kSavedStride + 0];
-  const float q = saved[t * kSavedStride + 1];
-  float z[kJ], dzh[kJ];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-  for (int j = 0; j < kJ; ++j) z[j] = saved[t * kSavedStride + 2 + j];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float hp = Hpre[t * 4 + i];
-    const float dhp = dHpre[t * 4 + i];
-    if (dHpre_out) dHpre_out[t * 4 + i] = dhp;
-    dzh[i] = dhp * (hp * (1.f - hp));
-    const float hq = Hpost[t * 4 + i];
-    dzh[4 + i] = dHpost[t * 4 + i] * (hq * (1.f - 0.5f * hq));
+  for (int e = 0; e < 27; ++e) {
+    const float s = wave_sum(contrib[e]);
+    if (lane == 0) red[wave][e] = s;
   }
-#pragma unroll
-  for (int e = 0; e < 16; ++e) dzh[8 + e] = dl[e];
-  float a3[3] = {1.f, 1.f, 1.f};
-  if (alpha) { a3[0] = alpha[0]; a3[1] = alpha[1]; a3[2] = alpha[2]; }
-  float da[3] = {0.f, 0.f, 0.f};
-  float S = 0.f;
-  float out[kRec];
-#pragma unroll
-  for (int j = 0; j < kJ; ++j) {
-    const int seg = j < 4 ? 0 : (j < 8 ? 1 : 2);
-    da[seg] += dzh[j] * z[j];
-    const float dz = a3[seg] * dzh[j];
-    S += dz * z[j];
-    out[j] = r * dz;
-    out[32 + j] = dzh[j];
-  }
-  // dr = sum_j dz_j p_j with p_j = z_j / r, and r (q + rms_eps) = 1, so the
-  // RMS coefficient -dr r^2 / (K q) equals -S r / (K q) with S = sum_j dz_j z_j.
-  out[24] = q > 0.f ? -S * r / ((float)K * q) : 0.f;
-  out[25] = da[0]; out[26] = da[1]; out[27] = da[2];
-  out[28] = out[29] = out[30] = out[31] = 0.f;
-#pragma unroll
-  for (int j = 56; j < kRec; ++j) out[j] = 0.f;
-#pragma unroll
-  for (int qd = 0; qd < kRec / 4; ++qd)
-    reinterpret_cast<float4 *>(rec + t * kRec)[qd] =
-        make_float4(out[4 * qd], out[4 * qd + 1], out[4 * qd + 2], out[4 * qd + 3]);
+  __syncthreads();
+  if (threadIdx.x < 27)
+    ppart[blockIdx.x * 32 + threadIdx.x] =
+        (red[0][threadIdx.x] + red[1][threadIdx.x]) + (red[2][threadIdx.x] + red[3][threadIdx.x]);
 }
 
-// dX[t][k] = (acc ? dX[t][k] : 0) + H_pre[t][i] g[t][c] + c_rms[t] x[t][k] + sum_j dp[t][j] W[k][j]
-// dW partial[tb][k][j] = sum_{t in tb} x[t][k] dp[t][j]
-template <typename T, bool ACCUM, bool HAS_G, bool DW>
-__global__ __launch_bounds__(256) void proj_bwd_dx_kernel(
-    const T *__restrict__ X, const float *__restrict__ W, const float *__restrict__ rec,
-    const float *__restrict__ Hpre, const T *__restrict__ gr, T *__restrict__ dX,
+// dhbias / dalpha: sum of the per-block partials in block order.
+__global__ void param_final_kernel(const float *__restrict__ ppart, int64_t nblk,
+                                   float *__restrict__ dalpha, float *__restrict__ dhbias) {
+  const int e = threadIdx.x;
+  if (e >= 27) return;
+  float s = 0.f;
+  for (int64_t b = 0; b < nblk; ++b) s += ppart[b * 32 + e];
+  if (e < kJ) {
+    if (dhbias) dhbias[e] = s;
+  } else if (dalpha) {
+    dalpha[e - kJ] = s;
+  }
+}
+
+// ------------------------------------------------------------------ MFMA dX / dW kernel
+// Workgroup = 4 waves, each owning 64 consecutive k; grid = k tiles x token
+// blocks.  Per 32-token sub-tile a wave: (a) 2 x 12 fp32 MFMAs give the dp W^T
+// tile (lane half h carries j = 12h .. 12h+11 of the 24-long contraction),
+// (b) stages it and its X tile in LDS, (c) writes dX row-major with 16-byte
+// accesses, (d) reads 8-token X columns from LDS as A fragments and adds
+// x^T dp into its dW accumulators (12 MFMAs).
+template <bool ACCUM, bool HAS_G, bool DW>
+__global__ __launch_bounds__(256) void proj_bwd_mfma_kernel(
+    const bf16_t *__restrict__ X, const float *__restrict__ W, const bf16_t *__restrict__ dpB,
+    const float *__restrict__ dpf, const float *__restrict__ Hpre,
+    const bf16_t *__restrict__ gr, bf16_t *__restrict__ dX, float *__restrict__ dWpart, int64_t N,
+    int64_t npad, int64_t C, int64_t tbsz) {
+  __shared__ __attribute__((aligned(16))) float lds_acc[4][32][kBwKW + 4];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_x[4][32][kBwKW + 8];
+  const int64_t K = 4 * C;
+  const int64_t nkt = (K + kBwKT - 1) / kBwKT;
+  const int64_t kt = blockIdx.x % nkt;
+  const int64_t tb = blockIdx.x / nkt;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 31, h = lane >> 5;
+  const int64_t kw = kt * kBwKT + wave * kBwKW;
+  const int tr = lane >> 1;             // row-major epilogue: token row
+  const int kh = (lane & 1) * 32;       // and 32-k half
+
+  float wf[2][12];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int64_t k = kw + 32 * ct + col;
+#pragma unroll
+    for (int s4 = 0; s4 < 3; ++s4) {
+      const float4 v = k < K ? *reinterpret_cast<const float4 *>(W + k * kJ + 12 * h + 4 * s4)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+      wf[ct][4 * s4] = v.x; wf[ct][4 * s4 + 1] = v.y; wf[ct][4 * s4 + 2] = v.z; wf[ct][4 * s4 + 3] = v.w;
+    }
+  }
+  f32x16 accW[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) accW[rt][r] = 0.f;
+
+  const int64_t t_begin = tb * tbsz;
+  const int64_t t_end = min(N, t_begin + tbsz);
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += 32) {
+    // (a) dp W^T for 32 tokens x 64 k
+    const int64_t ta = t0 + col;
+    float af[12];
+#pragma unroll
+    for (int s4 = 0; s4 < 3; ++s4) {
+      const float4 v = ta < N ? *reinterpret_cast<const float4 *>(dpf + ta * kDpf + 12 * h + 4 * s4)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+      af[4 * s4] = v.x; af[4 * s4 + 1] = v.y; af[4 * s4 + 2] = v.z; af[4 * s4 + 3] = v.w;
+    }
+    f32x16 accX[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) accX[ct][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 12; ++s)
+        accX[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[s], wf[ct][s], accX[ct], 0, 0, 0);
+    }
+    // (b) row-major loads for the epilogue: token t0 + tr, k = kw + kh + 8q
+    const int64_t tt = t0 + tr;
+    const bool tv = tt < N;
+    u32x4 xr[4], dr[4], gg[4];
+    float hp[4];
+    const float crms = tv ? dpf[tt * kDpf + kJ] : 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t k = kw + kh + 8 * q;
+      const bool v = tv && k < K;
+      xr[q] = v ? *reinterpret_cast<const u32x4 *>(X + tt * K + k) : u32x4{0u, 0u, 0u, 0u};
+      if (ACCUM) dr[q] = v ? *reinterpret_cast<const u32x4 *>(dX + tt * K + k) : u32x4{0u, 0u, 0u, 0u};
+      if (HAS_G) {
+        const int64_t si = k / C;
+        const int64_t c = k - si * C;
+        gg[q] = v ? *reinterpret_cast<const u32x4 *>(gr + tt * C + c) : u32x4{0u, 0u, 0u, 0u};
+        hp[q] = v ? Hpre[tt * 4 + si] : 0.f;
+      }
+    }
+    // (c) stage the accumulator tile and the X tile
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) lds_acc[wave][8 * (r >> 2) + 4 * h + (r & 3)][32 * ct + col] = accX[ct][r];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4 *>(&lds_x[wave][tr][kh + 8 * q]) = xr[q];
+    __syncthreads();
+    // (d) dX = base + dp W^T, row-major 16-byte stores
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t k = kw + kh + 8 * q;
+      if (!(tv && k < K)) continue;
+      const float4 a0 = *reinterpret_cast<const float4 *>(&lds_acc[wave][tr][kh + 8 * q]);
+      const float4 a1 = *reinterpret_cast<const float4 *>(&lds_acc[wave][tr][kh + 8 * q + 4]);
+      const float acc8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const uint32_t xw[4] = {xr[q].x, xr[q].y, xr[q].z, xr[q].w};
+      float o[8];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        o[2 * p] = acc8[2 * p] + crms * bf16_lo(xw[p]);
+        o[2 * p + 1] = acc8[2 * p + 1] + crms * bf16_hi(xw[p]);
+      }
+      if (HAS_G) {
+        const uint32_t gw[4] = {gg[q].x, gg[q].y, gg[q].z, gg[q].w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          o[2 * p] += hp[q] * bf16_lo(gw[p]);
+          o[2 * p + 1] += hp[q] * bf16_hi(gw[p]);
+        }
+      }
+      if (ACCUM) {
+        const uint32_t dw4[4] = {dr[q].x, dr[q].y, dr[q].z, dr[q].w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          o[2 * p] += bf16_lo(dw4[p]);
+          o[2 * p + 1] += bf16_hi(dw4[p]);
+        }
+      }
+      uint4 ow;
+      ow.x = pack_bf16x2(o[0], o[1]);
+      ow.y = pack_bf16x2(o[2], o[3]);
+      ow.z = pack_bf16x2(o[4], o[5]);
+      ow.w = pack_bf16x2(o[6], o[7]);
+      *reinterpret_cast<uint4 *>(dX + tt * K + k) = ow;
+    }
+    // (e) dW += X^T dp over these 32 tokens
+    if (DW) {
+      u32x4 xa[2][2];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          uint32_t w4[4];
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const uint32_t lo16 = lds_x[wave][16 * s + 8 * h + 2 * p][32 * rt + col];
+            const uint32_t hi16 = lds_x[wave][16 * s + 8 * h + 2 * p + 1][32 * rt + col];
+            w4[p] = lo16 | (hi16 << 16);
+          }
+          xa[rt][s] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+        }
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int tm = 0; tm < 3; ++tm) {
+          const u32x4 bfr = col < kJ
+              ? *reinterpret_cast<const u32x4 *>(dpB + (int64_t)(tm * kJ + col) * npad + t0 + 16 * s + 8 * h)
+              : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+            accW[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa[rt][s]),
+                                                               __builtin_bit_cast(bf16x8, bfr), accW[rt], 0, 0, 0);
+        }
+    }
+    __syncthreads();
+  }
+  if (DW && col < kJ) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t k = kw + 32 * rt + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (k < K) dWpart[(tb * K + k) * kJ + col] = accW[rt][r];
+      }
+  }
+}
+
+// ------------------------------------------------------------------ fp32 VALU dX / dW kernel
+template <bool ACCUM, bool HAS_G, bool DW>
+__global__ __launch_bounds__(256) void proj_bwd_dx_f32_kernel(
+    const float *__restrict__ X, const float *__restrict__ W, const float *__restrict__ dpf,
+    const float *__restrict__ Hpre, const float *__restrict__ gr, float *__restrict__ dX,
     float *__restrict__ dWpart, int64_t N, int64_t C, int64_t tbsz) {
   const int64_t K = 4 * C;
   const int64_t nkt = (K + kDxKT - 1) / kDxKT;
@@ -416,10 +679,9 @@ __global__ __launch_bounds__(256) void proj_bwd_dx_kernel(
   const int64_t tb = blockIdx.x / nkt;
   const int64_t k = kt * kDxKT + kDxK * threadIdx.x;
   const bool kv = k < K;
-  const int si = (int)(k / C);
+  const int64_t si = k / C;
   const int64_t c = k - si * C;
-  float w[kDxK][kJ];
-  float dw[kDxK][kJ];
+  float w[kDxK][kJ], dw[kDxK][kJ];
 #pragma unroll
   for (int e = 0; e < kDxK; ++e)
 #pragma unroll
@@ -429,70 +691,36 @@ __global__ __launch_bounds__(256) void proj_bwd_dx_kernel(
     }
   const int64_t t_end = min(N, (tb + 1) * tbsz);
   for (int64_t t = tb * tbsz; t < t_end; ++t) {
-    const float *rt = rec + t * kRec;
+    const float *rt = dpf + t * kDpf;
     float dp[kJ];
 #pragma unroll
     for (int j = 0; j < kJ; ++j) dp[j] = rt[j];
-    const float crms = rt[24];
-    if (kv) {
-      float xv[kDxK], o[kDxK];
-      if constexpr (sizeof(T) == 2) {
-        const uint2 w2 = *reinterpret_cast<const uint2 *>(X + t * K + k);
-        xv[0] = bf16_lo(w2.x); xv[1] = bf16_hi(w2.x); xv[2] = bf16_lo(w2.y); xv[3] = bf16_hi(w2.y);
-        if (ACCUM) {
-          const uint2 d2 = *reinterpret_cast<const uint2 *>(dX + t * K + k);
-          o[0] = bf16_lo(d2.x); o[1] = bf16_hi(d2.x); o[2] = bf16_lo(d2.y); o[3] = bf16_hi(d2.y);
-        }
-        if (HAS_G) {
-          const float hpi = Hpre[t * 4 + si];
-          const uint2 g2 = *reinterpret_cast<const uint2 *>(gr + t * C + c);
-          const float gv[4] = {bf16_lo(g2.x), bf16_hi(g2.x), bf16_lo(g2.y), bf16_hi(g2.y)};
+    const float crms = rt[kJ];
+    if (!kv) continue;
+    const float4 x4 = *reinterpret_cast<const float4 *>(X + t * K + k);
+    const float xv[kDxK] = {x4.x, x4.y, x4.z, x4.w};
+    float o[kDxK] = {0.f, 0.f, 0.f, 0.f};
+    if (ACCUM) {
+      const float4 d4 = *reinterpret_cast<const float4 *>(dX + t * K + k);
+      o[0] = d4.x; o[1] = d4.y; o[2] = d4.z; o[3] = d4.w;
+    }
+    if (HAS_G) {
+      const float hpi = Hpre[t * 4 + si];
+      const float4 g4 = *reinterpret_cast<const float4 *>(gr + t * C + c);
+      o[0] += hpi * g4.x; o[1] += hpi * g4.y; o[2] += hpi * g4.z; o[3] += hpi * g4.w;
+    }
 #pragma unroll
-          for (int e = 0; e < kDxK; ++e) o[e] = ACCUM ? o[e] + hpi * gv[e] : hpi * gv[e];
-        } else if (!ACCUM) {
+    for (int e = 0; e < kDxK; ++e) {
+      float acc = crms * xv[e];
 #pragma unroll
-          for (int e = 0; e < kDxK; ++e) o[e] = 0.f;
-        }
-      } else {
-        const float4 x4 = *reinterpret_cast<const float4 *>(X + t * K + k);
-        xv[0] = x4.x; xv[1] = x4.y; xv[2] = x4.z; xv[3] = x4.w;
-        if (ACCUM) {
-          const float4 d4 = *reinterpret_cast<const float4 *>(dX + t * K + k);
-          o[0] = d4.x; o[1] = d4.y; o[2] = d4.z; o[3] = d4.w;
-        }
-        if (HAS_G) {
-          const float hpi = Hpre[t * 4 + si];
-          const float4 g4 = *reinterpret_cast<const float4 *>(gr + t * C + c);
-          const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
-#pragma unroll
-          for (int e = 0; e < kDxK; ++e) o[e] = ACCUM ? o[e] + hpi * gv[e] : hpi * gv[e];
-        } else if (!ACCUM) {
-#pragma unroll
-          for (int e = 0; e < kDxK; ++e) o[e] = 0.f;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < kDxK; ++e) {
-        float acc = crms * xv[e];
-#pragma unroll
-        for (int j = 0; j < kJ; ++j) acc = fmaf(dp[j], w[e][j], acc);
-        o[e] += acc;
-      }
+      for (int j = 0; j < kJ; ++j) acc = fmaf(dp[j], w[e][j], acc);
+      o[e] += acc;
       if (DW) {
 #pragma unroll
-        for (int e = 0; e < kDxK; ++e)
-#pragma unroll
-          for (int j = 0; j < kJ; ++j) dw[e][j] = fmaf(xv[e], dp[j], dw[e][j]);
-      }
-      if constexpr (sizeof(T) == 2) {
-        uint2 o2;
-        o2.x = pack_bf16x2(o[0], o[1]);
-        o2.y = pack_bf16x2(o[2], o[3]);
-        *reinterpret_cast<uint2 *>(dX + t * K + k) = o2;
-      } else {
-        *reinterpret_cast<float4 *>(dX + t * K + k) = make_float4(o[0], o[1], o[2], o[3]);
+        for (int j = 0; j < kJ; ++j) dw[e][j] = fmaf(xv[e], dp[j], dw[e][j]);
       }
     }
+    *reinterpret_cast<float4 *>(dX + t * K + k) = make_float4(o[0], o[1], o[2], o[3]);
   }
   if (DW && kv) {
     float *dst = dWpart + (tb * K + k) * kJ;
@@ -516,86 +744,61 @@ __global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict_
   dW[idx] = s;
 }
 
-// d_alpha[3] and d_hbias[24]: one workgroup; thread i sums tokens i, i+256, ...
-// in order, then a fixed pairwise tree over the 256 threads.
-__global__ __launch_bounds__(256) void param_reduce_kernel(const float *__restrict__ rec,
-                                                           float *__restrict__ dalpha,
-                                                           float *__restrict__ dhbias, int64_t N) {
-  __shared__ float red[256][28];
-  float acc[27];
-#pragma unroll
-  for (int e = 0; e < 27; ++e) acc[e] = 0.f;
-  for (int64_t t = threadIdx.x; t < N; t += 256) {
-    const float *rt = rec + t * kRec;
-#pragma unroll
-    for (int j = 0; j < kJ; ++j) acc[j] += rt[32 + j];
-#pragma unroll
-    for (int s = 0; s < 3; ++s) acc[kJ + s] += rt[25 + s];
-  }
-#pragma unroll
-  for (int e = 0; e < 27; ++e) red[threadIdx.x][e] = acc[e];
-  __syncthreads();
-  for (int stride = 128; stride > 0; stride >>= 1) {
-    if (threadIdx.x < stride)
-      for (int e = 0; e < 27; ++e) red[threadIdx.x][e] += red[threadIdx.x + stride][e];
-    __syncthreads();
-  }
-  if (threadIdx.x < kJ && dhbias) dhbias[threadIdx.x] = red[0][threadIdx.x];
-  if (threadIdx.x < 3 && dalpha) dalpha[threadIdx.x] = red[0][kJ + threadIdx.x];
-}
-
-template <typename T, bool ACCUM, bool HAS_G>
-static void launch_dx(hipStream_t s, const ProjBwdArgs &a, const float *rec, float *dwp, int64_t tbsz,
-                      int64_t ntb) {
+template <bool ACCUM, bool HAS_G>
+static void launch_dx(hipStream_t s, const ProjBwdArgs &a, const BwdWs &L) {
   const int64_t K = 4 * a.C;
-  const int64_t nkt = (K + kDxKT - 1) / kDxKT;
-  const unsigned blocks = (unsigned)(nkt * ntb);
-  if (a.dW)
-    hipLaunchKernelGGL((proj_bwd_dx_kernel<T, ACCUM, HAS_G, true>), dim3(blocks), dim3(256), 0, s,
-                       (const T *)a.X, a.W, rec, a.H_pre, (const T *)a.g, (T *)a.dX, dwp, a.N, a.C, tbsz);
-  else
-    hipLaunchKernelGGL((proj_bwd_dx_kernel<T, ACCUM, HAS_G, false>), dim3(blocks), dim3(256), 0, s,
-                       (const T *)a.X, a.W, rec, a.H_pre, (const T *)a.g, (T *)a.dX, dwp, a.N, a.C, tbsz);
-}
-
-template <typename T>
-static void launch_dx_any(hipStream_t s, const ProjBwdArgs &a, const float *rec, float *dwp,
-                          int64_t tbsz, int64_t ntb) {
-  const bool hg = a.g != nullptr;
-  if (a.accumulate) {
-    if (hg) launch_dx<T, true, true>(s, a, rec, dwp, tbsz, ntb);
-    else launch_dx<T, true, false>(s, a, rec, dwp, tbsz, ntb);
+  if (a.f32) {
+    const unsigned blocks = (unsigned)(((K + kDxKT - 1) / kDxKT) * L.ntb);
+    if (a.dW)
+      hipLaunchKernelGGL((proj_bwd_dx_f32_kernel<ACCUM, HAS_G, true>), dim3(blocks), dim3(256), 0, s,
+                         (const float *)a.X, a.W, L.dpf, a.H_pre, (const float *)a.g, (float *)a.dX, L.dwpart,
+                         a.N, a.C, L.tbsz);
+    else
+      hipLaunchKernelGGL((proj_bwd_dx_f32_kernel<ACCUM, HAS_G, false>), dim3(blocks), dim3(256), 0, s,
+                         (const float *)a.X, a.W, L.dpf, a.H_pre, (const float *)a.g, (float *)a.dX, L.dwpart,
+                         a.N, a.C, L.tbsz);
   } else {
-    if (hg) launch_dx<T, false, true>(s, a, rec, dwp, tbsz, ntb);
-    else launch_dx<T, false, false>(s, a, rec, dwp, tbsz, ntb);
+    const unsigned blocks = (unsigned)(((K + kBwKT - 1) / kBwKT) * L.ntb);
+    if (a.dW)
+      hipLaunchKernelGGL((proj_bwd_mfma_kernel<ACCUM, HAS_G, true>), dim3(blocks), dim3(256), 0, s,
+                         (const bf16_t *)a.X, a.W, L.dpB, L.dpf, a.H_pre, (const bf16_t *)a.g,
+                         (bf16_t *)a.dX, L.dwpart, a.N, L.npad, a.C, L.tbsz);
+    else
+      hipLaunchKernelGGL((proj_bwd_mfma_kernel<ACCUM, HAS_G, false>), dim3(blocks), dim3(256), 0, s,
+                         (const bf16_t *)a.X, a.W, L.dpB, L.dpf, a.H_pre, (const bf16_t *)a.g,
+                         (bf16_t *)a.dX, L.dwpart, a.N, L.npad, a.C, L.tbsz);
   }
 }
 
 void launch_proj_bwd(hipStream_t s, const ProjBwdArgs &a) {
   const int64_t N = a.N, K = 4 * a.C;
-  const int64_t tbsz = bwd_token_block(N, K);
-  const int64_t ntb = (N + tbsz - 1) / tbsz;
-  char *base = (char *)a.ws;
-  float *rec = (float *)base;
-  float *dhpre_ws = (float *)(base + align256((size_t)N * kRec * 4));
-  float *dwp = (float *)(base + align256((size_t)N * kRec * 4) + align256((size_t)N * 16));
+  const BwdWs L = bwd_layout(a.ws, N, a.C, a.f32);
   const float *dHpre = a.dH_pre;
   if (a.g) {  // fused pre backward: dH_pre = g . X per stream
-    launch_h_aggregate_bwd(s, a.f32, N, a.C, a.g, a.X, a.H_pre, nullptr, false, dhpre_ws);
-    dHpre = dhpre_ws;
+    launch_h_aggregate_bwd(s, a.f32, N, a.C, a.g, a.X, a.H_pre, nullptr, false, L.dhpre);
+    dHpre = L.dhpre;
   }
-  hipLaunchKernelGGL(proj_bwd_token_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s,
-                     a.alpha, a.saved, a.H_pre, a.H_post, dHpre, a.dH_post, a.dL, a.dH_res, a.logits,
-                     a.iters, a.eps, rec, a.dL_out, a.dH_pre_out, N, K);
   if (a.f32)
-    launch_dx_any<float>(s, a, rec, dwp, tbsz, ntb);
+    hipLaunchKernelGGL((proj_bwd_token_kernel<false>), dim3((unsigned)L.nblk), dim3(256), 0, s, a.alpha, a.saved,
+                       a.H_pre, a.H_post, dHpre, a.dH_post, a.dL, a.dH_res, a.logits, a.iters, a.eps, L.dpf,
+                       L.dpB, L.ppart, a.dL_out, a.dH_pre_out, N, L.npad, K);
   else
-    launch_dx_any<bf16_t>(s, a, rec, dwp, tbsz, ntb);
+    hipLaunchKernelGGL((proj_bwd_token_kernel<true>), dim3((unsigned)L.nblk), dim3(256), 0, s, a.alpha, a.saved,
+                       a.H_pre, a.H_post, dHpre, a.dH_post, a.dL, a.dH_res, a.logits, a.iters, a.eps, L.dpf,
+                       L.dpB, L.ppart, a.dL_out, a.dH_pre_out, N, L.npad, K);
+  const bool hg = a.g != nullptr;
+  if (a.accumulate) {
+    if (hg) launch_dx<true, true>(s, a, L);
+    else launch_dx<true, false>(s, a, L);
+  } else {
+    if (hg) launch_dx<false, true>(s, a, L);
+    else launch_dx<false, false>(s, a, L);
+  }
   if (a.dW)
-    hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((K * kJ + 255) / 256)), dim3(256), 0, s, dwp,
-                       a.dW, ntb, K * kJ);
+    hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((K * kJ + 255) / 256)), dim3(256), 0, s, L.dwpart,
+                       a.dW, L.ntb, K * kJ);
   if (a.dalpha || a.dhbias)
-    hipLaunchKernelGGL(param_reduce_kernel, dim3(1), dim3(256), 0, s, rec, a.dalpha, a.dhbias, N);
+    hipLaunchKernelGGL(param_final_kernel, dim3(1), dim3(32), 0, s, L.ppart, L.nblk, a.dalpha, a.dhbias);
 }
 
 }  // namespace mhc
