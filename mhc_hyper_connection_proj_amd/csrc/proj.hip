@@ -331,8 +331,9 @@ void launch_proj_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *
 //    r = 1/eps amplifies dp to ~1e5 while dX entries cancel to O(1).
 //  * dW: bf16 MFMA.  The contraction runs over tokens, so each wave stages its 32x64 X
 //    tile in LDS and reads 8-token columns as A fragments; dp comes split
-//    exactly into hi + mid + lo bf16 terms, stored token-contiguous per (term,
-//    j) so each B fragment is one 16-byte load.
+//    exactly into hi + mid + lo bf16 terms, laid out per 32-token block as
+//    [half s][term][j][16 tokens] so the B fragment of one (s, term) is a
+//    contiguous 768-byte read across the wave.
 // fp32 activations use a VALU kernel for both contractions.
 constexpr int kDpf = 32;     // fp32 per-token record: dp[24], c_rms, pad
 constexpr int kBwKW = 64;    // k per wave in the MFMA kernel
@@ -382,6 +383,14 @@ size_t proj_bwd_ws(int64_t N, int64_t C, bool f32) {
 }
 
 __device__ __forceinline__ uint16_t bf16_bits(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+
+// dpB layout: per 32-token block, [half s (16 tokens)][term][j][16 tokens].
+// Element (t, j) of term 0; terms 1 and 2 follow at +kJ*16 and +2*kJ*16.
+__device__ __forceinline__ int64_t dpb_index(int64_t t, int j) {
+  const int64_t blk = t >> 5;
+  const int s = (int)((t >> 4) & 1), e = (int)(t & 15);
+  return blk * (2 * 3 * kJ * 16) + ((int64_t)(s * 3) * kJ + j) * 16 + e;
+}
 
 // One thread per token (grid covers npad tokens; tokens >= N only zero their
 // dpB column).  Block partial sums of dhbias (24) and dalpha (3) go to ppart.
@@ -462,14 +471,17 @@ __global__ __launch_bounds__(256) void proj_bwd_token_kernel(
       }
 #pragma unroll
       for (int j = 0; j < kJ; ++j) {
-        dpB[(0 * kJ + j) * npad + t] = hi[j];
-        dpB[(1 * kJ + j) * npad + t] = mid[j];
-        dpB[(2 * kJ + j) * npad + t] = lo[j];
+        bf16_t *blk = dpB + dpb_index(t, j);
+        blk[0 * kJ * 16] = hi[j];
+        blk[1 * kJ * 16] = mid[j];
+        blk[2 * kJ * 16] = lo[j];
       }
     }
   } else if (MFMA_OUT && t < npad) {
 #pragma unroll
-    for (int j = 0; j < 3 * kJ; ++j) dpB[(int64_t)j * npad + t] = 0;
+    for (int j = 0; j < kJ; ++j)
+#pragma unroll
+      for (int tm = 0; tm < 3; ++tm) dpB[dpb_index(t, j) + tm * kJ * 16] = 0;
   }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
@@ -498,12 +510,73 @@ __global__ void param_final_kernel(const float *__restrict__ ppart, int64_t nblk
 }
 
 // ------------------------------------------------------------------ MFMA dX / dW kernel
-// Workgroup = 4 waves, each owning 64 consecutive k; grid = k tiles x token
-// blocks.  Per 32-token sub-tile a wave: (a) 2 x 12 fp32 MFMAs give the dp W^T
-// tile (lane half h carries j = 12h .. 12h+11 of the 24-long contraction),
-// (b) stages it and its X tile in LDS, (c) writes dX row-major with 16-byte
-// accesses, (d) reads 8-token X columns from LDS as A fragments and adds
-// x^T dp into its dW accumulators (12 MFMAs).
+// Workgroup = 4 independent waves, each owning 64 consecutive k and its own
+// LDS region (wave-local synchronisation only); grid = k tiles x token blocks.
+// Per 32-token sub-tile a wave: (a) 2 x 12 fp32 MFMAs give the dp W^T tile
+// (lane half h carries j = 12h .. 12h+11 of the 24-long contraction), (b)
+// stages it and its X tile in LDS, (c) writes dX row-major with 16-byte
+// accesses, (d) reads 8-token X columns back from LDS as A fragments and adds
+// x^T dp into its dW accumulators (12 bf16 MFMAs).  Latency is hidden by
+// running 2 waves per SIMD (244 registers); double-buffering the loads in
+// registers pushed the kernel to 1 wave per SIMD and measured slower.
+struct BwdStage {
+  float af[12];        // dp[t0 + col][12h .. 12h+12)
+  u32x4 xr[4], dr[4], gg[4];  // row-major X, dX_in, g: token t0 + er + 8q, k = kw + ek .. +8
+  float hp[4], crms[4];
+  u32x4 bfr[2][3];     // dp terms for tokens t0 + 16s + 8h .. +8 at j = col
+};
+
+template <bool ACCUM, bool HAS_G, bool DW>
+__device__ __forceinline__ void bwd_load_stage(BwdStage &S, int64_t t0, const bf16_t *__restrict__ X,
+                                               const bf16_t *__restrict__ dpB, const float *__restrict__ dpf,
+                                               const float *__restrict__ Hpre, const bf16_t *__restrict__ gr,
+                                               const bf16_t *__restrict__ dX, int64_t N, int64_t npad,
+                                               int64_t C, int64_t K, int64_t kw, int col, int h, int er,
+                                               int ek) {
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+  const int64_t ta = t0 + col;
+#pragma unroll
+  for (int s4 = 0; s4 < 3; ++s4) {
+    const float4 v = ta < N ? *reinterpret_cast<const float4 *>(dpf + ta * kDpf + 12 * h + 4 * s4)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    S.af[4 * s4] = v.x; S.af[4 * s4 + 1] = v.y; S.af[4 * s4 + 2] = v.z; S.af[4 * s4 + 3] = v.w;
+  }
+  const int64_t k = kw + ek;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t tt = t0 + er + 8 * q;
+    const bool tv = tt < N;
+    S.crms[q] = tv ? dpf[tt * kDpf + kJ] : 0.f;
+    const bool v = tv && k < K;
+    S.xr[q] = v ? *reinterpret_cast<const u32x4 *>(X + tt * K + k) : z4;
+    if (ACCUM) S.dr[q] = v ? *reinterpret_cast<const u32x4 *>(dX + tt * K + k) : z4;
+    if (HAS_G) {
+      const int64_t si = k / C;
+      const int64_t c = k - si * C;
+      S.gg[q] = v ? *reinterpret_cast<const u32x4 *>(gr + tt * C + c) : z4;
+      S.hp[q] = v ? Hpre[tt * 4 + si] : 0.f;
+    }
+  }
+  if (DW) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int tm = 0; tm < 3; ++tm)
+        S.bfr[s][tm] = col < kJ
+            ? *reinterpret_cast<const u32x4 *>(dpB + (t0 >> 5) * (2 * 3 * kJ * 16) +
+                                               ((int64_t)(s * 3 + tm) * kJ + col) * 16 + 8 * h)
+            : z4;
+  }
+}
+
+// Orders this wave's LDS writes before its following LDS reads (the region
+// is private to the wave, so no workgroup barrier is needed).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <bool ACCUM, bool HAS_G, bool DW>
 __global__ __launch_bounds__(256) void proj_bwd_mfma_kernel(
     const bf16_t *__restrict__ X, const float *__restrict__ W, const bf16_t *__restrict__ dpB,
@@ -519,8 +592,12 @@ __global__ __launch_bounds__(256) void proj_bwd_mfma_kernel(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 31, h = lane >> 5;
   const int64_t kw = kt * kBwKT + wave * kBwKW;
-  const int tr = lane >> 1;             // row-major epilogue: token row
-  const int kh = (lane & 1) * 32;       // and 32-k half
+  // Row-major epilogue mapping: 8 lanes cover one token's 64 k (128 bytes),
+  // so each load/store instruction touches 8 whole 128-byte row segments.
+  const int er = lane >> 3;             // token row er + 8q, q = 0..3
+  const int ek = (lane & 7) * 8;        // k offset within the wave's 64
+  float(*acc_t)[kBwKW + 4] = lds_acc[wave];
+  bf16_t(*x_t)[kBwKW + 8] = lds_x[wave];
 
   float wf[2][12];
 #pragma unroll
@@ -541,16 +618,10 @@ __global__ __launch_bounds__(256) void proj_bwd_mfma_kernel(
 
   const int64_t t_begin = tb * tbsz;
   const int64_t t_end = min(N, t_begin + tbsz);
+  BwdStage cur;
   for (int64_t t0 = t_begin; t0 < t_end; t0 += 32) {
+    bwd_load_stage<ACCUM, HAS_G, DW>(cur, t0, X, dpB, dpf, Hpre, gr, dX, N, npad, C, K, kw, col, h, er, ek);
     // (a) dp W^T for 32 tokens x 64 k
-    const int64_t ta = t0 + col;
-    float af[12];
-#pragma unroll
-    for (int s4 = 0; s4 < 3; ++s4) {
-      const float4 v = ta < N ? *reinterpret_cast<const float4 *>(dpf + ta * kDpf + 12 * h + 4 * s4)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
-      af[4 * s4] = v.x; af[4 * s4 + 1] = v.y; af[4 * s4 + 2] = v.z; af[4 * s4 + 3] = v.w;
-    }
     f32x16 accX[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
@@ -558,60 +629,42 @@ __global__ __launch_bounds__(256) void proj_bwd_mfma_kernel(
       for (int r = 0; r < 16; ++r) accX[ct][r] = 0.f;
 #pragma unroll
       for (int s = 0; s < 12; ++s)
-        accX[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[s], wf[ct][s], accX[ct], 0, 0, 0);
+        accX[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur.af[s], wf[ct][s], accX[ct], 0, 0, 0);
     }
-    // (b) row-major loads for the epilogue: token t0 + tr, k = kw + kh + 8q
-    const int64_t tt = t0 + tr;
-    const bool tv = tt < N;
-    u32x4 xr[4], dr[4], gg[4];
-    float hp[4];
-    const float crms = tv ? dpf[tt * kDpf + kJ] : 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t k = kw + kh + 8 * q;
-      const bool v = tv && k < K;
-      xr[q] = v ? *reinterpret_cast<const u32x4 *>(X + tt * K + k) : u32x4{0u, 0u, 0u, 0u};
-      if (ACCUM) dr[q] = v ? *reinterpret_cast<const u32x4 *>(dX + tt * K + k) : u32x4{0u, 0u, 0u, 0u};
-      if (HAS_G) {
-        const int64_t si = k / C;
-        const int64_t c = k - si * C;
-        gg[q] = v ? *reinterpret_cast<const u32x4 *>(gr + tt * C + c) : u32x4{0u, 0u, 0u, 0u};
-        hp[q] = v ? Hpre[tt * 4 + si] : 0.f;
-      }
-    }
-    // (c) stage the accumulator tile and the X tile
+    // (b) stage the accumulator tile and the X tile
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) lds_acc[wave][8 * (r >> 2) + 4 * h + (r & 3)][32 * ct + col] = accX[ct][r];
+      for (int r = 0; r < 16; ++r) acc_t[8 * (r >> 2) + 4 * h + (r & 3)][32 * ct + col] = accX[ct][r];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4 *>(&lds_x[wave][tr][kh + 8 * q]) = xr[q];
-    __syncthreads();
-    // (d) dX = base + dp W^T, row-major 16-byte stores
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4 *>(&x_t[er + 8 * q][ek]) = cur.xr[q];
+    wave_lds_sync();
+    // (c) dX = base + dp W^T, row-major 16-byte stores
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int64_t k = kw + kh + 8 * q;
-      if (!(tv && k < K)) continue;
-      const float4 a0 = *reinterpret_cast<const float4 *>(&lds_acc[wave][tr][kh + 8 * q]);
-      const float4 a1 = *reinterpret_cast<const float4 *>(&lds_acc[wave][tr][kh + 8 * q + 4]);
+      const int64_t tt = t0 + er + 8 * q;
+      const int64_t k = kw + ek;
+      if (!(tt < N && k < K)) continue;
+      const float4 a0 = *reinterpret_cast<const float4 *>(&acc_t[er + 8 * q][ek]);
+      const float4 a1 = *reinterpret_cast<const float4 *>(&acc_t[er + 8 * q][ek + 4]);
       const float acc8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      const uint32_t xw[4] = {xr[q].x, xr[q].y, xr[q].z, xr[q].w};
+      const uint32_t xw[4] = {cur.xr[q].x, cur.xr[q].y, cur.xr[q].z, cur.xr[q].w};
       float o[8];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        o[2 * p] = acc8[2 * p] + crms * bf16_lo(xw[p]);
-        o[2 * p + 1] = acc8[2 * p + 1] + crms * bf16_hi(xw[p]);
+        o[2 * p] = acc8[2 * p] + cur.crms[q] * bf16_lo(xw[p]);
+        o[2 * p + 1] = acc8[2 * p + 1] + cur.crms[q] * bf16_hi(xw[p]);
       }
       if (HAS_G) {
-        const uint32_t gw[4] = {gg[q].x, gg[q].y, gg[q].z, gg[q].w};
+        const uint32_t gw[4] = {cur.gg[q].x, cur.gg[q].y, cur.gg[q].z, cur.gg[q].w};
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          o[2 * p] += hp[q] * bf16_lo(gw[p]);
-          o[2 * p + 1] += hp[q] * bf16_hi(gw[p]);
+          o[2 * p] += cur.hp[q] * bf16_lo(gw[p]);
+          o[2 * p + 1] += cur.hp[q] * bf16_hi(gw[p]);
         }
       }
       if (ACCUM) {
-        const uint32_t dw4[4] = {dr[q].x, dr[q].y, dr[q].z, dr[q].w};
+        const uint32_t dw4[4] = {cur.dr[q].x, cur.dr[q].y, cur.dr[q].z, cur.dr[q].w};
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           o[2 * p] += bf16_lo(dw4[p]);
@@ -625,7 +678,7 @@ __global__ __launch_bounds__(256) void proj_bwd_mfma_kernel(
       ow.w = pack_bf16x2(o[6], o[7]);
       *reinterpret_cast<uint4 *>(dX + tt * K + k) = ow;
     }
-    // (e) dW += X^T dp over these 32 tokens
+    // (d) dW += X^T dp over these 32 tokens
     if (DW) {
       u32x4 xa[2][2];
 #pragma unroll
@@ -635,8 +688,8 @@ __global__ __launch_bounds__(256) void proj_bwd_mfma_kernel(
           uint32_t w4[4];
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
-            const uint32_t lo16 = lds_x[wave][16 * s + 8 * h + 2 * p][32 * rt + col];
-            const uint32_t hi16 = lds_x[wave][16 * s + 8 * h + 2 * p + 1][32 * rt + col];
+            const uint32_t lo16 = x_t[16 * s + 8 * h + 2 * p][32 * rt + col];
+            const uint32_t hi16 = x_t[16 * s + 8 * h + 2 * p + 1][32 * rt + col];
             w4[p] = lo16 | (hi16 << 16);
           }
           xa[rt][s] = u32x4{w4[0], w4[1], w4[2], w4[3]};
@@ -644,17 +697,14 @@ __global__ __launch_bounds__(256) void proj_bwd_mfma_kernel(
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int tm = 0; tm < 3; ++tm) {
-          const u32x4 bfr = col < kJ
-              ? *reinterpret_cast<const u32x4 *>(dpB + (int64_t)(tm * kJ + col) * npad + t0 + 16 * s + 8 * h)
-              : u32x4{0u, 0u, 0u, 0u};
+        for (int tm = 0; tm < 3; ++tm)
 #pragma unroll
           for (int rt = 0; rt < 2; ++rt)
             accW[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa[rt][s]),
-                                                               __builtin_bit_cast(bf16x8, bfr), accW[rt], 0, 0, 0);
-        }
+                                                               __builtin_bit_cast(bf16x8, cur.bfr[s][tm]),
+                                                               accW[rt], 0, 0, 0);
     }
-    __syncthreads();
+    wave_lds_sync();  // LDS reads of this sub-tile precede the next sub-tile's writes
   }
   if (DW && col < kJ) {
 #pragma unroll
