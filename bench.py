@@ -199,13 +199,16 @@ def main():
     k_ms = mean["post_bwd"]
     k_bytes = led["post_bwd"] * N
     k_gbs = k_bytes / (k_ms * 1e-3) / 1e9
+    # HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    # summary, reported only while the kernel's sources are the ones measured
     traffic = None
-    pmc = os.path.join(ROOT, "profiles", "h_post_bda_bwd_full_layer_pmc.json")
+    pmc = os.path.join(ROOT, "profiles", "h_post_bda_bwd_full_layer_pmc.txt")
     if os.path.exists(pmc):
-        rec = json.load(open(pmc))
+        rec = dict(line.split(" = ", 1) for line in open(pmc).read().splitlines()
+                   if " = " in line and not line.startswith("#"))
         if rec.get("src_hash") == src_hash(["mhc_hyper_connection_proj_amd/csrc/streams.hip",
                                             "mhc_hyper_connection_proj_amd/csrc/device.h"]):
-            traffic = rec.get("hbm_bytes_per_launch")
+            traffic = float(rec["hbm_bytes_per_launch"])
 
     res = {
         "metric": METRIC,

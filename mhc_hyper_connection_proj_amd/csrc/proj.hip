@@ -495,17 +495,24 @@ __global__ __launch_bounds__(256) void proj_bwd_token_kernel(
         (red[0][threadIdx.x] + red[1][threadIdx.x]) + (red[2][threadIdx.x] + red[3][threadIdx.x]);
 }
 
-// dhbias / dalpha: sum of the per-block partials in block order.
-__global__ void param_final_kernel(const float *__restrict__ ppart, int64_t nblk,
-                                   float *__restrict__ dalpha, float *__restrict__ dhbias) {
-  const int e = threadIdx.x;
-  if (e >= 27) return;
+// dhbias / dalpha: 8 lanes per value stride the per-block partials, then the 8
+// partial sums are added in a fixed tree (deterministic).
+__global__ __launch_bounds__(256) void param_final_kernel(const float *__restrict__ ppart, int64_t nblk,
+                                                          float *__restrict__ dalpha,
+                                                          float *__restrict__ dhbias) {
+  __shared__ float red[8][32];
+  const int e = threadIdx.x & 31, part = threadIdx.x >> 5;
   float s = 0.f;
-  for (int64_t b = 0; b < nblk; ++b) s += ppart[b * 32 + e];
+  for (int64_t b = part; b < nblk; b += 8) s += ppart[b * 32 + e];
+  red[part][e] = s;
+  __syncthreads();
+  if (threadIdx.x >= 27) return;
+  const float tot = ((red[0][e] + red[1][e]) + (red[2][e] + red[3][e])) +
+                    ((red[4][e] + red[5][e]) + (red[6][e] + red[7][e]));
   if (e < kJ) {
-    if (dhbias) dhbias[e] = s;
+    if (dhbias) dhbias[e] = tot;
   } else if (dalpha) {
-    dalpha[e - kJ] = s;
+    dalpha[e - kJ] = tot;
   }
 }
 
@@ -518,7 +525,10 @@ __global__ void param_final_kernel(const float *__restrict__ ppart, int64_t nblk
 // accesses, (d) reads 8-token X columns back from LDS as A fragments and adds
 // x^T dp into its dW accumulators (12 bf16 MFMAs).  Latency is hidden by
 // running 2 waves per SIMD (244 registers); double-buffering the loads in
-// registers pushed the kernel to 1 wave per SIMD and measured slower.
+// registers pushed the kernel to 1 wave per SIMD and measured slower.  The
+// waves are independent (no workgroup barrier): staging g and the dp
+// fragments once per workgroup for all four streams removed g's re-reads
+// (~420 MiB at C=7168) but the per-sub-tile barrier cost more than it saved.
 struct BwdStage {
   float af[12];        // dp[t0 + col][12h .. 12h+12)
   u32x4 xr[4], dr[4], gg[4];  // row-major X, dX_in, g: token t0 + er + 8q, k = kw + ek .. +8
@@ -588,7 +598,9 @@ __global__ __launch_bounds__(256) void proj_bwd_mfma_kernel(
   const int64_t K = 4 * C;
   const int64_t nkt = (K + kBwKT - 1) / kBwKT;
   const int64_t kt = blockIdx.x % nkt;
-  const int64_t tb = blockIdx.x / nkt;
+  // token blocks from the last down: the preceding dH_pre pass read X and g
+  // in token order, so the first blocks here still sit in the Infinity Cache
+  const int64_t tb = (int64_t)gridDim.x / nkt - 1 - blockIdx.x / nkt;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 31, h = lane >> 5;
   const int64_t kw = kt * kBwKT + wave * kBwKW;
@@ -848,7 +860,7 @@ void launch_proj_bwd(hipStream_t s, const ProjBwdArgs &a) {
     hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((K * kJ + 255) / 256)), dim3(256), 0, s, L.dwpart,
                        a.dW, L.ntb, K * kJ);
   if (a.dalpha || a.dhbias)
-    hipLaunchKernelGGL(param_final_kernel, dim3(1), dim3(32), 0, s, L.ppart, L.nblk, a.dalpha, a.dhbias);
+    hipLaunchKernelGGL(param_final_kernel, dim3(1), dim3(256), 0, s, L.ppart, L.nblk, a.dalpha, a.dhbias);
 }
 
 }  // namespace mhc

@@ -10,6 +10,11 @@
 // (scalar loads).  Per-token reductions over C go lane -> wave (DPP) ->
 // workgroup (LDS, fixed wave order); cross-token sums (dbias) go through
 // per-workgroup partials reduced in a fixed order by a second kernel.
+//
+// Token order: the kernels that follow a full pass over X walk the tokens in
+// the opposite direction of that pass (h_aggregate forward and h_post_bda
+// backward run from the last token down), so their first reads hit the
+// data the previous kernel left in the 256 MB Infinity Cache.
 #include "device.h"
 #include "internal.h"
 
@@ -28,7 +33,7 @@ template <typename T, int GPT>
 __global__ __launch_bounds__(256) void h_aggregate_fwd_kernel(const T *__restrict__ X,
                                                                const float *__restrict__ Hpre,
                                                                T *__restrict__ out, int64_t C) {
-  const int64_t t = blockIdx.x;
+  const int64_t t = (int64_t)gridDim.x - 1 - blockIdx.x;  // last token first
   const int G = (int)(C / 8);
   const float h0 = Hpre[t * 4 + 0], h1 = Hpre[t * 4 + 1], h2 = Hpre[t * 4 + 2], h3 = Hpre[t * 4 + 3];
   const T *xt = X + t * 4 * C;
@@ -180,7 +185,7 @@ __global__ __launch_bounds__(256) void h_post_bda_bwd_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) dbp[j][e] = 0.f;
   }
-  const int64_t t0 = (int64_t)blockIdx.x * TG;
+  const int64_t t0 = ((int64_t)gridDim.x - 1 - blockIdx.x) * TG;  // last tokens first
   const int ntok = (int)min((int64_t)TG, N - t0);
   for (int tt = 0; tt < ntok; ++tt) {
     const int64_t t = t0 + tt;
@@ -274,7 +279,7 @@ __global__ __launch_bounds__(256) void h_post_bda_bwd_kernel(
     for (int j = 0; j < GPT; ++j) {
       const int g = threadIdx.x + j * blockDim.x;
       if (g < G) {
-        float *p = dbias_part + (int64_t)blockIdx.x * C + 8 * g;
+        float *p = dbias_part + (t0 / TG) * C + 8 * g;
         *reinterpret_cast<float4 *>(p) = make_float4(dbp[j][0], dbp[j][1], dbp[j][2], dbp[j][3]);
         *reinterpret_cast<float4 *>(p + 4) = make_float4(dbp[j][4], dbp[j][5], dbp[j][6], dbp[j][7]);
       }
