@@ -40,9 +40,11 @@ typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 static inline int64_t kpad64(int64_t K) { return (K + 63) / 64 * 64; }
 
+constexpr int kWcol = 32;  // bf16 packed W: 24 columns padded to the MFMA's 32
+
 static inline size_t wpack_bytes(int64_t C, bool f32) {
   const int64_t Kp = kpad64(4 * C);
-  return (size_t)(f32 ? Kp * kJ * 4 : Kp * kJ * 3 * 2);
+  return (size_t)(f32 ? Kp * kJ * 4 : Kp * kWcol * 3 * 2);
 }
 
 static inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
@@ -52,7 +54,8 @@ size_t proj_fwd_ws(int64_t N, int64_t C, bool f32) {
 }
 
 // ------------------------------------------------------------------ W pack
-// bf16: Wp[kg][term][j][8] (kg = k/8), term 0,1,2 = hi, mid, lo.
+// bf16: Wp[kg][term][32][8] (kg = k/8), term 0,1,2 = hi, mid, lo; columns
+// 24..31 are zero so a 64-k chunk is one contiguous 12 KB block.
 // fp32: Wf[kg][j][8].  Rows k >= K (padding to a multiple of 64) are zero.
 __device__ __forceinline__ float bf16_round(float v) {
   const __bf16 h = (__bf16)v;
@@ -62,11 +65,12 @@ __device__ __forceinline__ float bf16_round(float v) {
 template <bool F32>
 __global__ __launch_bounds__(256) void pack_w_kernel(const float *__restrict__ W, void *__restrict__ out,
                                                      int64_t K, int64_t Kp) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over Kp * 24
-  if (idx >= Kp * kJ) return;
-  const int64_t k = idx / kJ;
-  const int j = (int)(idx % kJ);
-  const float w = k < K ? W[k * kJ + j] : 0.f;
+  const int ncol = F32 ? kJ : kWcol;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over Kp * ncol
+  if (idx >= Kp * ncol) return;
+  const int64_t k = idx / ncol;
+  const int j = (int)(idx % ncol);
+  const float w = (k < K && j < kJ) ? W[k * kJ + j] : 0.f;
   const int64_t kg = k >> 3;
   const int e = (int)(k & 7);
   if (F32) {
@@ -77,19 +81,18 @@ __global__ __launch_bounds__(256) void pack_w_kernel(const float *__restrict__ W
     const float mid = bf16_round(r1);
     const float lo = bf16_round(r1 - mid);
     bf16_t *o = reinterpret_cast<bf16_t *>(out);
-    o[((kg * 3 + 0) * kJ + j) * 8 + e] = __builtin_bit_cast(uint16_t, (__bf16)hi);
-    o[((kg * 3 + 1) * kJ + j) * 8 + e] = __builtin_bit_cast(uint16_t, (__bf16)mid);
-    o[((kg * 3 + 2) * kJ + j) * 8 + e] = __builtin_bit_cast(uint16_t, (__bf16)lo);
+    o[((kg * 3 + 0) * kWcol + j) * 8 + e] = __builtin_bit_cast(uint16_t, (__bf16)hi);
+    o[((kg * 3 + 1) * kWcol + j) * 8 + e] = __builtin_bit_cast(uint16_t, (__bf16)mid);
+    o[((kg * 3 + 2) * kWcol + j) * 8 + e] = __builtin_bit_cast(uint16_t, (__bf16)lo);
   }
 }
 
 // ------------------------------------------------------------------ partial projection
-// Grid: ceil(N / kTB) * kSplitK workgroups of 256 threads; workgroup b handles
+// fp32 activations.  Grid: ceil(N / kTB) * kSplitK workgroups of 256 threads; workgroup b handles
 // token block b / kSplitK and k slice b % kSplitK.  Wave w takes the slice's
 // 64-k chunks w, w+4, ...  Output: part[slice][t][0..24) = partial x @ W,
 // part[slice][t][24] = partial sum x^2.
-template <bool F32>
-__global__ __launch_bounds__(256) void proj_partial_kernel(const void *__restrict__ Xv,
+__global__ __launch_bounds__(256) void proj_partial_f32_kernel(const void *__restrict__ Xv,
                                                            const void *__restrict__ Wpk,
                                                            float *__restrict__ part, int64_t N,
                                                            int64_t K) {
@@ -129,52 +132,7 @@ __global__ __launch_bounds__(256) void proj_partial_kernel(const void *__restric
     for (int u = 0; u < kTPW; ++u)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[u][r] = 0.f;
-    if constexpr (!F32) {
-      const bf16_t *X = reinterpret_cast<const bf16_t *>(Xv);
-      const bf16_t *Wp = reinterpret_cast<const bf16_t *>(Wpk);
-      u32x4 a[kTPW][4];
-#pragma unroll
-      for (int u = 0; u < kTPW; ++u) {
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(X + trow[u] * K + k0 + 32 * h);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) a[u][m] = (tvalid[u] && kvalid) ? src[m] : u32x4{0u, 0u, 0u, 0u};
-      }
-      u32x4 b[4][3];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int64_t kg = k0 / 8 + 4 * h + m;
-#pragma unroll
-        for (int tm = 0; tm < 3; ++tm)
-          b[m][tm] = bcol ? *reinterpret_cast<const u32x4 *>(Wp + ((kg * 3 + tm) * kJ + row) * 8)
-                          : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int tm = 0; tm < 3; ++tm)
-#pragma unroll
-          for (int u = 0; u < kTPW; ++u)
-            acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, a[u][m]), __builtin_bit_cast(bf16x8, b[m][tm]), acc[u], 0, 0, 0);
-      // sum of squares of this lane's 32 elements of each token row.  The
-      // dwords are pulled out by name: bit-casting an indexed ext-vector
-      // element (a[u][m][q]) makes hipcc reuse dword 0 for every q.
-#pragma unroll
-      for (int u = 0; u < kTPW; ++u) {
-        float s = 0.f;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const unsigned w4[4] = {a[u][m].x, a[u][m].y, a[u][m].z, a[u][m].w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-            const bf16x2 v = __builtin_bit_cast(bf16x2, w4[q]);
-            s = __builtin_amdgcn_fdot2_f32_bf16(v, v, s, false);
-          }
-        }
-        ss[u] += s;
-      }
-    } else {
+    {
       const float *X = reinterpret_cast<const float *>(Xv);
       const float *Wf = reinterpret_cast<const float *>(Wpk);
       float a[kTPW][32];
@@ -241,6 +199,152 @@ __global__ __launch_bounds__(256) void proj_partial_kernel(const void *__restric
   }
 }
 
+// ------------------------------------------------------------------ partial projection, bf16 (LDS-staged)
+// Workgroup = 8 waves x 32 tokens (256 tokens) on one k slice (slice =
+// workgroup % 8, one per XCD).  The k range is walked in 64-k chunks through a
+// 3-stage LDS ring filled with global_load_lds_dwordx4 (each instruction moves
+// 1 KB: 64 lanes x 16 bytes land at consecutive LDS addresses):
+//  * the W chunk (12 KB: 8 k-groups x 3 terms x 32 columns x 8) is shared by
+//    all waves; waves 0..5 load 2 KB of it each;
+//  * each wave loads its own 32 x 64 X tile (4 KB, 8 lanes per 128-byte row
+//    segment, so every instruction reads whole cache lines).  Row r's 16-byte
+//    piece p is stored in slot p ^ (r & 7) of its LDS row, which spreads the
+//    column reads of the MFMA fragments over the banks.
+// Two chunks are in flight while one is computed.  Each wave waits for its
+// own loads (s_waitcnt vmcnt), then one workgroup barrier makes every wave's
+// loads visible and guarantees the slot refilled next was read by everyone.
+// A wave owns its 32 tokens over the whole slice, so its accumulators are
+// the workgroup's output (no cross-wave reduction).
+constexpr int kDmaWaves = 8;
+constexpr int kDmaTok = 32 * kDmaWaves;      // 256 tokens per workgroup
+constexpr int kDmaStages = 3;
+constexpr int kWChunk = 8 * 3 * kWcol * 8;   // bf16 elements per 64-k W chunk (12 KB)
+constexpr int kXTile = 32 * 64;              // bf16 elements per wave X tile (4 KB)
+constexpr int kStageElems = kWChunk + kDmaWaves * kXTile;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ void dma16(const void *g, bf16_t *lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds_base, 16, 0, 0);
+}
+
+// s_waitcnt with vmcnt <= n (expcnt and lgkmcnt left unconstrained).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__global__ __launch_bounds__(512) void proj_partial_dma_kernel(const bf16_t *__restrict__ X,
+                                                               const bf16_t *__restrict__ Wp,
+                                                               float *__restrict__ part, int64_t N,
+                                                               int64_t K) {
+  extern __shared__ __attribute__((aligned(16))) bf16_t ring[];  // kDmaStages * kStageElems
+  const int slice = blockIdx.x % kSplitK;
+  const int64_t tb = blockIdx.x / kSplitK;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = lane & 31, h = lane >> 5;
+  const int64_t nch = (K + 63) / 64;
+  const int64_t cps = (nch + kSplitK - 1) / kSplitK;
+  const int64_t c_begin = min(nch, slice * cps);
+  const int nc = (int)(min(nch, c_begin + cps) - c_begin);
+  const int64_t tw = tb * kDmaTok + 32 * wave;  // this wave's first token
+
+  // issue the loads of chunk index i (0-based within the slice) into its slot
+  auto issue = [&](int i) {
+    bf16_t *st = ring + (i % kDmaStages) * kStageElems;
+    const int64_t k0 = (c_begin + i) * 64;
+    if (wave < 6) {
+      const bf16_t *wsrc = Wp + (k0 / 8) * 3 * kWcol * 8;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int blk = 2 * wave + q;  // 1 KB blocks of the chunk
+        dma16(wsrc + blk * 512 + lane * 8, st + blk * 512);
+      }
+    }
+    bf16_t *xs = st + kWChunk + wave * kXTile;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rr = 8 * q + (lane >> 3);                 // row within the wave's 32
+      const int p = (lane & 7) ^ (rr & 7);                // global 16-byte piece for this slot
+      const int64_t t = min(tw + rr, N - 1);              // rows past N re-read row N-1 (never stored)
+      int64_t k = k0 + 8 * p;
+      if (k >= K) k -= 32;                                // past K: any valid address (W rows there are 0)
+      dma16(X + t * K + k, xs + q * 512);
+    }
+  };
+
+  f32x16 outer;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) outer[r] = 0.f;
+  float ss = 0.f;
+  if (nc > 0) issue(0);
+  if (nc > 1) issue(1);
+  for (int i = 0; i < nc; ++i) {
+    // this wave's loads of chunk i are complete once at most those of chunk
+    // i+1 remain outstanding
+    if (i + 1 < nc) {
+      if (wave < 6) wait_vmcnt<6>(); else wait_vmcnt<4>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    // a bare barrier: __syncthreads' fence would also wait for the chunk
+    // still in flight.  The memory clobber keeps LDS reads below it.
+    asm volatile("s_barrier" ::: "memory");
+    if (i + 2 < nc) issue(i + 2);  // slot (i+2) % 3 was last read in iteration i-1
+    const bf16_t *st = ring + (i % kDmaStages) * kStageElems;
+    const bf16_t *xs = st + kWChunk + wave * kXTile;
+    const int64_t k0 = (c_begin + i) * 64;
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    u32x4 a[4], b[4][3];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int P = 4 * h + m;  // this lane's 16-byte piece (k = k0 + 8P .. +8)
+      a[m] = *reinterpret_cast<const u32x4 *>(xs + row * 64 + 8 * (P ^ (row & 7)));
+#pragma unroll
+      for (int tm = 0; tm < 3; ++tm)
+        b[m][tm] = *reinterpret_cast<const u32x4 *>(st + ((P * 3 + tm) * kWcol + row) * 8);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int tm = 0; tm < 3; ++tm)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[m]),
+                                                      __builtin_bit_cast(bf16x8, b[m][tm]), acc, 0, 0, 0);
+    // sum of squares of this lane's 32 elements of its row.  The dwords are
+    // pulled out by name: bit-casting an indexed ext-vector element (a[m][q])
+    // makes hipcc reuse dword 0 for every q.
+    float s = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      if (k0 + 8 * (4 * h + m) < K) {
+        const unsigned w4[4] = {a[m].x, a[m].y, a[m].z, a[m].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+          const bf16x2 v = __builtin_bit_cast(bf16x2, w4[q]);
+          s = __builtin_amdgcn_fdot2_f32_bf16(v, v, s, false);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) outer[r] += acc[r];
+    ss += s;
+  }
+  // sum of squares: the two lane halves hold the two 32-k halves of each row
+  ss += __shfl_xor(ss, 32);
+  if (row < kJ) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t t = tw + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (t < N) part[((int64_t)slice * N + t) * kPartStride + row] = outer[r];
+    }
+  }
+  if (h == 0 && tw + row < N) part[((int64_t)slice * N + tw + row) * kPartStride + kJ] = ss;
+}
+
 // ------------------------------------------------------------------ finalize
 // One thread per token: fixed-order sum of the kSplitK partials, RMS,
 // compute_h, and (when H_res != NULL) the Sinkhorn projection of the logits.
@@ -305,14 +409,18 @@ void launch_proj_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *
   char *base = (char *)ws;
   void *wpk = base;
   float *part = (float *)(base + align256(wpack_bytes(C, f32)));
-  const unsigned pack_blocks = (unsigned)((Kp * kJ + 255) / 256);
-  const unsigned pblocks = (unsigned)(((N + kTB - 1) / kTB) * kSplitK);
   if (f32) {
+    const unsigned pack_blocks = (unsigned)((Kp * kJ + 255) / 256);
+    const unsigned pblocks = (unsigned)(((N + kTB - 1) / kTB) * kSplitK);
     hipLaunchKernelGGL((pack_w_kernel<true>), dim3(pack_blocks), dim3(256), 0, s, W, wpk, K, Kp);
-    hipLaunchKernelGGL((proj_partial_kernel<true>), dim3(pblocks), dim3(256), 0, s, X, wpk, part, N, K);
+    hipLaunchKernelGGL(proj_partial_f32_kernel, dim3(pblocks), dim3(256), 0, s, X, wpk, part, N, K);
   } else {
+    const unsigned pack_blocks = (unsigned)((Kp * kWcol + 255) / 256);
+    const unsigned pblocks = (unsigned)(((N + kDmaTok - 1) / kDmaTok) * kSplitK);
+    const size_t lds = (size_t)kDmaStages * kStageElems * sizeof(bf16_t);
     hipLaunchKernelGGL((pack_w_kernel<false>), dim3(pack_blocks), dim3(256), 0, s, W, wpk, K, Kp);
-    hipLaunchKernelGGL((proj_partial_kernel<false>), dim3(pblocks), dim3(256), 0, s, X, wpk, part, N, K);
+    hipLaunchKernelGGL(proj_partial_dma_kernel, dim3(pblocks), dim3(kDmaWaves * 64), lds, s,
+                       (const bf16_t *)X, (const bf16_t *)wpk, part, N, K);
   }
   hipLaunchKernelGGL(proj_finalize_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, part,
                      alpha, hbias, rms_eps, H_pre, H_post, logits, saved, H_res, iters, eps, N, K);
