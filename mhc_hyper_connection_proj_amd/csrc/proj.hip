@@ -224,7 +224,7 @@ constexpr int kStageElems = kWChunk + kDmaWaves * kXTile;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-__device__ __forceinline__ void dma16(const void *g, bf16_t *lds_base) {
+__device__ __forceinline__ void dma16(const void *g, void *lds_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds_base, 16, 0, 0);
 }
 
@@ -625,67 +625,67 @@ __global__ __launch_bounds__(256) void param_final_kernel(const float *__restric
 }
 
 // ------------------------------------------------------------------ MFMA dX / dW kernel
-// Workgroup = 4 independent waves, each owning 64 consecutive k and its own
-// LDS region (wave-local synchronisation only); grid = k tiles x token blocks.
-// Per 32-token sub-tile a wave: (a) 2 x 12 fp32 MFMAs give the dp W^T tile
-// (lane half h carries j = 12h .. 12h+11 of the 24-long contraction), (b)
-// stages it and its X tile in LDS, (c) writes dX row-major with 16-byte
-// accesses, (d) reads 8-token X columns back from LDS as A fragments and adds
-// x^T dp into its dW accumulators (12 bf16 MFMAs).  Latency is hidden by
-// running 2 waves per SIMD (244 registers); double-buffering the loads in
-// registers pushed the kernel to 1 wave per SIMD and measured slower.  The
-// waves are independent (no workgroup barrier): staging g and the dp
-// fragments once per workgroup for all four streams removed g's re-reads
-// (~420 MiB at C=7168) but the per-sub-tile barrier cost more than it saved.
-struct BwdStage {
-  float af[12];        // dp[t0 + col][12h .. 12h+12)
-  u32x4 xr[4], dr[4], gg[4];  // row-major X, dX_in, g: token t0 + er + 8q, k = kw + ek .. +8
-  float hp[4], crms[4];
-  u32x4 bfr[2][3];     // dp terms for tokens t0 + 16s + 8h .. +8 at j = col
+// Workgroup = 8 waves on one token block and one k tile of four 64-k quarters,
+// walked in 32-token sub-tiles through a 3-stage LDS ring:
+//  * waves 4..7 (loaders) fill each stage with global_load_lds_dwordx4: the X
+//    tile, the g tile, the fp32 dp rows and the bf16 dp terms of the
+//    sub-tile, two sub-tiles ahead.  With dW they then run x^T dp on MFMA
+//    (loader w-4 owns quarter w-4; A fragments are 8-token X columns read
+//    from LDS, B fragments the dp terms);
+//  * waves 0..3 own one quarter each: dp W^T on fp32 MFMA (W held in
+//    registers), the accumulator tile transposed through a private LDS
+//    area, then the dX epilogue with dX_in loaded one sub-tile ahead into
+//    registers.
+// One barrier per sub-tile: loaders first wait for their own loads of the
+// sub-tile (s_waitcnt vmcnt), so the barrier both publishes the stage and
+// guarantees that the slot refilled next has been read by every wave.  The
+// loaders issue no other global memory instructions inside the loop, which
+// keeps their vmcnt arithmetic exact.
+// In every 128-byte LDS row (64 bf16 of X or g, 32 fp32 of dp) the 16-byte
+// piece p of row r sits in slot p ^ (r & 7): the DMA lanes of an instruction
+// cover 8 rows x 8 slots, and the row-wise and column-wise reads below spread
+// over all banks.
+// Channel tiles: SPW = one 64-channel range c0 for all 4 streams (quarter i =
+// stream i; the g tile is 32 x 64 and shared), else 256 consecutive k (g
+// pieces addressed per piece; when C is a multiple of 256 the four tiles
+// that read the same g tile run back to back on one XCD).
+constexpr int kB2Stages = 3;
+constexpr bool kB2Spw = false;  // channel tiling (see above)
+constexpr int kB2Quarter = 32 * 128;  // bytes of one 32 x 64 bf16 tile
+
+template <bool HAS_G, bool DW, bool SPW>
+struct B2Lay {
+  static constexpr int X = 0;
+  static constexpr int G = 4 * kB2Quarter;
+  static constexpr int P = G + (HAS_G ? (SPW ? 1 : 4) * kB2Quarter : 0);
+  static constexpr int B = P + 32 * kDpf * 4;
+  static constexpr int stage = B + (DW ? 2 * 3 * kJ * 16 * 2 : 0);
+  static constexpr int acc = kB2Stages * stage;
+  static constexpr int acc_row = kBwKW + 4;  // floats per row of a wave's accumulator tile
+  static constexpr int total = acc + 4 * 32 * acc_row * 4;
 };
 
-template <bool ACCUM, bool HAS_G, bool DW>
-__device__ __forceinline__ void bwd_load_stage(BwdStage &S, int64_t t0, const bf16_t *__restrict__ X,
-                                               const bf16_t *__restrict__ dpB, const float *__restrict__ dpf,
-                                               const float *__restrict__ Hpre, const bf16_t *__restrict__ gr,
-                                               const bf16_t *__restrict__ dX, int64_t N, int64_t npad,
-                                               int64_t C, int64_t K, int64_t kw, int col, int h, int er,
-                                               int ek) {
-  const u32x4 z4 = {0u, 0u, 0u, 0u};
-  const int64_t ta = t0 + col;
-#pragma unroll
-  for (int s4 = 0; s4 < 3; ++s4) {
-    const float4 v = ta < N ? *reinterpret_cast<const float4 *>(dpf + ta * kDpf + 12 * h + 4 * s4)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
-    S.af[4 * s4] = v.x; S.af[4 * s4 + 1] = v.y; S.af[4 * s4 + 2] = v.z; S.af[4 * s4 + 3] = v.w;
-  }
-  const int64_t k = kw + ek;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int64_t tt = t0 + er + 8 * q;
-    const bool tv = tt < N;
-    S.crms[q] = tv ? dpf[tt * kDpf + kJ] : 0.f;
-    const bool v = tv && k < K;
-    S.xr[q] = v ? *reinterpret_cast<const u32x4 *>(X + tt * K + k) : z4;
-    if (ACCUM) S.dr[q] = v ? *reinterpret_cast<const u32x4 *>(dX + tt * K + k) : z4;
-    if (HAS_G) {
-      const int64_t si = k / C;
-      const int64_t c = k - si * C;
-      S.gg[q] = v ? *reinterpret_cast<const u32x4 *>(gr + tt * C + c) : z4;
-      S.hp[q] = v ? Hpre[tt * 4 + si] : 0.f;
-    }
-  }
-  if (DW) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int tm = 0; tm < 3; ++tm)
-        S.bfr[s][tm] = col < kJ
-            ? *reinterpret_cast<const u32x4 *>(dpB + (t0 >> 5) * (2 * 3 * kJ * 16) +
-                                               ((int64_t)(s * 3 + tm) * kJ + col) * 16 + 8 * h)
-            : z4;
+// vmcnt <= n for a wave-uniform n; a value outside the table waits for all.
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  switch (n) {
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    default: wait_vmcnt<0>(); break;
   }
 }
+
+// LDS reads done, then a workgroup barrier.  The memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Orders this wave's LDS writes before its following LDS reads (the region
 // is private to the wave, so no workgroup barrier is needed).
@@ -695,144 +695,270 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <bool ACCUM, bool HAS_G, bool DW>
-__global__ __launch_bounds__(256) void proj_bwd_mfma_kernel(
+// dX_in and H_pre of one sub-tile for a dX lane (rows er + 8q)
+struct DxPre {
+  u32x4 d[4];
+  float hp[4];
+};
+
+template <bool ACCUM, bool HAS_G, bool DW, bool SPW>
+__global__ __launch_bounds__(512) void proj_bwd_mfma_kernel(
     const bf16_t *__restrict__ X, const float *__restrict__ W, const bf16_t *__restrict__ dpB,
-    const float *__restrict__ dpf, const float *__restrict__ Hpre,
-    const bf16_t *__restrict__ gr, bf16_t *__restrict__ dX, float *__restrict__ dWpart, int64_t N,
-    int64_t npad, int64_t C, int64_t tbsz) {
-  __shared__ __attribute__((aligned(16))) float lds_acc[4][32][kBwKW + 4];
-  __shared__ __attribute__((aligned(16))) bf16_t lds_x[4][32][kBwKW + 8];
+    const float *__restrict__ dpf, const float *__restrict__ Hpre, const bf16_t *__restrict__ gr,
+    bf16_t *__restrict__ dX, float *__restrict__ dWpart, int64_t N, int64_t C, int64_t tbsz, int group4) {
+  using L = B2Lay<HAS_G, DW, SPW>;
+  extern __shared__ __attribute__((aligned(16))) char b2lds[];
   const int64_t K = 4 * C;
-  const int64_t nkt = (K + kBwKT - 1) / kBwKT;
-  const int64_t kt = blockIdx.x % nkt;
+  const int64_t nkt = SPW ? (C + kBwKW - 1) / kBwKW : (K + 4 * kBwKW - 1) / (4 * kBwKW);
+  const int64_t ntb = (N + tbsz - 1) / tbsz;
+  int64_t kt, tbi;
+  if (!SPW && group4) {
+    const int64_t b = blockIdx.x, nct = C / (4 * kBwKW);
+    const int64_t pidx = (b / 32) * 8 + (b % 8);
+    if (pidx >= ntb * nct) return;  // grid padding to a multiple of 32 (whole workgroup)
+    tbi = pidx / nct;
+    kt = ((b / 8) % 4) * nct + pidx % nct;
+  } else {
+    tbi = blockIdx.x / nkt;
+    kt = blockIdx.x % nkt;
+  }
   // token blocks from the last down: the preceding dH_pre pass read X and g
   // in token order, so the first blocks here still sit in the Infinity Cache
-  const int64_t tb = (int64_t)gridDim.x / nkt - 1 - blockIdx.x / nkt;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t tb = ntb - 1 - tbi;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int col = lane & 31, h = lane >> 5;
-  const int64_t kw = kt * kBwKT + wave * kBwKW;
-  // Row-major epilogue mapping: 8 lanes cover one token's 64 k (128 bytes),
-  // so each load/store instruction touches 8 whole 128-byte row segments.
-  const int er = lane >> 3;             // token row er + 8q, q = 0..3
-  const int ek = (lane & 7) * 8;        // k offset within the wave's 64
-  float(*acc_t)[kBwKW + 4] = lds_acc[wave];
-  bf16_t(*x_t)[kBwKW + 8] = lds_x[wave];
+  const bool loader = wave >= 4;
+  const int kq = wave & 3;  // quarter of this wave
+  // k of the quarter's first column and the number of its real columns
+  const int64_t c0 = SPW ? kt * kBwKW : 0;
+  const int64_t kbase = SPW ? kq * C + c0 : kt * 4 * kBwKW + kq * kBwKW;
+  const int64_t nvalid = SPW ? min<int64_t>(kBwKW, C - c0) : max<int64_t>(0, min<int64_t>(kBwKW, K - kbase));
+  const int64_t ksafe = SPW ? kbase : kt * 4 * kBwKW;  // a real k of the tile (redirect target)
 
-  float wf[2][12];
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const int64_t k = kw + 32 * ct + col;
-#pragma unroll
-    for (int s4 = 0; s4 < 3; ++s4) {
-      const float4 v = k < K ? *reinterpret_cast<const float4 *>(W + k * kJ + 12 * h + 4 * s4)
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
-      wf[ct][4 * s4] = v.x; wf[ct][4 * s4 + 1] = v.y; wf[ct][4 * s4 + 2] = v.z; wf[ct][4 * s4 + 3] = v.w;
+  const int64_t t_begin = tb * tbsz;
+  const int64_t t_end = min(N, t_begin + tbsz);
+  const int nsub = (int)((t_end - t_begin + 31) / 32);
+
+  // ---- loader geometry: lane -> (row in its 8-row group, 16-byte piece)
+  const int drow = lane >> 3;
+  const int dpiece = (lane & 7) ^ drow;
+  const bool dvalid = 8 * dpiece < nvalid;
+  const int64_t xk = dvalid ? kbase + 8 * dpiece : ksafe;
+  int64_t gcol = 0;
+  if (HAS_G) {
+    if (SPW) {
+      gcol = dvalid ? c0 + 8 * dpiece : c0;
+    } else {
+      const int64_t si = xk / C;
+      gcol = xk - si * C;
     }
   }
+  const int nload = 4 + (HAS_G ? (SPW ? 1 : 4) : 0) + 1 + (DW ? (kq == 0 ? 2 : 1) : 0);
+
+  auto issue = [&](int i) {
+    char *st = b2lds + (i % kB2Stages) * L::stage;
+    const int64_t t0 = t_begin + 32 * (int64_t)i;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t t = min(t0 + 8 * q + drow, N - 1);
+      dma16(X + t * K + xk, st + L::X + kq * kB2Quarter + q * 1024);
+      if (HAS_G && !SPW) dma16(gr + t * C + gcol, st + L::G + kq * kB2Quarter + q * 1024);
+    }
+    const int64_t t = min(t0 + 8 * kq + drow, N - 1);
+    if (HAS_G && SPW) dma16(gr + t * C + gcol, st + L::G + kq * 1024);
+    dma16(dpf + t * kDpf + 4 * dpiece, st + L::P + kq * 1024);
+    if (DW) {
+      const bf16_t *src = dpB + (t0 >> 5) * (2 * 3 * kJ * 16);
+      dma16(src + kq * 512 + lane * 8, st + L::B + kq * 1024);
+      if (kq == 0 && lane < 32) dma16(src + 2048 + lane * 8, st + L::B + 4096);
+    }
+  };
+
+  // ---- dX geometry: lane -> token rows er + 8q, k = kbase + ek .. +8
+  const int er = lane >> 3;
+  const int ek = (lane & 7) * 8;
+  const bool ekv = ek < nvalid;
+  const int64_t kx = kbase + ek;
+  int si_x = kq;
+  if (!SPW) si_x = (int)(min<int64_t>(kx, K - 1) / C);
+
+  auto prefetch = [&](DxPre &P, int i) {
+    const int64_t t0 = t_begin + 32 * (int64_t)i;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t tt = t0 + er + 8 * q;
+      const bool v = tt < N && ekv;
+      if (ACCUM) P.d[q] = v ? *reinterpret_cast<const u32x4 *>(dX + tt * K + kx) : u32x4{0u, 0u, 0u, 0u};
+      if (HAS_G) P.hp[q] = v ? Hpre[tt * 4 + si_x] : 0.f;
+    }
+  };
+
+  float wf[2][12];
   f32x16 accW[2];
+  if (!loader) {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const bool kv = 32 * ct + col < nvalid;
+#pragma unroll
+      for (int s4 = 0; s4 < 3; ++s4) {
+        const float4 v = kv ? *reinterpret_cast<const float4 *>(W + (kbase + 32 * ct + col) * kJ + 12 * h + 4 * s4)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+        wf[ct][4 * s4] = v.x; wf[ct][4 * s4 + 1] = v.y; wf[ct][4 * s4 + 2] = v.z; wf[ct][4 * s4 + 3] = v.w;
+      }
+    }
+  }
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) accW[rt][r] = 0.f;
 
-  const int64_t t_begin = tb * tbsz;
-  const int64_t t_end = min(N, t_begin + tbsz);
-  BwdStage cur;
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += 32) {
-    bwd_load_stage<ACCUM, HAS_G, DW>(cur, t0, X, dpB, dpf, Hpre, gr, dX, N, npad, C, K, kw, col, h, er, ek);
-    // (a) dp W^T for 32 tokens x 64 k
-    f32x16 accX[2];
+  float *acc_t = reinterpret_cast<float *>(b2lds + L::acc) + kq * 32 * L::acc_row;
+
+  // The two roles run separate loops with the same barrier sequence: a dX
+  // wave never issues an LDS DMA, so its LDS reads need no wait on vmcnt.
+  if (loader) {
+    issue(0);
+    if (nsub > 1) issue(1);
+    for (int i = 0; i < nsub; ++i) {
+      if (i + 1 < nsub) wait_vmcnt_le(nload); else wait_vmcnt<0>();
+      lds_barrier();
+      const char *st = b2lds + (i % kB2Stages) * L::stage;
+      if (i + 2 < nsub) issue(i + 2);
+      if (DW) {
+        // dW += X^T dp: A = 8-token X columns (k = 32 rt + col), B = dp terms
+        const bf16_t *xs = reinterpret_cast<const bf16_t *>(st + L::X + kq * kB2Quarter);
+        u32x4 xa[2][2];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) accX[ct][r] = 0.f;
+          for (int s = 0; s < 2; ++s) {
+            uint32_t w4[4];
+            const int kk = 32 * rt + col;
 #pragma unroll
-      for (int s = 0; s < 12; ++s)
-        accX[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur.af[s], wf[ct][s], accX[ct], 0, 0, 0);
-    }
-    // (b) stage the accumulator tile and the X tile
+            for (int p = 0; p < 4; ++p) {
+              const int r0 = 16 * s + 8 * h + 2 * p;
+              const uint32_t lo16 = xs[r0 * 64 + 8 * ((kk >> 3) ^ (r0 & 7)) + (kk & 7)];
+              const uint32_t hi16 = xs[(r0 + 1) * 64 + 8 * ((kk >> 3) ^ ((r0 + 1) & 7)) + (kk & 7)];
+              w4[p] = lo16 | (hi16 << 16);
+            }
+            xa[rt][s] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+          }
+        const bf16_t *bs = reinterpret_cast<const bf16_t *>(st + L::B);
+        u32x4 bfr[2][3];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc_t[8 * (r >> 2) + 4 * h + (r & 3)][32 * ct + col] = accX[ct][r];
+          for (int tm = 0; tm < 3; ++tm)
+            bfr[s][tm] = col < kJ ? *reinterpret_cast<const u32x4 *>(bs + ((s * 3 + tm) * kJ + col) * 16 + 8 * h)
+                                  : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4 *>(&x_t[er + 8 * q][ek]) = cur.xr[q];
-    wave_lds_sync();
-    // (c) dX = base + dp W^T, row-major 16-byte stores
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t tt = t0 + er + 8 * q;
-      const int64_t k = kw + ek;
-      if (!(tt < N && k < K)) continue;
-      const float4 a0 = *reinterpret_cast<const float4 *>(&acc_t[er + 8 * q][ek]);
-      const float4 a1 = *reinterpret_cast<const float4 *>(&acc_t[er + 8 * q][ek + 4]);
-      const float acc8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      const uint32_t xw[4] = {cur.xr[q].x, cur.xr[q].y, cur.xr[q].z, cur.xr[q].w};
-      float o[8];
+          for (int tm = 0; tm < 3; ++tm)
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        o[2 * p] = acc8[2 * p] + cur.crms[q] * bf16_lo(xw[p]);
-        o[2 * p + 1] = acc8[2 * p + 1] + cur.crms[q] * bf16_hi(xw[p]);
+            for (int rt = 0; rt < 2; ++rt)
+              accW[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa[rt][s]),
+                                                                 __builtin_bit_cast(bf16x8, bfr[s][tm]),
+                                                                 accW[rt], 0, 0, 0);
       }
-      if (HAS_G) {
-        const uint32_t gw[4] = {cur.gg[q].x, cur.gg[q].y, cur.gg[q].z, cur.gg[q].w};
+    }
+  } else {
+    // W in registers before the loop, so the only loads pending inside it
+    // are the prefetches (otherwise every sub-tile waits for all of them)
+    wait_vmcnt<0>();
+    DxPre cur;
+    prefetch(cur, 0);
+    for (int i = 0; i < nsub; ++i) {
+      lds_barrier();
+      const char *st = b2lds + (i % kB2Stages) * L::stage;
+      const int64_t t0 = t_begin + 32 * (int64_t)i;
+      // (a) dp W^T for 32 tokens x 64 k; dp[t0 + col][12h .. 12h+12) from LDS
+      const char *ps = st + L::P;
+      float af[12];
+#pragma unroll
+      for (int s4 = 0; s4 < 3; ++s4) {
+        const float4 v = *reinterpret_cast<const float4 *>(ps + col * 128 + 16 * ((3 * h + s4) ^ (col & 7)));
+        af[4 * s4] = v.x; af[4 * s4 + 1] = v.y; af[4 * s4 + 2] = v.z; af[4 * s4 + 3] = v.w;
+      }
+      f32x16 accX[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) accX[ct][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < 12; ++s)
+          accX[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[s], wf[ct][s], accX[ct], 0, 0, 0);
+      }
+      // (b) transpose the accumulator tile through the wave's LDS area
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc_t[(8 * (r >> 2) + 4 * h + (r & 3)) * L::acc_row + 32 * ct + col] = accX[ct][r];
+      wave_lds_sync();
+      // (c) dX = dp W^T + c_rms x + H_pre g + dX_in, row-major 16-byte stores.
+      // The prefetched dX_in / H_pre are waited for here, once: a wait left
+      // to the first use inside the (branchy) row loop would also wait for
+      // the previous rows' stores.
+      wait_vmcnt<0>();
+      const char *xs = st + L::X + kq * kB2Quarter;
+      const char *gs = st + L::G + (SPW ? 0 : kq * kB2Quarter);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = er + 8 * q;
+        const int64_t tt = t0 + row;
+        if (!(tt < N && ekv)) continue;
+        const int slot = (ek >> 3) ^ (row & 7);
+        const float4 a0 = *reinterpret_cast<const float4 *>(&acc_t[row * L::acc_row + ek]);
+        const float4 a1 = *reinterpret_cast<const float4 *>(&acc_t[row * L::acc_row + ek + 4]);
+        const float acc8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const float crms = *reinterpret_cast<const float *>(ps + row * 128 + 16 * (6 ^ (row & 7)));
+        const u32x4 xv = *reinterpret_cast<const u32x4 *>(xs + row * 128 + 16 * slot);
+        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+        float o[8];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          o[2 * p] += cur.hp[q] * bf16_lo(gw[p]);
-          o[2 * p + 1] += cur.hp[q] * bf16_hi(gw[p]);
+          o[2 * p] = acc8[2 * p] + crms * bf16_lo(xw[p]);
+          o[2 * p + 1] = acc8[2 * p + 1] + crms * bf16_hi(xw[p]);
         }
-      }
-      if (ACCUM) {
-        const uint32_t dw4[4] = {cur.dr[q].x, cur.dr[q].y, cur.dr[q].z, cur.dr[q].w};
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          o[2 * p] += bf16_lo(dw4[p]);
-          o[2 * p + 1] += bf16_hi(dw4[p]);
-        }
-      }
-      uint4 ow;
-      ow.x = pack_bf16x2(o[0], o[1]);
-      ow.y = pack_bf16x2(o[2], o[3]);
-      ow.z = pack_bf16x2(o[4], o[5]);
-      ow.w = pack_bf16x2(o[6], o[7]);
-      *reinterpret_cast<uint4 *>(dX + tt * K + k) = ow;
-    }
-    // (d) dW += X^T dp over these 32 tokens
-    if (DW) {
-      u32x4 xa[2][2];
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          uint32_t w4[4];
+        if (HAS_G) {
+          const u32x4 gv = *reinterpret_cast<const u32x4 *>(gs + row * 128 + 16 * slot);
+          const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
-            const uint32_t lo16 = x_t[16 * s + 8 * h + 2 * p][32 * rt + col];
-            const uint32_t hi16 = x_t[16 * s + 8 * h + 2 * p + 1][32 * rt + col];
-            w4[p] = lo16 | (hi16 << 16);
+            o[2 * p] += cur.hp[q] * bf16_lo(gw[p]);
+            o[2 * p + 1] += cur.hp[q] * bf16_hi(gw[p]);
           }
-          xa[rt][s] = u32x4{w4[0], w4[1], w4[2], w4[3]};
         }
+        if (ACCUM) {
+          const uint32_t dw4[4] = {cur.d[q].x, cur.d[q].y, cur.d[q].z, cur.d[q].w};
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int tm = 0; tm < 3; ++tm)
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt)
-            accW[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa[rt][s]),
-                                                               __builtin_bit_cast(bf16x8, cur.bfr[s][tm]),
-                                                               accW[rt], 0, 0, 0);
+          for (int p = 0; p < 4; ++p) {
+            o[2 * p] += bf16_lo(dw4[p]);
+            o[2 * p + 1] += bf16_hi(dw4[p]);
+          }
+        }
+        uint4 ow;
+        ow.x = pack_bf16x2(o[0], o[1]);
+        ow.y = pack_bf16x2(o[2], o[3]);
+        ow.z = pack_bf16x2(o[4], o[5]);
+        ow.w = pack_bf16x2(o[6], o[7]);
+        *reinterpret_cast<uint4 *>(dX + tt * K + kx) = ow;
+      }
+      // the next sub-tile's dX_in and H_pre, in flight across the barrier
+      // and the next sub-tile's MFMAs
+      if (i + 1 < nsub) prefetch(cur, i + 1);
+      wave_lds_sync();  // this sub-tile's reads of the accumulator area precede the next writes
     }
-    wave_lds_sync();  // LDS reads of this sub-tile precede the next sub-tile's writes
   }
-  if (DW && col < kJ) {
+  if (DW && loader && col < kJ) {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t k = kw + 32 * rt + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (k < K) dWpart[(tb * K + k) * kJ + col] = accW[rt][r];
+        const int e = 32 * rt + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (e < nvalid) dWpart[(tb * K + kbase + e) * kJ + col] = accW[rt][r];
       }
   }
 }
@@ -914,6 +1040,24 @@ __global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict_
   dW[idx] = s;
 }
 
+template <bool ACCUM, bool HAS_G, bool DW>
+static void launch_b2_dw(hipStream_t s, const ProjBwdArgs &a, const BwdWs &L) {
+  const int64_t K = 4 * a.C;
+  const int64_t nkt = kB2Spw ? (a.C + kBwKW - 1) / kBwKW : (K + 4 * kBwKW - 1) / (4 * kBwKW);
+  const int group4 = (!kB2Spw && a.C % (4 * kBwKW) == 0) ? 1 : 0;
+  const int64_t blocks = group4 ? round_up(nkt * L.ntb, 32) : nkt * L.ntb;
+  const size_t lds = (size_t)B2Lay<HAS_G, DW, kB2Spw>::total;
+  hipLaunchKernelGGL((proj_bwd_mfma_kernel<ACCUM, HAS_G, DW, kB2Spw>), dim3((unsigned)blocks), dim3(512), lds, s,
+                     (const bf16_t *)a.X, a.W, L.dpB, L.dpf, a.H_pre, (const bf16_t *)a.g, (bf16_t *)a.dX, L.dwpart,
+                     a.N, a.C, L.tbsz, group4);
+}
+
+template <bool ACCUM, bool HAS_G>
+static void launch_b2(hipStream_t s, const ProjBwdArgs &a, const BwdWs &L) {
+  if (a.dW) launch_b2_dw<ACCUM, HAS_G, true>(s, a, L);
+  else launch_b2_dw<ACCUM, HAS_G, false>(s, a, L);
+}
+
 template <bool ACCUM, bool HAS_G>
 static void launch_dx(hipStream_t s, const ProjBwdArgs &a, const BwdWs &L) {
   const int64_t K = 4 * a.C;
@@ -928,15 +1072,7 @@ static void launch_dx(hipStream_t s, const ProjBwdArgs &a, const BwdWs &L) {
                          (const float *)a.X, a.W, L.dpf, a.H_pre, (const float *)a.g, (float *)a.dX, L.dwpart,
                          a.N, a.C, L.tbsz);
   } else {
-    const unsigned blocks = (unsigned)(((K + kBwKT - 1) / kBwKT) * L.ntb);
-    if (a.dW)
-      hipLaunchKernelGGL((proj_bwd_mfma_kernel<ACCUM, HAS_G, true>), dim3(blocks), dim3(256), 0, s,
-                         (const bf16_t *)a.X, a.W, L.dpB, L.dpf, a.H_pre, (const bf16_t *)a.g,
-                         (bf16_t *)a.dX, L.dwpart, a.N, L.npad, a.C, L.tbsz);
-    else
-      hipLaunchKernelGGL((proj_bwd_mfma_kernel<ACCUM, HAS_G, false>), dim3(blocks), dim3(256), 0, s,
-                         (const bf16_t *)a.X, a.W, L.dpB, L.dpf, a.H_pre, (const bf16_t *)a.g,
-                         (bf16_t *)a.dX, L.dwpart, a.N, L.npad, a.C, L.tbsz);
+    launch_b2<ACCUM, HAS_G>(s, a, L);
   }
 }
 
