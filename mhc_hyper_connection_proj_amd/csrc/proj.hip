@@ -452,10 +452,33 @@ constexpr int kDxKT = 256 * kDxK;
 static int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 
 // Token block of the dX/dW kernels: about 2048 workgroups, multiple of 32.
+// Tokens per block of the dX / dW kernels (a multiple of 32).  fp32: about
+// 2048 workgroups.  bf16: the LDS ring allows one workgroup per CU, so the
+// grid (token blocks x k tiles) is sized to fill whole rounds of kCUs
+// workgroups; among equally full choices the fewest token blocks win (fewer
+// dW partials to reduce).
+constexpr int64_t kCUs = 256;
 static int64_t bwd_token_block(int64_t N, int64_t K, bool f32) {
-  const int64_t nkt = f32 ? (K + kDxKT - 1) / kDxKT : (K + kBwKT - 1) / kBwKT;
-  int64_t tb = (N * nkt + 2047) / 2048;
-  return round_up(tb < 32 ? 32 : tb, 32);
+  if (f32) {
+    const int64_t nkt = (K + kDxKT - 1) / kDxKT;
+    const int64_t tb = (N * nkt + 2047) / 2048;
+    return round_up(tb < 32 ? 32 : tb, 32);
+  }
+  if (N <= 0) return 32;
+  const int64_t nkt = (K + kBwKT - 1) / kBwKT;
+  int64_t best_tb = round_up(N, 32), best_fill = -1, best_n = 0;
+  for (int64_t want = 1; want <= 64; ++want) {
+    const int64_t tb = round_up((N + want - 1) / want, 32);
+    const int64_t n = (N + tb - 1) / tb;
+    const int64_t wgs = n * nkt;
+    const int64_t fill = wgs * 100 / (round_up(wgs, kCUs));  // percent of the last round used
+    if (fill > best_fill || (fill == best_fill && n < best_n)) {
+      best_fill = fill;
+      best_n = n;
+      best_tb = tb;
+    }
+  }
+  return best_tb;
 }
 
 struct BwdWs {
