@@ -1,0 +1,156 @@
+"""GPU parity at the full workload sizes, with the arguments bench.py passes.
+
+The kernels run over every token, with the same grids as in the timed step;
+the oracle checks a sample of tokens that it computes one by one:
+
+  * per-token outputs (H tensors, logits, r/q/z, agg, out, dX, dH, dx) are
+    compared on the sampled tokens;
+  * for the sums over tokens (dW, dalpha, dhbias, dbias) the upstream
+    gradients are nonzero only on the sampled tokens.  Every other token then
+    contributes exact zeros (its gradients are exactly zero, checked on a
+    second sample), so the oracle's sums over the sample are the expected
+    values while the kernels still reduce over all token blocks.
+
+The sample holds the first and last tokens, tokens on both sides of the
+256- and 1024-token block edges, and random tokens.  Inputs are the seeded
+synthetic workloads; derived inputs of an op under test (H_res, saved state)
+come from the oracle, never from the GPU.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_util import assert_act, assert_mixed, assert_rel, dev, h64, log
+from mhc_hyper_connection_proj_amd import binding as B
+from mhc_hyper_connection_proj_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def sample_tokens(N: int, seed: int, k: int = 24) -> np.ndarray:
+    s = {0, 1, N - 2, N - 1}
+    for edge in (256, 1024):
+        for m in range(edge, N, edge * 5):
+            s.update((m - 1, m))
+    rng = np.random.default_rng(seed)
+    s.update(int(t) for t in rng.choice(N, size=k, replace=False))
+    return np.array(sorted(t for t in s if 0 <= t < N), dtype=np.int64)
+
+
+def others(N: int, S: np.ndarray, seed: int, k: int = 16) -> np.ndarray:
+    rng = np.random.default_rng(seed + 1)
+    rest = np.setdiff1d(rng.choice(N, size=4 * k, replace=False), S)
+    return np.sort(rest[:k])
+
+
+def rows(t: torch.Tensor, idx: np.ndarray) -> torch.Tensor:
+    return t[torch.from_numpy(idx).to(t.device)]
+
+
+@functools.lru_cache(maxsize=3)
+def residual(name: str) -> np.ndarray:
+    w = synth.WORKLOADS[name]
+    log(f"generating X for {name}: {w.tokens} x {w.n} x {w.C}")
+    return synth.tensor(w, "X")
+
+
+def only(a: np.ndarray, S: np.ndarray) -> np.ndarray:
+    """Copy of a with every token row outside S set to zero."""
+    z = np.zeros_like(a)
+    z[S] = a[S]
+    return z
+
+
+# ----------------------------------------------------------------- pre pass forward
+@pytest.mark.parametrize("name", ["full_layer", "pre_fwd"])
+def test_pre_fwd_full_size(name):
+    w = synth.WORKLOADS[name]
+    N = w.tokens
+    log(f"pre fwd full size {name}: N={N} C={w.C}")
+    X = residual(name)
+    W = synth.tensor(w, "W")
+    o = B.mhc_pre_fwd(dev(X), dev(W), None, None, w.rms_eps, w.iters, w.eps)
+    torch.cuda.synchronize()
+    S = sample_tokens(N, w.wid)
+    ref = O.pre_fwd(h64(X[S]), h64(W), None, None, w.rms_eps, w.iters, w.eps)
+    assert_rel("H_pre", rows(o["H_pre"], S), ref["H_pre"])
+    assert_rel("H_post", rows(o["H_post"], S), ref["H_post"])
+    assert_mixed("logits", rows(o["H_res_logits"], S), ref["L"])
+    assert_rel("H_res", rows(o["H_res"], S), ref["H_res"], rtol=2e-5)
+    sv = h64(rows(o["saved"], S))
+    assert_rel("r", sv[:, 0], ref["r"])
+    assert_rel("q", sv[:, 1], ref["q"])
+    assert_mixed("z", sv[:, 2:26], ref["z"])
+    assert_act("agg", rows(o["agg"], S), ref["agg"], w.act)
+
+
+# ----------------------------------------------------------------- post (h_post_bda) forward + backward
+@pytest.mark.parametrize("name", ["full_layer", "post_bda"])
+def test_post_bda_full_size(name):
+    w = synth.WORKLOADS[name]
+    N, C = w.tokens, w.C
+    log(f"post fwd/bwd full size {name}: N={N} C={C} bias={w.has_bias}")
+    X = residual(name)
+    x = synth.tensor(w, "x")
+    bias = synth.tensor(w, "bias") if w.has_bias else None
+    H_res = O.round_f64_to_f32(O.sinkhorn_fwd(h64(synth.tensor(w, "L")), w.iters, w.eps)).astype(np.float32)
+    lg = synth.tensor(w, "Hpost_logits").astype(np.float64)
+    H_post = (2.0 / (1.0 + np.exp(-lg))).astype(np.float32)  # input synthesis: a positive gate in (0, 2)
+    S = sample_tokens(N, w.wid)
+    Z = others(N, S, w.wid)
+    G = only(synth.tensor(w, "G"), S)
+    Xd, Hr, Hp, xd = dev(X), dev(H_res), dev(H_post), dev(x)
+    bd = dev(bias) if bias is not None else None
+    out = B.mhc_h_post_bda_fwd(Xd, Hr, Hp, xd, bd)
+    dX, dHr, dHp, dx, db = B.mhc_h_post_bda_bwd(dev(G), Xd, Hr, Hp, xd, bd)
+    torch.cuda.synchronize()
+    bias64 = h64(bias) if bias is not None else None
+    ro = O.h_post_bda_fwd(h64(X[S]), h64(H_res[S]), h64(H_post[S]), h64(x[S]), bias64)
+    rdX, rdHr, rdHp, rdx, rdb = O.h_post_bda_bwd(h64(G[S]), h64(X[S]), h64(H_res[S]), h64(H_post[S]),
+                                                 h64(x[S]), bias64)
+    assert_act("out", rows(out, S), ro, w.act)
+    assert_act("dX", rows(dX, S), rdX, w.act)
+    assert_mixed("dH_res", rows(dHr, S), rdHr)
+    assert_mixed("dH_post", rows(dHp, S), rdHp)
+    assert_act("dx", rows(dx, S), rdx, w.act)
+    for nm, t in (("dX", dX), ("dH_res", dHr), ("dH_post", dHp), ("dx", dx)):
+        assert not h64(rows(t, Z)).any(), f"{nm}: nonzero on tokens with zero upstream gradient"
+    if bias is not None:
+        assert_act("dbias", db, rdb, w.act)
+
+
+# ----------------------------------------------------------------- pre pass backward
+@pytest.mark.parametrize("name", ["full_layer", "pre_fwd"])
+def test_pre_bwd_full_size(name):
+    w = synth.WORKLOADS[name]
+    N, C, n = w.tokens, w.C, w.n
+    log(f"pre bwd full size {name}: N={N} C={C}")
+    X = residual(name)
+    W = synth.tensor(w, "W")
+    S = sample_tokens(N, w.wid)
+    Z = others(N, S, w.wid)
+    ref = O.pre_fwd(h64(X[S]), h64(W), None, None, w.rms_eps, w.iters, w.eps)
+    # forward state: the oracle's on the sampled tokens; any finite values
+    # elsewhere (their upstream gradients are zero)
+    saved = np.zeros((N, 32), np.float32); saved[:, 0] = 1.0; saved[:, 1] = 1.0
+    saved[S, 0] = ref["r"]; saved[S, 1] = ref["q"]; saved[S, 2:26] = ref["z"]
+    H_pre = np.full((N, n), 0.25, np.float32); H_pre[S] = ref["H_pre"]
+    H_post = np.ones((N, n), np.float32); H_post[S] = ref["H_post"]
+    L = np.zeros((N, n, n), np.float32); L[S] = ref["L"]
+    rng = np.random.default_rng(w.wid + 50)
+    g = only(synth.tensor(w, "x"), S)
+    dHp = np.zeros((N, n), np.float32); dHp[S] = rng.standard_normal((len(S), n))
+    dHr = np.zeros((N, n, n), np.float32); dHr[S] = rng.standard_normal((len(S), n, n))
+    dX0 = synth.tensor(w, "G")  # the post pass's dX, accumulated onto
+    ob = B.mhc_pre_bwd(dev(g), dev(dHp), dev(dHr), dev(X), dev(W), dev(saved), dev(H_pre), dev(H_post), dev(L),
+                       alpha=None, iters=w.iters, eps=w.eps, dX=dev(dX0), accumulate_dX=True)
+    torch.cuda.synchronize()
+    rb = O.pre_bwd(h64(g[S]), h64(dHp[S]), h64(dHr[S]), h64(X[S]), h64(W), None, None, w.rms_eps, w.iters, w.eps)
+    assert_act("dX", rows(ob["dX"], S), h64(dX0[S]) + rb["dX"], w.act)
+    assert np.array_equal(h64(rows(ob["dX"], Z)), h64(dX0[Z])), "dX changed on tokens with zero gradient"
+    assert_mixed("dW", ob["dW"], rb["dW"])
+    assert_mixed("dalpha", ob["dalpha"], rb["dalpha"])
+    assert_mixed("dhbias", ob["dhbias"], rb["dhbias"])
