@@ -38,8 +38,10 @@ def ledger_bytes_per_token(C: int, N: int) -> dict:
     phases = {
         "pre_fwd": 8 * C + 2 * C + 16 + 16 + 64 + 64 + 128 + w_amort,
         "post_fwd": 8 * C + 2 * C + 64 + 16 + 8 * C,
-        "post_bwd": 8 * C + 8 * C + 2 * C + 64 + 16 + 8 * C + 2 * C + 64 + 16,
-        "pre_bwd": 2 * C + 8 * C + 8 * C + 16 + 64 + 128 + 16 + 16 + 64 + 8 * C + 2 * w_amort,
+        # the post backward's dX term is formed inside the pre backward from G
+        # (read there instead of a materialised dX), so dX is written once
+        "post_bwd": 8 * C + 8 * C + 2 * C + 64 + 16 + 2 * C + 64 + 16,
+        "pre_bwd": 2 * C + 8 * C + 8 * C + 64 + 16 + 64 + 128 + 16 + 16 + 64 + 8 * C + 2 * w_amort,
     }
     phases["total"] = sum(phases.values())
     return phases
@@ -142,12 +144,12 @@ def main():
 
     def post_bwd():
         _lib.check(lib.mhc_h_post_bda_bwd(sp, N, n, C, MHC_BF16, P(Gd), P(Xd), P(H_res), P(H_post), P(x), None,
-                                          P(dX), P(dHr), P(dHp), P(dx), None, P(wsp), ws_p))
+                                          None, P(dHr), P(dHp), P(dx), None, P(wsp), ws_p))
 
     def pre_bwd():
         _lib.check(lib.mhc_pre_bwd(sp, N, n, C, MHC_BF16, P(g), P(dHp), P(dHr), P(Xd), P(Wd), None, P(saved),
-                                   P(H_pre), P(H_post), P(L), w.iters, w.eps, P(dX), 1, P(dW), P(da), P(db),
-                                   None, None, P(wsb), ws_b))
+                                   P(H_pre), P(H_post), P(L), w.iters, w.eps, P(Gd), P(H_res), P(dX), 0, P(dW),
+                                   P(da), P(db), None, None, P(wsb), ws_b))
 
     def layer_fwd():
         torch.mul(agg, sd, out=x)

@@ -173,7 +173,10 @@ mhc_status mhc_h_post_bda_fwd(void *stream, int64_t tokens, int32_t n, int64_t C
 
 /* Backward (`_torch_h_post_bda_bwd(grad_output, h_res, original_residual,
  * h_post, x, bias)` -> five gradients, the last optional):
- *   dX[j][c] = sum_i H_res[j][i] G[i][c]          (act, overwritten)
+ *   dX[j][c] = sum_i H_res[j][i] G[i][c]          (act, overwritten; dX may be
+ *                                                  NULL to skip it when the
+ *                                                  caller has mhc_pre_bwd add
+ *                                                  this term from G instead)
  *   dH_res[j][i] = sum_c X[j][c] G[i][c]          (fp32)
  *   dH_post[i] = sum_c G[i][c] (x[c] + bias[c])   (fp32)
  *   dx[c] = sum_i H_post[i] G[i][c]               (act)
@@ -209,18 +212,27 @@ mhc_status mhc_pre_fwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_d
  *
  * g [tokens][C] (act) is the gradient of the aggregated stream; dH_post
  * [tokens][n] and dH_res [tokens][n][n] (fp32) come from the h_post_bda
- * backward.  dX (act): overwritten, or accumulated into when
- * accumulate_dX != 0 (pass the h_post_bda dX to get the layer's full
- * residual gradient).  dW/dalpha/dhbias as mhc_proj_rms_h_bwd.  dH_pre_out
- * [tokens][n] and dlogits_out [tokens][n][n] (fp32) optionally receive the
- * intermediate gradients; pass NULL to skip them.
+ * backward.  The third residual term, the h_post_bda dX, is supplied one of
+ * two ways:
+ *   * post_G = NULL, post_H_res = NULL: pass the h_post_bda dX as dX with
+ *     accumulate_dX != 0 (dX is read and overwritten with the sum);
+ *   * post_G [tokens][n][C] (act, the h_post_bda upstream gradient G) and
+ *     post_H_res [tokens][n][n] (fp32): the term sum_i H_res[j][i] G[i][c]
+ *     is computed here, and mhc_h_post_bda_bwd can skip its dX (dX = NULL),
+ *     which saves writing and re-reading one residual-sized tensor.
+ *     Both must be given or both NULL.
+ * dX (act): overwritten, or accumulated into when accumulate_dX != 0.
+ * dW/dalpha/dhbias as mhc_proj_rms_h_bwd.  dH_pre_out [tokens][n] and
+ * dlogits_out [tokens][n][n] (fp32) optionally receive the intermediate
+ * gradients; pass NULL to skip them.
  * ---------------------------------------------------------------------- */
 size_t mhc_pre_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act);
 mhc_status mhc_pre_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
                        const void *g, const float *dH_post, const float *dH_res, const void *X,
                        const float *W, const float *alpha, const float *saved, const float *H_pre,
                        const float *H_post, const float *H_res_logits, int32_t iters, float eps,
-                       void *dX, int32_t accumulate_dX, float *dW, float *dalpha, float *dhbias,
+                       const void *post_G, const float *post_H_res, void *dX,
+                       int32_t accumulate_dX, float *dW, float *dalpha, float *dhbias,
                        float *dH_pre_out, float *dlogits_out, void *workspace,
                        size_t workspace_bytes);
 

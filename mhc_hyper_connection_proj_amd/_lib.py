@@ -56,8 +56,8 @@ SIGNATURES = {
                                    _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz]),
     "mhc_pre_bwd_workspace_size": (_sz, [_i64, _i32, _i64, ctypes.c_int]),
     "mhc_pre_bwd": (ctypes.c_int, [_vp, _i64, _i32, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
-                                   _vp, _vp, _vp, _vp, _vp, _i32, _f32, _vp, _i32, _vp, _vp, _vp,
-                                   _vp, _vp, _vp, _sz]),
+                                   _vp, _vp, _vp, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _i32, _vp,
+                                   _vp, _vp, _vp, _vp, _vp, _sz]),
 }
 
 _lib = None

@@ -156,14 +156,14 @@ def mhc_h_post_bda_fwd(X, H_res, H_post, x, bias=None):
     return out
 
 
-def mhc_h_post_bda_bwd(G, X, H_res, H_post, x, bias=None, want_dbias=True):
-    """Returns (dX, dH_res, dH_post, dx, dbias-or-None)."""
+def mhc_h_post_bda_bwd(G, X, H_res, H_post, x, bias=None, want_dbias=True, want_dX=True):
+    """Returns (dX-or-None, dH_res, dH_post, dx, dbias-or-None)."""
     N, n, C = _dims(X)
     act = _act(X)
     _need(X, "X"); _need(G, "G", X.dtype, X.numel()); _need(H_res, "H_res", f32, N * n * n)
     _need(H_post, "H_post", f32, N * n); _need(x, "x", X.dtype, N * C); _need(bias, "bias", X.dtype, C)
     d = X.device
-    dX = torch.empty_like(X)
+    dX = torch.empty_like(X) if want_dX else None
     dHr = torch.empty(*X.shape[:-2], n, n, dtype=f32, device=d)
     dHp = torch.empty(*X.shape[:-2], n, dtype=f32, device=d)
     dx = torch.empty(*X.shape[:-2], C, dtype=X.dtype, device=d)
@@ -194,14 +194,19 @@ def mhc_pre_fwd(X, W, alpha=None, hbias=None, rms_eps=1e-6, iters=20, eps=1e-6):
 
 
 def mhc_pre_bwd(g, dH_post, dH_res, X, W, saved, H_pre, H_post, H_res_logits, alpha=None, iters=20, eps=1e-6,
-                dX=None, accumulate_dX=False, want_intermediates=False):
-    """Fused pre pass backward.  Returns dict(dX, dW, dalpha, dhbias[, dH_pre, dlogits])."""
+                dX=None, accumulate_dX=False, want_intermediates=False, post_G=None, post_H_res=None):
+    """Fused pre pass backward.  Returns dict(dX, dW, dalpha, dhbias[, dH_pre, dlogits]).
+
+    post_G / post_H_res: the h_post_bda upstream gradient and H_res; when given,
+    the h_post_bda dX term is added here (call mhc_h_post_bda_bwd with want_dX=False).
+    """
     N, n, C = _dims(X)
     act = _act(X)
     _need(X, "X"); _need(g, "g", X.dtype, N * C); _need(dH_post, "dH_post", f32, N * n)
     _need(dH_res, "dH_res", f32, N * n * n); _need(W, "W", f32, n * C * J); _need(alpha, "alpha", f32, 3)
     _need(saved, "saved", f32, N * SAVED_STRIDE); _need(H_pre, "H_pre", f32, N * n)
     _need(H_post, "H_post", f32, N * n); _need(H_res_logits, "H_res_logits", f32, N * n * n)
+    _need(post_G, "post_G", X.dtype, X.numel()); _need(post_H_res, "post_H_res", f32, N * n * n)
     d = X.device
     if dX is None:
         if accumulate_dX:
@@ -215,7 +220,8 @@ def mhc_pre_bwd(g, dH_post, dH_res, X, W, saved, H_pre, H_post, H_res_logits, al
         o["dlogits"] = torch.empty(*X.shape[:-2], n, n, dtype=f32, device=d)
     ws, wsb = _ws(_lib.lib().mhc_pre_bwd_workspace_size(N, n, C, act), d)
     call("mhc_pre_bwd", _stream(X), N, n, C, act, _p(g), _p(dH_post), _p(dH_res), _p(X), _p(W), _p(alpha),
-         _p(saved), _p(H_pre), _p(H_post), _p(H_res_logits), iters, eps, _p(dX), int(accumulate_dX),
+         _p(saved), _p(H_pre), _p(H_post), _p(H_res_logits), iters, eps, _p(post_G), _p(post_H_res), _p(dX),
+         int(accumulate_dX),
          _p(o["dW"]), _p(o["dalpha"]), _p(o["dhbias"]), _p(o.get("dH_pre")), _p(o.get("dlogits")),
          _p(ws), wsb)
     return o

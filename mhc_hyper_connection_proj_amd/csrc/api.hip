@@ -368,7 +368,7 @@ mhc_status mhc_h_post_bda_bwd(void *stream, int64_t tokens, int32_t n, int64_t C
   v.in(H_post, tokens * 16, "H_post");
   v.in(x, tokens * C * esz(act), "x");
   v.in(bias, C * esz(act), "bias", true);
-  v.out(dX, tokens * 4 * C * esz(act), "dX");
+  v.out(dX, tokens * 4 * C * esz(act), "dX", true);
   v.out(dH_res, tokens * 64, "dH_res");
   v.out(dH_post, tokens * 16, "dH_post");
   v.out(dx, tokens * C * esz(act), "dx");
@@ -425,13 +425,16 @@ mhc_status mhc_pre_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_d
                        const void *g, const float *dH_post, const float *dH_res, const void *X,
                        const float *W, const float *alpha, const float *saved, const float *H_pre,
                        const float *H_post, const float *H_res_logits, int32_t iters, float eps,
-                       void *dX, int32_t accumulate_dX, float *dW, float *dalpha, float *dhbias,
+                       const void *post_G, const float *post_H_res, void *dX,
+                       int32_t accumulate_dX, float *dW, float *dalpha, float *dhbias,
                        float *dH_pre_out, float *dlogits_out, void *workspace,
                        size_t workspace_bytes) {
   Validator v("mhc_pre_bwd");
   v.dims(tokens, n, C, act);
   v.eps(eps, "eps");
   v.iters(iters);
+  if ((post_G == nullptr) != (post_H_res == nullptr))
+    v.fail(MHC_ERR_ARG, "post_G and post_H_res must be given together");
   if (!v.ok()) return v.status();
   const int64_t K = 4 * C;
   const hipStream_t s = (hipStream_t)stream;
@@ -453,6 +456,8 @@ mhc_status mhc_pre_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_d
   v.in(H_pre, tokens * 16, "H_pre");
   v.in(H_post, tokens * 16, "H_post");
   v.in(H_res_logits, tokens * 64, "H_res_logits");
+  v.in(post_G, tokens * K * esz(act), "post_G", true);
+  v.in(post_H_res, tokens * 64, "post_H_res", true);
   v.out(dX, tokens * K * esz(act), "dX");
   v.out(dW, K * J * 4, "dW", true);
   v.out(dalpha, 12, "dalpha", true);
@@ -467,6 +472,7 @@ mhc_status mhc_pre_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_d
   a.dH_res = dH_res; a.logits = H_res_logits; a.iters = iters; a.eps = eps; a.g = g; a.dX = dX;
   a.accumulate = accumulate_dX != 0; a.dW = dW; a.dalpha = dalpha; a.dhbias = dhbias;
   a.dH_pre_out = dH_pre_out; a.dL_out = dlogits_out; a.ws = workspace;
+  a.post_G = post_G; a.post_H_res = post_H_res;
   mhc::launch_proj_bwd(s, a);
   return launched("mhc_pre_bwd");
 }

@@ -71,6 +71,8 @@ struct ProjBwdArgs {
   float *dW, *dalpha, *dhbias;
   float *dH_pre_out, *dL_out;
   void *ws;
+  const void *post_G;       // h_post_bda upstream gradient, or NULL (see mhc_pre_bwd)
+  const float *post_H_res;  // H_res of the h_post_bda pass, with post_G
 };
 void launch_proj_bwd(hipStream_t s, const ProjBwdArgs &a);
 

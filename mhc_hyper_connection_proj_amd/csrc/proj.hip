@@ -651,41 +651,43 @@ __global__ __launch_bounds__(256) void param_final_kernel(const float *__restric
 // Workgroup = 8 waves on one token block and one k tile of four 64-k quarters,
 // walked in 32-token sub-tiles through a 3-stage LDS ring:
 //  * waves 4..7 (loaders) fill each stage with global_load_lds_dwordx4: the X
-//    tile, the g tile, the fp32 dp rows and the bf16 dp terms of the
-//    sub-tile, two sub-tiles ahead.  With dW they then run x^T dp on MFMA
-//    (loader w-4 owns quarter w-4; A fragments are 8-token X columns read
-//    from LDS, B fragments the dp terms);
+//    tile, the g tile, the h_post_bda upstream gradient G (POST), the fp32 dp
+//    rows and the bf16 dp terms of the sub-tile, two sub-tiles ahead.  With
+//    dW they then run x^T dp on MFMA (loader w-4 owns quarter w-4; A
+//    fragments are 8-token X columns read from LDS, B fragments the dp terms);
 //  * waves 0..3 own one quarter each: dp W^T on fp32 MFMA (W held in
-//    registers), the accumulator tile transposed through a private LDS
-//    area, then the dX epilogue with dX_in loaded one sub-tile ahead into
-//    registers.
+//    registers), each 32 x 32 half of the accumulator transposed through a
+//    private LDS area, then the dX epilogue with dX_in, H_pre and H_res rows
+//    loaded one sub-tile ahead into registers.
 // One barrier per sub-tile: loaders first wait for their own loads of the
 // sub-tile (s_waitcnt vmcnt), so the barrier both publishes the stage and
 // guarantees that the slot refilled next has been read by every wave.  The
 // loaders issue no other global memory instructions inside the loop, which
 // keeps their vmcnt arithmetic exact.
-// In every 128-byte LDS row (64 bf16 of X or g, 32 fp32 of dp) the 16-byte
-// piece p of row r sits in slot p ^ (r & 7): the DMA lanes of an instruction
-// cover 8 rows x 8 slots, and the row-wise and column-wise reads below spread
-// over all banks.
-// Channel tiles: SPW = one 64-channel range c0 for all 4 streams (quarter i =
-// stream i; the g tile is 32 x 64 and shared), else 256 consecutive k (g
-// pieces addressed per piece; when C is a multiple of 256 the four tiles
-// that read the same g tile run back to back on one XCD).
+// In every 128-byte LDS row (64 bf16 of X, g or G, 32 fp32 of dp) the
+// 16-byte piece p of row r sits in slot p ^ (r & 7): the DMA lanes of an
+// instruction cover 8 rows x 8 slots, and the row-wise and column-wise reads
+// below spread over the banks.
+// Channel tiles: without the h_post_bda term, 256 consecutive k (g pieces
+// addressed per piece; when C is a multiple of 256 the four tiles that read
+// the same g tile run back to back on one XCD).  With it (POST), one
+// 64-channel range c0 for all 4 streams (quarter i = stream i): the g tile
+// (32 x 64) and the G tile (4 x 32 x 64) are then loaded once and shared by
+// the four dX waves, which each need all four streams of G.
 constexpr int kB2Stages = 3;
-constexpr bool kB2Spw = false;  // channel tiling (see above)
 constexpr int kB2Quarter = 32 * 128;  // bytes of one 32 x 64 bf16 tile
+constexpr int kB2AccRow = 36;         // floats per row of a wave's 32 x 32 accumulator half
 
-template <bool HAS_G, bool DW, bool SPW>
+template <bool HAS_G, bool DW, bool POST>
 struct B2Lay {
   static constexpr int X = 0;
-  static constexpr int G = 4 * kB2Quarter;
-  static constexpr int P = G + (HAS_G ? (SPW ? 1 : 4) * kB2Quarter : 0);
+  static constexpr int G = 4 * kB2Quarter;                               // g
+  static constexpr int Q = G + (HAS_G ? (POST ? 1 : 4) * kB2Quarter : 0);  // G of h_post_bda
+  static constexpr int P = Q + (POST ? 4 * kB2Quarter : 0);
   static constexpr int B = P + 32 * kDpf * 4;
   static constexpr int stage = B + (DW ? 2 * 3 * kJ * 16 * 2 : 0);
   static constexpr int acc = kB2Stages * stage;
-  static constexpr int acc_row = kBwKW + 4;  // floats per row of a wave's accumulator tile
-  static constexpr int total = acc + 4 * 32 * acc_row * 4;
+  static constexpr int total = acc + 4 * 32 * kB2AccRow * 4;
 };
 
 // vmcnt <= n for a wave-uniform n; a value outside the table waits for all.
@@ -702,6 +704,7 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
     case 9: wait_vmcnt<9>(); break;
     case 10: wait_vmcnt<10>(); break;
     case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
     default: wait_vmcnt<0>(); break;
   }
 }
@@ -718,18 +721,22 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// dX_in and H_pre of one sub-tile for a dX lane (rows er + 8q)
+// Per-lane inputs of one sub-tile's dX epilogue, for rows er + 16q of the
+// accumulator half ct: dX_in, H_pre and the lane's H_res row.
 struct DxPre {
-  u32x4 d[4];
-  float hp[4];
+  u32x4 d[2][2];
+  float hp[2][2];
+  float4 hr[2];
 };
 
-template <bool ACCUM, bool HAS_G, bool DW, bool SPW>
+template <bool ACCUM, bool HAS_G, bool DW, bool POST>
 __global__ __launch_bounds__(512) void proj_bwd_mfma_kernel(
     const bf16_t *__restrict__ X, const float *__restrict__ W, const bf16_t *__restrict__ dpB,
     const float *__restrict__ dpf, const float *__restrict__ Hpre, const bf16_t *__restrict__ gr,
-    bf16_t *__restrict__ dX, float *__restrict__ dWpart, int64_t N, int64_t C, int64_t tbsz, int group4) {
-  using L = B2Lay<HAS_G, DW, SPW>;
+    const bf16_t *__restrict__ Gp, const float *__restrict__ Hres, bf16_t *__restrict__ dX,
+    float *__restrict__ dWpart, int64_t N, int64_t C, int64_t tbsz, int group4) {
+  constexpr bool SPW = POST;  // stream-per-wave channel tiles
+  using L = B2Lay<HAS_G, DW, POST>;
   extern __shared__ __attribute__((aligned(16))) char b2lds[];
   const int64_t K = 4 * C;
   const int64_t nkt = SPW ? (C + kBwKW - 1) / kBwKW : (K + 4 * kBwKW - 1) / (4 * kBwKW);
@@ -768,16 +775,10 @@ __global__ __launch_bounds__(512) void proj_bwd_mfma_kernel(
   const int dpiece = (lane & 7) ^ drow;
   const bool dvalid = 8 * dpiece < nvalid;
   const int64_t xk = dvalid ? kbase + 8 * dpiece : ksafe;
-  int64_t gcol = 0;
-  if (HAS_G) {
-    if (SPW) {
-      gcol = dvalid ? c0 + 8 * dpiece : c0;
-    } else {
-      const int64_t si = xk / C;
-      gcol = xk - si * C;
-    }
-  }
-  const int nload = 4 + (HAS_G ? (SPW ? 1 : 4) : 0) + 1 + (DW ? (kq == 0 ? 2 : 1) : 0);
+  // channel of the lane's piece (g and G tiles); a real channel when the
+  // piece lies past the tile
+  const int64_t gcol = SPW ? (dvalid ? c0 + 8 * dpiece : c0) : xk - (xk / C) * C;
+  const int nload = 4 + (HAS_G ? (SPW ? 1 : 4) : 0) + (POST ? 4 : 0) + 1 + (DW ? (kq == 0 ? 2 : 1) : 0);
 
   auto issue = [&](int i) {
     char *st = b2lds + (i % kB2Stages) * L::stage;
@@ -787,6 +788,7 @@ __global__ __launch_bounds__(512) void proj_bwd_mfma_kernel(
       const int64_t t = min(t0 + 8 * q + drow, N - 1);
       dma16(X + t * K + xk, st + L::X + kq * kB2Quarter + q * 1024);
       if (HAS_G && !SPW) dma16(gr + t * C + gcol, st + L::G + kq * kB2Quarter + q * 1024);
+      if (POST) dma16(Gp + (t * 4 + kq) * C + gcol, st + L::Q + kq * kB2Quarter + q * 1024);
     }
     const int64_t t = min(t0 + 8 * kq + drow, N - 1);
     if (HAS_G && SPW) dma16(gr + t * C + gcol, st + L::G + kq * 1024);
@@ -798,22 +800,33 @@ __global__ __launch_bounds__(512) void proj_bwd_mfma_kernel(
     }
   };
 
-  // ---- dX geometry: lane -> token rows er + 8q, k = kbase + ek .. +8
-  const int er = lane >> 3;
-  const int ek = (lane & 7) * 8;
-  const bool ekv = ek < nvalid;
-  const int64_t kx = kbase + ek;
-  int si_x = kq;
-  if (!SPW) si_x = (int)(min<int64_t>(kx, K - 1) / C);
+  // ---- dX geometry: in accumulator half ct (k = 32 ct .. +32 of the
+  // quarter), lane -> token rows er + 16q (q = 0, 1) and 8 k at 32 ct + ek
+  const int er = lane >> 2;
+  const int ek = (lane & 3) * 8;
+  bool ekv[2];
+  int64_t kx[2];
+  int si_x[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    ekv[ct] = 32 * ct + ek < nvalid;
+    kx[ct] = kbase + 32 * ct + ek;
+    si_x[ct] = SPW ? kq : (int)(min<int64_t>(kx[ct], K - 1) / C);
+  }
 
   auto prefetch = [&](DxPre &P, int i) {
     const int64_t t0 = t_begin + 32 * (int64_t)i;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t tt = t0 + er + 8 * q;
-      const bool v = tt < N && ekv;
-      if (ACCUM) P.d[q] = v ? *reinterpret_cast<const u32x4 *>(dX + tt * K + kx) : u32x4{0u, 0u, 0u, 0u};
-      if (HAS_G) P.hp[q] = v ? Hpre[tt * 4 + si_x] : 0.f;
+    for (int q = 0; q < 2; ++q) {
+      const int64_t tt = t0 + er + 16 * q;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const bool v = tt < N && ekv[ct];
+        if (ACCUM) P.d[ct][q] = v ? *reinterpret_cast<const u32x4 *>(dX + tt * K + kx[ct]) : u32x4{0u, 0u, 0u, 0u};
+        if (HAS_G) P.hp[ct][q] = v ? Hpre[tt * 4 + si_x[ct]] : 0.f;
+      }
+      if (POST)
+        P.hr[q] = tt < N ? *reinterpret_cast<const float4 *>(Hres + tt * 16 + kq * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
 
@@ -836,7 +849,7 @@ __global__ __launch_bounds__(512) void proj_bwd_mfma_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) accW[rt][r] = 0.f;
 
-  float *acc_t = reinterpret_cast<float *>(b2lds + L::acc) + kq * 32 * L::acc_row;
+  float *acc_t = reinterpret_cast<float *>(b2lds + L::acc) + kq * 32 * kB2AccRow;
 
   // The two roles run separate loops with the same barrier sequence: a dX
   // wave never issues an LDS DMA, so its LDS reads need no wait on vmcnt.
@@ -913,66 +926,86 @@ __global__ __launch_bounds__(512) void proj_bwd_mfma_kernel(
         for (int s = 0; s < 12; ++s)
           accX[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[s], wf[ct][s], accX[ct], 0, 0, 0);
       }
-      // (b) transpose the accumulator tile through the wave's LDS area
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          acc_t[(8 * (r >> 2) + 4 * h + (r & 3)) * L::acc_row + 32 * ct + col] = accX[ct][r];
-      wave_lds_sync();
-      // (c) dX = dp W^T + c_rms x + H_pre g + dX_in, row-major 16-byte stores.
-      // The prefetched dX_in / H_pre are waited for here, once: a wait left
-      // to the first use inside the (branchy) row loop would also wait for
-      // the previous rows' stores.
+      // (b) dX = dp W^T + c_rms x + H_pre g + sum_i H_res[j][i] G[i] + dX_in,
+      // one 32 x 32 half at a time: transpose through the wave's LDS area,
+      // then 16-byte row-major stores.  The prefetched inputs are waited for
+      // here, once: a wait left to their first use inside the (branchy) row
+      // loop would also wait for the previous rows' stores.  The scheduling
+      // fence keeps the MFMAs above the wait, so they cover its latency.
+      __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<0>();
       const char *xs = st + L::X + kq * kB2Quarter;
       const char *gs = st + L::G + (SPW ? 0 : kq * kB2Quarter);
+      const char *qs = st + L::Q;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = er + 8 * q;
-        const int64_t tt = t0 + row;
-        if (!(tt < N && ekv)) continue;
-        const int slot = (ek >> 3) ^ (row & 7);
-        const float4 a0 = *reinterpret_cast<const float4 *>(&acc_t[row * L::acc_row + ek]);
-        const float4 a1 = *reinterpret_cast<const float4 *>(&acc_t[row * L::acc_row + ek + 4]);
-        const float acc8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        const float crms = *reinterpret_cast<const float *>(ps + row * 128 + 16 * (6 ^ (row & 7)));
-        const u32x4 xv = *reinterpret_cast<const u32x4 *>(xs + row * 128 + 16 * slot);
-        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-        float o[8];
+      for (int ct = 0; ct < 2; ++ct) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          o[2 * p] = acc8[2 * p] + crms * bf16_lo(xw[p]);
-          o[2 * p + 1] = acc8[2 * p + 1] + crms * bf16_hi(xw[p]);
-        }
-        if (HAS_G) {
-          const u32x4 gv = *reinterpret_cast<const u32x4 *>(gs + row * 128 + 16 * slot);
-          const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+        for (int r = 0; r < 16; ++r) acc_t[(8 * (r >> 2) + 4 * h + (r & 3)) * kB2AccRow + col] = accX[ct][r];
+        wave_lds_sync();
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int row = er + 16 * q;
+          const int64_t tt = t0 + row;
+          if (!(tt < N && ekv[ct])) continue;
+          const int slot = ((32 * ct + ek) >> 3) ^ (row & 7);
+          const float4 a0 = *reinterpret_cast<const float4 *>(&acc_t[row * kB2AccRow + ek]);
+          const float4 a1 = *reinterpret_cast<const float4 *>(&acc_t[row * kB2AccRow + ek + 4]);
+          const float acc8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+          const float crms = *reinterpret_cast<const float *>(ps + row * 128 + 16 * (6 ^ (row & 7)));
+          const u32x4 xv = *reinterpret_cast<const u32x4 *>(xs + row * 128 + 16 * slot);
+          const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+          float o[8];
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
-            o[2 * p] += cur.hp[q] * bf16_lo(gw[p]);
-            o[2 * p + 1] += cur.hp[q] * bf16_hi(gw[p]);
+            o[2 * p] = acc8[2 * p] + crms * bf16_lo(xw[p]);
+            o[2 * p + 1] = acc8[2 * p + 1] + crms * bf16_hi(xw[p]);
           }
-        }
-        if (ACCUM) {
-          const uint32_t dw4[4] = {cur.d[q].x, cur.d[q].y, cur.d[q].z, cur.d[q].w};
+          if (HAS_G) {
+            const u32x4 gv = *reinterpret_cast<const u32x4 *>(gs + row * 128 + 16 * slot);
+            const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+            const float hp = cur.hp[ct][q];
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            o[2 * p] += bf16_lo(dw4[p]);
-            o[2 * p + 1] += bf16_hi(dw4[p]);
+            for (int p = 0; p < 4; ++p) {
+              o[2 * p] += hp * bf16_lo(gw[p]);
+              o[2 * p + 1] += hp * bf16_hi(gw[p]);
+            }
           }
+          if (POST) {  // h_post_bda term: sum_i H_res[j][i] G[i], j = this wave's stream
+            const float4 hr = cur.hr[q];
+            uint32_t gw[4][4];
+#pragma unroll
+            for (int si = 0; si < 4; ++si) {
+              const u32x4 v = *reinterpret_cast<const u32x4 *>(qs + si * kB2Quarter + row * 128 + 16 * slot);
+              gw[si][0] = v.x; gw[si][1] = v.y; gw[si][2] = v.z; gw[si][3] = v.w;
+            }
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              o[2 * p] += (hr.x * bf16_lo(gw[0][p]) + hr.y * bf16_lo(gw[1][p])) +
+                          (hr.z * bf16_lo(gw[2][p]) + hr.w * bf16_lo(gw[3][p]));
+              o[2 * p + 1] += (hr.x * bf16_hi(gw[0][p]) + hr.y * bf16_hi(gw[1][p])) +
+                              (hr.z * bf16_hi(gw[2][p]) + hr.w * bf16_hi(gw[3][p]));
+            }
+          }
+          if (ACCUM) {
+            const uint32_t dw4[4] = {cur.d[ct][q].x, cur.d[ct][q].y, cur.d[ct][q].z, cur.d[ct][q].w};
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              o[2 * p] += bf16_lo(dw4[p]);
+              o[2 * p + 1] += bf16_hi(dw4[p]);
+            }
+          }
+          uint4 ow;
+          ow.x = pack_bf16x2(o[0], o[1]);
+          ow.y = pack_bf16x2(o[2], o[3]);
+          ow.z = pack_bf16x2(o[4], o[5]);
+          ow.w = pack_bf16x2(o[6], o[7]);
+          *reinterpret_cast<uint4 *>(dX + tt * K + kx[ct]) = ow;
         }
-        uint4 ow;
-        ow.x = pack_bf16x2(o[0], o[1]);
-        ow.y = pack_bf16x2(o[2], o[3]);
-        ow.z = pack_bf16x2(o[4], o[5]);
-        ow.w = pack_bf16x2(o[6], o[7]);
-        *reinterpret_cast<uint4 *>(dX + tt * K + kx) = ow;
+        wave_lds_sync();  // this half's reads of the accumulator area precede the next writes
       }
-      // the next sub-tile's dX_in and H_pre, in flight across the barrier
-      // and the next sub-tile's MFMAs
+      // the next sub-tile's dX_in, H_pre and H_res, in flight across the
+      // barrier and the next sub-tile's MFMAs
       if (i + 1 < nsub) prefetch(cur, i + 1);
-      wave_lds_sync();  // this sub-tile's reads of the accumulator area precede the next writes
     }
   }
   if (DW && loader && col < kJ) {
@@ -990,8 +1023,9 @@ __global__ __launch_bounds__(512) void proj_bwd_mfma_kernel(
 template <bool ACCUM, bool HAS_G, bool DW>
 __global__ __launch_bounds__(256) void proj_bwd_dx_f32_kernel(
     const float *__restrict__ X, const float *__restrict__ W, const float *__restrict__ dpf,
-    const float *__restrict__ Hpre, const float *__restrict__ gr, float *__restrict__ dX,
-    float *__restrict__ dWpart, int64_t N, int64_t C, int64_t tbsz) {
+    const float *__restrict__ Hpre, const float *__restrict__ gr, const float *__restrict__ Gp,
+    const float *__restrict__ Hres, float *__restrict__ dX, float *__restrict__ dWpart, int64_t N, int64_t C,
+    int64_t tbsz) {
   const int64_t K = 4 * C;
   const int64_t nkt = (K + kDxKT - 1) / kDxKT;
   const int64_t kt = blockIdx.x % nkt;
@@ -1028,6 +1062,16 @@ __global__ __launch_bounds__(256) void proj_bwd_dx_f32_kernel(
       const float4 g4 = *reinterpret_cast<const float4 *>(gr + t * C + c);
       o[0] += hpi * g4.x; o[1] += hpi * g4.y; o[2] += hpi * g4.z; o[3] += hpi * g4.w;
     }
+    if (Gp) {  // h_post_bda term: sum_i H_res[si][i] G[i]
+      const float4 hr = *reinterpret_cast<const float4 *>(Hres + t * 16 + si * 4);
+      float4 gv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gv[i] = *reinterpret_cast<const float4 *>(Gp + (t * 4 + i) * C + c);
+      o[0] += (hr.x * gv[0].x + hr.y * gv[1].x) + (hr.z * gv[2].x + hr.w * gv[3].x);
+      o[1] += (hr.x * gv[0].y + hr.y * gv[1].y) + (hr.z * gv[2].y + hr.w * gv[3].y);
+      o[2] += (hr.x * gv[0].z + hr.y * gv[1].z) + (hr.z * gv[2].z + hr.w * gv[3].z);
+      o[3] += (hr.x * gv[0].w + hr.y * gv[1].w) + (hr.z * gv[2].w + hr.w * gv[3].w);
+    }
 #pragma unroll
     for (int e = 0; e < kDxK; ++e) {
       float acc = crms * xv[e];
@@ -1063,22 +1107,28 @@ __global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict_
   dW[idx] = s;
 }
 
-template <bool ACCUM, bool HAS_G, bool DW>
+template <bool ACCUM, bool HAS_G, bool DW, bool POST>
 static void launch_b2_dw(hipStream_t s, const ProjBwdArgs &a, const BwdWs &L) {
   const int64_t K = 4 * a.C;
-  const int64_t nkt = kB2Spw ? (a.C + kBwKW - 1) / kBwKW : (K + 4 * kBwKW - 1) / (4 * kBwKW);
-  const int group4 = (!kB2Spw && a.C % (4 * kBwKW) == 0) ? 1 : 0;
+  const int64_t nkt = POST ? (a.C + kBwKW - 1) / kBwKW : (K + 4 * kBwKW - 1) / (4 * kBwKW);
+  const int group4 = (!POST && a.C % (4 * kBwKW) == 0) ? 1 : 0;
   const int64_t blocks = group4 ? round_up(nkt * L.ntb, 32) : nkt * L.ntb;
-  const size_t lds = (size_t)B2Lay<HAS_G, DW, kB2Spw>::total;
-  hipLaunchKernelGGL((proj_bwd_mfma_kernel<ACCUM, HAS_G, DW, kB2Spw>), dim3((unsigned)blocks), dim3(512), lds, s,
-                     (const bf16_t *)a.X, a.W, L.dpB, L.dpf, a.H_pre, (const bf16_t *)a.g, (bf16_t *)a.dX, L.dwpart,
-                     a.N, a.C, L.tbsz, group4);
+  const size_t lds = (size_t)B2Lay<HAS_G, DW, POST>::total;
+  hipLaunchKernelGGL((proj_bwd_mfma_kernel<ACCUM, HAS_G, DW, POST>), dim3((unsigned)blocks), dim3(512), lds, s,
+                     (const bf16_t *)a.X, a.W, L.dpB, L.dpf, a.H_pre, (const bf16_t *)a.g, (const bf16_t *)a.post_G,
+                     a.post_H_res, (bf16_t *)a.dX, L.dwpart, a.N, a.C, L.tbsz, group4);
 }
 
 template <bool ACCUM, bool HAS_G>
 static void launch_b2(hipStream_t s, const ProjBwdArgs &a, const BwdWs &L) {
-  if (a.dW) launch_b2_dw<ACCUM, HAS_G, true>(s, a, L);
-  else launch_b2_dw<ACCUM, HAS_G, false>(s, a, L);
+  const bool post = a.post_G != nullptr;
+  if (a.dW) {
+    if (post) launch_b2_dw<ACCUM, HAS_G, true, true>(s, a, L);
+    else launch_b2_dw<ACCUM, HAS_G, true, false>(s, a, L);
+  } else {
+    if (post) launch_b2_dw<ACCUM, HAS_G, false, true>(s, a, L);
+    else launch_b2_dw<ACCUM, HAS_G, false, false>(s, a, L);
+  }
 }
 
 template <bool ACCUM, bool HAS_G>
@@ -1088,12 +1138,12 @@ static void launch_dx(hipStream_t s, const ProjBwdArgs &a, const BwdWs &L) {
     const unsigned blocks = (unsigned)(((K + kDxKT - 1) / kDxKT) * L.ntb);
     if (a.dW)
       hipLaunchKernelGGL((proj_bwd_dx_f32_kernel<ACCUM, HAS_G, true>), dim3(blocks), dim3(256), 0, s,
-                         (const float *)a.X, a.W, L.dpf, a.H_pre, (const float *)a.g, (float *)a.dX, L.dwpart,
-                         a.N, a.C, L.tbsz);
+                         (const float *)a.X, a.W, L.dpf, a.H_pre, (const float *)a.g, (const float *)a.post_G,
+                         a.post_H_res, (float *)a.dX, L.dwpart, a.N, a.C, L.tbsz);
     else
       hipLaunchKernelGGL((proj_bwd_dx_f32_kernel<ACCUM, HAS_G, false>), dim3(blocks), dim3(256), 0, s,
-                         (const float *)a.X, a.W, L.dpf, a.H_pre, (const float *)a.g, (float *)a.dX, L.dwpart,
-                         a.N, a.C, L.tbsz);
+                         (const float *)a.X, a.W, L.dpf, a.H_pre, (const float *)a.g, (const float *)a.post_G,
+                         a.post_H_res, (float *)a.dX, L.dwpart, a.N, a.C, L.tbsz);
   } else {
     launch_b2<ACCUM, HAS_G>(s, a, L);
   }

@@ -215,9 +215,10 @@ __global__ __launch_bounds__(256) void h_post_bda_bwd_kernel(
 #pragma unroll
           for (int e = 0; e < 8; ++e) lv[e] += bv[e];
         }
-        // dX[j] = sum_i H_res[j][i] G[i]
+        // dX[j] = sum_i H_res[j][i] G[i]  (skipped when the caller folds it
+        // into the pre pass backward; dX is then null for every thread)
 #pragma unroll
-        for (int js = 0; js < 4; ++js) {
+        for (int js = 0; js < 4 && dX != nullptr; ++js) {
           float o[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e)

@@ -7,6 +7,12 @@ Tolerances (stated by the benchmark spec for this path, applied element by element):
   * bf16 tensors: |g - o| <= 8e-3 |o| + 1e-5 rms(o), o being the oracle's fp64
     result rounded once to bf16 (8e-3 is one bf16 ulp; the small absolute
     term absorbs fp32 accumulation on cancelling sums).
+  * sums over tokens (dW, dalpha, dhbias, dbias): the rule of their type plus
+    1e-5 sum_t |o_t|, o_t being token t's own contribution from the oracle.
+    Each token's contribution carries the per-token 1e-5 relative error, and
+    the errors add across tokens; when the contributions cancel, the sum is
+    far smaller than they are and a bound relative to the sum alone is not
+    attainable in fp32.
 """
 import sys
 
@@ -60,6 +66,37 @@ def assert_mixed(name, g, o, rtol=1e-5):
     assert np.isfinite(g).all(), f"{name}: non-finite GPU values"
     rms = np.sqrt(np.mean(o * o)) if o.size else 0.0
     _report(name, g, o, rtol * (np.abs(o) + rms))
+
+
+def assert_tokensum(name, g, o, abs_parts, act="f32"):
+    """Sum over tokens: abs_parts = sum_t |o_t| (same shape as o), see the module rules."""
+    g = h64(g); o = np.asarray(o, np.float64); s = np.asarray(abs_parts, np.float64)
+    assert g.shape == o.shape == s.shape, (name, g.shape, o.shape, s.shape)
+    assert np.isfinite(g).all(), f"{name}: non-finite GPU values"
+    rms = np.sqrt(np.mean(o * o)) if o.size else 0.0
+    if act == "bf16":
+        ob = O.round_f64_to_bf16(o)
+        _report(name, g, ob, 8e-3 * np.abs(ob) + 1e-5 * rms + 1e-5 * s)
+    else:
+        _report(name, g, o, 1e-5 * (np.abs(o) + rms) + 1e-5 * s)
+
+
+def pre_bwd_abs_parts(g, dH_post, dH_res, X, W, *rest):
+    """sum_t |contribution of token t| to dW, dalpha, dhbias (oracle, one token at a time)."""
+    aW = aa = ab = 0.0
+    for t in range(X.shape[0]):
+        r = O.pre_bwd(g[t:t + 1], dH_post[t:t + 1], dH_res[t:t + 1], X[t:t + 1], W, *rest)
+        aW = aW + np.abs(r["dW"]); aa = aa + np.abs(r["dalpha"]); ab = ab + np.abs(r["dhbias"])
+    return aW, aa, ab
+
+
+def proj_bwd_abs_parts(X, W, dH_pre, dH_post, dL, *rest):
+    """As pre_bwd_abs_parts for the projection backward alone."""
+    aW = aa = ab = 0.0
+    for t in range(X.shape[0]):
+        _, dW, da, db = O.proj_rms_h_bwd(X[t:t + 1], W, dH_pre[t:t + 1], dH_post[t:t + 1], dL[t:t + 1], *rest)
+        aW = aW + np.abs(dW); aa = aa + np.abs(da); ab = ab + np.abs(db)
+    return aW, aa, ab
 
 
 def assert_act(name, g, o, act):

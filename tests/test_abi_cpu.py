@@ -149,14 +149,18 @@ def test_pre_validation(lib):
     assert f(*a) == ALIAS
     g = lib.mhc_pre_bwd
     wb = lib.mhc_pre_bwd_workspace_size(16, 4, 256, 1)
-    b = [None, 16, 4, 256, 1, p(0), p(1), p(2), p(3), p(4), None, p(5), p(6), p(7), p(8), 20, 1e-6, p(9), 1, p(10),
-         None, None, None, None, p(11), wb]
+    b = [None, 16, 4, 256, 1, p(0), p(1), p(2), p(3), p(4), None, p(5), p(6), p(7), p(8), 20, 1e-6, None, None,
+         p(9), 1, p(10), None, None, None, None, p(11), wb]
     b2 = list(b); b2[5] = None
     assert g(*b2) == NULL
-    b2 = list(b); b2[17] = p(3)                                    # dX aliases X
+    b2 = list(b); b2[19] = p(3)                                    # dX aliases X
     assert g(*b2) == ALIAS
-    b2 = list(b); b2[25] = wb - 16
+    b2 = list(b); b2[27] = wb - 16
     assert g(*b2) == WS
+    b2 = list(b); b2[17] = p(12)                                   # post_G without post_H_res
+    assert g(*b2) == ARG
+    b2 = list(b); b2[17] = p(12); b2[18] = p(13); b2[19] = p(12)   # dX aliases post_G
+    assert g(*b2) == ALIAS
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

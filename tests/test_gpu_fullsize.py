@@ -23,7 +23,7 @@ import pytest
 import torch
 
 import oracle as O
-from gpu_util import assert_act, assert_mixed, assert_rel, dev, h64, log
+from gpu_util import assert_act, assert_mixed, assert_rel, assert_tokensum, dev, h64, log, pre_bwd_abs_parts
 from mhc_hyper_connection_proj_amd import binding as B
 from mhc_hyper_connection_proj_amd import synth
 
@@ -119,15 +119,15 @@ def test_post_bda_full_size(name):
     for nm, t in (("dX", dX), ("dH_res", dHr), ("dH_post", dHp), ("dx", dx)):
         assert not h64(rows(t, Z)).any(), f"{nm}: nonzero on tokens with zero upstream gradient"
     if bias is not None:
-        assert_act("dbias", db, rdb, w.act)
+        assert_tokensum("dbias", db, rdb, np.abs(rdx).sum(axis=0), w.act)
 
 
 # ----------------------------------------------------------------- pre pass backward
-@pytest.mark.parametrize("name", ["full_layer", "pre_fwd"])
-def test_pre_bwd_full_size(name):
+@pytest.mark.parametrize("name,mode", [("full_layer", "post"), ("full_layer", "accumulate"), ("pre_fwd", "post")])
+def test_pre_bwd_full_size(name, mode):
     w = synth.WORKLOADS[name]
     N, C, n = w.tokens, w.C, w.n
-    log(f"pre bwd full size {name}: N={N} C={C}")
+    log(f"pre bwd full size {name}: N={N} C={C} mode={mode}")
     X = residual(name)
     W = synth.tensor(w, "W")
     S = sample_tokens(N, w.wid)
@@ -144,13 +144,29 @@ def test_pre_bwd_full_size(name):
     g = only(synth.tensor(w, "x"), S)
     dHp = np.zeros((N, n), np.float32); dHp[S] = rng.standard_normal((len(S), n))
     dHr = np.zeros((N, n, n), np.float32); dHr[S] = rng.standard_normal((len(S), n, n))
-    dX0 = synth.tensor(w, "G")  # the post pass's dX, accumulated onto
-    ob = B.mhc_pre_bwd(dev(g), dev(dHp), dev(dHr), dev(X), dev(W), dev(saved), dev(H_pre), dev(H_post), dev(L),
-                       alpha=None, iters=w.iters, eps=w.eps, dX=dev(dX0), accumulate_dX=True)
+    if mode == "accumulate":  # the post pass's dX, materialised and accumulated onto
+        dX0 = synth.tensor(w, "G")
+        ob = B.mhc_pre_bwd(dev(g), dev(dHp), dev(dHr), dev(X), dev(W), dev(saved), dev(H_pre), dev(H_post),
+                           dev(L), alpha=None, iters=w.iters, eps=w.eps, dX=dev(dX0), accumulate_dX=True)
+        base_S, base_Z = h64(dX0[S]), h64(dX0[Z])
+    else:  # as timed: the post pass's dX term formed here from its G (all tokens) and H_res
+        Gp = synth.tensor(w, "G")
+        Hrp = O.round_f64_to_f32(O.sinkhorn_fwd(h64(synth.tensor(w, "L")), w.iters, w.eps)).astype(np.float32)
+        ob = B.mhc_pre_bwd(dev(g), dev(dHp), dev(dHr), dev(X), dev(W), dev(saved), dev(H_pre), dev(H_post),
+                           dev(L), alpha=None, iters=w.iters, eps=w.eps, post_G=dev(Gp), post_H_res=dev(Hrp))
+        zero4, zc = np.zeros((len(S), n)), np.zeros((len(S), C))
+        base_S = O.h_post_bda_bwd(h64(Gp[S]), h64(X[S]), h64(Hrp[S]), zero4, zc)[0]
+        zero4, zc = np.zeros((len(Z), n)), np.zeros((len(Z), C))
+        base_Z = O.round_f64_to_bf16(O.h_post_bda_bwd(h64(Gp[Z]), h64(X[Z]), h64(Hrp[Z]), zero4, zc)[0])
     torch.cuda.synchronize()
     rb = O.pre_bwd(h64(g[S]), h64(dHp[S]), h64(dHr[S]), h64(X[S]), h64(W), None, None, w.rms_eps, w.iters, w.eps)
-    assert_act("dX", rows(ob["dX"], S), h64(dX0[S]) + rb["dX"], w.act)
-    assert np.array_equal(h64(rows(ob["dX"], Z)), h64(dX0[Z])), "dX changed on tokens with zero gradient"
-    assert_mixed("dW", ob["dW"], rb["dW"])
-    assert_mixed("dalpha", ob["dalpha"], rb["dalpha"])
-    assert_mixed("dhbias", ob["dhbias"], rb["dhbias"])
+    assert_act("dX", rows(ob["dX"], S), base_S + rb["dX"], w.act)
+    if mode == "accumulate":
+        assert np.array_equal(h64(rows(ob["dX"], Z)), base_Z), "dX changed on tokens with zero gradient"
+    else:  # zero pre-pass gradient there: dX is the post term alone
+        assert_act("dX (post term only)", rows(ob["dX"], Z), base_Z, w.act)
+    aW, aa, ab = pre_bwd_abs_parts(h64(g[S]), h64(dHp[S]), h64(dHr[S]), h64(X[S]), h64(W), None, None, w.rms_eps,
+                                   w.iters, w.eps)
+    assert_tokensum("dW", ob["dW"], rb["dW"], aW)
+    assert_tokensum("dalpha", ob["dalpha"], rb["dalpha"], aa)
+    assert_tokensum("dhbias", ob["dhbias"], rb["dhbias"], ab)

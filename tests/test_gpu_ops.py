@@ -9,7 +9,8 @@ import pytest
 import torch
 
 import oracle as O
-from gpu_util import assert_act, assert_mixed, assert_rel, dev, h64, log
+from gpu_util import (assert_act, assert_mixed, assert_rel, assert_tokensum, dev, h64, log, pre_bwd_abs_parts,
+                      proj_bwd_abs_parts)
 from mhc_hyper_connection_proj_amd import binding as B
 from mhc_hyper_connection_proj_amd import synth
 
@@ -113,9 +114,16 @@ def test_h_post_bda(act, N, C, bias):
     assert_mixed("dH_post", dHp, odHp)
     assert_act("dx", dx, odx, act)
     if bias:
-        assert_act("dbias", db, odb, act)
+        assert_tokensum("dbias", db, odb, np.abs(odx).sum(axis=0), act)
     else:
         assert db is None
+    # without dX (the pre backward forms it): every other output is unchanged
+    nX, nHr, nHp, ndx, ndb = B.mhc_h_post_bda_bwd(dev(G), dev(X), dev(Hr), dev(Hp), dev(x),
+                                                  dev(b) if bias else None, want_dX=False)
+    torch.cuda.synchronize()
+    assert nX is None
+    for a, c in ((nHr, dHr), (nHp, dHp), (ndx, dx)) + (((ndb, db),) if bias else ()):
+        assert torch.equal(a, c)
 
 
 def test_h_post_bda_identity_h_res_exact_bf16():
@@ -181,15 +189,17 @@ def test_proj_rms_h_bwd(act, N, C):
     odX, odW, oda, odb = O.proj_rms_h_bwd(h64(X), h64(W), h64(dHp), h64(dHq), h64(dL), h64(alpha), h64(hb), 1e-6)
     assert_act("dX", dX, odX, act)
     assert_act("dX accumulated", dXa, h64(dX0) + odX, act)
-    assert_mixed("dW", dW, odW)
-    assert_mixed("dalpha", da, oda)
-    assert_mixed("dhbias", db, odb)
+    aW, aa, ab = proj_bwd_abs_parts(h64(X), h64(W), h64(dHp), h64(dHq), h64(dL), h64(alpha), h64(hb), 1e-6)
+    assert_tokensum("dW", dW, odW, aW)
+    assert_tokensum("dalpha", da, oda, aa)
+    assert_tokensum("dhbias", db, odb, ab)
 
 
 # ----------------------------------------------------------------- fused pre pass
+@pytest.mark.parametrize("mode", ["accumulate", "post"])
 @pytest.mark.parametrize("act,N,C", [("f32", 64, 256), ("bf16", 37, 296), ("bf16", 66, 7168), ("bf16", 130, 4096)])
-def test_pre_fwd_bwd(act, N, C):
-    log(f"pre fwd/bwd act={act} N={N} C={C}")
+def test_pre_fwd_bwd(act, N, C, mode):
+    log(f"pre fwd/bwd act={act} N={N} C={C} mode={mode}")
     X, W, alpha, hb = _proj_inputs(act, N, C)
     o = B.mhc_pre_fwd(dev(X), dev(W), dev(alpha), dev(hb), 1e-6, 20, 1e-6)
     torch.cuda.synchronize()
@@ -207,18 +217,29 @@ def test_pre_fwd_bwd(act, N, C):
     g = store(RNG.standard_normal((N, C)), act)
     dHq = f32(RNG.standard_normal((N, 4)))
     dHr = f32(RNG.standard_normal((N, 4, 4)))
-    dX0 = store(RNG.standard_normal((N, 4, C)), act)
-    ob = B.mhc_pre_bwd(dev(g), dev(dHq), dev(dHr), dev(X), dev(W), dev(saved), dev(f32(ref["H_pre"])),
-                       dev(f32(ref["H_post"])), dev(f32(ref["L"])), alpha=dev(alpha), iters=20, eps=1e-6,
-                       dX=dev(dX0), accumulate_dX=True, want_intermediates=True)
+    if mode == "accumulate":  # the h_post_bda dX comes in materialised
+        dX0 = store(RNG.standard_normal((N, 4, C)), act)
+        ob = B.mhc_pre_bwd(dev(g), dev(dHq), dev(dHr), dev(X), dev(W), dev(saved), dev(f32(ref["H_pre"])),
+                           dev(f32(ref["H_post"])), dev(f32(ref["L"])), alpha=dev(alpha), iters=20, eps=1e-6,
+                           dX=dev(dX0), accumulate_dX=True, want_intermediates=True)
+        base = h64(dX0)
+    else:  # the h_post_bda dX term formed here from its G and H_res
+        Gp = store(RNG.standard_normal((N, 4, C)), act)
+        Hrp = f32(O.sinkhorn_fwd(RNG.standard_normal((N, 4, 4)), 20, 1e-6))
+        ob = B.mhc_pre_bwd(dev(g), dev(dHq), dev(dHr), dev(X), dev(W), dev(saved), dev(f32(ref["H_pre"])),
+                           dev(f32(ref["H_post"])), dev(f32(ref["L"])), alpha=dev(alpha), iters=20, eps=1e-6,
+                           want_intermediates=True, post_G=dev(Gp), post_H_res=dev(Hrp))
+        zeros = np.zeros((N, 4)); zc = np.zeros((N, C))
+        base = O.h_post_bda_bwd(h64(Gp), h64(X), h64(Hrp), zeros, zc)[0]
     torch.cuda.synchronize()
     rb = O.pre_bwd(h64(g), h64(dHq), h64(dHr), h64(X), h64(W), h64(alpha), h64(hb), 1e-6, 20, 1e-6)
     assert_mixed("dH_pre", ob["dH_pre"], rb["dH_pre"])
     assert_mixed("dlogits", ob["dlogits"], rb["dL"])
-    assert_act("dX", ob["dX"], h64(dX0) + rb["dX"], act)
-    assert_mixed("dW", ob["dW"], rb["dW"])
-    assert_mixed("dalpha", ob["dalpha"], rb["dalpha"])
-    assert_mixed("dhbias", ob["dhbias"], rb["dhbias"])
+    assert_act("dX", ob["dX"], base + rb["dX"], act)
+    aW, aa, ab = pre_bwd_abs_parts(h64(g), h64(dHq), h64(dHr), h64(X), h64(W), h64(alpha), h64(hb), 1e-6, 20, 1e-6)
+    assert_tokensum("dW", ob["dW"], rb["dW"], aW)
+    assert_tokensum("dalpha", ob["dalpha"], rb["dalpha"], aa)
+    assert_tokensum("dhbias", ob["dhbias"], rb["dhbias"], ab)
 
 
 # ----------------------------------------------------------------- edge cases
