@@ -13,8 +13,8 @@ constexpr int kSavedStride = 32;
 
 // ---- launch geometry for per-token streaming kernels
 struct StreamGeom {
-  int tpb;  // threads per block (64, 128 or 256)
-  int gpt;  // 8-channel groups per thread (1, 2, 4 or 8): C <= 16384
+  int tpb;  // threads per block (a multiple of 64, at most 512)
+  int gpt;  // 8-channel groups per thread (1, 2 or 4): C <= 16384
 };
 constexpr int64_t kMaxC = 16384;
 StreamGeom stream_geom(int64_t C);

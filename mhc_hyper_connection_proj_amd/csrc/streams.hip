@@ -20,39 +20,52 @@
 
 namespace mhc {
 
+// Threads per workgroup (a multiple of 64, at most 512) and 8-channel groups
+// per thread (1, 2 or 4; C <= 16384 gives at most 2048 groups), chosen so
+// that tpb * gpt covers C/8 with the fewest idle groups (exactly, when C is
+// a multiple of 512 * gpt or of the size below it: C = 7168 gives 448 x 2).
 StreamGeom stream_geom(int64_t C) {
   const int64_t G = C / 8;
-  if (G <= 64) return {64, 1};
-  if (G <= 128) return {128, 1};
-  const int64_t per = (G + 255) / 256;
-  return {256, per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8};
+  const int gpt = G <= 512 ? 1 : G <= 1024 ? 2 : 4;
+  const int64_t per = (G + gpt - 1) / gpt;
+  return {(int)((per + 63) / 64 * 64), gpt};
+}
+
+// Each kernel first issues every load of a token (all groups of the thread,
+// raw and unconditional: a group past C/8 re-reads the last real group and
+// is never stored or summed), then converts and computes.  Loads issued
+// inside per-group branches are waited for group by group, which leaves a
+// fraction of the bytes in flight.
+__device__ __forceinline__ int clamp_group(int j, int G) {
+  return min((int)threadIdx.x + j * (int)blockDim.x, G - 1);
 }
 
 // ============================================================ h_aggregate fwd
 template <typename T, int GPT>
-__global__ __launch_bounds__(256) void h_aggregate_fwd_kernel(const T *__restrict__ X,
+__global__ __launch_bounds__(512) void h_aggregate_fwd_kernel(const T *__restrict__ X,
                                                                const float *__restrict__ Hpre,
                                                                T *__restrict__ out, int64_t C) {
+  using R = typename Io8<T>::raw_t;
   const int64_t t = (int64_t)gridDim.x - 1 - blockIdx.x;  // last token first
   const int G = (int)(C / 8);
-  const float h0 = Hpre[t * 4 + 0], h1 = Hpre[t * 4 + 1], h2 = Hpre[t * 4 + 2], h3 = Hpre[t * 4 + 3];
   const T *xt = X + t * 4 * C;
-  float v[GPT][4][8];
+  R rx[GPT][4];
 #pragma unroll
   for (int j = 0; j < GPT; ++j) {
-    const int g = threadIdx.x + j * blockDim.x;
-    if (g < G) {
+    const int gc = clamp_group(j, G);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Io8<T>::load(xt + i * C + 8 * g, v[j][i]);
-    }
+    for (int i = 0; i < 4; ++i) rx[j][i] = Io8<T>::ld_nt(xt + i * C + 8 * gc);
   }
+  const float h0 = Hpre[t * 4 + 0], h1 = Hpre[t * 4 + 1], h2 = Hpre[t * 4 + 2], h3 = Hpre[t * 4 + 3];
 #pragma unroll
   for (int j = 0; j < GPT; ++j) {
     const int g = threadIdx.x + j * blockDim.x;
     if (g < G) {
-      float o[8];
+      float v[4][8], o[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = h0 * v[j][0][e] + h1 * v[j][1][e] + h2 * v[j][2][e] + h3 * v[j][3][e];
+      for (int i = 0; i < 4; ++i) Io8<T>::cvt(rx[j][i], v[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = h0 * v[0][e] + h1 * v[1][e] + h2 * v[2][e] + h3 * v[3][e];
       Io8<T>::store(out + t * C + 8 * g, o);
     }
   }
@@ -61,13 +74,26 @@ __global__ __launch_bounds__(256) void h_aggregate_fwd_kernel(const T *__restric
 // ============================================================ h_aggregate bwd
 // dH_pre[t][i] = sum_c g[t][c] X[t][i][c];  optionally dX (+)= H_pre[i] g.
 template <typename T, int GPT, bool WRITE_DX, bool ACCUM>
-__global__ __launch_bounds__(256) void h_aggregate_bwd_kernel(
+__global__ __launch_bounds__(512) void h_aggregate_bwd_kernel(
     const T *__restrict__ gr, const T *__restrict__ X, const float *__restrict__ Hpre,
     T *__restrict__ dX, float *__restrict__ dHpre, int64_t C) {
-  __shared__ float red[4][4];
+  using R = typename Io8<T>::raw_t;
+  __shared__ float red[8][4];
   const int64_t t = blockIdx.x;
   const int G = (int)(C / 8);
   const T *xt = X + t * 4 * C;
+  R rg[GPT], rx[GPT][4], rd[GPT][4];
+#pragma unroll
+  for (int j = 0; j < GPT; ++j) {
+    const int gc = clamp_group(j, G);
+    rg[j] = Io8<T>::ld_nt(gr + t * C + 8 * gc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rx[j][i] = Io8<T>::ld_nt(xt + i * C + 8 * gc);
+    if (WRITE_DX && ACCUM) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rd[j][i] = Io8<T>::ld_nt(dX + (t * 4 + i) * C + 8 * gc);
+    }
+  }
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   float h[4];
 #pragma unroll
@@ -77,9 +103,9 @@ __global__ __launch_bounds__(256) void h_aggregate_bwd_kernel(
     const int g = threadIdx.x + j * blockDim.x;
     if (g < G) {
       float gv[8], xv[4][8];
-      Io8<T>::load(gr + t * C + 8 * g, gv);
+      Io8<T>::cvt(rg[j], gv);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Io8<T>::load(xt + i * C + 8 * g, xv[i]);
+      for (int i = 0; i < 4; ++i) Io8<T>::cvt(rx[j][i], xv[i]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float s = 0.f;
@@ -90,17 +116,16 @@ __global__ __launch_bounds__(256) void h_aggregate_bwd_kernel(
       if (WRITE_DX) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          T *p = dX + (t * 4 + i) * C + 8 * g;
           float d[8];
           if (ACCUM) {
-            Io8<T>::load(p, d);
+            Io8<T>::cvt(rd[j][i], d);
 #pragma unroll
             for (int e = 0; e < 8; ++e) d[e] += h[i] * gv[e];
           } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) d[e] = h[i] * gv[e];
           }
-          Io8<T>::store(p, d);
+          Io8<T>::store(dX + (t * 4 + i) * C + 8 * g, d);
         }
       }
     }
@@ -122,17 +147,26 @@ __global__ __launch_bounds__(256) void h_aggregate_bwd_kernel(
 
 // ============================================================ h_post_bda fwd
 template <typename T, int GPT, bool HAS_BIAS>
-__global__ __launch_bounds__(256) void h_post_bda_fwd_kernel(
+__global__ __launch_bounds__(512) void h_post_bda_fwd_kernel(
     const T *__restrict__ X, const float *__restrict__ Hres, const float *__restrict__ Hpost,
     const T *__restrict__ x, const T *__restrict__ bias, T *__restrict__ out, int64_t C) {
+  using R = typename Io8<T>::raw_t;
   const int64_t t = blockIdx.x;
   const int G = (int)(C / 8);
+  const T *xt = X + t * 4 * C;
+  R rx[GPT][4], rl[GPT];
+#pragma unroll
+  for (int j = 0; j < GPT; ++j) {
+    const int gc = clamp_group(j, G);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rx[j][i] = Io8<T>::ld_nt(xt + i * C + 8 * gc);
+    rl[j] = Io8<T>::ld_nt(x + t * C + 8 * gc);
+  }
   float hr[16], hp[4];
 #pragma unroll
   for (int e = 0; e < 16; ++e) hr[e] = Hres[t * 16 + e];
 #pragma unroll
   for (int i = 0; i < 4; ++i) hp[i] = Hpost[t * 4 + i];
-  const T *xt = X + t * 4 * C;
   T *ot = out + t * 4 * C;
 #pragma unroll
   for (int j = 0; j < GPT; ++j) {
@@ -140,8 +174,8 @@ __global__ __launch_bounds__(256) void h_post_bda_fwd_kernel(
     if (g < G) {
       float xv[4][8], lv[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Io8<T>::load(xt + i * C + 8 * g, xv[i]);
-      Io8<T>::load(x + t * C + 8 * g, lv);
+      for (int i = 0; i < 4; ++i) Io8<T>::cvt(rx[j][i], xv[i]);
+      Io8<T>::cvt(rl[j], lv);
       if (HAS_BIAS) {
         float bv[8];
         Io8<T>::load(bias + 8 * g, bv);
@@ -162,11 +196,15 @@ __global__ __launch_bounds__(256) void h_post_bda_fwd_kernel(
 }
 
 // ============================================================ h_post_bda bwd
-// Workgroup b owns tokens [b*TG, b*TG + TG).  Per token: dX, dx streamed out;
-// 16 dH_res + 4 dH_post dot products reduced to LDS; after the token loop
-// one barrier and the per-token sums are written.  With DBIAS, each thread
-// keeps the fp32 dx sums of its channels over the workgroup's tokens and
-// writes them as one partial row.
+// Workgroup b owns tokens [b*TG, b*TG + TG).  Per token: dX (unless null) and
+// dx streamed out; 16 dH_res + 4 dH_post dot products reduced to LDS; after
+// the token loop one barrier and the per-token sums are written.  With
+// DBIAS, each thread keeps the fp32 dx sums of its channels over the
+// workgroup's tokens and writes them as one partial row.
+// This kernel keeps 256-thread workgroups with the loads of a group issued
+// and consumed together (about 120 registers, four workgroups per CU): the
+// two-phase form of the other streaming kernels needs ~190 registers here,
+// which leaves one workgroup per CU and measured slower.
 constexpr int kPostTG = 16;
 
 template <typename T, int GPT, bool HAS_BIAS, bool DBIAS>
@@ -205,10 +243,10 @@ __global__ __launch_bounds__(256) void h_post_bda_bwd_kernel(
       if (g < G) {
         float gv[4][8], xv[4][8], lv[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Io8<T>::load(gt + i * C + 8 * g, gv[i]);
+        for (int i = 0; i < 4; ++i) Io8<T>::load_nt(gt + i * C + 8 * g, gv[i]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Io8<T>::load(xt + i * C + 8 * g, xv[i]);
-        Io8<T>::load(x + t * C + 8 * g, lv);
+        for (int i = 0; i < 4; ++i) Io8<T>::load_nt(xt + i * C + 8 * g, xv[i]);
+        Io8<T>::load_nt(x + t * C + 8 * g, lv);
         if (HAS_BIAS) {
           float bv[8];
           Io8<T>::load(bias + 8 * g, bv);
@@ -318,6 +356,12 @@ __global__ __launch_bounds__(256) void dbias_reduce_kernel(const float *__restri
   switch (GPT_VAL) {                                         \
     case 1: { constexpr int GPT = 1; __VA_ARGS__; } break;   \
     case 2: { constexpr int GPT = 2; __VA_ARGS__; } break;   \
+    default: { constexpr int GPT = 4; __VA_ARGS__; } break;  \
+  }
+#define MHC_GPT_DISPATCH8(GPT_VAL, ...)                      \
+  switch (GPT_VAL) {                                         \
+    case 1: { constexpr int GPT = 1; __VA_ARGS__; } break;   \
+    case 2: { constexpr int GPT = 2; __VA_ARGS__; } break;   \
     case 4: { constexpr int GPT = 4; __VA_ARGS__; } break;   \
     default: { constexpr int GPT = 8; __VA_ARGS__; } break;  \
   }
@@ -403,11 +447,14 @@ template <typename T, bool HAS_BIAS, bool DBIAS>
 static void post_bwd3(hipStream_t s, int64_t N, int64_t C, const void *G, const void *X,
                       const float *Hr, const float *Hp, const void *x, const void *b, void *dX,
                       float *dHr, float *dHp, void *dx, float *part) {
-  const StreamGeom geo = stream_geom(C);
+  const int64_t ng = C / 8;  // 8-channel groups; 256 threads take 1, 2, 4 or 8 each
+  const StreamGeom geo = ng <= 64 ? StreamGeom{64, 1} : ng <= 128 ? StreamGeom{128, 1}
+                         : ng <= 256 ? StreamGeom{256, 1} : ng <= 512 ? StreamGeom{256, 2}
+                         : ng <= 1024 ? StreamGeom{256, 4} : StreamGeom{256, 8};
   const int TG = DBIAS ? kPostTG : 1;
   const unsigned blocks = (unsigned)((N + TG - 1) / TG);
   const size_t lds = (size_t)(geo.tpb / 64) * TG * 20 * sizeof(float);
-  MHC_GPT_DISPATCH(geo.gpt,
+  MHC_GPT_DISPATCH8(geo.gpt,
                    hipLaunchKernelGGL((h_post_bda_bwd_kernel<T, GPT, HAS_BIAS, DBIAS>),
                                       dim3(blocks), dim3(geo.tpb), lds, s, (const T *)G,
                                       (const T *)X, Hr, Hp, (const T *)x, (const T *)b, (T *)dX,
