@@ -118,6 +118,11 @@ def main():
     s = synth.tensor(w, "scale")
     G = synth.tensor(w, "G", tokens=N)
     Xd, Wd, sd, Gd = to_dev(X), to_dev(W), to_dev(s), to_dev(G)
+    # Consecutive steps use two copies of the residual (same values, other
+    # addresses): a step then cannot find the previous step's X in the 256 MB
+    # Infinity Cache, as in a model where every layer has its own residual.
+    Xcopies = [Xd, Xd.clone()]
+    cur = {"X": Xd}
 
     f32 = torch.float32
     e = lambda *shape, dt=f32: torch.empty(*shape, dtype=dt, device=dev)
@@ -136,18 +141,18 @@ def main():
     sp = stream.cuda_stream
 
     def pre_fwd():
-        _lib.check(lib.mhc_pre_fwd(sp, N, n, C, MHC_BF16, P(Xd), P(Wd), None, None, w.rms_eps, w.iters, w.eps,
+        _lib.check(lib.mhc_pre_fwd(sp, N, n, C, MHC_BF16, P(cur["X"]), P(Wd), None, None, w.rms_eps, w.iters, w.eps,
                                    P(H_pre), P(H_post), P(H_res), P(L), P(saved), P(agg), P(wsf), ws_f))
 
     def post_fwd():
-        _lib.check(lib.mhc_h_post_bda_fwd(sp, N, n, C, MHC_BF16, P(Xd), P(H_res), P(H_post), P(x), None, P(out)))
+        _lib.check(lib.mhc_h_post_bda_fwd(sp, N, n, C, MHC_BF16, P(cur["X"]), P(H_res), P(H_post), P(x), None, P(out)))
 
     def post_bwd():
-        _lib.check(lib.mhc_h_post_bda_bwd(sp, N, n, C, MHC_BF16, P(Gd), P(Xd), P(H_res), P(H_post), P(x), None,
+        _lib.check(lib.mhc_h_post_bda_bwd(sp, N, n, C, MHC_BF16, P(Gd), P(cur["X"]), P(H_res), P(H_post), P(x), None,
                                           None, P(dHr), P(dHp), P(dx), None, P(wsp), ws_p))
 
     def pre_bwd():
-        _lib.check(lib.mhc_pre_bwd(sp, N, n, C, MHC_BF16, P(g), P(dHp), P(dHr), P(Xd), P(Wd), None, P(saved),
+        _lib.check(lib.mhc_pre_bwd(sp, N, n, C, MHC_BF16, P(g), P(dHp), P(dHr), P(cur["X"]), P(Wd), None, P(saved),
                                    P(H_pre), P(H_post), P(L), w.iters, w.eps, P(Gd), P(H_res), P(dX), 0, P(dW),
                                    P(da), P(db), None, None, P(wsb), ws_b))
 
@@ -168,7 +173,8 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    for _ in range(args.warmup):
+    for it in range(args.warmup):
+        cur["X"] = Xcopies[it % 2]
         for _, fn, _ in seq:
             fn()
     torch.cuda.synchronize()
@@ -177,6 +183,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for st in range(args.steps):
+        cur["X"] = Xcopies[(args.warmup + st) % 2]
         evs[st][0].record(stream)
         for i, (_, fn, _) in enumerate(seq):
             fn()
