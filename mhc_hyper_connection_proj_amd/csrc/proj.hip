@@ -444,6 +444,7 @@ void launch_proj_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *
 //    contiguous 768-byte read across the wave.
 // fp32 activations use a VALU kernel for both contractions.
 constexpr int kDpf = 32;     // fp32 per-token record: dp[24], c_rms, pad
+constexpr int kDpaBytes = 160;  // bf16 per-token record: dp terms [3][24], c_rms (fp32), pad
 constexpr int kBwKW = 64;    // k per wave in the MFMA kernel
 constexpr int kBwKT = 4 * kBwKW;
 constexpr int kDxK = 4;      // k per thread in the fp32 VALU kernel
@@ -483,7 +484,7 @@ static int64_t bwd_token_block(int64_t N, int64_t K, bool f32) {
 
 struct BwdWs {
   float *dpf, *dhpre, *ppart, *dwpart;
-  bf16_t *dpB;
+  char *dpA;
   int64_t npad, nblk, tbsz, ntb;
 };
 
@@ -500,7 +501,7 @@ static BwdWs bwd_layout(void *ws, int64_t N, int64_t C, bool f32) {
   L.dpf = (float *)take((size_t)N * kDpf * 4);
   L.dhpre = (float *)take((size_t)N * 16);
   L.ppart = (float *)take((size_t)L.nblk * 32 * 4);
-  if (!f32) L.dpB = (bf16_t *)take((size_t)3 * kJ * L.npad * 2);
+  if (!f32) L.dpA = take((size_t)kDpaBytes * L.npad);
   L.dwpart = (float *)take((size_t)L.ntb * K * kJ * 4);
   return L;
 }
@@ -509,28 +510,23 @@ size_t proj_bwd_ws(int64_t N, int64_t C, bool f32) {
   const int64_t K = 4 * C;
   BwdWs L = bwd_layout(nullptr, N, C, f32);
   size_t total = align256((size_t)N * kDpf * 4) + align256((size_t)N * 16) + align256((size_t)L.nblk * 128);
-  if (!f32) total += align256((size_t)3 * kJ * L.npad * 2);
+  if (!f32) total += align256((size_t)kDpaBytes * L.npad);
   return total + align256((size_t)L.ntb * K * kJ * 4);
 }
 
 __device__ __forceinline__ uint16_t bf16_bits(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
 
-// dpB layout: per 32-token block, [half s (16 tokens)][term][j][16 tokens].
-// Element (t, j) of term 0; terms 1 and 2 follow at +kJ*16 and +2*kJ*16.
-__device__ __forceinline__ int64_t dpb_index(int64_t t, int j) {
-  const int64_t blk = t >> 5;
-  const int s = (int)((t >> 4) & 1), e = (int)(t & 15);
-  return blk * (2 * 3 * kJ * 16) + ((int64_t)(s * 3) * kJ + j) * 16 + e;
-}
-
 // One thread per token (grid covers npad tokens; tokens >= N only zero their
-// dpB column).  Block partial sums of dhbias (24) and dalpha (3) go to ppart.
+// dpA record).  Block partial sums of dhbias (24) and dalpha (3) go to ppart.
+// MFMA_OUT (bf16 activations): the token's record for the MFMA kernel is the
+// exact three-term bf16 split of dp, [term][j], then c_rms (fp32) and zero
+// padding (kDpaBytes).  Otherwise dp and c_rms go to the fp32 row dpf.
 template <bool MFMA_OUT>
 __global__ __launch_bounds__(256) void proj_bwd_token_kernel(
     const float *__restrict__ alpha, const float *__restrict__ saved, const float *__restrict__ Hpre,
     const float *__restrict__ Hpost, const float *__restrict__ dHpre, const float *__restrict__ dHpost,
     const float *__restrict__ dL_in, const float *__restrict__ dHres, const float *__restrict__ logits,
-    int iters, float eps, float *__restrict__ dpf, bf16_t *__restrict__ dpB,
+    int iters, float eps, float *__restrict__ dpf, char *__restrict__ dpA,
     float *__restrict__ ppart, float *__restrict__ dL_out, float *__restrict__ dHpre_out, int64_t N,
     int64_t npad, int64_t K) {
   __shared__ float red[4][28];
@@ -579,40 +575,45 @@ __global__ __launch_bounds__(256) void proj_bwd_token_kernel(
       dp[j] = r * dz;
     }
     const float crms = q > 0.f ? -S * r / ((float)K * q) : 0.f;
-    float rowf[kDpf];
-#pragma unroll
-    for (int j = 0; j < kJ; ++j) rowf[j] = dp[j];
-    rowf[kJ] = crms;
-#pragma unroll
-    for (int j = kJ + 1; j < kDpf; ++j) rowf[j] = 0.f;
-#pragma unroll
-    for (int qd = 0; qd < kDpf / 4; ++qd)
-      reinterpret_cast<float4 *>(dpf + t * kDpf)[qd] =
-          make_float4(rowf[4 * qd], rowf[4 * qd + 1], rowf[4 * qd + 2], rowf[4 * qd + 3]);
     if (MFMA_OUT) {
-      uint16_t hi[kJ], mid[kJ], lo[kJ];
+      uint32_t w[3][kJ / 2];  // [term][j pair]
 #pragma unroll
-      for (int j = 0; j < kJ; ++j) {
-        const float h = bf16_round(dp[j]);
-        const float r1 = dp[j] - h;
-        const float m = bf16_round(r1);
-        hi[j] = bf16_bits(h);
-        mid[j] = bf16_bits(m);
-        lo[j] = bf16_bits(r1 - m);
-      }
+      for (int j = 0; j < kJ; j += 2) {
+        float h2[2], m2[2], l2[2];
 #pragma unroll
-      for (int j = 0; j < kJ; ++j) {
-        bf16_t *blk = dpB + dpb_index(t, j);
-        blk[0 * kJ * 16] = hi[j];
-        blk[1 * kJ * 16] = mid[j];
-        blk[2 * kJ * 16] = lo[j];
+        for (int e = 0; e < 2; ++e) {
+          h2[e] = bf16_round(dp[j + e]);
+          const float r1 = dp[j + e] - h2[e];
+          m2[e] = bf16_round(r1);
+          l2[e] = r1 - m2[e];
+        }
+        w[0][j / 2] = pack_bf16x2(h2[0], h2[1]);
+        w[1][j / 2] = pack_bf16x2(m2[0], m2[1]);
+        w[2][j / 2] = pack_bf16x2(l2[0], l2[1]);
       }
+      uint4 *rec = reinterpret_cast<uint4 *>(dpA + t * kDpaBytes);
+#pragma unroll
+      for (int tm = 0; tm < 3; ++tm)
+#pragma unroll
+        for (int m = 0; m < 3; ++m)
+          rec[tm * 3 + m] = make_uint4(w[tm][4 * m], w[tm][4 * m + 1], w[tm][4 * m + 2], w[tm][4 * m + 3]);
+      rec[9] = make_uint4(__float_as_uint(crms), 0u, 0u, 0u);
+    } else {
+      float rowf[kDpf];
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) rowf[j] = dp[j];
+      rowf[kJ] = crms;
+#pragma unroll
+      for (int j = kJ + 1; j < kDpf; ++j) rowf[j] = 0.f;
+#pragma unroll
+      for (int qd = 0; qd < kDpf / 4; ++qd)
+        reinterpret_cast<float4 *>(dpf + t * kDpf)[qd] =
+            make_float4(rowf[4 * qd], rowf[4 * qd + 1], rowf[4 * qd + 2], rowf[4 * qd + 3]);
     }
   } else if (MFMA_OUT && t < npad) {
+    uint4 *rec = reinterpret_cast<uint4 *>(dpA + t * kDpaBytes);
 #pragma unroll
-    for (int j = 0; j < kJ; ++j)
-#pragma unroll
-      for (int tm = 0; tm < 3; ++tm) dpB[dpb_index(t, j) + tm * kJ * 16] = 0;
+    for (int i = 0; i < kDpaBytes / 16; ++i) rec[i] = make_uint4(0u, 0u, 0u, 0u);
   }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
@@ -678,17 +679,24 @@ constexpr int kB2Stages = 3;
 constexpr int kB2Quarter = 32 * 128;  // bytes of one 32 x 64 bf16 tile
 constexpr int kB2AccRow = 36;         // floats per row of a wave's 32 x 32 accumulator half
 
-template <bool HAS_G, bool DW, bool POST>
+template <bool HAS_G, bool POST>
 struct B2Lay {
   static constexpr int X = 0;
   static constexpr int G = 4 * kB2Quarter;                               // g
   static constexpr int Q = G + (HAS_G ? (POST ? 1 : 4) * kB2Quarter : 0);  // G of h_post_bda
-  static constexpr int P = Q + (POST ? 4 * kB2Quarter : 0);
-  static constexpr int B = P + 32 * kDpf * 4;
-  static constexpr int stage = B + (DW ? 2 * 3 * kJ * 16 * 2 : 0);
+  static constexpr int P = Q + (POST ? 4 * kB2Quarter : 0);              // 32 dp records
+  static constexpr int stage = P + 32 * kDpaBytes;
   static constexpr int acc = kB2Stages * stage;
   static constexpr int total = acc + 4 * 32 * kB2AccRow * 4;
 };
+
+// dp W^T runs on bf16 MFMA with dp and W both split exactly into three bf16
+// terms (hi, mid, lo); of the nine term products the six above 2^-24 relative
+// are kept: (hi,hi) (hi,mid) (mid,hi) (hi,lo) (lo,hi) (mid,mid).  The
+// contraction runs over (pair, j): 6 x 24 = 144 = 9 chunks of 16, and in
+// chunk c lane half h takes the 8 j of group (2c + h) % 3 of pair (2c + h) / 3.
+__constant__ constexpr int kPairA[6] = {0, 0, 1, 0, 2, 1};  // dp term of each pair
+__constant__ constexpr int kPairB[6] = {0, 1, 0, 2, 0, 1};  // W term of each pair
 
 // vmcnt <= n for a wave-uniform n; a value outside the table waits for all.
 __device__ __forceinline__ void wait_vmcnt_le(int n) {
@@ -731,12 +739,12 @@ struct DxPre {
 
 template <bool ACCUM, bool HAS_G, bool DW, bool POST>
 __global__ __launch_bounds__(512) void proj_bwd_mfma_kernel(
-    const bf16_t *__restrict__ X, const float *__restrict__ W, const bf16_t *__restrict__ dpB,
-    const float *__restrict__ dpf, const float *__restrict__ Hpre, const bf16_t *__restrict__ gr,
-    const bf16_t *__restrict__ Gp, const float *__restrict__ Hres, bf16_t *__restrict__ dX,
-    float *__restrict__ dWpart, int64_t N, int64_t C, int64_t tbsz, int group4) {
+    const bf16_t *__restrict__ X, const float *__restrict__ W, const char *__restrict__ dpA,
+    const float *__restrict__ Hpre, const bf16_t *__restrict__ gr, const bf16_t *__restrict__ Gp,
+    const float *__restrict__ Hres, bf16_t *__restrict__ dX, float *__restrict__ dWpart, int64_t N, int64_t C,
+    int64_t tbsz, int group4) {
   constexpr bool SPW = POST;  // stream-per-wave channel tiles
-  using L = B2Lay<HAS_G, DW, POST>;
+  using L = B2Lay<HAS_G, POST>;
   extern __shared__ __attribute__((aligned(16))) char b2lds[];
   const int64_t K = 4 * C;
   const int64_t nkt = SPW ? (C + kBwKW - 1) / kBwKW : (K + 4 * kBwKW - 1) / (4 * kBwKW);
@@ -778,7 +786,7 @@ __global__ __launch_bounds__(512) void proj_bwd_mfma_kernel(
   // channel of the lane's piece (g and G tiles); a real channel when the
   // piece lies past the tile
   const int64_t gcol = SPW ? (dvalid ? c0 + 8 * dpiece : c0) : xk - (xk / C) * C;
-  const int nload = 4 + (HAS_G ? (SPW ? 1 : 4) : 0) + (POST ? 4 : 0) + 1 + (DW ? (kq == 0 ? 2 : 1) : 0);
+  const int nload = 4 + (HAS_G ? (SPW ? 1 : 4) : 0) + (POST ? 4 : 0) + (kq == 0 ? 2 : 1);
 
   auto issue = [&](int i) {
     char *st = b2lds + (i % kB2Stages) * L::stage;
@@ -790,14 +798,15 @@ __global__ __launch_bounds__(512) void proj_bwd_mfma_kernel(
       if (HAS_G && !SPW) dma16(gr + t * C + gcol, st + L::G + kq * kB2Quarter + q * 1024);
       if (POST) dma16(Gp + (t * 4 + kq) * C + gcol, st + L::Q + kq * kB2Quarter + q * 1024);
     }
-    const int64_t t = min(t0 + 8 * kq + drow, N - 1);
-    if (HAS_G && SPW) dma16(gr + t * C + gcol, st + L::G + kq * 1024);
-    dma16(dpf + t * kDpf + 4 * dpiece, st + L::P + kq * 1024);
-    if (DW) {
-      const bf16_t *src = dpB + (t0 >> 5) * (2 * 3 * kJ * 16);
-      dma16(src + kq * 512 + lane * 8, st + L::B + kq * 1024);
-      if (kq == 0 && lane < 32) dma16(src + 2048 + lane * 8, st + L::B + 4096);
+    if (HAS_G && SPW) {
+      const int64_t t = min(t0 + 8 * kq + drow, N - 1);
+      dma16(gr + t * C + gcol, st + L::G + kq * 1024);
     }
+    // the sub-tile's 32 dp records are contiguous (records exist up to the
+    // 32-token padding, zero past N): 5 KB in five 1 KB copies
+    const char *rs = dpA + t0 * kDpaBytes;
+    dma16(rs + kq * 1024 + lane * 16, st + L::P + kq * 1024);
+    if (kq == 0) dma16(rs + 4096 + lane * 16, st + L::P + 4096);
   };
 
   // ---- dX geometry: in accumulator half ct (k = 32 ct .. +32 of the
@@ -830,17 +839,39 @@ __global__ __launch_bounds__(512) void proj_bwd_mfma_kernel(
     }
   };
 
-  float wf[2][12];
+  // B fragments of dp W^T: W[k][*] of this lane's column k split into its
+  // three terms, arranged by chunk (see kPairB)
+  u32x4 wb[2][9];
   f32x16 accW[2];
   if (!loader) {
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       const bool kv = 32 * ct + col < nvalid;
+      uint32_t tw[3][kJ / 2];  // [term][j pair]
 #pragma unroll
-      for (int s4 = 0; s4 < 3; ++s4) {
-        const float4 v = kv ? *reinterpret_cast<const float4 *>(W + (kbase + 32 * ct + col) * kJ + 12 * h + 4 * s4)
+      for (int s4 = 0; s4 < kJ / 4; ++s4) {
+        const float4 v = kv ? *reinterpret_cast<const float4 *>(W + (kbase + 32 * ct + col) * kJ + 4 * s4)
                             : make_float4(0.f, 0.f, 0.f, 0.f);
-        wf[ct][4 * s4] = v.x; wf[ct][4 * s4 + 1] = v.y; wf[ct][4 * s4 + 2] = v.z; wf[ct][4 * s4 + 3] = v.w;
+        const float w4[4] = {v.x, v.y, v.z, v.w};
+        float th[4], tmid[4], tl[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          th[e] = bf16_round(w4[e]);
+          const float r1 = w4[e] - th[e];
+          tmid[e] = bf16_round(r1);
+          tl[e] = r1 - tmid[e];
+        }
+        tw[0][2 * s4] = pack_bf16x2(th[0], th[1]); tw[0][2 * s4 + 1] = pack_bf16x2(th[2], th[3]);
+        tw[1][2 * s4] = pack_bf16x2(tmid[0], tmid[1]); tw[1][2 * s4 + 1] = pack_bf16x2(tmid[2], tmid[3]);
+        tw[2][2 * s4] = pack_bf16x2(tl[0], tl[1]); tw[2][2 * s4 + 1] = pack_bf16x2(tl[2], tl[3]);
+      }
+#pragma unroll
+      for (int c = 0; c < 9; ++c) {
+        const int g0 = 2 * c, g1 = 2 * c + 1;
+        const int b0 = kPairB[g0 / 3], m0 = g0 % 3, b1 = kPairB[g1 / 3], m1 = g1 % 3;
+        const u32x4 v0 = {tw[b0][4 * m0], tw[b0][4 * m0 + 1], tw[b0][4 * m0 + 2], tw[b0][4 * m0 + 3]};
+        const u32x4 v1 = {tw[b1][4 * m1], tw[b1][4 * m1 + 1], tw[b1][4 * m1 + 2], tw[b1][4 * m1 + 3]};
+        wb[ct][c] = h ? v1 : v0;
       }
     }
   }
@@ -880,14 +911,27 @@ __global__ __launch_bounds__(512) void proj_bwd_mfma_kernel(
             }
             xa[rt][s] = u32x4{w4[0], w4[1], w4[2], w4[3]};
           }
-        const bf16_t *bs = reinterpret_cast<const bf16_t *>(st + L::B);
+        // B = dp term tm at j = col for the same 8 tokens, gathered from the
+        // sub-tile's dp records
+        const char *ps = st + L::P;
         u32x4 bfr[2][3];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
-          for (int tm = 0; tm < 3; ++tm)
-            bfr[s][tm] = col < kJ ? *reinterpret_cast<const u32x4 *>(bs + ((s * 3 + tm) * kJ + col) * 16 + 8 * h)
-                                  : u32x4{0u, 0u, 0u, 0u};
+          for (int tm = 0; tm < 3; ++tm) {
+            uint32_t w4[4] = {0u, 0u, 0u, 0u};
+            if (col < kJ) {
+#pragma unroll
+              for (int p = 0; p < 4; ++p) {
+                const int r0 = 16 * s + 8 * h + 2 * p;
+                const int off = (tm * 3 + (col >> 3)) * 16 + (col & 7) * 2;
+                const uint32_t lo16 = *reinterpret_cast<const uint16_t *>(ps + r0 * kDpaBytes + off);
+                const uint32_t hi16 = *reinterpret_cast<const uint16_t *>(ps + (r0 + 1) * kDpaBytes + off);
+                w4[p] = lo16 | (hi16 << 16);
+              }
+            }
+            bfr[s][tm] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+          }
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -909,13 +953,15 @@ __global__ __launch_bounds__(512) void proj_bwd_mfma_kernel(
       lds_barrier();
       const char *st = b2lds + (i % kB2Stages) * L::stage;
       const int64_t t0 = t_begin + 32 * (int64_t)i;
-      // (a) dp W^T for 32 tokens x 64 k; dp[t0 + col][12h .. 12h+12) from LDS
+      // (a) dp W^T for 32 tokens x 64 k: A fragments (token t0 + col) from
+      // the dp records, 2 x 9 bf16 MFMAs
       const char *ps = st + L::P;
-      float af[12];
+      u32x4 af[9];
 #pragma unroll
-      for (int s4 = 0; s4 < 3; ++s4) {
-        const float4 v = *reinterpret_cast<const float4 *>(ps + col * 128 + 16 * ((3 * h + s4) ^ (col & 7)));
-        af[4 * s4] = v.x; af[4 * s4 + 1] = v.y; af[4 * s4 + 2] = v.z; af[4 * s4 + 3] = v.w;
+      for (int c = 0; c < 9; ++c) {
+        const int g0 = 2 * c, g1 = 2 * c + 1;
+        const int p0 = kPairA[g0 / 3] * 3 + g0 % 3, p1 = kPairA[g1 / 3] * 3 + g1 % 3;
+        af[c] = *reinterpret_cast<const u32x4 *>(ps + col * kDpaBytes + (h ? p1 : p0) * 16);
       }
       f32x16 accX[2];
 #pragma unroll
@@ -923,8 +969,9 @@ __global__ __launch_bounds__(512) void proj_bwd_mfma_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) accX[ct][r] = 0.f;
 #pragma unroll
-        for (int s = 0; s < 12; ++s)
-          accX[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[s], wf[ct][s], accX[ct], 0, 0, 0);
+        for (int c = 0; c < 9; ++c)
+          accX[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[c]),
+                                                            __builtin_bit_cast(bf16x8, wb[ct][c]), accX[ct], 0, 0, 0);
       }
       // (b) dX = dp W^T + c_rms x + H_pre g + sum_i H_res[j][i] G[i] + dX_in,
       // one 32 x 32 half at a time: transpose through the wave's LDS area,
@@ -951,7 +998,7 @@ __global__ __launch_bounds__(512) void proj_bwd_mfma_kernel(
           const float4 a0 = *reinterpret_cast<const float4 *>(&acc_t[row * kB2AccRow + ek]);
           const float4 a1 = *reinterpret_cast<const float4 *>(&acc_t[row * kB2AccRow + ek + 4]);
           const float acc8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-          const float crms = *reinterpret_cast<const float *>(ps + row * 128 + 16 * (6 ^ (row & 7)));
+          const float crms = *reinterpret_cast<const float *>(ps + row * kDpaBytes + 9 * 16);
           const u32x4 xv = *reinterpret_cast<const u32x4 *>(xs + row * 128 + 16 * slot);
           const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
           float o[8];
@@ -1113,10 +1160,10 @@ static void launch_b2_dw(hipStream_t s, const ProjBwdArgs &a, const BwdWs &L) {
   const int64_t nkt = POST ? (a.C + kBwKW - 1) / kBwKW : (K + 4 * kBwKW - 1) / (4 * kBwKW);
   const int group4 = (!POST && a.C % (4 * kBwKW) == 0) ? 1 : 0;
   const int64_t blocks = group4 ? round_up(nkt * L.ntb, 32) : nkt * L.ntb;
-  const size_t lds = (size_t)B2Lay<HAS_G, DW, POST>::total;
+  const size_t lds = (size_t)B2Lay<HAS_G, POST>::total;
   hipLaunchKernelGGL((proj_bwd_mfma_kernel<ACCUM, HAS_G, DW, POST>), dim3((unsigned)blocks), dim3(512), lds, s,
-                     (const bf16_t *)a.X, a.W, L.dpB, L.dpf, a.H_pre, (const bf16_t *)a.g, (const bf16_t *)a.post_G,
-                     a.post_H_res, (bf16_t *)a.dX, L.dwpart, a.N, a.C, L.tbsz, group4);
+                     (const bf16_t *)a.X, a.W, (const char *)L.dpA, a.H_pre, (const bf16_t *)a.g,
+                     (const bf16_t *)a.post_G, a.post_H_res, (bf16_t *)a.dX, L.dwpart, a.N, a.C, L.tbsz, group4);
 }
 
 template <bool ACCUM, bool HAS_G>
@@ -1160,11 +1207,11 @@ void launch_proj_bwd(hipStream_t s, const ProjBwdArgs &a) {
   if (a.f32)
     hipLaunchKernelGGL((proj_bwd_token_kernel<false>), dim3((unsigned)L.nblk), dim3(256), 0, s, a.alpha, a.saved,
                        a.H_pre, a.H_post, dHpre, a.dH_post, a.dL, a.dH_res, a.logits, a.iters, a.eps, L.dpf,
-                       L.dpB, L.ppart, a.dL_out, a.dH_pre_out, N, L.npad, K);
+                       L.dpA, L.ppart, a.dL_out, a.dH_pre_out, N, L.npad, K);
   else
     hipLaunchKernelGGL((proj_bwd_token_kernel<true>), dim3((unsigned)L.nblk), dim3(256), 0, s, a.alpha, a.saved,
                        a.H_pre, a.H_post, dHpre, a.dH_post, a.dL, a.dH_res, a.logits, a.iters, a.eps, L.dpf,
-                       L.dpB, L.ppart, a.dL_out, a.dH_pre_out, N, L.npad, K);
+                       L.dpA, L.ppart, a.dL_out, a.dH_pre_out, N, L.npad, K);
   const bool hg = a.g != nullptr;
   if (a.accumulate) {
     if (hg) launch_dx<true, true>(s, a, L);
