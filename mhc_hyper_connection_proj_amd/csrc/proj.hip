@@ -227,6 +227,10 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ void dma16(const void *g, void *lds_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds_base, 16, 0, 0);
 }
+// The same with the non-temporal cache policy, for a stream read once.
+__device__ __forceinline__ void dma16_nt(const void *g, void *lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds_base, 16, 0, 2);
+}
 
 // s_waitcnt with vmcnt <= n (expcnt and lgkmcnt left unconstrained).
 template <int n>
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(512) void proj_partial_dma_kernel(const bf16_t *__r
       const int64_t t = min(tw + rr, N - 1);              // rows past N re-read row N-1 (never stored)
       int64_t k = k0 + 8 * p;
       if (k >= K) k -= 32;                                // past K: any valid address (W rows there are 0)
-      dma16(X + t * K + k, xs + q * 512);
+      dma16_nt(X + t * K + k, xs + q * 512);
     }
   };
 
