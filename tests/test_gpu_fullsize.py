@@ -120,6 +120,14 @@ def test_post_bda_full_size(name):
         assert not h64(rows(t, Z)).any(), f"{nm}: nonzero on tokens with zero upstream gradient"
     if bias is not None:
         assert_tokensum("dbias", db, rdb, np.abs(rdx).sum(axis=0), w.act)
+    # as timed: no dX (the pre backward forms it) and no dbias
+    _, dHr2, dHp2, dx2, _ = B.mhc_h_post_bda_bwd(dev(G), Xd, Hr, Hp, xd, bd, want_dbias=False, want_dX=False)
+    torch.cuda.synchronize()
+    assert_mixed("dH_res (no dX)", rows(dHr2, S), rdHr)
+    assert_mixed("dH_post (no dX)", rows(dHp2, S), rdHp)
+    assert_act("dx (no dX)", rows(dx2, S), rdx, w.act)
+    for nm, t in (("dH_res", dHr2), ("dH_post", dHp2), ("dx", dx2)):
+        assert not h64(rows(t, Z)).any(), f"{nm} (no dX): nonzero on tokens with zero upstream gradient"
 
 
 # ----------------------------------------------------------------- pre pass backward
