@@ -145,7 +145,7 @@ def test_h_post_bda_identity_h_res_exact_bf16():
 
 # ----------------------------------------------------------------- projection
 PROJ = [("f32", 64, 256), ("bf16", 37, 296), ("bf16", 70, 4096), ("bf16", 67, 7168),
-        ("bf16", 5, 8), ("f32", 33, 1032), ("bf16", 129, 1024)]
+        ("bf16", 5, 8), ("f32", 33, 1032), ("bf16", 129, 1024), ("bf16", 33, 16384)]
 
 
 def _proj_inputs(act, N, C, zero_row=True):
@@ -203,7 +203,8 @@ def test_proj_rms_h_bwd(act, N, C):
 
 # ----------------------------------------------------------------- fused pre pass
 @pytest.mark.parametrize("mode", ["accumulate", "post"])
-@pytest.mark.parametrize("act,N,C", [("f32", 64, 256), ("bf16", 37, 296), ("bf16", 66, 7168), ("bf16", 130, 4096)])
+@pytest.mark.parametrize("act,N,C", [("f32", 64, 256), ("bf16", 37, 296), ("bf16", 66, 7168), ("bf16", 130, 4096),
+                                     ("bf16", 1000, 2048), ("bf16", 33, 16384)])
 def test_pre_fwd_bwd(act, N, C, mode):
     log(f"pre fwd/bwd act={act} N={N} C={C} mode={mode}")
     X, W, alpha, hb = _proj_inputs(act, N, C)
