@@ -438,14 +438,16 @@ void launch_proj_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *
 //   dX[t][k] (+)= H_pre[t][i] g[t][c] + c_rms[t] x[t][k] + sum_j dp[t][j] W[k][j]
 //   dW[k][j]    = sum_t x[t][k] dp[t][j]
 // Both contractions run on MFMA for bf16 activations:
-//  * dX: fp32 MFMA (32x32x2) on dp and W as they are.  A bf16 split of dp
-//    and W is not accurate enough here: for an all-zero residual row
-//    r = 1/eps amplifies dp to ~1e5 while dX entries cancel to O(1).
-//  * dW: bf16 MFMA.  The contraction runs over tokens, so each wave stages its 32x64 X
-//    tile in LDS and reads 8-token columns as A fragments; dp comes split
-//    exactly into hi + mid + lo bf16 terms, laid out per 32-token block as
-//    [half s][term][j][16 tokens] so the B fragment of one (s, term) is a
-//    contiguous 768-byte read across the wave.
+//  * dX: bf16 MFMA on the exact three-term splits of dp (hi + mid + lo, from
+//    the per-token record) and of W (split in registers), keeping the six
+//    term products hh, hm, mh, hl, lh, mm; the three dropped ones are below
+//    2^-24 of |dp||W|.  Two terms are not enough here: for an all-zero
+//    residual row r = 1/eps amplifies dp to ~1e5 while dX entries cancel to
+//    O(1).
+//  * dW: bf16 MFMA.  The contraction runs over tokens, so the X tile is
+//    staged in LDS and 8-token columns are read as A fragments; the B
+//    fragments are 8-token columns of the dp terms gathered from the
+//    records.
 // fp32 activations use a VALU kernel for both contractions.
 constexpr int kDpf = 32;     // fp32 per-token record: dp[24], c_rms, pad
 constexpr int kDpaBytes = 160;  // bf16 per-token record: dp terms [3][24], c_rms (fp32), pad
@@ -487,9 +489,10 @@ static int64_t bwd_token_block(int64_t N, int64_t K, bool f32) {
 }
 
 struct BwdWs {
-  float *dpf, *dhpre, *ppart, *dwpart;
-  char *dpA;
+  float *dpf, *dhpre, *ppart, *dwpart;  // dpf: fp32 activations only
+  char *dpA;                            // bf16 activations only
   int64_t npad, nblk, tbsz, ntb;
+  size_t bytes;                         // workspace size
 };
 
 static BwdWs bwd_layout(void *ws, int64_t N, int64_t C, bool f32) {
@@ -502,21 +505,16 @@ static BwdWs bwd_layout(void *ws, int64_t N, int64_t C, bool f32) {
   size_t off = 0;
   char *b = (char *)ws;
   auto take = [&](size_t bytes) { char *p = b ? b + off : nullptr; off += align256(bytes); return p; };
-  L.dpf = (float *)take((size_t)N * kDpf * 4);
+  if (f32) L.dpf = (float *)take((size_t)N * kDpf * 4);
+  else L.dpA = take((size_t)kDpaBytes * L.npad);
   L.dhpre = (float *)take((size_t)N * 16);
   L.ppart = (float *)take((size_t)L.nblk * 32 * 4);
-  if (!f32) L.dpA = take((size_t)kDpaBytes * L.npad);
   L.dwpart = (float *)take((size_t)L.ntb * K * kJ * 4);
+  L.bytes = off;
   return L;
 }
 
-size_t proj_bwd_ws(int64_t N, int64_t C, bool f32) {
-  const int64_t K = 4 * C;
-  BwdWs L = bwd_layout(nullptr, N, C, f32);
-  size_t total = align256((size_t)N * kDpf * 4) + align256((size_t)N * 16) + align256((size_t)L.nblk * 128);
-  if (!f32) total += align256((size_t)kDpaBytes * L.npad);
-  return total + align256((size_t)L.ntb * K * kJ * 4);
-}
+size_t proj_bwd_ws(int64_t N, int64_t C, bool f32) { return bwd_layout(nullptr, N, C, f32).bytes; }
 
 __device__ __forceinline__ uint16_t bf16_bits(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
 
@@ -656,12 +654,12 @@ __global__ __launch_bounds__(256) void param_final_kernel(const float *__restric
 // Workgroup = 8 waves on one token block and one k tile of four 64-k quarters,
 // walked in 32-token sub-tiles through a 3-stage LDS ring:
 //  * waves 4..7 (loaders) fill each stage with global_load_lds_dwordx4: the X
-//    tile, the g tile, the h_post_bda upstream gradient G (POST), the fp32 dp
-//    rows and the bf16 dp terms of the sub-tile, two sub-tiles ahead.  With
+//    tile, the g tile, the h_post_bda upstream gradient G (POST) and the 32
+//    per-token dp records of the sub-tile, two sub-tiles ahead.  With
 //    dW they then run x^T dp on MFMA (loader w-4 owns quarter w-4; A
 //    fragments are 8-token X columns read from LDS, B fragments the dp terms);
-//  * waves 0..3 own one quarter each: dp W^T on fp32 MFMA (W held in
-//    registers), each 32 x 32 half of the accumulator transposed through a
+//  * waves 0..3 own one quarter each: dp W^T on bf16 MFMA (W's three terms
+//    held in registers), each 32 x 32 half of the accumulator transposed through a
 //    private LDS area, then the dX epilogue with dX_in, H_pre and H_res rows
 //    loaded one sub-tile ahead into registers.
 // One barrier per sub-tile: loaders first wait for their own loads of the
@@ -669,10 +667,10 @@ __global__ __launch_bounds__(256) void param_final_kernel(const float *__restric
 // guarantees that the slot refilled next has been read by every wave.  The
 // loaders issue no other global memory instructions inside the loop, which
 // keeps their vmcnt arithmetic exact.
-// In every 128-byte LDS row (64 bf16 of X, g or G, 32 fp32 of dp) the
-// 16-byte piece p of row r sits in slot p ^ (r & 7): the DMA lanes of an
-// instruction cover 8 rows x 8 slots, and the row-wise and column-wise reads
-// below spread over the banks.
+// In every 128-byte LDS row (64 bf16 of X, g or G) the 16-byte piece p of
+// row r sits in slot p ^ (r & 7): the DMA lanes of an instruction cover 8
+// rows x 8 slots, and the row-wise and column-wise reads below spread over
+// the banks.  The 32 dp records (160 bytes each) are copied as they are.
 // Channel tiles: without the h_post_bda term, 256 consecutive k (g pieces
 // addressed per piece; when C is a multiple of 256 the four tiles that read
 // the same g tile run back to back on one XCD).  With it (POST), one
@@ -754,7 +752,16 @@ __global__ __launch_bounds__(512) void proj_bwd_mfma_kernel(
   const int64_t nkt = SPW ? (C + kBwKW - 1) / kBwKW : (K + 4 * kBwKW - 1) / (4 * kBwKW);
   const int64_t ntb = (N + tbsz - 1) / tbsz;
   int64_t kt, tbi;
-  if (!SPW && group4) {
+  if (SPW) {
+    // XCD-contiguous order: workgroups are dispatched round-robin over the 8
+    // XCDs, so XCD b % 8 takes tiles [x * per, (x + 1) * per) in order and its
+    // CUs read neighbouring 128-byte row pieces of the same tokens together
+    const int64_t T = nkt * ntb, per = (T + 7) / 8;
+    const int64_t tile = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+    if (tile >= T) return;  // grid padding to a multiple of 8 (whole workgroup)
+    tbi = tile / nkt;
+    kt = tile % nkt;
+  } else if (group4) {
     const int64_t b = blockIdx.x, nct = C / (4 * kBwKW);
     const int64_t pidx = (b / 32) * 8 + (b % 8);
     if (pidx >= ntb * nct) return;  // grid padding to a multiple of 32 (whole workgroup)
@@ -1163,7 +1170,7 @@ static void launch_b2_dw(hipStream_t s, const ProjBwdArgs &a, const BwdWs &L) {
   const int64_t K = 4 * a.C;
   const int64_t nkt = POST ? (a.C + kBwKW - 1) / kBwKW : (K + 4 * kBwKW - 1) / (4 * kBwKW);
   const int group4 = (!POST && a.C % (4 * kBwKW) == 0) ? 1 : 0;
-  const int64_t blocks = group4 ? round_up(nkt * L.ntb, 32) : nkt * L.ntb;
+  const int64_t blocks = POST ? round_up(nkt * L.ntb, 8) : group4 ? round_up(nkt * L.ntb, 32) : nkt * L.ntb;
   const size_t lds = (size_t)B2Lay<HAS_G, POST>::total;
   hipLaunchKernelGGL((proj_bwd_mfma_kernel<ACCUM, HAS_G, DW, POST>), dim3((unsigned)blocks), dim3(512), lds, s,
                      (const bf16_t *)a.X, a.W, (const char *)L.dpA, a.H_pre, (const bf16_t *)a.g,
