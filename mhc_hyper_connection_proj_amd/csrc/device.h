@@ -75,6 +75,15 @@ template <> struct Io8<bf16_t> {
     w.w = pack_bf16x2(v[6], v[7]);
     *reinterpret_cast<uint4 *>(p) = w;
   }
+  // non-temporal store, for outputs that no later kernel of the pass reads
+  static __device__ __forceinline__ void store_nt(bf16_t *p, const float v[8]) {
+    nt_u32x4 w;
+    w.x = pack_bf16x2(v[0], v[1]);
+    w.y = pack_bf16x2(v[2], v[3]);
+    w.z = pack_bf16x2(v[4], v[5]);
+    w.w = pack_bf16x2(v[6], v[7]);
+    __builtin_nontemporal_store(w, reinterpret_cast<nt_u32x4 *>(p));
+  }
 };
 
 template <> struct Io8<float> {
@@ -109,6 +118,10 @@ template <> struct Io8<float> {
   static __device__ __forceinline__ void store(float *p, const float v[8]) {
     *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
     *reinterpret_cast<float4 *>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  static __device__ __forceinline__ void store_nt(float *p, const float v[8]) {
+    __builtin_nontemporal_store(nt_f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<nt_f32x4 *>(p));
+    __builtin_nontemporal_store(nt_f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<nt_f32x4 *>(p + 4));
   }
 };
 

@@ -146,6 +146,11 @@ __global__ __launch_bounds__(512) void h_aggregate_bwd_kernel(
 }
 
 // ============================================================ h_post_bda fwd
+// The new residual is written with non-temporal stores: its 8C bytes per
+// token otherwise sit dirty in the caches when the kernel ends, and their
+// write-back then lands in the next kernel's read stream (on MI355X the
+// following h_post_bda backward measured ~50 us slower at C = 7168, 16384
+// tokens; this kernel itself ran no slower).
 template <typename T, int GPT, bool HAS_BIAS>
 __global__ __launch_bounds__(512) void h_post_bda_fwd_kernel(
     const T *__restrict__ X, const float *__restrict__ Hres, const float *__restrict__ Hpost,
@@ -189,7 +194,7 @@ __global__ __launch_bounds__(512) void h_post_bda_fwd_kernel(
         for (int e = 0; e < 8; ++e)
           o[e] = (hr[0 * 4 + i] * xv[0][e] + hr[1 * 4 + i] * xv[1][e]) +
                  (hr[2 * 4 + i] * xv[2][e] + hr[3 * 4 + i] * xv[3][e]) + hp[i] * lv[e];
-        Io8<T>::store(ot + i * C + 8 * g, o);
+        Io8<T>::store_nt(ot + i * C + 8 * g, o);
       }
     }
   }

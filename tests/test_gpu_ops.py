@@ -93,7 +93,8 @@ def test_h_aggregate_one_hot_exact():
 # ----------------------------------------------------------------- h_post_bda
 @pytest.mark.parametrize("act,N,C,bias", [
     ("bf16", 1, 256, True), ("bf16", 37, 296, True), ("bf16", 50, 4096, True), ("bf16", 21, 7168, False),
-    ("f32", 64, 256, True), ("f32", 17, 1032, False), ("bf16", 33, 8, True), ("bf16", 3, 16384, True)])
+    ("f32", 64, 256, True), ("f32", 17, 1032, False), ("bf16", 33, 8, True), ("bf16", 3, 16384, True),
+    ("bf16", 9, 5120, False), ("bf16", 6, 6144, True), ("bf16", 4, 8192, False), ("bf16", 5, 7168, True)])
 def test_h_post_bda(act, N, C, bias):
     log(f"h_post_bda act={act} N={N} C={C} bias={bias}")
     X = store(RNG.standard_normal((N, 4, C)), act)
@@ -120,11 +121,14 @@ def test_h_post_bda(act, N, C, bias):
     # without dX (the pre backward forms it), also without dbias: the other
     # outputs to the same rules (another kernel may serve this case, so the
     # fp32 summation order, and the last bits, can differ from the run above)
-    for want_db in ((True, False) if bias else (False,)):
+    for want_db, want_dX in (((True, False), (False, False), (False, True)) if bias else ((False, False),)):
         nX, nHr, nHp, ndx, ndb = B.mhc_h_post_bda_bwd(dev(G), dev(X), dev(Hr), dev(Hp), dev(x),
-                                                      dev(b) if bias else None, want_dbias=want_db, want_dX=False)
+                                                      dev(b) if bias else None, want_dbias=want_db, want_dX=want_dX)
         torch.cuda.synchronize()
-        assert nX is None
+        if want_dX:
+            assert_act("dX (no dbias)", nX, odX, act)
+        else:
+            assert nX is None
         assert_mixed("dH_res (no dX)", nHr, odHr)
         assert_mixed("dH_post (no dX)", nHp, odHp)
         assert_act("dx (no dX)", ndx, odx, act)
