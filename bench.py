@@ -44,6 +44,9 @@ def ledger_bytes_per_token(C: int, N: int) -> dict:
         "pre_bwd": 2 * C + 8 * C + 8 * C + 64 + 16 + 64 + 128 + 16 + 16 + 64 + 8 * C + 2 * w_amort,
     }
     phases["total"] = sum(phases.values())
+    # the dX / dW kernel of the pre backward (the dominant kernel): X, g and
+    # the h_post_bda upstream gradient G in, dX out, H_pre and H_res rows
+    phases["dxdw_kernel"] = 8 * C + 2 * C + 8 * C + 8 * C + 16 + 64
     return phases
 
 
@@ -52,6 +55,19 @@ def src_hash(paths) -> str:
     for p in paths:
         h.update(open(os.path.join(ROOT, p), "rb").read())
     return h.hexdigest()[:16]
+
+
+def pmc_traffic(name: str, sources) -> float | None:
+    """HBM bytes per launch from a committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
+    reported only while the kernel's sources are the ones that were measured."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    rec = dict(line.split(" = ", 1) for line in open(path).read().splitlines()
+               if " = " in line and not line.startswith("#"))
+    if rec.get("src_hash") != src_hash(sources):
+        return None
+    return float(rec["hbm_bytes_per_launch"])
 
 
 def cpu_baseline(w, X, W, s, G, budget_s: float) -> dict:
@@ -180,13 +196,25 @@ def main():
     torch.cuda.synchronize()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 1)] for _ in range(args.steps)]
+    # the dX / dW kernel inside mhc_pre_bwd is timed by events that the
+    # library records around its launch (mhc_set_kernel_events); torch creates
+    # an event's handle at its first record, so each is recorded once here
+    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for pair in kev:
+        for ev in pair:
+            ev.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for st in range(args.steps):
         cur["X"] = Xcopies[(args.warmup + st) % 2]
         evs[st][0].record(stream)
-        for i, (_, fn, _) in enumerate(seq):
+        for i, (name, fn, _) in enumerate(seq):
+            if name == "pre_bwd":
+                _lib.check(lib.mhc_set_kernel_events(_lib.MHC_KERNEL_PROJ_BWD_DXDW, kev[st][0]._as_parameter_,
+                                                     kev[st][1]._as_parameter_))
             fn()
+            if name == "pre_bwd":
+                _lib.check(lib.mhc_set_kernel_events(0, None, None))
             evs[st][i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -203,21 +231,18 @@ def main():
     tot_bytes = led["total"] * N
     gbs = tot_bytes / (mhc_ms * 1e-3) / 1e9
 
-    # dominant kernel: h_post_bda backward is one kernel (no bias) and the largest byte mover
-    kname = "h_post_bda_bwd_kernel"
-    k_ms = mean["post_bwd"]
-    k_bytes = led["post_bwd"] * N
+    # dominant kernel: the dX / dW kernel of the pre backward, timed alone
+    kname = "proj_bwd_mfma_kernel"
+    k_ms = float(np.mean([kev[st][0].elapsed_time(kev[st][1]) for st in range(args.steps)]))
+    k_bytes = led["dxdw_kernel"] * N
     k_gbs = k_bytes / (k_ms * 1e-3) / 1e9
-    # HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    # summary, reported only while the kernel's sources are the ones measured
-    traffic = None
-    pmc = os.path.join(ROOT, "profiles", "h_post_bda_bwd_full_layer_pmc.txt")
-    if os.path.exists(pmc):
-        rec = dict(line.split(" = ", 1) for line in open(pmc).read().splitlines()
-                   if " = " in line and not line.startswith("#"))
-        if rec.get("src_hash") == src_hash(["mhc_hyper_connection_proj_amd/csrc/streams.hip",
-                                            "mhc_hyper_connection_proj_amd/csrc/device.h"]):
-            traffic = float(rec["hbm_bytes_per_launch"])
+    traffic = pmc_traffic("proj_bwd_mfma_full_layer_pmc.txt", ["mhc_hyper_connection_proj_amd/csrc/proj.hip",
+                                                               "mhc_hyper_connection_proj_amd/csrc/device.h"])
+    # the h_post_bda backward (one kernel, the whole post_bwd phase), for context
+    p_bytes = led["post_bwd"] * N
+    p_gbs = p_bytes / (mean["post_bwd"] * 1e-3) / 1e9
+    p_traffic = pmc_traffic("h_post_bda_bwd_full_layer_pmc.txt", ["mhc_hyper_connection_proj_amd/csrc/streams.hip",
+                                                                  "mhc_hyper_connection_proj_amd/csrc/device.h"])
 
     res = {
         "metric": METRIC,
@@ -244,6 +269,10 @@ def main():
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": k_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": k_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": k_bytes, "avg_launch_ms": k_ms},
+        "roofline_h_post_bda_bwd": {"bound": "hbm", "kernel": "h_post_bda_bwd_kernel", "achieved": p_gbs,
+                                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": p_gbs / HBM_PEAK_GBS,
+                                    "traffic": p_traffic, "algorithmic_bytes_per_launch": p_bytes,
+                                    "avg_launch_ms": mean["post_bwd"]},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

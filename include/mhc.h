@@ -71,6 +71,22 @@ const char *mhc_last_error(void);
 const char *mhc_version(void);
 
 /* -------------------------------------------------------------------------
+ * Measurement hook (benchmarks and profilers; nothing is computed through it).
+ * A call such as mhc_pre_bwd launches several kernels; to time one of them
+ * alone, register two caller-owned HIP events (hipEvent_t, passed as void *)
+ * for it.  While registered, on the calling host thread only, every launch of
+ * that kernel by a libmhc call made from this thread is bracketed by
+ * hipEventRecord(start_event) and hipEventRecord(stop_event) on the call's
+ * stream.  kernel = MHC_KERNEL_NONE, or both events NULL, clears the hook.
+ * Returns MHC_ERR_ARG for an unknown kernel id or exactly one NULL event.
+ * A failed event record is ignored: it cannot change any result.
+ *   MHC_KERNEL_PROJ_BWD_DXDW: the projection backward's dX / dW kernel
+ *   (launched by mhc_proj_rms_h_bwd and mhc_pre_bwd).
+ * ---------------------------------------------------------------------- */
+typedef enum mhc_kernel_id { MHC_KERNEL_NONE = 0, MHC_KERNEL_PROJ_BWD_DXDW = 1 } mhc_kernel_id;
+mhc_status mhc_set_kernel_events(int32_t kernel, void *start_event, void *stop_event);
+
+/* -------------------------------------------------------------------------
  * Projection + RMS + compute_h, forward.
  * Megatron Core "core.fusions.fused_mhc_kernels", operation
  * proj_rms_compute_h (`_torch_proj_rms_compute_h(x, weight, alpha_pre,

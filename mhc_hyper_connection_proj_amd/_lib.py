@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libmhc.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "mhc.h")
 
 MHC_BF16, MHC_F32 = 0, 1
+MHC_KERNEL_NONE, MHC_KERNEL_PROJ_BWD_DXDW = 0, 1  # mhc_kernel_id (mhc_set_kernel_events)
 SAVED_STRIDE = 32
 STATUS = ["MHC_OK", "MHC_ERR_NULL", "MHC_ERR_SHAPE", "MHC_ERR_UNSUPPORTED", "MHC_ERR_ALIGN",
           "MHC_ERR_ALIAS", "MHC_ERR_WORKSPACE", "MHC_ERR_ARG", "MHC_ERR_HIP"]
@@ -35,6 +36,7 @@ SIGNATURES = {
     "mhc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mhc_last_error": (ctypes.c_char_p, []),
     "mhc_version": (ctypes.c_char_p, []),
+    "mhc_set_kernel_events": (ctypes.c_int, [_i32, _vp, _vp]),
     "mhc_proj_rms_h_workspace_size": (_sz, [_i64, _i32, _i64, ctypes.c_int]),
     "mhc_proj_rms_h": (ctypes.c_int, [_vp, _i64, _i32, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _f32,
                                       _vp, _vp, _vp, _vp, _vp, _sz]),

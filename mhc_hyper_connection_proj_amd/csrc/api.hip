@@ -15,6 +15,13 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// mhc_set_kernel_events registration, per host thread
+struct KernelEvents {
+  int kernel = 0;
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+thread_local KernelEvents g_kernel_events;
+
 struct Span {
   const char *name;
   uintptr_t lo, hi;
@@ -150,6 +157,14 @@ constexpr int64_t J = mhc::kJ;
 
 }  // namespace
 
+static_assert(mhc::kKernelProjBwdDxDw == MHC_KERNEL_PROJ_BWD_DXDW, "kernel ids");
+
+void mhc::kernel_event(int id, hipStream_t s, bool start) {
+  const KernelEvents &k = g_kernel_events;
+  if (k.kernel != id) return;
+  (void)hipEventRecord(start ? k.start : k.stop, s);
+}
+
 extern "C" {
 
 const char *mhc_status_string(mhc_status s) {
@@ -170,6 +185,23 @@ const char *mhc_status_string(mhc_status s) {
 const char *mhc_last_error(void) { return g_last_error.c_str(); }
 
 const char *mhc_version(void) { return "libmhc 0.1 gfx950"; }
+
+mhc_status mhc_set_kernel_events(int32_t kernel, void *start_event, void *stop_event) {
+  if (kernel == MHC_KERNEL_NONE || (!start_event && !stop_event)) {
+    g_kernel_events = KernelEvents{};
+    return MHC_OK;
+  }
+  if (kernel != MHC_KERNEL_PROJ_BWD_DXDW) {
+    g_last_error = "mhc_set_kernel_events: unknown kernel id " + std::to_string(kernel);
+    return MHC_ERR_ARG;
+  }
+  if (!start_event || !stop_event) {
+    g_last_error = "mhc_set_kernel_events: start_event and stop_event must both be set or both be NULL";
+    return MHC_ERR_ARG;
+  }
+  g_kernel_events = KernelEvents{kernel, (hipEvent_t)start_event, (hipEvent_t)stop_event};
+  return MHC_OK;
+}
 
 // ------------------------------------------------------------------ projection fwd
 size_t mhc_proj_rms_h_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {

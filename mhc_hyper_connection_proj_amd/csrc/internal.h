@@ -19,6 +19,11 @@ struct StreamGeom {
 constexpr int64_t kMaxC = 16384;
 StreamGeom stream_geom(int64_t C);
 
+// Measurement hook (mhc_set_kernel_events): records the registered start /
+// stop event on s around a launch of kernel `id` (ids of mhc_kernel_id).
+constexpr int kKernelProjBwdDxDw = 1;  // MHC_KERNEL_PROJ_BWD_DXDW
+void kernel_event(int id, hipStream_t s, bool start);
+
 // ---- Sinkhorn
 void launch_sinkhorn_fwd(hipStream_t s, int64_t count, const float *L, float *H, int iters, float eps);
 void launch_sinkhorn_bwd(hipStream_t s, int64_t count, const float *dH, const float *L, float *dL,

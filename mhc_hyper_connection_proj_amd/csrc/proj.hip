@@ -1190,7 +1190,7 @@ static void launch_b2(hipStream_t s, const ProjBwdArgs &a, const BwdWs &L) {
 }
 
 template <bool ACCUM, bool HAS_G>
-static void launch_dx(hipStream_t s, const ProjBwdArgs &a, const BwdWs &L) {
+static void launch_dx_kernel(hipStream_t s, const ProjBwdArgs &a, const BwdWs &L) {
   const int64_t K = 4 * a.C;
   if (a.f32) {
     const unsigned blocks = (unsigned)(((K + kDxKT - 1) / kDxKT) * L.ntb);
@@ -1205,6 +1205,13 @@ static void launch_dx(hipStream_t s, const ProjBwdArgs &a, const BwdWs &L) {
   } else {
     launch_b2<ACCUM, HAS_G>(s, a, L);
   }
+}
+
+template <bool ACCUM, bool HAS_G>
+static void launch_dx(hipStream_t s, const ProjBwdArgs &a, const BwdWs &L) {
+  kernel_event(kKernelProjBwdDxDw, s, true);
+  launch_dx_kernel<ACCUM, HAS_G>(s, a, L);
+  kernel_event(kKernelProjBwdDxDw, s, false);
 }
 
 void launch_proj_bwd(hipStream_t s, const ProjBwdArgs &a) {

@@ -57,6 +57,17 @@ def _last(lib):
     return lib.mhc_last_error().decode()
 
 
+def test_kernel_events_hook_validation(lib):
+    # handles are only stored (no HIP call is made until a kernel launches)
+    fake = 0x1000
+    assert lib.mhc_set_kernel_events(L.MHC_KERNEL_PROJ_BWD_DXDW, fake, fake + 64) == 0
+    assert lib.mhc_set_kernel_events(7, fake, fake + 64) == L.STATUS.index("MHC_ERR_ARG")
+    assert "unknown kernel id" in _last(lib)
+    assert lib.mhc_set_kernel_events(L.MHC_KERNEL_PROJ_BWD_DXDW, fake, None) == L.STATUS.index("MHC_ERR_ARG")
+    assert lib.mhc_set_kernel_events(L.MHC_KERNEL_PROJ_BWD_DXDW, None, None) == 0  # clears
+    assert lib.mhc_set_kernel_events(L.MHC_KERNEL_NONE, fake, fake) == 0  # clears
+
+
 def test_sinkhorn_validation(lib):
     f = lib.mhc_sinkhorn_fwd
     assert f(None, -1, 4, p(0), p(1), 20, 1e-6) == SHAPE

@@ -253,6 +253,36 @@ def test_pre_fwd_bwd(act, N, C, mode):
     assert_tokensum("dhbias", ob["dhbias"], rb["dhbias"], ab)
 
 
+# ----------------------------------------------------------------- measurement hook
+def test_kernel_events_hook_times_dxdw_and_changes_nothing():
+    from mhc_hyper_connection_proj_amd import _lib as L
+    N, C = 300, 1024
+    log(f"kernel events hook N={N} C={C}")
+    X, W, alpha, hb = _proj_inputs("bf16", N, C)
+    ref = O.pre_fwd(h64(X), h64(W), h64(alpha), h64(hb), 1e-6, 20, 1e-6)
+    saved = np.zeros((N, 32), np.float32)
+    saved[:, 0] = ref["r"]; saved[:, 1] = ref["q"]; saved[:, 2:26] = ref["z"]
+    g = store(RNG.standard_normal((N, C)), "bf16")
+    dHq, dHr = f32(RNG.standard_normal((N, 4))), f32(RNG.standard_normal((N, 4, 4)))
+    args = (dev(g), dev(dHq), dev(dHr), dev(X), dev(W), dev(saved), dev(f32(ref["H_pre"])), dev(f32(ref["H_post"])),
+            dev(f32(ref["L"])))
+    plain = B.mhc_pre_bwd(*args, alpha=dev(alpha), iters=20, eps=1e-6)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for e in ev:
+        e.record(stream)
+    lib = L.lib()
+    L.check(lib.mhc_set_kernel_events(L.MHC_KERNEL_PROJ_BWD_DXDW, ev[0]._as_parameter_, ev[1]._as_parameter_))
+    try:
+        hooked = B.mhc_pre_bwd(*args, alpha=dev(alpha), iters=20, eps=1e-6)
+    finally:
+        L.check(lib.mhc_set_kernel_events(L.MHC_KERNEL_NONE, None, None))
+    torch.cuda.synchronize()
+    assert ev[0].elapsed_time(ev[1]) > 0.0
+    for k in ("dX", "dW", "dalpha", "dhbias"):
+        assert torch.equal(plain[k], hooked[k]), k
+
+
 # ----------------------------------------------------------------- edge cases
 def test_zero_tokens_is_noop_and_zero_param_grads():
     C = 64
