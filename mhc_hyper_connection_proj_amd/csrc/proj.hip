@@ -62,28 +62,47 @@ __device__ __forceinline__ float bf16_round(float v) {
   return (float)h;
 }
 
+// One thread per (8-k group, column): 8 strided reads of W (coalesced over
+// the column), 16- or 32-byte contiguous writes of the packed group.
 template <bool F32>
 __global__ __launch_bounds__(256) void pack_w_kernel(const float *__restrict__ W, void *__restrict__ out,
                                                      int64_t K, int64_t Kp) {
   const int ncol = F32 ? kJ : kWcol;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over Kp * ncol
-  if (idx >= Kp * ncol) return;
-  const int64_t k = idx / ncol;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over Kp / 8 * ncol
+  if (idx >= Kp / 8 * ncol) return;
+  const int64_t kg = idx / ncol;
   const int j = (int)(idx % ncol);
-  const float w = (k < K && j < kJ) ? W[k * kJ + j] : 0.f;
-  const int64_t kg = k >> 3;
-  const int e = (int)(k & 7);
+  float w[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int64_t k = kg * 8 + e;
+    w[e] = (k < K && j < kJ) ? W[k * kJ + j] : 0.f;
+  }
   if (F32) {
-    reinterpret_cast<float *>(out)[(kg * kJ + j) * 8 + e] = w;
+    float4 *o = reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + (kg * kJ + j) * 8);
+    o[0] = make_float4(w[0], w[1], w[2], w[3]);
+    o[1] = make_float4(w[4], w[5], w[6], w[7]);
   } else {
-    const float hi = bf16_round(w);
-    const float r1 = w - hi;
-    const float mid = bf16_round(r1);
-    const float lo = bf16_round(r1 - mid);
+    uint32_t t[3][4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      float hi[2], mid[2], lo[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const float v = w[2 * p + q];
+        hi[q] = bf16_round(v);
+        const float r1 = v - hi[q];
+        mid[q] = bf16_round(r1);
+        lo[q] = bf16_round(r1 - mid[q]);
+      }
+      t[0][p] = pack_bf16x2(hi[0], hi[1]);
+      t[1][p] = pack_bf16x2(mid[0], mid[1]);
+      t[2][p] = pack_bf16x2(lo[0], lo[1]);
+    }
     bf16_t *o = reinterpret_cast<bf16_t *>(out);
-    o[((kg * 3 + 0) * kWcol + j) * 8 + e] = __builtin_bit_cast(uint16_t, (__bf16)hi);
-    o[((kg * 3 + 1) * kWcol + j) * 8 + e] = __builtin_bit_cast(uint16_t, (__bf16)mid);
-    o[((kg * 3 + 2) * kWcol + j) * 8 + e] = __builtin_bit_cast(uint16_t, (__bf16)lo);
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+      *reinterpret_cast<uint4 *>(o + ((kg * 3 + m) * kWcol + j) * 8) = make_uint4(t[m][0], t[m][1], t[m][2], t[m][3]);
   }
 }
 
@@ -414,12 +433,12 @@ void launch_proj_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *
   void *wpk = base;
   float *part = (float *)(base + align256(wpack_bytes(C, f32)));
   if (f32) {
-    const unsigned pack_blocks = (unsigned)((Kp * kJ + 255) / 256);
+    const unsigned pack_blocks = (unsigned)((Kp / 8 * kJ + 255) / 256);
     const unsigned pblocks = (unsigned)(((N + kTB - 1) / kTB) * kSplitK);
     hipLaunchKernelGGL((pack_w_kernel<true>), dim3(pack_blocks), dim3(256), 0, s, W, wpk, K, Kp);
     hipLaunchKernelGGL(proj_partial_f32_kernel, dim3(pblocks), dim3(256), 0, s, X, wpk, part, N, K);
   } else {
-    const unsigned pack_blocks = (unsigned)((Kp * kWcol + 255) / 256);
+    const unsigned pack_blocks = (unsigned)((Kp / 8 * kWcol + 255) / 256);
     const unsigned pblocks = (unsigned)(((N + kDmaTok - 1) / kDmaTok) * kSplitK);
     const size_t lds = (size_t)kDmaStages * kStageElems * sizeof(bf16_t);
     hipLaunchKernelGGL((pack_w_kernel<false>), dim3(pack_blocks), dim3(256), 0, s, W, wpk, K, Kp);
@@ -1154,15 +1173,20 @@ __global__ __launch_bounds__(256) void proj_bwd_dx_f32_kernel(
   }
 }
 
-// dW[k][j] = sum over token blocks of the partials, in block order.
+// dW[k][j] = sum over token blocks of the partials, in block order; four
+// consecutive entries per thread (K * 24 is a multiple of 4), the partials
+// read once with non-temporal loads.
 __global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict__ part,
                                                         float *__restrict__ dW, int64_t ntb,
                                                         int64_t KJ) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= KJ) return;
-  float s = 0.f;
-  for (int64_t b = 0; b < ntb; ++b) s += part[b * KJ + idx];
-  dW[idx] = s;
+  const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (4 * i4 >= KJ) return;
+  const nt_f32x4 *p = reinterpret_cast<const nt_f32x4 *>(part) + i4;
+  const int64_t stride = KJ / 4;
+  nt_f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int64_t b = 0; b < ntb; ++b) s += __builtin_nontemporal_load(p + b * stride);
+  reinterpret_cast<nt_f32x4 *>(dW)[i4] = s;
 }
 
 template <bool ACCUM, bool HAS_G, bool DW, bool POST>
@@ -1239,7 +1263,7 @@ void launch_proj_bwd(hipStream_t s, const ProjBwdArgs &a) {
     else launch_dx<false, false>(s, a, L);
   }
   if (a.dW)
-    hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((K * kJ + 255) / 256)), dim3(256), 0, s, L.dwpart,
+    hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((K * kJ / 4 + 255) / 256)), dim3(256), 0, s, L.dwpart,
                        a.dW, L.ntb, K * kJ);
   if (a.dalpha || a.dhbias)
     hipLaunchKernelGGL(param_final_kernel, dim3(1), dim3(256), 0, s, L.ppart, L.nblk, a.dalpha, a.dhbias);
