@@ -316,6 +316,59 @@ def test_deterministic_bitwise():
                            if b2.dtype == torch.bfloat16 else b2)
 
 
+def _bits(t):
+    t = t.detach().cpu()
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("act,C", [("bf16", 2048), ("f32", 256)])
+def test_per_token_results_batch_invariant(act, C):
+    """Every per-token output is a function of that token's inputs alone, bit for bit: the same
+    37 tokens computed as a batch of their own and at rows 700..736 of a 1300-token batch (other
+    token blocks, split-K slices, MFMA sub-tiles and workgroup counts) give identical bits.
+    Sums over tokens (dW, dalpha, dhbias, dbias) are excluded: they depend on the batch."""
+    n_small, n_big, at = 37, 1300, 700
+    log(f"batch invariance act={act} C={C}")
+    Xb, W, alpha, hb = _proj_inputs(act, n_big, C)
+    Gb = store(RNG.standard_normal((n_big, 4, C)), act)
+    xb = store(RNG.standard_normal((n_big, C)), act)
+    gb = store(RNG.standard_normal((n_big, C)), act)
+    bias = store(RNG.standard_normal(C) * 0.1, act)
+    dHpb = f32(RNG.standard_normal((n_big, 4)))
+    dHrb = f32(RNG.standard_normal((n_big, 4, 4)))
+    sl = slice(at, at + n_small)
+
+    def run(X, G, x, g, dHp, dHr):
+        r = {}
+        o = B.mhc_pre_fwd(dev(X), dev(W), dev(alpha), dev(hb))
+        r.update({f"pre_fwd.{k}": v for k, v in o.items()})
+        Hp, Hq, L, sv = B.mhc_proj_rms_h(dev(X), dev(W), dev(alpha), dev(hb))
+        r.update({"proj.H_pre": Hp, "proj.H_post": Hq, "proj.L": L, "proj.saved": sv})
+        r["sk_fwd"] = B.mhc_sinkhorn_fwd(o["H_res_logits"])
+        r["sk_bwd"] = B.mhc_sinkhorn_bwd(dev(dHr), o["H_res_logits"])
+        r["agg_fwd"] = B.mhc_h_aggregate_fwd(dev(X), o["H_pre"])
+        adX, adH = B.mhc_h_aggregate_bwd(dev(g), dev(X), o["H_pre"])
+        r.update({"agg_bwd.dX": adX, "agg_bwd.dH": adH})
+        r["post_fwd"] = B.mhc_h_post_bda_fwd(dev(X), o["H_res"], o["H_post"], dev(x), dev(bias))
+        pdX, pdHr, pdHp, pdx, _ = B.mhc_h_post_bda_bwd(dev(G), dev(X), o["H_res"], o["H_post"], dev(x), dev(bias),
+                                                       want_dbias=False)
+        r.update({"post_bwd.dX": pdX, "post_bwd.dH_res": pdHr, "post_bwd.dH_post": pdHp, "post_bwd.dx": pdx})
+        pjdX = B.mhc_proj_rms_h_bwd(dev(X), dev(W), o["saved"], o["H_pre"], o["H_post"], dev(dHp), dev(dHp),
+                                    dev(dHr), alpha=dev(alpha))[0]
+        r["proj_bwd.dX"] = pjdX
+        bw = B.mhc_pre_bwd(dev(g), dev(dHp), dev(dHr), dev(X), dev(W), o["saved"], o["H_pre"], o["H_post"],
+                           o["H_res_logits"], alpha=dev(alpha), want_intermediates=True, post_G=dev(G),
+                           post_H_res=o["H_res"])
+        r.update({"pre_bwd.dX": bw["dX"], "pre_bwd.dH_pre": bw["dH_pre"], "pre_bwd.dlogits": bw["dlogits"]})
+        torch.cuda.synchronize()
+        return r
+
+    big = run(Xb, Gb, xb, gb, dHpb, dHrb)
+    small = run(*(np.ascontiguousarray(a[sl]) for a in (Xb, Gb, xb, gb, dHpb, dHrb)))
+    for k, v in small.items():
+        assert torch.equal(_bits(v), _bits(big[k][sl])), f"{k}: per-token result depends on the batch"
+
+
 def test_invalid_arguments_raise():
     X = torch.zeros(4, 3, 64, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(B._lib.MhcError) as e:
