@@ -66,10 +66,18 @@ def _lib():
                                                   _dp, _dp, _dp, _dp, _dp]
         lib.mhc_oracle_proj_rms_h_bwd.argtypes = [_i64, _i32, _i64, _dp, _dp, _dp, _dp, ctypes.c_double,
                                                   _dp, _dp, _dp, _dp, _dp, _dp, _dp]
+        lib.mhc_oracle_stream_mix_fwd.argtypes = [_i64, _i32, _i64, _dp, _dp, _dp]
+        lib.mhc_oracle_stream_mix_bwd.argtypes = [_i64, _i32, _i64, _dp, _dp, _dp, _dp, _dp]
+        lib.mhc_oracle_stream_distribute_fwd.argtypes = [_i64, _i32, _i64, _dp, _dp, _dp]
+        lib.mhc_oracle_stream_distribute_bwd.argtypes = [_i64, _i32, _i64, _dp, _dp, _dp, _dp, _dp]
+        lib.mhc_oracle_h_aggregate_static_fwd.argtypes = [_i64, _i32, _i64, _dp, _dp, _dp]
+        lib.mhc_oracle_h_aggregate_static_bwd.argtypes = [_i64, _i32, _i64, _dp, _dp, _dp, _dp, _dp]
         for f in ("mhc_oracle_proj_rms_h", "mhc_oracle_sinkhorn_fwd", "mhc_oracle_sinkhorn_bwd",
                   "mhc_oracle_h_aggregate_fwd", "mhc_oracle_h_aggregate_bwd",
                   "mhc_oracle_h_post_bda_fwd", "mhc_oracle_h_post_bda_bwd",
-                  "mhc_oracle_proj_rms_h_bwd"):
+                  "mhc_oracle_proj_rms_h_bwd", "mhc_oracle_stream_mix_fwd", "mhc_oracle_stream_mix_bwd",
+                  "mhc_oracle_stream_distribute_fwd", "mhc_oracle_stream_distribute_bwd",
+                  "mhc_oracle_h_aggregate_static_fwd", "mhc_oracle_h_aggregate_static_bwd"):
             getattr(lib, f).restype = None
         _lib_handle = lib
     return _lib_handle
@@ -220,6 +228,60 @@ def h_post_bda_bwd(G, X, H_res, H_post, x, bias=None):
                                      _p(b) if b is not None else None, _p(dX), _p(dHr), _p(dHp),
                                      _p(dx), _p(db) if db is not None else None)
     return dX, dHr, dHp, dx, db
+
+
+def stream_mix_fwd(X, M) -> np.ndarray:
+    """F5: out[t,i,c] = sum_j M[t,j,i] X[t,j,c] (rwkv-ops Stream Mix FFI)."""
+    X = _f64(X); M = _f64(M)
+    N, n, C = X.shape
+    out = np.empty((N, n, C))
+    _lib().mhc_oracle_stream_mix_fwd(N, n, C, _p(X), _p(M), _p(out))
+    return out
+
+
+def stream_mix_bwd(G, X, M):
+    """B5: returns (dX [N,n,C], dM [N,n,n])."""
+    G = _f64(G); X = _f64(X); M = _f64(M)
+    N, n, C = X.shape
+    dX = np.empty((N, n, C)); dM = np.empty((N, n, n))
+    _lib().mhc_oracle_stream_mix_bwd(N, n, C, _p(G), _p(X), _p(M), _p(dX), _p(dM))
+    return dX, dM
+
+
+def stream_distribute_fwd(x, H_post) -> np.ndarray:
+    """F6: out[t,i,c] = H_post[t,i] x[t,c] (rwkv-ops Stream Distribute FFI)."""
+    x = _f64(x); H_post = _f64(H_post)
+    (N, C), n = x.shape, H_post.shape[1]
+    out = np.empty((N, n, C))
+    _lib().mhc_oracle_stream_distribute_fwd(N, n, C, _p(x), _p(H_post), _p(out))
+    return out
+
+
+def stream_distribute_bwd(G, x, H_post):
+    """B6: returns (dx [N,C], dH_post [N,n])."""
+    G = _f64(G); x = _f64(x); H_post = _f64(H_post)
+    (N, C), n = x.shape, H_post.shape[1]
+    dx = np.empty((N, C)); dH = np.empty((N, n))
+    _lib().mhc_oracle_stream_distribute_bwd(N, n, C, _p(G), _p(x), _p(H_post), _p(dx), _p(dH))
+    return dx, dH
+
+
+def h_aggregate_static_fwd(X, H_pre) -> np.ndarray:
+    """F3s: agg[t, c] = sum_i H_pre[i] X[t, i, c], one H_pre row [n] for all tokens."""
+    X = _f64(X); H_pre = _f64(H_pre)
+    N, n, C = X.shape
+    agg = np.empty((N, C))
+    _lib().mhc_oracle_h_aggregate_static_fwd(N, n, C, _p(X), _p(H_pre), _p(agg))
+    return agg
+
+
+def h_aggregate_static_bwd(g, X, H_pre):
+    """B3s: returns (dX [N,n,C], dH_pre [n]) with dH_pre summed over tokens."""
+    X = _f64(X); H_pre = _f64(H_pre); g = _f64(g)
+    N, n, C = X.shape
+    dX = np.empty((N, n, C)); dH = np.empty(n)
+    _lib().mhc_oracle_h_aggregate_static_bwd(N, n, C, _p(g), _p(X), _p(H_pre), _p(dX), _p(dH))
+    return dX, dH
 
 
 def proj_rms_h_bwd(X, W, dH_pre, dH_post, dL, alpha=None, hbias=None, eps_rms=1e-6):

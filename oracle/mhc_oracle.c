@@ -281,6 +281,108 @@ void mhc_oracle_h_post_bda_bwd(int64_t N, int n, int64_t C, const double *G,
 }
 
 /* ------------------------------------------------------------------------
+ * F5  stream mix  [RWKV Stream Mix FFI: inp [B,T,n,C], M [B,T,n,n] -> out
+ * [B,T,n,C]; the mixing orientation read as the post-op's H_res mix]
+ *   out[i][c] = sum_j M[j][i] X[j][c]
+ * B5  its backward (d_inp, d_M)
+ *   dX[j][c] = sum_i M[j][i] G[i][c],   dM[j][i] = sum_c X[j][c] G[i][c]
+ * ---------------------------------------------------------------------- */
+void mhc_oracle_stream_mix_fwd(int64_t N, int n, int64_t C, const double *X,
+                               const double *M, double *out) {
+  for (int64_t t = 0; t < N; ++t)
+    for (int i = 0; i < n; ++i)
+      for (int64_t c = 0; c < C; ++c) {
+        double acc = 0.0;
+        for (int j = 0; j < n; ++j)
+          acc += M[t * n * n + j * n + i] * X[(t * n + j) * C + c];
+        out[(t * n + i) * C + c] = acc;
+      }
+}
+
+void mhc_oracle_stream_mix_bwd(int64_t N, int n, int64_t C, const double *G,
+                               const double *X, const double *M, double *dX,
+                               double *dM) {
+  for (int64_t t = 0; t < N; ++t) {
+    for (int j = 0; j < n; ++j)
+      for (int64_t c = 0; c < C; ++c) {
+        double acc = 0.0;
+        for (int i = 0; i < n; ++i)
+          acc += M[t * n * n + j * n + i] * G[(t * n + i) * C + c];
+        dX[(t * n + j) * C + c] = acc;
+      }
+    for (int j = 0; j < n; ++j)
+      for (int i = 0; i < n; ++i) {
+        double acc = 0.0;
+        for (int64_t c = 0; c < C; ++c)
+          acc += X[(t * n + j) * C + c] * G[(t * n + i) * C + c];
+        dM[t * n * n + j * n + i] = acc;
+      }
+  }
+}
+
+/* ------------------------------------------------------------------------
+ * F6  stream distribute  [RWKV Stream Distribute FFI: inp [B,T,C], H_post
+ * [B,T,n] -> out [B,T,n,C]]
+ *   out[i][c] = H_post[i] x[c]
+ * B6  its backward (d_inp, d_H_post: the dx and dh kernels of that section)
+ *   dx[c] = sum_i H_post[i] G[i][c],   dH_post[i] = sum_c G[i][c] x[c]
+ * ---------------------------------------------------------------------- */
+void mhc_oracle_stream_distribute_fwd(int64_t N, int n, int64_t C, const double *x,
+                                      const double *H_post, double *out) {
+  for (int64_t t = 0; t < N; ++t)
+    for (int i = 0; i < n; ++i)
+      for (int64_t c = 0; c < C; ++c)
+        out[(t * n + i) * C + c] = H_post[t * n + i] * x[t * C + c];
+}
+
+void mhc_oracle_stream_distribute_bwd(int64_t N, int n, int64_t C, const double *G,
+                                      const double *x, const double *H_post,
+                                      double *dx, double *dH_post) {
+  for (int64_t t = 0; t < N; ++t) {
+    for (int64_t c = 0; c < C; ++c) {
+      double acc = 0.0;
+      for (int i = 0; i < n; ++i)
+        acc += H_post[t * n + i] * G[(t * n + i) * C + c];
+      dx[t * C + c] = acc;
+    }
+    for (int i = 0; i < n; ++i) {
+      double acc = 0.0;
+      for (int64_t c = 0; c < C; ++c)
+        acc += G[(t * n + i) * C + c] * x[t * C + c];
+      dH_post[t * n + i] = acc;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------
+ * F3s / B3s  h_aggregate with one H_pre row for all tokens  [RWKV Stream
+ * Aggregate FFI with per_token = false: H_pre [n], d_H_pre [n]]
+ *   agg[t][c] = sum_i H_pre[i] X[t][i][c]
+ *   dX[t][i][c] = H_pre[i] g[t][c],   dH_pre[i] = sum_t sum_c g[t][c] X[t][i][c]
+ * ---------------------------------------------------------------------- */
+void mhc_oracle_h_aggregate_static_fwd(int64_t N, int n, int64_t C, const double *X,
+                                       const double *H_pre, double *agg) {
+  for (int64_t t = 0; t < N; ++t)
+    for (int64_t c = 0; c < C; ++c) {
+      double acc = 0.0;
+      for (int i = 0; i < n; ++i) acc += H_pre[i] * X[(t * n + i) * C + c];
+      agg[t * C + c] = acc;
+    }
+}
+
+void mhc_oracle_h_aggregate_static_bwd(int64_t N, int n, int64_t C, const double *g,
+                                       const double *X, const double *H_pre,
+                                       double *dX, double *dH_pre) {
+  for (int i = 0; i < n; ++i) dH_pre[i] = 0.0;
+  for (int64_t t = 0; t < N; ++t)
+    for (int i = 0; i < n; ++i)
+      for (int64_t c = 0; c < C; ++c) {
+        dX[(t * n + i) * C + c] = H_pre[i] * g[t * C + c];
+        dH_pre[i] += g[t * C + c] * X[(t * n + i) * C + c];
+      }
+}
+
+/* ------------------------------------------------------------------------
  * B1  proj_rms_compute_h backward  [RLK review comment on the RMS backward:
  * dx = dx_gemm + dx_rms, with the q == 0 guard; RLK commit message: three
  * segment gains, so d_alpha is three scalars]

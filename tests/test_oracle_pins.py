@@ -332,6 +332,68 @@ def test_post_bwd_adjoints_and_dbias():
     assert none is None
 
 
+# ---------------------------------------------------------------- F5/F6, B5/B6 stream mix / distribute
+def test_mix_plus_distribute_is_post_bda():
+    # the two halves of h_post_bda (pinned above) add up to it, forward and backward
+    N, n, C = 5, 4, 24
+    X = rnd(N, n, C); Hr = rnd(N, n, n); Hp = rnd(N, n); x = rnd(N, C); G = rnd(N, n, C)
+    np.testing.assert_allclose(O.stream_mix_fwd(X, Hr) + O.stream_distribute_fwd(x, Hp),
+                               O.h_post_bda_fwd(X, Hr, Hp, x, None), rtol=1e-14, atol=1e-14)
+    dX, dHr, dHp, dx, _ = O.h_post_bda_bwd(G, X, Hr, Hp, x, None)
+    mdX, mdM = O.stream_mix_bwd(G, X, Hr)
+    ddx, ddH = O.stream_distribute_bwd(G, x, Hp)
+    np.testing.assert_allclose(mdX, dX, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(mdM, dHr, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(ddx, dx, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(ddH, dHp, rtol=1e-14, atol=1e-14)
+
+
+def test_mix_transpose_permutation_and_adjoints():
+    N, n, C = 4, 4, 16
+    X = rnd(N, n, C)
+    M = np.zeros((N, n, n)); M[:, 0, 1] = 1.0          # out_1 = X_0, all else 0
+    out = O.stream_mix_fwd(X, M)
+    np.testing.assert_array_equal(out[:, 1], X[:, 0])
+    np.testing.assert_array_equal(out[:, [0, 2, 3]], 0.0)
+    perm = RNG.permutation(n)
+    out = O.stream_mix_fwd(X, np.broadcast_to(np.eye(n)[perm], (N, n, n)))
+    np.testing.assert_array_equal(out, X[:, np.argsort(perm), :])
+    M = rnd(N, n, n); G = rnd(N, n, C)
+    dX, dM = O.stream_mix_bwd(G, X, M)
+    lhs = (G * O.stream_mix_fwd(X, M)).sum()
+    np.testing.assert_allclose(lhs, (dX * X).sum(), rtol=1e-12)
+    np.testing.assert_allclose(lhs, (dM * M).sum(), rtol=1e-12)
+
+
+def test_distribute_outer_product_and_adjoints():
+    N, n, C = 3, 4, 10
+    x = rnd(N, C); Hp = rnd(N, n); G = rnd(N, n, C)
+    np.testing.assert_array_equal(O.stream_distribute_fwd(x, Hp), Hp[:, :, None] * x[:, None, :])
+    dx, dH = O.stream_distribute_bwd(G, x, Hp)
+    lhs = (G * O.stream_distribute_fwd(x, Hp)).sum()
+    np.testing.assert_allclose(lhs, (dx * x).sum(), rtol=1e-12)
+    np.testing.assert_allclose(lhs, (dH * Hp).sum(), rtol=1e-12)
+    xt = torch.tensor(x, requires_grad=True); ht = torch.tensor(Hp, requires_grad=True)
+    (torch.tensor(G) * (ht[:, :, None] * xt[:, None, :])).sum().backward()
+    np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(dH, ht.grad.numpy(), rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------- F3s/B3s one shared H_pre row
+def test_static_aggregate_is_broadcast_per_token_aggregate():
+    # one H_pre row for all tokens: the per-token oracle (pinned above) with that row
+    # repeated; dH_pre is the token sum of the per-token rows
+    N, n, C = 6, 4, 18
+    X = rnd(N, n, C); h = rnd(n); g = rnd(N, C)
+    Hrows = np.broadcast_to(h, (N, n)).copy()
+    np.testing.assert_allclose(O.h_aggregate_static_fwd(X, h), O.h_aggregate_fwd(X, Hrows), rtol=1e-15, atol=0)
+    dX, dH = O.h_aggregate_static_bwd(g, X, h)
+    pdX, pdH = O.h_aggregate_bwd(g, X, Hrows)
+    np.testing.assert_allclose(dX, pdX, rtol=1e-15, atol=0)
+    np.testing.assert_allclose(dH, pdH.sum(0), rtol=1e-13, atol=1e-13)
+    assert dH.shape == (n,)
+
+
 # ---------------------------------------------------------------- B1 projection backward
 def _proj_loss(X, W, alpha, hb, dHp, dHq, dL, eps):
     p = O.proj_rms_h(X, W, alpha, hb, eps)
