@@ -70,6 +70,45 @@ def pmc_traffic(name: str, sources) -> float | None:
     return float(rec["hbm_bytes_per_launch"])
 
 
+def measure_variants(lib, L, sp, N, n, C, X, G, H_res, H_post, x, g, out, dX, dM, dH, dx, stream, torch):
+    """The h_post_bda halves and the shared-row h_aggregate at the same size, after the timed
+    steps: mean of 5 event-timed calls each; GB/s on algorithmic bytes (each tensor once)."""
+    from mhc_hyper_connection_proj_amd._lib import MHC_BF16
+    P = lambda t: t.data_ptr()
+    dev = X.device
+    h = torch.tensor([0.4, 0.3, 0.2, 0.1], device=dev)
+    dh = torch.empty(4, device=dev)
+    wsn = lib.mhc_h_aggregate_static_bwd_workspace_size(N, n, C, MHC_BF16)
+    ws = torch.empty(max(wsn, 16), dtype=torch.uint8, device=dev)
+    calls = {
+        "stream_mix_fwd": (16 * C + 64, lambda: lib.mhc_stream_mix_fwd(sp, N, n, C, MHC_BF16, P(X), P(H_res), P(out))),
+        "stream_mix_bwd": (24 * C + 128, lambda: lib.mhc_stream_mix_bwd(sp, N, n, C, MHC_BF16, P(G), P(X), P(H_res),
+                                                                         P(dX), P(dM))),
+        "stream_distribute_fwd": (10 * C + 16, lambda: lib.mhc_stream_distribute_fwd(sp, N, n, C, MHC_BF16, P(x),
+                                                                                      P(H_post), P(out))),
+        "stream_distribute_bwd": (12 * C + 32, lambda: lib.mhc_stream_distribute_bwd(sp, N, n, C, MHC_BF16, P(G), P(x),
+                                                                                      P(H_post), P(dx), P(dH))),
+        "h_aggregate_static_fwd": (10 * C, lambda: lib.mhc_h_aggregate_static_fwd(sp, N, n, C, MHC_BF16, P(X), P(h),
+                                                                                   P(x))),
+        "h_aggregate_static_bwd": (18 * C, lambda: lib.mhc_h_aggregate_static_bwd(sp, N, n, C, MHC_BF16, P(g), P(X),
+                                                                                   P(h), P(dX), 0, P(dh), P(ws), wsn)),
+    }
+    res = {}
+    for name, (bytes_per_token, fn) in calls.items():
+        L.check(fn())
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        evs[0].record(stream)
+        for i in range(5):
+            L.check(fn())
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(5)]))
+        gbs = bytes_per_token * N / (ms * 1e-3) / 1e9
+        res[name] = {"ms": ms, "algorithmic_bytes_per_token": bytes_per_token, "achieved_gbs": gbs,
+                     "frac": gbs / HBM_PEAK_GBS}
+    return res
+
+
 def cpu_baseline(w, X, W, s, G, budget_s: float) -> dict:
     """Time the fp64 oracle (single thread, as written) on the first tokens of the workload."""
     import oracle as O
@@ -227,6 +266,9 @@ def main():
     mhc_ms = sum(mean[k] for k, _, m in seq if m)
     step_ms = sum(mean.values())
 
+    variants = measure_variants(lib, _lib, sp, N, n, C, cur["X"], Gd, H_res, H_post, x, g, out, dX, dHr, dHp, dx,
+                                stream, torch)
+
     led = ledger_bytes_per_token(C, N)
     tot_bytes = led["total"] * N
     gbs = tot_bytes / (mhc_ms * 1e-3) / 1e9
@@ -273,6 +315,7 @@ def main():
                                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": p_gbs / HBM_PEAK_GBS,
                                     "traffic": p_traffic, "algorithmic_bytes_per_launch": p_bytes,
                                     "avg_launch_ms": mean["post_bwd"]},
+        "variants": variants,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

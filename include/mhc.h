@@ -208,6 +208,44 @@ mhc_status mhc_h_post_bda_bwd(void *stream, int64_t tokens, int32_t n, int64_t C
                               void *workspace, size_t workspace_bytes);
 
 /* -------------------------------------------------------------------------
+ * The two halves of h_post_bda as operations of their own (rwkv-ops
+ * mhu_ffi.cu, sections "Stream Mix FFI" and "Stream Distribute FFI"); the
+ * mix uses the same orientation as h_post_bda's H_res term.
+ *   stream mix:        out[i][c] = sum_j M[j][i] X[j][c]
+ *                      dX[j][c] = sum_i M[j][i] G[i][c], dM[j][i] = sum_c X[j][c] G[i][c]
+ *   stream distribute: out[i][c] = H_post[i] x[c]
+ *                      dx[c] = sum_i H_post[i] G[i][c], dH_post[i] = sum_c G[i][c] x[c]
+ * X, G, out, dX [tokens][n][C] (act); x, dx [tokens][C] (act); M, dM
+ * [tokens][n][n] fp32; H_post, dH_post [tokens][n] fp32.  Every output is
+ * written in full; none may overlap an input or another output.
+ * ---------------------------------------------------------------------- */
+mhc_status mhc_stream_mix_fwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                              const void *X, const float *M, void *out);
+mhc_status mhc_stream_mix_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                              const void *G, const void *X, const float *M, void *dX, float *dM);
+mhc_status mhc_stream_distribute_fwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                                     const void *x, const float *H_post, void *out);
+mhc_status mhc_stream_distribute_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                                     const void *G, const void *x, const float *H_post, void *dx,
+                                     float *dH_post);
+
+/* -------------------------------------------------------------------------
+ * h_aggregate with one H_pre row for all tokens (rwkv-ops "Stream Aggregate
+ * FFI" with per_token = false): H_pre and dH_pre are fp32 [n].
+ *   agg[t][c] = sum_i H_pre[i] X[t][i][c]
+ *   dX[t][i][c] (+)= H_pre[i] g[t][c],  dH_pre[i] = sum_t sum_c g[t][c] X[t][i][c]
+ * dH_pre is a fixed-order sum over tokens (per-token rows in the workspace,
+ * then one reduction); with tokens == 0 it is set to zero.
+ * ---------------------------------------------------------------------- */
+mhc_status mhc_h_aggregate_static_fwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                                      const void *X, const float *H_pre, void *out);
+size_t mhc_h_aggregate_static_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act);
+mhc_status mhc_h_aggregate_static_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                                      const void *g, const void *X, const float *H_pre, void *dX,
+                                      int32_t accumulate_dX, float *dH_pre, void *workspace,
+                                      size_t workspace_bytes);
+
+/* -------------------------------------------------------------------------
  * Fused pre pass (rwkv-ops "MHC Pre-Op FFI" fuses aggregate + sigmoid +
  * Sinkhorn; here the projection is fused in as well):
  *   forward  = proj_rms_h -> sinkhorn(H_res_logits) -> h_aggregate(X, H_pre)

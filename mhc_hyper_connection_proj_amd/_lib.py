@@ -53,6 +53,15 @@ SIGNATURES = {
     "mhc_h_post_bda_bwd_workspace_size": (_sz, [_i64, _i32, _i64, ctypes.c_int, _i32]),
     "mhc_h_post_bda_bwd": (ctypes.c_int, [_vp, _i64, _i32, _i64, ctypes.c_int, _vp, _vp, _vp, _vp,
                                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz]),
+    "mhc_stream_mix_fwd": (ctypes.c_int, [_vp, _i64, _i32, _i64, ctypes.c_int, _vp, _vp, _vp]),
+    "mhc_stream_mix_bwd": (ctypes.c_int, [_vp, _i64, _i32, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp]),
+    "mhc_stream_distribute_fwd": (ctypes.c_int, [_vp, _i64, _i32, _i64, ctypes.c_int, _vp, _vp, _vp]),
+    "mhc_stream_distribute_bwd": (ctypes.c_int, [_vp, _i64, _i32, _i64, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                                 _vp]),
+    "mhc_h_aggregate_static_fwd": (ctypes.c_int, [_vp, _i64, _i32, _i64, ctypes.c_int, _vp, _vp, _vp]),
+    "mhc_h_aggregate_static_bwd_workspace_size": (_sz, [_i64, _i32, _i64, ctypes.c_int]),
+    "mhc_h_aggregate_static_bwd": (ctypes.c_int, [_vp, _i64, _i32, _i64, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                                  _i32, _vp, _vp, _sz]),
     "mhc_pre_fwd_workspace_size": (_sz, [_i64, _i32, _i64, ctypes.c_int]),
     "mhc_pre_fwd": (ctypes.c_int, [_vp, _i64, _i32, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _f32,
                                    _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz]),

@@ -146,6 +146,73 @@ def mhc_h_aggregate_bwd(g, X, H_pre, dX=None, accumulate_dX=False):
     return dX, dH
 
 
+def mhc_h_aggregate_static_fwd(X, H_pre):
+    """h_aggregate with one H_pre row [n] for all tokens."""
+    N, n, C = _dims(X)
+    act = _act(X)
+    _need(X, "X"); _need(H_pre, "H_pre", f32, n)
+    out = torch.empty(*X.shape[:-2], C, dtype=X.dtype, device=X.device)
+    call("mhc_h_aggregate_static_fwd", _stream(X), N, n, C, act, _p(X), _p(H_pre), _p(out))
+    return out
+
+
+def mhc_h_aggregate_static_bwd(g, X, H_pre, dX=None, accumulate_dX=False):
+    """Returns (dX, dH_pre [n]) for one shared H_pre row; dH_pre is summed over tokens."""
+    N, n, C = _dims(X)
+    act = _act(X)
+    _need(X, "X"); _need(g, "g", X.dtype, N * C); _need(H_pre, "H_pre", f32, n)
+    if dX is None:
+        if accumulate_dX:
+            raise ValueError("accumulate_dX needs dX")
+        dX = torch.empty_like(X)
+    _need(dX, "dX", X.dtype, X.numel())
+    dH = torch.empty(n, dtype=f32, device=X.device)
+    ws, wsb = _ws(_lib.lib().mhc_h_aggregate_static_bwd_workspace_size(N, n, C, act), X.device)
+    call("mhc_h_aggregate_static_bwd", _stream(X), N, n, C, act, _p(g), _p(X), _p(H_pre), _p(dX),
+         int(accumulate_dX), _p(dH), _p(ws), wsb)
+    return dX, dH
+
+
+def mhc_stream_mix_fwd(X, M):
+    """out[i] = sum_j M[j][i] X[j] per token."""
+    N, n, C = _dims(X)
+    _need(X, "X"); _need(M, "M", f32, N * n * n)
+    out = torch.empty_like(X)
+    call("mhc_stream_mix_fwd", _stream(X), N, n, C, _act(X), _p(X), _p(M), _p(out))
+    return out
+
+
+def mhc_stream_mix_bwd(G, X, M):
+    """Returns (dX, dM)."""
+    N, n, C = _dims(X)
+    _need(X, "X"); _need(G, "G", X.dtype, X.numel()); _need(M, "M", f32, N * n * n)
+    dX = torch.empty_like(X)
+    dM = torch.empty(*X.shape[:-2], n, n, dtype=f32, device=X.device)
+    call("mhc_stream_mix_bwd", _stream(X), N, n, C, _act(X), _p(G), _p(X), _p(M), _p(dX), _p(dM))
+    return dX, dM
+
+
+def mhc_stream_distribute_fwd(x, H_post):
+    """out[i] = H_post[i] x per token; x [..., C], H_post [..., n] -> [..., n, C]."""
+    n, C = H_post.shape[-1], x.shape[-1]
+    N = x.numel() // C if C else 0
+    _need(x, "x"); _need(H_post, "H_post", f32, N * n)
+    out = torch.empty(*x.shape[:-1], n, C, dtype=x.dtype, device=x.device)
+    call("mhc_stream_distribute_fwd", _stream(x), N, n, C, _act(x), _p(x), _p(H_post), _p(out))
+    return out
+
+
+def mhc_stream_distribute_bwd(G, x, H_post):
+    """Returns (dx, dH_post)."""
+    n, C = H_post.shape[-1], x.shape[-1]
+    N = x.numel() // C if C else 0
+    _need(x, "x"); _need(G, "G", x.dtype, N * n * C); _need(H_post, "H_post", f32, N * n)
+    dx = torch.empty_like(x)
+    dH = torch.empty(*x.shape[:-1], n, dtype=f32, device=x.device)
+    call("mhc_stream_distribute_bwd", _stream(x), N, n, C, _act(x), _p(G), _p(x), _p(H_post), _p(dx), _p(dH))
+    return dx, dH
+
+
 def mhc_h_post_bda_fwd(X, H_res, H_post, x, bias=None):
     N, n, C = _dims(X)
     act = _act(X)

@@ -412,6 +412,114 @@ mhc_status mhc_h_post_bda_bwd(void *stream, int64_t tokens, int32_t n, int64_t C
   return launched("mhc_h_post_bda_bwd");
 }
 
+// ------------------------------------------------------------------ stream mix / distribute
+mhc_status mhc_stream_mix_fwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                              const void *X, const float *M, void *out) {
+  Validator v("mhc_stream_mix_fwd");
+  v.dims(tokens, n, C, act);
+  if (!v.ok()) return v.status();
+  if (tokens == 0) return MHC_OK;
+  v.in(X, tokens * 4 * C * esz(act), "X");
+  v.in(M, tokens * 64, "M");
+  v.out(out, tokens * 4 * C * esz(act), "out");
+  if (v.finish() != MHC_OK) return v.status();
+  mhc::launch_stream_mix_fwd((hipStream_t)stream, act == MHC_F32, tokens, C, X, M, out);
+  return launched("mhc_stream_mix_fwd");
+}
+
+mhc_status mhc_stream_mix_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                              const void *G, const void *X, const float *M, void *dX, float *dM) {
+  Validator v("mhc_stream_mix_bwd");
+  v.dims(tokens, n, C, act);
+  if (!v.ok()) return v.status();
+  if (tokens == 0) return MHC_OK;
+  v.in(G, tokens * 4 * C * esz(act), "G");
+  v.in(X, tokens * 4 * C * esz(act), "X");
+  v.in(M, tokens * 64, "M");
+  v.out(dX, tokens * 4 * C * esz(act), "dX");
+  v.out(dM, tokens * 64, "dM");
+  if (v.finish() != MHC_OK) return v.status();
+  mhc::launch_stream_mix_bwd((hipStream_t)stream, act == MHC_F32, tokens, C, G, X, M, dX, dM);
+  return launched("mhc_stream_mix_bwd");
+}
+
+mhc_status mhc_stream_distribute_fwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                                     const void *x, const float *H_post, void *out) {
+  Validator v("mhc_stream_distribute_fwd");
+  v.dims(tokens, n, C, act);
+  if (!v.ok()) return v.status();
+  if (tokens == 0) return MHC_OK;
+  v.in(x, tokens * C * esz(act), "x");
+  v.in(H_post, tokens * 16, "H_post");
+  v.out(out, tokens * 4 * C * esz(act), "out");
+  if (v.finish() != MHC_OK) return v.status();
+  mhc::launch_stream_distribute_fwd((hipStream_t)stream, act == MHC_F32, tokens, C, x, H_post, out);
+  return launched("mhc_stream_distribute_fwd");
+}
+
+mhc_status mhc_stream_distribute_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                                     const void *G, const void *x, const float *H_post, void *dx,
+                                     float *dH_post) {
+  Validator v("mhc_stream_distribute_bwd");
+  v.dims(tokens, n, C, act);
+  if (!v.ok()) return v.status();
+  if (tokens == 0) return MHC_OK;
+  v.in(G, tokens * 4 * C * esz(act), "G");
+  v.in(x, tokens * C * esz(act), "x");
+  v.in(H_post, tokens * 16, "H_post");
+  v.out(dx, tokens * C * esz(act), "dx");
+  v.out(dH_post, tokens * 16, "dH_post");
+  if (v.finish() != MHC_OK) return v.status();
+  mhc::launch_stream_distribute_bwd((hipStream_t)stream, act == MHC_F32, tokens, C, G, x, H_post, dx, dH_post);
+  return launched("mhc_stream_distribute_bwd");
+}
+
+// ------------------------------------------------------------------ h_aggregate, one shared H_pre row
+mhc_status mhc_h_aggregate_static_fwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                                      const void *X, const float *H_pre, void *out) {
+  Validator v("mhc_h_aggregate_static_fwd");
+  v.dims(tokens, n, C, act);
+  if (!v.ok()) return v.status();
+  if (tokens == 0) return MHC_OK;
+  v.in(X, tokens * 4 * C * esz(act), "X");
+  v.in(H_pre, 16, "H_pre");
+  v.out(out, tokens * C * esz(act), "out");
+  if (v.finish() != MHC_OK) return v.status();
+  mhc::launch_h_aggregate_fwd((hipStream_t)stream, act == MHC_F32, tokens, C, X, H_pre, out, 0);
+  return launched("mhc_h_aggregate_static_fwd");
+}
+
+size_t mhc_h_aggregate_static_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
+  (void)act;
+  if (tokens <= 0 || n != 4 || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
+  return mhc::h_aggregate_static_bwd_ws(tokens);
+}
+
+mhc_status mhc_h_aggregate_static_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                                      const void *g, const void *X, const float *H_pre, void *dX,
+                                      int32_t accumulate_dX, float *dH_pre, void *workspace,
+                                      size_t workspace_bytes) {
+  Validator v("mhc_h_aggregate_static_bwd");
+  v.dims(tokens, n, C, act);
+  if (!v.ok()) return v.status();
+  const hipStream_t s = (hipStream_t)stream;
+  if (tokens == 0) {
+    v.out(dH_pre, 16, "dH_pre");
+    if (v.finish() != MHC_OK) return v.status();
+    return zero_f32(s, dH_pre, 4) ? launched("mhc_h_aggregate_static_bwd") : MHC_OK;
+  }
+  v.in(g, tokens * C * esz(act), "g");
+  v.in(X, tokens * 4 * C * esz(act), "X");
+  v.in(H_pre, 16, "H_pre");
+  v.out(dX, tokens * 4 * C * esz(act), "dX");
+  v.out(dH_pre, 16, "dH_pre");
+  v.workspace(workspace, workspace_bytes, mhc::h_aggregate_static_bwd_ws(tokens));
+  if (v.finish() != MHC_OK) return v.status();
+  mhc::launch_h_aggregate_static_bwd(s, act == MHC_F32, tokens, C, g, X, H_pre, dX, accumulate_dX != 0,
+                                     dH_pre, workspace);
+  return launched("mhc_h_aggregate_static_bwd");
+}
+
 // ------------------------------------------------------------------ fused pre pass
 size_t mhc_pre_fwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
   return mhc_proj_rms_h_workspace_size(tokens, n, C, act);

@@ -30,8 +30,9 @@ void launch_sinkhorn_bwd(hipStream_t s, int64_t count, const float *dH, const fl
                          int iters, float eps);
 
 // ---- streaming ops; `f32` selects fp32 activations, else bf16
+// h_stride: H_pre's token stride, 4 (a row per token) or 0 (one shared row).
 void launch_h_aggregate_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *X,
-                            const float *H_pre, void *out);
+                            const float *H_pre, void *out, int64_t h_stride = 4);
 // dX may be NULL (only dH_pre is produced).
 void launch_h_aggregate_bwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *g,
                             const void *X, const float *H_pre, void *dX, bool accumulate,
@@ -39,6 +40,22 @@ void launch_h_aggregate_bwd(hipStream_t s, bool f32, int64_t N, int64_t C, const
 void launch_h_post_bda_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *X,
                            const float *H_res, const float *H_post, const void *x,
                            const void *bias, void *out);
+// One H_pre row [4] for all tokens: dX as above, dH_pre [4] = sum over tokens
+// (per-token rows in ws, then a fixed-order sum).
+size_t h_aggregate_static_bwd_ws(int64_t N);
+void launch_h_aggregate_static_bwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *g,
+                                   const void *X, const float *H_pre, void *dX, bool accumulate,
+                                   float *dH_pre, void *ws);
+// The two halves of h_post_bda on their own: stream mix out[i] = sum_j M[j][i] X[j]
+// and stream distribute out[i] = H_post[i] x, with their backwards.
+void launch_stream_mix_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *X, const float *M,
+                           void *out);
+void launch_stream_mix_bwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *G, const void *X,
+                           const float *M, void *dX, float *dM);
+void launch_stream_distribute_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *x,
+                                  const float *H_post, void *out);
+void launch_stream_distribute_bwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *G,
+                                  const void *x, const float *H_post, void *dx, float *dH_post);
 size_t h_post_bda_bwd_ws(int64_t N, int64_t C, bool with_dbias);
 void launch_h_post_bda_bwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *G,
                            const void *X, const float *H_res, const float *H_post, const void *x,

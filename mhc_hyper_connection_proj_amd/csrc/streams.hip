@@ -41,10 +41,11 @@ __device__ __forceinline__ int clamp_group(int j, int G) {
 }
 
 // ============================================================ h_aggregate fwd
+// hs: H_pre's token stride, 4 (one row per token) or 0 (one row for all).
 template <typename T, int GPT>
 __global__ __launch_bounds__(512) void h_aggregate_fwd_kernel(const T *__restrict__ X,
                                                                const float *__restrict__ Hpre,
-                                                               T *__restrict__ out, int64_t C) {
+                                                               T *__restrict__ out, int64_t C, int64_t hs) {
   using R = typename Io8<T>::raw_t;
   const int64_t t = (int64_t)gridDim.x - 1 - blockIdx.x;  // last token first
   const int G = (int)(C / 8);
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(512) void h_aggregate_fwd_kernel(const T *__restric
 #pragma unroll
     for (int i = 0; i < 4; ++i) rx[j][i] = Io8<T>::ld_nt(xt + i * C + 8 * gc);
   }
-  const float h0 = Hpre[t * 4 + 0], h1 = Hpre[t * 4 + 1], h2 = Hpre[t * 4 + 2], h3 = Hpre[t * 4 + 3];
+  const float h0 = Hpre[t * hs + 0], h1 = Hpre[t * hs + 1], h2 = Hpre[t * hs + 2], h3 = Hpre[t * hs + 3];
 #pragma unroll
   for (int j = 0; j < GPT; ++j) {
     const int g = threadIdx.x + j * blockDim.x;
@@ -72,11 +73,12 @@ __global__ __launch_bounds__(512) void h_aggregate_fwd_kernel(const T *__restric
 }
 
 // ============================================================ h_aggregate bwd
-// dH_pre[t][i] = sum_c g[t][c] X[t][i][c];  optionally dX (+)= H_pre[i] g.
+// dH_pre[t][i] = sum_c g[t][c] X[t][i][c];  optionally dX (+)= H_pre[i] g
+// (H_pre's token stride hs as in the forward).
 template <typename T, int GPT, bool WRITE_DX, bool ACCUM>
 __global__ __launch_bounds__(512) void h_aggregate_bwd_kernel(
     const T *__restrict__ gr, const T *__restrict__ X, const float *__restrict__ Hpre,
-    T *__restrict__ dX, float *__restrict__ dHpre, int64_t C) {
+    T *__restrict__ dX, float *__restrict__ dHpre, int64_t C, int64_t hs) {
   using R = typename Io8<T>::raw_t;
   __shared__ float red[8][4];
   const int64_t t = blockIdx.x;
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(512) void h_aggregate_bwd_kernel(
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   float h[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) h[i] = Hpre[t * 4 + i];
+  for (int i = 0; i < 4; ++i) h[i] = Hpre[t * hs + i];
 #pragma unroll
   for (int j = 0; j < GPT; ++j) {
     const int g = threadIdx.x + j * blockDim.x;
@@ -145,17 +147,45 @@ __global__ __launch_bounds__(512) void h_aggregate_bwd_kernel(
   }
 }
 
+// dH_pre[i] = sum over tokens of the per-token rows part[t][i], for one
+// shared H_pre row: thread k adds tokens k, k + 256, ... in order, then
+// thread 0 adds the 256 thread sums in order (fixed order, no atomics).
+__global__ __launch_bounds__(256) void hpre_rows_sum_kernel(const float *__restrict__ part,
+                                                            float *__restrict__ dH, int64_t N) {
+  __shared__ float4 red[256];
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t t = threadIdx.x; t < N; t += 256) {
+    const float4 v = reinterpret_cast<const float4 *>(part)[t];
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  red[threadIdx.x] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float4 tot = red[0];
+    for (int k = 1; k < 256; ++k) {
+      tot.x += red[k].x; tot.y += red[k].y; tot.z += red[k].z; tot.w += red[k].w;
+    }
+    dH[0] = tot.x; dH[1] = tot.y; dH[2] = tot.z; dH[3] = tot.w;
+  }
+}
+
 // ============================================================ h_post_bda fwd
+// MODE: kPostFull  out[i] = sum_j H_res[j][i] X[j] + H_post[i] (x + bias)
+//       kPostMix   out[i] = sum_j H_res[j][i] X[j]          (x, H_post unused)
+//       kPostDist  out[i] = H_post[i] x                      (X, H_res unused)
 // The new residual is written with non-temporal stores: its 8C bytes per
 // token otherwise sit dirty in the caches when the kernel ends, and their
 // write-back then lands in the next kernel's read stream (on MI355X the
 // following h_post_bda backward measured ~50 us slower at C = 7168, 16384
 // tokens; this kernel itself ran no slower).
-template <typename T, int GPT, bool HAS_BIAS>
+enum : int { kPostFull = 0, kPostMix = 1, kPostDist = 2 };
+
+template <typename T, int GPT, bool HAS_BIAS, int MODE>
 __global__ __launch_bounds__(512) void h_post_bda_fwd_kernel(
     const T *__restrict__ X, const float *__restrict__ Hres, const float *__restrict__ Hpost,
     const T *__restrict__ x, const T *__restrict__ bias, T *__restrict__ out, int64_t C) {
   using R = typename Io8<T>::raw_t;
+  constexpr bool MIX = MODE != kPostDist, DIST = MODE != kPostMix;
   const int64_t t = blockIdx.x;
   const int G = (int)(C / 8);
   const T *xt = X + t * 4 * C;
@@ -163,37 +193,54 @@ __global__ __launch_bounds__(512) void h_post_bda_fwd_kernel(
 #pragma unroll
   for (int j = 0; j < GPT; ++j) {
     const int gc = clamp_group(j, G);
+    if (MIX) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rx[j][i] = Io8<T>::ld_nt(xt + i * C + 8 * gc);
-    rl[j] = Io8<T>::ld_nt(x + t * C + 8 * gc);
+      for (int i = 0; i < 4; ++i) rx[j][i] = Io8<T>::ld_nt(xt + i * C + 8 * gc);
+    }
+    if (DIST) rl[j] = Io8<T>::ld_nt(x + t * C + 8 * gc);
   }
   float hr[16], hp[4];
+  if (MIX) {
 #pragma unroll
-  for (int e = 0; e < 16; ++e) hr[e] = Hres[t * 16 + e];
+    for (int e = 0; e < 16; ++e) hr[e] = Hres[t * 16 + e];
+  }
+  if (DIST) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) hp[i] = Hpost[t * 4 + i];
+    for (int i = 0; i < 4; ++i) hp[i] = Hpost[t * 4 + i];
+  }
   T *ot = out + t * 4 * C;
 #pragma unroll
   for (int j = 0; j < GPT; ++j) {
     const int g = threadIdx.x + j * blockDim.x;
     if (g < G) {
       float xv[4][8], lv[8];
+      if (MIX) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Io8<T>::cvt(rx[j][i], xv[i]);
-      Io8<T>::cvt(rl[j], lv);
-      if (HAS_BIAS) {
-        float bv[8];
-        Io8<T>::load(bias + 8 * g, bv);
+        for (int i = 0; i < 4; ++i) Io8<T>::cvt(rx[j][i], xv[i]);
+      }
+      if (DIST) {
+        Io8<T>::cvt(rl[j], lv);
+        if (HAS_BIAS) {
+          float bv[8];
+          Io8<T>::load(bias + 8 * g, bv);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) lv[e] += bv[e];
+          for (int e = 0; e < 8; ++e) lv[e] += bv[e];
+        }
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float o[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          o[e] = (hr[0 * 4 + i] * xv[0][e] + hr[1 * 4 + i] * xv[1][e]) +
-                 (hr[2 * 4 + i] * xv[2][e] + hr[3 * 4 + i] * xv[3][e]) + hp[i] * lv[e];
+        for (int e = 0; e < 8; ++e) {
+          if (MODE == kPostFull)
+            o[e] = (hr[0 * 4 + i] * xv[0][e] + hr[1 * 4 + i] * xv[1][e]) +
+                   (hr[2 * 4 + i] * xv[2][e] + hr[3 * 4 + i] * xv[3][e]) + hp[i] * lv[e];
+          else if (MODE == kPostMix)
+            o[e] = (hr[0 * 4 + i] * xv[0][e] + hr[1 * 4 + i] * xv[1][e]) +
+                   (hr[2 * 4 + i] * xv[2][e] + hr[3 * 4 + i] * xv[3][e]);
+          else
+            o[e] = hp[i] * lv[e];
+        }
         Io8<T>::store_nt(ot + i * C + 8 * g, o);
       }
     }
@@ -212,13 +259,18 @@ __global__ __launch_bounds__(512) void h_post_bda_fwd_kernel(
 // which leaves one workgroup per CU and measured slower.
 constexpr int kPostTG = 16;
 
-template <typename T, int GPT, bool HAS_BIAS, bool DBIAS>
+// MODE as in the forward: kPostMix computes dX and dH_res only (x, H_post,
+// dx, dH_post unused), kPostDist dx and dH_post only (X, H_res, dX, dH_res
+// unused).
+template <typename T, int GPT, bool HAS_BIAS, bool DBIAS, int MODE>
 __global__ __launch_bounds__(256) void h_post_bda_bwd_kernel(
     const T *__restrict__ Gr, const T *__restrict__ X, const float *__restrict__ Hres,
     const float *__restrict__ Hpost, const T *__restrict__ x, const T *__restrict__ bias,
     T *__restrict__ dX, float *__restrict__ dHres, float *__restrict__ dHpost, T *__restrict__ dx,
     float *__restrict__ dbias_part, int64_t N, int64_t C, int TG) {
   extern __shared__ float red[];  // [nwaves][TG][20]
+  constexpr bool MIX = MODE != kPostDist, DIST = MODE != kPostMix;
+  constexpr int E0 = MIX ? 0 : 16, E1 = DIST ? 20 : 16;  // sums used: dH_res 0..15, dH_post 16..19
   const int G = (int)(C / 8);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   float dbp[GPT][8];
@@ -233,10 +285,14 @@ __global__ __launch_bounds__(256) void h_post_bda_bwd_kernel(
   for (int tt = 0; tt < ntok; ++tt) {
     const int64_t t = t0 + tt;
     float hr[16], hp[4];
+    if (MIX) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) hr[e] = Hres[t * 16 + e];
+      for (int e = 0; e < 16; ++e) hr[e] = Hres[t * 16 + e];
+    }
+    if (DIST) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) hp[i] = Hpost[t * 4 + i];
+      for (int i = 0; i < 4; ++i) hp[i] = Hpost[t * 4 + i];
+    }
     float acc[20];
 #pragma unroll
     for (int e = 0; e < 20; ++e) acc[e] = 0.f;
@@ -249,10 +305,12 @@ __global__ __launch_bounds__(256) void h_post_bda_bwd_kernel(
         float gv[4][8], xv[4][8], lv[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) Io8<T>::load_nt(gt + i * C + 8 * g, gv[i]);
+        if (MIX) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Io8<T>::load_nt(xt + i * C + 8 * g, xv[i]);
-        Io8<T>::load_nt(x + t * C + 8 * g, lv);
-        if (HAS_BIAS) {
+          for (int i = 0; i < 4; ++i) Io8<T>::load_nt(xt + i * C + 8 * g, xv[i]);
+        }
+        if (DIST) Io8<T>::load_nt(x + t * C + 8 * g, lv);
+        if (DIST && HAS_BIAS) {
           float bv[8];
           Io8<T>::load(bias + 8 * g, bv);
 #pragma unroll
@@ -261,7 +319,7 @@ __global__ __launch_bounds__(256) void h_post_bda_bwd_kernel(
         // dX[j] = sum_i H_res[j][i] G[i]  (skipped when the caller folds it
         // into the pre pass backward; dX is then null for every thread)
 #pragma unroll
-        for (int js = 0; js < 4 && dX != nullptr; ++js) {
+        for (int js = 0; js < 4 && MIX && dX != nullptr; ++js) {
           float o[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e)
@@ -270,7 +328,7 @@ __global__ __launch_bounds__(256) void h_post_bda_bwd_kernel(
           Io8<T>::store(dX + (t * 4 + js) * C + 8 * g, o);
         }
         // dx = sum_i H_post[i] G[i]
-        {
+        if (DIST) {
           float o[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e)
@@ -282,34 +340,38 @@ __global__ __launch_bounds__(256) void h_post_bda_bwd_kernel(
           }
         }
         // dH_res[js][i] += X[js] . G[i];  dH_post[i] += G[i] . (x + bias)
+        if (MIX) {
 #pragma unroll
-        for (int js = 0; js < 4; ++js)
+          for (int js = 0; js < 4; ++js)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float s = 0.f;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) s += xv[js][e] * gv[i][e];
+              acc[js * 4 + i] += s;
+            }
+        }
+        if (DIST) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             float s = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s += xv[js][e] * gv[i][e];
-            acc[js * 4 + i] += s;
+            for (int e = 0; e < 8; ++e) s += gv[i][e] * lv[e];
+            acc[16 + i] += s;
           }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float s = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) s += gv[i][e] * lv[e];
-          acc[16 + i] += s;
         }
       }
     }
 #pragma unroll
-    for (int e = 0; e < 20; ++e) {
+    for (int e = E0; e < E1; ++e) {
       const float s = wave_sum(acc[e]);
       if (lane == 0) red[(wave * TG + tt) * 20 + e] = s;
     }
   }
   __syncthreads();
   const int nw = blockDim.x >> 6;
-  for (int k = threadIdx.x; k < ntok * 20; k += blockDim.x) {
-    const int tt = k / 20, e = k % 20;
+  for (int k = threadIdx.x; k < ntok * (E1 - E0); k += blockDim.x) {
+    const int tt = k / (E1 - E0), e = E0 + k % (E1 - E0);
     float s = 0.f;
     for (int w = 0; w < nw; ++w) s += red[(w * TG + tt) * 20 + e];
     const int64_t t = t0 + tt;
@@ -372,61 +434,74 @@ __global__ __launch_bounds__(256) void dbias_reduce_kernel(const float *__restri
   }
 
 template <typename T>
-static void agg_fwd(hipStream_t s, int64_t N, int64_t C, const void *X, const float *H, void *out) {
+static void agg_fwd(hipStream_t s, int64_t N, int64_t C, const void *X, const float *H, void *out, int64_t hs) {
   const StreamGeom g = stream_geom(C);
   MHC_GPT_DISPATCH(g.gpt, hipLaunchKernelGGL((h_aggregate_fwd_kernel<T, GPT>), dim3((unsigned)N),
-                                              dim3(g.tpb), 0, s, (const T *)X, H, (T *)out, C));
+                                              dim3(g.tpb), 0, s, (const T *)X, H, (T *)out, C, hs));
 }
 
 void launch_h_aggregate_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *X,
-                            const float *H_pre, void *out) {
+                            const float *H_pre, void *out, int64_t h_stride) {
   if (f32)
-    agg_fwd<float>(s, N, C, X, H_pre, out);
+    agg_fwd<float>(s, N, C, X, H_pre, out, h_stride);
   else
-    agg_fwd<bf16_t>(s, N, C, X, H_pre, out);
+    agg_fwd<bf16_t>(s, N, C, X, H_pre, out, h_stride);
 }
 
 template <typename T, bool WRITE_DX, bool ACCUM>
 static void agg_bwd3(hipStream_t s, int64_t N, int64_t C, const void *g, const void *X,
-                     const float *H, void *dX, float *dH) {
+                     const float *H, void *dX, float *dH, int64_t hs) {
   const StreamGeom geo = stream_geom(C);
   MHC_GPT_DISPATCH(geo.gpt,
                    hipLaunchKernelGGL((h_aggregate_bwd_kernel<T, GPT, WRITE_DX, ACCUM>),
                                       dim3((unsigned)N), dim3(geo.tpb), 0, s, (const T *)g,
-                                      (const T *)X, H, (T *)dX, dH, C));
+                                      (const T *)X, H, (T *)dX, dH, C, hs));
 }
 
 template <typename T>
 static void agg_bwd(hipStream_t s, int64_t N, int64_t C, const void *g, const void *X,
-                    const float *H, void *dX, bool acc, float *dH) {
+                    const float *H, void *dX, bool acc, float *dH, int64_t hs) {
   if (!dX)
-    agg_bwd3<T, false, false>(s, N, C, g, X, H, dX, dH);
+    agg_bwd3<T, false, false>(s, N, C, g, X, H, dX, dH, hs);
   else if (acc)
-    agg_bwd3<T, true, true>(s, N, C, g, X, H, dX, dH);
+    agg_bwd3<T, true, true>(s, N, C, g, X, H, dX, dH, hs);
   else
-    agg_bwd3<T, true, false>(s, N, C, g, X, H, dX, dH);
+    agg_bwd3<T, true, false>(s, N, C, g, X, H, dX, dH, hs);
 }
 
 void launch_h_aggregate_bwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *g,
                             const void *X, const float *H_pre, void *dX, bool accumulate,
                             float *dH_pre) {
   if (f32)
-    agg_bwd<float>(s, N, C, g, X, H_pre, dX, accumulate, dH_pre);
+    agg_bwd<float>(s, N, C, g, X, H_pre, dX, accumulate, dH_pre, 4);
   else
-    agg_bwd<bf16_t>(s, N, C, g, X, H_pre, dX, accumulate, dH_pre);
+    agg_bwd<bf16_t>(s, N, C, g, X, H_pre, dX, accumulate, dH_pre, 4);
 }
 
-template <typename T>
+size_t h_aggregate_static_bwd_ws(int64_t N) { return (size_t)N * 16; }
+
+void launch_h_aggregate_static_bwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *g,
+                                   const void *X, const float *H_pre, void *dX, bool accumulate,
+                                   float *dH_pre, void *ws) {
+  float *rows = (float *)ws;  // per-token dH_pre rows [N][4]
+  if (f32)
+    agg_bwd<float>(s, N, C, g, X, H_pre, dX, accumulate, rows, 0);
+  else
+    agg_bwd<bf16_t>(s, N, C, g, X, H_pre, dX, accumulate, rows, 0);
+  hipLaunchKernelGGL(hpre_rows_sum_kernel, dim3(1), dim3(256), 0, s, rows, dH_pre, N);
+}
+
+template <typename T, int MODE>
 static void post_fwd(hipStream_t s, int64_t N, int64_t C, const void *X, const float *Hr,
                      const float *Hp, const void *x, const void *b, void *out) {
   const StreamGeom geo = stream_geom(C);
   if (b) {
-    MHC_GPT_DISPATCH(geo.gpt, hipLaunchKernelGGL((h_post_bda_fwd_kernel<T, GPT, true>),
+    MHC_GPT_DISPATCH(geo.gpt, hipLaunchKernelGGL((h_post_bda_fwd_kernel<T, GPT, true, MODE>),
                                                   dim3((unsigned)N), dim3(geo.tpb), 0, s,
                                                   (const T *)X, Hr, Hp, (const T *)x,
                                                   (const T *)b, (T *)out, C));
   } else {
-    MHC_GPT_DISPATCH(geo.gpt, hipLaunchKernelGGL((h_post_bda_fwd_kernel<T, GPT, false>),
+    MHC_GPT_DISPATCH(geo.gpt, hipLaunchKernelGGL((h_post_bda_fwd_kernel<T, GPT, false, MODE>),
                                                   dim3((unsigned)N), dim3(geo.tpb), 0, s,
                                                   (const T *)X, Hr, Hp, (const T *)x,
                                                   (const T *)nullptr, (T *)out, C));
@@ -437,9 +512,25 @@ void launch_h_post_bda_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const 
                            const float *H_res, const float *H_post, const void *x,
                            const void *bias, void *out) {
   if (f32)
-    post_fwd<float>(s, N, C, X, H_res, H_post, x, bias, out);
+    post_fwd<float, kPostFull>(s, N, C, X, H_res, H_post, x, bias, out);
   else
-    post_fwd<bf16_t>(s, N, C, X, H_res, H_post, x, bias, out);
+    post_fwd<bf16_t, kPostFull>(s, N, C, X, H_res, H_post, x, bias, out);
+}
+
+void launch_stream_mix_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *X, const float *M,
+                           void *out) {
+  if (f32)
+    post_fwd<float, kPostMix>(s, N, C, X, M, nullptr, nullptr, nullptr, out);
+  else
+    post_fwd<bf16_t, kPostMix>(s, N, C, X, M, nullptr, nullptr, nullptr, out);
+}
+
+void launch_stream_distribute_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *x,
+                                  const float *H_post, void *out) {
+  if (f32)
+    post_fwd<float, kPostDist>(s, N, C, nullptr, nullptr, H_post, x, nullptr, out);
+  else
+    post_fwd<bf16_t, kPostDist>(s, N, C, nullptr, nullptr, H_post, x, nullptr, out);
 }
 
 size_t h_post_bda_bwd_ws(int64_t N, int64_t C, bool with_dbias) {
@@ -448,7 +539,7 @@ size_t h_post_bda_bwd_ws(int64_t N, int64_t C, bool with_dbias) {
   return (size_t)(rows * C) * sizeof(float);
 }
 
-template <typename T, bool HAS_BIAS, bool DBIAS>
+template <typename T, bool HAS_BIAS, bool DBIAS, int MODE = kPostFull>
 static void post_bwd3(hipStream_t s, int64_t N, int64_t C, const void *G, const void *X,
                       const float *Hr, const float *Hp, const void *x, const void *b, void *dX,
                       float *dHr, float *dHp, void *dx, float *part) {
@@ -460,7 +551,7 @@ static void post_bwd3(hipStream_t s, int64_t N, int64_t C, const void *G, const 
   const unsigned blocks = (unsigned)((N + TG - 1) / TG);
   const size_t lds = (size_t)(geo.tpb / 64) * TG * 20 * sizeof(float);
   MHC_GPT_DISPATCH8(geo.gpt,
-                   hipLaunchKernelGGL((h_post_bda_bwd_kernel<T, GPT, HAS_BIAS, DBIAS>),
+                   hipLaunchKernelGGL((h_post_bda_bwd_kernel<T, GPT, HAS_BIAS, DBIAS, MODE>),
                                       dim3(blocks), dim3(geo.tpb), lds, s, (const T *)G,
                                       (const T *)X, Hr, Hp, (const T *)x, (const T *)b, (T *)dX,
                                       dHr, dHp, (T *)dx, part, N, C, TG));
@@ -481,6 +572,26 @@ static void post_bwd(hipStream_t s, int64_t N, int64_t C, const void *G, const v
   } else {
     post_bwd3<T, false, false>(s, N, C, G, X, Hr, Hp, x, b, dX, dHr, dHp, dx, nullptr);
   }
+}
+
+void launch_stream_mix_bwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *G, const void *X,
+                           const float *M, void *dX, float *dM) {
+  if (f32)
+    post_bwd3<float, false, false, kPostMix>(s, N, C, G, X, M, nullptr, nullptr, nullptr, dX, dM, nullptr,
+                                             nullptr, nullptr);
+  else
+    post_bwd3<bf16_t, false, false, kPostMix>(s, N, C, G, X, M, nullptr, nullptr, nullptr, dX, dM, nullptr,
+                                              nullptr, nullptr);
+}
+
+void launch_stream_distribute_bwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *G,
+                                  const void *x, const float *H_post, void *dx, float *dH_post) {
+  if (f32)
+    post_bwd3<float, false, false, kPostDist>(s, N, C, G, nullptr, nullptr, H_post, x, nullptr, nullptr,
+                                              nullptr, dH_post, dx, nullptr);
+  else
+    post_bwd3<bf16_t, false, false, kPostDist>(s, N, C, G, nullptr, nullptr, H_post, x, nullptr, nullptr,
+                                               nullptr, dH_post, dx, nullptr);
 }
 
 void launch_h_post_bda_bwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *G,

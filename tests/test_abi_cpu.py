@@ -57,6 +57,25 @@ def _last(lib):
     return lib.mhc_last_error().decode()
 
 
+def test_variant_entry_points_validate_before_launch(lib):
+    E = {n: i for i, n in enumerate(L.STATUS)}
+    fake = 0x10000
+    # n != 4, C % 8 != 0, NULL inputs, a misaligned output: all rejected on the host
+    assert lib.mhc_stream_mix_fwd(None, 4, 3, 64, 0, fake, fake + 4096, fake + 8192) == E["MHC_ERR_UNSUPPORTED"]
+    assert lib.mhc_stream_mix_fwd(None, 4, 4, 60, 0, fake, fake + 4096, fake + 8192) == E["MHC_ERR_UNSUPPORTED"]
+    assert lib.mhc_stream_mix_bwd(None, 4, 4, 64, 0, None, fake, fake, fake, fake) == E["MHC_ERR_NULL"]
+    assert lib.mhc_stream_distribute_fwd(None, 4, 4, 64, 0, fake, fake + 4096, fake + 8200) == E["MHC_ERR_ALIGN"]
+    assert lib.mhc_stream_distribute_bwd(None, 4, 4, 64, 0, fake, None, fake, fake, fake) == E["MHC_ERR_NULL"]
+    assert lib.mhc_h_aggregate_static_fwd(None, 4, 4, 64, 0, fake, None, fake + 8192) == E["MHC_ERR_NULL"]
+    # the shared-row backward needs a workspace of 16 bytes per token
+    assert lib.mhc_h_aggregate_static_bwd_workspace_size(100, 4, 64, 0) == 1600
+    st = lib.mhc_h_aggregate_static_bwd(None, 100, 4, 64, 0, fake, fake + (1 << 20), fake + (2 << 20),
+                                        fake + (3 << 20), 0, fake + (4 << 20), fake + (5 << 20), 16)
+    assert st == E["MHC_ERR_WORKSPACE"]
+    # overlapping output and input
+    assert lib.mhc_stream_mix_fwd(None, 4, 4, 64, 0, fake, fake + 8192, fake + 1024) == E["MHC_ERR_ALIAS"]
+
+
 def test_kernel_events_hook_validation(lib):
     # handles are only stored (no HIP call is made until a kernel launches)
     fake = 0x1000

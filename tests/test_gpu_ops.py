@@ -136,6 +136,69 @@ def test_h_post_bda(act, N, C, bias):
             assert_tokensum("dbias (no dX)", ndb, odb, np.abs(odx).sum(axis=0), act)
 
 
+# ----------------------------------------------------------------- stream mix / distribute, shared-row aggregate
+VARIANT_SHAPES = [("bf16", 1, 8), ("bf16", 37, 296), ("bf16", 50, 4096), ("f32", 17, 1032), ("bf16", 21, 7168),
+                  ("bf16", 3, 16384)]
+
+
+@pytest.mark.parametrize("act,N,C", VARIANT_SHAPES)
+def test_stream_mix(act, N, C):
+    log(f"stream mix act={act} N={N} C={C}")
+    X = store(RNG.standard_normal((N, 4, C)), act)
+    G = store(RNG.standard_normal((N, 4, C)), act)
+    M = f32(RNG.standard_normal((N, 4, 4)))
+    out = B.mhc_stream_mix_fwd(dev(X), dev(M))
+    dX, dM = B.mhc_stream_mix_bwd(dev(G), dev(X), dev(M))
+    torch.cuda.synchronize()
+    assert_act("out", out, O.stream_mix_fwd(h64(X), h64(M)), act)
+    odX, odM = O.stream_mix_bwd(h64(G), h64(X), h64(M))
+    assert_act("dX", dX, odX, act)
+    assert_mixed("dM", dM, odM)
+
+
+@pytest.mark.parametrize("act,N,C", VARIANT_SHAPES)
+def test_stream_distribute(act, N, C):
+    log(f"stream distribute act={act} N={N} C={C}")
+    x = store(RNG.standard_normal((N, C)), act)
+    G = store(RNG.standard_normal((N, 4, C)), act)
+    Hp = f32(RNG.standard_normal((N, 4)))
+    out = B.mhc_stream_distribute_fwd(dev(x), dev(Hp))
+    dx, dH = B.mhc_stream_distribute_bwd(dev(G), dev(x), dev(Hp))
+    torch.cuda.synchronize()
+    assert_act("out", out, O.stream_distribute_fwd(h64(x), h64(Hp)), act)
+    odx, odH = O.stream_distribute_bwd(h64(G), h64(x), h64(Hp))
+    assert_act("dx", dx, odx, act)
+    assert_mixed("dH_post", dH, odH)
+
+
+@pytest.mark.parametrize("act,N,C", VARIANT_SHAPES)
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_h_aggregate_static(act, N, C, accumulate):
+    log(f"h_aggregate static act={act} N={N} C={C} accumulate={accumulate}")
+    X = store(RNG.standard_normal((N, 4, C)), act)
+    g = store(RNG.standard_normal((N, C)), act)
+    h = f32(RNG.standard_normal(4))
+    out = B.mhc_h_aggregate_static_fwd(dev(X), dev(h))
+    dX0 = store(RNG.standard_normal((N, 4, C)), act) if accumulate else None
+    dX, dH = B.mhc_h_aggregate_static_bwd(dev(g), dev(X), dev(h), dX=dev(dX0) if accumulate else None,
+                                          accumulate_dX=accumulate)
+    torch.cuda.synchronize()
+    assert_act("agg", out, O.h_aggregate_static_fwd(h64(X), h64(h)), act)
+    odX, odH = O.h_aggregate_static_bwd(h64(g), h64(X), h64(h))
+    assert_act("dX", dX, odX + (h64(dX0) if accumulate else 0.0), act)
+    parts = np.abs(O.h_aggregate_bwd(h64(g), h64(X), np.broadcast_to(h64(h), (N, 4)).copy())[1]).sum(axis=0)
+    assert_tokensum("dH_pre", dH, odH, parts)
+
+
+def test_variants_zero_tokens():
+    X = torch.empty(0, 4, 64, dtype=torch.bfloat16, device="cuda")
+    dX, dH = B.mhc_h_aggregate_static_bwd(torch.empty(0, 64, dtype=torch.bfloat16, device="cuda"), X,
+                                          torch.ones(4, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(dH.cpu(), torch.zeros(4))
+    assert B.mhc_stream_mix_fwd(X, torch.empty(0, 4, 4, device="cuda")).shape == X.shape
+
+
 def test_h_post_bda_identity_h_res_exact_bf16():
     # H_res = I and H_post = 0: out must reproduce the residual bit for bit
     N, C = 19, 4096
