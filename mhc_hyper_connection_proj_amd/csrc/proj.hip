@@ -369,13 +369,15 @@ __global__ __launch_bounds__(512) void proj_partial_dma_kernel(const bf16_t *__r
 }
 
 // ------------------------------------------------------------------ finalize
-// One thread per token: fixed-order sum of the kSplitK partials, RMS,
-// compute_h, and (when H_res != NULL) the Sinkhorn projection of the logits.
-__global__ __launch_bounds__(256) void proj_finalize_kernel(
+// One thread per token, one wave per workgroup (so the few waves a layer's
+// tokens make spread over all CUs): fixed-order sum of the kSplitK partials,
+// RMS, compute_h, and (when H_res != NULL) the Sinkhorn projection of the
+// logits.
+__global__ __launch_bounds__(64) void proj_finalize_kernel(
     const float *__restrict__ part, const float *__restrict__ alpha, const float *__restrict__ hbias,
     float rms_eps, float *__restrict__ Hpre, float *__restrict__ Hpost, float *__restrict__ logits,
     float *__restrict__ saved, float *__restrict__ Hres, int iters, float eps, int64_t N, int64_t K) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * 64 + threadIdx.x;
   if (t >= N) return;
   float p[kJ + 1];
 #pragma unroll
@@ -445,7 +447,7 @@ void launch_proj_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *
     hipLaunchKernelGGL(proj_partial_dma_kernel, dim3(pblocks), dim3(kDmaWaves * 64), lds, s,
                        (const bf16_t *)X, (const bf16_t *)wpk, part, N, K);
   }
-  hipLaunchKernelGGL(proj_finalize_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, part,
+  hipLaunchKernelGGL(proj_finalize_kernel, dim3((unsigned)((N + 63) / 64)), dim3(64), 0, s, part,
                      alpha, hbias, rms_eps, H_pre, H_post, logits, saved, H_res, iters, eps, N, K);
 }
 
@@ -539,6 +541,8 @@ __device__ __forceinline__ uint16_t bf16_bits(float v) { return __builtin_bit_ca
 
 // One thread per token (grid covers npad tokens; tokens >= N only zero their
 // dpA record).  Block partial sums of dhbias (24) and dalpha (3) go to ppart.
+// (One-wave workgroups measured no faster here: the Sinkhorn backward chain
+// bounds each wave, and four times the partials slow the final sum.)
 // MFMA_OUT (bf16 activations): the token's record for the MFMA kernel is the
 // exact three-term bf16 split of dp, [term][j], then c_rms (fp32) and zero
 // padding (kDpaBytes).  Otherwise dp and c_rms go to the fp32 row dpf.

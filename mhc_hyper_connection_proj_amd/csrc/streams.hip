@@ -148,24 +148,29 @@ __global__ __launch_bounds__(512) void h_aggregate_bwd_kernel(
 }
 
 // dH_pre[i] = sum over tokens of the per-token rows part[t][i], for one
-// shared H_pre row: thread k adds tokens k, k + 256, ... in order, then
-// thread 0 adds the 256 thread sums in order (fixed order, no atomics).
+// shared H_pre row: thread k adds tokens k, k + 256, ... in order (eight
+// loads in flight), then a fixed pairwise tree over the 256 thread sums.
 __global__ __launch_bounds__(256) void hpre_rows_sum_kernel(const float *__restrict__ part,
                                                             float *__restrict__ dH, int64_t N) {
   __shared__ float4 red[256];
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4 *p = reinterpret_cast<const float4 *>(part);
+#pragma unroll 8
   for (int64_t t = threadIdx.x; t < N; t += 256) {
-    const float4 v = reinterpret_cast<const float4 *>(part)[t];
+    const float4 v = p[t];
     s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
   }
   red[threadIdx.x] = s;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float4 tot = red[0];
-    for (int k = 1; k < 256; ++k) {
-      tot.x += red[k].x; tot.y += red[k].y; tot.z += red[k].z; tot.w += red[k].w;
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      const float4 a = red[threadIdx.x], b = red[threadIdx.x + w];
+      red[threadIdx.x] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
     }
-    dH[0] = tot.x; dH[1] = tot.y; dH[2] = tot.z; dH[3] = tot.w;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    dH[0] = red[0].x; dH[1] = red[0].y; dH[2] = red[0].z; dH[3] = red[0].w;
   }
 }
 
