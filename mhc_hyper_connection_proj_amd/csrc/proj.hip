@@ -369,59 +369,76 @@ __global__ __launch_bounds__(512) void proj_partial_dma_kernel(const bf16_t *__r
 }
 
 // ------------------------------------------------------------------ finalize
-// One thread per token, one wave per workgroup (so the few waves a layer's
-// tokens make spread over all CUs): fixed-order sum of the kSplitK partials,
-// RMS, compute_h, and (when H_res != NULL) the Sinkhorn projection of the
-// logits.
+// Four lanes per token (quad layout of the Sinkhorn code: lane r = row r of
+// H_res), 16 tokens per one-wave workgroup, so a layer's tokens make enough
+// waves to spread over all CUs.  Lane r owns the columns r (PRE), 4 + r
+// (POST) and 8 + 4r .. 11 + 4r (RES row r): fixed-order sum of the kSplitK
+// partials, RMS, compute_h, and (when H_res != NULL) the Sinkhorn projection.
+// Every value is computed as in a one-lane-per-token form, bit for bit.
 __global__ __launch_bounds__(64) void proj_finalize_kernel(
     const float *__restrict__ part, const float *__restrict__ alpha, const float *__restrict__ hbias,
     float rms_eps, float *__restrict__ Hpre, float *__restrict__ Hpost, float *__restrict__ logits,
     float *__restrict__ saved, float *__restrict__ Hres, int iters, float eps, int64_t N, int64_t K) {
-  const int64_t t = (int64_t)blockIdx.x * 64 + threadIdx.x;
-  if (t >= N) return;
-  float p[kJ + 1];
+  const int r4 = threadIdx.x & 3;
+  const int64_t t = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 2);
+  if (t >= N) return;  // whole quads
+  // owned columns: jp = r4, jq = 4 + r4, jr = 8 + 4 r4 .. + 3; and the sum of squares
+  float vp[kSplitK], vq[kSplitK], vr[kSplitK][4], vs[kSplitK];
 #pragma unroll
-  for (int j = 0; j < kJ + 1; ++j) {
+  for (int sl = 0; sl < kSplitK; ++sl) {
+    const float *row = part + ((int64_t)sl * N + t) * kPartStride;
+    vp[sl] = row[r4];
+    vq[sl] = row[4 + r4];
+    const float4 w = reinterpret_cast<const float4 *>(row)[2 + r4];
+    vr[sl][0] = w.x; vr[sl][1] = w.y; vr[sl][2] = w.z; vr[sl][3] = w.w;
+    vs[sl] = row[kJ];
+  }
+  auto tree = [](const float v[kSplitK]) {
+    return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+  };
+  static_assert(kSplitK == 8, "tree");
+  float p[6];
+  p[0] = tree(vp);
+  p[1] = tree(vq);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
     float v[kSplitK];
 #pragma unroll
-    for (int s = 0; s < kSplitK; ++s) v[s] = part[((int64_t)s * N + t) * kPartStride + j];
-    p[j] = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    for (int sl = 0; sl < kSplitK; ++sl) v[sl] = vr[sl][b];
+    p[2 + b] = tree(v);
   }
-  const float q = sqrtf(p[kJ] / (float)K);
+  const float q = sqrtf(tree(vs) / (float)K);
   const float r = 1.0f / (q + rms_eps);
-  float z[kJ], zh[kJ];
+  const int jcol[6] = {r4, 4 + r4, 8 + 4 * r4, 9 + 4 * r4, 10 + 4 * r4, 11 + 4 * r4};
+  float z[6], zh[6];
 #pragma unroll
-  for (int j = 0; j < kJ; ++j) {
-    z[j] = r * p[j];
-    const int seg = j < 4 ? 0 : (j < 8 ? 1 : 2);
+  for (int u = 0; u < 6; ++u) {
+    z[u] = r * p[u];
+    const int seg = u == 0 ? 0 : (u == 1 ? 1 : 2);
     const float a = alpha ? alpha[seg] : 1.f;
-    const float b = hbias ? hbias[j] : 0.f;
-    zh[j] = a * z[j] + b;
+    const float b = hbias ? hbias[jcol[u]] : 0.f;
+    zh[u] = a * z[u] + b;
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    Hpre[t * 4 + i] = 1.0f / (1.0f + expf(-zh[i]));
-    Hpost[t * 4 + i] = 2.0f / (1.0f + expf(-zh[4 + i]));
-  }
-  store16(logits + t * 16, zh + 8);
+  Hpre[t * 4 + r4] = 1.0f / (1.0f + expf(-zh[0]));
+  Hpost[t * 4 + r4] = 2.0f / (1.0f + expf(-zh[1]));
+  reinterpret_cast<float4 *>(logits + t * 16)[r4] = make_float4(zh[2], zh[3], zh[4], zh[5]);
   if (saved) {
-    float sv[kSavedStride];
-    sv[0] = r;
-    sv[1] = q;
-#pragma unroll
-    for (int j = 0; j < kJ; ++j) sv[2 + j] = z[j];
-#pragma unroll
-    for (int j = 2 + kJ; j < kSavedStride; ++j) sv[j] = 0.f;
-#pragma unroll
-    for (int qd = 0; qd < kSavedStride / 4; ++qd)
-      reinterpret_cast<float4 *>(saved + t * kSavedStride)[qd] =
-          make_float4(sv[4 * qd], sv[4 * qd + 1], sv[4 * qd + 2], sv[4 * qd + 3]);
+    float *sv = saved + t * kSavedStride;
+    sv[2 + r4] = z[0];
+    sv[6 + r4] = z[1];
+    reinterpret_cast<float2 *>(sv + 10 + 4 * r4)[0] = make_float2(z[2], z[3]);
+    reinterpret_cast<float2 *>(sv + 12 + 4 * r4)[0] = make_float2(z[4], z[5]);
+    if (r4 == 0) {
+      reinterpret_cast<float2 *>(sv)[0] = make_float2(r, q);
+      reinterpret_cast<float2 *>(sv + 26)[0] = make_float2(0.f, 0.f);
+      reinterpret_cast<float4 *>(sv + 28)[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   }
   if (Hres) {
-    float M[16];
-    sk_exp(zh + 8, M);
-    sk_forward(M, iters, eps);
-    store16(Hres + t * 16, M);
+    float m[4];
+    sk_exp4(zh + 2, m);
+    sk_forward_q(m, iters, eps, r4);
+    reinterpret_cast<float4 *>(Hres + t * 16)[r4] = make_float4(m[0], m[1], m[2], m[3]);
   }
 }
 
@@ -447,7 +464,7 @@ void launch_proj_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *
     hipLaunchKernelGGL(proj_partial_dma_kernel, dim3(pblocks), dim3(kDmaWaves * 64), lds, s,
                        (const bf16_t *)X, (const bf16_t *)wpk, part, N, K);
   }
-  hipLaunchKernelGGL(proj_finalize_kernel, dim3((unsigned)((N + 63) / 64)), dim3(64), 0, s, part,
+  hipLaunchKernelGGL(proj_finalize_kernel, dim3((unsigned)((N + 15) / 16)), dim3(64), 0, s, part,
                      alpha, hbias, rms_eps, H_pre, H_post, logits, saved, H_res, iters, eps, N, K);
 }
 
@@ -472,6 +489,7 @@ void launch_proj_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *
 // fp32 activations use a VALU kernel for both contractions.
 constexpr int kDpf = 32;     // fp32 per-token record: dp[24], c_rms, pad
 constexpr int kDpaBytes = 160;  // bf16 per-token record: dp terms [3][24], c_rms (fp32), pad
+constexpr int kTokTB = 64;      // tokens per workgroup of the per-token kernel
 constexpr int kBwKW = 64;    // k per wave in the MFMA kernel
 constexpr int kBwKT = 4 * kBwKW;
 constexpr int kDxK = 4;      // k per thread in the fp32 VALU kernel
@@ -520,7 +538,7 @@ static BwdWs bwd_layout(void *ws, int64_t N, int64_t C, bool f32) {
   const int64_t K = 4 * C;
   BwdWs L{};
   L.npad = round_up(N, 32);
-  L.nblk = (L.npad + 255) / 256;
+  L.nblk = (L.npad + kTokTB - 1) / kTokTB;  // per-token kernel workgroups
   L.tbsz = bwd_token_block(N, K, f32);
   L.ntb = (N + L.tbsz - 1) / L.tbsz;
   size_t off = 0;
@@ -539,13 +557,14 @@ size_t proj_bwd_ws(int64_t N, int64_t C, bool f32) { return bwd_layout(nullptr, 
 
 __device__ __forceinline__ uint16_t bf16_bits(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
 
-// One thread per token (grid covers npad tokens; tokens >= N only zero their
-// dpA record).  Block partial sums of dhbias (24) and dalpha (3) go to ppart.
-// (One-wave workgroups measured no faster here: the Sinkhorn backward chain
-// bounds each wave, and four times the partials slow the final sum.)
-// MFMA_OUT (bf16 activations): the token's record for the MFMA kernel is the
-// exact three-term bf16 split of dp, [term][j], then c_rms (fp32) and zero
-// padding (kDpaBytes).  Otherwise dp and c_rms go to the fp32 row dpf.
+// Four lanes per token (the quad layout of the Sinkhorn code), 64 tokens per
+// 256-thread workgroup; lane r owns the columns r (PRE), 4 + r (POST) and
+// 8 + 4r .. 11 + 4r (RES row r).  The grid covers npad tokens (tokens >= N
+// only zero their dpA record).  Workgroup partial sums of dhbias (24) and
+// dalpha (3) go to ppart.  MFMA_OUT (bf16 activations): the token's record
+// for the MFMA kernel is the exact three-term bf16 split of dp, [term][j],
+// then c_rms (fp32) and zero padding (kDpaBytes), staged in LDS and written
+// as whole 16-byte pieces.  Otherwise dp and c_rms go to the fp32 row dpf.
 template <bool MFMA_OUT>
 __global__ __launch_bounds__(256) void proj_bwd_token_kernel(
     const float *__restrict__ alpha, const float *__restrict__ saved, const float *__restrict__ Hpre,
@@ -554,91 +573,108 @@ __global__ __launch_bounds__(256) void proj_bwd_token_kernel(
     int iters, float eps, float *__restrict__ dpf, char *__restrict__ dpA,
     float *__restrict__ ppart, float *__restrict__ dL_out, float *__restrict__ dHpre_out, int64_t N,
     int64_t npad, int64_t K) {
+  constexpr int kRec = MFMA_OUT ? kDpaBytes : kDpf * 4;  // bytes per staged token
   __shared__ float red[4][28];
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  __shared__ __attribute__((aligned(16))) char stage[kTokTB * kRec];
+  const int r4 = threadIdx.x & 3;
+  const int tl = threadIdx.x >> 2;
+  const int64_t t0 = (int64_t)blockIdx.x * kTokTB;
+  const int64_t t = t0 + tl;
+  char *st = stage + tl * kRec;
   float contrib[27];
 #pragma unroll
   for (int e = 0; e < 27; ++e) contrib[e] = 0.f;
-  if (t < N) {
-    float dl[16];
-    if (dL_in) {
-      load16(dL_in + t * 16, dl);
-    } else {
-      float lg[16];
-      load16(logits + t * 16, lg);
-      load16(dHres + t * 16, dl);
-      sk_backward(lg, dl, iters, eps);
+  if (t < N) {  // whole quads
+    float g[4];
+    {
+      const float4 w = reinterpret_cast<const float4 *>((dL_in ? dL_in : dHres) + t * 16)[r4];
+      g[0] = w.x; g[1] = w.y; g[2] = w.z; g[3] = w.w;
     }
-    if (dL_out) store16(dL_out + t * 16, dl);
-    const float r = saved[t * kSavedStride + 0];
-    const float q = saved[t * kSavedStride + 1];
-    float z[kJ], dzh[kJ];
-#pragma unroll
-    for (int j = 0; j < kJ; ++j) z[j] = saved[t * kSavedStride + 2 + j];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float hp = Hpre[t * 4 + i];
-      const float dhp = dHpre[t * 4 + i];
-      if (dHpre_out) dHpre_out[t * 4 + i] = dhp;
-      dzh[i] = dhp * (hp * (1.f - hp));
-      const float hq = Hpost[t * 4 + i];
-      dzh[4 + i] = dHpost[t * 4 + i] * (hq * (1.f - 0.5f * hq));
+    if (!dL_in) {
+      const float4 w = reinterpret_cast<const float4 *>(logits + t * 16)[r4];
+      const float l[4] = {w.x, w.y, w.z, w.w};
+      sk_backward_q(l, g, iters, eps, r4);
     }
+    if (dL_out) reinterpret_cast<float4 *>(dL_out + t * 16)[r4] = make_float4(g[0], g[1], g[2], g[3]);
+    const float *sv = saved + t * kSavedStride;
+    const float r = sv[0], q = sv[1];
+    // owned columns u: 0 -> r4 (PRE), 1 -> 4 + r4 (POST), 2..5 -> 8 + 4 r4 + (u - 2) (RES)
+    float z[6], dzh[6];
+    z[0] = sv[2 + r4];
+    z[1] = sv[6 + r4];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) dzh[8 + e] = dl[e];
+    for (int b = 0; b < 4; ++b) z[2 + b] = sv[10 + 4 * r4 + b];
+    const float hp = Hpre[t * 4 + r4];
+    const float dhp = dHpre[t * 4 + r4];
+    if (dHpre_out) dHpre_out[t * 4 + r4] = dhp;
+    dzh[0] = dhp * (hp * (1.f - hp));
+    const float hq = Hpost[t * 4 + r4];
+    dzh[1] = dHpost[t * 4 + r4] * (hq * (1.f - 0.5f * hq));
+#pragma unroll
+    for (int b = 0; b < 4; ++b) dzh[2 + b] = g[b];
     float a3[3] = {1.f, 1.f, 1.f};
     if (alpha) { a3[0] = alpha[0]; a3[1] = alpha[1]; a3[2] = alpha[2]; }
-    float S = 0.f;
-    float dp[kJ];
+    float Sp = 0.f, dp[6];
+#pragma unroll
+    for (int u = 0; u < 6; ++u) {
+      const int seg = u == 0 ? 0 : (u == 1 ? 1 : 2);
+      contrib[kJ + seg] += dzh[u] * z[u];
+      const float dz = a3[seg] * dzh[u];
+      Sp += dz * z[u];
+      dp[u] = r * dz;
+    }
+    // dhbias contributions of the owned columns (compile-time slots, lane-selected)
 #pragma unroll
     for (int j = 0; j < kJ; ++j) {
-      const int seg = j < 4 ? 0 : (j < 8 ? 1 : 2);
-      contrib[j] = dzh[j];
-      contrib[kJ + seg] += dzh[j] * z[j];
-      const float dz = a3[seg] * dzh[j];
-      S += dz * z[j];
-      dp[j] = r * dz;
+      const int owner = j < 4 ? j : (j < 8 ? j - 4 : (j - 8) >> 2);
+      const int u = j < 4 ? 0 : (j < 8 ? 1 : 2 + ((j - 8) & 3));
+      contrib[j] = r4 == owner ? dzh[u] : 0.f;
     }
+    const float S = quad_sum(Sp);
     const float crms = q > 0.f ? -S * r / ((float)K * q) : 0.f;
     if (MFMA_OUT) {
-      uint32_t w[3][kJ / 2];  // [term][j pair]
+      // terms [3][24] bf16 at byte 48 * term + 2 * j, then c_rms at byte 144
+      uint16_t hb[3][6];
 #pragma unroll
-      for (int j = 0; j < kJ; j += 2) {
-        float h2[2], m2[2], l2[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          h2[e] = bf16_round(dp[j + e]);
-          const float r1 = dp[j + e] - h2[e];
-          m2[e] = bf16_round(r1);
-          l2[e] = r1 - m2[e];
-        }
-        w[0][j / 2] = pack_bf16x2(h2[0], h2[1]);
-        w[1][j / 2] = pack_bf16x2(m2[0], m2[1]);
-        w[2][j / 2] = pack_bf16x2(l2[0], l2[1]);
+      for (int u = 0; u < 6; ++u) {
+        const float h = bf16_round(dp[u]);
+        const float r1 = dp[u] - h;
+        const float m = bf16_round(r1);
+        hb[0][u] = bf16_bits(h);
+        hb[1][u] = bf16_bits(m);
+        hb[2][u] = bf16_bits(r1 - m);
       }
-      uint4 *rec = reinterpret_cast<uint4 *>(dpA + t * kDpaBytes);
 #pragma unroll
-      for (int tm = 0; tm < 3; ++tm)
-#pragma unroll
-        for (int m = 0; m < 3; ++m)
-          rec[tm * 3 + m] = make_uint4(w[tm][4 * m], w[tm][4 * m + 1], w[tm][4 * m + 2], w[tm][4 * m + 3]);
-      rec[9] = make_uint4(__float_as_uint(crms), 0u, 0u, 0u);
+      for (int tm = 0; tm < 3; ++tm) {
+        uint16_t *row = reinterpret_cast<uint16_t *>(st + 48 * tm);
+        row[r4] = hb[tm][0];
+        row[4 + r4] = hb[tm][1];
+        *reinterpret_cast<uint2 *>(row + 8 + 4 * r4) =
+            make_uint2((uint32_t)hb[tm][2] | ((uint32_t)hb[tm][3] << 16), (uint32_t)hb[tm][4] | ((uint32_t)hb[tm][5] << 16));
+      }
+      if (r4 == 0) *reinterpret_cast<uint4 *>(st + 144) = make_uint4(__float_as_uint(crms), 0u, 0u, 0u);
     } else {
-      float rowf[kDpf];
-#pragma unroll
-      for (int j = 0; j < kJ; ++j) rowf[j] = dp[j];
-      rowf[kJ] = crms;
-#pragma unroll
-      for (int j = kJ + 1; j < kDpf; ++j) rowf[j] = 0.f;
-#pragma unroll
-      for (int qd = 0; qd < kDpf / 4; ++qd)
-        reinterpret_cast<float4 *>(dpf + t * kDpf)[qd] =
-            make_float4(rowf[4 * qd], rowf[4 * qd + 1], rowf[4 * qd + 2], rowf[4 * qd + 3]);
+      float *row = reinterpret_cast<float *>(st);
+      row[r4] = dp[0];
+      row[4 + r4] = dp[1];
+      *reinterpret_cast<float4 *>(row + 8 + 4 * r4) = make_float4(dp[2], dp[3], dp[4], dp[5]);
+      if (r4 == 0) {
+        *reinterpret_cast<float4 *>(row + 24) = make_float4(crms, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4 *>(row + 28) = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
-  } else if (MFMA_OUT && t < npad) {
-    uint4 *rec = reinterpret_cast<uint4 *>(dpA + t * kDpaBytes);
-#pragma unroll
-    for (int i = 0; i < kDpaBytes / 16; ++i) rec[i] = make_uint4(0u, 0u, 0u, 0u);
+  } else if (MFMA_OUT && t < npad) {  // padding token: a zero record
+    reinterpret_cast<uint4 *>(st)[r4] = make_uint4(0u, 0u, 0u, 0u);
+    reinterpret_cast<uint4 *>(st)[4 + r4] = make_uint4(0u, 0u, 0u, 0u);
+    if (r4 < 2) reinterpret_cast<uint4 *>(st)[8 + r4] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __syncthreads();
+  // staged records -> global, whole 16-byte pieces
+  const int64_t nt = min<int64_t>(kTokTB, (MFMA_OUT ? npad : N) - t0);
+  if (nt > 0) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(stage);
+    uint4 *dst = reinterpret_cast<uint4 *>(MFMA_OUT ? dpA + t0 * kDpaBytes : reinterpret_cast<char *>(dpf + t0 * kDpf));
+    for (int i = threadIdx.x; i < nt * (kRec / 16); i += 256) dst[i] = src[i];
   }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
@@ -652,20 +688,25 @@ __global__ __launch_bounds__(256) void proj_bwd_token_kernel(
         (red[0][threadIdx.x] + red[1][threadIdx.x]) + (red[2][threadIdx.x] + red[3][threadIdx.x]);
 }
 
-// dhbias / dalpha: 8 lanes per value stride the per-block partials, then the 8
-// partial sums are added in a fixed tree (deterministic).
-__global__ __launch_bounds__(256) void param_final_kernel(const float *__restrict__ ppart, int64_t nblk,
-                                                          float *__restrict__ dalpha,
-                                                          float *__restrict__ dhbias) {
-  __shared__ float red[8][32];
+// dhbias / dalpha: 32 lanes per value stride the per-block partials (four
+// loads in flight each), then the 32 partial sums are added in a fixed
+// pairwise tree (deterministic).
+__global__ __launch_bounds__(1024) void param_final_kernel(const float *__restrict__ ppart, int64_t nblk,
+                                                           float *__restrict__ dalpha,
+                                                           float *__restrict__ dhbias) {
+  __shared__ float red[32][32];
   const int e = threadIdx.x & 31, part = threadIdx.x >> 5;
   float s = 0.f;
-  for (int64_t b = part; b < nblk; b += 8) s += ppart[b * 32 + e];
+#pragma unroll 4
+  for (int64_t b = part; b < nblk; b += 32) s += ppart[b * 32 + e];
   red[part][e] = s;
   __syncthreads();
+  for (int w = 16; w > 0; w >>= 1) {
+    if (part < w) red[part][e] += red[part + w][e];
+    __syncthreads();
+  }
   if (threadIdx.x >= 27) return;
-  const float tot = ((red[0][e] + red[1][e]) + (red[2][e] + red[3][e])) +
-                    ((red[4][e] + red[5][e]) + (red[6][e] + red[7][e]));
+  const float tot = red[0][e];
   if (e < kJ) {
     if (dhbias) dhbias[e] = tot;
   } else if (dalpha) {
@@ -1270,7 +1311,7 @@ void launch_proj_bwd(hipStream_t s, const ProjBwdArgs &a) {
     hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((K * kJ / 4 + 255) / 256)), dim3(256), 0, s, L.dwpart,
                        a.dW, L.ntb, K * kJ);
   if (a.dalpha || a.dhbias)
-    hipLaunchKernelGGL(param_final_kernel, dim3(1), dim3(256), 0, s, L.ppart, L.nblk, a.dalpha, a.dhbias);
+    hipLaunchKernelGGL(param_final_kernel, dim3(1), dim3(1024), 0, s, L.ppart, L.nblk, a.dalpha, a.dhbias);
 }
 
 }  // namespace mhc

@@ -116,6 +116,106 @@ __device__ __forceinline__ void sk_backward(const float L[16], float G[16], int 
   for (int e = 0; e < 16; ++e) G[e] *= E[e];
 }
 
+// ---------------------------------------------------------------- quad layout
+// Four lanes per matrix (lanes 4k..4k+3 of a wave): lane r = threadIdx.x & 3
+// holds row r in m[4].  Row sums stay in the lane; a column sum adds the
+// four lanes' entries with two quad permutes, (r0 + r1) + (r2 + r3) on every
+// lane, the same association as the one-lane code above, so the forward is
+// bit-identical to it.  Used where one layer's tokens give too few waves for
+// one matrix per lane to fill the chip.
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp<DPP_QUAD_1032>(v);
+  v += dpp<DPP_QUAD_2301>(v);
+  return v;
+}
+
+// value of lane b of the quad, on every lane of it
+template <int B>
+__device__ __forceinline__ float quad_bcast(float v) {
+  return dpp<B * 0x55>(v);
+}
+
+__device__ __forceinline__ void sk_exp4(const float l[4], float m[4]) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) m[b] = expf(l[b]);
+}
+
+__device__ __forceinline__ void sk_row_pass_q(float m[4], float eps, float &d) {
+  d = ((m[0] + m[1]) + (m[2] + m[3])) + eps;
+  const float inv = fast_rcp(d);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) m[b] *= inv;
+}
+
+// dcol: this lane's own column's denominator (column r)
+__device__ __forceinline__ void sk_col_pass_q(float m[4], float eps, int r, float &dcol) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const float d = quad_sum(m[b]) + eps;
+    dcol = r == b ? d : dcol;
+    m[b] *= fast_rcp(d);
+  }
+}
+
+// In place: logits row -> H_res row.
+__device__ __forceinline__ void sk_forward_q(float m[4], int iters, float eps, int r) {
+  float d, dc = 0.f;
+  for (int it = 0; it < iters; ++it) {
+    sk_row_pass_q(m, eps, d);
+    sk_col_pass_q(m, eps, r, dc);
+  }
+}
+
+// g: in = dH_res row r, out = dL row r.  l: logits row r.  Same replay as
+// sk_backward; each lane keeps its row's and its own column's denominators
+// and takes the other columns' from their lanes.
+__device__ __forceinline__ void sk_backward_q(const float l[4], float g[4], int iters, float eps, int r) {
+  const int nseg = (iters + SK_SEG - 1) / SK_SEG;
+  for (int s = nseg - 1; s >= 0; --s) {
+    float m[4];
+    float drow[SK_SEG], dcol[SK_SEG];
+#pragma unroll
+    for (int j = 0; j < SK_SEG; ++j) dcol[j] = 0.f;
+    sk_exp4(l, m);
+    for (int it = 0; it < s * SK_SEG; ++it) {
+      sk_row_pass_q(m, eps, drow[0]);
+      sk_col_pass_q(m, eps, r, dcol[0]);
+    }
+    const int cnt = min(iters - s * SK_SEG, SK_SEG);
+#pragma unroll
+    for (int j = 0; j < SK_SEG; ++j) {
+      if (j < cnt) {
+        sk_row_pass_q(m, eps, drow[j]);
+        sk_col_pass_q(m, eps, r, dcol[j]);
+      }
+    }
+#pragma unroll
+    for (int j = SK_SEG - 1; j >= 0; --j) {
+      if (j < cnt) {
+        const float dc[4] = {quad_bcast<0>(dcol[j]), quad_bcast<1>(dcol[j]), quad_bcast<2>(dcol[j]),
+                             quad_bcast<3>(dcol[j])};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const float dot = quad_sum(g[b] * m[b]);
+          g[b] = (g[b] - dot) * fast_rcp(dc[b]);
+          m[b] *= dc[b];
+        }
+        const float dot = (g[0] * m[0] + g[1] * m[1]) + (g[2] * m[2] + g[3] * m[3]);
+        const float inv = fast_rcp(drow[j]);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          g[b] = (g[b] - dot) * inv;
+          m[b] *= drow[j];
+        }
+      }
+    }
+  }
+  float e[4];
+  sk_exp4(l, e);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) g[b] *= e[b];
+}
+
 __device__ __forceinline__ void load16(const float *p, float v[16]) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
