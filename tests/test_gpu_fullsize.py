@@ -178,3 +178,44 @@ def test_pre_bwd_full_size(name, mode):
     assert_tokensum("dW", ob["dW"], rb["dW"], aW)
     assert_tokensum("dalpha", ob["dalpha"], rb["dalpha"], aa)
     assert_tokensum("dhbias", ob["dhbias"], rb["dhbias"], ab)
+
+
+# ----------------------------------------------------------------- stream mix / distribute, shared-row aggregate
+def test_variants_full_size():
+    w = synth.WORKLOADS["full_layer"]
+    N, C, n = w.tokens, w.C, w.n
+    log(f"variants full size: N={N} C={C}")
+    X = residual("full_layer")
+    S = sample_tokens(N, w.wid + 7)
+    Z = others(N, S, w.wid + 7)
+    rng = np.random.default_rng(w.wid + 70)
+    G = only(synth.tensor(w, "G"), S)
+    x = synth.tensor(w, "x")
+    M = rng.standard_normal((N, n, n)).astype(np.float32)
+    Hp = rng.standard_normal((N, n)).astype(np.float32)
+    h = np.array([0.4, -0.3, 0.2, 0.7], np.float32)
+    Xd, Gd, xd = dev(X), dev(G), dev(x)
+    out_m = B.mhc_stream_mix_fwd(Xd, dev(M))
+    dX_m, dM_m = B.mhc_stream_mix_bwd(Gd, Xd, dev(M))
+    out_d = B.mhc_stream_distribute_fwd(xd, dev(Hp))
+    dx_d, dH_d = B.mhc_stream_distribute_bwd(Gd, xd, dev(Hp))
+    agg_s = B.mhc_h_aggregate_static_fwd(Xd, dev(h))
+    g = only(x, S)  # upstream gradient on the sampled tokens only
+    dX_s, dH_s = B.mhc_h_aggregate_static_bwd(dev(g), Xd, dev(h))
+    torch.cuda.synchronize()
+    XS, GS, xS = h64(X[S]), h64(G[S]), h64(x[S])
+    assert_act("mix out", rows(out_m, S), O.stream_mix_fwd(XS, h64(M[S])), w.act)
+    odX, odM = O.stream_mix_bwd(GS, XS, h64(M[S]))
+    assert_act("mix dX", rows(dX_m, S), odX, w.act)
+    assert_mixed("mix dM", rows(dM_m, S), odM)
+    assert_act("dist out", rows(out_d, S), O.stream_distribute_fwd(xS, h64(Hp[S])), w.act)
+    odx, odH = O.stream_distribute_bwd(GS, xS, h64(Hp[S]))
+    assert_act("dist dx", rows(dx_d, S), odx, w.act)
+    assert_mixed("dist dH_post", rows(dH_d, S), odH)
+    for nm, t in (("mix dX", dX_m), ("mix dM", dM_m), ("dist dx", dx_d), ("dist dH_post", dH_d)):
+        assert not h64(rows(t, Z)).any(), f"{nm}: nonzero on tokens with zero upstream gradient"
+    assert_act("static agg", rows(agg_s, S), O.h_aggregate_static_fwd(XS, h64(h)), w.act)
+    sdX, sdH = O.h_aggregate_static_bwd(h64(g[S]), XS, h64(h))
+    assert_act("static dX", rows(dX_s, S), sdX, w.act)
+    parts = np.abs(O.h_aggregate_bwd(h64(g[S]), XS, np.broadcast_to(h64(h), (len(S), n)).copy())[1]).sum(axis=0)
+    assert_tokensum("static dH_pre", dH_s, sdH, parts)
