@@ -743,7 +743,7 @@ __global__ __launch_bounds__(1024) void param_final_kernel(const float *__restri
 // the four dX waves, which each need all four streams of G.
 constexpr int kB2Stages = 3;
 constexpr int kB2Quarter = 32 * 128;  // bytes of one 32 x 64 bf16 tile
-constexpr int kB2AccRow = 36;         // floats per row of a wave's 32 x 32 accumulator half
+constexpr int kB2AccRow = 68;         // floats per row of a wave's 32 x 64 accumulator tile
 
 template <bool HAS_G, bool POST>
 struct B2Lay {
@@ -754,6 +754,7 @@ struct B2Lay {
   static constexpr int stage = P + 32 * kDpaBytes;
   static constexpr int acc = kB2Stages * stage;
   static constexpr int total = acc + 4 * 32 * kB2AccRow * 4;
+  static_assert(total <= 160 * 1024, "LDS of one workgroup");
 };
 
 // dp W^T runs on bf16 MFMA with dp and W both split exactly into three bf16
@@ -795,12 +796,12 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Per-lane inputs of one sub-tile's dX epilogue, for rows er + 16q of the
-// accumulator half ct: dX_in, H_pre and the lane's H_res row.
+// Per-lane inputs of one sub-tile's dX epilogue, for rows er + 8q: dX_in,
+// H_pre and the row's H_res row.
 struct DxPre {
-  u32x4 d[2][2];
-  float hp[2][2];
-  float4 hr[2];
+  u32x4 d[4];
+  float hp[4];
+  float4 hr[4];
 };
 
 template <bool ACCUM, bool HAS_G, bool DW, bool POST>
@@ -884,31 +885,22 @@ __global__ __launch_bounds__(512) void proj_bwd_mfma_kernel(
     if (kq == 0) dma16(rs + 4096 + lane * 16, st + L::P + 4096);
   };
 
-  // ---- dX geometry: in accumulator half ct (k = 32 ct .. +32 of the
-  // quarter), lane -> token rows er + 16q (q = 0, 1) and 8 k at 32 ct + ek
-  const int er = lane >> 2;
-  const int ek = (lane & 3) * 8;
-  bool ekv[2];
-  int64_t kx[2];
-  int si_x[2];
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    ekv[ct] = 32 * ct + ek < nvalid;
-    kx[ct] = kbase + 32 * ct + ek;
-    si_x[ct] = SPW ? kq : (int)(min<int64_t>(kx[ct], K - 1) / C);
-  }
+  // ---- dX geometry: lane -> token rows er + 8q (q = 0..3) and 8 k at ek of
+  // the quarter's 64, so eight lanes store one row's whole 128-byte line
+  const int er = lane >> 3;
+  const int ek = (lane & 7) * 8;
+  const bool ekv = ek < nvalid;
+  const int64_t kx = kbase + ek;
+  const int si_x = SPW ? kq : (int)(min<int64_t>(kx, K - 1) / C);
 
   auto prefetch = [&](DxPre &P, int i) {
     const int64_t t0 = t_begin + 32 * (int64_t)i;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int64_t tt = t0 + er + 16 * q;
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const bool v = tt < N && ekv[ct];
-        if (ACCUM) P.d[ct][q] = v ? *reinterpret_cast<const u32x4 *>(dX + tt * K + kx[ct]) : u32x4{0u, 0u, 0u, 0u};
-        if (HAS_G) P.hp[ct][q] = v ? Hpre[tt * 4 + si_x[ct]] : 0.f;
-      }
+    for (int q = 0; q < 4; ++q) {
+      const int64_t tt = t0 + er + 8 * q;
+      const bool v = tt < N && ekv;
+      if (ACCUM) P.d[q] = v ? *reinterpret_cast<const u32x4 *>(dX + tt * K + kx) : u32x4{0u, 0u, 0u, 0u};
+      if (HAS_G) P.hp[q] = v ? Hpre[tt * 4 + si_x] : 0.f;
       if (POST)
         P.hr[q] = tt < N ? *reinterpret_cast<const float4 *>(Hres + tt * 16 + kq * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
@@ -1048,83 +1040,84 @@ __global__ __launch_bounds__(512) void proj_bwd_mfma_kernel(
           accX[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[c]),
                                                             __builtin_bit_cast(bf16x8, wb[ct][c]), accX[ct], 0, 0, 0);
       }
-      // (b) dX = dp W^T + c_rms x + H_pre g + sum_i H_res[j][i] G[i] + dX_in,
-      // one 32 x 32 half at a time: transpose through the wave's LDS area,
-      // then 16-byte row-major stores.  The prefetched inputs are waited for
-      // here, once: a wait left to their first use inside the (branchy) row
-      // loop would also wait for the previous rows' stores.  The scheduling
-      // fence keeps the MFMAs above the wait, so they cover its latency.
+      // (b) dX = dp W^T + c_rms x + H_pre g + sum_i H_res[j][i] G[i] + dX_in:
+      // the 32 x 64 accumulators are transposed through the wave's LDS area,
+      // then each row is stored as one 128-byte line by eight lanes.  The
+      // prefetched inputs are waited for here, once: a wait left to their
+      // first use inside the (branchy) row loop would also wait for the
+      // previous rows' stores.  The scheduling fence keeps the MFMAs above
+      // the wait, so they cover its latency.
       __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<0>();
       const char *xs = st + L::X + kq * kB2Quarter;
       const char *gs = st + L::G + (SPW ? 0 : kq * kB2Quarter);
       const char *qs = st + L::Q;
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
+      for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc_t[(8 * (r >> 2) + 4 * h + (r & 3)) * kB2AccRow + col] = accX[ct][r];
-        wave_lds_sync();
+        for (int r = 0; r < 16; ++r)
+          acc_t[(8 * (r >> 2) + 4 * h + (r & 3)) * kB2AccRow + 32 * ct + col] = accX[ct][r];
+      wave_lds_sync();
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int row = er + 16 * q;
-          const int64_t tt = t0 + row;
-          if (!(tt < N && ekv[ct])) continue;
-          const int slot = ((32 * ct + ek) >> 3) ^ (row & 7);
-          const float4 a0 = *reinterpret_cast<const float4 *>(&acc_t[row * kB2AccRow + ek]);
-          const float4 a1 = *reinterpret_cast<const float4 *>(&acc_t[row * kB2AccRow + ek + 4]);
-          const float acc8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-          const float crms = *reinterpret_cast<const float *>(ps + row * kDpaBytes + 9 * 16);
-          const u32x4 xv = *reinterpret_cast<const u32x4 *>(xs + row * 128 + 16 * slot);
-          const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-          float o[8];
+      for (int q = 0; q < 4; ++q) {
+        const int row = er + 8 * q;
+        const int64_t tt = t0 + row;
+        if (!(tt < N && ekv)) continue;
+        const int slot = (ek >> 3) ^ (row & 7);
+        const float4 a0 = *reinterpret_cast<const float4 *>(&acc_t[row * kB2AccRow + ek]);
+        const float4 a1 = *reinterpret_cast<const float4 *>(&acc_t[row * kB2AccRow + ek + 4]);
+        const float acc8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const float crms = *reinterpret_cast<const float *>(ps + row * kDpaBytes + 9 * 16);
+        const u32x4 xv = *reinterpret_cast<const u32x4 *>(xs + row * 128 + 16 * slot);
+        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+        float o[8];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          o[2 * p] = acc8[2 * p] + crms * bf16_lo(xw[p]);
+          o[2 * p + 1] = acc8[2 * p + 1] + crms * bf16_hi(xw[p]);
+        }
+        if (HAS_G) {
+          const u32x4 gv = *reinterpret_cast<const u32x4 *>(gs + row * 128 + 16 * slot);
+          const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+          const float hp = cur.hp[q];
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
-            o[2 * p] = acc8[2 * p] + crms * bf16_lo(xw[p]);
-            o[2 * p + 1] = acc8[2 * p + 1] + crms * bf16_hi(xw[p]);
+            o[2 * p] += hp * bf16_lo(gw[p]);
+            o[2 * p + 1] += hp * bf16_hi(gw[p]);
           }
-          if (HAS_G) {
-            const u32x4 gv = *reinterpret_cast<const u32x4 *>(gs + row * 128 + 16 * slot);
-            const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-            const float hp = cur.hp[ct][q];
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-              o[2 * p] += hp * bf16_lo(gw[p]);
-              o[2 * p + 1] += hp * bf16_hi(gw[p]);
-            }
-          }
-          if (POST) {  // h_post_bda term: sum_i H_res[j][i] G[i], j = this wave's stream
-            const float4 hr = cur.hr[q];
-            uint32_t gw[4][4];
-#pragma unroll
-            for (int si = 0; si < 4; ++si) {
-              const u32x4 v = *reinterpret_cast<const u32x4 *>(qs + si * kB2Quarter + row * 128 + 16 * slot);
-              gw[si][0] = v.x; gw[si][1] = v.y; gw[si][2] = v.z; gw[si][3] = v.w;
-            }
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-              o[2 * p] += (hr.x * bf16_lo(gw[0][p]) + hr.y * bf16_lo(gw[1][p])) +
-                          (hr.z * bf16_lo(gw[2][p]) + hr.w * bf16_lo(gw[3][p]));
-              o[2 * p + 1] += (hr.x * bf16_hi(gw[0][p]) + hr.y * bf16_hi(gw[1][p])) +
-                              (hr.z * bf16_hi(gw[2][p]) + hr.w * bf16_hi(gw[3][p]));
-            }
-          }
-          if (ACCUM) {
-            const uint32_t dw4[4] = {cur.d[ct][q].x, cur.d[ct][q].y, cur.d[ct][q].z, cur.d[ct][q].w};
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-              o[2 * p] += bf16_lo(dw4[p]);
-              o[2 * p + 1] += bf16_hi(dw4[p]);
-            }
-          }
-          uint4 ow;
-          ow.x = pack_bf16x2(o[0], o[1]);
-          ow.y = pack_bf16x2(o[2], o[3]);
-          ow.z = pack_bf16x2(o[4], o[5]);
-          ow.w = pack_bf16x2(o[6], o[7]);
-          *reinterpret_cast<uint4 *>(dX + tt * K + kx[ct]) = ow;
         }
-        wave_lds_sync();  // this half's reads of the accumulator area precede the next writes
+        if (POST) {  // h_post_bda term: sum_i H_res[j][i] G[i], j = this wave's stream
+          const float4 hr = cur.hr[q];
+          uint32_t gw[4][4];
+#pragma unroll
+          for (int si = 0; si < 4; ++si) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(qs + si * kB2Quarter + row * 128 + 16 * slot);
+            gw[si][0] = v.x; gw[si][1] = v.y; gw[si][2] = v.z; gw[si][3] = v.w;
+          }
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            o[2 * p] += (hr.x * bf16_lo(gw[0][p]) + hr.y * bf16_lo(gw[1][p])) +
+                        (hr.z * bf16_lo(gw[2][p]) + hr.w * bf16_lo(gw[3][p]));
+            o[2 * p + 1] += (hr.x * bf16_hi(gw[0][p]) + hr.y * bf16_hi(gw[1][p])) +
+                            (hr.z * bf16_hi(gw[2][p]) + hr.w * bf16_hi(gw[3][p]));
+          }
+        }
+        if (ACCUM) {
+          const uint32_t dw4[4] = {cur.d[q].x, cur.d[q].y, cur.d[q].z, cur.d[q].w};
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            o[2 * p] += bf16_lo(dw4[p]);
+            o[2 * p + 1] += bf16_hi(dw4[p]);
+          }
+        }
+        uint4 ow;
+        ow.x = pack_bf16x2(o[0], o[1]);
+        ow.y = pack_bf16x2(o[2], o[3]);
+        ow.z = pack_bf16x2(o[4], o[5]);
+        ow.w = pack_bf16x2(o[6], o[7]);
+        *reinterpret_cast<uint4 *>(dX + tt * K + kx) = ow;
       }
+      wave_lds_sync();  // the reads of the accumulator area precede the next sub-tile's writes
       // the next sub-tile's dX_in, H_pre and H_res, in flight across the
       // barrier and the next sub-tile's MFMAs
       if (i + 1 < nsub) prefetch(cur, i + 1);
