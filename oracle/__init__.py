@@ -72,12 +72,15 @@ def _lib():
         lib.mhc_oracle_stream_distribute_bwd.argtypes = [_i64, _i32, _i64, _dp, _dp, _dp, _dp, _dp]
         lib.mhc_oracle_h_aggregate_static_fwd.argtypes = [_i64, _i32, _i64, _dp, _dp, _dp]
         lib.mhc_oracle_h_aggregate_static_bwd.argtypes = [_i64, _i32, _i64, _dp, _dp, _dp, _dp, _dp]
+        lib.mhc_oracle_rmsnorm_fwd.argtypes = [_i64, _i64, _dp, _dp, ctypes.c_double, _dp, _dp]
+        lib.mhc_oracle_rmsnorm_bwd.argtypes = [_i64, _i64, _dp, _dp, _dp, ctypes.c_double, _dp, _dp]
         for f in ("mhc_oracle_proj_rms_h", "mhc_oracle_sinkhorn_fwd", "mhc_oracle_sinkhorn_bwd",
                   "mhc_oracle_h_aggregate_fwd", "mhc_oracle_h_aggregate_bwd",
                   "mhc_oracle_h_post_bda_fwd", "mhc_oracle_h_post_bda_bwd",
                   "mhc_oracle_proj_rms_h_bwd", "mhc_oracle_stream_mix_fwd", "mhc_oracle_stream_mix_bwd",
                   "mhc_oracle_stream_distribute_fwd", "mhc_oracle_stream_distribute_bwd",
-                  "mhc_oracle_h_aggregate_static_fwd", "mhc_oracle_h_aggregate_static_bwd"):
+                  "mhc_oracle_h_aggregate_static_fwd", "mhc_oracle_h_aggregate_static_bwd",
+                  "mhc_oracle_rmsnorm_fwd", "mhc_oracle_rmsnorm_bwd"):
             getattr(lib, f).restype = None
         _lib_handle = lib
     return _lib_handle
@@ -282,6 +285,28 @@ def h_aggregate_static_bwd(g, X, H_pre):
     dX = np.empty((N, n, C)); dH = np.empty(n)
     _lib().mhc_oracle_h_aggregate_static_bwd(N, n, C, _p(g), _p(X), _p(H_pre), _p(dX), _p(dH))
     return dX, dH
+
+
+def rmsnorm_fwd(x, gamma=None, eps=1e-6):
+    """F7: y[t,c] = gamma[c] x[t,c] / (sqrt(mean_c x[t,c]^2) + eps) (rwkv-ops RMSNorm FFI; gain
+    per RL-Kernel's rmsnorm_residual).  gamma None = weightless.  Returns (y [N,C], r [N])."""
+    x = _f64(x)
+    N, C = x.shape
+    g = _f64(gamma) if gamma is not None else None
+    y = np.empty((N, C)); r = np.empty(N)
+    _lib().mhc_oracle_rmsnorm_fwd(N, C, _p(x), _p(g) if g is not None else None, float(eps), _p(y), _p(r))
+    return y, r
+
+
+def rmsnorm_bwd(dy, x, gamma=None, eps=1e-6):
+    """B7: returns (dx [N,C], dgamma [C] summed over tokens, or None when gamma is None)."""
+    x = _f64(x); dy = _f64(dy)
+    N, C = x.shape
+    g = _f64(gamma) if gamma is not None else None
+    dx = np.empty((N, C)); dg = np.empty(C) if g is not None else None
+    _lib().mhc_oracle_rmsnorm_bwd(N, C, _p(dy), _p(x), _p(g) if g is not None else None, float(eps),
+                                  _p(dx), _p(dg) if dg is not None else None)
+    return dx, dg
 
 
 def proj_rms_h_bwd(X, W, dH_pre, dH_post, dL, alpha=None, hbias=None, eps_rms=1e-6):

@@ -454,3 +454,54 @@ void mhc_oracle_proj_rms_h_bwd(int64_t N, int n, int64_t C, const double *X,
   free(p);
   free(dp);
 }
+
+/* ------------------------------------------------------------------------
+ * F7  RMSNorm of one activation row  [RWKV: the RMSNorm forward/backward FFI
+ * handlers (inp [N,C] -> out [N,C], attribute eps; no weight); RLK: P1-5
+ * rmsnorm_residual with a norm gain whose gradient dgamma is summed across
+ * ranks; RLK review comment: r = 1/(q+eps) removes the zero-row singularity]
+ *
+ *   q = sqrt(sum_c x_c^2 / C),  r = 1/(q + eps),  y_c = gamma_c r x_c
+ *   gamma == NULL means gamma_c = 1 (the weightless form).
+ * B7  its backward
+ *   S = sum_c gamma_c dy_c x_c
+ *   dx_k = r gamma_k dy_k - S r^2 x_k / (C q)        (second term 0 when q == 0)
+ *   dgamma_c = sum_t dy_{t,c} r_t x_{t,c}            (when dgamma != NULL)
+ * r_out (may be NULL) receives r per row.
+ * ---------------------------------------------------------------------- */
+void mhc_oracle_rmsnorm_fwd(int64_t N, int64_t C, const double *x,
+                            const double *gamma, double eps, double *y,
+                            double *r_out) {
+  for (int64_t t = 0; t < N; ++t) {
+    const double *xt = x + t * C;
+    double s = 0.0;
+    for (int64_t c = 0; c < C; ++c) s += xt[c] * xt[c];
+    const double q = sqrt(s / (double)C);
+    const double r = 1.0 / (q + eps);
+    for (int64_t c = 0; c < C; ++c)
+      y[t * C + c] = (gamma ? gamma[c] : 1.0) * r * xt[c];
+    if (r_out) r_out[t] = r;
+  }
+}
+
+void mhc_oracle_rmsnorm_bwd(int64_t N, int64_t C, const double *dy,
+                            const double *x, const double *gamma, double eps,
+                            double *dx, double *dgamma) {
+  if (dgamma)
+    for (int64_t c = 0; c < C; ++c) dgamma[c] = 0.0;
+  for (int64_t t = 0; t < N; ++t) {
+    const double *xt = x + t * C;
+    const double *gt = dy + t * C;
+    double s = 0.0;
+    for (int64_t c = 0; c < C; ++c) s += xt[c] * xt[c];
+    const double q = sqrt(s / (double)C);
+    const double r = 1.0 / (q + eps);
+    double S = 0.0;
+    for (int64_t c = 0; c < C; ++c) S += (gamma ? gamma[c] : 1.0) * gt[c] * xt[c];
+    const double coef = (q > 0.0) ? (-S * r * r / ((double)C * q)) : 0.0;
+    for (int64_t c = 0; c < C; ++c) {
+      dx[t * C + c] = r * (gamma ? gamma[c] : 1.0) * gt[c] + coef * xt[c];
+      if (dgamma) dgamma[c] += gt[c] * r * xt[c];
+    }
+  }
+}

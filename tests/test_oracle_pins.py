@@ -489,3 +489,72 @@ def test_tiny_chain_workload_brute_force_consistency():
     H = f["H_res"]
     # row sums of the returned matrix: close to 1 at the tiny chain's logit spread
     assert np.abs(H.sum(2) - 1).max() < 1e-5 and np.abs(H.sum(1) - 1).max() < 1e-5
+
+
+# ---------------------------------------------------------------- F7/B7 RMSNorm of the aggregated stream
+def test_rmsnorm_matches_library_norm():
+    x = rnd(7, 40, std=3.0); gam = RNG.uniform(0.5, 1.5, 40)
+    for eps in (1e-6, 0.5):
+        y, r = O.rmsnorm_fwd(x, gam, eps)
+        q = np.linalg.norm(x, axis=1) / np.sqrt(40)
+        np.testing.assert_allclose(r, 1 / (q + eps), rtol=1e-14)
+        np.testing.assert_allclose(y, gam * x / (q + eps)[:, None], rtol=1e-14)
+    y0, _ = O.rmsnorm_fwd(x, None, 1e-6)
+    y1, _ = O.rmsnorm_fwd(x, np.ones(40), 1e-6)
+    np.testing.assert_array_equal(y0, y1)  # no gain = unit gain
+
+
+@pytest.mark.parametrize("c", [1.0, -2.5, 1e-3])
+def test_rmsnorm_of_constant_row_is_pm_one_and_zero_row_finite(c):
+    x = np.full((2, 24), c); x[1] = 0.0
+    y, r = O.rmsnorm_fwd(x, None, 1e-6)
+    np.testing.assert_allclose(y[0], np.sign(c) * abs(c) / (abs(c) + 1e-6), rtol=1e-15)
+    assert abs(abs(y[0, 0]) - 1) <= 1e-6 / abs(c)
+    assert np.all(y[1] == 0.0) and r[1] == 1e6
+    dy = rnd(2, 24)
+    dx, _ = O.rmsnorm_bwd(dy, x, None, 1e-6)
+    assert np.isfinite(dx).all()
+    np.testing.assert_allclose(dx[1], 1e6 * dy[1], rtol=1e-15)  # zero row: only the r * dy leg
+
+
+def test_rmsnorm_scale_invariance():
+    x = rnd(4, 64)
+    y, _ = O.rmsnorm_fwd(x, None, 1e-6)
+    for lam in (0.01, 7.0):
+        yl, _ = O.rmsnorm_fwd(lam * x, None, 1e-6)
+        q = np.linalg.norm(x, axis=1) / 8.0
+        # y(lam x) = x / (q + eps / lam) exactly: only eps sees the scale
+        np.testing.assert_allclose(yl, x / (q + 1e-6 / lam)[:, None], rtol=1e-13)
+        assert np.all(np.abs(yl - y) <= np.abs(y) * (1e-6 * abs(1 - 1 / lam) / q)[:, None])
+
+
+def test_rmsnorm_bwd_matches_torch_autograd():
+    N, C = 5, 33
+    x = rnd(N, C); gam = RNG.uniform(0.5, 1.5, C); dy = rnd(N, C)
+    xt = torch.tensor(x, requires_grad=True); gt = torch.tensor(gam, requires_grad=True)
+    eps = 1e-3
+    q = torch.sqrt((xt * xt).mean(1, keepdim=True))
+    (torch.tensor(dy) * (gt * xt / (q + eps))).sum().backward()
+    dx, dg = O.rmsnorm_bwd(dy, x, gam, eps)
+    np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(dg, gt.grad.numpy(), rtol=1e-11, atol=1e-13)
+    dx0, dg0 = O.rmsnorm_bwd(dy, x, None, eps)
+    assert dg0 is None
+    np.testing.assert_array_equal(dx0, O.rmsnorm_bwd(dy, x, np.ones(C), eps)[0])
+
+
+def test_rmsnorm_bwd_finite_difference():
+    N, C = 3, 6
+    x = rnd(N, C); gam = RNG.uniform(0.5, 1.5, C); dy = rnd(N, C); eps = 0.05
+    loss = lambda xv, gv: float((dy * O.rmsnorm_fwd(xv, gv, eps)[0]).sum())
+    dx, dg = O.rmsnorm_bwd(dy, x, gam, eps)
+    fdx = _fd(lambda v: loss(v, gam), x)
+    fdg = _fd(lambda v: loss(x, v), gam)
+    assert np.linalg.norm(dx - fdx) <= 1e-6 * np.linalg.norm(fdx)
+    assert np.linalg.norm(dg - fdg) <= 1e-6 * np.linalg.norm(fdg)
+    # the weightless RMSNorm output is orthogonal to its own input gradient direction:
+    # y(x) is 0-homogeneous up to eps, so <dx, x> = <dy, y> * eps / (q + eps) per row
+    dx0, _ = O.rmsnorm_bwd(dy, x, None, eps)
+    y0, r0 = O.rmsnorm_fwd(x, None, eps)
+    q0 = 1 / r0 - eps
+    np.testing.assert_allclose((dx0 * x).sum(1), (dy * y0).sum(1) * eps / (q0 + eps), rtol=1e-10)
