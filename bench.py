@@ -93,6 +93,14 @@ def measure_variants(lib, L, sp, N, n, C, X, G, H_res, H_post, x, g, out, dX, dM
         "h_aggregate_static_bwd": (18 * C, lambda: lib.mhc_h_aggregate_static_bwd(sp, N, n, C, MHC_BF16, P(g), P(X),
                                                                                    P(h), P(dX), 0, P(dh), P(ws), wsn)),
     }
+    # RMSNorm of the aggregated stream [N][C] (x as its input, g as its upstream gradient), with a gain
+    gam = torch.linspace(0.5, 1.5, C, device=dev)
+    dgam = torch.empty(C, device=dev)
+    wsr = lib.mhc_rmsnorm_bwd_workspace_size(N, C, MHC_BF16, 1)
+    wsn_ = torch.empty(max(wsr, 16), dtype=torch.uint8, device=dev)
+    calls["rmsnorm_fwd"] = (4 * C, lambda: lib.mhc_rmsnorm_fwd(sp, N, C, MHC_BF16, P(x), P(gam), 1e-6, P(dx)))
+    calls["rmsnorm_bwd"] = (6 * C, lambda: lib.mhc_rmsnorm_bwd(sp, N, C, MHC_BF16, P(g), P(x), P(gam), 1e-6, P(dx), 0,
+                                                                P(dgam), P(wsn_), wsr))
     res = {}
     for name, (bytes_per_token, fn) in calls.items():
         L.check(fn())

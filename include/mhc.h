@@ -290,6 +290,48 @@ mhc_status mhc_pre_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_d
                        float *dH_pre_out, float *dlogits_out, void *workspace,
                        size_t workspace_bytes);
 
+/* -------------------------------------------------------------------------
+ * RMSNorm of the aggregated stream, the step right after h_aggregate
+ * (rwkv-ops mhu_ffi.cu, RMSNorm forward/backward FFI: a [N][C] row norm with
+ * one eps; RL-Kernel PR #383, P1-5 rmsnorm_residual, which adds a norm gain
+ * whose gradient dgamma is summed over tokens (and ranks), and removes the
+ * zero-row singularity with r = 1/(q + eps)).  Per token row x [C]:
+ *   q = sqrt(sum_c x_c^2 / C),  r = 1/(q + eps),  y_c = gamma_c r x_c
+ *   dx_k (+)= r gamma_k dy_k - S r^2 x_k / (C q),  S = sum_c gamma_c dy_c x_c
+ *             (the second term is 0 for an all-zero row)
+ *   dgamma_c = sum_t dy_{t,c} r_t x_{t,c}
+ * x, y, dy, dx [tokens][C] (act); gamma, dgamma [C] fp32.  gamma == NULL
+ * means a unit gain (the weightless norm); dgamma == NULL skips it (it may
+ * be requested with gamma == NULL).  The residual fork: the aggregated
+ * stream x is kept as a tensor of its own beside y; its own gradient is
+ * added by passing it in dx with accumulate_dx != 0.  dgamma is a
+ * fixed-order sum over tokens through the workspace
+ * (mhc_rmsnorm_bwd_workspace_size; 0 bytes without dgamma); with
+ * tokens == 0 it is set to zero.  n plays no part: C % 8 == 0 and
+ * C <= 16384 as elsewhere.
+ * ---------------------------------------------------------------------- */
+mhc_status mhc_rmsnorm_fwd(void *stream, int64_t tokens, int64_t C, mhc_dtype act, const void *x,
+                           const float *gamma, float eps, void *y);
+size_t mhc_rmsnorm_bwd_workspace_size(int64_t tokens, int64_t C, mhc_dtype act, int32_t with_dgamma);
+mhc_status mhc_rmsnorm_bwd(void *stream, int64_t tokens, int64_t C, mhc_dtype act, const void *dy,
+                           const void *x, const float *gamma, float eps, void *dx,
+                           int32_t accumulate_dx, float *dgamma, void *workspace,
+                           size_t workspace_bytes);
+
+/* Fused pre pass with the norm as its epilogue: mhc_pre_fwd, and in the
+ * same pass over the residual that writes agg, normed = RMSNorm(agg) as
+ * stored (the values after rounding to act), so the result equals
+ * mhc_pre_fwd followed by mhc_rmsnorm_fwd on its agg.  gamma [C] fp32 or
+ * NULL, norm_eps >= 0, normed [tokens][C] (act).  The backward is
+ * mhc_rmsnorm_bwd (dy -> gradient of agg) followed by mhc_pre_bwd.
+ * ---------------------------------------------------------------------- */
+mhc_status mhc_pre_rmsnorm_fwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                               const void *X, const float *W, const float *alpha, const float *hbias,
+                               float rms_eps, int32_t iters, float eps, const float *gamma,
+                               float norm_eps, float *H_pre, float *H_post, float *H_res,
+                               float *H_res_logits, float *saved, void *agg, void *normed,
+                               void *workspace, size_t workspace_bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -260,6 +260,67 @@ def mhc_pre_fwd(X, W, alpha=None, hbias=None, rms_eps=1e-6, iters=20, eps=1e-6):
     return o
 
 
+def _rows(x: torch.Tensor):
+    if x.dim() < 1:
+        raise ValueError("x must be [..., C]")
+    C = x.shape[-1]
+    return (x.numel() // C if C else 0), C
+
+
+def mhc_rmsnorm_fwd(x, gamma=None, eps=1e-6):
+    """RMSNorm of each row of x [..., C] with optional fp32 gain gamma [C]."""
+    N, C = _rows(x)
+    act = _act(x)
+    _need(x, "x"); _need(gamma, "gamma", f32, C)
+    y = torch.empty_like(x)
+    call("mhc_rmsnorm_fwd", _stream(x), N, C, act, _p(x), _p(gamma), eps, _p(y))
+    return y
+
+
+def mhc_rmsnorm_bwd(dy, x, gamma=None, eps=1e-6, dx=None, accumulate_dx=False, want_dgamma=None):
+    """Returns (dx, dgamma-or-None).  dgamma is produced when gamma is given (or want_dgamma=True).
+
+    dx with accumulate_dx=True adds the norm's input gradient onto dx (the residual fork's own gradient).
+    """
+    N, C = _rows(x)
+    act = _act(x)
+    _need(x, "x"); _need(dy, "dy", x.dtype, x.numel()); _need(gamma, "gamma", f32, C)
+    if dx is None:
+        if accumulate_dx:
+            raise ValueError("accumulate_dx needs dx")
+        dx = torch.empty_like(x)
+    _need(dx, "dx", x.dtype, x.numel())
+    if want_dgamma is None:
+        want_dgamma = gamma is not None
+    dg = torch.empty(C, dtype=f32, device=x.device) if want_dgamma else None
+    ws, wsb = _ws(_lib.lib().mhc_rmsnorm_bwd_workspace_size(N, C, act, int(want_dgamma)), x.device)
+    call("mhc_rmsnorm_bwd", _stream(x), N, C, act, _p(dy), _p(x), _p(gamma), eps, _p(dx), int(accumulate_dx),
+         _p(dg), _p(ws), wsb)
+    return dx, dg
+
+
+def mhc_pre_rmsnorm_fwd(X, W, gamma=None, alpha=None, hbias=None, rms_eps=1e-6, iters=20, eps=1e-6,
+                        norm_eps=1e-6):
+    """Fused pre pass with the norm epilogue.  Returns mhc_pre_fwd's dict plus 'normed' = RMSNorm(agg)."""
+    N, n, C = _dims(X)
+    act = _act(X)
+    _need(X, "X"); _need(W, "W", f32, n * C * J); _need(alpha, "alpha", f32, 3); _need(hbias, "hbias", f32, J)
+    _need(gamma, "gamma", f32, C)
+    lead = X.shape[:-2]
+    d = X.device
+    o = dict(H_pre=torch.empty(*lead, n, dtype=f32, device=d), H_post=torch.empty(*lead, n, dtype=f32, device=d),
+             H_res=torch.empty(*lead, n, n, dtype=f32, device=d),
+             H_res_logits=torch.empty(*lead, n, n, dtype=f32, device=d),
+             saved=torch.empty(*lead, SAVED_STRIDE, dtype=f32, device=d),
+             agg=torch.empty(*lead, C, dtype=X.dtype, device=d),
+             normed=torch.empty(*lead, C, dtype=X.dtype, device=d))
+    ws, wsb = _ws(_lib.lib().mhc_pre_fwd_workspace_size(N, n, C, act), d)
+    call("mhc_pre_rmsnorm_fwd", _stream(X), N, n, C, act, _p(X), _p(W), _p(alpha), _p(hbias), rms_eps, iters,
+         eps, _p(gamma), norm_eps, _p(o["H_pre"]), _p(o["H_post"]), _p(o["H_res"]), _p(o["H_res_logits"]),
+         _p(o["saved"]), _p(o["agg"]), _p(o["normed"]), _p(ws), wsb)
+    return o
+
+
 def mhc_pre_bwd(g, dH_post, dH_res, X, W, saved, H_pre, H_post, H_res_logits, alpha=None, iters=20, eps=1e-6,
                 dX=None, accumulate_dX=False, want_intermediates=False, post_G=None, post_H_res=None):
     """Fused pre pass backward.  Returns dict(dX, dW, dalpha, dhbias[, dH_pre, dlogits]).

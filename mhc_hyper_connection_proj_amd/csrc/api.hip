@@ -557,6 +557,90 @@ mhc_status mhc_pre_fwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_d
   return launched("mhc_pre_fwd");
 }
 
+// ------------------------------------------------------------------ RMSNorm of the aggregated stream
+mhc_status mhc_rmsnorm_fwd(void *stream, int64_t tokens, int64_t C, mhc_dtype act, const void *x,
+                           const float *gamma, float eps, void *y) {
+  Validator v("mhc_rmsnorm_fwd");
+  v.dims(tokens, mhc::kN, C, act);
+  v.eps(eps, "eps");
+  if (!v.ok()) return v.status();
+  if (tokens == 0) return MHC_OK;
+  v.in(x, tokens * C * esz(act), "x");
+  v.in(gamma, C * 4, "gamma", true);
+  v.out(y, tokens * C * esz(act), "y");
+  if (v.finish() != MHC_OK) return v.status();
+  mhc::launch_rmsnorm_fwd((hipStream_t)stream, act == MHC_F32, tokens, C, x, gamma, eps, y);
+  return launched("mhc_rmsnorm_fwd");
+}
+
+size_t mhc_rmsnorm_bwd_workspace_size(int64_t tokens, int64_t C, mhc_dtype act, int32_t with_dgamma) {
+  (void)act;
+  if (tokens <= 0 || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
+  return mhc::rmsnorm_bwd_ws(tokens, C, with_dgamma != 0);
+}
+
+mhc_status mhc_rmsnorm_bwd(void *stream, int64_t tokens, int64_t C, mhc_dtype act, const void *dy,
+                           const void *x, const float *gamma, float eps, void *dx,
+                           int32_t accumulate_dx, float *dgamma, void *workspace,
+                           size_t workspace_bytes) {
+  Validator v("mhc_rmsnorm_bwd");
+  v.dims(tokens, mhc::kN, C, act);
+  v.eps(eps, "eps");
+  if (!v.ok()) return v.status();
+  const hipStream_t s = (hipStream_t)stream;
+  if (tokens == 0) {
+    v.out(dgamma, C * 4, "dgamma", true);
+    if (v.finish() != MHC_OK) return v.status();
+    return zero_f32(s, dgamma, C) ? launched("mhc_rmsnorm_bwd") : MHC_OK;
+  }
+  v.in(dy, tokens * C * esz(act), "dy");
+  v.in(x, tokens * C * esz(act), "x");
+  v.in(gamma, C * 4, "gamma", true);
+  v.out(dx, tokens * C * esz(act), "dx");
+  v.out(dgamma, C * 4, "dgamma", true);
+  v.workspace(workspace, workspace_bytes, mhc::rmsnorm_bwd_ws(tokens, C, dgamma != nullptr));
+  if (v.finish() != MHC_OK) return v.status();
+  mhc::launch_rmsnorm_bwd(s, act == MHC_F32, tokens, C, dy, x, gamma, eps, dx, accumulate_dx != 0, dgamma,
+                          workspace);
+  return launched("mhc_rmsnorm_bwd");
+}
+
+mhc_status mhc_pre_rmsnorm_fwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                               const void *X, const float *W, const float *alpha, const float *hbias,
+                               float rms_eps, int32_t iters, float eps, const float *gamma,
+                               float norm_eps, float *H_pre, float *H_post, float *H_res,
+                               float *H_res_logits, float *saved, void *agg, void *normed,
+                               void *workspace, size_t workspace_bytes) {
+  Validator v("mhc_pre_rmsnorm_fwd");
+  v.dims(tokens, n, C, act);
+  v.eps(rms_eps, "rms_eps");
+  v.eps(eps, "eps");
+  v.eps(norm_eps, "norm_eps");
+  v.iters(iters);
+  if (!v.ok()) return v.status();
+  if (tokens == 0) return MHC_OK;
+  const int64_t K = 4 * C;
+  v.in(X, tokens * K * esz(act), "X");
+  v.in(W, K * J * 4, "W");
+  v.in(alpha, 12, "alpha", true);
+  v.in(hbias, J * 4, "hbias", true);
+  v.in(gamma, C * 4, "gamma", true);
+  v.out(H_pre, tokens * 16, "H_pre");
+  v.out(H_post, tokens * 16, "H_post");
+  v.out(H_res, tokens * 64, "H_res");
+  v.out(H_res_logits, tokens * 64, "H_res_logits");
+  v.out(saved, tokens * MHC_SAVED_STRIDE * 4, "saved", true);
+  v.out(agg, tokens * C * esz(act), "agg");
+  v.out(normed, tokens * C * esz(act), "normed");
+  v.workspace(workspace, workspace_bytes, mhc::proj_fwd_ws(tokens, C, act == MHC_F32));
+  if (v.finish() != MHC_OK) return v.status();
+  const hipStream_t s = (hipStream_t)stream;
+  mhc::launch_proj_fwd(s, act == MHC_F32, tokens, C, X, W, alpha, hbias, rms_eps, H_pre, H_post,
+                       H_res_logits, saved, H_res, iters, eps, workspace);
+  mhc::launch_h_aggregate_rmsnorm_fwd(s, act == MHC_F32, tokens, C, X, H_pre, gamma, norm_eps, agg, normed);
+  return launched("mhc_pre_rmsnorm_fwd");
+}
+
 size_t mhc_pre_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
   return mhc_proj_rms_h_bwd_workspace_size(tokens, n, C, act);
 }

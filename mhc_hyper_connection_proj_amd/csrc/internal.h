@@ -62,6 +62,18 @@ void launch_h_post_bda_bwd(hipStream_t s, bool f32, int64_t N, int64_t C, const 
                            const void *bias, void *dX, float *dH_res, float *dH_post, void *dx,
                            void *dbias, void *ws);
 
+// ---- RMSNorm of the aggregated stream [N][C]; gamma [C] fp32 or NULL (unit gain)
+void launch_rmsnorm_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *x, const float *gamma,
+                        float eps, void *y);
+// h_aggregate writing agg, then y = RMSNorm(agg as stored), in one pass (H_pre [N][4]).
+void launch_h_aggregate_rmsnorm_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *X,
+                                    const float *H_pre, const float *gamma, float eps, void *agg, void *y);
+// dx (+)= the RMSNorm input gradient; dgamma (may be NULL) = sum over tokens,
+// through per-workgroup partial rows in ws (rmsnorm_bwd_ws bytes).
+size_t rmsnorm_bwd_ws(int64_t N, int64_t C, bool with_dgamma);
+void launch_rmsnorm_bwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *dy, const void *x,
+                        const float *gamma, float eps, void *dx, bool accumulate, float *dgamma, void *ws);
+
 // ---- projection (forward)
 size_t proj_fwd_ws(int64_t N, int64_t C, bool f32);
 // Writes H_pre, H_post, logits, saved (may be NULL); if H_res != NULL also

@@ -6,7 +6,7 @@ same host arrays to the HIP library and to the CPU oracle.
 
 Seeding: numpy PCG64 with seed = 1000 * workload_id + tensor_id, where the
 tensor ids are X=1, W=2, x=3, bias=4, G=5, H_res logits=6, H_post logits=7,
-layer scale=8.  Normals are drawn in float32 and scaled by their standard
+layer scale=8, norm gain=9, norm upstream grad=10.  Normals are drawn in float32 and scaled by their standard
 deviation; bf16 tensors are the round-to-nearest-even bf16 of those float32
 values, returned as uint16 bit patterns.
 """
@@ -16,7 +16,8 @@ from dataclasses import dataclass
 
 import numpy as np
 
-TENSOR_IDS = {"X": 1, "W": 2, "x": 3, "bias": 4, "G": 5, "L": 6, "Hpost_logits": 7, "scale": 8}
+TENSOR_IDS = {"X": 1, "W": 2, "x": 3, "bias": 4, "G": 5, "L": 6, "Hpost_logits": 7, "scale": 8, "gamma": 9,
+              "dy": 10}
 
 
 @dataclass(frozen=True)
@@ -97,7 +98,8 @@ def tensor(w: Workload, name: str, tokens: int | None = None, C: int | None = No
 
     Names: X [N,n,C] (act), W [n*C, n*n+2n] f32, x [N,C] (act), bias [C] (act),
     G [N,n,C] (act), L [N,n,n] f32 (logits), Hpost_logits [N,n] f32,
-    scale [C] (act, U(0.5,1.5)), dH [N,n,n] f32 (Sinkhorn upstream grad).
+    scale [C] (act, U(0.5,1.5)), dH [N,n,n] f32 (Sinkhorn upstream grad),
+    gamma [C] f32 U(0.5,1.5) (norm gain), dy [N,C] (act, N(0,1): upstream grad of the norm).
     """
     N = w.tokens if tokens is None else tokens
     C = w.C if C is None else C
@@ -118,6 +120,10 @@ def tensor(w: Workload, name: str, tokens: int | None = None, C: int | None = No
         return normal_f32(w.wid, "G", (N, n, n))
     if name == "Hpost_logits":
         return normal_f32(w.wid, "Hpost_logits", (N, n))
+    if name == "gamma":
+        return uniform_f32(w.wid, "gamma", (C,), 0.5, 1.5)
+    if name == "dy":
+        return store(normal_f32(w.wid, "dy", (N, C)), w.act)
     if name == "scale":
         return store(uniform_f32(w.wid, "scale", (C,), 0.5, 1.5), w.act)
     raise KeyError(name)

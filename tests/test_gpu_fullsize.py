@@ -219,3 +219,41 @@ def test_variants_full_size():
     assert_act("static dX", rows(dX_s, S), sdX, w.act)
     parts = np.abs(O.h_aggregate_bwd(h64(g[S]), XS, np.broadcast_to(h64(h), (len(S), n)).copy())[1]).sum(axis=0)
     assert_tokensum("static dH_pre", dH_s, sdH, parts)
+
+
+# ----------------------------------------------------------------- RMSNorm of the aggregated stream
+def test_rmsnorm_full_size():
+    """Standalone norm fwd/bwd at 16384 x 7168 (bf16) and the fused pre pass + norm at full size."""
+    w = synth.WORKLOADS["full_layer"]
+    N, C = w.tokens, w.C
+    log(f"rmsnorm full size: N={N} C={C}")
+    S = sample_tokens(N, w.wid + 9)
+    Z = others(N, S, w.wid + 9)
+    x = synth.tensor(w, "x")
+    gamma = synth.tensor(w, "gamma")
+    dy = only(synth.tensor(w, "dy"), S)
+    xd, gd = dev(x), dev(gamma)
+    y = B.mhc_rmsnorm_fwd(xd, gd, w.rms_eps)
+    dx, dg = B.mhc_rmsnorm_bwd(dev(dy), xd, gd, w.rms_eps)
+    torch.cuda.synchronize()
+    xS = h64(x[S])
+    yo, r = O.rmsnorm_fwd(xS, h64(gamma), w.rms_eps)
+    assert_act("y", rows(y, S), yo, w.act)
+    dxo, dgo = O.rmsnorm_bwd(h64(dy[S]), xS, h64(gamma), w.rms_eps)
+    assert_act("dx", rows(dx, S), dxo, w.act)
+    assert not h64(rows(dx, Z)).any(), "dx: nonzero on tokens with zero upstream gradient"
+    assert_tokensum("dgamma", dg, dgo, np.abs(h64(dy[S]) * r[:, None] * xS).sum(0))
+    del y, dx, dg, xd
+
+    X = residual("full_layer")
+    W = synth.tensor(w, "W")
+    f = B.mhc_pre_rmsnorm_fwd(dev(X), dev(W), gd, None, None, w.rms_eps, w.iters, w.eps, w.rms_eps)
+    torch.cuda.synchronize()
+    ref = O.pre_fwd(h64(X[S]), h64(W), None, None, w.rms_eps, w.iters, w.eps)
+    assert_act("agg", rows(f["agg"], S), ref["agg"], w.act)
+    assert_rel("H_res", rows(f["H_res"], S), ref["H_res"])
+    yo, _ = O.rmsnorm_fwd(O.round_to(ref["agg"], w.act), h64(gamma), w.rms_eps)
+    ob = O.round_f64_to_bf16(yo)
+    g = h64(rows(f["normed"], S))
+    # two ulps: the stored agg may sit one ulp from the oracle's, carried over by the row scale
+    assert np.all(np.abs(g - ob) <= 16e-3 * np.abs(ob) + 1e-5 * np.sqrt(np.mean(yo * yo)))
