@@ -101,6 +101,14 @@ def measure_variants(lib, L, sp, N, n, C, X, G, H_res, H_post, x, g, out, dX, dM
     calls["rmsnorm_fwd"] = (4 * C, lambda: lib.mhc_rmsnorm_fwd(sp, N, C, MHC_BF16, P(x), P(gam), 1e-6, P(dx)))
     calls["rmsnorm_bwd"] = (6 * C, lambda: lib.mhc_rmsnorm_bwd(sp, N, C, MHC_BF16, P(g), P(x), P(gam), 1e-6, P(dx), 0,
                                                                 P(dgam), P(wsn_), wsr))
+    # h_post_bda backward with a bias (dbias summed over tokens), dX left to the pre backward
+    bias = torch.full((C,), 0.1, dtype=torch.bfloat16, device=dev)
+    dbias = torch.empty(C, dtype=torch.bfloat16, device=dev)
+    wsb = lib.mhc_h_post_bda_bwd_workspace_size(N, n, C, MHC_BF16, 1)
+    wsb_ = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    calls["h_post_bda_bwd_dbias"] = (20 * C + 160, lambda: lib.mhc_h_post_bda_bwd(
+        sp, N, n, C, MHC_BF16, P(G), P(X), P(H_res), P(H_post), P(x), P(bias), None, P(dM), P(dH), P(dx),
+        P(dbias), P(wsb_), wsb))
     res = {}
     for name, (bytes_per_token, fn) in calls.items():
         L.check(fn())

@@ -62,6 +62,12 @@ void launch_h_post_bda_bwd(hipStream_t s, bool f32, int64_t N, int64_t C, const 
                            const void *bias, void *dX, float *dH_res, float *dH_post, void *dx,
                            void *dbias, void *ws);
 
+// ---- fixed-order column sums of per-workgroup partial rows part[R][C] (fp32)
+// into out[C] (fp32 or bf16); mid: kRowSumSlices * C floats of scratch.
+constexpr int kRowSumSlices = 16;
+void launch_rows_sum(hipStream_t s, const float *part, int64_t R, int64_t C, float *mid, void *out,
+                     bool out_bf16);
+
 // ---- RMSNorm of the aggregated stream [N][C]; gamma [C] fp32 or NULL (unit gain)
 void launch_rmsnorm_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *x, const float *gamma,
                         float eps, void *y);

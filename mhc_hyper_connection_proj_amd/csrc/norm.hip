@@ -16,7 +16,7 @@
 // with a 128-bit access, and per-token sums go lane -> wave (DPP) ->
 // workgroup (LDS, fixed wave order), so results are bitwise reproducible.
 // dgamma: per-workgroup partial rows (TG tokens each, fixed token order) in
-// the workspace, summed over rows in a fixed order by dgamma_rows_sum_kernel.
+// the workspace, summed over rows in a fixed order (launch_rows_sum).
 #include "device.h"
 #include "internal.h"
 
@@ -183,15 +183,30 @@ __global__ __launch_bounds__(512) void rmsnorm_bwd_kernel(
   }
   const int64_t t0 = (int64_t)blockIdx.x * TG;
   const int64_t t1 = min(t0 + (int64_t)TG, N);
-  for (int64_t t = t0; t < t1; ++t) {
-    R rx[GPT], rg[GPT], rd[GPT];
+  // The next token's rows are loaded while this token is reduced and
+  // written, so a workgroup always has one token's loads in flight.
+  R nx[GPT], ng[GPT], nd[GPT];
+  auto issue = [&](int64_t tt) {
 #pragma unroll
     for (int j = 0; j < GPT; ++j) {
       const int gc = group_of(j, G);
-      rx[j] = Io8<T>::ld_nt(x + t * C + 8 * gc);
-      rg[j] = Io8<T>::ld_nt(dy + t * C + 8 * gc);
-      if (ACCUM) rd[j] = Io8<T>::ld_nt(dx + t * C + 8 * gc);
+      nx[j] = Io8<T>::ld_nt(x + tt * C + 8 * gc);
+      ng[j] = Io8<T>::ld_nt(dy + tt * C + 8 * gc);
+      if (ACCUM) nd[j] = Io8<T>::ld_nt(dx + tt * C + 8 * gc);
     }
+  };
+  // One token: reduce, then write dx and add to the dgamma partials.  The
+  // loop issues token t+1 unconditionally and the last token is peeled, so
+  // the waits for token t never have to cover the prefetch.
+  auto token = [&](int64_t t) {
+    R rx[GPT], rg[GPT], rd[GPT];
+#pragma unroll
+    for (int j = 0; j < GPT; ++j) {
+      rx[j] = nx[j];
+      rg[j] = ng[j];
+      if (ACCUM) rd[j] = nd[j];
+    }
+    if (t + 1 < t1) issue(t + 1);
     float xv[GPT][8], gy[GPT][8];
     float sums[2] = {0.f, 0.f};  // sum x^2, sum gamma dy x
 #pragma unroll
@@ -225,6 +240,11 @@ __global__ __launch_bounds__(512) void rmsnorm_bwd_kernel(
         Io8<T>::store(dx + t * C + 8 * g, o);
       }
     }
+  };
+  if (t0 < t1) {
+    issue(t0);
+    for (int64_t t = t0; t + 1 < t1; ++t) token(t);
+    token(t1 - 1);
   }
   if (DGAMMA) {
 #pragma unroll
@@ -237,22 +257,6 @@ __global__ __launch_bounds__(512) void rmsnorm_bwd_kernel(
       }
     }
   }
-}
-
-// dgamma[c] = sum over the partial rows, fixed order: 4 waves stride the
-// rows, then the 4 wave sums are added in wave order.  Block = 64 channels.
-__global__ __launch_bounds__(256) void dgamma_rows_sum_kernel(const float *__restrict__ part,
-                                                              float *__restrict__ out, int64_t rows,
-                                                              int64_t C) {
-  __shared__ float red[4][64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
-  float s = 0.f;
-  if (c < C)
-    for (int64_t r = wave; r < rows; r += 4) s += part[r * C + c];
-  red[wave][lane] = s;
-  __syncthreads();
-  if (wave == 0 && c < C) out[c] = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
 }
 
 #define MHC_NORM_GPT_DISPATCH(GPT_VAL, ...)                  \
@@ -298,8 +302,8 @@ void norm_bwd(hipStream_t s, int64_t N, int64_t C, const void *dy, const void *x
       norm_bwd4<T, GAMMA, true, true>(s, N, C, dy, x, gamma, eps, dx, part);
     else
       norm_bwd4<T, GAMMA, false, true>(s, N, C, dy, x, gamma, eps, dx, part);
-    hipLaunchKernelGGL(dgamma_rows_sum_kernel, dim3((unsigned)((C + 63) / 64)), dim3(256), 0, s, part, dgamma,
-                       (N + kNormTG - 1) / kNormTG, C);
+    const int64_t R = (N + kNormTG - 1) / kNormTG;
+    launch_rows_sum(s, part, R, C, part + R * C, dgamma, false);
   } else if (acc) {
     norm_bwd4<T, GAMMA, true, false>(s, N, C, dy, x, gamma, eps, dx, nullptr);
   } else {
@@ -328,7 +332,7 @@ void launch_h_aggregate_rmsnorm_fwd(hipStream_t s, bool f32, int64_t N, int64_t 
 }
 
 size_t rmsnorm_bwd_ws(int64_t N, int64_t C, bool with_dgamma) {
-  return with_dgamma ? (size_t)((N + kNormTG - 1) / kNormTG) * (size_t)C * 4 : 0;
+  return with_dgamma ? ((size_t)((N + kNormTG - 1) / kNormTG) + kRowSumSlices) * (size_t)C * 4 : 0;
 }
 
 void launch_rmsnorm_bwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *dy, const void *x,

@@ -9,7 +9,7 @@
 // the 4x4 mix stays in registers.  The per-token H values are wave-uniform
 // (scalar loads).  Per-token reductions over C go lane -> wave (DPP) ->
 // workgroup (LDS, fixed wave order); cross-token sums (dbias) go through
-// per-workgroup partials reduced in a fixed order by a second kernel.
+// per-workgroup partials summed in a fixed order by launch_rows_sum (reduce.hip).
 //
 // Token order: the kernels that follow a full pass over X walk the tokens in
 // the opposite direction of that pass (h_aggregate forward and h_post_bda
@@ -398,31 +398,6 @@ __global__ __launch_bounds__(256) void h_post_bda_bwd_kernel(
   }
 }
 
-// dbias[c] = sum over partial rows, fixed order: 4 waves stride the rows,
-// then the 4 wave sums are added in wave order.  Block = 64 channels.
-template <typename T>
-__global__ __launch_bounds__(256) void dbias_reduce_kernel(const float *__restrict__ part,
-                                                           T *__restrict__ dbias, int64_t rows,
-                                                           int64_t C) {
-  __shared__ float red[4][64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
-  float s = 0.f;
-  if (c < C)
-    for (int64_t r = wave; r < rows; r += 4) s += part[r * C + c];
-  red[wave][lane] = s;
-  __syncthreads();
-  if (wave == 0 && c < C) {
-    const float tot = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
-    if constexpr (sizeof(T) == 2) {
-      const __bf16 h = (__bf16)tot;
-      dbias[c] = __builtin_bit_cast(uint16_t, h);
-    } else {
-      dbias[c] = tot;
-    }
-  }
-}
-
 // ============================================================ launchers
 #define MHC_GPT_DISPATCH(GPT_VAL, ...)                       \
   switch (GPT_VAL) {                                         \
@@ -541,7 +516,7 @@ void launch_stream_distribute_fwd(hipStream_t s, bool f32, int64_t N, int64_t C,
 size_t h_post_bda_bwd_ws(int64_t N, int64_t C, bool with_dbias) {
   if (!with_dbias) return 0;
   const int64_t rows = (N + kPostTG - 1) / kPostTG;
-  return (size_t)(rows * C) * sizeof(float);
+  return (size_t)((rows + kRowSumSlices) * C) * sizeof(float);
 }
 
 template <typename T, bool HAS_BIAS, bool DBIAS, int MODE = kPostFull>
@@ -570,8 +545,7 @@ static void post_bwd(hipStream_t s, int64_t N, int64_t C, const void *G, const v
     float *part = (float *)ws;
     post_bwd3<T, true, true>(s, N, C, G, X, Hr, Hp, x, b, dX, dHr, dHp, dx, part);
     const int64_t rows = (N + kPostTG - 1) / kPostTG;
-    hipLaunchKernelGGL((dbias_reduce_kernel<T>), dim3((unsigned)((C + 63) / 64)), dim3(256), 0, s,
-                       part, (T *)db, rows, C);
+    launch_rows_sum(s, part, rows, C, part + rows * C, db, sizeof(T) == 2);
   } else if (b) {
     post_bwd3<T, true, false>(s, N, C, G, X, Hr, Hp, x, b, dX, dHr, dHp, dx, nullptr);
   } else {
