@@ -5,7 +5,10 @@
  * Notation (per token): n residual streams of C channels; K = n*C; the
  * flattened stream index is k = i*C + c; J = n*n + 2n controller outputs,
  * ordered PRE [0,n) | POST [n,2n) | RES [2n, 2n+n*n) with RES row-major.
- * This build supports n == 4 (J = 24) on the GPU.
+ * Every entry point takes 1 <= n <= 8 (the pages' kernels read n from the
+ * tensor shapes).  n == 4 (J = 24, every benchmark workload) runs on kernels
+ * laid out for it; other n run on simpler kernels templated on n, with the
+ * same definitions, layouts, validation and determinism.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -29,7 +32,7 @@
  *  - Fail-closed validation BEFORE anything is enqueued: a bad argument
  *    returns an error and leaves every output untouched.  MHC_ERR_NULL for a
  *    missing required pointer, MHC_ERR_SHAPE for negative/zero sizes,
- *    MHC_ERR_UNSUPPORTED for n != 4, C % 8 != 0, C > 16384 or iters > 4096,
+ *    MHC_ERR_UNSUPPORTED for n > 8, C % 8 != 0, C > 16384 or iters > 4096,
  *    MHC_ERR_ALIGN for pointers not 16-byte aligned, MHC_ERR_ALIAS when an
  *    output overlaps an input or another output, MHC_ERR_WORKSPACE when the
  *    workspace is missing or too small, MHC_ERR_ARG for eps < 0, a
@@ -62,9 +65,13 @@ typedef enum mhc_status {
 typedef enum mhc_dtype { MHC_BF16 = 0, MHC_F32 = 1 } mhc_dtype;
 
 /* Per-token record written by the projection forward and read by its
- * backward: fp32 [tokens][MHC_SAVED_STRIDE] = { r, q, z[0..J), 0 ... } with
- * q = sqrt(sum x^2 / K), r = 1/(q + rms_eps) and z = r * (x @ W) (pre-gain). */
+ * backward: fp32 [tokens][mhc_saved_stride(n)] = { r, q, z[0..J), 0 ... }
+ * with q = sqrt(sum x^2 / K), r = 1/(q + rms_eps) and z = r * (x @ W)
+ * (pre-gain).  The stride is MHC_SAVED_STRIDE (32) while 2 + J <= 32
+ * (n <= 4), else 2 + J rounded up to a multiple of 8; mhc_saved_stride
+ * returns 0 for n outside [1, 8]. */
 #define MHC_SAVED_STRIDE 32
+int32_t mhc_saved_stride(int32_t n);
 
 const char *mhc_status_string(mhc_status s);
 const char *mhc_last_error(void);
@@ -100,7 +107,7 @@ mhc_status mhc_set_kernel_events(int32_t kernel, void *start_event, void *stop_e
  * X [tokens][n][C] (act); W [K][J] fp32; alpha [3] fp32 (pre, post, res) or
  * NULL for ones; hbias [J] fp32 or NULL for zeros.  Outputs (fp32): H_pre
  * [tokens][n], H_post [tokens][n], H_res_logits [tokens][n][n], saved
- * [tokens][MHC_SAVED_STRIDE].  `saved` may be NULL when no backward follows.
+ * [tokens][mhc_saved_stride(n)].  `saved` may be NULL when no backward follows.
  * ---------------------------------------------------------------------- */
 size_t mhc_proj_rms_h_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act);
 mhc_status mhc_proj_rms_h(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,

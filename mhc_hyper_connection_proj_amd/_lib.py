@@ -36,6 +36,7 @@ SIGNATURES = {
     "mhc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mhc_last_error": (ctypes.c_char_p, []),
     "mhc_version": (ctypes.c_char_p, []),
+    "mhc_saved_stride": (_i32, [_i32]),
     "mhc_set_kernel_events": (ctypes.c_int, [_i32, _vp, _vp]),
     "mhc_proj_rms_h_workspace_size": (_sz, [_i64, _i32, _i64, ctypes.c_int]),
     "mhc_proj_rms_h": (ctypes.c_int, [_vp, _i64, _i32, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _f32,

@@ -9,10 +9,17 @@ from __future__ import annotations
 import torch
 
 from . import _lib
-from ._lib import MHC_BF16, MHC_F32, SAVED_STRIDE, call
+from ._lib import MHC_BF16, MHC_F32, call
 
-N_STREAMS = 4
-J = N_STREAMS * N_STREAMS + 2 * N_STREAMS
+
+def n_outputs(n: int) -> int:
+    """J = n*n + 2n controller outputs for n streams."""
+    return n * n + 2 * n
+
+
+def saved_stride(n: int) -> int:
+    """Row stride of the saved forward state (mhc_saved_stride)."""
+    return int(_lib.lib().mhc_saved_stride(n))
 
 
 def _act(t: torch.Tensor) -> int:
@@ -61,6 +68,7 @@ f32 = torch.float32
 def mhc_proj_rms_h(X, W, alpha=None, hbias=None, rms_eps=1e-6):
     """Projection + RMS + compute_h.  Returns (H_pre, H_post, H_res_logits, saved)."""
     N, n, C = _dims(X)
+    J = n_outputs(n)
     act = _act(X)
     _need(X, "X"); _need(W, "W", f32, n * C * J); _need(alpha, "alpha", f32, 3); _need(hbias, "hbias", f32, J)
     lead = X.shape[:-2]
@@ -68,7 +76,7 @@ def mhc_proj_rms_h(X, W, alpha=None, hbias=None, rms_eps=1e-6):
     H_pre = torch.empty(*lead, n, dtype=f32, device=d)
     H_post = torch.empty(*lead, n, dtype=f32, device=d)
     L = torch.empty(*lead, n, n, dtype=f32, device=d)
-    saved = torch.empty(*lead, SAVED_STRIDE, dtype=f32, device=d)
+    saved = torch.empty(*lead, saved_stride(n), dtype=f32, device=d)
     ws, wsb = _ws(_lib.lib().mhc_proj_rms_h_workspace_size(N, n, C, act), d)
     call("mhc_proj_rms_h", _stream(X), N, n, C, act, _p(X), _p(W), _p(alpha), _p(hbias), rms_eps,
          _p(H_pre), _p(H_post), _p(L), _p(saved), _p(ws), wsb)
@@ -79,8 +87,9 @@ def mhc_proj_rms_h_bwd(X, W, saved, H_pre, H_post, dH_pre, dH_post, dH_res_logit
                        dX=None, accumulate_dX=False, want_dW=True, want_dalpha=True, want_dhbias=True):
     """Projection backward.  Returns (dX, dW, dalpha, dhbias); skipped grads are None."""
     N, n, C = _dims(X)
+    J = n_outputs(n)
     act = _act(X)
-    for t, nm, ne in ((saved, "saved", N * SAVED_STRIDE), (H_pre, "H_pre", N * n), (H_post, "H_post", N * n),
+    for t, nm, ne in ((saved, "saved", N * saved_stride(n)), (H_pre, "H_pre", N * n), (H_post, "H_post", N * n),
                       (dH_pre, "dH_pre", N * n), (dH_post, "dH_post", N * n),
                       (dH_res_logits, "dH_res_logits", N * n * n)):
         _need(t, nm, f32, ne)
@@ -244,6 +253,7 @@ def mhc_h_post_bda_bwd(G, X, H_res, H_post, x, bias=None, want_dbias=True, want_
 def mhc_pre_fwd(X, W, alpha=None, hbias=None, rms_eps=1e-6, iters=20, eps=1e-6):
     """Fused pre pass.  Returns dict(H_pre, H_post, H_res, H_res_logits, saved, agg)."""
     N, n, C = _dims(X)
+    J = n_outputs(n)
     act = _act(X)
     _need(X, "X"); _need(W, "W", f32, n * C * J); _need(alpha, "alpha", f32, 3); _need(hbias, "hbias", f32, J)
     lead = X.shape[:-2]
@@ -251,7 +261,7 @@ def mhc_pre_fwd(X, W, alpha=None, hbias=None, rms_eps=1e-6, iters=20, eps=1e-6):
     o = dict(H_pre=torch.empty(*lead, n, dtype=f32, device=d), H_post=torch.empty(*lead, n, dtype=f32, device=d),
              H_res=torch.empty(*lead, n, n, dtype=f32, device=d),
              H_res_logits=torch.empty(*lead, n, n, dtype=f32, device=d),
-             saved=torch.empty(*lead, SAVED_STRIDE, dtype=f32, device=d),
+             saved=torch.empty(*lead, saved_stride(n), dtype=f32, device=d),
              agg=torch.empty(*lead, C, dtype=X.dtype, device=d))
     ws, wsb = _ws(_lib.lib().mhc_pre_fwd_workspace_size(N, n, C, act), d)
     call("mhc_pre_fwd", _stream(X), N, n, C, act, _p(X), _p(W), _p(alpha), _p(hbias), rms_eps, iters, eps,
@@ -303,6 +313,7 @@ def mhc_pre_rmsnorm_fwd(X, W, gamma=None, alpha=None, hbias=None, rms_eps=1e-6, 
                         norm_eps=1e-6):
     """Fused pre pass with the norm epilogue.  Returns mhc_pre_fwd's dict plus 'normed' = RMSNorm(agg)."""
     N, n, C = _dims(X)
+    J = n_outputs(n)
     act = _act(X)
     _need(X, "X"); _need(W, "W", f32, n * C * J); _need(alpha, "alpha", f32, 3); _need(hbias, "hbias", f32, J)
     _need(gamma, "gamma", f32, C)
@@ -311,7 +322,7 @@ def mhc_pre_rmsnorm_fwd(X, W, gamma=None, alpha=None, hbias=None, rms_eps=1e-6, 
     o = dict(H_pre=torch.empty(*lead, n, dtype=f32, device=d), H_post=torch.empty(*lead, n, dtype=f32, device=d),
              H_res=torch.empty(*lead, n, n, dtype=f32, device=d),
              H_res_logits=torch.empty(*lead, n, n, dtype=f32, device=d),
-             saved=torch.empty(*lead, SAVED_STRIDE, dtype=f32, device=d),
+             saved=torch.empty(*lead, saved_stride(n), dtype=f32, device=d),
              agg=torch.empty(*lead, C, dtype=X.dtype, device=d),
              normed=torch.empty(*lead, C, dtype=X.dtype, device=d))
     ws, wsb = _ws(_lib.lib().mhc_pre_fwd_workspace_size(N, n, C, act), d)
@@ -329,10 +340,11 @@ def mhc_pre_bwd(g, dH_post, dH_res, X, W, saved, H_pre, H_post, H_res_logits, al
     the h_post_bda dX term is added here (call mhc_h_post_bda_bwd with want_dX=False).
     """
     N, n, C = _dims(X)
+    J = n_outputs(n)
     act = _act(X)
     _need(X, "X"); _need(g, "g", X.dtype, N * C); _need(dH_post, "dH_post", f32, N * n)
     _need(dH_res, "dH_res", f32, N * n * n); _need(W, "W", f32, n * C * J); _need(alpha, "alpha", f32, 3)
-    _need(saved, "saved", f32, N * SAVED_STRIDE); _need(H_pre, "H_pre", f32, N * n)
+    _need(saved, "saved", f32, N * saved_stride(n)); _need(H_pre, "H_pre", f32, N * n)
     _need(H_post, "H_post", f32, N * n); _need(H_res_logits, "H_res_logits", f32, N * n * n)
     _need(post_G, "post_G", X.dtype, X.numel()); _need(post_H_res, "post_H_res", f32, N * n * n)
     d = X.device

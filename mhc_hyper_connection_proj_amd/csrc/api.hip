@@ -45,7 +45,7 @@ class Validator {
     if (tokens < 0) fail(MHC_ERR_SHAPE, "tokens must be >= 0");
     if (n <= 0) fail(MHC_ERR_SHAPE, "n must be > 0");
     if (C <= 0) fail(MHC_ERR_SHAPE, "C must be > 0");
-    if (n > 0 && n != mhc::kN) fail(MHC_ERR_UNSUPPORTED, "only n == 4 is supported");
+    if (n > mhc::kMaxN) fail(MHC_ERR_UNSUPPORTED, "n must be <= 8");
     if (C > 0 && C % 8 != 0) fail(MHC_ERR_UNSUPPORTED, "C must be a multiple of 8");
     if (C > mhc::kMaxC) fail(MHC_ERR_UNSUPPORTED, "C must be <= 16384");
     if (act != MHC_BF16 && act != MHC_F32) fail(MHC_ERR_ARG, "unknown activation dtype");
@@ -153,7 +153,6 @@ bool zero_act(hipStream_t s, void *p, int64_t n, mhc_dtype act) {
   return true;
 }
 
-constexpr int64_t J = mhc::kJ;
 
 }  // namespace
 
@@ -186,6 +185,8 @@ const char *mhc_last_error(void) { return g_last_error.c_str(); }
 
 const char *mhc_version(void) { return "libmhc 0.1 gfx950"; }
 
+int32_t mhc_saved_stride(int32_t n) { return (n < 1 || n > mhc::kMaxN) ? 0 : mhc::saved_stride(n); }
+
 mhc_status mhc_set_kernel_events(int32_t kernel, void *start_event, void *stop_event) {
   if (kernel == MHC_KERNEL_NONE || (!start_event && !stop_event)) {
     g_kernel_events = KernelEvents{};
@@ -205,8 +206,8 @@ mhc_status mhc_set_kernel_events(int32_t kernel, void *start_event, void *stop_e
 
 // ------------------------------------------------------------------ projection fwd
 size_t mhc_proj_rms_h_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
-  if (tokens <= 0 || n != 4 || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
-  return mhc::proj_fwd_ws(tokens, C, act == MHC_F32);
+  if (tokens <= 0 || n < 1 || n > mhc::kMaxN || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
+  return n == 4 ? mhc::proj_fwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_fwd_ws(n, tokens);
 }
 
 mhc_status mhc_proj_rms_h(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
@@ -218,26 +219,31 @@ mhc_status mhc_proj_rms_h(void *stream, int64_t tokens, int32_t n, int64_t C, mh
   v.eps(rms_eps, "rms_eps");
   if (!v.ok()) return v.status();
   if (tokens == 0) return MHC_OK;
-  const int64_t K = 4 * C;
+  const int64_t K = (int64_t)n * C;
+  const int64_t J = (int64_t)n * n + 2 * n;
   v.in(X, tokens * K * esz(act), "X");
   v.in(W, K * J * 4, "W");
   v.in(alpha, 3 * 4, "alpha", true);
   v.in(hbias, J * 4, "hbias", true);
-  v.out(H_pre, tokens * 16, "H_pre");
-  v.out(H_post, tokens * 16, "H_post");
-  v.out(H_res_logits, tokens * 64, "H_res_logits");
-  v.out(saved, tokens * MHC_SAVED_STRIDE * 4, "saved", true);
-  v.workspace(workspace, workspace_bytes, mhc::proj_fwd_ws(tokens, C, act == MHC_F32));
+  v.out(H_pre, tokens * n * 4, "H_pre");
+  v.out(H_post, tokens * n * 4, "H_post");
+  v.out(H_res_logits, tokens * n * n * 4, "H_res_logits");
+  v.out(saved, tokens * mhc::saved_stride(n) * 4, "saved", true);
+  v.workspace(workspace, workspace_bytes, n == 4 ? mhc::proj_fwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_fwd_ws(n, tokens));
   if (v.finish() != MHC_OK) return v.status();
-  mhc::launch_proj_fwd((hipStream_t)stream, act == MHC_F32, tokens, C, X, W, alpha, hbias, rms_eps,
-                       H_pre, H_post, H_res_logits, saved, nullptr, 0, 0.f, workspace);
+  if (n == 4)
+    mhc::launch_proj_fwd((hipStream_t)stream, act == MHC_F32, tokens, C, X, W, alpha, hbias, rms_eps,
+                         H_pre, H_post, H_res_logits, saved, nullptr, 0, 0.f, workspace);
+  else
+    mhc::glaunch_proj_fwd((hipStream_t)stream, act == MHC_F32, n, tokens, C, X, W, alpha, hbias, rms_eps,
+                          H_pre, H_post, H_res_logits, saved, nullptr, 0, 0.f, workspace);
   return launched("mhc_proj_rms_h");
 }
 
 // ------------------------------------------------------------------ projection bwd
 size_t mhc_proj_rms_h_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
-  if (tokens <= 0 || n != 4 || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
-  return mhc::proj_bwd_ws(tokens, C, act == MHC_F32);
+  if (tokens <= 0 || n < 1 || n > mhc::kMaxN || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
+  return n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_bwd_ws(n, tokens, C);
 }
 
 mhc_status mhc_proj_rms_h_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
@@ -249,7 +255,8 @@ mhc_status mhc_proj_rms_h_bwd(void *stream, int64_t tokens, int32_t n, int64_t C
   Validator v("mhc_proj_rms_h_bwd");
   v.dims(tokens, n, C, act);
   if (!v.ok()) return v.status();
-  const int64_t K = 4 * C;
+  const int64_t K = (int64_t)n * C;
+  const int64_t J = (int64_t)n * n + 2 * n;
   const hipStream_t s = (hipStream_t)stream;
   if (tokens == 0) {
     v.out(dW, K * J * 4, "dW", true);
@@ -262,17 +269,17 @@ mhc_status mhc_proj_rms_h_bwd(void *stream, int64_t tokens, int32_t n, int64_t C
   v.in(X, tokens * K * esz(act), "X");
   v.in(W, K * J * 4, "W");
   v.in(alpha, 12, "alpha", true);
-  v.in(saved, tokens * MHC_SAVED_STRIDE * 4, "saved");
-  v.in(H_pre, tokens * 16, "H_pre");
-  v.in(H_post, tokens * 16, "H_post");
-  v.in(dH_pre, tokens * 16, "dH_pre");
-  v.in(dH_post, tokens * 16, "dH_post");
-  v.in(dH_res_logits, tokens * 64, "dH_res_logits");
+  v.in(saved, tokens * mhc::saved_stride(n) * 4, "saved");
+  v.in(H_pre, tokens * n * 4, "H_pre");
+  v.in(H_post, tokens * n * 4, "H_post");
+  v.in(dH_pre, tokens * n * 4, "dH_pre");
+  v.in(dH_post, tokens * n * 4, "dH_post");
+  v.in(dH_res_logits, tokens * n * n * 4, "dH_res_logits");
   v.out(dX, tokens * K * esz(act), "dX");
   v.out(dW, K * J * 4, "dW", true);
   v.out(dalpha, 12, "dalpha", true);
   v.out(dhbias, J * 4, "dhbias", true);
-  v.workspace(workspace, workspace_bytes, mhc::proj_bwd_ws(tokens, C, act == MHC_F32));
+  v.workspace(workspace, workspace_bytes, n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_bwd_ws(n, tokens, C));
   if (v.finish() != MHC_OK) return v.status();
   mhc::ProjBwdArgs a{};
   a.f32 = act == MHC_F32; a.N = tokens; a.C = C; a.X = X; a.W = W; a.alpha = alpha; a.saved = saved;
@@ -280,7 +287,10 @@ mhc_status mhc_proj_rms_h_bwd(void *stream, int64_t tokens, int32_t n, int64_t C
   a.dH_res = nullptr; a.logits = nullptr; a.iters = 0; a.eps = 0.f; a.g = nullptr; a.dX = dX;
   a.accumulate = accumulate_dX != 0; a.dW = dW; a.dalpha = dalpha; a.dhbias = dhbias;
   a.dH_pre_out = nullptr; a.dL_out = nullptr; a.ws = workspace;
-  mhc::launch_proj_bwd(s, a);
+  if (n == 4)
+    mhc::launch_proj_bwd(s, a);
+  else
+    mhc::glaunch_proj_bwd(s, n, a);
   return launched("mhc_proj_rms_h_bwd");
 }
 
@@ -290,15 +300,18 @@ mhc_status mhc_sinkhorn_fwd(void *stream, int64_t count, int32_t n, const float 
   Validator v("mhc_sinkhorn_fwd");
   if (count < 0) v.fail(MHC_ERR_SHAPE, "count must be >= 0");
   if (n <= 0) v.fail(MHC_ERR_SHAPE, "n must be > 0");
-  else if (n != 4) v.fail(MHC_ERR_UNSUPPORTED, "only n == 4 is supported");
+  else if (n > mhc::kMaxN) v.fail(MHC_ERR_UNSUPPORTED, "n must be <= 8");
   v.iters(iters);
   v.eps(eps, "eps");
   if (!v.ok()) return v.status();
   if (count == 0) return MHC_OK;
-  v.in(logits, count * 64, "logits");
-  v.out(H_res, count * 64, "H_res");
+  v.in(logits, count * n * n * 4, "logits");
+  v.out(H_res, count * n * n * 4, "H_res");
   if (v.finish() != MHC_OK) return v.status();
-  mhc::launch_sinkhorn_fwd((hipStream_t)stream, count, logits, H_res, iters, eps);
+  if (n == 4)
+    mhc::launch_sinkhorn_fwd((hipStream_t)stream, count, logits, H_res, iters, eps);
+  else
+    mhc::glaunch_sinkhorn_fwd((hipStream_t)stream, n, count, logits, H_res, iters, eps);
   return launched("mhc_sinkhorn_fwd");
 }
 
@@ -307,16 +320,19 @@ mhc_status mhc_sinkhorn_bwd(void *stream, int64_t count, int32_t n, const float 
   Validator v("mhc_sinkhorn_bwd");
   if (count < 0) v.fail(MHC_ERR_SHAPE, "count must be >= 0");
   if (n <= 0) v.fail(MHC_ERR_SHAPE, "n must be > 0");
-  else if (n != 4) v.fail(MHC_ERR_UNSUPPORTED, "only n == 4 is supported");
+  else if (n > mhc::kMaxN) v.fail(MHC_ERR_UNSUPPORTED, "n must be <= 8");
   v.iters(iters);
   v.eps(eps, "eps");
   if (!v.ok()) return v.status();
   if (count == 0) return MHC_OK;
-  v.in(dH_res, count * 64, "dH_res");
-  v.in(logits, count * 64, "logits");
-  v.out(dlogits, count * 64, "dlogits");
+  v.in(dH_res, count * n * n * 4, "dH_res");
+  v.in(logits, count * n * n * 4, "logits");
+  v.out(dlogits, count * n * n * 4, "dlogits");
   if (v.finish() != MHC_OK) return v.status();
-  mhc::launch_sinkhorn_bwd((hipStream_t)stream, count, dH_res, logits, dlogits, iters, eps);
+  if (n == 4)
+    mhc::launch_sinkhorn_bwd((hipStream_t)stream, count, dH_res, logits, dlogits, iters, eps);
+  else
+    mhc::glaunch_sinkhorn_bwd((hipStream_t)stream, n, count, dH_res, logits, dlogits, iters, eps);
   return launched("mhc_sinkhorn_bwd");
 }
 
@@ -327,11 +343,14 @@ mhc_status mhc_h_aggregate_fwd(void *stream, int64_t tokens, int32_t n, int64_t 
   v.dims(tokens, n, C, act);
   if (!v.ok()) return v.status();
   if (tokens == 0) return MHC_OK;
-  v.in(X, tokens * 4 * C * esz(act), "X");
-  v.in(H_pre, tokens * 16, "H_pre");
+  v.in(X, tokens * n * C * esz(act), "X");
+  v.in(H_pre, tokens * n * 4, "H_pre");
   v.out(out, tokens * C * esz(act), "out");
   if (v.finish() != MHC_OK) return v.status();
-  mhc::launch_h_aggregate_fwd((hipStream_t)stream, act == MHC_F32, tokens, C, X, H_pre, out);
+  if (n == 4)
+    mhc::launch_h_aggregate_fwd((hipStream_t)stream, act == MHC_F32, tokens, C, X, H_pre, out);
+  else
+    mhc::glaunch_h_aggregate_fwd((hipStream_t)stream, act == MHC_F32, n, tokens, C, X, H_pre, out, n);
   return launched("mhc_h_aggregate_fwd");
 }
 
@@ -343,13 +362,17 @@ mhc_status mhc_h_aggregate_bwd(void *stream, int64_t tokens, int32_t n, int64_t 
   if (!v.ok()) return v.status();
   if (tokens == 0) return MHC_OK;
   v.in(g, tokens * C * esz(act), "g");
-  v.in(X, tokens * 4 * C * esz(act), "X");
-  v.in(H_pre, tokens * 16, "H_pre");
-  v.out(dX, tokens * 4 * C * esz(act), "dX");
-  v.out(dH_pre, tokens * 16, "dH_pre");
+  v.in(X, tokens * n * C * esz(act), "X");
+  v.in(H_pre, tokens * n * 4, "H_pre");
+  v.out(dX, tokens * n * C * esz(act), "dX");
+  v.out(dH_pre, tokens * n * 4, "dH_pre");
   if (v.finish() != MHC_OK) return v.status();
-  mhc::launch_h_aggregate_bwd((hipStream_t)stream, act == MHC_F32, tokens, C, g, X, H_pre, dX,
-                              accumulate_dX != 0, dH_pre);
+  if (n == 4)
+    mhc::launch_h_aggregate_bwd((hipStream_t)stream, act == MHC_F32, tokens, C, g, X, H_pre, dX,
+                                accumulate_dX != 0, dH_pre);
+  else
+    mhc::glaunch_h_aggregate_bwd((hipStream_t)stream, act == MHC_F32, n, tokens, C, g, X, H_pre, dX,
+                                 accumulate_dX != 0, dH_pre);
   return launched("mhc_h_aggregate_bwd");
 }
 
@@ -361,22 +384,25 @@ mhc_status mhc_h_post_bda_fwd(void *stream, int64_t tokens, int32_t n, int64_t C
   v.dims(tokens, n, C, act);
   if (!v.ok()) return v.status();
   if (tokens == 0) return MHC_OK;
-  v.in(X, tokens * 4 * C * esz(act), "X");
-  v.in(H_res, tokens * 64, "H_res");
-  v.in(H_post, tokens * 16, "H_post");
+  v.in(X, tokens * n * C * esz(act), "X");
+  v.in(H_res, tokens * n * n * 4, "H_res");
+  v.in(H_post, tokens * n * 4, "H_post");
   v.in(x, tokens * C * esz(act), "x");
   v.in(bias, C * esz(act), "bias", true);
-  v.out(out, tokens * 4 * C * esz(act), "out");
+  v.out(out, tokens * n * C * esz(act), "out");
   if (v.finish() != MHC_OK) return v.status();
-  mhc::launch_h_post_bda_fwd((hipStream_t)stream, act == MHC_F32, tokens, C, X, H_res, H_post, x, bias, out);
+  if (n == 4)
+    mhc::launch_h_post_bda_fwd((hipStream_t)stream, act == MHC_F32, tokens, C, X, H_res, H_post, x, bias, out);
+  else
+    mhc::glaunch_h_post_bda_fwd((hipStream_t)stream, act == MHC_F32, n, tokens, C, X, H_res, H_post, x, bias, out);
   return launched("mhc_h_post_bda_fwd");
 }
 
 size_t mhc_h_post_bda_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
                                          int32_t with_dbias) {
   (void)act;
-  if (tokens <= 0 || n != 4 || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
-  return mhc::h_post_bda_bwd_ws(tokens, C, with_dbias != 0);
+  if (tokens <= 0 || n < 1 || n > mhc::kMaxN || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
+  return n == 4 ? mhc::h_post_bda_bwd_ws(tokens, C, with_dbias != 0) : mhc::gh_post_bda_bwd_ws(tokens, C, with_dbias != 0);
 }
 
 mhc_status mhc_h_post_bda_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
@@ -394,21 +420,25 @@ mhc_status mhc_h_post_bda_bwd(void *stream, int64_t tokens, int32_t n, int64_t C
     if (v.finish() != MHC_OK) return v.status();
     return zero_act(s, dbias, C, act) ? launched("mhc_h_post_bda_bwd") : MHC_OK;
   }
-  v.in(G, tokens * 4 * C * esz(act), "G");
-  v.in(X, tokens * 4 * C * esz(act), "X");
-  v.in(H_res, tokens * 64, "H_res");
-  v.in(H_post, tokens * 16, "H_post");
+  v.in(G, tokens * n * C * esz(act), "G");
+  v.in(X, tokens * n * C * esz(act), "X");
+  v.in(H_res, tokens * n * n * 4, "H_res");
+  v.in(H_post, tokens * n * 4, "H_post");
   v.in(x, tokens * C * esz(act), "x");
   v.in(bias, C * esz(act), "bias", true);
-  v.out(dX, tokens * 4 * C * esz(act), "dX", true);
-  v.out(dH_res, tokens * 64, "dH_res");
-  v.out(dH_post, tokens * 16, "dH_post");
+  v.out(dX, tokens * n * C * esz(act), "dX", true);
+  v.out(dH_res, tokens * n * n * 4, "dH_res");
+  v.out(dH_post, tokens * n * 4, "dH_post");
   v.out(dx, tokens * C * esz(act), "dx");
   v.out(dbias, C * esz(act), "dbias", true);
-  v.workspace(workspace, workspace_bytes, mhc::h_post_bda_bwd_ws(tokens, C, dbias != nullptr));
+  v.workspace(workspace, workspace_bytes, n == 4 ? mhc::h_post_bda_bwd_ws(tokens, C, dbias != nullptr) : mhc::gh_post_bda_bwd_ws(tokens, C, dbias != nullptr));
   if (v.finish() != MHC_OK) return v.status();
-  mhc::launch_h_post_bda_bwd(s, act == MHC_F32, tokens, C, G, X, H_res, H_post, x, bias, dX, dH_res,
-                             dH_post, dx, dbias, workspace);
+  if (n == 4)
+    mhc::launch_h_post_bda_bwd(s, act == MHC_F32, tokens, C, G, X, H_res, H_post, x, bias, dX, dH_res,
+                               dH_post, dx, dbias, workspace);
+  else
+    mhc::glaunch_h_post_bda_bwd(s, act == MHC_F32, n, tokens, C, G, X, H_res, H_post, x, bias, dX, dH_res,
+                                dH_post, dx, dbias, workspace);
   return launched("mhc_h_post_bda_bwd");
 }
 
@@ -419,11 +449,14 @@ mhc_status mhc_stream_mix_fwd(void *stream, int64_t tokens, int32_t n, int64_t C
   v.dims(tokens, n, C, act);
   if (!v.ok()) return v.status();
   if (tokens == 0) return MHC_OK;
-  v.in(X, tokens * 4 * C * esz(act), "X");
-  v.in(M, tokens * 64, "M");
-  v.out(out, tokens * 4 * C * esz(act), "out");
+  v.in(X, tokens * n * C * esz(act), "X");
+  v.in(M, tokens * n * n * 4, "M");
+  v.out(out, tokens * n * C * esz(act), "out");
   if (v.finish() != MHC_OK) return v.status();
-  mhc::launch_stream_mix_fwd((hipStream_t)stream, act == MHC_F32, tokens, C, X, M, out);
+  if (n == 4)
+    mhc::launch_stream_mix_fwd((hipStream_t)stream, act == MHC_F32, tokens, C, X, M, out);
+  else
+    mhc::glaunch_stream_mix_fwd((hipStream_t)stream, act == MHC_F32, n, tokens, C, X, M, out);
   return launched("mhc_stream_mix_fwd");
 }
 
@@ -433,13 +466,16 @@ mhc_status mhc_stream_mix_bwd(void *stream, int64_t tokens, int32_t n, int64_t C
   v.dims(tokens, n, C, act);
   if (!v.ok()) return v.status();
   if (tokens == 0) return MHC_OK;
-  v.in(G, tokens * 4 * C * esz(act), "G");
-  v.in(X, tokens * 4 * C * esz(act), "X");
-  v.in(M, tokens * 64, "M");
-  v.out(dX, tokens * 4 * C * esz(act), "dX");
-  v.out(dM, tokens * 64, "dM");
+  v.in(G, tokens * n * C * esz(act), "G");
+  v.in(X, tokens * n * C * esz(act), "X");
+  v.in(M, tokens * n * n * 4, "M");
+  v.out(dX, tokens * n * C * esz(act), "dX");
+  v.out(dM, tokens * n * n * 4, "dM");
   if (v.finish() != MHC_OK) return v.status();
-  mhc::launch_stream_mix_bwd((hipStream_t)stream, act == MHC_F32, tokens, C, G, X, M, dX, dM);
+  if (n == 4)
+    mhc::launch_stream_mix_bwd((hipStream_t)stream, act == MHC_F32, tokens, C, G, X, M, dX, dM);
+  else
+    mhc::glaunch_stream_mix_bwd((hipStream_t)stream, act == MHC_F32, n, tokens, C, G, X, M, dX, dM);
   return launched("mhc_stream_mix_bwd");
 }
 
@@ -450,10 +486,13 @@ mhc_status mhc_stream_distribute_fwd(void *stream, int64_t tokens, int32_t n, in
   if (!v.ok()) return v.status();
   if (tokens == 0) return MHC_OK;
   v.in(x, tokens * C * esz(act), "x");
-  v.in(H_post, tokens * 16, "H_post");
-  v.out(out, tokens * 4 * C * esz(act), "out");
+  v.in(H_post, tokens * n * 4, "H_post");
+  v.out(out, tokens * n * C * esz(act), "out");
   if (v.finish() != MHC_OK) return v.status();
-  mhc::launch_stream_distribute_fwd((hipStream_t)stream, act == MHC_F32, tokens, C, x, H_post, out);
+  if (n == 4)
+    mhc::launch_stream_distribute_fwd((hipStream_t)stream, act == MHC_F32, tokens, C, x, H_post, out);
+  else
+    mhc::glaunch_stream_distribute_fwd((hipStream_t)stream, act == MHC_F32, n, tokens, C, x, H_post, out);
   return launched("mhc_stream_distribute_fwd");
 }
 
@@ -464,13 +503,17 @@ mhc_status mhc_stream_distribute_bwd(void *stream, int64_t tokens, int32_t n, in
   v.dims(tokens, n, C, act);
   if (!v.ok()) return v.status();
   if (tokens == 0) return MHC_OK;
-  v.in(G, tokens * 4 * C * esz(act), "G");
+  v.in(G, tokens * n * C * esz(act), "G");
   v.in(x, tokens * C * esz(act), "x");
-  v.in(H_post, tokens * 16, "H_post");
+  v.in(H_post, tokens * n * 4, "H_post");
   v.out(dx, tokens * C * esz(act), "dx");
-  v.out(dH_post, tokens * 16, "dH_post");
+  v.out(dH_post, tokens * n * 4, "dH_post");
   if (v.finish() != MHC_OK) return v.status();
-  mhc::launch_stream_distribute_bwd((hipStream_t)stream, act == MHC_F32, tokens, C, G, x, H_post, dx, dH_post);
+  if (n == 4)
+    mhc::launch_stream_distribute_bwd((hipStream_t)stream, act == MHC_F32, tokens, C, G, x, H_post, dx, dH_post);
+  else
+    mhc::glaunch_stream_distribute_bwd((hipStream_t)stream, act == MHC_F32, n, tokens, C, G, x, H_post, dx,
+                                       dH_post);
   return launched("mhc_stream_distribute_bwd");
 }
 
@@ -481,18 +524,21 @@ mhc_status mhc_h_aggregate_static_fwd(void *stream, int64_t tokens, int32_t n, i
   v.dims(tokens, n, C, act);
   if (!v.ok()) return v.status();
   if (tokens == 0) return MHC_OK;
-  v.in(X, tokens * 4 * C * esz(act), "X");
-  v.in(H_pre, 16, "H_pre");
+  v.in(X, tokens * n * C * esz(act), "X");
+  v.in(H_pre, n * 4, "H_pre");
   v.out(out, tokens * C * esz(act), "out");
   if (v.finish() != MHC_OK) return v.status();
-  mhc::launch_h_aggregate_fwd((hipStream_t)stream, act == MHC_F32, tokens, C, X, H_pre, out, 0);
+  if (n == 4)
+    mhc::launch_h_aggregate_fwd((hipStream_t)stream, act == MHC_F32, tokens, C, X, H_pre, out, 0);
+  else
+    mhc::glaunch_h_aggregate_fwd((hipStream_t)stream, act == MHC_F32, n, tokens, C, X, H_pre, out, 0);
   return launched("mhc_h_aggregate_static_fwd");
 }
 
 size_t mhc_h_aggregate_static_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
   (void)act;
-  if (tokens <= 0 || n != 4 || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
-  return mhc::h_aggregate_static_bwd_ws(tokens);
+  if (tokens <= 0 || n < 1 || n > mhc::kMaxN || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
+  return n == 4 ? mhc::h_aggregate_static_bwd_ws(tokens) : mhc::gh_aggregate_static_bwd_ws(n, tokens);
 }
 
 mhc_status mhc_h_aggregate_static_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
@@ -504,19 +550,23 @@ mhc_status mhc_h_aggregate_static_bwd(void *stream, int64_t tokens, int32_t n, i
   if (!v.ok()) return v.status();
   const hipStream_t s = (hipStream_t)stream;
   if (tokens == 0) {
-    v.out(dH_pre, 16, "dH_pre");
+    v.out(dH_pre, n * 4, "dH_pre");
     if (v.finish() != MHC_OK) return v.status();
-    return zero_f32(s, dH_pre, 4) ? launched("mhc_h_aggregate_static_bwd") : MHC_OK;
+    return zero_f32(s, dH_pre, n) ? launched("mhc_h_aggregate_static_bwd") : MHC_OK;
   }
   v.in(g, tokens * C * esz(act), "g");
-  v.in(X, tokens * 4 * C * esz(act), "X");
-  v.in(H_pre, 16, "H_pre");
-  v.out(dX, tokens * 4 * C * esz(act), "dX");
-  v.out(dH_pre, 16, "dH_pre");
-  v.workspace(workspace, workspace_bytes, mhc::h_aggregate_static_bwd_ws(tokens));
+  v.in(X, tokens * n * C * esz(act), "X");
+  v.in(H_pre, n * 4, "H_pre");
+  v.out(dX, tokens * n * C * esz(act), "dX");
+  v.out(dH_pre, n * 4, "dH_pre");
+  v.workspace(workspace, workspace_bytes, n == 4 ? mhc::h_aggregate_static_bwd_ws(tokens) : mhc::gh_aggregate_static_bwd_ws(n, tokens));
   if (v.finish() != MHC_OK) return v.status();
-  mhc::launch_h_aggregate_static_bwd(s, act == MHC_F32, tokens, C, g, X, H_pre, dX, accumulate_dX != 0,
-                                     dH_pre, workspace);
+  if (n == 4)
+    mhc::launch_h_aggregate_static_bwd(s, act == MHC_F32, tokens, C, g, X, H_pre, dX, accumulate_dX != 0,
+                                       dH_pre, workspace);
+  else
+    mhc::glaunch_h_aggregate_static_bwd(s, act == MHC_F32, n, tokens, C, g, X, H_pre, dX, accumulate_dX != 0,
+                                        dH_pre, workspace);
   return launched("mhc_h_aggregate_static_bwd");
 }
 
@@ -537,23 +587,30 @@ mhc_status mhc_pre_fwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_d
   v.iters(iters);
   if (!v.ok()) return v.status();
   if (tokens == 0) return MHC_OK;
-  const int64_t K = 4 * C;
+  const int64_t K = (int64_t)n * C;
+  const int64_t J = (int64_t)n * n + 2 * n;
   v.in(X, tokens * K * esz(act), "X");
   v.in(W, K * J * 4, "W");
   v.in(alpha, 12, "alpha", true);
   v.in(hbias, J * 4, "hbias", true);
-  v.out(H_pre, tokens * 16, "H_pre");
-  v.out(H_post, tokens * 16, "H_post");
-  v.out(H_res, tokens * 64, "H_res");
-  v.out(H_res_logits, tokens * 64, "H_res_logits");
-  v.out(saved, tokens * MHC_SAVED_STRIDE * 4, "saved", true);
+  v.out(H_pre, tokens * n * 4, "H_pre");
+  v.out(H_post, tokens * n * 4, "H_post");
+  v.out(H_res, tokens * n * n * 4, "H_res");
+  v.out(H_res_logits, tokens * n * n * 4, "H_res_logits");
+  v.out(saved, tokens * mhc::saved_stride(n) * 4, "saved", true);
   v.out(agg, tokens * C * esz(act), "agg");
-  v.workspace(workspace, workspace_bytes, mhc::proj_fwd_ws(tokens, C, act == MHC_F32));
+  v.workspace(workspace, workspace_bytes, n == 4 ? mhc::proj_fwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_fwd_ws(n, tokens));
   if (v.finish() != MHC_OK) return v.status();
   const hipStream_t s = (hipStream_t)stream;
-  mhc::launch_proj_fwd(s, act == MHC_F32, tokens, C, X, W, alpha, hbias, rms_eps, H_pre, H_post,
-                       H_res_logits, saved, H_res, iters, eps, workspace);
-  mhc::launch_h_aggregate_fwd(s, act == MHC_F32, tokens, C, X, H_pre, agg);
+  if (n == 4) {
+    mhc::launch_proj_fwd(s, act == MHC_F32, tokens, C, X, W, alpha, hbias, rms_eps, H_pre, H_post,
+                         H_res_logits, saved, H_res, iters, eps, workspace);
+    mhc::launch_h_aggregate_fwd(s, act == MHC_F32, tokens, C, X, H_pre, agg);
+  } else {
+    mhc::glaunch_proj_fwd(s, act == MHC_F32, n, tokens, C, X, W, alpha, hbias, rms_eps, H_pre, H_post,
+                          H_res_logits, saved, H_res, iters, eps, workspace);
+    mhc::glaunch_h_aggregate_fwd(s, act == MHC_F32, n, tokens, C, X, H_pre, agg, n);
+  }
   return launched("mhc_pre_fwd");
 }
 
@@ -619,25 +676,33 @@ mhc_status mhc_pre_rmsnorm_fwd(void *stream, int64_t tokens, int32_t n, int64_t 
   v.iters(iters);
   if (!v.ok()) return v.status();
   if (tokens == 0) return MHC_OK;
-  const int64_t K = 4 * C;
+  const int64_t K = (int64_t)n * C;
+  const int64_t J = (int64_t)n * n + 2 * n;
   v.in(X, tokens * K * esz(act), "X");
   v.in(W, K * J * 4, "W");
   v.in(alpha, 12, "alpha", true);
   v.in(hbias, J * 4, "hbias", true);
   v.in(gamma, C * 4, "gamma", true);
-  v.out(H_pre, tokens * 16, "H_pre");
-  v.out(H_post, tokens * 16, "H_post");
-  v.out(H_res, tokens * 64, "H_res");
-  v.out(H_res_logits, tokens * 64, "H_res_logits");
-  v.out(saved, tokens * MHC_SAVED_STRIDE * 4, "saved", true);
+  v.out(H_pre, tokens * n * 4, "H_pre");
+  v.out(H_post, tokens * n * 4, "H_post");
+  v.out(H_res, tokens * n * n * 4, "H_res");
+  v.out(H_res_logits, tokens * n * n * 4, "H_res_logits");
+  v.out(saved, tokens * mhc::saved_stride(n) * 4, "saved", true);
   v.out(agg, tokens * C * esz(act), "agg");
   v.out(normed, tokens * C * esz(act), "normed");
-  v.workspace(workspace, workspace_bytes, mhc::proj_fwd_ws(tokens, C, act == MHC_F32));
+  v.workspace(workspace, workspace_bytes, n == 4 ? mhc::proj_fwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_fwd_ws(n, tokens));
   if (v.finish() != MHC_OK) return v.status();
   const hipStream_t s = (hipStream_t)stream;
-  mhc::launch_proj_fwd(s, act == MHC_F32, tokens, C, X, W, alpha, hbias, rms_eps, H_pre, H_post,
-                       H_res_logits, saved, H_res, iters, eps, workspace);
-  mhc::launch_h_aggregate_rmsnorm_fwd(s, act == MHC_F32, tokens, C, X, H_pre, gamma, norm_eps, agg, normed);
+  if (n == 4) {
+    mhc::launch_proj_fwd(s, act == MHC_F32, tokens, C, X, W, alpha, hbias, rms_eps, H_pre, H_post,
+                         H_res_logits, saved, H_res, iters, eps, workspace);
+    mhc::launch_h_aggregate_rmsnorm_fwd(s, act == MHC_F32, tokens, C, X, H_pre, gamma, norm_eps, agg, normed);
+  } else {  // other n: aggregate, then the norm of the stored agg (same result, one more pass over agg)
+    mhc::glaunch_proj_fwd(s, act == MHC_F32, n, tokens, C, X, W, alpha, hbias, rms_eps, H_pre, H_post,
+                          H_res_logits, saved, H_res, iters, eps, workspace);
+    mhc::glaunch_h_aggregate_fwd(s, act == MHC_F32, n, tokens, C, X, H_pre, agg, n);
+    mhc::launch_rmsnorm_fwd(s, act == MHC_F32, tokens, C, agg, gamma, norm_eps, normed);
+  }
   return launched("mhc_pre_rmsnorm_fwd");
 }
 
@@ -660,7 +725,8 @@ mhc_status mhc_pre_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_d
   if ((post_G == nullptr) != (post_H_res == nullptr))
     v.fail(MHC_ERR_ARG, "post_G and post_H_res must be given together");
   if (!v.ok()) return v.status();
-  const int64_t K = 4 * C;
+  const int64_t K = (int64_t)n * C;
+  const int64_t J = (int64_t)n * n + 2 * n;
   const hipStream_t s = (hipStream_t)stream;
   if (tokens == 0) {
     v.out(dW, K * J * 4, "dW", true);
@@ -671,24 +737,24 @@ mhc_status mhc_pre_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_d
     return any ? launched("mhc_pre_bwd") : MHC_OK;
   }
   v.in(g, tokens * C * esz(act), "g");
-  v.in(dH_post, tokens * 16, "dH_post");
-  v.in(dH_res, tokens * 64, "dH_res");
+  v.in(dH_post, tokens * n * 4, "dH_post");
+  v.in(dH_res, tokens * n * n * 4, "dH_res");
   v.in(X, tokens * K * esz(act), "X");
   v.in(W, K * J * 4, "W");
   v.in(alpha, 12, "alpha", true);
-  v.in(saved, tokens * MHC_SAVED_STRIDE * 4, "saved");
-  v.in(H_pre, tokens * 16, "H_pre");
-  v.in(H_post, tokens * 16, "H_post");
-  v.in(H_res_logits, tokens * 64, "H_res_logits");
+  v.in(saved, tokens * mhc::saved_stride(n) * 4, "saved");
+  v.in(H_pre, tokens * n * 4, "H_pre");
+  v.in(H_post, tokens * n * 4, "H_post");
+  v.in(H_res_logits, tokens * n * n * 4, "H_res_logits");
   v.in(post_G, tokens * K * esz(act), "post_G", true);
-  v.in(post_H_res, tokens * 64, "post_H_res", true);
+  v.in(post_H_res, tokens * n * n * 4, "post_H_res", true);
   v.out(dX, tokens * K * esz(act), "dX");
   v.out(dW, K * J * 4, "dW", true);
   v.out(dalpha, 12, "dalpha", true);
   v.out(dhbias, J * 4, "dhbias", true);
-  v.out(dH_pre_out, tokens * 16, "dH_pre_out", true);
-  v.out(dlogits_out, tokens * 64, "dlogits_out", true);
-  v.workspace(workspace, workspace_bytes, mhc::proj_bwd_ws(tokens, C, act == MHC_F32));
+  v.out(dH_pre_out, tokens * n * 4, "dH_pre_out", true);
+  v.out(dlogits_out, tokens * n * n * 4, "dlogits_out", true);
+  v.workspace(workspace, workspace_bytes, n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_bwd_ws(n, tokens, C));
   if (v.finish() != MHC_OK) return v.status();
   mhc::ProjBwdArgs a{};
   a.f32 = act == MHC_F32; a.N = tokens; a.C = C; a.X = X; a.W = W; a.alpha = alpha; a.saved = saved;
@@ -697,7 +763,10 @@ mhc_status mhc_pre_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_d
   a.accumulate = accumulate_dX != 0; a.dW = dW; a.dalpha = dalpha; a.dhbias = dhbias;
   a.dH_pre_out = dH_pre_out; a.dL_out = dlogits_out; a.ws = workspace;
   a.post_G = post_G; a.post_H_res = post_H_res;
-  mhc::launch_proj_bwd(s, a);
+  if (n == 4)
+    mhc::launch_proj_bwd(s, a);
+  else
+    mhc::glaunch_proj_bwd(s, n, a);
   return launched("mhc_pre_bwd");
 }
 

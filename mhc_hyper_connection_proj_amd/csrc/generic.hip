@@ -1,0 +1,959 @@
+// generic.hip -- the whole mHC path for a stream count n other than 4
+// (1 <= n <= 8), on straightforward kernels templated on n.
+//
+// The kernels for n = 4 (proj.hip, streams.hip, sinkhorn.hip) are laid out
+// for that n: the 4x4 mix and the 24 projection columns live in registers
+// and the MFMA tiles hold exactly one column tile.  The pages' kernels take
+// n at run time (rwkv-ops reads it from the tensor shape), so the same
+// operations are provided here for any n up to 8, with the same
+// definitions, layouts, determinism (fixed-order reductions, no atomics)
+// and boundary checks, but simpler, less tuned kernels:
+//  * projection forward: split-K over 8 slices, fp32 MFMA (32x32x2) on the
+//    activations converted exactly to fp32 and W read directly from its
+//    [K][J] layout, ceil(J/32) column tiles; a per-token finalize sums the
+//    slices in order and applies RMS, gains, sigmoid and Sinkhorn;
+//  * projection backward: a per-token kernel (sigmoid / Sinkhorn backward,
+//    dp = r alpha dzh and the RMS coefficient), then a VALU kernel with one
+//    thread per k that owns W's row k and its dW row, walking a token block;
+//  * Sinkhorn: one n x n matrix per thread; the backward replays the
+//    forward from checkpoints spaced ~sqrt(2 iters) half-steps apart, so it
+//    needs no storage beyond registers;
+//  * streaming ops: one workgroup per token, 8-channel groups per thread,
+//    per-token sums lane -> wave -> workgroup in fixed order.
+#include <algorithm>
+
+#include "device.h"
+#include "internal.h"
+
+namespace mhc {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(16))) float gf32x16;
+
+// h_post_bda parts, as in the n = 4 kernels: the whole op, its H_res mix
+// alone (stream mix), its H_post distribution alone (stream distribute).
+enum : int { kPostFull = 0, kPostMix = 1, kPostDist = 2 };
+
+template <int NS> struct Dim {
+  static constexpr int J = NS * NS + 2 * NS;   // controller outputs
+  static constexpr int JT = (J + 31) / 32;     // 32-column MFMA tiles
+  static constexpr int PS = J + 1;             // partial row: x @ W, then sum x^2
+};
+
+constexpr int kGSplitK = 8;   // k slices of the forward projection
+constexpr int kGTok = 32;     // tokens per forward workgroup (one MFMA tile)
+constexpr int kGBwdK = 256;   // k per backward workgroup (one per thread)
+constexpr int kGMaxTB = 16;   // at most this many token blocks in the backward
+
+// ------------------------------------------------------------------ helpers
+template <typename T> struct Ld;
+template <> struct Ld<float> {
+  static __device__ __forceinline__ float one(const float *p) { return *p; }
+};
+template <> struct Ld<bf16_t> {
+  static __device__ __forceinline__ float one(const bf16_t *p) { return __uint_as_float((uint32_t)*p << 16); }
+};
+
+template <typename T> __device__ __forceinline__ void st_one(T *p, float v);
+template <> __device__ __forceinline__ void st_one<float>(float *p, float v) { *p = v; }
+template <> __device__ __forceinline__ void st_one<bf16_t>(bf16_t *p, float v) {
+  const __bf16 h = (__bf16)v;
+  *p = __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float sigm(float v) { return 1.0f / (1.0f + __expf(-v)); }
+
+// Sum of NV per-thread values over a workgroup of at most 512 threads; the
+// totals go to every thread.  Fixed order: wave DPP tree, then waves in order.
+template <int NV>
+__device__ __forceinline__ void gblock_sum(float v[NV], float (*red)[NV]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) v[k] = wave_sum(v[k]);
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) red[wave][k] = v[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    float s = 0.f;
+    for (int w = 0; w < nw; ++w) s += red[w][k];
+    v[k] = s;
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------ Sinkhorn, one matrix per thread
+template <int NS>
+__device__ __forceinline__ void sk_half(float m[NS * NS], int h, float eps) {
+  if ((h & 1) == 0) {
+#pragma unroll
+    for (int a = 0; a < NS; ++a) {
+      float s = 0.f;
+#pragma unroll
+      for (int b = 0; b < NS; ++b) s += m[a * NS + b];
+      const float d = 1.0f / (s + eps);
+#pragma unroll
+      for (int b = 0; b < NS; ++b) m[a * NS + b] *= d;
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < NS; ++b) {
+      float s = 0.f;
+#pragma unroll
+      for (int a = 0; a < NS; ++a) s += m[a * NS + b];
+      const float d = 1.0f / (s + eps);
+#pragma unroll
+      for (int a = 0; a < NS; ++a) m[a * NS + b] *= d;
+    }
+  }
+}
+
+// Reverse of half-step h given its input state m (left unchanged): dm := d(input).
+// For a row pass with line sum s_a, d_a = 1/(s_a + eps), M' = M d_a:
+//   dM[a][b] = d_a (dM'[a][b] - sum_b' dM'[a][b'] M'[a][b'])
+//            = d_a (sum_b' (dM'[a][b] - dM'[a][b']) M'[a][b'] + dM'[a][b] eps d_a)
+// using 1 - sum_b' M'[a][b'] = eps d_a.  The second form has no cancellation
+// when the line is nearly normalised (with one stream the first form loses
+// everything but eps d_a of dM'); a column pass is the same over columns.
+template <int NS>
+__device__ __forceinline__ void sk_half_bwd(const float m[NS * NS], float dm[NS * NS], int h, float eps) {
+  const bool rows = (h & 1) == 0;
+#pragma unroll
+  for (int a = 0; a < NS; ++a) {
+    // line a: elements e(b) = a*NS + b (row pass) or b*NS + a (column pass)
+    float s = 0.f;
+#pragma unroll
+    for (int b = 0; b < NS; ++b) s += m[rows ? a * NS + b : b * NS + a];
+    const float d = 1.0f / (s + eps);
+    float mp[NS], g[NS], o[NS];
+#pragma unroll
+    for (int b = 0; b < NS; ++b) {
+      const int e = rows ? a * NS + b : b * NS + a;
+      mp[b] = m[e] * d;
+      g[b] = dm[e];
+    }
+#pragma unroll
+    for (int b = 0; b < NS; ++b) {
+      float acc = g[b] * (eps * d);
+#pragma unroll
+      for (int bp = 0; bp < NS; ++bp) acc += (g[b] - g[bp]) * mp[bp];
+      o[b] = d * acc;
+    }
+#pragma unroll
+    for (int b = 0; b < NS; ++b) dm[rows ? a * NS + b : b * NS + a] = o[b];
+  }
+}
+
+template <int NS>
+__device__ __forceinline__ void sk_exp(const float *L, float m[NS * NS]) {
+#pragma unroll
+  for (int e = 0; e < NS * NS; ++e) m[e] = __expf(L[e]);
+}
+
+template <int NS>
+__device__ void sk_forward(const float *L, float m[NS * NS], int iters, float eps) {
+  sk_exp<NS>(L, m);
+  for (int h = 0; h < 2 * iters; ++h) sk_half<NS>(m, h, eps);
+}
+
+// dL for logits L (global, NS*NS) given dH in dm; dm is overwritten with dL.
+// Checkpoints every `seg` half-steps: the state at a segment's start is
+// replayed from exp(L), each half-step's input inside the segment from the
+// segment start, so the cost is ~H^2/(2 seg) + H seg/2 half-steps.
+template <int NS>
+__device__ void sk_backward(const float *L, float dm[NS * NS], int iters, float eps) {
+  const int H = 2 * iters;
+  int seg = 1;
+  while (seg * seg < H) ++seg;
+  float ms[NS * NS], m[NS * NS];
+  const int nseg = (H + seg - 1) / seg;
+  for (int sgi = nseg - 1; sgi >= 0; --sgi) {
+    const int h0 = sgi * seg, h1 = min(H, h0 + seg);
+    sk_exp<NS>(L, ms);
+    for (int h = 0; h < h0; ++h) sk_half<NS>(ms, h, eps);
+    for (int h = h1 - 1; h >= h0; --h) {
+#pragma unroll
+      for (int e = 0; e < NS * NS; ++e) m[e] = ms[e];
+      for (int hh = h0; hh < h; ++hh) sk_half<NS>(m, hh, eps);
+      sk_half_bwd<NS>(m, dm, h, eps);
+    }
+  }
+  sk_exp<NS>(L, m);
+#pragma unroll
+  for (int e = 0; e < NS * NS; ++e) dm[e] *= m[e];
+}
+
+template <int NS>
+__global__ __launch_bounds__(64) void gsinkhorn_fwd_kernel(int64_t count, const float *__restrict__ L,
+                                                          float *__restrict__ H, int iters, float eps) {
+  const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (i >= count) return;
+  float m[NS * NS];
+  sk_forward<NS>(L + i * NS * NS, m, iters, eps);
+#pragma unroll
+  for (int e = 0; e < NS * NS; ++e) H[i * NS * NS + e] = m[e];
+}
+
+template <int NS>
+__global__ __launch_bounds__(64) void gsinkhorn_bwd_kernel(int64_t count, const float *__restrict__ dH,
+                                                          const float *__restrict__ L, float *__restrict__ dL,
+                                                          int iters, float eps) {
+  const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (i >= count) return;
+  float dm[NS * NS];
+#pragma unroll
+  for (int e = 0; e < NS * NS; ++e) dm[e] = dH[i * NS * NS + e];
+  sk_backward<NS>(L + i * NS * NS, dm, iters, eps);
+#pragma unroll
+  for (int e = 0; e < NS * NS; ++e) dL[i * NS * NS + e] = dm[e];
+}
+
+// ------------------------------------------------------------------ streaming ops
+// One workgroup per token (per TG tokens for the dbias partials); thread
+// owns 8-channel groups g = tid, tid + TPB, ...
+template <typename T, int NS>
+__global__ __launch_bounds__(256) void gagg_fwd_kernel(const T *__restrict__ X, const float *__restrict__ Hpre,
+                                                      int64_t hs, T *__restrict__ out, int64_t C) {
+  const int64_t t = blockIdx.x;
+  const int64_t G = C / 8;
+  float h[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) h[i] = Hpre[t * hs + i];
+  for (int64_t g = threadIdx.x; g < G; g += blockDim.x) {
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      float v[8];
+      Io8<T>::load(X + (t * NS + i) * C + 8 * g, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] += h[i] * v[e];
+    }
+    Io8<T>::store(out + t * C + 8 * g, o);
+  }
+}
+
+// dH_pre rows [N][NS] (dHrow), optionally dX (+)= H_pre g.
+template <typename T, int NS>
+__global__ __launch_bounds__(256) void gagg_bwd_kernel(const T *__restrict__ gr, const T *__restrict__ X,
+                                                      const float *__restrict__ Hpre, int64_t hs,
+                                                      T *__restrict__ dX, float *__restrict__ dHrow, int64_t C,
+                                                      bool WRITE_DX, bool ACCUM) {
+  __shared__ float red[4][NS];
+  const int64_t t = blockIdx.x;
+  const int64_t G = C / 8;
+  float h[NS], acc[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) { h[i] = Hpre[t * hs + i]; acc[i] = 0.f; }
+  for (int64_t g = threadIdx.x; g < G; g += blockDim.x) {
+    float gv[8];
+    Io8<T>::load(gr + t * C + 8 * g, gv);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      float v[8];
+      Io8<T>::load(X + (t * NS + i) * C + 8 * g, v);
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += gv[e] * v[e];
+      acc[i] += s;
+      if (WRITE_DX) {
+        float d[8];
+        if (ACCUM) Io8<T>::load(dX + (t * NS + i) * C + 8 * g, d);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d[e] = (ACCUM ? d[e] : 0.f) + h[i] * gv[e];
+        Io8<T>::store(dX + (t * NS + i) * C + 8 * g, d);
+      }
+    }
+  }
+  gblock_sum<NS>(acc, red);
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) dHrow[t * NS + i] = acc[i];
+  }
+}
+
+// Column sums of rows[R][NC] in a fixed order: block b sums column b, thread
+// i takes rows i, i + 256, ..., then the workgroup tree.
+__global__ __launch_bounds__(256) void gcol_sum_kernel(const float *__restrict__ rows, float *__restrict__ out,
+                                                      int64_t R, int NC) {
+  __shared__ float red[4][1];
+  const int col = blockIdx.x;
+  float s[1] = {0.f};
+  for (int64_t r = threadIdx.x; r < R; r += 256) s[0] += rows[r * NC + col];
+  gblock_sum<1>(s, red);
+  if (threadIdx.x == 0) out[col] = s[0];
+}
+
+// h_post_bda forward and its halves (modes as the n = 4 kernels).
+template <typename T, int NS, int MODE>
+__global__ __launch_bounds__(256) void gpost_fwd_kernel(const T *__restrict__ X, const float *__restrict__ Hr,
+                                                       const float *__restrict__ Hp, const T *__restrict__ x,
+                                                       const T *__restrict__ bias, T *__restrict__ out, int64_t C) {
+  const bool HAS_BIAS = bias != nullptr;
+  const int64_t t = blockIdx.x;
+  const int64_t G = C / 8;
+  for (int64_t g = threadIdx.x; g < G; g += blockDim.x) {
+    float xb[8], xv[NS][8];
+    if (MODE != kPostMix) {
+      Io8<T>::load(x + t * C + 8 * g, xb);
+      if (HAS_BIAS) {
+        float b[8];
+        Io8<T>::load(bias + 8 * g, b);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xb[e] += b[e];
+      }
+    }
+    if (MODE != kPostDist) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) Io8<T>::load(X + (t * NS + j) * C + 8 * g, xv[j]);
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (MODE != kPostDist) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          const float w = Hr[t * NS * NS + j * NS + i];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] += w * xv[j][e];
+        }
+      }
+      if (MODE != kPostMix) {
+        const float hp = Hp[t * NS + i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] += hp * xb[e];
+      }
+      Io8<T>::store(out + (t * NS + i) * C + 8 * g, o);
+    }
+  }
+}
+
+// h_post_bda backward and its halves.  Per token: dX[j] = sum_i H_res[j][i]
+// G[i] (WRITE_DX), dH_res[j][i] = <X_j, G_i> (MODE != dist), dH_post[i] =
+// <G_i, x + bias> and dx = sum_i H_post[i] G_i (MODE != mix).  DBIAS: TG
+// tokens per workgroup; each thread adds its groups' dx into the workgroup's
+// partial row part[blockIdx.x][C] (owned by this thread alone: no atomics).
+template <typename T, int NS, int MODE>
+__global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr, const T *__restrict__ X,
+                                                       const float *__restrict__ Hr, const float *__restrict__ Hp,
+                                                       const T *__restrict__ x, const T *__restrict__ bias,
+                                                       T *__restrict__ dX, float *__restrict__ dHr,
+                                                       float *__restrict__ dHp, T *__restrict__ dx,
+                                                       float *__restrict__ part, int64_t N, int64_t C, int TG) {
+  const bool HAS_BIAS = bias != nullptr, WRITE_DX = dX != nullptr, DBIAS = part != nullptr;
+  constexpr int NR = (MODE == kPostDist ? 0 : NS * NS) + (MODE == kPostMix ? 0 : NS);
+  __shared__ float red[4][NR];
+  const int64_t G = C / 8;
+  const int64_t t0 = (int64_t)blockIdx.x * TG;
+  const int64_t t1 = min(t0 + (int64_t)TG, N);
+  for (int64_t t = t0; t < t1; ++t) {
+    float acc[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) acc[k] = 0.f;
+    for (int64_t g = threadIdx.x; g < G; g += blockDim.x) {
+      float gv[NS][8];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) Io8<T>::load(Gr + (t * NS + i) * C + 8 * g, gv[i]);
+      if (MODE != kPostDist) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          float xv[8];
+          Io8<T>::load(X + (t * NS + j) * C + 8 * g, xv);
+#pragma unroll
+          for (int i = 0; i < NS; ++i) {
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s += xv[e] * gv[i][e];
+            acc[j * NS + i] += s;
+          }
+          if (WRITE_DX) {
+            float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+              const float w = Hr[t * NS * NS + j * NS + i];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) d[e] += w * gv[i][e];
+            }
+            Io8<T>::store(dX + (t * NS + j) * C + 8 * g, d);
+          }
+        }
+      }
+      if (MODE != kPostMix) {
+        constexpr int off = MODE == kPostDist ? 0 : NS * NS;
+        float xb[8], o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        Io8<T>::load(x + t * C + 8 * g, xb);
+        if (HAS_BIAS) {
+          float b[8];
+          Io8<T>::load(bias + 8 * g, b);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xb[e] += b[e];
+        }
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          const float hp = Hp[t * NS + i];
+          float s = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            s += gv[i][e] * xb[e];
+            o[e] += hp * gv[i][e];
+          }
+          acc[off + i] += s;
+        }
+        Io8<T>::store(dx + t * C + 8 * g, o);
+        if (DBIAS) {
+          float *p = part + (int64_t)blockIdx.x * C + 8 * g;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) p[e] = (t == t0 ? 0.f : p[e]) + o[e];
+        }
+      }
+    }
+    gblock_sum<NR>(acc, red);
+    if (threadIdx.x == 0) {
+      if (MODE != kPostDist) {
+#pragma unroll
+        for (int k = 0; k < NS * NS; ++k) dHr[t * NS * NS + k] = acc[k];
+      }
+      if (MODE != kPostMix) {
+        constexpr int off = MODE == kPostDist ? 0 : NS * NS;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) dHp[t * NS + i] = acc[off + i];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ projection forward
+// Grid: ceil(N / 32) * kGSplitK workgroups of 4 waves; workgroup b takes token
+// block b / kGSplitK and k slice b % kGSplitK; wave w the slice's 64-k chunks
+// w, w + 4, ...  Each chunk is summed from zero on the MFMA and then added to
+// the running sum (two-level blocking), the four waves' sums are added in
+// wave order.  part[slice][t][0..J) = partial x @ W, part[slice][t][J] =
+// partial sum x^2.
+template <typename T, int NS>
+__global__ __launch_bounds__(256) void gproj_partial_kernel(const T *__restrict__ X, const float *__restrict__ W,
+                                                           float *__restrict__ part, int64_t N, int64_t K) {
+  constexpr int J = Dim<NS>::J, JT = Dim<NS>::JT, PS = Dim<NS>::PS;
+  __shared__ float red_p[4][kGTok][PS];
+  const int slice = blockIdx.x % kGSplitK;
+  const int64_t tb = blockIdx.x / kGSplitK;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = lane & 31, h = lane >> 5;
+  const int64_t nch = (K + 63) / 64;
+  const int64_t cps = (nch + kGSplitK - 1) / kGSplitK;
+  const int64_t c_begin = slice * cps;
+  const int64_t c_end = min(nch, c_begin + cps);
+  const int64_t trow = tb * kGTok + row;
+  const bool tvalid = trow < N;
+
+  gf32x16 outer[JT];
+#pragma unroll
+  for (int u = 0; u < JT; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) outer[u][r] = 0.f;
+  float ss = 0.f;
+
+  for (int64_t c = c_begin + wave; c < c_end; c += 4) {
+    const int64_t k0 = c * 64 + 32 * h;  // this lane's 32 k values: k0 .. k0 + 31
+    // K % 8 == 0 and k0 % 32 == 0: an 8-value group is either wholly inside K or wholly past it
+    float a[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (tvalid && k0 + 8 * q < K) {
+        Io8<T>::load(X + trow * K + k0 + 8 * q, a + 8 * q);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[8 * q + e] = 0.f;
+      }
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) s = fmaf(a[e], a[e], s);
+    ss += s;
+#pragma unroll
+    for (int u = 0; u < JT; ++u) {
+      const int col = 32 * u + row;
+      gf32x16 acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const float b = (col < J && k0 + e < K) ? W[(k0 + e) * J + col] : 0.f;
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b, acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) outer[u][r] += acc[r];
+    }
+  }
+  // accumulator layout of a 32x32 MFMA: lane (col, h), register r holds row
+  // 8*(r/4) + 4*h + (r%4), column col.  Sum of squares: the two k halves of a
+  // token's row sit on lanes row and row + 32.
+#pragma unroll
+  for (int u = 0; u < JT; ++u) {
+    const int col = 32 * u + row;
+    if (col < J) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red_p[wave][8 * (r >> 2) + 4 * h + (r & 3)][col] = outer[u][r];
+    }
+  }
+  const float ss_other = __shfl_xor(ss, 32);
+  if (h == 0) red_p[wave][row][J] = ss + ss_other;
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < kGTok * PS; idx += 256) {
+    const int tt = idx / PS, j = idx % PS;
+    const int64_t t = tb * kGTok + tt;
+    if (t >= N) continue;
+    const float v = (red_p[0][tt][j] + red_p[1][tt][j]) + (red_p[2][tt][j] + red_p[3][tt][j]);
+    part[((int64_t)slice * N + t) * PS + j] = v;
+  }
+}
+
+// One thread per token: slices summed in order, then RMS, gains, sigmoid;
+// saved[t] = {r, q, z[0..J), 0...} (stride SS); Sinkhorn when Hres != NULL.
+template <int NS>
+__global__ __launch_bounds__(64) void gproj_finalize_kernel(const float *__restrict__ part, int64_t N, int64_t K,
+                                                           const float *__restrict__ alpha,
+                                                           const float *__restrict__ hbias, float rms_eps,
+                                                           float *__restrict__ Hpre, float *__restrict__ Hpost,
+                                                           float *__restrict__ logits, float *__restrict__ saved,
+                                                           int SS, float *__restrict__ Hres, int iters, float eps) {
+  constexpr int J = Dim<NS>::J, PS = Dim<NS>::PS;
+  const int64_t t = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (t >= N) return;
+  float p[PS];
+#pragma unroll
+  for (int j = 0; j < PS; ++j) p[j] = 0.f;
+  for (int sl = 0; sl < kGSplitK; ++sl) {
+#pragma unroll
+    for (int j = 0; j < PS; ++j) p[j] += part[((int64_t)sl * N + t) * PS + j];
+  }
+  const float q = sqrtf(p[J] / (float)K);
+  const float r = 1.0f / (q + rms_eps);
+  const float a0 = alpha ? alpha[0] : 1.f, a1 = alpha ? alpha[1] : 1.f, a2 = alpha ? alpha[2] : 1.f;
+  float L[NS * NS];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const float z = r * p[j];
+    const float a = j < NS ? a0 : j < 2 * NS ? a1 : a2;
+    const float zh = a * z + (hbias ? hbias[j] : 0.f);
+    if (j < NS)
+      Hpre[t * NS + j] = sigm(zh);
+    else if (j < 2 * NS)
+      Hpost[t * NS + j - NS] = 2.0f * sigm(zh);
+    else
+      L[j - 2 * NS] = zh;
+    if (saved) saved[t * SS + 2 + j] = z;
+  }
+#pragma unroll
+  for (int e = 0; e < NS * NS; ++e) logits[t * NS * NS + e] = L[e];
+  if (saved) {
+    saved[t * SS + 0] = r;
+    saved[t * SS + 1] = q;
+    for (int j = 2 + J; j < SS; ++j) saved[t * SS + j] = 0.f;
+  }
+  if (Hres) {
+    float m[NS * NS];
+    sk_forward<NS>(L, m, iters, eps);
+#pragma unroll
+    for (int e = 0; e < NS * NS; ++e) Hres[t * NS * NS + e] = m[e];
+  }
+}
+
+// ------------------------------------------------------------------ projection backward
+// Per token (one thread): dzh from the saved forward state; rec[t] =
+// {dp[0..J) = r alpha dzh, c_rms = -r sum_j dz_j z_j / (K q) (0 if q == 0)};
+// prm[t] = {dzh[0..J) (dhbias terms), sum_seg dzh z (dalpha terms, 3)}.
+// dH_res and the logits (Sinkhorn backward) replace dL when dL == NULL.
+template <int NS>
+__global__ __launch_bounds__(64) void gproj_bwd_token_kernel(
+    int64_t N, int64_t K, const float *__restrict__ alpha, const float *__restrict__ saved, int SS,
+    const float *__restrict__ Hpre, const float *__restrict__ Hpost, const float *__restrict__ dHpre,
+    const float *__restrict__ dHpost, const float *__restrict__ dL, const float *__restrict__ dHres,
+    const float *__restrict__ logits, int iters, float eps, float *__restrict__ rec, float *__restrict__ prm,
+    float *__restrict__ dL_out) {
+  constexpr int J = Dim<NS>::J;
+  const int64_t t = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (t >= N) return;
+  const float r = saved[t * SS], q = saved[t * SS + 1];
+  const float al[3] = {alpha ? alpha[0] : 1.f, alpha ? alpha[1] : 1.f, alpha ? alpha[2] : 1.f};
+  float dl[NS * NS];
+  if (dL) {
+#pragma unroll
+    for (int e = 0; e < NS * NS; ++e) dl[e] = dL[t * NS * NS + e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < NS * NS; ++e) dl[e] = dHres[t * NS * NS + e];
+    sk_backward<NS>(logits + t * NS * NS, dl, iters, eps);
+  }
+  if (dL_out) {
+#pragma unroll
+    for (int e = 0; e < NS * NS; ++e) dL_out[t * NS * NS + e] = dl[e];
+  }
+  float S = 0.f, da[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    float dzh;
+    int sg;
+    if (j < NS) {
+      const float sv = Hpre[t * NS + j];
+      dzh = dHpre[t * NS + j] * sv * (1.f - sv);
+      sg = 0;
+    } else if (j < 2 * NS) {
+      const float sv = 0.5f * Hpost[t * NS + j - NS];
+      dzh = dHpost[t * NS + j - NS] * 2.f * sv * (1.f - sv);
+      sg = 1;
+    } else {
+      dzh = dl[j - 2 * NS];
+      sg = 2;
+    }
+    const float z = saved[t * SS + 2 + j];
+    const float dz = al[sg] * dzh;
+    S += dz * z;
+    da[sg] += dzh * z;
+    rec[t * (J + 1) + j] = r * dz;
+    prm[t * (J + 3) + j] = dzh;
+  }
+  rec[t * (J + 1) + J] = q > 0.f ? -S * r / ((float)K * q) : 0.f;
+  prm[t * (J + 3) + J] = da[0];
+  prm[t * (J + 3) + J + 1] = da[1];
+  prm[t * (J + 3) + J + 2] = da[2];
+}
+
+// dX and dW.  Grid: (K / 256 k tiles) x (token blocks); thread = one k =
+// i*C + c, holding W[k][0..J) and its dW partial.  For each token of the
+// block (records staged in LDS):
+//   dX[t][k] = (dX_in) + H_pre[t][i] g[t][c] + sum_j dp[t][j] W[k][j]
+//              + c_rms[t] x[t][k] + sum_i' H_res[t][i][i'] G[t][i'][c]
+// all in fp32 with one rounding at the store; dW[k][j] += x[t][k] dp[t][j].
+template <typename T, int NS, bool DW>
+__global__ __launch_bounds__(256) void gproj_bwd_dx_kernel(
+    const T *__restrict__ X, const float *__restrict__ W, const float *__restrict__ rec,
+    const float *__restrict__ Hpre, const T *__restrict__ gr, const T *__restrict__ Gp,
+    const float *__restrict__ Hr, T *__restrict__ dX, float *__restrict__ dwpart, int64_t N, int64_t C,
+    int64_t TB, bool ACCUM) {
+  const bool HAS_G = gr != nullptr, POST = Gp != nullptr;
+  constexpr int J = Dim<NS>::J;
+  constexpr int RT = 16;  // tokens per LDS record stage
+  __shared__ float srec[RT][J + 1];
+  const int64_t K = NS * C;
+  const int64_t k = (int64_t)blockIdx.x * kGBwdK + threadIdx.x;
+  const bool kv = k < K;
+  const int64_t i = kv ? k / C : 0, c = kv ? k % C : 0;
+  float w[J], dw[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    w[j] = kv ? W[k * J + j] : 0.f;
+    dw[j] = 0.f;
+  }
+  const int64_t t0 = (int64_t)blockIdx.y * TB;
+  const int64_t t1 = min(t0 + TB, N);
+  for (int64_t ts = t0; ts < t1; ts += RT) {
+    const int nt = (int)min((int64_t)RT, t1 - ts);
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < nt * (J + 1); idx += blockDim.x)
+      srec[idx / (J + 1)][idx % (J + 1)] = rec[(ts + idx / (J + 1)) * (J + 1) + idx % (J + 1)];
+    __syncthreads();
+    if (kv) {
+      for (int u = 0; u < nt; ++u) {
+        const int64_t t = ts + u;
+        const float xv = Ld<T>::one(X + t * K + k);
+        float acc = ACCUM ? Ld<T>::one(dX + t * K + k) : 0.f;
+        if (HAS_G) acc += Hpre[t * NS + i] * Ld<T>::one(gr + t * C + c);
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          s += srec[u][j] * w[j];
+          if (DW) dw[j] += xv * srec[u][j];
+        }
+        acc += s + srec[u][J] * xv;
+        if (POST) {
+#pragma unroll
+          for (int ip = 0; ip < NS; ++ip) acc += Hr[t * NS * NS + i * NS + ip] * Ld<T>::one(Gp + (t * NS + ip) * C + c);
+        }
+        st_one<T>(dX + t * K + k, acc);
+      }
+    }
+  }
+  if (DW && kv) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) dwpart[((int64_t)blockIdx.y * K + k) * J + j] = dw[j];
+  }
+}
+
+// dW[k][j] = sum over token blocks in block order.
+__global__ __launch_bounds__(256) void gdw_reduce_kernel(const float *__restrict__ part, float *__restrict__ dW,
+                                                        int64_t ntb, int64_t KJ) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= KJ) return;
+  float s = 0.f;
+  for (int64_t b = 0; b < ntb; ++b) s += part[b * KJ + e];
+  dW[e] = s;
+}
+
+// ------------------------------------------------------------------ launch helpers
+#define MHC_NS_DISPATCH(NV, ...)                                   \
+  switch (NV) {                                                    \
+    case 1: { constexpr int NS = 1; __VA_ARGS__; } break;          \
+    case 2: { constexpr int NS = 2; __VA_ARGS__; } break;          \
+    case 3: { constexpr int NS = 3; __VA_ARGS__; } break;          \
+    case 5: { constexpr int NS = 5; __VA_ARGS__; } break;          \
+    case 6: { constexpr int NS = 6; __VA_ARGS__; } break;          \
+    case 7: { constexpr int NS = 7; __VA_ARGS__; } break;          \
+    default: { constexpr int NS = 8; __VA_ARGS__; } break;         \
+  }
+
+int gtpb(int64_t C) {
+  const int64_t G = C / 8;
+  return G <= 64 ? 64 : G <= 128 ? 128 : 256;
+}
+
+inline size_t al256(size_t b) { return (b + 255) / 256 * 256; }
+
+struct GBwdLay {
+  int64_t ntb, tb;
+  size_t rec, prm, dw, dhrow, total;
+};
+
+GBwdLay gbwd_layout(int64_t N, int64_t C, int n) {
+  const int64_t J = (int64_t)n * n + 2 * n, K = (int64_t)n * C;
+  GBwdLay L;
+  L.ntb = std::min<int64_t>(kGMaxTB, std::max<int64_t>(1, (N + 63) / 64));
+  L.tb = (N + L.ntb - 1) / L.ntb;
+  L.rec = al256((size_t)N * (J + 1) * 4);
+  L.prm = al256((size_t)N * (J + 3) * 4);
+  L.dw = al256((size_t)L.ntb * K * J * 4);
+  L.dhrow = al256((size_t)N * n * 4);
+  L.total = L.rec + L.prm + L.dw + L.dhrow;
+  return L;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ public launchers
+int saved_stride(int n) {
+  const int need = 2 + n * n + 2 * n;
+  return need <= 32 ? 32 : (need + 7) / 8 * 8;
+}
+
+void glaunch_sinkhorn_fwd(hipStream_t s, int n, int64_t count, const float *L, float *H, int iters, float eps) {
+  const unsigned b = (unsigned)((count + 63) / 64);
+  MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gsinkhorn_fwd_kernel<NS>), dim3(b), dim3(64), 0, s, count, L, H, iters,
+                                        eps));
+}
+
+void glaunch_sinkhorn_bwd(hipStream_t s, int n, int64_t count, const float *dH, const float *L, float *dL,
+                          int iters, float eps) {
+  const unsigned b = (unsigned)((count + 63) / 64);
+  MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gsinkhorn_bwd_kernel<NS>), dim3(b), dim3(64), 0, s, count, dH, L, dL,
+                                        iters, eps));
+}
+
+void glaunch_h_aggregate_fwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *X,
+                             const float *H_pre, void *out, int64_t hs) {
+  const int tpb = gtpb(C);
+  if (f32)
+    MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gagg_fwd_kernel<float, NS>), dim3((unsigned)N), dim3(tpb), 0, s,
+                                          (const float *)X, H_pre, hs, (float *)out, C))
+  else
+    MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gagg_fwd_kernel<bf16_t, NS>), dim3((unsigned)N), dim3(tpb), 0, s,
+                                          (const bf16_t *)X, H_pre, hs, (bf16_t *)out, C))
+}
+
+template <typename T>
+static void gagg_bwd(hipStream_t s, int n, int64_t N, int64_t C, const void *g, const void *X, const float *H,
+                     int64_t hs, void *dX, bool acc, float *rows) {
+  MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gagg_bwd_kernel<T, NS>), dim3((unsigned)N), dim3(gtpb(C)), 0, s,
+                                        (const T *)g, (const T *)X, H, hs, (T *)dX, rows, C, dX != nullptr,
+                                        dX != nullptr && acc));
+}
+
+void glaunch_h_aggregate_bwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *g, const void *X,
+                             const float *H_pre, void *dX, bool accumulate, float *dH_pre) {
+  if (f32)
+    gagg_bwd<float>(s, n, N, C, g, X, H_pre, n, dX, accumulate, dH_pre);
+  else
+    gagg_bwd<bf16_t>(s, n, N, C, g, X, H_pre, n, dX, accumulate, dH_pre);
+}
+
+size_t gh_aggregate_static_bwd_ws(int n, int64_t N) { return (size_t)N * n * 4; }
+
+void glaunch_h_aggregate_static_bwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *g,
+                                    const void *X, const float *H_pre, void *dX, bool accumulate, float *dH_pre,
+                                    void *ws) {
+  float *rows = (float *)ws;
+  if (f32)
+    gagg_bwd<float>(s, n, N, C, g, X, H_pre, 0, dX, accumulate, rows);
+  else
+    gagg_bwd<bf16_t>(s, n, N, C, g, X, H_pre, 0, dX, accumulate, rows);
+  hipLaunchKernelGGL(gcol_sum_kernel, dim3((unsigned)n), dim3(256), 0, s, rows, dH_pre, N, n);
+}
+
+template <typename T, int MODE>
+static void gpost_fwd(hipStream_t s, int n, int64_t N, int64_t C, const void *X, const float *Hr, const float *Hp,
+                      const void *x, const void *b, void *out) {
+  MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gpost_fwd_kernel<T, NS, MODE>), dim3((unsigned)N), dim3(gtpb(C)), 0, s,
+                                        (const T *)X, Hr, Hp, (const T *)x, (const T *)b, (T *)out, C));
+}
+
+void glaunch_h_post_bda_fwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *X,
+                            const float *H_res, const float *H_post, const void *x, const void *bias, void *out) {
+  if (f32)
+    gpost_fwd<float, kPostFull>(s, n, N, C, X, H_res, H_post, x, bias, out);
+  else
+    gpost_fwd<bf16_t, kPostFull>(s, n, N, C, X, H_res, H_post, x, bias, out);
+}
+
+void glaunch_stream_mix_fwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *X, const float *M,
+                            void *out) {
+  if (f32)
+    gpost_fwd<float, kPostMix>(s, n, N, C, X, M, nullptr, nullptr, nullptr, out);
+  else
+    gpost_fwd<bf16_t, kPostMix>(s, n, N, C, X, M, nullptr, nullptr, nullptr, out);
+}
+
+void glaunch_stream_distribute_fwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *x,
+                                   const float *H_post, void *out) {
+  if (f32)
+    gpost_fwd<float, kPostDist>(s, n, N, C, nullptr, nullptr, H_post, x, nullptr, out);
+  else
+    gpost_fwd<bf16_t, kPostDist>(s, n, N, C, nullptr, nullptr, H_post, x, nullptr, out);
+}
+
+constexpr int kGPostTG = 16;
+
+size_t gh_post_bda_bwd_ws(int64_t N, int64_t C, bool with_dbias) {
+  if (!with_dbias) return 0;
+  const int64_t rows = (N + kGPostTG - 1) / kGPostTG;
+  return (size_t)((rows + kRowSumSlices) * C) * sizeof(float);
+}
+
+// part != NULL: dbias partial rows (TG tokens per workgroup), else one token per workgroup.
+template <typename T, int MODE>
+static void gpost_bwd5(hipStream_t s, int n, int64_t N, int64_t C, const void *G, const void *X, const float *Hr,
+                       const float *Hp, const void *x, const void *b, void *dX, float *dHr, float *dHp, void *dx,
+                       float *part) {
+  const int TG = part ? kGPostTG : 1;
+  const unsigned blocks = (unsigned)((N + TG - 1) / TG);
+  MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gpost_bwd_kernel<T, NS, MODE>), dim3(blocks), dim3(gtpb(C)), 0, s,
+                                        (const T *)G, (const T *)X, Hr, Hp, (const T *)x, (const T *)b, (T *)dX,
+                                        dHr, dHp, (T *)dx, part, N, C, TG));
+}
+
+template <typename T>
+static void gpost_bwd(hipStream_t s, int n, int64_t N, int64_t C, const void *G, const void *X, const float *Hr,
+                      const float *Hp, const void *x, const void *b, void *dX, float *dHr, float *dHp, void *dx,
+                      void *db, void *ws) {
+  if (b && db) {
+    float *part = (float *)ws;
+    gpost_bwd5<T, kPostFull>(s, n, N, C, G, X, Hr, Hp, x, b, dX, dHr, dHp, dx, part);
+    const int64_t rows = (N + kGPostTG - 1) / kGPostTG;
+    launch_rows_sum(s, part, rows, C, part + rows * C, db, sizeof(T) == 2);
+  } else {
+    gpost_bwd5<T, kPostFull>(s, n, N, C, G, X, Hr, Hp, x, b, dX, dHr, dHp, dx, nullptr);
+  }
+}
+
+void glaunch_h_post_bda_bwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *G, const void *X,
+                            const float *H_res, const float *H_post, const void *x, const void *bias, void *dX,
+                            float *dH_res, float *dH_post, void *dx, void *dbias, void *ws) {
+  if (f32)
+    gpost_bwd<float>(s, n, N, C, G, X, H_res, H_post, x, bias, dX, dH_res, dH_post, dx, dbias, ws);
+  else
+    gpost_bwd<bf16_t>(s, n, N, C, G, X, H_res, H_post, x, bias, dX, dH_res, dH_post, dx, dbias, ws);
+}
+
+void glaunch_stream_mix_bwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *G, const void *X,
+                            const float *M, void *dX, float *dM) {
+  if (f32)
+    gpost_bwd5<float, kPostMix>(s, n, N, C, G, X, M, nullptr, nullptr, nullptr, dX, dM, nullptr, nullptr, nullptr);
+  else
+    gpost_bwd5<bf16_t, kPostMix>(s, n, N, C, G, X, M, nullptr, nullptr, nullptr, dX, dM, nullptr, nullptr,
+                                 nullptr);
+}
+
+void glaunch_stream_distribute_bwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *G,
+                                   const void *x, const float *H_post, void *dx, float *dH_post) {
+  if (f32)
+    gpost_bwd5<float, kPostDist>(s, n, N, C, G, nullptr, nullptr, H_post, x, nullptr, nullptr, nullptr, dH_post,
+                                 dx, nullptr);
+  else
+    gpost_bwd5<bf16_t, kPostDist>(s, n, N, C, G, nullptr, nullptr, H_post, x, nullptr, nullptr, nullptr, dH_post,
+                                  dx, nullptr);
+}
+
+size_t gproj_fwd_ws(int n, int64_t N) {
+  const int64_t J = (int64_t)n * n + 2 * n;
+  return al256((size_t)kGSplitK * N * (J + 1) * 4);
+}
+
+void glaunch_proj_fwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *X, const float *W,
+                      const float *alpha, const float *hbias, float rms_eps, float *H_pre, float *H_post,
+                      float *logits, float *saved, float *H_res, int iters, float eps, void *ws) {
+  const int64_t K = (int64_t)n * C;
+  float *part = (float *)ws;
+  const unsigned pb = (unsigned)(((N + kGTok - 1) / kGTok) * kGSplitK);
+  if (f32)
+    MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_partial_kernel<float, NS>), dim3(pb), dim3(256), 0, s,
+                                          (const float *)X, W, part, N, K))
+  else
+    MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_partial_kernel<bf16_t, NS>), dim3(pb), dim3(256), 0, s,
+                                          (const bf16_t *)X, W, part, N, K))
+  const unsigned fb = (unsigned)((N + 63) / 64);
+  MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_finalize_kernel<NS>), dim3(fb), dim3(64), 0, s, part, N, K, alpha,
+                                        hbias, rms_eps, H_pre, H_post, logits, saved, saved_stride(n), H_res,
+                                        iters, eps));
+}
+
+size_t gproj_bwd_ws(int n, int64_t N, int64_t C) { return gbwd_layout(N, C, n).total; }
+
+template <typename T>
+static void gdx(hipStream_t s, int n, const ProjBwdArgs &a, const GBwdLay &L, const float *rec, float *dwp) {
+  const int64_t K = (int64_t)n * a.C;
+  const dim3 grid((unsigned)((K + kGBwdK - 1) / kGBwdK), (unsigned)L.ntb);
+  if (a.dW)
+    MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_bwd_dx_kernel<T, NS, true>), grid, dim3(kGBwdK), 0, s,
+                                          (const T *)a.X, a.W, rec, a.H_pre, (const T *)a.g, (const T *)a.post_G,
+                                          a.post_H_res, (T *)a.dX, dwp, a.N, a.C, L.tb, a.accumulate))
+  else
+    MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_bwd_dx_kernel<T, NS, false>), grid, dim3(kGBwdK), 0, s,
+                                          (const T *)a.X, a.W, rec, a.H_pre, (const T *)a.g, (const T *)a.post_G,
+                                          a.post_H_res, (T *)a.dX, dwp, a.N, a.C, L.tb, a.accumulate))
+}
+
+void glaunch_proj_bwd(hipStream_t s, int n, const ProjBwdArgs &a) {
+  const GBwdLay L = gbwd_layout(a.N, a.C, n);
+  const int64_t J = (int64_t)n * n + 2 * n, K = (int64_t)n * a.C;
+  char *base = (char *)a.ws;
+  float *rec = (float *)base;
+  float *prm = (float *)(base + L.rec);
+  float *dwp = (float *)(base + L.rec + L.prm);
+  float *dhrow = (float *)(base + L.rec + L.prm + L.dw);
+  const float *dHpre = a.dH_pre;
+  if (a.g) {  // fused pre backward: dH_pre = <g, X_i> first (into dH_pre_out when given)
+    float *rows = a.dH_pre_out ? a.dH_pre_out : dhrow;
+    if (a.f32)
+      gagg_bwd<float>(s, n, a.N, a.C, a.g, a.X, a.H_pre, n, nullptr, false, rows);
+    else
+      gagg_bwd<bf16_t>(s, n, a.N, a.C, a.g, a.X, a.H_pre, n, nullptr, false, rows);
+    dHpre = rows;
+  }
+  const unsigned tb = (unsigned)((a.N + 63) / 64);
+  MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_bwd_token_kernel<NS>), dim3(tb), dim3(64), 0, s, a.N, K, a.alpha,
+                                        a.saved, saved_stride(n), a.H_pre, a.H_post, dHpre, a.dH_post, a.dL,
+                                        a.dH_res, a.logits, a.iters, a.eps, rec, prm, a.dL_out));
+  if (a.f32)
+    gdx<float>(s, n, a, L, rec, dwp);
+  else
+    gdx<bf16_t>(s, n, a, L, rec, dwp);
+  if (a.dW)
+    hipLaunchKernelGGL(gdw_reduce_kernel, dim3((unsigned)((K * J + 255) / 256)), dim3(256), 0, s, dwp, a.dW, L.ntb,
+                       K * J);
+  // parameter sums: columns 0..J-1 of prm are dhbias terms, J..J+2 dalpha terms
+  if (a.dhbias)
+    hipLaunchKernelGGL(gcol_sum_kernel, dim3((unsigned)J), dim3(256), 0, s, prm, a.dhbias, a.N, (int)(J + 3));
+  if (a.dalpha)
+    hipLaunchKernelGGL(gcol_sum_kernel, dim3(3u), dim3(256), 0, s, prm + J, a.dalpha, a.N, (int)(J + 3));
+}
+
+}  // namespace mhc

@@ -116,4 +116,42 @@ struct ProjBwdArgs {
 };
 void launch_proj_bwd(hipStream_t s, const ProjBwdArgs &a);
 
+// ---- any stream count 1 <= n <= 8 other than 4 (generic.hip); same
+// arguments as the n = 4 launchers above, with n explicit.
+constexpr int kMaxN = 8;
+// Row stride of the saved forward state {r, q, z[J], 0...}: 32 while
+// 2 + J fits, else 2 + J rounded up to a multiple of 8.
+int saved_stride(int n);
+void glaunch_sinkhorn_fwd(hipStream_t s, int n, int64_t count, const float *L, float *H, int iters, float eps);
+void glaunch_sinkhorn_bwd(hipStream_t s, int n, int64_t count, const float *dH, const float *L, float *dL,
+                          int iters, float eps);
+void glaunch_h_aggregate_fwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *X,
+                             const float *H_pre, void *out, int64_t hs);
+void glaunch_h_aggregate_bwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *g, const void *X,
+                             const float *H_pre, void *dX, bool accumulate, float *dH_pre);
+size_t gh_aggregate_static_bwd_ws(int n, int64_t N);
+void glaunch_h_aggregate_static_bwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *g,
+                                    const void *X, const float *H_pre, void *dX, bool accumulate, float *dH_pre,
+                                    void *ws);
+void glaunch_h_post_bda_fwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *X,
+                            const float *H_res, const float *H_post, const void *x, const void *bias, void *out);
+void glaunch_stream_mix_fwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *X, const float *M,
+                            void *out);
+void glaunch_stream_distribute_fwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *x,
+                                   const float *H_post, void *out);
+size_t gh_post_bda_bwd_ws(int64_t N, int64_t C, bool with_dbias);
+void glaunch_h_post_bda_bwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *G, const void *X,
+                            const float *H_res, const float *H_post, const void *x, const void *bias, void *dX,
+                            float *dH_res, float *dH_post, void *dx, void *dbias, void *ws);
+void glaunch_stream_mix_bwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *G, const void *X,
+                            const float *M, void *dX, float *dM);
+void glaunch_stream_distribute_bwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *G,
+                                   const void *x, const float *H_post, void *dx, float *dH_post);
+size_t gproj_fwd_ws(int n, int64_t N);
+void glaunch_proj_fwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *X, const float *W,
+                      const float *alpha, const float *hbias, float rms_eps, float *H_pre, float *H_post,
+                      float *logits, float *saved, float *H_res, int iters, float eps, void *ws);
+size_t gproj_bwd_ws(int n, int64_t N, int64_t C);
+void glaunch_proj_bwd(hipStream_t s, int n, const ProjBwdArgs &a);
+
 }  // namespace mhc

@@ -60,8 +60,8 @@ def _last(lib):
 def test_variant_entry_points_validate_before_launch(lib):
     E = {n: i for i, n in enumerate(L.STATUS)}
     fake = 0x10000
-    # n != 4, C % 8 != 0, NULL inputs, a misaligned output: all rejected on the host
-    assert lib.mhc_stream_mix_fwd(None, 4, 3, 64, 0, fake, fake + 4096, fake + 8192) == E["MHC_ERR_UNSUPPORTED"]
+    # n > 8, C % 8 != 0, NULL inputs, a misaligned output: all rejected on the host
+    assert lib.mhc_stream_mix_fwd(None, 4, 9, 64, 0, fake, fake + 8192, fake + 16384) == E["MHC_ERR_UNSUPPORTED"]
     assert lib.mhc_stream_mix_fwd(None, 4, 4, 60, 0, fake, fake + 4096, fake + 8192) == E["MHC_ERR_UNSUPPORTED"]
     assert lib.mhc_stream_mix_bwd(None, 4, 4, 64, 0, None, fake, fake, fake, fake) == E["MHC_ERR_NULL"]
     assert lib.mhc_stream_distribute_fwd(None, 4, 4, 64, 0, fake, fake + 4096, fake + 8200) == E["MHC_ERR_ALIGN"]
@@ -90,7 +90,7 @@ def test_kernel_events_hook_validation(lib):
 def test_sinkhorn_validation(lib):
     f = lib.mhc_sinkhorn_fwd
     assert f(None, -1, 4, p(0), p(1), 20, 1e-6) == SHAPE
-    assert f(None, 10, 3, p(0), p(1), 20, 1e-6) == UNSUP
+    assert f(None, 10, 9, p(0), p(1), 20, 1e-6) == UNSUP
     assert f(None, 10, 0, p(0), p(1), 20, 1e-6) == SHAPE
     assert f(None, 10, 4, p(0), p(1), -1, 1e-6) == ARG
     assert f(None, 10, 4, p(0), p(1), 5000, 1e-6) == UNSUP
@@ -110,7 +110,8 @@ def test_dims_validation(lib):
     assert f(None, 4, 4, 63, 0, p(0), p(1), p(2)) == UNSUP       # C % 8
     assert f(None, 4, 4, 0, 0, p(0), p(1), p(2)) == SHAPE
     assert f(None, 4, 4, 16392, 0, p(0), p(1), p(2)) == UNSUP    # C > 16384
-    assert f(None, 4, 5, 64, 0, p(0), p(1), p(2)) == UNSUP       # n != 4
+    assert f(None, 4, 9, 64, 0, p(0), p(1), p(2)) == UNSUP       # n > 8
+    assert f(None, 4, 0, 64, 0, p(0), p(1), p(2)) == SHAPE       # n < 1
     assert f(None, 4, 4, 64, 7, p(0), p(1), p(2)) == ARG         # dtype
     assert f(None, -2, 4, 64, 0, p(0), p(1), p(2)) == SHAPE
     assert f(None, 0, 4, 64, 0, None, None, None) == OK
@@ -198,3 +199,17 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         L.lib()
+
+
+def test_general_n_sizes(lib):
+    # saved-state stride and workspace queries for every supported n
+    assert [lib.mhc_saved_stride(n) for n in range(0, 10)] == [0, 32, 32, 32, 32, 40, 56, 72, 88, 0]
+    for n in (1, 2, 3, 5, 8):
+        assert lib.mhc_proj_rms_h_workspace_size(100, n, 64, 0) > 0
+        assert lib.mhc_proj_rms_h_bwd_workspace_size(100, n, 64, 0) > 0
+        assert lib.mhc_h_aggregate_static_bwd_workspace_size(100, n, 64, 0) == 100 * n * 4
+    assert lib.mhc_proj_rms_h_workspace_size(100, 9, 64, 0) == 0
+    # buffer sizes follow n: X of 4 tokens x 8 streams x 64 bf16 = 4096 bytes, so an output 4000 bytes in overlaps
+    f = lib.mhc_h_aggregate_fwd
+    assert f(None, 4, 8, 64, 0, p(0), p(1), p(0) + 4000) == ALIAS
+    assert f(None, 4, 2, 64, 0, p(0), p(1), p(0) + 1008) == ALIAS  # X: 4 x 2 x 64 bf16 = 1024 bytes

@@ -433,7 +433,7 @@ def test_per_token_results_batch_invariant(act, C):
 
 
 def test_invalid_arguments_raise():
-    X = torch.zeros(4, 3, 64, dtype=torch.bfloat16, device="cuda")
+    X = torch.zeros(4, 9, 64, dtype=torch.bfloat16, device="cuda")  # n = 9 > 8
     with pytest.raises(B._lib.MhcError) as e:
-        B.mhc_h_aggregate_fwd(X, torch.zeros(4, 3, device="cuda"))
+        B.mhc_h_aggregate_fwd(X, torch.zeros(4, 9, device="cuda"))
     assert e.value.name == "MHC_ERR_UNSUPPORTED"
