@@ -125,6 +125,46 @@ def measure_variants(lib, L, sp, N, n, C, X, G, H_res, H_post, x, g, out, dX, dM
     return res
 
 
+def measure_general_n(N: int, stream, torch) -> dict:
+    """One mHC step (pre fwd, post fwd, post bwd, pre bwd with the h_post_bda dX term) at stream counts
+    other than 4, on the kernels templated on n: same token count as the headline workload, a width
+    that keeps the residual near 0.5 GB, synthetic N(0,1) bf16 inputs, W ~ N(0, 0.02).  Mean of 3
+    event-timed steps after one warm-up; GB/s on each boundary tensor once per phase,
+    (16 n + 10) C bytes per token."""
+    from mhc_hyper_connection_proj_amd import binding as B
+    dev = torch.device("cuda", 0)
+    gen = torch.Generator(device=dev).manual_seed(5)
+    res = {}
+    for n, C in ((2, 7168), (8, 2048)):
+        X = torch.randn(N, n, C, device=dev, generator=gen).to(torch.bfloat16)
+        G = torch.randn(N, n, C, device=dev, generator=gen).to(torch.bfloat16)
+        W = torch.randn(n * C, n * n + 2 * n, device=dev, generator=gen) * 0.02
+        s = torch.rand(C, device=dev, generator=gen).to(torch.bfloat16) + 0.5
+
+        def step():
+            f = B.mhc_pre_fwd(X, W)
+            x = f["agg"] * s
+            B.mhc_h_post_bda_fwd(X, f["H_res"], f["H_post"], x)
+            _, dHr, dHp, dx, _ = B.mhc_h_post_bda_bwd(G, X, f["H_res"], f["H_post"], x, want_dX=False)
+            B.mhc_pre_bwd(dx * s, dHp, dHr, X, W, f["saved"], f["H_pre"], f["H_post"], f["H_res_logits"],
+                          post_G=G, post_H_res=f["H_res"])
+
+        step()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record(stream)
+        for i in range(3):
+            step()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(3)]))
+        gbs = (16 * n + 10) * C * N / (ms * 1e-3) / 1e9
+        res[f"n{n}_C{C}"] = {"ms_per_step_incl_layer": ms, "tokens_per_s": N / (ms * 1e-3), "achieved_gbs": gbs,
+                             "frac": gbs / HBM_PEAK_GBS}
+        del X, G, W
+    return res
+
+
 def cpu_baseline(w, X, W, s, G, budget_s: float) -> dict:
     """Time the fp64 oracle (single thread, as written) on the first tokens of the workload."""
     import oracle as O
@@ -284,6 +324,7 @@ def main():
 
     variants = measure_variants(lib, _lib, sp, N, n, C, cur["X"], Gd, H_res, H_post, x, g, out, dX, dHr, dHp, dx,
                                 stream, torch)
+    general_n = measure_general_n(N, stream, torch)
 
     led = ledger_bytes_per_token(C, N)
     tot_bytes = led["total"] * N
@@ -332,6 +373,7 @@ def main():
                                     "traffic": p_traffic, "algorithmic_bytes_per_launch": p_bytes,
                                     "avg_launch_ms": mean["post_bwd"]},
         "variants": variants,
+        "general_n": general_n,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
