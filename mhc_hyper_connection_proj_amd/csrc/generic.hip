@@ -44,7 +44,8 @@ template <int NS> struct Dim {
 constexpr int kGSplitK = 8;   // k slices of the forward projection
 constexpr int kGTok = 32;     // tokens per forward workgroup (one MFMA tile)
 constexpr int kGBwdK = 256;   // k per backward workgroup (one per thread)
-constexpr int kGMaxTB = 16;   // at most this many token blocks in the backward
+constexpr int kGMaxTB = 64;   // at most this many token blocks in the backward
+constexpr int64_t kGDwBudget = 512ll << 20;  // bytes of dW partials the token blocks may take
 
 // ------------------------------------------------------------------ helpers
 template <typename T> struct Ld;
@@ -335,6 +336,9 @@ __global__ __launch_bounds__(256) void gpost_fwd_kernel(const T *__restrict__ X,
 // <G_i, x + bias> and dx = sum_i H_post[i] G_i (MODE != mix).  DBIAS: TG
 // tokens per workgroup; each thread adds its groups' dx into the workgroup's
 // partial row part[blockIdx.x][C] (owned by this thread alone: no atomics).
+// The rows j of X are taken JB at a time (JB = 2 for n > 4), each pass with
+// its own JB * n sums, so the per-thread sums stay few; G is re-read per pass
+// (from the caches).  The token's H values are staged in LDS first.
 template <typename T, int NS, int MODE>
 __global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr, const T *__restrict__ X,
                                                        const float *__restrict__ Hr, const float *__restrict__ Hp,
@@ -343,82 +347,102 @@ __global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr
                                                        float *__restrict__ dHp, T *__restrict__ dx,
                                                        float *__restrict__ part, int64_t N, int64_t C, int TG) {
   const bool HAS_BIAS = bias != nullptr, WRITE_DX = dX != nullptr, DBIAS = part != nullptr;
-  constexpr int NR = (MODE == kPostDist ? 0 : NS * NS) + (MODE == kPostMix ? 0 : NS);
+  constexpr bool MIX = MODE != kPostDist, DIST = MODE != kPostMix;
+  constexpr int JB = NS > 4 ? 2 : NS;
+  constexpr int NPASS = MIX ? (NS + JB - 1) / JB : 1;
+  constexpr int NR = (MIX ? JB * NS : 0) + (DIST ? NS : 0);
   __shared__ float red[4][NR];
+  __shared__ float sH[NS * NS + NS];
   const int64_t G = C / 8;
   const int64_t t0 = (int64_t)blockIdx.x * TG;
   const int64_t t1 = min(t0 + (int64_t)TG, N);
   for (int64_t t = t0; t < t1; ++t) {
-    float acc[NR];
+    __syncthreads();
+    for (int e = threadIdx.x; e < NS * NS + NS; e += blockDim.x)
+      sH[e] = e < NS * NS ? (MIX ? Hr[t * NS * NS + e] : 0.f) : (DIST ? Hp[t * NS + e - NS * NS] : 0.f);
+    __syncthreads();
+#pragma unroll 1
+    for (int pass = 0; pass < NPASS; ++pass) {
+      const int j0 = pass * JB;
+      const bool dist_here = DIST && pass == 0;
+      float acc[NR];
 #pragma unroll
-    for (int k = 0; k < NR; ++k) acc[k] = 0.f;
-    for (int64_t g = threadIdx.x; g < G; g += blockDim.x) {
-      float gv[NS][8];
+      for (int r = 0; r < NR; ++r) acc[r] = 0.f;
+      for (int64_t g = threadIdx.x; g < G; g += blockDim.x) {
+        float gv[NS][8];
 #pragma unroll
-      for (int i = 0; i < NS; ++i) Io8<T>::load(Gr + (t * NS + i) * C + 8 * g, gv[i]);
-      if (MODE != kPostDist) {
+        for (int i = 0; i < NS; ++i) Io8<T>::load(Gr + (t * NS + i) * C + 8 * g, gv[i]);
+        if (MIX) {
 #pragma unroll
-        for (int j = 0; j < NS; ++j) {
-          float xv[8];
-          Io8<T>::load(X + (t * NS + j) * C + 8 * g, xv);
+          for (int jj = 0; jj < JB; ++jj) {
+            const int j = j0 + jj;
+            if (j < NS) {
+              float xv[8];
+              Io8<T>::load(X + (t * NS + j) * C + 8 * g, xv);
+#pragma unroll
+              for (int i = 0; i < NS; ++i) {
+                float sdot = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sdot += xv[e] * gv[i][e];
+                acc[jj * NS + i] += sdot;
+              }
+              if (WRITE_DX) {
+                float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < NS; ++i) {
+                  const float w = sH[j * NS + i];
+#pragma unroll
+                  for (int e = 0; e < 8; ++e) d[e] += w * gv[i][e];
+                }
+                Io8<T>::store(dX + (t * NS + j) * C + 8 * g, d);
+              }
+            }
+          }
+        }
+        if (DIST && dist_here) {
+          constexpr int off = MIX ? JB * NS : 0;
+          float xb[8], o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          Io8<T>::load(x + t * C + 8 * g, xb);
+          if (HAS_BIAS) {
+            float b[8];
+            Io8<T>::load(bias + 8 * g, b);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xb[e] += b[e];
+          }
 #pragma unroll
           for (int i = 0; i < NS; ++i) {
-            float s = 0.f;
+            const float hp = sH[NS * NS + i];
+            float sdot = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s += xv[e] * gv[i][e];
-            acc[j * NS + i] += s;
-          }
-          if (WRITE_DX) {
-            float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int i = 0; i < NS; ++i) {
-              const float w = Hr[t * NS * NS + j * NS + i];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) d[e] += w * gv[i][e];
+            for (int e = 0; e < 8; ++e) {
+              sdot += gv[i][e] * xb[e];
+              o[e] += hp * gv[i][e];
             }
-            Io8<T>::store(dX + (t * NS + j) * C + 8 * g, d);
+            acc[off + i] += sdot;
+          }
+          Io8<T>::store(dx + t * C + 8 * g, o);
+          if (DBIAS) {
+            float *p = part + (int64_t)blockIdx.x * C + 8 * g;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p[e] = (t == t0 ? 0.f : p[e]) + o[e];
           }
         }
       }
-      if (MODE != kPostMix) {
-        constexpr int off = MODE == kPostDist ? 0 : NS * NS;
-        float xb[8], o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        Io8<T>::load(x + t * C + 8 * g, xb);
-        if (HAS_BIAS) {
-          float b[8];
-          Io8<T>::load(bias + 8 * g, b);
+      gblock_sum<NR>(acc, red);
+      if (threadIdx.x == 0) {
+        if (MIX) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) xb[e] += b[e];
+          for (int jj = 0; jj < JB; ++jj)
+            if (j0 + jj < NS) {
+#pragma unroll
+              for (int i = 0; i < NS; ++i) dHr[t * NS * NS + (j0 + jj) * NS + i] = acc[jj * NS + i];
+            }
         }
+        if (dist_here) {
+          constexpr int off = MIX ? JB * NS : 0;
 #pragma unroll
-        for (int i = 0; i < NS; ++i) {
-          const float hp = Hp[t * NS + i];
-          float s = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            s += gv[i][e] * xb[e];
-            o[e] += hp * gv[i][e];
-          }
-          acc[off + i] += s;
+          for (int i = 0; i < NS; ++i) dHp[t * NS + i] = acc[off + i];
         }
-        Io8<T>::store(dx + t * C + 8 * g, o);
-        if (DBIAS) {
-          float *p = part + (int64_t)blockIdx.x * C + 8 * g;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) p[e] = (t == t0 ? 0.f : p[e]) + o[e];
-        }
-      }
-    }
-    gblock_sum<NR>(acc, red);
-    if (threadIdx.x == 0) {
-      if (MODE != kPostDist) {
-#pragma unroll
-        for (int k = 0; k < NS * NS; ++k) dHr[t * NS * NS + k] = acc[k];
-      }
-      if (MODE != kPostMix) {
-        constexpr int off = MODE == kPostDist ? 0 : NS * NS;
-#pragma unroll
-        for (int i = 0; i < NS; ++i) dHp[t * NS + i] = acc[off + i];
       }
     }
   }
@@ -635,7 +659,10 @@ __global__ __launch_bounds__(256) void gproj_bwd_dx_kernel(
   const bool HAS_G = gr != nullptr, POST = Gp != nullptr;
   constexpr int J = Dim<NS>::J;
   constexpr int RT = 16;  // tokens per LDS record stage
-  __shared__ float srec[RT][J + 1];
+  constexpr int UB = 4;   // tokens whose global loads are issued together
+  constexpr int JP = (J + 1 + 3) / 4 * 4;  // record row padded to 16 bytes (128-bit LDS reads)
+  __shared__ __align__(16) float srec[RT][JP];
+  __shared__ float sh[RT][NS + NS * NS];  // H_pre row, then H_res rows (POST)
   const int64_t K = NS * C;
   const int64_t k = (int64_t)blockIdx.x * kGBwdK + threadIdx.x;
   const bool kv = k < K;
@@ -653,25 +680,48 @@ __global__ __launch_bounds__(256) void gproj_bwd_dx_kernel(
     __syncthreads();
     for (int idx = threadIdx.x; idx < nt * (J + 1); idx += blockDim.x)
       srec[idx / (J + 1)][idx % (J + 1)] = rec[(ts + idx / (J + 1)) * (J + 1) + idx % (J + 1)];
+    for (int idx = threadIdx.x; idx < nt * (NS + NS * NS); idx += blockDim.x) {
+      const int u = idx / (NS + NS * NS), e = idx % (NS + NS * NS);
+      float v = 0.f;
+      if (e < NS) {
+        if (HAS_G) v = Hpre[(ts + u) * NS + e];
+      } else if (POST) {
+        v = Hr[(ts + u) * NS * NS + e - NS];
+      }
+      sh[u][e] = v;
+    }
     __syncthreads();
     if (kv) {
-      for (int u = 0; u < nt; ++u) {
-        const int64_t t = ts + u;
-        const float xv = Ld<T>::one(X + t * K + k);
-        float acc = ACCUM ? Ld<T>::one(dX + t * K + k) : 0.f;
-        if (HAS_G) acc += Hpre[t * NS + i] * Ld<T>::one(gr + t * C + c);
-        float s = 0.f;
+      for (int u0 = 0; u0 < nt; u0 += UB) {
+        // loads of UB tokens first (a token past the block re-reads the last one; it is not stored)
+        float xv[UB], gv[UB], din[UB], Gv[UB][NS];
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-          s += srec[u][j] * w[j];
-          if (DW) dw[j] += xv * srec[u][j];
-        }
-        acc += s + srec[u][J] * xv;
-        if (POST) {
+        for (int q = 0; q < UB; ++q) {
+          const int64_t t = ts + min(u0 + q, nt - 1);
+          xv[q] = Ld<T>::one(X + t * K + k);
+          din[q] = ACCUM ? Ld<T>::one(dX + t * K + k) : 0.f;
+          gv[q] = HAS_G ? Ld<T>::one(gr + t * C + c) : 0.f;
 #pragma unroll
-          for (int ip = 0; ip < NS; ++ip) acc += Hr[t * NS * NS + i * NS + ip] * Ld<T>::one(Gp + (t * NS + ip) * C + c);
+          for (int ip = 0; ip < NS; ++ip) Gv[q][ip] = POST ? Ld<T>::one(Gp + (t * NS + ip) * C + c) : 0.f;
         }
-        st_one<T>(dX + t * K + k, acc);
+#pragma unroll
+        for (int q = 0; q < UB; ++q) {
+          const int u = u0 + q;
+          if (u < nt) {
+            float acc = din[q] + sh[u][i] * gv[q];
+            float s0 = 0.f, s1 = 0.f;  // two chains for the J-long dot product
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+              if (j & 1) s1 += srec[u][j] * w[j];
+              else s0 += srec[u][j] * w[j];
+              if (DW) dw[j] += xv[q] * srec[u][j];
+            }
+            acc += (s0 + s1) + srec[u][J] * xv[q];
+#pragma unroll
+            for (int ip = 0; ip < NS; ++ip) acc += sh[u][NS + i * NS + ip] * Gv[q][ip];
+            st_one<T>(dX + (ts + u) * K + k, acc);
+          }
+        }
       }
     }
   }
@@ -718,7 +768,9 @@ struct GBwdLay {
 GBwdLay gbwd_layout(int64_t N, int64_t C, int n) {
   const int64_t J = (int64_t)n * n + 2 * n, K = (int64_t)n * C;
   GBwdLay L;
-  L.ntb = std::min<int64_t>(kGMaxTB, std::max<int64_t>(1, (N + 63) / 64));
+  // token blocks of >= 64 tokens, at most kGMaxTB, and dW partials within kGDwBudget
+  const int64_t by_budget = std::max<int64_t>(1, kGDwBudget / (K * J * 4));
+  L.ntb = std::min<int64_t>(std::min<int64_t>(kGMaxTB, by_budget), std::max<int64_t>(1, (N + 63) / 64));
   L.tb = (N + L.ntb - 1) / L.ntb;
   L.rec = al256((size_t)N * (J + 1) * 4);
   L.prm = al256((size_t)N * (J + 3) * 4);
