@@ -165,6 +165,68 @@ def measure_general_n(N: int, stream, torch) -> dict:
     return res
 
 
+def measure_configs(stream, torch) -> dict:
+    """The other stated workloads at their full sizes (seeded synthetic inputs from synth): batched
+    Sinkhorn fwd + bwd (1,048,576 4x4 matrices), the pre forward (32768 tokens, C = 4096) and the
+    h_post_bda forward + backward with bias (32768 tokens, C = 4096).  Mean of 5 event-timed calls
+    after one warm-up; algorithmic bytes: Sinkhorn 128 + 192 bytes per matrix, pre forward
+    10C + 260 per token (X read; agg, H, logits, saved written), h_post_bda 18C + 80 (fwd) and
+    28C + 160 (bwd with dX, dx, dH and dbias) per token, bias and dbias once.  H_res / H_post of the
+    h_post_bda leg are the uniform doubly stochastic matrix and ones: their values do not change the
+    work or the traffic."""
+    from mhc_hyper_connection_proj_amd import binding as B, synth
+    dev = torch.device("cuda", 0)
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+
+    res = {}
+    w = synth.WORKLOADS["sinkhorn_batched"]
+    L, dH = to_dev(synth.tensor(w, "L")), to_dev(synth.tensor(w, "dH"))
+    ms_f = timed(lambda: B.mhc_sinkhorn_fwd(L, w.iters, w.eps))
+    ms_b = timed(lambda: B.mhc_sinkhorn_bwd(dH, L, w.iters, w.eps))
+    M = w.tokens
+    res["sinkhorn_batched"] = {"matrices": M, "fwd_ms": ms_f, "bwd_ms": ms_b,
+                               "matrices_per_s": M / ((ms_f + ms_b) * 1e-3),
+                               "achieved_gbs": 320 * M / ((ms_f + ms_b) * 1e-3) / 1e9,
+                               "frac": 320 * M / ((ms_f + ms_b) * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del L, dH
+    w = synth.WORKLOADS["pre_fwd"]
+    N, C = w.tokens, w.C
+    X, W = to_dev(synth.tensor(w, "X")), to_dev(synth.tensor(w, "W"))
+    ms = timed(lambda: B.mhc_pre_fwd(X, W, None, None, w.rms_eps, w.iters, w.eps))
+    byt = (10 * C + 260) * N
+    res["pre_fwd"] = {"tokens": N, "C": C, "ms": ms, "tokens_per_s": N / (ms * 1e-3),
+                      "achieved_gbs": byt / (ms * 1e-3) / 1e9, "frac": byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del X, W
+    w = synth.WORKLOADS["post_bda"]
+    N, C = w.tokens, w.C
+    X, G, x, b = (to_dev(synth.tensor(w, t)) for t in ("X", "G", "x", "bias"))
+    Hr = to_dev(np.ascontiguousarray(np.full((N, 4, 4), 0.25, np.float32)))
+    Hp = to_dev(np.ascontiguousarray(np.full((N, 4), 1.0, np.float32)))
+    ms_f = timed(lambda: B.mhc_h_post_bda_fwd(X, Hr, Hp, x, b))
+    ms_b = timed(lambda: B.mhc_h_post_bda_bwd(G, X, Hr, Hp, x, b))
+    byt = ((18 * C + 80) + (28 * C + 160)) * N + 4 * C
+    res["post_bda_fwd_bwd"] = {"tokens": N, "C": C, "fwd_ms": ms_f, "bwd_ms": ms_b,
+                               "tokens_per_s": N / ((ms_f + ms_b) * 1e-3),
+                               "achieved_gbs": byt / ((ms_f + ms_b) * 1e-3) / 1e9,
+                               "frac": byt / ((ms_f + ms_b) * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return res
+
+
 def cpu_baseline(w, X, W, s, G, budget_s: float) -> dict:
     """Time the fp64 oracle (single thread, as written) on the first tokens of the workload."""
     import oracle as O
@@ -325,6 +387,7 @@ def main():
     variants = measure_variants(lib, _lib, sp, N, n, C, cur["X"], Gd, H_res, H_post, x, g, out, dX, dHr, dHp, dx,
                                 stream, torch)
     general_n = measure_general_n(N, stream, torch)
+    configs = measure_configs(stream, torch)
 
     led = ledger_bytes_per_token(C, N)
     tot_bytes = led["total"] * N
@@ -374,6 +437,7 @@ def main():
                                     "avg_launch_ms": mean["post_bwd"]},
         "variants": variants,
         "general_n": general_n,
+        "configs": configs,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
