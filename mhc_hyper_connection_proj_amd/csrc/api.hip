@@ -51,6 +51,9 @@ class Validator {
     if (act != MHC_BF16 && act != MHC_F32) fail(MHC_ERR_ARG, "unknown activation dtype");
   }
 
+  // [tokens][C] rows with no stream dimension (the RMSNorm of the aggregated stream)
+  void rows(int64_t tokens, int64_t C, mhc_dtype act) { dims(tokens, 1, C, act); }
+
   void eps(float e, const char *what) {
     if (!std::isfinite(e) || e < 0.f) fail(MHC_ERR_ARG, std::string(what) + " must be finite and >= 0");
   }
@@ -618,7 +621,7 @@ mhc_status mhc_pre_fwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_d
 mhc_status mhc_rmsnorm_fwd(void *stream, int64_t tokens, int64_t C, mhc_dtype act, const void *x,
                            const float *gamma, float eps, void *y) {
   Validator v("mhc_rmsnorm_fwd");
-  v.dims(tokens, mhc::kN, C, act);
+  v.rows(tokens, C, act);
   v.eps(eps, "eps");
   if (!v.ok()) return v.status();
   if (tokens == 0) return MHC_OK;
@@ -641,7 +644,7 @@ mhc_status mhc_rmsnorm_bwd(void *stream, int64_t tokens, int64_t C, mhc_dtype ac
                            int32_t accumulate_dx, float *dgamma, void *workspace,
                            size_t workspace_bytes) {
   Validator v("mhc_rmsnorm_bwd");
-  v.dims(tokens, mhc::kN, C, act);
+  v.rows(tokens, C, act);
   v.eps(eps, "eps");
   if (!v.ok()) return v.status();
   const hipStream_t s = (hipStream_t)stream;

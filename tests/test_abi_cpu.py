@@ -213,3 +213,30 @@ def test_general_n_sizes(lib):
     f = lib.mhc_h_aggregate_fwd
     assert f(None, 4, 8, 64, 0, p(0), p(1), p(0) + 4000) == ALIAS
     assert f(None, 4, 2, 64, 0, p(0), p(1), p(0) + 1008) == ALIAS  # X: 4 x 2 x 64 bf16 = 1024 bytes
+
+
+def test_rmsnorm_validation(lib):
+    # every call below must fail validation: the pointers are fake
+    f = lib.mhc_rmsnorm_fwd
+    # stream, tokens, C, act, x, gamma, eps, y
+    assert f(None, 4, 60, 0, p(0), None, 1e-6, p(1)) == UNSUP                 # C % 8
+    assert f(None, 4, 64, 0, p(0), None, -1.0, p(1)) == ARG                   # eps < 0
+    assert f(None, 4, 64, 0, None, None, 1e-6, p(1)) == NULL and "x" in _last(lib)
+    assert f(None, 4, 64, 0, p(0), None, 1e-6, p(0) + 256) == ALIAS           # y inside x (4*64*2 bytes)
+    assert f(None, 4, 64, 0, p(0), p(0) + 64, 1e-6, p(0) + 128) == ALIAS      # y inside x, gamma given
+    assert f(None, 0, 64, 0, None, None, 1e-6, None) == OK                    # empty: no-op
+    g = lib.mhc_rmsnorm_bwd
+    # stream, tokens, C, act, dy, x, gamma, eps, dx, accumulate, dgamma, ws, ws_bytes
+    need = lib.mhc_rmsnorm_bwd_workspace_size(100, 64, 0, 1)
+    assert need >= (7 + 16) * 64 * 4 and lib.mhc_rmsnorm_bwd_workspace_size(100, 64, 0, 0) == 0
+    assert g(None, 100, 64, 0, p(0), p(1), None, 1e-6, p(2), 0, p(3), None, 0) == WS
+    assert g(None, 100, 64, 0, p(0), p(1), None, 1e-6, p(0), 0, None, None, 0) == ALIAS   # dx is dy
+    assert g(None, 100, 64, 0, p(0), None, None, 1e-6, p(2), 0, None, None, 0) == NULL
+    h = lib.mhc_pre_rmsnorm_fwd
+    # stream, tokens, n, C, act, X, W, alpha, hbias, rms_eps, iters, eps, gamma, norm_eps,
+    # H_pre, H_post, H_res, logits, saved, agg, normed, ws, ws_bytes
+    ws = lib.mhc_pre_fwd_workspace_size(8, 4, 64, 0)
+    assert h(None, 8, 4, 64, 0, p(0), p(1), None, None, 1e-6, 20, 1e-6, None, 1e-6,
+             p(2), p(3), p(4), p(5), None, p(6), p(6) + 64, p(7), ws) == ALIAS     # normed inside agg
+    assert h(None, 8, 4, 64, 0, p(0), p(1), None, None, 1e-6, 20, 1e-6, None, -1.0,
+             p(2), p(3), p(4), p(5), None, p(6), p(8), p(7), ws) == ARG            # norm_eps < 0
