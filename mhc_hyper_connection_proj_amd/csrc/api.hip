@@ -246,7 +246,7 @@ mhc_status mhc_proj_rms_h(void *stream, int64_t tokens, int32_t n, int64_t C, mh
 // ------------------------------------------------------------------ projection bwd
 size_t mhc_proj_rms_h_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
   if (tokens <= 0 || n < 1 || n > mhc::kMaxN || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
-  return n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_bwd_ws(n, tokens, C);
+  return n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_bwd_ws(n, tokens, C, false);
 }
 
 mhc_status mhc_proj_rms_h_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
@@ -282,7 +282,7 @@ mhc_status mhc_proj_rms_h_bwd(void *stream, int64_t tokens, int32_t n, int64_t C
   v.out(dW, K * J * 4, "dW", true);
   v.out(dalpha, 12, "dalpha", true);
   v.out(dhbias, J * 4, "dhbias", true);
-  v.workspace(workspace, workspace_bytes, n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_bwd_ws(n, tokens, C));
+  v.workspace(workspace, workspace_bytes, n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_bwd_ws(n, tokens, C, false));
   if (v.finish() != MHC_OK) return v.status();
   mhc::ProjBwdArgs a{};
   a.f32 = act == MHC_F32; a.N = tokens; a.C = C; a.X = X; a.W = W; a.alpha = alpha; a.saved = saved;
@@ -710,7 +710,8 @@ mhc_status mhc_pre_rmsnorm_fwd(void *stream, int64_t tokens, int32_t n, int64_t 
 }
 
 size_t mhc_pre_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
-  return mhc_proj_rms_h_bwd_workspace_size(tokens, n, C, act);
+  if (tokens <= 0 || n < 1 || n > mhc::kMaxN || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
+  return n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_bwd_ws(n, tokens, C, true);
 }
 
 mhc_status mhc_pre_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
@@ -757,7 +758,7 @@ mhc_status mhc_pre_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_d
   v.out(dhbias, J * 4, "dhbias", true);
   v.out(dH_pre_out, tokens * n * 4, "dH_pre_out", true);
   v.out(dlogits_out, tokens * n * n * 4, "dlogits_out", true);
-  v.workspace(workspace, workspace_bytes, n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_bwd_ws(n, tokens, C));
+  v.workspace(workspace, workspace_bytes, n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_bwd_ws(n, tokens, C, true));
   if (v.finish() != MHC_OK) return v.status();
   mhc::ProjBwdArgs a{};
   a.f32 = act == MHC_F32; a.N = tokens; a.C = C; a.X = X; a.W = W; a.alpha = alpha; a.saved = saved;

@@ -644,29 +644,71 @@ __global__ __launch_bounds__(64) void gproj_bwd_token_kernel(
   prm[t * (J + 3) + J + 2] = da[2];
 }
 
+// The residual-gradient terms of the fused pre backward that need no
+// projection state, formed per token with 128-bit loads into an fp32
+// workspace row term[t][k], k = j*C + c:
+//   term = H_pre[t][j] g[t][c]  (g given)  +  sum_i H_res[t][j][i] G[t][i][c]  (G given)
+// so the dX/dW kernel reads one value per element instead of n + 1 narrow
+// ones.  One workgroup per token, H values staged in LDS.
+template <typename T, int NS>
+__global__ __launch_bounds__(256) void gpre_terms_kernel(const T *__restrict__ gr, const float *__restrict__ Hpre,
+                                                        const T *__restrict__ Gp, const float *__restrict__ Hr,
+                                                        float *__restrict__ term, int64_t C) {
+  __shared__ float sH[NS + NS * NS];
+  const int64_t t = blockIdx.x;
+  const bool HAS_G = gr != nullptr, POST = Gp != nullptr;
+  for (int e = threadIdx.x; e < NS + NS * NS; e += blockDim.x)
+    sH[e] = e < NS ? (HAS_G ? Hpre[t * NS + e] : 0.f) : (POST ? Hr[t * NS * NS + e - NS] : 0.f);
+  __syncthreads();
+  const int64_t G = C / 8;
+  for (int64_t g = threadIdx.x; g < G; g += blockDim.x) {
+    float gv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, Gv[NS][8];
+    if (HAS_G) Io8<T>::load(gr + t * C + 8 * g, gv);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (POST) {
+        Io8<T>::load(Gp + (t * NS + i) * C + 8 * g, Gv[i]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Gv[i][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = sH[j] * gv[e];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const float w = sH[NS + j * NS + i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] += w * Gv[i][e];
+      }
+      float *dst = term + (t * NS + j) * C + 8 * g;
+      *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<float4 *>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+    }
+  }
+}
+
 // dX and dW.  Grid: (K / 256 k tiles) x (token blocks); thread = one k =
 // i*C + c, holding W[k][0..J) and its dW partial.  For each token of the
-// block (records staged in LDS):
-//   dX[t][k] = (dX_in) + H_pre[t][i] g[t][c] + sum_j dp[t][j] W[k][j]
-//              + c_rms[t] x[t][k] + sum_i' H_res[t][i][i'] G[t][i'][c]
+// block (records staged in LDS, four tokens' loads issued together):
+//   dX[t][k] = (dX_in) + term[t][k] + sum_j dp[t][j] W[k][j] + c_rms[t] x[t][k]
 // all in fp32 with one rounding at the store; dW[k][j] += x[t][k] dp[t][j].
 template <typename T, int NS, bool DW>
 __global__ __launch_bounds__(256) void gproj_bwd_dx_kernel(
     const T *__restrict__ X, const float *__restrict__ W, const float *__restrict__ rec,
-    const float *__restrict__ Hpre, const T *__restrict__ gr, const T *__restrict__ Gp,
-    const float *__restrict__ Hr, T *__restrict__ dX, float *__restrict__ dwpart, int64_t N, int64_t C,
+    const float *__restrict__ term, T *__restrict__ dX, float *__restrict__ dwpart, int64_t N, int64_t C,
     int64_t TB, bool ACCUM) {
-  const bool HAS_G = gr != nullptr, POST = Gp != nullptr;
   constexpr int J = Dim<NS>::J;
   constexpr int RT = 16;  // tokens per LDS record stage
   constexpr int UB = 4;   // tokens whose global loads are issued together
   constexpr int JP = (J + 1 + 3) / 4 * 4;  // record row padded to 16 bytes (128-bit LDS reads)
   __shared__ __align__(16) float srec[RT][JP];
-  __shared__ float sh[RT][NS + NS * NS];  // H_pre row, then H_res rows (POST)
   const int64_t K = NS * C;
   const int64_t k = (int64_t)blockIdx.x * kGBwdK + threadIdx.x;
   const bool kv = k < K;
-  const int64_t i = kv ? k / C : 0, c = kv ? k % C : 0;
   float w[J], dw[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
@@ -680,35 +722,21 @@ __global__ __launch_bounds__(256) void gproj_bwd_dx_kernel(
     __syncthreads();
     for (int idx = threadIdx.x; idx < nt * (J + 1); idx += blockDim.x)
       srec[idx / (J + 1)][idx % (J + 1)] = rec[(ts + idx / (J + 1)) * (J + 1) + idx % (J + 1)];
-    for (int idx = threadIdx.x; idx < nt * (NS + NS * NS); idx += blockDim.x) {
-      const int u = idx / (NS + NS * NS), e = idx % (NS + NS * NS);
-      float v = 0.f;
-      if (e < NS) {
-        if (HAS_G) v = Hpre[(ts + u) * NS + e];
-      } else if (POST) {
-        v = Hr[(ts + u) * NS * NS + e - NS];
-      }
-      sh[u][e] = v;
-    }
     __syncthreads();
     if (kv) {
       for (int u0 = 0; u0 < nt; u0 += UB) {
         // loads of UB tokens first (a token past the block re-reads the last one; it is not stored)
-        float xv[UB], gv[UB], din[UB], Gv[UB][NS];
+        float xv[UB], tv[UB];
 #pragma unroll
         for (int q = 0; q < UB; ++q) {
           const int64_t t = ts + min(u0 + q, nt - 1);
           xv[q] = Ld<T>::one(X + t * K + k);
-          din[q] = ACCUM ? Ld<T>::one(dX + t * K + k) : 0.f;
-          gv[q] = HAS_G ? Ld<T>::one(gr + t * C + c) : 0.f;
-#pragma unroll
-          for (int ip = 0; ip < NS; ++ip) Gv[q][ip] = POST ? Ld<T>::one(Gp + (t * NS + ip) * C + c) : 0.f;
+          tv[q] = (term ? term[t * K + k] : 0.f) + (ACCUM ? Ld<T>::one(dX + t * K + k) : 0.f);
         }
 #pragma unroll
         for (int q = 0; q < UB; ++q) {
           const int u = u0 + q;
           if (u < nt) {
-            float acc = din[q] + sh[u][i] * gv[q];
             float s0 = 0.f, s1 = 0.f;  // two chains for the J-long dot product
 #pragma unroll
             for (int j = 0; j < J; ++j) {
@@ -716,10 +744,7 @@ __global__ __launch_bounds__(256) void gproj_bwd_dx_kernel(
               else s0 += srec[u][j] * w[j];
               if (DW) dw[j] += xv[q] * srec[u][j];
             }
-            acc += (s0 + s1) + srec[u][J] * xv[q];
-#pragma unroll
-            for (int ip = 0; ip < NS; ++ip) acc += sh[u][NS + i * NS + ip] * Gv[q][ip];
-            st_one<T>(dX + (ts + u) * K + k, acc);
+            st_one<T>(dX + (ts + u) * K + k, tv[q] + (s0 + s1) + srec[u][J] * xv[q]);
           }
         }
       }
@@ -762,10 +787,11 @@ inline size_t al256(size_t b) { return (b + 255) / 256 * 256; }
 
 struct GBwdLay {
   int64_t ntb, tb;
-  size_t rec, prm, dw, dhrow, total;
+  size_t rec, prm, dw, dhrow, term, total;
 };
 
-GBwdLay gbwd_layout(int64_t N, int64_t C, int n) {
+// terms: room for the fp32 residual-gradient terms (the fused pre backward).
+GBwdLay gbwd_layout(int64_t N, int64_t C, int n, bool terms) {
   const int64_t J = (int64_t)n * n + 2 * n, K = (int64_t)n * C;
   GBwdLay L;
   // token blocks of >= 64 tokens, at most kGMaxTB, and dW partials within kGDwBudget
@@ -776,7 +802,8 @@ GBwdLay gbwd_layout(int64_t N, int64_t C, int n) {
   L.prm = al256((size_t)N * (J + 3) * 4);
   L.dw = al256((size_t)L.ntb * K * J * 4);
   L.dhrow = al256((size_t)N * n * 4);
-  L.total = L.rec + L.prm + L.dw + L.dhrow;
+  L.term = terms ? al256((size_t)N * K * 4) : 0;
+  L.total = L.rec + L.prm + L.dw + L.dhrow + L.term;
   return L;
 }
 
@@ -957,30 +984,39 @@ void glaunch_proj_fwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, cons
                                         iters, eps));
 }
 
-size_t gproj_bwd_ws(int n, int64_t N, int64_t C) { return gbwd_layout(N, C, n).total; }
+size_t gproj_bwd_ws(int n, int64_t N, int64_t C, bool terms) { return gbwd_layout(N, C, n, terms).total; }
 
 template <typename T>
-static void gdx(hipStream_t s, int n, const ProjBwdArgs &a, const GBwdLay &L, const float *rec, float *dwp) {
+static void gdx(hipStream_t s, int n, const ProjBwdArgs &a, const GBwdLay &L, const float *rec, const float *term,
+                float *dwp) {
   const int64_t K = (int64_t)n * a.C;
   const dim3 grid((unsigned)((K + kGBwdK - 1) / kGBwdK), (unsigned)L.ntb);
   if (a.dW)
     MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_bwd_dx_kernel<T, NS, true>), grid, dim3(kGBwdK), 0, s,
-                                          (const T *)a.X, a.W, rec, a.H_pre, (const T *)a.g, (const T *)a.post_G,
-                                          a.post_H_res, (T *)a.dX, dwp, a.N, a.C, L.tb, a.accumulate))
+                                          (const T *)a.X, a.W, rec, term, (T *)a.dX, dwp, a.N, a.C, L.tb,
+                                          a.accumulate))
   else
     MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_bwd_dx_kernel<T, NS, false>), grid, dim3(kGBwdK), 0, s,
-                                          (const T *)a.X, a.W, rec, a.H_pre, (const T *)a.g, (const T *)a.post_G,
-                                          a.post_H_res, (T *)a.dX, dwp, a.N, a.C, L.tb, a.accumulate))
+                                          (const T *)a.X, a.W, rec, term, (T *)a.dX, dwp, a.N, a.C, L.tb,
+                                          a.accumulate))
+}
+
+template <typename T>
+static void gterms(hipStream_t s, int n, const ProjBwdArgs &a, float *term) {
+  MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gpre_terms_kernel<T, NS>), dim3((unsigned)a.N), dim3(gtpb(a.C)), 0, s,
+                                        (const T *)a.g, a.H_pre, (const T *)a.post_G, a.post_H_res, term, a.C));
 }
 
 void glaunch_proj_bwd(hipStream_t s, int n, const ProjBwdArgs &a) {
-  const GBwdLay L = gbwd_layout(a.N, a.C, n);
+  const bool terms = a.g != nullptr || a.post_G != nullptr;
+  const GBwdLay L = gbwd_layout(a.N, a.C, n, terms);
   const int64_t J = (int64_t)n * n + 2 * n, K = (int64_t)n * a.C;
   char *base = (char *)a.ws;
   float *rec = (float *)base;
   float *prm = (float *)(base + L.rec);
   float *dwp = (float *)(base + L.rec + L.prm);
   float *dhrow = (float *)(base + L.rec + L.prm + L.dw);
+  float *term = terms ? (float *)(base + L.rec + L.prm + L.dw + L.dhrow) : nullptr;
   const float *dHpre = a.dH_pre;
   if (a.g) {  // fused pre backward: dH_pre = <g, X_i> first (into dH_pre_out when given)
     float *rows = a.dH_pre_out ? a.dH_pre_out : dhrow;
@@ -994,10 +1030,16 @@ void glaunch_proj_bwd(hipStream_t s, int n, const ProjBwdArgs &a) {
   MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_bwd_token_kernel<NS>), dim3(tb), dim3(64), 0, s, a.N, K, a.alpha,
                                         a.saved, saved_stride(n), a.H_pre, a.H_post, dHpre, a.dH_post, a.dL,
                                         a.dH_res, a.logits, a.iters, a.eps, rec, prm, a.dL_out));
+  if (terms) {
+    if (a.f32)
+      gterms<float>(s, n, a, term);
+    else
+      gterms<bf16_t>(s, n, a, term);
+  }
   if (a.f32)
-    gdx<float>(s, n, a, L, rec, dwp);
+    gdx<float>(s, n, a, L, rec, term, dwp);
   else
-    gdx<bf16_t>(s, n, a, L, rec, dwp);
+    gdx<bf16_t>(s, n, a, L, rec, term, dwp);
   if (a.dW)
     hipLaunchKernelGGL(gdw_reduce_kernel, dim3((unsigned)((K * J + 255) / 256)), dim3(256), 0, s, dwp, a.dW, L.ntb,
                        K * J);

@@ -151,7 +151,8 @@ size_t gproj_fwd_ws(int n, int64_t N);
 void glaunch_proj_fwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *X, const float *W,
                       const float *alpha, const float *hbias, float rms_eps, float *H_pre, float *H_post,
                       float *logits, float *saved, float *H_res, int iters, float eps, void *ws);
-size_t gproj_bwd_ws(int n, int64_t N, int64_t C);
+// terms: the fused pre backward (aggregate and h_post_bda residual terms formed first)
+size_t gproj_bwd_ws(int n, int64_t N, int64_t C, bool terms);
 void glaunch_proj_bwd(hipStream_t s, int n, const ProjBwdArgs &a);
 
 }  // namespace mhc
