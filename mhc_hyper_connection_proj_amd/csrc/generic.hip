@@ -42,7 +42,7 @@ template <int NS> struct Dim {
 };
 
 constexpr int kGSplitK = 8;   // k slices of the forward projection
-constexpr int kGTok = 32;     // tokens per forward workgroup (one MFMA tile)
+constexpr int kGTok = 32;     // tokens per wave in the forward projection (one MFMA tile)
 constexpr int kGBwdK = 256;   // k per backward workgroup (one per thread)
 constexpr int kGMaxTB = 64;   // at most this many token blocks in the backward
 constexpr int64_t kGDwBudget = 512ll << 20;  // bytes of dW partials the token blocks may take
@@ -449,17 +449,23 @@ __global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr
 }
 
 // ------------------------------------------------------------------ projection forward
-// Grid: ceil(N / 32) * kGSplitK workgroups of 4 waves; workgroup b takes token
-// block b / kGSplitK and k slice b % kGSplitK; wave w the slice's 64-k chunks
-// w, w + 4, ...  Each chunk is summed from zero on the MFMA and then added to
-// the running sum (two-level blocking), the four waves' sums are added in
-// wave order.  part[slice][t][0..J) = partial x @ W, part[slice][t][J] =
-// partial sum x^2.
+// Grid: ceil(N / 128) * kGSplitK workgroups of 4 waves; workgroup b takes
+// token block b / kGSplitK (128 tokens, 32 per wave) and k slice
+// b % kGSplitK.  The slice's 64-k chunks are walked by all four waves
+// together: each chunk of W (64 k x J) is loaded once per workgroup into LDS,
+// transposed to [column][k] so a lane reads its 32 k values with 128-bit
+// reads, and every wave multiplies it with its own tokens' x on the fp32
+// MFMA (32x32x2).  Each chunk is summed from zero and then added to the
+// running sum (two-level blocking).  part[slice][t][0..J) = partial x @ W,
+// part[slice][t][J] = partial sum x^2.
+constexpr int kGTokWG = 4 * kGTok;  // tokens per forward workgroup
+
 template <typename T, int NS>
 __global__ __launch_bounds__(256) void gproj_partial_kernel(const T *__restrict__ X, const float *__restrict__ W,
                                                            float *__restrict__ part, int64_t N, int64_t K) {
   constexpr int J = Dim<NS>::J, JT = Dim<NS>::JT, PS = Dim<NS>::PS;
-  __shared__ float red_p[4][kGTok][PS];
+  constexpr int SWS = 64 + 4;  // LDS row stride of the transposed W chunk (floats)
+  __shared__ __align__(16) float sW[32 * JT][SWS];
   const int slice = blockIdx.x % kGSplitK;
   const int64_t tb = blockIdx.x / kGSplitK;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -468,7 +474,7 @@ __global__ __launch_bounds__(256) void gproj_partial_kernel(const T *__restrict_
   const int64_t cps = (nch + kGSplitK - 1) / kGSplitK;
   const int64_t c_begin = slice * cps;
   const int64_t c_end = min(nch, c_begin + cps);
-  const int64_t trow = tb * kGTok + row;
+  const int64_t trow = tb * kGTokWG + wave * kGTok + row;
   const bool tvalid = trow < N;
 
   gf32x16 outer[JT];
@@ -478,34 +484,67 @@ __global__ __launch_bounds__(256) void gproj_partial_kernel(const T *__restrict_
     for (int r = 0; r < 16; ++r) outer[u][r] = 0.f;
   float ss = 0.f;
 
-  for (int64_t c = c_begin + wave; c < c_end; c += 4) {
-    const int64_t k0 = c * 64 + 32 * h;  // this lane's 32 k values: k0 .. k0 + 31
-    // K % 8 == 0 and k0 % 32 == 0: an 8-value group is either wholly inside K or wholly past it
+  // The next chunk's W values and x groups are loaded into registers while
+  // the current chunk is multiplied (K % 8 == 0 and k0 % 32 == 0: an 8-value
+  // x group is either wholly inside K or wholly past it).
+  constexpr int WPT = (64 * 32 * JT + 255) / 256;  // W values per thread per chunk
+  using R = typename Io8<T>::raw_t;
+  float wreg[WPT];
+  R xr[4];
+  bool xok[4];
+  auto fetch = [&](int64_t c) {
+    const int64_t kc = c * 64;
+#pragma unroll
+    for (int q = 0; q < WPT; ++q) {
+      const int idx = threadIdx.x + q * 256;
+      const int kk = idx / (32 * JT), j = idx % (32 * JT);
+      wreg[q] = (idx < 64 * 32 * JT && j < J && kc + kk < K) ? W[(kc + kk) * J + j] : 0.f;
+    }
+    const int64_t k0 = kc + 32 * h;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      xok[q] = tvalid && k0 + 8 * q < K;
+      if (xok[q]) xr[q] = Io8<T>::ld_nt(X + trow * K + k0 + 8 * q);
+    }
+  };
+  if (c_begin < c_end) fetch(c_begin);
+  for (int64_t c = c_begin; c < c_end; ++c) {
+    __syncthreads();  // the previous chunk's reads of sW are done
+#pragma unroll
+    for (int q = 0; q < WPT; ++q) {
+      const int idx = threadIdx.x + q * 256;
+      if (idx < 64 * 32 * JT) sW[idx % (32 * JT)][idx / (32 * JT)] = wreg[q];
+    }
     float a[32];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if (tvalid && k0 + 8 * q < K) {
-        Io8<T>::load(X + trow * K + k0 + 8 * q, a + 8 * q);
+      if (xok[q]) {
+        Io8<T>::cvt(xr[q], a + 8 * q);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) a[8 * q + e] = 0.f;
       }
     }
-    float s = 0.f;
+    __syncthreads();
+    if (c + 1 < c_end) fetch(c + 1);
+    float sq = 0.f;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) s = fmaf(a[e], a[e], s);
-    ss += s;
+    for (int e = 0; e < 32; ++e) sq = fmaf(a[e], a[e], sq);
+    ss += sq;
 #pragma unroll
     for (int u = 0; u < JT; ++u) {
-      const int col = 32 * u + row;
+      float b[32];
+      const float4 *src = reinterpret_cast<const float4 *>(&sW[32 * u + row][32 * h]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 v = src[q];
+        b[4 * q] = v.x; b[4 * q + 1] = v.y; b[4 * q + 2] = v.z; b[4 * q + 3] = v.w;
+      }
       gf32x16 acc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const float b = (col < J && k0 + e < K) ? W[(k0 + e) * J + col] : 0.f;
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b, acc, 0, 0, 0);
-      }
+      for (int e = 0; e < 32; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], acc, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) outer[u][r] += acc[r];
     }
@@ -518,19 +557,14 @@ __global__ __launch_bounds__(256) void gproj_partial_kernel(const T *__restrict_
     const int col = 32 * u + row;
     if (col < J) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) red_p[wave][8 * (r >> 2) + 4 * h + (r & 3)][col] = outer[u][r];
+      for (int r = 0; r < 16; ++r) {
+        const int64_t t = tb * kGTokWG + wave * kGTok + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (t < N) part[((int64_t)slice * N + t) * PS + col] = outer[u][r];
+      }
     }
   }
   const float ss_other = __shfl_xor(ss, 32);
-  if (h == 0) red_p[wave][row][J] = ss + ss_other;
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < kGTok * PS; idx += 256) {
-    const int tt = idx / PS, j = idx % PS;
-    const int64_t t = tb * kGTok + tt;
-    if (t >= N) continue;
-    const float v = (red_p[0][tt][j] + red_p[1][tt][j]) + (red_p[2][tt][j] + red_p[3][tt][j]);
-    part[((int64_t)slice * N + t) * PS + j] = v;
-  }
+  if (h == 0 && tvalid) part[((int64_t)slice * N + trow) * PS + J] = ss + ss_other;
 }
 
 // One thread per token: slices summed in order, then RMS, gains, sigmoid;
@@ -971,7 +1005,7 @@ void glaunch_proj_fwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, cons
                       float *logits, float *saved, float *H_res, int iters, float eps, void *ws) {
   const int64_t K = (int64_t)n * C;
   float *part = (float *)ws;
-  const unsigned pb = (unsigned)(((N + kGTok - 1) / kGTok) * kGSplitK);
+  const unsigned pb = (unsigned)(((N + kGTokWG - 1) / kGTokWG) * kGSplitK);
   if (f32)
     MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_partial_kernel<float, NS>), dim3(pb), dim3(256), 0, s,
                                           (const float *)X, W, part, N, K))
