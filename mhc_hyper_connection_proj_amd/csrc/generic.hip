@@ -9,12 +9,15 @@
 // definitions, layouts, determinism (fixed-order reductions, no atomics)
 // and boundary checks, but simpler, less tuned kernels:
 //  * projection forward: split-K over 8 slices, fp32 MFMA (32x32x2) on the
-//    activations converted exactly to fp32 and W read directly from its
-//    [K][J] layout, ceil(J/32) column tiles; a per-token finalize sums the
-//    slices in order and applies RMS, gains, sigmoid and Sinkhorn;
+//    activations converted exactly to fp32, each 64-k W chunk staged once per
+//    workgroup in LDS for four waves of 32 tokens, ceil(J/32) column tiles;
+//    a per-token finalize sums the slices in order and applies RMS, gains,
+//    sigmoid and Sinkhorn;
 //  * projection backward: a per-token kernel (sigmoid / Sinkhorn backward,
-//    dp = r alpha dzh and the RMS coefficient), then a VALU kernel with one
-//    thread per k that owns W's row k and its dW row, walking a token block;
+//    dp = r alpha dzh and the RMS coefficient); in the fused pre backward a
+//    per-token pass forming the aggregate and h_post_bda residual terms in
+//    an fp32 workspace; then a VALU kernel with one thread per k that owns
+//    W's row k and its dW row, walking a token block;
 //  * Sinkhorn: one n x n matrix per thread; the backward replays the
 //    forward from checkpoints spaced ~sqrt(2 iters) half-steps apart, so it
 //    needs no storage beyond registers;
