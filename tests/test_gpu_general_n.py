@@ -231,3 +231,36 @@ def test_general_n_deterministic_and_zero_tokens():
     o = B.mhc_pre_fwd(Z, Wz)
     torch.cuda.synchronize()
     assert o["agg"].shape == (0, 64)
+
+
+@pytest.mark.parametrize("n", [2, 8])
+def test_general_n_max_width(n):
+    """C = 16384 (the largest width) with a ragged token count: pre forward and the fused
+    pre backward with the h_post_bda term, against the oracle."""
+    N, C, act = 5, 16384, "bf16"
+    log(f"general n max width n={n} N={N} C={C}")
+    X, W, alpha, hb = _proj_inputs(n, act, N, C)
+    J = n * n + 2 * n
+    o = B.mhc_pre_fwd(dev(X), dev(W), dev(alpha), dev(hb), 1e-6, 20, 1e-6)
+    torch.cuda.synchronize()
+    ref = O.pre_fwd(h64(X), h64(W), h64(alpha), h64(hb), 1e-6, 20, 1e-6)
+    assert_rel("H_pre", o["H_pre"], ref["H_pre"])
+    assert_rel("H_res", o["H_res"], ref["H_res"], rtol=2e-5)
+    assert_act("agg", o["agg"], ref["agg"], act)
+    sv = np.zeros((N, B.saved_stride(n)), np.float32)
+    sv[:, 0] = ref["r"]; sv[:, 1] = ref["q"]; sv[:, 2:2 + J] = ref["z"]
+    g = store(RNG.standard_normal((N, C)), act)
+    dHq = f32(RNG.standard_normal((N, n)))
+    dHr = f32(RNG.standard_normal((N, n, n)))
+    Gp = store(RNG.standard_normal((N, n, C)), act)
+    Hrp = f32(O.sinkhorn_fwd(RNG.standard_normal((N, n, n)), 20, 1e-6))
+    ob = B.mhc_pre_bwd(dev(g), dev(dHq), dev(dHr), dev(X), dev(W), dev(sv), dev(f32(ref["H_pre"])),
+                       dev(f32(ref["H_post"])), dev(f32(ref["L"])), alpha=dev(alpha), iters=20, eps=1e-6,
+                       post_G=dev(Gp), post_H_res=dev(Hrp))
+    torch.cuda.synchronize()
+    rb = O.pre_bwd(h64(g), h64(dHq), h64(dHr), h64(X), h64(W), h64(alpha), h64(hb), 1e-6, 20, 1e-6)
+    base = O.stream_mix_bwd(h64(Gp), h64(X), h64(Hrp))[0]
+    assert_act("dX", ob["dX"], base + rb["dX"], act)
+    aW, aa, ab = _abs_parts_pre(h64(g), h64(dHq), h64(dHr), h64(X), h64(W), h64(alpha), h64(hb))
+    assert_tokensum("dW", ob["dW"], rb["dW"], aW)
+    assert_tokensum("dalpha", ob["dalpha"], rb["dalpha"], aa)
