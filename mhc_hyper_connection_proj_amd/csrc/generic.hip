@@ -339,7 +339,7 @@ __global__ __launch_bounds__(256) void gpost_fwd_kernel(const T *__restrict__ X,
 // <G_i, x + bias> and dx = sum_i H_post[i] G_i (MODE != mix).  DBIAS: TG
 // tokens per workgroup; each thread adds its groups' dx into the workgroup's
 // partial row part[blockIdx.x][C] (owned by this thread alone: no atomics).
-// The rows j of X are taken JB at a time (JB = 2 for n > 4), each pass with
+// The rows j of X are taken JB at a time (JB = 4 for n > 4), each pass with
 // its own JB * n sums, so the per-thread sums stay few; G is re-read per pass
 // (from the caches).  The token's H values are staged in LDS first.
 template <typename T, int NS, int MODE>
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr
                                                        float *__restrict__ part, int64_t N, int64_t C, int TG) {
   const bool HAS_BIAS = bias != nullptr, WRITE_DX = dX != nullptr, DBIAS = part != nullptr;
   constexpr bool MIX = MODE != kPostDist, DIST = MODE != kPostMix;
-  constexpr int JB = NS > 4 ? 2 : NS;
+  constexpr int JB = NS > 4 ? 4 : NS;
   constexpr int NPASS = MIX ? (NS + JB - 1) / JB : 1;
   constexpr int NR = (MIX ? JB * NS : 0) + (DIST ? NS : 0);
   __shared__ float red[4][NR];
