@@ -17,6 +17,7 @@ Tolerances (stated by the benchmark spec for this path, applied element by element):
     far smaller than they are and a bound relative to the sum alone is not
     attainable in fp32.
 """
+import os
 import sys
 
 import numpy as np
@@ -46,11 +47,28 @@ def h64(a) -> np.ndarray:
     return np.asarray(a, dtype=np.float64)
 
 
+DUMP_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out", "parity_dumps")
+
+
+def _dump(name, g, o, bound):
+    """On a parity failure, keep the compared tensors (gpu, oracle, bound) for offline reading."""
+    try:
+        os.makedirs(DUMP_DIR, exist_ok=True)
+        safe = "".join(ch if ch.isalnum() else "_" for ch in name)
+        path = os.path.join(DUMP_DIR, f"{safe}_{os.getpid()}.npz")
+        np.savez_compressed(path, gpu=g, oracle=o, bound=np.broadcast_to(bound, np.shape(g)))
+        return path
+    except OSError:
+        return None
+
+
 def _report(name, g, o, bound):
     err = np.abs(g - o)
     bad = err > bound
     if bad.any():
         i = np.unravel_index(np.argmax(err - bound), err.shape)
+        path = _dump(name, g, o, bound)
+        log(f"{name}: parity failure, tensors kept in {path}")
         raise AssertionError(
             f"{name}: {bad.sum()} of {bad.size} elements out of tolerance; worst at {i}: "
             f"gpu={g[i]!r} oracle={o[i]!r} err={err[i]:.3e} bound={bound[i] if np.ndim(bound) else bound:.3e}")
