@@ -17,7 +17,7 @@ from mhc_hyper_connection_proj_amd import binding as B
 pytestmark = pytest.mark.gpu
 
 RNG = np.random.default_rng(23)
-NS = [1, 2, 3, 5, 8]
+NS = [1, 2, 3, 5, 6, 7, 8]
 
 
 def f32(a):
