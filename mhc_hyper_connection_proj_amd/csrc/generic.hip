@@ -336,12 +336,14 @@ __global__ __launch_bounds__(256) void gpost_fwd_kernel(const T *__restrict__ X,
 
 // h_post_bda backward and its halves.  Per token: dX[j] = sum_i H_res[j][i]
 // G[i] (WRITE_DX), dH_res[j][i] = <X_j, G_i> (MODE != dist), dH_post[i] =
-// <G_i, x + bias> and dx = sum_i H_post[i] G_i (MODE != mix).  DBIAS: TG
-// tokens per workgroup; each thread adds its groups' dx into the workgroup's
-// partial row part[blockIdx.x][C] (owned by this thread alone: no atomics).
-// The rows j of X are taken JB at a time (JB = 4 for n > 4), each pass with
-// its own JB * n sums, so the per-thread sums stay few; G is re-read per pass
-// (from the caches).  The token's H values are staged in LDS first.
+// <G_i, x + bias> and dx = sum_i H_post[i] G_i (MODE != mix).  One wave per
+// token, four waves per workgroup working independently: a lane owns the
+// 8-channel groups g = lane, lane + 64, ..., and the per-token sums are wave
+// reductions (no barrier).  The rows j of X are taken JB at a time (JB = 4
+// for n > 4), each pass with its own JB * n sums, so the per-lane sums stay
+// few; G is re-read per pass (from the caches).  DBIAS: each wave walks TG
+// tokens and adds its lanes' dx into its own partial row part[wave][C]
+// (owned by that lane alone: no atomics).
 template <typename T, int NS, int MODE>
 __global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr, const T *__restrict__ X,
                                                        const float *__restrict__ Hr, const float *__restrict__ Hp,
@@ -354,16 +356,12 @@ __global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr
   constexpr int JB = NS > 4 ? 4 : NS;
   constexpr int NPASS = MIX ? (NS + JB - 1) / JB : 1;
   constexpr int NR = (MIX ? JB * NS : 0) + (DIST ? NS : 0);
-  __shared__ float red[4][NR];
-  __shared__ float sH[NS * NS + NS];
+  const int lane = threadIdx.x & 63;
+  const int64_t wv = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);  // global wave index
   const int64_t G = C / 8;
-  const int64_t t0 = (int64_t)blockIdx.x * TG;
+  const int64_t t0 = wv * TG;
   const int64_t t1 = min(t0 + (int64_t)TG, N);
   for (int64_t t = t0; t < t1; ++t) {
-    __syncthreads();
-    for (int e = threadIdx.x; e < NS * NS + NS; e += blockDim.x)
-      sH[e] = e < NS * NS ? (MIX ? Hr[t * NS * NS + e] : 0.f) : (DIST ? Hp[t * NS + e - NS * NS] : 0.f);
-    __syncthreads();
 #pragma unroll 1
     for (int pass = 0; pass < NPASS; ++pass) {
       const int j0 = pass * JB;
@@ -371,7 +369,7 @@ __global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr
       float acc[NR];
 #pragma unroll
       for (int r = 0; r < NR; ++r) acc[r] = 0.f;
-      for (int64_t g = threadIdx.x; g < G; g += blockDim.x) {
+      for (int64_t g = lane; g < G; g += 64) {
         float gv[NS][8];
 #pragma unroll
         for (int i = 0; i < NS; ++i) Io8<T>::load(Gr + (t * NS + i) * C + 8 * g, gv[i]);
@@ -393,7 +391,7 @@ __global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr
                 float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int i = 0; i < NS; ++i) {
-                  const float w = sH[j * NS + i];
+                  const float w = Hr[t * NS * NS + j * NS + i];
 #pragma unroll
                   for (int e = 0; e < 8; ++e) d[e] += w * gv[i][e];
                 }
@@ -407,14 +405,14 @@ __global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr
           float xb[8], o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
           Io8<T>::load(x + t * C + 8 * g, xb);
           if (HAS_BIAS) {
-            float b[8];
-            Io8<T>::load(bias + 8 * g, b);
+            float bv[8];
+            Io8<T>::load(bias + 8 * g, bv);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) xb[e] += b[e];
+            for (int e = 0; e < 8; ++e) xb[e] += bv[e];
           }
 #pragma unroll
           for (int i = 0; i < NS; ++i) {
-            const float hp = sH[NS * NS + i];
+            const float hp = Hp[t * NS + i];
             float sdot = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -425,14 +423,15 @@ __global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr
           }
           Io8<T>::store(dx + t * C + 8 * g, o);
           if (DBIAS) {
-            float *p = part + (int64_t)blockIdx.x * C + 8 * g;
+            float *p = part + wv * C + 8 * g;
 #pragma unroll
             for (int e = 0; e < 8; ++e) p[e] = (t == t0 ? 0.f : p[e]) + o[e];
           }
         }
       }
-      gblock_sum<NR>(acc, red);
-      if (threadIdx.x == 0) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[r] = wave_sum(acc[r]);
+      if (lane == 0) {
         if (MIX) {
 #pragma unroll
           for (int jj = 0; jj < JB; ++jj)
@@ -938,10 +937,12 @@ void glaunch_stream_distribute_fwd(hipStream_t s, bool f32, int n, int64_t N, in
 
 constexpr int kGPostTG = 16;
 
+// dbias partial rows: one per wave slot of the grid (ceil(N / TG) waves rounded up to whole workgroups)
+static int64_t gpost_rows(int64_t N) { return ((N + kGPostTG - 1) / kGPostTG + 3) / 4 * 4; }
+
 size_t gh_post_bda_bwd_ws(int64_t N, int64_t C, bool with_dbias) {
   if (!with_dbias) return 0;
-  const int64_t rows = (N + kGPostTG - 1) / kGPostTG;
-  return (size_t)((rows + kRowSumSlices) * C) * sizeof(float);
+  return (size_t)((gpost_rows(N) + kRowSumSlices) * C) * sizeof(float);
 }
 
 // part != NULL: dbias partial rows (TG tokens per workgroup), else one token per workgroup.
@@ -950,8 +951,9 @@ static void gpost_bwd5(hipStream_t s, int n, int64_t N, int64_t C, const void *G
                        const float *Hp, const void *x, const void *b, void *dX, float *dHr, float *dHp, void *dx,
                        float *part) {
   const int TG = part ? kGPostTG : 1;
-  const unsigned blocks = (unsigned)((N + TG - 1) / TG);
-  MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gpost_bwd_kernel<T, NS, MODE>), dim3(blocks), dim3(gtpb(C)), 0, s,
+  const int64_t waves = (N + TG - 1) / TG;  // one wave per TG tokens, four waves per workgroup
+  const unsigned blocks = (unsigned)((waves + 3) / 4);
+  MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gpost_bwd_kernel<T, NS, MODE>), dim3(blocks), dim3(256), 0, s,
                                         (const T *)G, (const T *)X, Hr, Hp, (const T *)x, (const T *)b, (T *)dX,
                                         dHr, dHp, (T *)dx, part, N, C, TG));
 }
@@ -963,8 +965,8 @@ static void gpost_bwd(hipStream_t s, int n, int64_t N, int64_t C, const void *G,
   if (b && db) {
     float *part = (float *)ws;
     gpost_bwd5<T, kPostFull>(s, n, N, C, G, X, Hr, Hp, x, b, dX, dHr, dHp, dx, part);
-    const int64_t rows = (N + kGPostTG - 1) / kGPostTG;
-    launch_rows_sum(s, part, rows, C, part + rows * C, db, sizeof(T) == 2);
+    const int64_t waves = (N + kGPostTG - 1) / kGPostTG, rows = gpost_rows(N);
+    launch_rows_sum(s, part, waves, C, part + rows * C, db, sizeof(T) == 2);
   } else {
     gpost_bwd5<T, kPostFull>(s, n, N, C, G, X, Hr, Hp, x, b, dX, dHr, dHp, dx, nullptr);
   }
