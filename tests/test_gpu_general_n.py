@@ -264,3 +264,45 @@ def test_general_n_max_width(n):
     aW, aa, ab = _abs_parts_pre(h64(g), h64(dHq), h64(dHr), h64(X), h64(W), h64(alpha), h64(hb))
     assert_tokensum("dW", ob["dW"], rb["dW"], aW)
     assert_tokensum("dalpha", ob["dalpha"], rb["dalpha"], aa)
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("n,C", [(2, 1032), (8, 296)])
+def test_general_n_per_token_results_batch_invariant(n, C):
+    """As for n = 4: the same 37 tokens alone and at rows 700..736 of a 1300-token batch give the
+    same bits for every per-token output (sums over tokens excluded)."""
+    n_small, n_big, at = 37, 1300, 700
+    log(f"general n batch invariance n={n} C={C}")
+    act = "bf16"
+    Xb, W, alpha, hb = _proj_inputs(n, act, n_big, C)
+    Gb = store(RNG.standard_normal((n_big, n, C)), act)
+    xb = store(RNG.standard_normal((n_big, C)), act)
+    gb = store(RNG.standard_normal((n_big, C)), act)
+    bias = store(RNG.standard_normal(C) * 0.1, act)
+    dHpb = f32(RNG.standard_normal((n_big, n)))
+    dHrb = f32(RNG.standard_normal((n_big, n, n)))
+    sl = slice(at, at + n_small)
+
+    def run(X, G, x, g, dHp, dHr):
+        r = {}
+        o = B.mhc_pre_fwd(dev(X), dev(W), dev(alpha), dev(hb))
+        r.update({f"pre_fwd.{k}": v for k, v in o.items()})
+        r["sk_bwd"] = B.mhc_sinkhorn_bwd(dev(dHr), o["H_res_logits"])
+        r["post_fwd"] = B.mhc_h_post_bda_fwd(dev(X), o["H_res"], o["H_post"], dev(x), dev(bias))
+        pdX, pdHr, pdHp, pdx, _ = B.mhc_h_post_bda_bwd(dev(G), dev(X), o["H_res"], o["H_post"], dev(x), dev(bias),
+                                                       want_dbias=False)
+        r.update({"post_bwd.dX": pdX, "post_bwd.dH_res": pdHr, "post_bwd.dH_post": pdHp, "post_bwd.dx": pdx})
+        bw = B.mhc_pre_bwd(dev(g), dev(dHp), dev(dHr), dev(X), dev(W), o["saved"], o["H_pre"], o["H_post"],
+                           o["H_res_logits"], alpha=dev(alpha), want_intermediates=True, post_G=dev(G),
+                           post_H_res=o["H_res"])
+        r.update({"pre_bwd.dX": bw["dX"], "pre_bwd.dH_pre": bw["dH_pre"], "pre_bwd.dlogits": bw["dlogits"]})
+        torch.cuda.synchronize()
+        return r
+
+    big = run(Xb, Gb, xb, gb, dHpb, dHrb)
+    small = run(*(np.ascontiguousarray(a[sl]) for a in (Xb, Gb, xb, gb, dHpb, dHrb)))
+    for k, v in small.items():
+        assert torch.equal(_bits(v), _bits(big[k][sl])), f"{k}: per-token result depends on the batch"
