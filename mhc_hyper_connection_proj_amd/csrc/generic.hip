@@ -190,6 +190,101 @@ __device__ void sk_backward(const float *L, float dm[NS * NS], int iters, float 
   for (int e = 0; e < NS * NS; ++e) dm[e] *= m[e];
 }
 
+// The same gradient with each half-step's line sums kept instead of
+// replayed: one forward pass records e_a = s_a + eps per line, and the state
+// at every kSkCkpt-th half-step, in the caller's thread-private LDS slots
+// (word w of the thread at es[w * stride]); the reverse walk takes each
+// half-step's output M', applies the half-step backward with d = 1/e (the
+// forward's reciprocal, recomputed bit-identically) and rebuilds the
+// half-step's input as M' e, restarting from the exact recorded state at
+// every checkpoint so that rebuilt states carry at most kSkCkpt - 1
+// roundings (rebuilding across all 40 half-steps of 20 iterations had put
+// n = 5 gradients ~5e-6 off).  2 iters half-steps forward and back instead
+// of ~2 iters sqrt(2 iters).
+constexpr int kSkCkpt = 8;
+
+inline size_t sk_stored_words(int n, int iters) {
+  const int H = 2 * iters;
+  return (size_t)H * n + (size_t)((H + kSkCkpt - 1) / kSkCkpt) * n * n;
+}
+
+template <int NS>
+__device__ void sk_backward_stored(const float *L, float dm[NS * NS], int iters, float eps, float *es,
+                                   int stride) {
+  const int H = 2 * iters;
+  float *ck = es + (size_t)H * NS * stride;  // checkpoints: state before half-steps 0, kSkCkpt, ...
+  float m[NS * NS];
+  sk_exp<NS>(L, m);
+  for (int h = 0; h < H; ++h) {
+    if (h % kSkCkpt == 0) {
+#pragma unroll
+      for (int e = 0; e < NS * NS; ++e) ck[((h / kSkCkpt) * NS * NS + e) * stride] = m[e];
+    }
+    const bool rows = (h & 1) == 0;
+#pragma unroll
+    for (int a = 0; a < NS; ++a) {
+      float sum = 0.f;
+#pragma unroll
+      for (int b = 0; b < NS; ++b) sum += m[rows ? a * NS + b : b * NS + a];
+      const float e = sum + eps;
+      es[(h * NS + a) * stride] = e;
+      const float d = 1.0f / e;
+#pragma unroll
+      for (int b = 0; b < NS; ++b) m[rows ? a * NS + b : b * NS + a] *= d;
+    }
+  }
+  for (int h = H - 1; h >= 0; --h) {
+    if ((h + 1) % kSkCkpt == 0 && h + 1 < H) {  // exact state after half-step h
+#pragma unroll
+      for (int e = 0; e < NS * NS; ++e) m[e] = ck[(((h + 1) / kSkCkpt) * NS * NS + e) * stride];
+    }
+    const bool rows = (h & 1) == 0;
+#pragma unroll
+    for (int a = 0; a < NS; ++a) {
+      const float e = es[(h * NS + a) * stride];
+      const float d = 1.0f / e;
+      float mp[NS], g[NS], o[NS];
+#pragma unroll
+      for (int b = 0; b < NS; ++b) {
+        const int el = rows ? a * NS + b : b * NS + a;
+        mp[b] = m[el];
+        g[b] = dm[el];
+      }
+#pragma unroll
+      for (int b = 0; b < NS; ++b) {
+        float acc = g[b] * (eps * d);
+#pragma unroll
+        for (int bp = 0; bp < NS; ++bp) acc += (g[b] - g[bp]) * mp[bp];
+        o[b] = d * acc;
+      }
+#pragma unroll
+      for (int b = 0; b < NS; ++b) {
+        const int el = rows ? a * NS + b : b * NS + a;
+        dm[el] = o[b];
+        m[el] = mp[b] * e;
+      }
+    }
+  }
+  sk_exp<NS>(L, m);
+#pragma unroll
+  for (int e = 0; e < NS * NS; ++e) dm[e] *= m[e];
+}
+
+// Threads per block and whether the recorded sums and checkpoints fit in
+// LDS (64 KB of dynamic LDS per block) for a Sinkhorn backward of `iters`
+// iterations.
+struct SkBwdGeom {
+  int threads;
+  bool stored;
+  size_t lds;
+};
+inline SkBwdGeom sk_bwd_geom(int n, int iters) {
+  const size_t per = sk_stored_words(n, iters) * sizeof(float);
+  for (int t : {64, 32, 16})
+    if (per * t <= 65536) return {t, true, per * t};
+  return {64, false, 0};
+}
+
 template <int NS>
 __global__ __launch_bounds__(64) void gsinkhorn_fwd_kernel(int64_t count, const float *__restrict__ L,
                                                           float *__restrict__ H, int iters, float eps) {
@@ -201,16 +296,20 @@ __global__ __launch_bounds__(64) void gsinkhorn_fwd_kernel(int64_t count, const 
   for (int e = 0; e < NS * NS; ++e) H[i * NS * NS + e] = m[e];
 }
 
-template <int NS>
+template <int NS, bool STORED>
 __global__ __launch_bounds__(64) void gsinkhorn_bwd_kernel(int64_t count, const float *__restrict__ dH,
                                                           const float *__restrict__ L, float *__restrict__ dL,
                                                           int iters, float eps) {
-  const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  extern __shared__ float sk_lds[];  // STORED: line sums, thread-private slots
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= count) return;
   float dm[NS * NS];
 #pragma unroll
   for (int e = 0; e < NS * NS; ++e) dm[e] = dH[i * NS * NS + e];
-  sk_backward<NS>(L + i * NS * NS, dm, iters, eps);
+  if (STORED)
+    sk_backward_stored<NS>(L + i * NS * NS, dm, iters, eps, sk_lds + threadIdx.x, blockDim.x);
+  else
+    sk_backward<NS>(L + i * NS * NS, dm, iters, eps);
 #pragma unroll
   for (int e = 0; e < NS * NS; ++e) dL[i * NS * NS + e] = dm[e];
 }
@@ -625,15 +724,16 @@ __global__ __launch_bounds__(64) void gproj_finalize_kernel(const float *__restr
 // {dp[0..J) = r alpha dzh, c_rms = -r sum_j dz_j z_j / (K q) (0 if q == 0)};
 // prm[t] = {dzh[0..J) (dhbias terms), sum_seg dzh z (dalpha terms, 3)}.
 // dH_res and the logits (Sinkhorn backward) replace dL when dL == NULL.
-template <int NS>
+template <int NS, bool STORED>
 __global__ __launch_bounds__(64) void gproj_bwd_token_kernel(
     int64_t N, int64_t K, const float *__restrict__ alpha, const float *__restrict__ saved, int SS,
     const float *__restrict__ Hpre, const float *__restrict__ Hpost, const float *__restrict__ dHpre,
     const float *__restrict__ dHpost, const float *__restrict__ dL, const float *__restrict__ dHres,
     const float *__restrict__ logits, int iters, float eps, float *__restrict__ rec, float *__restrict__ prm,
     float *__restrict__ dL_out) {
+  extern __shared__ float sk_lds[];  // STORED: Sinkhorn line sums, thread-private slots
   constexpr int J = Dim<NS>::J;
-  const int64_t t = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= N) return;
   const float r = saved[t * SS], q = saved[t * SS + 1];
   const float al[3] = {alpha ? alpha[0] : 1.f, alpha ? alpha[1] : 1.f, alpha ? alpha[2] : 1.f};
@@ -644,7 +744,10 @@ __global__ __launch_bounds__(64) void gproj_bwd_token_kernel(
   } else {
 #pragma unroll
     for (int e = 0; e < NS * NS; ++e) dl[e] = dHres[t * NS * NS + e];
-    sk_backward<NS>(logits + t * NS * NS, dl, iters, eps);
+    if (STORED)
+      sk_backward_stored<NS>(logits + t * NS * NS, dl, iters, eps, sk_lds + threadIdx.x, blockDim.x);
+    else
+      sk_backward<NS>(logits + t * NS * NS, dl, iters, eps);
   }
   if (dL_out) {
 #pragma unroll
@@ -859,9 +962,14 @@ void glaunch_sinkhorn_fwd(hipStream_t s, int n, int64_t count, const float *L, f
 
 void glaunch_sinkhorn_bwd(hipStream_t s, int n, int64_t count, const float *dH, const float *L, float *dL,
                           int iters, float eps) {
-  const unsigned b = (unsigned)((count + 63) / 64);
-  MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gsinkhorn_bwd_kernel<NS>), dim3(b), dim3(64), 0, s, count, dH, L, dL,
-                                        iters, eps));
+  const SkBwdGeom g = sk_bwd_geom(n, iters);
+  const unsigned b = (unsigned)((count + g.threads - 1) / g.threads);
+  if (g.stored)
+    MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gsinkhorn_bwd_kernel<NS, true>), dim3(b), dim3(g.threads), g.lds, s,
+                                          count, dH, L, dL, iters, eps))
+  else
+    MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gsinkhorn_bwd_kernel<NS, false>), dim3(b), dim3(g.threads), 0, s,
+                                          count, dH, L, dL, iters, eps))
 }
 
 void glaunch_h_aggregate_fwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *X,
@@ -1065,10 +1173,17 @@ void glaunch_proj_bwd(hipStream_t s, int n, const ProjBwdArgs &a) {
       gagg_bwd<bf16_t>(s, n, a.N, a.C, a.g, a.X, a.H_pre, n, nullptr, false, rows);
     dHpre = rows;
   }
-  const unsigned tb = (unsigned)((a.N + 63) / 64);
-  MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_bwd_token_kernel<NS>), dim3(tb), dim3(64), 0, s, a.N, K, a.alpha,
-                                        a.saved, saved_stride(n), a.H_pre, a.H_post, dHpre, a.dH_post, a.dL,
-                                        a.dH_res, a.logits, a.iters, a.eps, rec, prm, a.dL_out));
+  // the Sinkhorn backward runs here only when the logits' gradient is not given
+  const SkBwdGeom g = a.dL ? SkBwdGeom{64, false, 0} : sk_bwd_geom(n, a.iters);
+  const unsigned tb = (unsigned)((a.N + g.threads - 1) / g.threads);
+  if (g.stored)
+    MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_bwd_token_kernel<NS, true>), dim3(tb), dim3(g.threads), g.lds, s,
+                                          a.N, K, a.alpha, a.saved, saved_stride(n), a.H_pre, a.H_post, dHpre,
+                                          a.dH_post, a.dL, a.dH_res, a.logits, a.iters, a.eps, rec, prm, a.dL_out))
+  else
+    MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_bwd_token_kernel<NS, false>), dim3(tb), dim3(g.threads), 0, s,
+                                          a.N, K, a.alpha, a.saved, saved_stride(n), a.H_pre, a.H_post, dHpre,
+                                          a.dH_post, a.dL, a.dH_res, a.logits, a.iters, a.eps, rec, prm, a.dL_out))
   if (terms) {
     if (a.f32)
       gterms<float>(s, n, a, term);
