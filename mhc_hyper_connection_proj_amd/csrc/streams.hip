@@ -398,6 +398,145 @@ __global__ __launch_bounds__(256) void h_post_bda_bwd_kernel(
   }
 }
 
+// ---------------------------------------------- h_post_bda bwd with dbias, bf16
+// The kernel above walks a workgroup's 16 tokens one after another and issues
+// a token's loads only once the previous token is done; with the bias
+// gradient its N/16 workgroups fill the GPU about once, so no other
+// workgroup hides that latency.  For bf16 rows of up to 1024 8-channel groups
+// this kernel gives each thread one group (a workgroup spans the row) and
+// loads token t + 1 while token t is computed: two register sets used in
+// turn, every load unconditional (a lane past C/8 re-reads the last group and
+// neither stores nor sums it), so the wait for one set counts only the loads
+// issued after it.  Results per token and the dbias partial rows follow the
+// same arithmetic as above with one group per thread.
+struct PostRowsBf16 {
+  nt_u32x4 g[4], X[4], x;
+};
+
+__device__ __forceinline__ void post_rows_issue(PostRowsBf16 &r, const bf16_t *__restrict__ Gr,
+                                                const bf16_t *__restrict__ X, const bf16_t *__restrict__ x,
+                                                int64_t t, int64_t C, int c8) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.g[i] = Io8<bf16_t>::ld_nt(Gr + (t * 4 + i) * C + c8);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.X[i] = Io8<bf16_t>::ld_nt(X + (t * 4 + i) * C + c8);
+  r.x = Io8<bf16_t>::ld_nt(x + t * C + c8);
+}
+
+template <bool DXO>
+__device__ __forceinline__ void post_rows_compute(const PostRowsBf16 &r, const float *__restrict__ Hres,
+                                                  const float *__restrict__ Hpost, nt_u32x4 braw,
+                                                  bf16_t *__restrict__ dX, bf16_t *__restrict__ dx, float dbp[8],
+                                                  float *__restrict__ red, int64_t t, int tt, int64_t C, int c8,
+                                                  bool live) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float gv[4][8], lv[8], bv[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) Io8<bf16_t>::cvt(r.g[i], gv[i]);
+  Io8<bf16_t>::cvt(r.x, lv);
+  Io8<bf16_t>::cvt(braw, bv);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) lv[e] += bv[e];
+  if (DXO) {
+#pragma unroll
+    for (int js = 0; js < 4; ++js) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        o[e] = (Hres[t * 16 + js * 4 + 0] * gv[0][e] + Hres[t * 16 + js * 4 + 1] * gv[1][e]) +
+               (Hres[t * 16 + js * 4 + 2] * gv[2][e] + Hres[t * 16 + js * 4 + 3] * gv[3][e]);
+      if (live) Io8<bf16_t>::store(dX + (t * 4 + js) * C + c8, o);
+    }
+  }
+  {
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      o[e] = (Hpost[t * 4 + 0] * gv[0][e] + Hpost[t * 4 + 1] * gv[1][e]) +
+             (Hpost[t * 4 + 2] * gv[2][e] + Hpost[t * 4 + 3] * gv[3][e]);
+    if (live) {
+      Io8<bf16_t>::store(dx + t * C + c8, o);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dbp[e] += o[e];
+    }
+  }
+  // dH_res[js][i] = X[js] . G[i], dH_post[i] = G[i] . (x + bias), each summed
+  // over the wave as soon as it is formed
+#pragma unroll
+  for (int js = 0; js < 4; ++js) {
+    float xv[8];
+    Io8<bf16_t>::cvt(r.X[js], xv);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a += xv[e] * gv[i][e];
+      const float sum = wave_sum(live ? a : 0.f);
+      if (lane == 0) red[(wave * kPostTG + tt) * 20 + js * 4 + i] = sum;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float a = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a += gv[i][e] * lv[e];
+    const float sum = wave_sum(live ? a : 0.f);
+    if (lane == 0) red[(wave * kPostTG + tt) * 20 + 16 + i] = sum;
+  }
+}
+
+template <bool DXO>
+__global__ __launch_bounds__(1024) void h_post_bda_bwd_dbias_bf16_kernel(
+    const bf16_t *__restrict__ Gr, const bf16_t *__restrict__ X, const float *__restrict__ Hres,
+    const float *__restrict__ Hpost, const bf16_t *__restrict__ x, const bf16_t *__restrict__ bias,
+    bf16_t *__restrict__ dX, float *__restrict__ dHres, float *__restrict__ dHpost, bf16_t *__restrict__ dx,
+    float *__restrict__ dbias_part, int64_t N, int64_t C) {
+  extern __shared__ float red[];  // [nwaves][kPostTG][20]
+  const int G = (int)(C / 8);
+  const bool live = (int)threadIdx.x < G;
+  const int c8 = 8 * min((int)threadIdx.x, G - 1);
+  const int64_t t0 = ((int64_t)gridDim.x - 1 - blockIdx.x) * kPostTG;  // last tokens first
+  const int ntok = (int)min((int64_t)kPostTG, N - t0);
+  float dbp[8];
+  const nt_u32x4 braw = *reinterpret_cast<const nt_u32x4 *>(bias + c8);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dbp[e] = 0.f;
+  PostRowsBf16 ra, rb;
+  post_rows_issue(ra, Gr, X, x, t0, C, c8);
+  int tt = 0;
+  // two tokens per trip, both prefetches unconditional inside the loop
+  for (; tt + 2 < ntok; tt += 2) {
+    post_rows_issue(rb, Gr, X, x, t0 + tt + 1, C, c8);
+    post_rows_compute<DXO>(ra, Hres, Hpost, braw, dX, dx, dbp, red, t0 + tt, tt, C, c8, live);
+    post_rows_issue(ra, Gr, X, x, t0 + tt + 2, C, c8);
+    post_rows_compute<DXO>(rb, Hres, Hpost, braw, dX, dx, dbp, red, t0 + tt + 1, tt + 1, C, c8, live);
+  }
+  if (tt + 1 < ntok) {
+    post_rows_issue(rb, Gr, X, x, t0 + tt + 1, C, c8);
+    post_rows_compute<DXO>(ra, Hres, Hpost, braw, dX, dx, dbp, red, t0 + tt, tt, C, c8, live);
+    post_rows_compute<DXO>(rb, Hres, Hpost, braw, dX, dx, dbp, red, t0 + tt + 1, tt + 1, C, c8, live);
+  } else {
+    post_rows_compute<DXO>(ra, Hres, Hpost, braw, dX, dx, dbp, red, t0 + tt, tt, C, c8, live);
+  }
+  __syncthreads();
+  const int nw = blockDim.x >> 6;
+  for (int k = threadIdx.x; k < ntok * 20; k += blockDim.x) {
+    const int t1 = k / 20, e = k % 20;
+    float s = 0.f;
+    for (int w = 0; w < nw; ++w) s += red[(w * kPostTG + t1) * 20 + e];
+    const int64_t t = t0 + t1;
+    if (e < 16)
+      dHres[t * 16 + e] = s;
+    else
+      dHpost[t * 4 + (e - 16)] = s;
+  }
+  if (live) {
+    float *p = dbias_part + (t0 / kPostTG) * C + c8;
+    *reinterpret_cast<float4 *>(p) = make_float4(dbp[0], dbp[1], dbp[2], dbp[3]);
+    *reinterpret_cast<float4 *>(p + 4) = make_float4(dbp[4], dbp[5], dbp[6], dbp[7]);
+  }
+}
+
 // ============================================================ launchers
 #define MHC_GPT_DISPATCH(GPT_VAL, ...)                       \
   switch (GPT_VAL) {                                         \
@@ -543,8 +682,21 @@ static void post_bwd(hipStream_t s, int64_t N, int64_t C, const void *G, const v
                      float *dHr, float *dHp, void *dx, void *db, void *ws) {
   if (b && db) {
     float *part = (float *)ws;
-    post_bwd3<T, true, true>(s, N, C, G, X, Hr, Hp, x, b, dX, dHr, dHp, dx, part);
     const int64_t rows = (N + kPostTG - 1) / kPostTG;
+    if (sizeof(T) == 2 && C / 8 <= 1024) {
+      const unsigned tpb = (unsigned)((C / 8 + 63) / 64 * 64);
+      const size_t lds = (size_t)(tpb / 64) * kPostTG * 20 * sizeof(float);
+      if (dX)
+        hipLaunchKernelGGL(h_post_bda_bwd_dbias_bf16_kernel<true>, dim3((unsigned)rows), dim3(tpb), lds, s,
+                           (const bf16_t *)G, (const bf16_t *)X, Hr, Hp, (const bf16_t *)x, (const bf16_t *)b,
+                           (bf16_t *)dX, dHr, dHp, (bf16_t *)dx, part, N, C);
+      else
+        hipLaunchKernelGGL(h_post_bda_bwd_dbias_bf16_kernel<false>, dim3((unsigned)rows), dim3(tpb), lds, s,
+                           (const bf16_t *)G, (const bf16_t *)X, Hr, Hp, (const bf16_t *)x, (const bf16_t *)b,
+                           nullptr, dHr, dHp, (bf16_t *)dx, part, N, C);
+    } else {
+      post_bwd3<T, true, true>(s, N, C, G, X, Hr, Hp, x, b, dX, dHr, dHp, dx, part);
+    }
     launch_rows_sum(s, part, rows, C, part + rows * C, db, sizeof(T) == 2);
   } else if (b) {
     post_bwd3<T, true, false>(s, N, C, G, X, Hr, Hp, x, b, dX, dHr, dHp, dx, nullptr);
