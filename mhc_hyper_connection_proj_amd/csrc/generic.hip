@@ -668,6 +668,134 @@ __global__ __launch_bounds__(256) void gproj_partial_kernel(const T *__restrict_
   if (h == 0 && tvalid) part[((int64_t)slice * N + trow) * PS + J] = ss + ss_other;
 }
 
+// bf16 activations: the same blocking on the bf16 MFMA (32x32x16).  Each W
+// value is split exactly into three bf16 terms (hi = W rounded to bf16,
+// mid = the rest rounded, lo = what remains: 8 + 8 + 8 significant bits
+// cover fp32's 24), and bf16 x times a bf16 term is exact in the fp32
+// accumulator, so the three products give x @ W to fp32 accumulation.  The
+// chunk's terms sit in LDS as [term][column][k]; a lane's A operand is the
+// 8 x values it already holds (k = 32h + 8q .. +8 for MFMA q) and its B
+// operand the same 8 k of its column, read as one 16-byte LDS access (the k
+// order inside an MFMA is free as long as A and B agree).
+typedef __attribute__((ext_vector_type(8))) __bf16 gbf16x8;
+
+template <int NS>
+__global__ __launch_bounds__(256) void gproj_partial_bf16_kernel(const bf16_t *__restrict__ X,
+                                                                const float *__restrict__ W,
+                                                                float *__restrict__ part, int64_t N, int64_t K) {
+  constexpr int J = Dim<NS>::J, JT = Dim<NS>::JT, PS = Dim<NS>::PS;
+  constexpr int SWB = 64 + 8;  // LDS row stride of a term's [column][k] rows (bf16; 144 bytes)
+  __shared__ __align__(16) uint16_t sWb[3][32 * JT][SWB];
+  const int slice = blockIdx.x % kGSplitK;
+  const int64_t tb = blockIdx.x / kGSplitK;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = lane & 31, h = lane >> 5;
+  const int64_t nch = (K + 63) / 64;
+  const int64_t cps = (nch + kGSplitK - 1) / kGSplitK;
+  const int64_t c_begin = slice * cps;
+  const int64_t c_end = min(nch, c_begin + cps);
+  const int64_t trow = tb * kGTokWG + wave * kGTok + row;
+  const bool tvalid = trow < N;
+
+  gf32x16 outer[JT];
+#pragma unroll
+  for (int u = 0; u < JT; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) outer[u][r] = 0.f;
+  float ss = 0.f;
+
+  // W is taken as (k, k + 1) pairs of one column, so each term's pair is one
+  // 32-bit LDS store; the next chunk's pairs and x groups are loaded while
+  // the current chunk is multiplied.
+  constexpr int NPAIR = 32 * 32 * JT;            // k pairs x columns per chunk
+  constexpr int PPT = (NPAIR + 255) / 256;       // pairs per thread
+  using R = Io8<bf16_t>::raw_t;
+  float wlo[PPT], whi[PPT];
+  R xr[4];
+  bool xok[4];
+  auto fetch = [&](int64_t c) {
+    const int64_t kc = c * 64;
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) {
+      const int idx = threadIdx.x + q * 256;
+      const int kp = idx / (32 * JT), j = idx % (32 * JT);
+      const int64_t k = kc + 2 * kp;
+      const bool ok = idx < NPAIR && j < J;
+      wlo[q] = (ok && k < K) ? W[k * J + j] : 0.f;
+      whi[q] = (ok && k + 1 < K) ? W[(k + 1) * J + j] : 0.f;
+    }
+    const int64_t k0 = kc + 32 * h;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      xok[q] = tvalid && k0 + 8 * q < K;
+      xr[q] = xok[q] ? Io8<bf16_t>::ld_nt(X + trow * K + k0 + 8 * q) : R{0u, 0u, 0u, 0u};
+    }
+  };
+  if (c_begin < c_end) fetch(c_begin);
+  for (int64_t c = c_begin; c < c_end; ++c) {
+    __syncthreads();  // the previous chunk's reads of sWb are done
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) {
+      const int idx = threadIdx.x + q * 256;
+      if (idx < NPAIR) {
+        const int kp = idx / (32 * JT), j = idx % (32 * JT);
+        const float a0 = wlo[q], a1 = whi[q];
+        const float h0 = (float)(__bf16)a0, h1 = (float)(__bf16)a1;
+        const float r0 = a0 - h0, r1 = a1 - h1;
+        const float m0 = (float)(__bf16)r0, m1 = (float)(__bf16)r1;
+        *reinterpret_cast<uint32_t *>(&sWb[0][j][2 * kp]) = pack_bf16x2(h0, h1);
+        *reinterpret_cast<uint32_t *>(&sWb[1][j][2 * kp]) = pack_bf16x2(m0, m1);
+        *reinterpret_cast<uint32_t *>(&sWb[2][j][2 * kp]) = pack_bf16x2(r0 - m0, r1 - m1);
+      }
+    }
+    R xa[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xa[q] = xr[q];
+    __syncthreads();
+    if (c + 1 < c_end) fetch(c + 1);
+    float sq = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float v[8];
+      Io8<bf16_t>::cvt(xa[q], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sq = fmaf(v[e], v[e], sq);
+    }
+    ss += sq;
+#pragma unroll
+    for (int u = 0; u < JT; ++u) {
+      gf32x16 acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const gbf16x8 a = __builtin_bit_cast(gbf16x8, xa[q]);
+#pragma unroll
+        for (int term = 0; term < 3; ++term) {
+          const uint4 bw = *reinterpret_cast<const uint4 *>(&sWb[term][32 * u + row][32 * h + 8 * q]);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(gbf16x8, bw), acc, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) outer[u][r] += acc[r];
+    }
+  }
+  // accumulator layout as in the fp32 kernel above
+#pragma unroll
+  for (int u = 0; u < JT; ++u) {
+    const int col = 32 * u + row;
+    if (col < J) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t t = tb * kGTokWG + wave * kGTok + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (t < N) part[((int64_t)slice * N + t) * PS + col] = outer[u][r];
+      }
+    }
+  }
+  const float ss_other = __shfl_xor(ss, 32);
+  if (h == 0 && tvalid) part[((int64_t)slice * N + trow) * PS + J] = ss + ss_other;
+}
+
 // One thread per token: slices summed in order, then RMS, gains, sigmoid;
 // saved[t] = {r, q, z[0..J), 0...} (stride SS); Sinkhorn when Hres != NULL.
 template <int NS>
@@ -1123,7 +1251,7 @@ void glaunch_proj_fwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, cons
     MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_partial_kernel<float, NS>), dim3(pb), dim3(256), 0, s,
                                           (const float *)X, W, part, N, K))
   else
-    MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_partial_kernel<bf16_t, NS>), dim3(pb), dim3(256), 0, s,
+    MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_partial_bf16_kernel<NS>), dim3(pb), dim3(256), 0, s,
                                           (const bf16_t *)X, W, part, N, K))
   const unsigned fb = (unsigned)((N + 63) / 64);
   MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_finalize_kernel<NS>), dim3(fb), dim3(64), 0, s, part, N, K, alpha,
