@@ -47,7 +47,7 @@ template <int NS> struct Dim {
 constexpr int kGSplitK = 8;   // k slices of the forward projection
 constexpr int kGTok = 32;     // tokens per wave in the forward projection (one MFMA tile)
 constexpr int kGBwdK = 256;   // k per backward workgroup (one per thread)
-constexpr int kGMaxTB = 64;   // at most this many token blocks in the backward
+constexpr int kGMaxTB = 32;   // at most this many token blocks in the backward
 constexpr int64_t kGDwBudget = 512ll << 20;  // bytes of dW partials the token blocks may take
 
 // ------------------------------------------------------------------ helpers
