@@ -94,7 +94,10 @@ def test_h_aggregate_one_hot_exact():
 @pytest.mark.parametrize("act,N,C,bias", [
     ("bf16", 1, 256, True), ("bf16", 37, 296, True), ("bf16", 50, 4096, True), ("bf16", 21, 7168, False),
     ("f32", 64, 256, True), ("f32", 17, 1032, False), ("bf16", 33, 8, True), ("bf16", 3, 16384, True),
-    ("bf16", 9, 5120, False), ("bf16", 6, 6144, True), ("bf16", 4, 8192, False), ("bf16", 5, 7168, True)])
+    ("bf16", 9, 5120, False), ("bf16", 6, 6144, True), ("bf16", 4, 8192, False), ("bf16", 5, 7168, True),
+    # with dbias, bf16 rows of up to 1024 8-channel groups take the one-token-ahead kernel (C = 8192: a
+    # 1024-thread workgroup); C = 8200 is the first width that falls back to the four-groups-per-thread form
+    ("bf16", 19, 8192, True), ("bf16", 7, 8200, True)])
 def test_h_post_bda(act, N, C, bias):
     log(f"h_post_bda act={act} N={N} C={C} bias={bias}")
     X = store(RNG.standard_normal((N, 4, C)), act)
