@@ -285,6 +285,123 @@ inline SkBwdGeom sk_bwd_geom(int n, int iters) {
   return {64, false, 0};
 }
 
+// Row per lane: the same gradient with token i's n rows on n lanes of a
+// group of GW = n rounded up to a power of two (lanes past n hold zeros and
+// only join the shuffles).  A row pass is in-lane; in a column pass each lane
+// reads column b of every row of its group by shuffles and takes the sums
+// and the half-step backward in the per-token form's order, so the result
+// is the per-token stored form's, operation for operation.  Lane a records e
+// of its row (row pass) or of column a (column pass) for every half-step, and
+// its row at every kSkCkpt-th half-step, in its own LDS slots (word w at
+// lds[w * blockDim]).
+constexpr int sk_group(int n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8; }
+
+inline size_t sk_lane_words(int n, int iters) {
+  const int H = 2 * iters;
+  return (size_t)H + (size_t)((H + kSkCkpt - 1) / kSkCkpt) * n;
+}
+
+template <int NS>
+__global__ __launch_bounds__(256) void gsinkhorn_bwd_lanes_kernel(int64_t count, const float *__restrict__ dH,
+                                                                 const float *__restrict__ L,
+                                                                 float *__restrict__ dL, int iters, float eps) {
+  constexpr int GW = sk_group(NS);
+  extern __shared__ float sk_lds[];
+  const int T = blockDim.x;
+  float *my = sk_lds + threadIdx.x;
+  const int64_t i = ((int64_t)blockIdx.x * T + threadIdx.x) / GW;
+  const int a = threadIdx.x % GW;
+  const int base = (threadIdx.x & 63) - a;  // the group's first lane within the wave
+  const bool act = a < NS && i < count;
+  const int H = 2 * iters;
+  float *ck = my + (size_t)H * T;
+  float m[NS], dm[NS];
+#pragma unroll
+  for (int b = 0; b < NS; ++b) {
+    m[b] = act ? __expf(L[(i * NS + a) * NS + b]) : 0.f;
+    dm[b] = act ? dH[(i * NS + a) * NS + b] : 0.f;
+  }
+  // forward, recording line sums (+ eps) and checkpoints
+  for (int h = 0; h < H; ++h) {
+    if (h % kSkCkpt == 0) {
+#pragma unroll
+      for (int b = 0; b < NS; ++b) ck[((h / kSkCkpt) * NS + b) * T] = m[b];
+    }
+    if ((h & 1) == 0) {
+      float sum = 0.f;
+#pragma unroll
+      for (int b = 0; b < NS; ++b) sum += m[b];
+      const float e = sum + eps;
+      my[h * T] = e;
+      const float d = act ? 1.0f / e : 0.f;
+#pragma unroll
+      for (int b = 0; b < NS; ++b) m[b] *= d;
+    } else {
+      float mine = 0.f;
+#pragma unroll
+      for (int b = 0; b < NS; ++b) {
+        float sum = 0.f;
+#pragma unroll
+        for (int r = 0; r < NS; ++r) sum += __shfl(m[b], base + r, 64);
+        const float e = sum + eps;
+        if (b == a) mine = e;
+        m[b] *= act ? 1.0f / e : 0.f;
+      }
+      my[h * T] = mine;
+    }
+  }
+  // reverse walk: m holds the output of half-step h
+  for (int h = H - 1; h >= 0; --h) {
+    if ((h + 1) % kSkCkpt == 0 && h + 1 < H) {
+#pragma unroll
+      for (int b = 0; b < NS; ++b) m[b] = ck[(((h + 1) / kSkCkpt) * NS + b) * T];
+    }
+    const float er = my[h * T];
+    if ((h & 1) == 0) {
+      const float d = act ? 1.0f / er : 0.f;
+      float o[NS];
+#pragma unroll
+      for (int b = 0; b < NS; ++b) {
+        float acc = dm[b] * (eps * d);
+#pragma unroll
+        for (int bp = 0; bp < NS; ++bp) acc += (dm[b] - dm[bp]) * m[bp];
+        o[b] = d * acc;
+      }
+#pragma unroll
+      for (int b = 0; b < NS; ++b) {
+        dm[b] = o[b];
+        m[b] *= act ? er : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < NS; ++b) {
+        const float e = __shfl(er, base + b, 64);  // column b's e, recorded by lane b of the group
+        const float d = act ? 1.0f / e : 0.f;
+        float acc = dm[b] * (eps * d);
+#pragma unroll
+        for (int r = 0; r < NS; ++r) acc += (dm[b] - __shfl(dm[b], base + r, 64)) * __shfl(m[b], base + r, 64);
+        dm[b] = d * acc;
+        m[b] *= act ? e : 0.f;
+      }
+    }
+  }
+  if (act) {
+#pragma unroll
+    for (int b = 0; b < NS; ++b) dL[(i * NS + a) * NS + b] = dm[b] * __expf(L[(i * NS + a) * NS + b]);
+  }
+}
+
+// Threads per block of the row-per-lane kernel whose records fit in 64 KB of
+// LDS (0: they do not, or n <= 2, where a token per lane measured faster:
+// the per-token kernels serve those cases).
+inline int sk_lane_threads(int n, int iters) {
+  if (n <= 2) return 0;
+  const size_t per = sk_lane_words(n, iters) * sizeof(float);
+  for (int t : {256, 128, 64})
+    if (per * t <= 65536) return t;
+  return 0;
+}
+
 template <int NS>
 __global__ __launch_bounds__(64) void gsinkhorn_fwd_kernel(int64_t count, const float *__restrict__ L,
                                                           float *__restrict__ H, int iters, float eps) {
@@ -1054,7 +1171,7 @@ inline size_t al256(size_t b) { return (b + 255) / 256 * 256; }
 
 struct GBwdLay {
   int64_t ntb, tb;
-  size_t rec, prm, dw, dhrow, term, total;
+  size_t rec, prm, dw, dhrow, term, dl, total;
 };
 
 // terms: room for the fp32 residual-gradient terms (the fused pre backward).
@@ -1070,7 +1187,8 @@ GBwdLay gbwd_layout(int64_t N, int64_t C, int n, bool terms) {
   L.dw = al256((size_t)L.ntb * K * J * 4);
   L.dhrow = al256((size_t)N * n * 4);
   L.term = terms ? al256((size_t)N * K * 4) : 0;
-  L.total = L.rec + L.prm + L.dw + L.dhrow + L.term;
+  L.dl = al256((size_t)N * n * n * 4);  // the logits' gradient when the row-per-lane Sinkhorn backward forms it
+  L.total = L.rec + L.prm + L.dw + L.dhrow + L.term + L.dl;
   return L;
 }
 
@@ -1090,6 +1208,15 @@ void glaunch_sinkhorn_fwd(hipStream_t s, int n, int64_t count, const float *L, f
 
 void glaunch_sinkhorn_bwd(hipStream_t s, int n, int64_t count, const float *dH, const float *L, float *dL,
                           int iters, float eps) {
+  const int lt = sk_lane_threads(n, iters);
+  if (lt > 0) {
+    const int64_t per_block = lt / sk_group(n);
+    const unsigned b = (unsigned)((count + per_block - 1) / per_block);
+    MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gsinkhorn_bwd_lanes_kernel<NS>), dim3(b), dim3(lt),
+                                          sk_lane_words(n, iters) * sizeof(float) * lt, s, count, dH, L, dL,
+                                          iters, eps))
+    return;
+  }
   const SkBwdGeom g = sk_bwd_geom(n, iters);
   const unsigned b = (unsigned)((count + g.threads - 1) / g.threads);
   if (g.stored)
@@ -1301,17 +1428,26 @@ void glaunch_proj_bwd(hipStream_t s, int n, const ProjBwdArgs &a) {
       gagg_bwd<bf16_t>(s, n, a.N, a.C, a.g, a.X, a.H_pre, n, nullptr, false, rows);
     dHpre = rows;
   }
-  // the Sinkhorn backward runs here only when the logits' gradient is not given
-  const SkBwdGeom g = a.dL ? SkBwdGeom{64, false, 0} : sk_bwd_geom(n, a.iters);
+  // The logits' gradient, when not given: by the row-per-lane Sinkhorn backward first where its records
+  // fit (into dL_out when the caller wants it, else the workspace), else inside the per-token kernel.
+  const float *dLin = a.dL;
+  float *dLout = a.dL_out;
+  if (!dLin && sk_lane_threads(n, a.iters) > 0) {
+    float *dst = a.dL_out ? a.dL_out : (float *)(base + L.rec + L.prm + L.dw + L.dhrow + L.term);
+    glaunch_sinkhorn_bwd(s, n, a.N, a.dH_res, a.logits, dst, a.iters, a.eps);
+    dLin = dst;
+    dLout = nullptr;
+  }
+  const SkBwdGeom g = dLin ? SkBwdGeom{64, false, 0} : sk_bwd_geom(n, a.iters);
   const unsigned tb = (unsigned)((a.N + g.threads - 1) / g.threads);
   if (g.stored)
     MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_bwd_token_kernel<NS, true>), dim3(tb), dim3(g.threads), g.lds, s,
                                           a.N, K, a.alpha, a.saved, saved_stride(n), a.H_pre, a.H_post, dHpre,
-                                          a.dH_post, a.dL, a.dH_res, a.logits, a.iters, a.eps, rec, prm, a.dL_out))
+                                          a.dH_post, dLin, a.dH_res, a.logits, a.iters, a.eps, rec, prm, dLout))
   else
     MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_bwd_token_kernel<NS, false>), dim3(tb), dim3(g.threads), 0, s,
                                           a.N, K, a.alpha, a.saved, saved_stride(n), a.H_pre, a.H_post, dHpre,
-                                          a.dH_post, a.dL, a.dH_res, a.logits, a.iters, a.eps, rec, prm, a.dL_out))
+                                          a.dH_post, dLin, a.dH_res, a.logits, a.iters, a.eps, rec, prm, dLout))
   if (terms) {
     if (a.f32)
       gterms<float>(s, n, a, term);

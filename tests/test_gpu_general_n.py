@@ -36,8 +36,9 @@ def sig(v):
 @pytest.mark.parametrize("iters,eps,std", [(20, 1e-6, 1.0), (0, 1e-6, 1.0), (1, 1e-6, 2.0), (7, 0.25, 1.0),
                                            (45, 1e-6, 1.0), (150, 0.25, 1.0)])
 def test_sinkhorn_general_n(n, iters, eps, std):
-    # The backward keeps every half-step's line sums in LDS when they fit (all but the largest
-    # n x iters here), else replays the forward from checkpoints: both paths are exercised.
+    # The backward keeps every half-step's line sums in LDS: for n >= 3 with a row per lane where its
+    # records fit (20 and 45 iterations here), else (and for n <= 2) with one token per lane where they
+    # fit, else it replays the forward from checkpoints (150 iterations at n >= 3): all three paths run.
     # An fp32 reverse pass gathers rounding over every half-step it walks: the stated 1e-5 holds
     # at the workloads' 20 iterations (and at 45), and a CPU fp32 emulation of the exact-state
     # reverse pass exceeds it 1.2-2.8x at 140-200 iterations, so beyond 50 iterations the bound
