@@ -32,7 +32,8 @@
  *  - Fail-closed validation BEFORE anything is enqueued: a bad argument
  *    returns an error and leaves every output untouched.  MHC_ERR_NULL for a
  *    missing required pointer, MHC_ERR_SHAPE for negative/zero sizes,
- *    MHC_ERR_UNSUPPORTED for n > 8, C % 8 != 0, C > 16384 or iters > 4096,
+ *    MHC_ERR_UNSUPPORTED for n > 8, C % 8 != 0, C > 16384, iters > 4096 or
+ *    tokens (count) > 4194304 (2^22; each launch then stays below 2^31 threads),
  *    MHC_ERR_ALIGN for pointers not 16-byte aligned, MHC_ERR_ALIAS when an
  *    output overlaps an input or another output, MHC_ERR_WORKSPACE when the
  *    workspace is missing or too small, MHC_ERR_ARG for eps < 0, a

@@ -43,6 +43,7 @@ class Validator {
 
   void dims(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
     if (tokens < 0) fail(MHC_ERR_SHAPE, "tokens must be >= 0");
+    if (tokens > mhc::kMaxTokens) fail(MHC_ERR_UNSUPPORTED, "tokens must be <= 4194304");
     if (n <= 0) fail(MHC_ERR_SHAPE, "n must be > 0");
     if (C <= 0) fail(MHC_ERR_SHAPE, "C must be > 0");
     if (n > mhc::kMaxN) fail(MHC_ERR_UNSUPPORTED, "n must be <= 8");
@@ -56,6 +57,12 @@ class Validator {
 
   void eps(float e, const char *what) {
     if (!std::isfinite(e) || e < 0.f) fail(MHC_ERR_ARG, std::string(what) + " must be finite and >= 0");
+  }
+
+  // matrix count of the Sinkhorn entry points
+  void count(int64_t c) {
+    if (c < 0) fail(MHC_ERR_SHAPE, "count must be >= 0");
+    if (c > mhc::kMaxTokens) fail(MHC_ERR_UNSUPPORTED, "count must be <= 4194304");
   }
 
   void iters(int32_t it) {
@@ -209,7 +216,7 @@ mhc_status mhc_set_kernel_events(int32_t kernel, void *start_event, void *stop_e
 
 // ------------------------------------------------------------------ projection fwd
 size_t mhc_proj_rms_h_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
-  if (tokens <= 0 || n < 1 || n > mhc::kMaxN || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
+  if (tokens <= 0 || tokens > mhc::kMaxTokens || n < 1 || n > mhc::kMaxN || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
   return n == 4 ? mhc::proj_fwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_fwd_ws(n, tokens);
 }
 
@@ -245,7 +252,7 @@ mhc_status mhc_proj_rms_h(void *stream, int64_t tokens, int32_t n, int64_t C, mh
 
 // ------------------------------------------------------------------ projection bwd
 size_t mhc_proj_rms_h_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
-  if (tokens <= 0 || n < 1 || n > mhc::kMaxN || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
+  if (tokens <= 0 || tokens > mhc::kMaxTokens || n < 1 || n > mhc::kMaxN || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
   return n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_bwd_ws(n, tokens, C, false);
 }
 
@@ -301,7 +308,7 @@ mhc_status mhc_proj_rms_h_bwd(void *stream, int64_t tokens, int32_t n, int64_t C
 mhc_status mhc_sinkhorn_fwd(void *stream, int64_t count, int32_t n, const float *logits,
                             float *H_res, int32_t iters, float eps) {
   Validator v("mhc_sinkhorn_fwd");
-  if (count < 0) v.fail(MHC_ERR_SHAPE, "count must be >= 0");
+  v.count(count);
   if (n <= 0) v.fail(MHC_ERR_SHAPE, "n must be > 0");
   else if (n > mhc::kMaxN) v.fail(MHC_ERR_UNSUPPORTED, "n must be <= 8");
   v.iters(iters);
@@ -321,7 +328,7 @@ mhc_status mhc_sinkhorn_fwd(void *stream, int64_t count, int32_t n, const float 
 mhc_status mhc_sinkhorn_bwd(void *stream, int64_t count, int32_t n, const float *dH_res,
                             const float *logits, float *dlogits, int32_t iters, float eps) {
   Validator v("mhc_sinkhorn_bwd");
-  if (count < 0) v.fail(MHC_ERR_SHAPE, "count must be >= 0");
+  v.count(count);
   if (n <= 0) v.fail(MHC_ERR_SHAPE, "n must be > 0");
   else if (n > mhc::kMaxN) v.fail(MHC_ERR_UNSUPPORTED, "n must be <= 8");
   v.iters(iters);
@@ -404,7 +411,7 @@ mhc_status mhc_h_post_bda_fwd(void *stream, int64_t tokens, int32_t n, int64_t C
 size_t mhc_h_post_bda_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
                                          int32_t with_dbias) {
   (void)act;
-  if (tokens <= 0 || n < 1 || n > mhc::kMaxN || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
+  if (tokens <= 0 || tokens > mhc::kMaxTokens || n < 1 || n > mhc::kMaxN || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
   return n == 4 ? mhc::h_post_bda_bwd_ws(tokens, C, with_dbias != 0) : mhc::gh_post_bda_bwd_ws(tokens, C, with_dbias != 0);
 }
 
@@ -540,7 +547,7 @@ mhc_status mhc_h_aggregate_static_fwd(void *stream, int64_t tokens, int32_t n, i
 
 size_t mhc_h_aggregate_static_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
   (void)act;
-  if (tokens <= 0 || n < 1 || n > mhc::kMaxN || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
+  if (tokens <= 0 || tokens > mhc::kMaxTokens || n < 1 || n > mhc::kMaxN || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
   return n == 4 ? mhc::h_aggregate_static_bwd_ws(tokens) : mhc::gh_aggregate_static_bwd_ws(n, tokens);
 }
 
@@ -635,7 +642,7 @@ mhc_status mhc_rmsnorm_fwd(void *stream, int64_t tokens, int64_t C, mhc_dtype ac
 
 size_t mhc_rmsnorm_bwd_workspace_size(int64_t tokens, int64_t C, mhc_dtype act, int32_t with_dgamma) {
   (void)act;
-  if (tokens <= 0 || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
+  if (tokens <= 0 || tokens > mhc::kMaxTokens || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
   return mhc::rmsnorm_bwd_ws(tokens, C, with_dgamma != 0);
 }
 
@@ -710,7 +717,7 @@ mhc_status mhc_pre_rmsnorm_fwd(void *stream, int64_t tokens, int32_t n, int64_t 
 }
 
 size_t mhc_pre_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
-  if (tokens <= 0 || n < 1 || n > mhc::kMaxN || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
+  if (tokens <= 0 || tokens > mhc::kMaxTokens || n < 1 || n > mhc::kMaxN || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
   return n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_bwd_ws(n, tokens, C, true);
 }
 

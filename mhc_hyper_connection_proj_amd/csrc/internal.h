@@ -17,6 +17,9 @@ struct StreamGeom {
   int gpt;  // 8-channel groups per thread (1, 2 or 4): C <= 16384
 };
 constexpr int64_t kMaxC = 16384;
+// Largest token (or matrix) count an entry point accepts: a launch runs at
+// most 512 threads per token, so every grid stays below 2^31 threads.
+constexpr int64_t kMaxTokens = int64_t(1) << 22;
 StreamGeom stream_geom(int64_t C);
 
 // Measurement hook (mhc_set_kernel_events): records the registered start /

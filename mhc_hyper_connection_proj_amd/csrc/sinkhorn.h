@@ -6,6 +6,12 @@
 // 16 entries, so row and column sums need no cross-lane traffic and each
 // reciprocal is computed once (4 v_rcp_f32 per half-step).
 //
+// Floating-point contraction is off in the passes and in the quad sum: a
+// row pass's scaling (M *= 1/d) would otherwise be fused into the next
+// column sum as an fma, which rounds one term fewer, and differently in the
+// one-lane and the quad layouts.  Every entry is rounded after its scaling,
+// so both layouts run the same operation sequence.
+//
 // Backward: exact reverse mode of the unrolled map.  A half-step M' = M / d
 // (d = line sum + eps) has the adjoint dM = (G - <G, M'>_line) / d.  The
 // replay stores each half-step's 4 denominators in registers and walks back
@@ -22,6 +28,7 @@ namespace mhc {
 constexpr int SK_SEG = 20;
 
 __device__ __forceinline__ void sk_row_pass(float M[16], float eps, float d[4]) {
+#pragma clang fp contract(off)
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     d[a] = ((M[4 * a] + M[4 * a + 1]) + (M[4 * a + 2] + M[4 * a + 3])) + eps;
@@ -32,6 +39,7 @@ __device__ __forceinline__ void sk_row_pass(float M[16], float eps, float d[4]) 
 }
 
 __device__ __forceinline__ void sk_col_pass(float M[16], float eps, float d[4]) {
+#pragma clang fp contract(off)
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     d[b] = ((M[b] + M[4 + b]) + (M[8 + b] + M[12 + b])) + eps;
@@ -124,6 +132,7 @@ __device__ __forceinline__ void sk_backward(const float L[16], float G[16], int 
 // bit-identical to it.  Used where one layer's tokens give too few waves for
 // one matrix per lane to fill the chip.
 __device__ __forceinline__ float quad_sum(float v) {
+#pragma clang fp contract(off)
   v += dpp<DPP_QUAD_1032>(v);
   v += dpp<DPP_QUAD_2301>(v);
   return v;
@@ -141,6 +150,7 @@ __device__ __forceinline__ void sk_exp4(const float l[4], float m[4]) {
 }
 
 __device__ __forceinline__ void sk_row_pass_q(float m[4], float eps, float &d) {
+#pragma clang fp contract(off)
   d = ((m[0] + m[1]) + (m[2] + m[3])) + eps;
   const float inv = fast_rcp(d);
 #pragma unroll
@@ -149,6 +159,7 @@ __device__ __forceinline__ void sk_row_pass_q(float m[4], float eps, float &d) {
 
 // dcol: this lane's own column's denominator (column r)
 __device__ __forceinline__ void sk_col_pass_q(float m[4], float eps, int r, float &dcol) {
+#pragma clang fp contract(off)
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const float d = quad_sum(m[b]) + eps;

@@ -240,3 +240,23 @@ def test_rmsnorm_validation(lib):
              p(2), p(3), p(4), p(5), None, p(6), p(6) + 64, p(7), ws) == ALIAS     # normed inside agg
     assert h(None, 8, 4, 64, 0, p(0), p(1), None, None, 1e-6, 20, 1e-6, None, -1.0,
              p(2), p(3), p(4), p(5), None, p(6), p(8), p(7), ws) == ARG            # norm_eps < 0
+
+
+def test_token_count_limit_rejected_before_launch(lib):
+    """tokens (or a Sinkhorn count) above 2^22 would take some launch past 2^31 threads: rejected on the
+    host with MHC_ERR_UNSUPPORTED, before anything is enqueued; 2^22 itself passes the check and stops
+    at the next one (a missing input)."""
+    E = {n: i for i, n in enumerate(L.STATUS)}
+    big = (1 << 22) + 1
+    fake = 0x10000
+    assert lib.mhc_h_aggregate_fwd(None, big, 1, 8, 0, fake, fake, fake) == E["MHC_ERR_UNSUPPORTED"]
+    assert "4194304" in _last(lib)
+    assert lib.mhc_rmsnorm_fwd(None, big, 8, 0, fake, None, 1e-6, fake) == E["MHC_ERR_UNSUPPORTED"]
+    assert lib.mhc_sinkhorn_fwd(None, big, 4, fake, fake, 20, 1e-6) == E["MHC_ERR_UNSUPPORTED"]
+    assert lib.mhc_sinkhorn_bwd(None, big, 2, fake, fake, fake, 20, 1e-6) == E["MHC_ERR_UNSUPPORTED"]
+    assert lib.mhc_pre_fwd(None, big, 4, 8, 0, fake, fake, None, None, 1e-6, 20, 1e-6, fake, fake, fake, fake,
+                           None, fake, fake, 1 << 30) == E["MHC_ERR_UNSUPPORTED"]
+    for q in (lib.mhc_pre_fwd_workspace_size, lib.mhc_pre_bwd_workspace_size, lib.mhc_proj_rms_h_workspace_size):
+        assert q(big, 4, 8, 0) == 0 and q(1 << 22, 4, 8, 0) > 0
+    # at the limit the token check passes and the missing X is reported instead
+    assert lib.mhc_h_aggregate_fwd(None, 1 << 22, 1, 8, 0, None, fake, fake) == E["MHC_ERR_NULL"]

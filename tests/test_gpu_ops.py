@@ -9,8 +9,8 @@ import pytest
 import torch
 
 import oracle as O
-from gpu_util import (assert_act, assert_mixed, assert_rel, assert_tokensum, dev, h64, log, pre_bwd_abs_parts,
-                      proj_bwd_abs_parts)
+from gpu_util import (assert_act, assert_h_res, assert_mixed, assert_rel, assert_tokensum, dev, h64, log,
+                      pre_bwd_abs_parts, proj_bwd_abs_parts, sinkhorn_rtol, sum_depth)
 from mhc_hyper_connection_proj_amd import binding as B
 from mhc_hyper_connection_proj_amd import synth
 
@@ -31,7 +31,9 @@ def store(a64, act):
 # ----------------------------------------------------------------- Sinkhorn
 @pytest.mark.parametrize("count,iters,eps,std", [
     (1, 20, 1e-6, 1.0), (5000, 20, 1e-6, 1.0), (777, 20, 1e-6, 3.4), (300, 0, 1e-6, 1.0),
-    (300, 1, 1e-6, 1.0), (300, 45, 1e-6, 1.0), (300, 7, 0.25, 1.0), (300, 20, 0.0, 1.0)])
+    (300, 1, 1e-6, 1.0), (300, 45, 1e-6, 1.0), (300, 7, 0.25, 1.0), (300, 20, 0.0, 1.0),
+    # long runs: the backward replays 20-iteration segments, rebuilding each half-step's input as M' d
+    (1000, 100, 1e-6, 1.0), (1000, 150, 0.25, 1.0), (1000, 200, 1e-6, 1.0), (1000, 200, 1e-6, 2.0)])
 def test_sinkhorn_fwd_bwd(count, iters, eps, std):
     log(f"sinkhorn count={count} iters={iters} eps={eps} std={std}")
     L = f32(RNG.standard_normal((count, 4, 4)) * std)
@@ -39,8 +41,12 @@ def test_sinkhorn_fwd_bwd(count, iters, eps, std):
     H = B.mhc_sinkhorn_fwd(dev(L), iters, eps)
     dL = B.mhc_sinkhorn_bwd(dev(dH), dev(L), iters, eps)
     torch.cuda.synchronize()
-    assert_rel("H_res", H, O.sinkhorn_fwd(h64(L), iters, eps))
-    assert_mixed("dlogits", dL, O.sinkhorn_bwd(h64(dH), h64(L), iters, eps))
+    oH, odL = O.sinkhorn_fwd(h64(L), iters, eps), O.sinkhorn_bwd(h64(dH), h64(L), iters, eps)
+    rms = np.sqrt(np.mean(odL * odL))
+    log(f"  worst error / 1e-5 bound: H_res {np.max(np.abs(h64(H) - oH) / (1e-5 * np.abs(oH))):.3f}, "
+        f"dlogits {np.max(np.abs(h64(dL) - odL) / (1e-5 * (np.abs(odL) + rms))):.3f}")
+    assert_rel("H_res", H, oH, rtol=sinkhorn_rtol(iters, grad=False))
+    assert_mixed("dlogits", dL, odL, rtol=sinkhorn_rtol(iters, grad=True))
 
 
 def test_sinkhorn_batched_workload_full():
@@ -118,7 +124,7 @@ def test_h_post_bda(act, N, C, bias):
     assert_mixed("dH_post", dHp, odHp)
     assert_act("dx", dx, odx, act)
     if bias:
-        assert_tokensum("dbias", db, odb, np.abs(odx).sum(axis=0), act)
+        assert_tokensum("dbias", db, odb, np.abs(odx).sum(axis=0), act, sum_depth("rows", N))
     else:
         assert db is None
     # without dX (the pre backward forms it), also without dbias: the other
@@ -136,7 +142,7 @@ def test_h_post_bda(act, N, C, bias):
         assert_mixed("dH_post (no dX)", nHp, odHp)
         assert_act("dx (no dX)", ndx, odx, act)
         if want_db:
-            assert_tokensum("dbias (no dX)", ndb, odb, np.abs(odx).sum(axis=0), act)
+            assert_tokensum("dbias (no dX)", ndb, odb, np.abs(odx).sum(axis=0), act, sum_depth("rows", N))
 
 
 # ----------------------------------------------------------------- stream mix / distribute, shared-row aggregate
@@ -190,7 +196,7 @@ def test_h_aggregate_static(act, N, C, accumulate):
     odX, odH = O.h_aggregate_static_bwd(h64(g), h64(X), h64(h))
     assert_act("dX", dX, odX + (h64(dX0) if accumulate else 0.0), act)
     parts = np.abs(O.h_aggregate_bwd(h64(g), h64(X), np.broadcast_to(h64(h), (N, 4)).copy())[1]).sum(axis=0)
-    assert_tokensum("dH_pre", dH, odH, parts)
+    assert_tokensum("dH_pre", dH, odH, parts, depth=sum_depth("hpre", N))
 
 
 def test_variants_zero_tokens():
@@ -266,9 +272,9 @@ def test_proj_rms_h_bwd(act, N, C):
     assert_act("dX", dX, odX, act)
     assert_act("dX accumulated", dXa, h64(dX0) + odX, act)
     aW, aa, ab = proj_bwd_abs_parts(h64(X), h64(W), h64(dHp), h64(dHq), h64(dL), h64(alpha), h64(hb), 1e-6)
-    assert_tokensum("dW", dW, odW, aW)
-    assert_tokensum("dalpha", da, oda, aa)
-    assert_tokensum("dhbias", db, odb, ab)
+    assert_tokensum("dW", dW, odW, aW, depth=sum_depth("proj", N, C, act=act))
+    assert_tokensum("dalpha", da, oda, aa, depth=sum_depth("param", N))
+    assert_tokensum("dhbias", db, odb, ab, depth=sum_depth("param", N))
 
 
 # ----------------------------------------------------------------- fused pre pass
@@ -284,9 +290,8 @@ def test_pre_fwd_bwd(act, N, C, mode):
     assert_rel("H_pre", o["H_pre"], ref["H_pre"])
     assert_rel("H_post", o["H_post"], ref["H_post"])
     assert_mixed("logits", o["H_res_logits"], ref["L"])
-    # Sinkhorn of the GPU's own logits is checked by the Sinkhorn tests; here
-    # H_res is compared end to end, where logit rounding enters through exp.
-    assert_rel("H_res", o["H_res"], ref["H_res"], rtol=2e-5)
+    assert_h_res(o["H_res"], o["H_res_logits"], ref["H_res"], ref["L"], 20, 1e-6,
+                 alone=B.mhc_sinkhorn_fwd(o["H_res_logits"], 20, 1e-6))
     assert_act("agg", o["agg"], ref["agg"], act)
     # backward from oracle-produced forward state
     saved = np.zeros((N, 32), np.float32)
@@ -314,9 +319,39 @@ def test_pre_fwd_bwd(act, N, C, mode):
     assert_mixed("dlogits", ob["dlogits"], rb["dL"])
     assert_act("dX", ob["dX"], base + rb["dX"], act)
     aW, aa, ab = pre_bwd_abs_parts(h64(g), h64(dHq), h64(dHr), h64(X), h64(W), h64(alpha), h64(hb), 1e-6, 20, 1e-6)
-    assert_tokensum("dW", ob["dW"], rb["dW"], aW)
-    assert_tokensum("dalpha", ob["dalpha"], rb["dalpha"], aa)
-    assert_tokensum("dhbias", ob["dhbias"], rb["dhbias"], ab)
+    assert_tokensum("dW", ob["dW"], rb["dW"], aW, depth=sum_depth("proj", N, C, act=act))
+    assert_tokensum("dalpha", ob["dalpha"], rb["dalpha"], aa, depth=sum_depth("param", N))
+    assert_tokensum("dhbias", ob["dhbias"], rb["dhbias"], ab, depth=sum_depth("param", N))
+
+
+@pytest.mark.parametrize("iters,eps", [(100, 1e-6), (200, 1e-6), (150, 0.25)])
+def test_pre_fwd_bwd_long_iterations(iters, eps):
+    """The fused pre pass runs its Sinkhorn in the quad layout (finalize forward, per-token backward):
+    long iteration counts, against the oracle at the iteration-count rule."""
+    N, C, act = 37, 296, "bf16"
+    log(f"pre fwd/bwd long iterations iters={iters} eps={eps}")
+    X, W, alpha, hb = _proj_inputs(act, N, C)
+    o = B.mhc_pre_fwd(dev(X), dev(W), dev(alpha), dev(hb), 1e-6, iters, eps)
+    torch.cuda.synchronize()
+    ref = O.pre_fwd(h64(X), h64(W), h64(alpha), h64(hb), 1e-6, iters, eps)
+    assert_mixed("logits", o["H_res_logits"], ref["L"])
+    assert_h_res(o["H_res"], o["H_res_logits"], ref["H_res"], ref["L"], iters, eps,
+                 alone=B.mhc_sinkhorn_fwd(o["H_res_logits"], iters, eps))
+    saved = np.zeros((N, 32), np.float32)
+    saved[:, 0] = ref["r"]; saved[:, 1] = ref["q"]; saved[:, 2:26] = ref["z"]
+    g = store(RNG.standard_normal((N, C)), act)
+    dHq, dHr = f32(RNG.standard_normal((N, 4))), f32(RNG.standard_normal((N, 4, 4)))
+    ob = B.mhc_pre_bwd(dev(g), dev(dHq), dev(dHr), dev(X), dev(W), dev(saved), dev(f32(ref["H_pre"])),
+                       dev(f32(ref["H_post"])), dev(f32(ref["L"])), alpha=dev(alpha), iters=iters, eps=eps,
+                       want_intermediates=True)
+    alone = B.mhc_sinkhorn_bwd(dev(dHr), dev(f32(ref["L"])), iters, eps)
+    torch.cuda.synchronize()
+    odL = O.sinkhorn_bwd(h64(dHr), h64(f32(ref["L"])), iters, eps)
+    rms = np.sqrt(np.mean(odL * odL))
+    log(f"  dlogits worst error / 1e-5 bound: fused {np.max(np.abs(h64(ob['dlogits']) - odL) / (1e-5 * (np.abs(odL) + rms))):.3f}"
+        f", standalone {np.max(np.abs(h64(alone) - odL) / (1e-5 * (np.abs(odL) + rms))):.3f}")
+    assert_mixed("dlogits (fused)", ob["dlogits"], odL, rtol=sinkhorn_rtol(iters, grad=True))
+    assert_mixed("dlogits (standalone)", alone, odL, rtol=sinkhorn_rtol(iters, grad=True))
 
 
 # ----------------------------------------------------------------- measurement hook
