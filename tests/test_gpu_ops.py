@@ -45,8 +45,8 @@ def test_sinkhorn_fwd_bwd(count, iters, eps, std):
     rms = np.sqrt(np.mean(odL * odL))
     log(f"  worst error / 1e-5 bound: H_res {np.max(np.abs(h64(H) - oH) / (1e-5 * np.abs(oH))):.3f}, "
         f"dlogits {np.max(np.abs(h64(dL) - odL) / (1e-5 * (np.abs(odL) + rms))):.3f}")
-    assert_rel("H_res", H, oH, rtol=sinkhorn_rtol(iters, grad=False))
-    assert_mixed("dlogits", dL, odL, rtol=sinkhorn_rtol(iters, grad=True))
+    assert_rel("H_res", H, oH)
+    assert_mixed("dlogits", dL, odL, rtol=sinkhorn_rtol(iters, grad=True, n=4))
 
 
 def test_sinkhorn_batched_workload_full():
@@ -350,8 +350,8 @@ def test_pre_fwd_bwd_long_iterations(iters, eps):
     rms = np.sqrt(np.mean(odL * odL))
     log(f"  dlogits worst error / 1e-5 bound: fused {np.max(np.abs(h64(ob['dlogits']) - odL) / (1e-5 * (np.abs(odL) + rms))):.3f}"
         f", standalone {np.max(np.abs(h64(alone) - odL) / (1e-5 * (np.abs(odL) + rms))):.3f}")
-    assert_mixed("dlogits (fused)", ob["dlogits"], odL, rtol=sinkhorn_rtol(iters, grad=True))
-    assert_mixed("dlogits (standalone)", alone, odL, rtol=sinkhorn_rtol(iters, grad=True))
+    assert_mixed("dlogits (fused)", ob["dlogits"], odL, rtol=sinkhorn_rtol(iters, grad=True, n=4))
+    assert_mixed("dlogits (standalone)", alone, odL, rtol=sinkhorn_rtol(iters, grad=True, n=4))
 
 
 # ----------------------------------------------------------------- measurement hook
