@@ -267,6 +267,26 @@ mhc_status mhc_pre_fwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_d
                        float *H_res, float *H_res_logits, float *saved, void *agg,
                        void *workspace, size_t workspace_bytes);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): mhc_pre_fwd with the same
+ * arguments and results, bit for bit, but no workspace.  Its scratch is a
+ * static device array of MHC_NOALLOC_SCRATCH_BYTES (64 MiB) that every GPU
+ * loading the library holds until the process ends; the call itself
+ * allocates nothing.  A call whose scratch need, mhc_pre_fwd_workspace_size
+ * for the same arguments, exceeds it returns MHC_ERR_UNSUPPORTED before
+ * anything is enqueued (16384 tokens at C = 7168, n = 4, need about 22 MiB).
+ * All calls on one GPU share that GPU's array: calls that can overlap on one
+ * GPU (other streams, other host threads) race and must be ordered by the
+ * caller.  Every scratch byte a call reads is written earlier in the same
+ * call, so nothing is carried over from the previous call.  The first call
+ * on a device looks up that device's array (hipGetSymbolAddress) and may
+ * return MHC_ERR_HIP if the lookup fails. */
+#define MHC_NOALLOC_SCRATCH_BYTES (64u << 20)
+mhc_status mhc_pre_fwd_noalloc(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                               const void *X, const float *W, const float *alpha, const float *hbias,
+                               float rms_eps, int32_t iters, float eps, float *H_pre, float *H_post,
+                               float *H_res, float *H_res_logits, float *saved, void *agg);
+
 /* Fused pre pass backward: h_aggregate backward (dH_pre and the H_pre * g
  * residual term) + Sinkhorn backward (dH_res -> logits) + projection
  * backward, with the residual gradient terms summed into dX (Megatron Core

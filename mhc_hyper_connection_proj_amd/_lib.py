@@ -66,6 +66,8 @@ SIGNATURES = {
     "mhc_pre_fwd_workspace_size": (_sz, [_i64, _i32, _i64, ctypes.c_int]),
     "mhc_pre_fwd": (ctypes.c_int, [_vp, _i64, _i32, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _f32,
                                    _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz]),
+    "mhc_pre_fwd_noalloc": (ctypes.c_int, [_vp, _i64, _i32, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _f32,
+                                           _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "mhc_rmsnorm_fwd": (ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, _vp, _vp, _f32, _vp]),
     "mhc_rmsnorm_bwd_workspace_size": (_sz, [_i64, _i64, ctypes.c_int, _i32]),
     "mhc_rmsnorm_bwd": (ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, _vp, _vp, _vp, _f32, _vp, _i32, _vp,

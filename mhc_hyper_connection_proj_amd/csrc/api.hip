@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -163,6 +164,96 @@ bool zero_act(hipStream_t s, void *p, int64_t n, mhc_dtype act) {
   return true;
 }
 
+
+// ---- fused pre forward: checks and launches shared by mhc_pre_fwd and mhc_pre_fwd_noalloc
+size_t pre_fwd_ws(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
+  return n == 4 ? mhc::proj_fwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_fwd_ws(n, tokens);
+}
+
+// Shapes, scalars and every tensor argument (no workspace).  False when a check failed or
+// tokens == 0 (then v.status() is the result).
+bool pre_fwd_check(Validator &v, int64_t tokens, int32_t n, int64_t C, mhc_dtype act, const void *X,
+                   const float *W, const float *alpha, const float *hbias, float rms_eps, int32_t iters,
+                   float eps, float *H_pre, float *H_post, float *H_res, float *H_res_logits, float *saved,
+                   void *agg) {
+  v.dims(tokens, n, C, act);
+  v.eps(rms_eps, "rms_eps");
+  v.eps(eps, "eps");
+  v.iters(iters);
+  if (!v.ok()) return false;
+  if (tokens == 0) return true;
+  const int64_t K = (int64_t)n * C;
+  const int64_t J = (int64_t)n * n + 2 * n;
+  v.in(X, tokens * K * esz(act), "X");
+  v.in(W, K * J * 4, "W");
+  v.in(alpha, 12, "alpha", true);
+  v.in(hbias, J * 4, "hbias", true);
+  v.out(H_pre, tokens * n * 4, "H_pre");
+  v.out(H_post, tokens * n * 4, "H_post");
+  v.out(H_res, tokens * n * n * 4, "H_res");
+  v.out(H_res_logits, tokens * n * n * 4, "H_res_logits");
+  v.out(saved, tokens * mhc::saved_stride(n) * 4, "saved", true);
+  v.out(agg, tokens * C * esz(act), "agg");
+  return v.ok();
+}
+
+void pre_fwd_launch(hipStream_t s, int64_t tokens, int32_t n, int64_t C, mhc_dtype act, const void *X,
+                    const float *W, const float *alpha, const float *hbias, float rms_eps, int32_t iters,
+                    float eps, float *H_pre, float *H_post, float *H_res, float *H_res_logits, float *saved,
+                    void *agg, void *ws) {
+  if (n == 4) {
+    mhc::launch_proj_fwd(s, act == MHC_F32, tokens, C, X, W, alpha, hbias, rms_eps, H_pre, H_post,
+                         H_res_logits, saved, H_res, iters, eps, ws);
+    mhc::launch_h_aggregate_fwd(s, act == MHC_F32, tokens, C, X, H_pre, agg);
+  } else {
+    mhc::glaunch_proj_fwd(s, act == MHC_F32, n, tokens, C, X, W, alpha, hbias, rms_eps, H_pre, H_post,
+                          H_res_logits, saved, H_res, iters, eps, ws);
+    mhc::glaunch_h_aggregate_fwd(s, act == MHC_F32, n, tokens, C, X, H_pre, agg, n);
+  }
+}
+
+}  // namespace
+
+// ---- the static scratch of mhc_pre_fwd_noalloc
+// One array of MHC_NOALLOC_SCRATCH_BYTES in device memory: every GPU that
+// loads this library holds its own copy, at its own address, until the
+// process ends.  In host code `scratch` names a host-side stand-in, never
+// the device memory: the device address comes from hipGetSymbolAddress,
+// looked up once per device with that device current, and only that
+// address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[MHC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices];  // device address of `scratch` per device id, once looked up
+
+// Device address of the current device's scratch array (looked up on the first call per device).
+mhc_status scratch_of_current_device(void **addr, const char *fn) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_error = std::string(fn) + ": hipGetDevice failed: " + hipGetErrorString(e);
+    return MHC_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    g_last_error = std::string(fn) + ": device id " + std::to_string(dev) + " out of range";
+    return MHC_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      g_last_error = std::string(fn) + ": hipGetSymbolAddress(scratch) failed: " + hipGetErrorString(e);
+      return MHC_ERR_HIP;
+    }
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return MHC_OK;
+}
 
 }  // namespace
 
@@ -591,37 +682,39 @@ mhc_status mhc_pre_fwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_d
                        float *H_res, float *H_res_logits, float *saved, void *agg,
                        void *workspace, size_t workspace_bytes) {
   Validator v("mhc_pre_fwd");
-  v.dims(tokens, n, C, act);
-  v.eps(rms_eps, "rms_eps");
-  v.eps(eps, "eps");
-  v.iters(iters);
-  if (!v.ok()) return v.status();
+  if (!pre_fwd_check(v, tokens, n, C, act, X, W, alpha, hbias, rms_eps, iters, eps, H_pre, H_post, H_res,
+                     H_res_logits, saved, agg))
+    return v.status();
   if (tokens == 0) return MHC_OK;
-  const int64_t K = (int64_t)n * C;
-  const int64_t J = (int64_t)n * n + 2 * n;
-  v.in(X, tokens * K * esz(act), "X");
-  v.in(W, K * J * 4, "W");
-  v.in(alpha, 12, "alpha", true);
-  v.in(hbias, J * 4, "hbias", true);
-  v.out(H_pre, tokens * n * 4, "H_pre");
-  v.out(H_post, tokens * n * 4, "H_post");
-  v.out(H_res, tokens * n * n * 4, "H_res");
-  v.out(H_res_logits, tokens * n * n * 4, "H_res_logits");
-  v.out(saved, tokens * mhc::saved_stride(n) * 4, "saved", true);
-  v.out(agg, tokens * C * esz(act), "agg");
-  v.workspace(workspace, workspace_bytes, n == 4 ? mhc::proj_fwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_fwd_ws(n, tokens));
+  v.workspace(workspace, workspace_bytes, pre_fwd_ws(tokens, n, C, act));
   if (v.finish() != MHC_OK) return v.status();
-  const hipStream_t s = (hipStream_t)stream;
-  if (n == 4) {
-    mhc::launch_proj_fwd(s, act == MHC_F32, tokens, C, X, W, alpha, hbias, rms_eps, H_pre, H_post,
-                         H_res_logits, saved, H_res, iters, eps, workspace);
-    mhc::launch_h_aggregate_fwd(s, act == MHC_F32, tokens, C, X, H_pre, agg);
-  } else {
-    mhc::glaunch_proj_fwd(s, act == MHC_F32, n, tokens, C, X, W, alpha, hbias, rms_eps, H_pre, H_post,
-                          H_res_logits, saved, H_res, iters, eps, workspace);
-    mhc::glaunch_h_aggregate_fwd(s, act == MHC_F32, n, tokens, C, X, H_pre, agg, n);
-  }
+  pre_fwd_launch((hipStream_t)stream, tokens, n, C, act, X, W, alpha, hbias, rms_eps, iters, eps, H_pre, H_post,
+                 H_res, H_res_logits, saved, agg, workspace);
   return launched("mhc_pre_fwd");
+}
+
+mhc_status mhc_pre_fwd_noalloc(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                               const void *X, const float *W, const float *alpha, const float *hbias,
+                               float rms_eps, int32_t iters, float eps, float *H_pre, float *H_post,
+                               float *H_res, float *H_res_logits, float *saved, void *agg) {
+  Validator v("mhc_pre_fwd_noalloc");
+  if (!pre_fwd_check(v, tokens, n, C, act, X, W, alpha, hbias, rms_eps, iters, eps, H_pre, H_post, H_res,
+                     H_res_logits, saved, agg))
+    return v.status();
+  if (tokens == 0) return MHC_OK;
+  const size_t need = pre_fwd_ws(tokens, n, C, act);
+  if (need > (size_t)MHC_NOALLOC_SCRATCH_BYTES)
+    v.fail(MHC_ERR_UNSUPPORTED, "this call needs " + std::to_string(need) +
+                                    " bytes of scratch; the static scratch holds " +
+                                    std::to_string((size_t)MHC_NOALLOC_SCRATCH_BYTES) +
+                                    " (use mhc_pre_fwd with a workspace)");
+  if (v.finish() != MHC_OK) return v.status();
+  void *ws = nullptr;
+  const mhc_status st = scratch_of_current_device(&ws, "mhc_pre_fwd_noalloc");
+  if (st != MHC_OK) return st;
+  pre_fwd_launch((hipStream_t)stream, tokens, n, C, act, X, W, alpha, hbias, rms_eps, iters, eps, H_pre, H_post,
+                 H_res, H_res_logits, saved, agg, ws);
+  return launched("mhc_pre_fwd_noalloc");
 }
 
 // ------------------------------------------------------------------ RMSNorm of the aggregated stream

@@ -260,3 +260,22 @@ def test_token_count_limit_rejected_before_launch(lib):
         assert q(big, 4, 8, 0) == 0 and q(1 << 22, 4, 8, 0) > 0
     # at the limit the token check passes and the missing X is reported instead
     assert lib.mhc_h_aggregate_fwd(None, 1 << 22, 1, 8, 0, None, fake, fake) == E["MHC_ERR_NULL"]
+
+
+def test_noalloc_pre_fwd_rejects_beyond_its_scratch(lib):
+    """mhc_pre_fwd_noalloc: a call whose scratch need exceeds the static array is rejected on the host,
+    before any HIP call (300000 tokens at n = 4, C = 8 need 8 split-K rows of 128 bytes per token)."""
+    E = {n: i for i, n in enumerate(L.STATUS)}
+    N = 300000
+    assert lib.mhc_pre_fwd_workspace_size(N, 4, 8, 0) > 64 << 20
+    st = lib.mhc_pre_fwd_noalloc(None, N, 4, 8, 0, p(0), p(1), None, None, 1e-6, 20, 1e-6, p(2), p(3), p(4), p(5),
+                                 None, p(6))
+    assert st == E["MHC_ERR_UNSUPPORTED"]
+    assert "static scratch" in _last(lib)
+    # the same checks as mhc_pre_fwd come first
+    assert lib.mhc_pre_fwd_noalloc(None, 4, 4, 8, 0, None, p(1), None, None, 1e-6, 20, 1e-6, p(2), p(3), p(4), p(5),
+                                   None, p(6)) == E["MHC_ERR_NULL"]
+    assert lib.mhc_pre_fwd_noalloc(None, 4, 4, 8, 0, p(0), p(1), None, None, 1e-6, -1, 1e-6, p(2), p(3), p(4), p(5),
+                                   None, p(6)) == E["MHC_ERR_ARG"]
+    assert lib.mhc_pre_fwd_noalloc(None, 0, 4, 8, 0, None, None, None, None, 1e-6, 20, 1e-6, None, None, None, None,
+                                   None, None) == E["MHC_OK"]
