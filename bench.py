@@ -125,6 +125,34 @@ def measure_variants(lib, L, sp, N, n, C, X, G, H_res, H_post, x, g, out, dX, dM
     return res
 
 
+def measure_projection_choice(lib, L, sp, stream, torch, X, W, N, n, C) -> dict:
+    """The forward projection at the workload's shape with x @ W on the matrix cores (mhc_proj_rms_h)
+    and as fp32 FMAs on the vector ALUs (mhc_proj_rms_h_fma), same inputs: mean of 5 event-timed calls
+    each after one warm-up; GB/s on the residual read (8C bytes per token)."""
+    dev = X.device
+    e = lambda *sh: torch.empty(*sh, dtype=torch.float32, device=dev)
+    Hp, Hq, Lg, sv = e(N, 4), e(N, 4), e(N, 4, 4), e(N, 32)
+    wsb = lib.mhc_proj_rms_h_workspace_size(N, n, C, L.MHC_BF16)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    P = lambda t: t.data_ptr()
+    res = {}
+    for name, fn in (("mfma", lib.mhc_proj_rms_h), ("fma", lib.mhc_proj_rms_h_fma)):
+        call = lambda: L.check(fn(sp, N, n, C, L.MHC_BF16, P(X), P(W), None, None, 1e-6, P(Hp), P(Hq), P(Lg), P(sv),
+                                  P(ws), wsb))
+        call()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        ev[0].record(stream)
+        for i in range(5):
+            call()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(5)]))
+        res[name + "_ms"] = ms
+        res[name + "_gbs"] = 8 * C * N / (ms * 1e-3) / 1e9
+    return res
+
+
 def measure_general_n(N: int, stream, torch) -> dict:
     """One mHC step (pre fwd, post fwd, post bwd, pre bwd with the h_post_bda dX term) at stream counts
     other than 4, on the kernels templated on n: same token count as the headline workload, a width
@@ -171,9 +199,9 @@ def measure_configs(stream, torch) -> dict:
     h_post_bda forward + backward with bias (32768 tokens, C = 4096).  Mean of 5 event-timed calls
     after one warm-up; algorithmic bytes: Sinkhorn 128 + 192 bytes per matrix, pre forward
     10C + 260 per token (X read; agg, H, logits, saved written), h_post_bda 18C + 80 (fwd) and
-    28C + 160 (bwd with dX, dx, dH and dbias) per token, bias and dbias once.  H_res / H_post of the
-    h_post_bda leg are the uniform doubly stochastic matrix and ones: their values do not change the
-    work or the traffic."""
+    28C + 160 (bwd with dX, dx, dH and dbias) per token, bias and dbias once.  The h_post_bda leg's
+    H_res is the library's 20-iteration Sinkhorn of N(0,1) logits and its H_post 2 sigmoid(N(0,1)),
+    as the workload states."""
     from mhc_hyper_connection_proj_amd import binding as B, synth
     dev = torch.device("cuda", 0)
 
@@ -215,8 +243,10 @@ def measure_configs(stream, torch) -> dict:
     w = synth.WORKLOADS["post_bda"]
     N, C = w.tokens, w.C
     X, G, x, b = (to_dev(synth.tensor(w, t)) for t in ("X", "G", "x", "bias"))
-    Hr = to_dev(np.ascontiguousarray(np.full((N, 4, 4), 0.25, np.float32)))
-    Hp = to_dev(np.ascontiguousarray(np.full((N, 4), 1.0, np.float32)))
+    # as stated: H_res doubly stochastic by 20 Sinkhorn iterations on N(0,1) logits (the library's
+    # Sinkhorn), H_post = 2 sigmoid(N(0,1))
+    Hr = B.mhc_sinkhorn_fwd(to_dev(synth.tensor(w, "L")), w.iters, w.eps)
+    Hp = 2.0 * torch.sigmoid(to_dev(synth.tensor(w, "Hpost_logits")))
     ms_f = timed(lambda: B.mhc_h_post_bda_fwd(X, Hr, Hp, x, b))
     ms_b = timed(lambda: B.mhc_h_post_bda_bwd(G, X, Hr, Hp, x, b))
     byt = ((18 * C + 80) + (28 * C + 160)) * N + 4 * C
@@ -227,30 +257,109 @@ def measure_configs(stream, torch) -> dict:
     return res
 
 
+def measure_ceilings(lib, L, sp, stream, torch, nbytes: int) -> dict:
+    """Practical memory rates of this GPU at the workload's shape (mhc_bandwidth_probe over buffers of
+    the residual's size, three rotated so that no call finds its input in the 256 MB Infinity Cache):
+    read only and copy (read + write bytes), with default and non-temporal loads; and the re-read of
+    one 256 MB buffer, which stays in the Infinity Cache.  Median of 8 event-timed calls."""
+    dev = torch.device("cuda", 0)
+    bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(3)]
+    sink = torch.empty(4096, dtype=torch.uint8, device=dev)
+
+    def med(fn, reps=8):
+        fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+
+    res = {"bytes": nbytes}
+    for name, kind in (("read", L.MHC_PROBE_READ), ("read_nt", L.MHC_PROBE_READ | L.MHC_PROBE_NONTEMPORAL),
+                       ("copy", L.MHC_PROBE_COPY), ("copy_nt", L.MHC_PROBE_COPY | L.MHC_PROBE_NONTEMPORAL)):
+        k = [0]
+        copy = kind & L.MHC_PROBE_COPY
+
+        def fn():
+            src, dst = bufs[k[0] % 3], (bufs[(k[0] + 1) % 3] if copy else sink)
+            L.check(lib.mhc_bandwidth_probe(sp, kind, src.data_ptr(), dst.data_ptr(), nbytes))
+            k[0] += 1
+        ms = med(fn)
+        gbs = (2 if copy else 1) * nbytes / (ms * 1e-3) / 1e9
+        res[name + "_gbs"] = gbs
+        res[name + "_frac"] = gbs / HBM_PEAK_GBS
+    small = 256 << 20
+    ms = med(lambda: L.check(lib.mhc_bandwidth_probe(sp, L.MHC_PROBE_READ | L.MHC_PROBE_NONTEMPORAL,
+                                                     bufs[0].data_ptr(), sink.data_ptr(), small)))
+    res["reread_256MiB_nt_gbs"] = small / (ms * 1e-3) / 1e9
+    del bufs
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, X, W, s, G, budget_s: float) -> dict:
-    """Time the fp64 oracle (single thread, as written) on the first tokens of the workload."""
+    """Time the fp64 oracle, as written, on the workload's tokens: the whole mHC fwd + bwd chain (with
+    the layer's scale) on chunks of 16 tokens, first on one thread, then on a pool of threads (the
+    oracle is C behind ctypes, which releases the GIL) sized to this process's CPU share, at most 16.
+    Each leg runs for about budget_s / 2 seconds on its own tokens."""
     import oracle as O
+    from concurrent.futures import ThreadPoolExecutor
 
     O._lib()
     C = w.C
-    n_done, t_used, chunk = 0, 0.0, 16
     Wd = W.astype(np.float64)
     sd = O.bf16_bits_to_f64(s)
-    while t_used < budget_s and n_done + chunk <= X.shape[0]:
-        sl = slice(n_done, n_done + chunk)
+
+    def chain(t0, n):
+        sl = slice(t0, t0 + n)
         Xc = O.bf16_bits_to_f64(X[sl]); Gc = O.bf16_bits_to_f64(G[sl])
-        t0 = time.perf_counter()
         f = O.pre_fwd(Xc, Wd, eps_rms=w.rms_eps, iters=w.iters, eps=w.eps)
         x = O.round_f64_to_bf16(O.round_f64_to_bf16(f["agg"]) * sd)
         O.h_post_bda_fwd(Xc, f["H_res"], f["H_post"], x, None)
         dX, dHr, dHp, dx, _ = O.h_post_bda_bwd(Gc, Xc, f["H_res"], f["H_post"], x, None)
         g = O.round_f64_to_bf16(O.round_f64_to_bf16(dx) * sd)
         O.pre_bwd(g, dHp, dHr, Xc, Wd, eps_rms=w.rms_eps, iters=w.iters, eps=w.eps)
+        return n
+
+    chunk, leg = 16, budget_s / 2
+    n1, t_used = 0, 0.0
+    while t_used < leg and n1 + chunk <= X.shape[0]:
+        t0 = time.perf_counter()
+        chain(n1, chunk)
         t_used += time.perf_counter() - t0
-        n_done += chunk
-    return {"value": n_done / t_used, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n_done} tokens of the workload (C={C}), full mHC fwd+bwd chain incl. "
-                      f"layer scale, fp64, {t_used:.1f} s single-threaded"}
+        n1 += chunk
+    single = n1 / t_used
+    try:
+        share = len(os.sched_getaffinity(0))
+    except AttributeError:
+        share = os.cpu_count() or 1
+    threads = max(1, min(16, share))
+    nchunks = X.shape[0] // chunk
+    nt, t0 = 0, time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        while time.perf_counter() - t0 < leg:  # the pool walks the workload's chunks, wrapping around
+            base = n1 // chunk + nt // chunk
+            nt += sum(ex.map(lambda i: chain(((base + i) % nchunks) * chunk, chunk), range(threads)))
+    t_pool = time.perf_counter() - t0
+    return {"value": nt / t_pool, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nt} tokens of the workload (C={C}) from token {n1} on, wrapping, full mHC fwd+bwd chain "
+                      f"incl. layer scale, fp64, {t_pool:.1f} s on {threads} threads",
+            "cpu_model": cpu_model(), "cpu_share": share,
+            "single_thread": {"value": single, "unit": "tokens/s", "cores": 1,
+                              "sample": f"first {n1} tokens, {t_used:.1f} s on one thread"}}
 
 
 def main():
@@ -260,7 +369,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--tokens", type=int, default=None, help="override token count (testing only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a 1 GiB device copy (for HBM counter calibration under rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -384,6 +493,8 @@ def main():
     mhc_ms = sum(mean[k] for k, _, m in seq if m)
     step_ms = sum(mean.values())
 
+    ceilings = measure_ceilings(lib, _lib, sp, stream, torch, N * n * C * 2)
+    projection_choice = measure_projection_choice(lib, _lib, sp, stream, torch, cur["X"], Wd, N, n, C)
     variants = measure_variants(lib, _lib, sp, N, n, C, cur["X"], Gd, H_res, H_post, x, g, out, dX, dHr, dHp, dx,
                                 stream, torch)
     general_n = measure_general_n(N, stream, torch)
@@ -425,6 +536,11 @@ def main():
         "achieved_gbs": gbs,
         "hbm_frac": gbs / HBM_PEAK_GBS,
         "ledger_bytes_per_token": led["total"],
+        "ledger": "74C+1336 bytes per token: every boundary tensor once per phase, the h_post_bda residual "
+                  "gradient formed inside the pre backward from G (so dX is written once), W and dW amortised",
+        "hbm_frac_82C_ledger": (82 * C + 1232) * N / (mhc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "ceilings": ceilings,
+        "projection_mfma_vs_fma": projection_choice,
         "phases_ms": mean,
         "ms_per_step_incl_layer": step_ms,
         "wall_ms_per_step": wall * 1e3 / args.steps,

@@ -94,6 +94,20 @@ const char *mhc_version(void);
 typedef enum mhc_kernel_id { MHC_KERNEL_NONE = 0, MHC_KERNEL_PROJ_BWD_DXDW = 1 } mhc_kernel_id;
 mhc_status mhc_set_kernel_events(int32_t kernel, void *start_event, void *stop_event);
 
+/* Measurement hook: the practical memory rates of the device, reported beside
+ * its HBM peak; nothing of the mHC path is computed.  Streams `bytes` (a
+ * multiple of 16) of src with 16-byte vector loads, four per thread in
+ * flight, 8192 workgroups of 256 threads each taking one contiguous share.
+ * kind = MHC_PROBE_READ: read only; dst (at least 4096 bytes) receives an
+ * unspecified checksum.  kind = MHC_PROBE_COPY: src is copied to dst (bytes
+ * each, not overlapping).  Add MHC_PROBE_NONTEMPORAL for loads (and copy
+ * stores) with the non-temporal cache policy.  Validation as for every
+ * entry point. */
+typedef enum mhc_probe_kind {
+  MHC_PROBE_READ = 0, MHC_PROBE_COPY = 1, MHC_PROBE_NONTEMPORAL = 2
+} mhc_probe_kind;
+mhc_status mhc_bandwidth_probe(void *stream, int32_t kind, const void *src, void *dst, size_t bytes);
+
 /* -------------------------------------------------------------------------
  * Projection + RMS + compute_h, forward.
  * Megatron Core "core.fusions.fused_mhc_kernels", operation
@@ -115,6 +129,17 @@ mhc_status mhc_proj_rms_h(void *stream, int64_t tokens, int32_t n, int64_t C, mh
                           const void *X, const float *W, const float *alpha, const float *hbias,
                           float rms_eps, float *H_pre, float *H_post, float *H_res_logits,
                           float *saved, void *workspace, size_t workspace_bytes);
+
+/* The same forward with the contraction x @ W as fp32 FMAs on the vector ALUs
+ * instead of the matrix cores: the comparison point that the MFMA choice is
+ * measured against (n == 4 and bf16 activations only, else
+ * MHC_ERR_UNSUPPORTED; the workspace of mhc_proj_rms_h_workspace_size).
+ * Results agree with mhc_proj_rms_h to fp32 rounding (a different summation
+ * order), not bit for bit. */
+mhc_status mhc_proj_rms_h_fma(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                              const void *X, const float *W, const float *alpha, const float *hbias,
+                              float rms_eps, float *H_pre, float *H_post, float *H_res_logits,
+                              float *saved, void *workspace, size_t workspace_bytes);
 
 /* -------------------------------------------------------------------------
  * Projection + RMS + compute_h, backward (RL-Kernel PR #383: the RMS

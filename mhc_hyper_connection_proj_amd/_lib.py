@@ -17,6 +17,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "mhc.h")
 
 MHC_BF16, MHC_F32 = 0, 1
 MHC_KERNEL_NONE, MHC_KERNEL_PROJ_BWD_DXDW = 0, 1  # mhc_kernel_id (mhc_set_kernel_events)
+MHC_PROBE_READ, MHC_PROBE_COPY, MHC_PROBE_NONTEMPORAL = 0, 1, 2  # mhc_probe_kind (mhc_bandwidth_probe)
 SAVED_STRIDE = 32
 STATUS = ["MHC_OK", "MHC_ERR_NULL", "MHC_ERR_SHAPE", "MHC_ERR_UNSUPPORTED", "MHC_ERR_ALIGN",
           "MHC_ERR_ALIAS", "MHC_ERR_WORKSPACE", "MHC_ERR_ARG", "MHC_ERR_HIP"]
@@ -38,9 +39,12 @@ SIGNATURES = {
     "mhc_version": (ctypes.c_char_p, []),
     "mhc_saved_stride": (_i32, [_i32]),
     "mhc_set_kernel_events": (ctypes.c_int, [_i32, _vp, _vp]),
+    "mhc_bandwidth_probe": (ctypes.c_int, [_vp, _i32, _vp, _vp, _sz]),
     "mhc_proj_rms_h_workspace_size": (_sz, [_i64, _i32, _i64, ctypes.c_int]),
     "mhc_proj_rms_h": (ctypes.c_int, [_vp, _i64, _i32, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _f32,
                                       _vp, _vp, _vp, _vp, _vp, _sz]),
+    "mhc_proj_rms_h_fma": (ctypes.c_int, [_vp, _i64, _i32, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _f32,
+                                          _vp, _vp, _vp, _vp, _vp, _sz]),
     "mhc_proj_rms_h_bwd_workspace_size": (_sz, [_i64, _i32, _i64, ctypes.c_int]),
     "mhc_proj_rms_h_bwd": (ctypes.c_int, [_vp, _i64, _i32, _i64, ctypes.c_int, _vp, _vp, _vp, _vp,
                                           _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _sz]),

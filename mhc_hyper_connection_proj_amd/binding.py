@@ -65,7 +65,7 @@ def _dims(X: torch.Tensor):
 f32 = torch.float32
 
 
-def mhc_proj_rms_h(X, W, alpha=None, hbias=None, rms_eps=1e-6):
+def mhc_proj_rms_h(X, W, alpha=None, hbias=None, rms_eps=1e-6, _entry="mhc_proj_rms_h"):
     """Projection + RMS + compute_h.  Returns (H_pre, H_post, H_res_logits, saved)."""
     N, n, C = _dims(X)
     J = n_outputs(n)
@@ -78,9 +78,15 @@ def mhc_proj_rms_h(X, W, alpha=None, hbias=None, rms_eps=1e-6):
     L = torch.empty(*lead, n, n, dtype=f32, device=d)
     saved = torch.empty(*lead, saved_stride(n), dtype=f32, device=d)
     ws, wsb = _ws(_lib.lib().mhc_proj_rms_h_workspace_size(N, n, C, act), d)
-    call("mhc_proj_rms_h", _stream(X), N, n, C, act, _p(X), _p(W), _p(alpha), _p(hbias), rms_eps,
+    call(_entry, _stream(X), N, n, C, act, _p(X), _p(W), _p(alpha), _p(hbias), rms_eps,
          _p(H_pre), _p(H_post), _p(L), _p(saved), _p(ws), wsb)
     return H_pre, H_post, L, saved
+
+
+def mhc_proj_rms_h_fma(X, W, alpha=None, hbias=None, rms_eps=1e-6):
+    """mhc_proj_rms_h with x @ W as fp32 FMAs on the vector ALUs (the comparison point of the MFMA form;
+    n = 4, bf16).  Returns (H_pre, H_post, H_res_logits, saved)."""
+    return mhc_proj_rms_h(X, W, alpha, hbias, rms_eps, _entry="mhc_proj_rms_h_fma")
 
 
 def mhc_proj_rms_h_bwd(X, W, saved, H_pre, H_post, dH_pre, dH_post, dH_res_logits, alpha=None,

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmhc.so")
-SOURCES = ["api.hip", "sinkhorn.hip", "streams.hip", "proj.hip", "norm.hip", "reduce.hip", "generic.hip"]
+SOURCES = ["api.hip", "sinkhorn.hip", "streams.hip", "proj.hip", "norm.hip", "reduce.hip", "generic.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

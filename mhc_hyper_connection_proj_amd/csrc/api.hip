@@ -305,6 +305,22 @@ mhc_status mhc_set_kernel_events(int32_t kernel, void *start_event, void *stop_e
   return MHC_OK;
 }
 
+mhc_status mhc_bandwidth_probe(void *stream, int32_t kind, const void *src, void *dst, size_t bytes) {
+  Validator v("mhc_bandwidth_probe");
+  const bool copy = (kind & MHC_PROBE_COPY) != 0;
+  if (kind < 0 || kind > (MHC_PROBE_COPY | MHC_PROBE_NONTEMPORAL)) v.fail(MHC_ERR_ARG, "unknown probe kind");
+  if (bytes % 16) v.fail(MHC_ERR_SHAPE, "bytes must be a multiple of 16");
+  if (bytes > ((size_t)1 << 40)) v.fail(MHC_ERR_UNSUPPORTED, "bytes must be <= 2^40");
+  if (!v.ok()) return v.status();
+  if (bytes == 0) return MHC_OK;
+  v.in(src, bytes, "src");
+  v.out(dst, copy ? bytes : (size_t)mhc::kProbeSinkWords * 4, "dst");
+  if (v.finish() != MHC_OK) return v.status();
+  mhc::launch_bandwidth_probe((hipStream_t)stream, copy, (kind & MHC_PROBE_NONTEMPORAL) != 0, src, dst,
+                              (int64_t)bytes);
+  return launched("mhc_bandwidth_probe");
+}
+
 // ------------------------------------------------------------------ projection fwd
 size_t mhc_proj_rms_h_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
   if (tokens <= 0 || tokens > mhc::kMaxTokens || n < 1 || n > mhc::kMaxN || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
@@ -339,6 +355,32 @@ mhc_status mhc_proj_rms_h(void *stream, int64_t tokens, int32_t n, int64_t C, mh
     mhc::glaunch_proj_fwd((hipStream_t)stream, act == MHC_F32, n, tokens, C, X, W, alpha, hbias, rms_eps,
                           H_pre, H_post, H_res_logits, saved, nullptr, 0, 0.f, workspace);
   return launched("mhc_proj_rms_h");
+}
+
+mhc_status mhc_proj_rms_h_fma(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                              const void *X, const float *W, const float *alpha, const float *hbias,
+                              float rms_eps, float *H_pre, float *H_post, float *H_res_logits,
+                              float *saved, void *workspace, size_t workspace_bytes) {
+  Validator v("mhc_proj_rms_h_fma");
+  v.dims(tokens, n, C, act);
+  v.eps(rms_eps, "rms_eps");
+  if (v.ok() && (n != 4 || act != MHC_BF16)) v.fail(MHC_ERR_UNSUPPORTED, "the FMA form takes n == 4 and bf16 only");
+  if (!v.ok()) return v.status();
+  if (tokens == 0) return MHC_OK;
+  const int64_t K = 4 * C;
+  v.in(X, tokens * K * 2, "X");
+  v.in(W, K * 24 * 4, "W");
+  v.in(alpha, 3 * 4, "alpha", true);
+  v.in(hbias, 24 * 4, "hbias", true);
+  v.out(H_pre, tokens * 16, "H_pre");
+  v.out(H_post, tokens * 16, "H_post");
+  v.out(H_res_logits, tokens * 64, "H_res_logits");
+  v.out(saved, tokens * mhc::kSavedStride * 4, "saved", true);
+  v.workspace(workspace, workspace_bytes, mhc::proj_fwd_ws(tokens, C, false));
+  if (v.finish() != MHC_OK) return v.status();
+  mhc::launch_proj_fwd_fma((hipStream_t)stream, tokens, C, X, W, alpha, hbias, rms_eps, H_pre, H_post,
+                           H_res_logits, saved, workspace);
+  return launched("mhc_proj_rms_h_fma");
 }
 
 // ------------------------------------------------------------------ projection bwd

@@ -27,6 +27,11 @@ StreamGeom stream_geom(int64_t C);
 constexpr int kKernelProjBwdDxDw = 1;  // MHC_KERNEL_PROJ_BWD_DXDW
 void kernel_event(int id, hipStream_t s, bool start);
 
+// ---- bandwidth probe (measurement only): read `bytes` of src (checksums to a
+// kProbeSinkWords-word sink at dst) or copy them to dst; bytes % 16 == 0.
+constexpr int kProbeSinkWords = 1024;
+void launch_bandwidth_probe(hipStream_t s, bool copy, bool nt, const void *src, void *dst, int64_t bytes);
+
 // ---- Sinkhorn
 void launch_sinkhorn_fwd(hipStream_t s, int64_t count, const float *L, float *H, int iters, float eps);
 void launch_sinkhorn_bwd(hipStream_t s, int64_t count, const float *dH, const float *L, float *dL,
@@ -91,6 +96,12 @@ void launch_proj_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *
                      const float *alpha, const float *hbias, float rms_eps, float *H_pre,
                      float *H_post, float *logits, float *saved, float *H_res, int iters,
                      float eps, void *ws);
+
+// The same forward (bf16 activations) with x @ W on the VALU: the comparison
+// point for the MFMA projection (same workspace layout, Sinkhorn not run).
+void launch_proj_fwd_fma(hipStream_t s, int64_t N, int64_t C, const void *X, const float *W, const float *alpha,
+                         const float *hbias, float rms_eps, float *H_pre, float *H_post, float *logits,
+                         float *saved, void *ws);
 
 // ---- projection (backward).  Two front ends share the dX / dW kernels:
 //  - proj_rms_h_bwd: dL given directly (dH_res_logits)

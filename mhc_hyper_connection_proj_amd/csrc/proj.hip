@@ -368,6 +368,94 @@ __global__ __launch_bounds__(512) void proj_partial_dma_kernel(const bf16_t *__r
   if (h == 0 && tw + row < N) part[((int64_t)slice * N + tw + row) * kPartStride + kJ] = ss;
 }
 
+// ------------------------------------------------------------------ partial projection, bf16 on the VALU
+// The comparison point for the MFMA kernel above: the same token blocks x k
+// slices and the same partial records, with x @ W as fp32 FMAs.  Thread =
+// one token (256 per workgroup).  The slice's 64-k chunks of W (fp32,
+// [k][24], 6 KB) pass through a two-slot LDS buffer, the next chunk's loaded
+// into registers while the current one is used; every lane reads the same W
+// words (LDS broadcast).  A chunk's eight 16-byte groups of the token's x
+// are loaded together, then 64 x 24 FMAs accumulate into a fresh per-chunk
+// sum that is added to the running one (the same two-level blocking).
+constexpr int kFmaTok = 256;
+
+__global__ __launch_bounds__(256) void proj_partial_fma_kernel(const bf16_t *__restrict__ X,
+                                                               const float *__restrict__ W,
+                                                               float *__restrict__ part, int64_t N,
+                                                               int64_t K) {
+  __shared__ float4 wl[2][64 * kJ / 4];
+  const int slice = blockIdx.x % kSplitK;
+  const int64_t tb = blockIdx.x / kSplitK;
+  const int64_t t = tb * kFmaTok + threadIdx.x;
+  const bool tv = t < N;
+  const bf16_t *xr = X + (tv ? t : N - 1) * K;
+  const int64_t nch = (K + 63) / 64;
+  const int64_t cps = (nch + kSplitK - 1) / kSplitK;
+  const int64_t c_begin = min(nch, slice * cps);
+  const int nc = (int)(min(nch, c_begin + cps) - c_begin);
+  // W chunk i: 64 k x 24 floats = 384 float4; thread e and e + 256 load float4 e of it
+  float4 wr[2];
+  auto load_w = [&](int i) {
+    const int64_t k0 = (c_begin + i) * 64;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = threadIdx.x + 256 * q;
+      const int64_t k = k0 + e / 6;
+      wr[q] = (e < 384 && k < K) ? reinterpret_cast<const float4 *>(W + k * kJ)[e % 6]
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  float outer[kJ];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) outer[j] = 0.f;
+  float ss = 0.f;
+  if (nc > 0) load_w(0);
+  for (int i = 0; i < nc; ++i) {
+    float4 *slot = wl[i & 1];
+    slot[threadIdx.x] = wr[0];
+    if (threadIdx.x < 128) slot[threadIdx.x + 256] = wr[1];
+    __syncthreads();  // slot i & 1 was last read two chunks ago, before the previous barrier
+    if (i + 1 < nc) load_w(i + 1);
+    const int64_t k0 = (c_begin + i) * 64;
+    uint4 xg[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+      xg[g] = k0 + 8 * g < K ? *reinterpret_cast<const uint4 *>(xr + k0 + 8 * g) : make_uint4(0u, 0u, 0u, 0u);
+    float acc[kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) acc[j] = 0.f;
+    float s = 0.f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const uint32_t w4[4] = {xg[g].x, xg[g].y, xg[g].z, xg[g].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float xv = (e & 1) ? bf16_hi(w4[e >> 1]) : bf16_lo(w4[e >> 1]);
+        s = fmaf(xv, xv, s);
+        const float4 *wrow = slot + (8 * g + e) * (kJ / 4);
+#pragma unroll
+        for (int q = 0; q < kJ / 4; ++q) {
+          const float4 wv = wrow[q];
+          acc[4 * q] = fmaf(xv, wv.x, acc[4 * q]);
+          acc[4 * q + 1] = fmaf(xv, wv.y, acc[4 * q + 1]);
+          acc[4 * q + 2] = fmaf(xv, wv.z, acc[4 * q + 2]);
+          acc[4 * q + 3] = fmaf(xv, wv.w, acc[4 * q + 3]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) outer[j] += acc[j];
+    ss += s;
+  }
+  if (tv) {
+    float *dst = part + ((int64_t)slice * N + t) * kPartStride;
+#pragma unroll
+    for (int q = 0; q < kJ / 4; ++q)
+      reinterpret_cast<float4 *>(dst)[q] = make_float4(outer[4 * q], outer[4 * q + 1], outer[4 * q + 2], outer[4 * q + 3]);
+    dst[kJ] = ss;
+  }
+}
+
 // ------------------------------------------------------------------ finalize
 // Four lanes per token (quad layout of the Sinkhorn code: lane r = row r of
 // H_res), 16 tokens per one-wave workgroup, so a layer's tokens make enough
@@ -466,6 +554,17 @@ void launch_proj_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *
   }
   hipLaunchKernelGGL(proj_finalize_kernel, dim3((unsigned)((N + 15) / 16)), dim3(64), 0, s, part,
                      alpha, hbias, rms_eps, H_pre, H_post, logits, saved, H_res, iters, eps, N, K);
+}
+
+void launch_proj_fwd_fma(hipStream_t s, int64_t N, int64_t C, const void *X, const float *W, const float *alpha,
+                         const float *hbias, float rms_eps, float *H_pre, float *H_post, float *logits,
+                         float *saved, void *ws) {
+  const int64_t K = 4 * C;
+  float *part = (float *)((char *)ws + align256(wpack_bytes(C, false)));
+  const unsigned pblocks = (unsigned)(((N + kFmaTok - 1) / kFmaTok) * kSplitK);
+  hipLaunchKernelGGL(proj_partial_fma_kernel, dim3(pblocks), dim3(256), 0, s, (const bf16_t *)X, W, part, N, K);
+  hipLaunchKernelGGL(proj_finalize_kernel, dim3((unsigned)((N + 15) / 16)), dim3(64), 0, s, part, alpha, hbias,
+                     rms_eps, H_pre, H_post, logits, saved, (float *)nullptr, 0, 0.f, N, K);
 }
 
 // ================================================================== backward

@@ -87,6 +87,13 @@ def test_pre_fwd_full_size(name):
     assert_rel("q", sv[:, 1], ref["q"])
     assert_mixed("z", sv[:, 2:26], ref["z"])
     assert_act("agg", rows(o["agg"], S), ref["agg"], w.act)
+    # the VALU (FMA) form of the projection at the same size
+    Hp, Hq, L, sv2 = B.mhc_proj_rms_h_fma(dev(X), dev(W), None, None, w.rms_eps)
+    torch.cuda.synchronize()
+    assert_rel("H_pre (fma)", rows(Hp, S), ref["H_pre"])
+    assert_rel("H_post (fma)", rows(Hq, S), ref["H_post"])
+    assert_mixed("logits (fma)", rows(L, S), ref["L"])
+    assert_rel("r (fma)", h64(rows(sv2, S))[:, 0], ref["r"])
 
 
 # ----------------------------------------------------------------- post (h_post_bda) forward + backward

@@ -252,6 +252,24 @@ def test_proj_rms_h_fwd(act, N, C):
     assert_rel("H_post", Hq, p.H_post)
 
 
+@pytest.mark.parametrize("N,C", [(37, 296), (70, 4096), (67, 7168), (5, 8), (129, 1024), (33, 16384), (300, 64)])
+def test_proj_rms_h_fma(N, C):
+    """The VALU (FMA) form of the forward projection, kept as the MFMA choice's comparison point."""
+    log(f"proj_rms_h fma N={N} C={C}")
+    X, W, alpha, hb = _proj_inputs("bf16", N, C)
+    Hp, Hq, L, saved = B.mhc_proj_rms_h_fma(dev(X), dev(W), dev(alpha), dev(hb), 1e-6)
+    torch.cuda.synchronize()
+    p = O.proj_rms_h(h64(X), h64(W), h64(alpha), h64(hb), 1e-6)
+    s = h64(saved)
+    assert_rel("q", s[:, 1], p.q)
+    assert_rel("r", s[:, 0], p.r)
+    assert_mixed("z", s[:, 2:26], p.z)
+    np.testing.assert_array_equal(s[:, 26:], 0.0)
+    assert_mixed("logits", L, p.L)
+    assert_rel("H_pre", Hp, p.H_pre)
+    assert_rel("H_post", Hq, p.H_post)
+
+
 @pytest.mark.parametrize("act,N,C", PROJ)
 def test_proj_rms_h_bwd(act, N, C):
     log(f"proj_rms_h bwd act={act} N={N} C={C}")
