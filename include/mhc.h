@@ -376,13 +376,40 @@ mhc_status mhc_rmsnorm_bwd(void *stream, int64_t tokens, int64_t C, mhc_dtype ac
  * stored (the values after rounding to act), so the result equals
  * mhc_pre_fwd followed by mhc_rmsnorm_fwd on its agg.  gamma [C] fp32 or
  * NULL, norm_eps >= 0, normed [tokens][C] (act).  The backward is
- * mhc_rmsnorm_bwd (dy -> gradient of agg) followed by mhc_pre_bwd.
+ * mhc_pre_rmsnorm_bwd (or mhc_rmsnorm_bwd followed by mhc_pre_bwd).
  * ---------------------------------------------------------------------- */
 mhc_status mhc_pre_rmsnorm_fwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
                                const void *X, const float *W, const float *alpha, const float *hbias,
                                float rms_eps, int32_t iters, float eps, const float *gamma,
                                float norm_eps, float *H_pre, float *H_post, float *H_res,
                                float *H_res_logits, float *saved, void *agg, void *normed,
+                               void *workspace, size_t workspace_bytes);
+
+/* Fused pre pass backward with the norm's backward in front, the backward of
+ * mhc_pre_rmsnorm_fwd (RL-Kernel PR #383, P1-5 rmsnorm_residual: the norm and
+ * its residual fork in front of the pre pass).  Results equal, bit for bit,
+ *   mhc_rmsnorm_bwd(dy, agg, gamma, norm_eps, dx = g_fork copy, accumulate_dx =
+ *                   g_fork != NULL, dgamma)          -> d_agg (act, rounded)
+ *   mhc_pre_bwd(g = d_agg, dH_post, dH_res, X, ...)  -> dX, dW, dalpha, dhbias
+ * but for n == 4 one pass over dy, agg and X forms both d_agg and the dH_pre
+ * that the pre backward needs, so d_agg is written once and read once instead
+ * of written, read and read again.
+ * dy [tokens][C] (act): gradient of the normed output; agg [tokens][C] (act):
+ * the norm's input as the forward stored it; gamma [C] fp32 or NULL (unit
+ * gain); g_fork [tokens][C] (act) or NULL: agg's own upstream gradient (the
+ * residual fork), added to the norm's input gradient.  dgamma [C] fp32 or
+ * NULL; d_agg_out [tokens][C] (act) or NULL: receives d_agg.  The other
+ * arguments as mhc_pre_bwd (without the intermediate outputs).  tokens == 0
+ * zero-fills dW, dalpha, dhbias and dgamma. */
+size_t mhc_pre_rmsnorm_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                                          int32_t with_dgamma);
+mhc_status mhc_pre_rmsnorm_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                               const void *dy, const void *agg, const float *gamma, float norm_eps,
+                               const void *g_fork, const float *dH_post, const float *dH_res, const void *X,
+                               const float *W, const float *alpha, const float *saved, const float *H_pre,
+                               const float *H_post, const float *H_res_logits, int32_t iters, float eps,
+                               const void *post_G, const float *post_H_res, void *dX, int32_t accumulate_dX,
+                               float *dW, float *dalpha, float *dhbias, float *dgamma, void *d_agg_out,
                                void *workspace, size_t workspace_bytes);
 
 #ifdef __cplusplus

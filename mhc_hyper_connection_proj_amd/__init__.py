@@ -12,7 +12,10 @@ from .binding import (  # noqa: F401
     mhc_h_post_bda_fwd,
     mhc_pre_bwd,
     mhc_pre_fwd,
+    mhc_pre_rmsnorm_bwd,
+    mhc_pre_rmsnorm_fwd,
     mhc_proj_rms_h,
+    mhc_proj_rms_h_fma,
     mhc_proj_rms_h_bwd,
     mhc_sinkhorn_bwd,
     mhc_sinkhorn_fwd,

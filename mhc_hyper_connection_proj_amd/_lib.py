@@ -83,6 +83,10 @@ SIGNATURES = {
     "mhc_pre_bwd": (ctypes.c_int, [_vp, _i64, _i32, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _vp, _vp, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _i32, _vp,
                                    _vp, _vp, _vp, _vp, _vp, _sz]),
+    "mhc_pre_rmsnorm_bwd_workspace_size": (_sz, [_i64, _i32, _i64, ctypes.c_int, _i32]),
+    "mhc_pre_rmsnorm_bwd": (ctypes.c_int, [_vp, _i64, _i32, _i64, ctypes.c_int, _vp, _vp, _vp, _f32, _vp, _vp, _vp,
+                                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _i32, _vp,
+                                           _vp, _vp, _vp, _vp, _vp, _sz]),
 }
 
 _lib = None

@@ -371,3 +371,39 @@ def mhc_pre_bwd(g, dH_post, dH_res, X, W, saved, H_pre, H_post, H_res_logits, al
          _p(o["dW"]), _p(o["dalpha"]), _p(o["dhbias"]), _p(o.get("dH_pre")), _p(o.get("dlogits")),
          _p(ws), wsb)
     return o
+
+
+def mhc_pre_rmsnorm_bwd(dy, agg, dH_post, dH_res, X, W, saved, H_pre, H_post, H_res_logits, gamma=None,
+                        norm_eps=1e-6, g_fork=None, alpha=None, iters=20, eps=1e-6, dX=None, accumulate_dX=False,
+                        post_G=None, post_H_res=None, want_dgamma=None, want_d_agg=False):
+    """Fused pre pass backward with the norm's backward in front (the backward of mhc_pre_rmsnorm_fwd).
+    Returns dict(dX, dW, dalpha, dhbias[, dgamma][, d_agg]).  g_fork: agg's own upstream gradient."""
+    N, n, C = _dims(X)
+    J = n_outputs(n)
+    act = _act(X)
+    _need(X, "X"); _need(dy, "dy", X.dtype, N * C); _need(agg, "agg", X.dtype, N * C)
+    _need(gamma, "gamma", f32, C); _need(g_fork, "g_fork", X.dtype, N * C)
+    _need(dH_post, "dH_post", f32, N * n); _need(dH_res, "dH_res", f32, N * n * n); _need(W, "W", f32, n * C * J)
+    _need(alpha, "alpha", f32, 3); _need(saved, "saved", f32, N * saved_stride(n)); _need(H_pre, "H_pre", f32, N * n)
+    _need(H_post, "H_post", f32, N * n); _need(H_res_logits, "H_res_logits", f32, N * n * n)
+    _need(post_G, "post_G", X.dtype, X.numel()); _need(post_H_res, "post_H_res", f32, N * n * n)
+    d = X.device
+    if dX is None:
+        if accumulate_dX:
+            raise ValueError("accumulate_dX needs dX")
+        dX = torch.empty_like(X)
+    _need(dX, "dX", X.dtype, X.numel())
+    if want_dgamma is None:
+        want_dgamma = gamma is not None
+    o = dict(dX=dX, dW=torch.empty(n * C, J, dtype=f32, device=d), dalpha=torch.empty(3, dtype=f32, device=d),
+             dhbias=torch.empty(J, dtype=f32, device=d))
+    if want_dgamma:
+        o["dgamma"] = torch.empty(C, dtype=f32, device=d)
+    if want_d_agg:
+        o["d_agg"] = torch.empty(N, C, dtype=X.dtype, device=d)
+    ws, wsb = _ws(_lib.lib().mhc_pre_rmsnorm_bwd_workspace_size(N, n, C, act, int(want_dgamma)), d)
+    call("mhc_pre_rmsnorm_bwd", _stream(X), N, n, C, act, _p(dy), _p(agg), _p(gamma), norm_eps, _p(g_fork),
+         _p(dH_post), _p(dH_res), _p(X), _p(W), _p(alpha), _p(saved), _p(H_pre), _p(H_post), _p(H_res_logits),
+         iters, eps, _p(post_G), _p(post_H_res), _p(dX), int(accumulate_dX), _p(o["dW"]), _p(o["dalpha"]),
+         _p(o["dhbias"]), _p(o.get("dgamma")), _p(o.get("d_agg")), _p(ws), wsb)
+    return o

@@ -157,6 +157,19 @@ bool zero_f32(hipStream_t s, float *p, int64_t n) {
   return true;
 }
 
+__global__ void copy16_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst, int64_t n16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n16) dst[i] = src[i];
+}
+
+// dst = src, `bytes` a multiple of 16 (a kernel, not a copy node, so callers may capture the call)
+void copy16(hipStream_t s, const void *src, void *dst, int64_t bytes) {
+  const int64_t n16 = bytes / 16;
+  if (n16 <= 0) return;
+  hipLaunchKernelGGL(copy16_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s, (const uint4 *)src,
+                     (uint4 *)dst, n16);
+}
+
 bool zero_act(hipStream_t s, void *p, int64_t n, mhc_dtype act) {
   if (!p || n <= 0) return false;
   if (act == MHC_F32) return zero_f32(s, (float *)p, n);
@@ -849,6 +862,110 @@ mhc_status mhc_pre_rmsnorm_fwd(void *stream, int64_t tokens, int32_t n, int64_t 
     mhc::launch_rmsnorm_fwd(s, act == MHC_F32, tokens, C, agg, gamma, norm_eps, normed);
   }
   return launched("mhc_pre_rmsnorm_fwd");
+}
+
+// ------------------------------------------------------------------ fused pre backward with the norm
+namespace {
+struct PreNormBwdWs {
+  size_t pre, dagg, dhpre, norm, total;
+};
+PreNormBwdWs pre_norm_bwd_ws(int64_t tokens, int32_t n, int64_t C, mhc_dtype act, bool dgamma) {
+  auto a256 = [](size_t b) { return (b + 255) / 256 * 256; };
+  PreNormBwdWs w{};
+  w.pre = a256(n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_bwd_ws(n, tokens, C, true));
+  w.dagg = a256((size_t)tokens * C * esz(act));
+  w.dhpre = a256((size_t)tokens * 4 * 4);
+  w.norm = a256(mhc::rmsnorm_bwd_ws(tokens, C, dgamma));
+  w.total = w.pre + w.dagg + w.dhpre + w.norm;
+  return w;
+}
+}  // namespace
+
+size_t mhc_pre_rmsnorm_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                                          int32_t with_dgamma) {
+  if (tokens <= 0 || tokens > mhc::kMaxTokens || n < 1 || n > mhc::kMaxN || C <= 0 || C % 8 || C > mhc::kMaxC)
+    return 0;
+  return pre_norm_bwd_ws(tokens, n, C, act, with_dgamma != 0).total;
+}
+
+mhc_status mhc_pre_rmsnorm_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
+                               const void *dy, const void *agg, const float *gamma, float norm_eps,
+                               const void *g_fork, const float *dH_post, const float *dH_res, const void *X,
+                               const float *W, const float *alpha, const float *saved, const float *H_pre,
+                               const float *H_post, const float *H_res_logits, int32_t iters, float eps,
+                               const void *post_G, const float *post_H_res, void *dX, int32_t accumulate_dX,
+                               float *dW, float *dalpha, float *dhbias, float *dgamma, void *d_agg_out,
+                               void *workspace, size_t workspace_bytes) {
+  Validator v("mhc_pre_rmsnorm_bwd");
+  v.dims(tokens, n, C, act);
+  v.eps(eps, "eps");
+  v.eps(norm_eps, "norm_eps");
+  v.iters(iters);
+  if ((post_G == nullptr) != (post_H_res == nullptr))
+    v.fail(MHC_ERR_ARG, "post_G and post_H_res must be given together");
+  if (!v.ok()) return v.status();
+  const int64_t K = (int64_t)n * C;
+  const int64_t J = (int64_t)n * n + 2 * n;
+  const hipStream_t s = (hipStream_t)stream;
+  if (tokens == 0) {
+    v.out(dW, K * J * 4, "dW", true);
+    v.out(dalpha, 12, "dalpha", true);
+    v.out(dhbias, J * 4, "dhbias", true);
+    v.out(dgamma, C * 4, "dgamma", true);
+    if (v.finish() != MHC_OK) return v.status();
+    const bool any = zero_f32(s, dW, K * J) | zero_f32(s, dalpha, 3) | zero_f32(s, dhbias, J) | zero_f32(s, dgamma, C);
+    return any ? launched("mhc_pre_rmsnorm_bwd") : MHC_OK;
+  }
+  v.in(dy, tokens * C * esz(act), "dy");
+  v.in(agg, tokens * C * esz(act), "agg");
+  v.in(gamma, C * 4, "gamma", true);
+  v.in(g_fork, tokens * C * esz(act), "g_fork", true);
+  v.in(dH_post, tokens * n * 4, "dH_post");
+  v.in(dH_res, tokens * n * n * 4, "dH_res");
+  v.in(X, tokens * K * esz(act), "X");
+  v.in(W, K * J * 4, "W");
+  v.in(alpha, 12, "alpha", true);
+  v.in(saved, tokens * mhc::saved_stride(n) * 4, "saved");
+  v.in(H_pre, tokens * n * 4, "H_pre");
+  v.in(H_post, tokens * n * 4, "H_post");
+  v.in(H_res_logits, tokens * n * n * 4, "H_res_logits");
+  v.in(post_G, tokens * K * esz(act), "post_G", true);
+  v.in(post_H_res, tokens * n * n * 4, "post_H_res", true);
+  v.out(dX, tokens * K * esz(act), "dX");
+  v.out(dW, K * J * 4, "dW", true);
+  v.out(dalpha, 12, "dalpha", true);
+  v.out(dhbias, J * 4, "dhbias", true);
+  v.out(dgamma, C * 4, "dgamma", true);
+  v.out(d_agg_out, tokens * C * esz(act), "d_agg_out", true);
+  const PreNormBwdWs lay = pre_norm_bwd_ws(tokens, n, C, act, dgamma != nullptr);
+  v.workspace(workspace, workspace_bytes, lay.total);
+  if (v.finish() != MHC_OK) return v.status();
+  char *ws = (char *)workspace;
+  void *dagg = d_agg_out ? d_agg_out : (void *)(ws + lay.pre);
+  float *dhpre = (float *)(ws + lay.pre + lay.dagg);
+  void *norm_ws = ws + lay.pre + lay.dagg + lay.dhpre;
+  mhc::ProjBwdArgs a{};
+  a.f32 = act == MHC_F32; a.N = tokens; a.C = C; a.X = X; a.W = W; a.alpha = alpha; a.saved = saved;
+  a.H_pre = H_pre; a.H_post = H_post; a.dH_pre = nullptr; a.dH_post = dH_post; a.dL = nullptr;
+  a.dH_res = dH_res; a.logits = H_res_logits; a.iters = iters; a.eps = eps; a.g = dagg; a.dX = dX;
+  a.accumulate = accumulate_dX != 0; a.dW = dW; a.dalpha = dalpha; a.dhbias = dhbias;
+  a.dH_pre_out = nullptr; a.dL_out = nullptr; a.ws = ws;
+  a.post_G = post_G; a.post_H_res = post_H_res;
+  if (n == 4) {
+    // the norm's backward and the dH_pre pass in one pass over dy, agg and X
+    mhc::launch_h_aggregate_rmsnorm_bwd(s, act == MHC_F32, tokens, C, dy, agg, gamma, g_fork, X, norm_eps, dagg,
+                                        dhpre, dgamma, norm_ws);
+    a.dH_pre = dhpre;
+    mhc::launch_proj_bwd(s, a);
+  } else {  // other n: the norm's backward, then the pre backward (the same results)
+    if (g_fork) {  // agg's own gradient is the accumulation base
+      copy16(s, g_fork, dagg, tokens * C * (int64_t)esz(act));
+    }
+    mhc::launch_rmsnorm_bwd(s, act == MHC_F32, tokens, C, dy, agg, gamma, norm_eps, dagg, g_fork != nullptr,
+                            dgamma, norm_ws);
+    mhc::glaunch_proj_bwd(s, n, a);
+  }
+  return launched("mhc_pre_rmsnorm_bwd");
 }
 
 size_t mhc_pre_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {

@@ -23,8 +23,8 @@ import pytest
 import torch
 
 import oracle as O
-from gpu_util import (assert_act, assert_h_res, assert_mixed, assert_rel, assert_tokensum, dev, h64, log,
-                      pre_bwd_abs_parts, sum_depth)
+from gpu_util import (assert_act, assert_h_res, assert_mixed, assert_normed, assert_rel, assert_tokensum, dev,
+                      h64, log, pre_bwd_abs_parts, sum_depth)
 from mhc_hyper_connection_proj_amd import binding as B
 from mhc_hyper_connection_proj_amd import synth
 
@@ -261,6 +261,4 @@ def test_rmsnorm_full_size():
     ref = O.pre_fwd(h64(X[S]), h64(W), None, None, w.rms_eps, w.iters, w.eps)
     assert_act("agg", rows(f["agg"], S), ref["agg"], w.act)
     assert_rel("H_res", rows(f["H_res"], S), ref["H_res"])
-    # boundary by boundary: the norm of the agg rows the GPU stored, one bf16 ulp
-    yo, _ = O.rmsnorm_fwd(h64(rows(f["agg"], S)), h64(gamma), w.rms_eps)
-    assert_act("normed", rows(f["normed"], S), yo, w.act)
+    assert_normed("normed", rows(f["normed"], S), rows(f["agg"], S), ref["agg"], h64(gamma), w.rms_eps, w.act)
