@@ -153,6 +153,64 @@ def measure_projection_choice(lib, L, sp, stream, torch, X, W, N, n, C) -> dict:
     return res
 
 
+def measure_norm_bwd_fusion(lib, L, sp, stream, torch, N, n, C, X, W, G, H_res, agg, dy, saved, H_pre, H_post,
+                            logits, dHp, dHr) -> dict:
+    """The pre backward with the norm's backward in front, at the workload's shape (the h_post_bda term
+    formed from G), with a gain and dgamma and without: mhc_pre_rmsnorm_bwd against mhc_rmsnorm_bwd
+    followed by mhc_pre_bwd (the same results, bit for bit).  Mean of 5 event-timed calls after one
+    warm-up."""
+    dev = X.device
+    bf = torch.bfloat16
+    P = lambda t: t.data_ptr() if t is not None else None
+    gam = torch.linspace(0.5, 1.5, C, device=dev)
+    dgam = torch.empty(C, device=dev)
+    dX = torch.empty(N, n, C, dtype=bf, device=dev)
+    dagg = torch.empty(N, C, dtype=bf, device=dev)
+    dW, da, db = (torch.empty(*sh, device=dev) for sh in ((n * C, 24), (3,), (24,)))
+    wf = lib.mhc_pre_rmsnorm_bwd_workspace_size(N, n, C, L.MHC_BF16, 1)
+    wsf = torch.empty(wf, dtype=torch.uint8, device=dev)
+    wn = lib.mhc_rmsnorm_bwd_workspace_size(N, C, L.MHC_BF16, 1)
+    wsn = torch.empty(wn, dtype=torch.uint8, device=dev)
+    wp = lib.mhc_pre_bwd_workspace_size(N, n, C, L.MHC_BF16)
+    wsp = torch.empty(wp, dtype=torch.uint8, device=dev)
+
+    def fused():
+        L.check(lib.mhc_pre_rmsnorm_bwd(sp, N, n, C, L.MHC_BF16, P(dy), P(agg), P(gam), 1e-6, None, P(dHp), P(dHr),
+                                        P(X), P(W), None, P(saved), P(H_pre), P(H_post), P(logits), 20, 1e-6, P(G),
+                                        P(H_res), P(dX), 0, P(dW), P(da), P(db), P(dgam), None, P(wsf), wf))
+
+    def composed():
+        L.check(lib.mhc_rmsnorm_bwd(sp, N, C, L.MHC_BF16, P(dy), P(agg), P(gam), 1e-6, P(dagg), 0, P(dgam), P(wsn), wn))
+        L.check(lib.mhc_pre_bwd(sp, N, n, C, L.MHC_BF16, P(dagg), P(dHp), P(dHr), P(X), P(W), None, P(saved),
+                                P(H_pre), P(H_post), P(logits), 20, 1e-6, P(G), P(H_res), P(dX), 0, P(dW), P(da),
+                                P(db), None, None, P(wsp), wp))
+
+    def fused_nog():
+        L.check(lib.mhc_pre_rmsnorm_bwd(sp, N, n, C, L.MHC_BF16, P(dy), P(agg), None, 1e-6, None, P(dHp), P(dHr),
+                                        P(X), P(W), None, P(saved), P(H_pre), P(H_post), P(logits), 20, 1e-6, P(G),
+                                        P(H_res), P(dX), 0, P(dW), P(da), P(db), None, None, P(wsf), wf))
+
+    def composed_nog():
+        L.check(lib.mhc_rmsnorm_bwd(sp, N, C, L.MHC_BF16, P(dy), P(agg), None, 1e-6, P(dagg), 0, None, None, 0))
+        L.check(lib.mhc_pre_bwd(sp, N, n, C, L.MHC_BF16, P(dagg), P(dHp), P(dHr), P(X), P(W), None, P(saved),
+                                P(H_pre), P(H_post), P(logits), 20, 1e-6, P(G), P(H_res), P(dX), 0, P(dW), P(da),
+                                P(db), None, None, P(wsp), wp))
+
+    res = {}
+    for name, fn in (("fused_ms", fused), ("norm_then_pre_bwd_ms", composed), ("fused_no_gain_ms", fused_nog),
+                     ("norm_then_pre_bwd_no_gain_ms", composed_nog)):
+        fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        ev[0].record(stream)
+        for i in range(5):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        res[name] = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(5)]))
+    return res
+
+
 def measure_general_n(N: int, stream, torch) -> dict:
     """One mHC step (pre fwd, post fwd, post bwd, pre bwd with the h_post_bda dX term) at stream counts
     other than 4, on the kernels templated on n: same token count as the headline workload, a width
@@ -495,6 +553,8 @@ def main():
 
     ceilings = measure_ceilings(lib, _lib, sp, stream, torch, N * n * C * 2)
     projection_choice = measure_projection_choice(lib, _lib, sp, stream, torch, cur["X"], Wd, N, n, C)
+    norm_bwd_fusion = measure_norm_bwd_fusion(lib, _lib, sp, stream, torch, N, n, C, cur["X"], Wd, Gd, H_res, agg, g,
+                                              saved, H_pre, H_post, L, dHp, dHr)
     variants = measure_variants(lib, _lib, sp, N, n, C, cur["X"], Gd, H_res, H_post, x, g, out, dX, dHr, dHp, dx,
                                 stream, torch)
     general_n = measure_general_n(N, stream, torch)
@@ -541,6 +601,7 @@ def main():
         "hbm_frac_82C_ledger": (82 * C + 1232) * N / (mhc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "ceilings": ceilings,
         "projection_mfma_vs_fma": projection_choice,
+        "pre_rmsnorm_bwd": norm_bwd_fusion,
         "phases_ms": mean,
         "ms_per_step_incl_layer": step_ms,
         "wall_ms_per_step": wall * 1e3 / args.steps,

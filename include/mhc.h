@@ -391,9 +391,8 @@ mhc_status mhc_pre_rmsnorm_fwd(void *stream, int64_t tokens, int32_t n, int64_t 
  *   mhc_rmsnorm_bwd(dy, agg, gamma, norm_eps, dx = g_fork copy, accumulate_dx =
  *                   g_fork != NULL, dgamma)          -> d_agg (act, rounded)
  *   mhc_pre_bwd(g = d_agg, dH_post, dH_res, X, ...)  -> dX, dW, dalpha, dhbias
- * but for n == 4 one pass over dy, agg and X forms both d_agg and the dH_pre
- * that the pre backward needs, so d_agg is written once and read once instead
- * of written, read and read again.
+ * in one call (the two kernels run in sequence on the caller's stream; one
+ * pass forming d_agg and dH_pre together measured slower on MI355X).
  * dy [tokens][C] (act): gradient of the normed output; agg [tokens][C] (act):
  * the norm's input as the forward stored it; gamma [C] fp32 or NULL (unit
  * gain); g_fork [tokens][C] (act) or NULL: agg's own upstream gradient (the

@@ -867,16 +867,15 @@ mhc_status mhc_pre_rmsnorm_fwd(void *stream, int64_t tokens, int32_t n, int64_t 
 // ------------------------------------------------------------------ fused pre backward with the norm
 namespace {
 struct PreNormBwdWs {
-  size_t pre, dagg, dhpre, norm, total;
+  size_t pre, dagg, norm, total;
 };
 PreNormBwdWs pre_norm_bwd_ws(int64_t tokens, int32_t n, int64_t C, mhc_dtype act, bool dgamma) {
   auto a256 = [](size_t b) { return (b + 255) / 256 * 256; };
   PreNormBwdWs w{};
   w.pre = a256(n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_bwd_ws(n, tokens, C, true));
   w.dagg = a256((size_t)tokens * C * esz(act));
-  w.dhpre = a256((size_t)tokens * 4 * 4);
   w.norm = a256(mhc::rmsnorm_bwd_ws(tokens, C, dgamma));
-  w.total = w.pre + w.dagg + w.dhpre + w.norm;
+  w.total = w.pre + w.dagg + w.norm;
   return w;
 }
 }  // namespace
@@ -942,8 +941,7 @@ mhc_status mhc_pre_rmsnorm_bwd(void *stream, int64_t tokens, int32_t n, int64_t 
   if (v.finish() != MHC_OK) return v.status();
   char *ws = (char *)workspace;
   void *dagg = d_agg_out ? d_agg_out : (void *)(ws + lay.pre);
-  float *dhpre = (float *)(ws + lay.pre + lay.dagg);
-  void *norm_ws = ws + lay.pre + lay.dagg + lay.dhpre;
+  void *norm_ws = ws + lay.pre + lay.dagg;
   mhc::ProjBwdArgs a{};
   a.f32 = act == MHC_F32; a.N = tokens; a.C = C; a.X = X; a.W = W; a.alpha = alpha; a.saved = saved;
   a.H_pre = H_pre; a.H_post = H_post; a.dH_pre = nullptr; a.dH_post = dH_post; a.dL = nullptr;
@@ -951,20 +949,17 @@ mhc_status mhc_pre_rmsnorm_bwd(void *stream, int64_t tokens, int32_t n, int64_t 
   a.accumulate = accumulate_dX != 0; a.dW = dW; a.dalpha = dalpha; a.dhbias = dhbias;
   a.dH_pre_out = nullptr; a.dL_out = nullptr; a.ws = ws;
   a.post_G = post_G; a.post_H_res = post_H_res;
-  if (n == 4) {
-    // the norm's backward and the dH_pre pass in one pass over dy, agg and X
-    mhc::launch_h_aggregate_rmsnorm_bwd(s, act == MHC_F32, tokens, C, dy, agg, gamma, g_fork, X, norm_eps, dagg,
-                                        dhpre, dgamma, norm_ws);
-    a.dH_pre = dhpre;
+  // The norm's backward into d_agg (agg's own gradient as the accumulation base), then the pre
+  // backward on it.  A single pass forming d_agg and dH_pre together (so d_agg is read once less)
+  // measured slower at 16384 x 7168: holding the norm's rows and X's together takes 150-208 VGPRs,
+  // one workgroup per CU, where the separate dH_pre pass keeps several per CU.
+  if (g_fork) copy16(s, g_fork, dagg, tokens * C * (int64_t)esz(act));
+  mhc::launch_rmsnorm_bwd(s, act == MHC_F32, tokens, C, dy, agg, gamma, norm_eps, dagg, g_fork != nullptr, dgamma,
+                          norm_ws);
+  if (n == 4)
     mhc::launch_proj_bwd(s, a);
-  } else {  // other n: the norm's backward, then the pre backward (the same results)
-    if (g_fork) {  // agg's own gradient is the accumulation base
-      copy16(s, g_fork, dagg, tokens * C * (int64_t)esz(act));
-    }
-    mhc::launch_rmsnorm_bwd(s, act == MHC_F32, tokens, C, dy, agg, gamma, norm_eps, dagg, g_fork != nullptr,
-                            dgamma, norm_ws);
+  else
     mhc::glaunch_proj_bwd(s, n, a);
-  }
   return launched("mhc_pre_rmsnorm_bwd");
 }
 

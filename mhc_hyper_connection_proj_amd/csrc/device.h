@@ -67,11 +67,6 @@ template <> struct Io8<bf16_t> {
   static __device__ __forceinline__ void store_pairs(bf16_t *p, const pair_t q[4]) {
     *reinterpret_cast<uint4 *>(p) = make_uint4(q[0], q[1], q[2], q[3]);
   }
-  // the values store() writes, as floats (round to nearest even)
-  static __device__ __forceinline__ void rounded(const float o[8], float v[8]) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (float)(__bf16)o[e];
-  }
   static __device__ __forceinline__ void store(bf16_t *p, const float v[8]) {
     uint4 w;
     w.x = pack_bf16x2(v[0], v[1]);
@@ -119,10 +114,6 @@ template <> struct Io8<float> {
   static __device__ __forceinline__ void store_pairs(float *p, const pair_t q[4]) {
     *reinterpret_cast<float4 *>(p) = make_float4(q[0].x, q[0].y, q[1].x, q[1].y);
     *reinterpret_cast<float4 *>(p + 4) = make_float4(q[2].x, q[2].y, q[3].x, q[3].y);
-  }
-  static __device__ __forceinline__ void rounded(const float o[8], float v[8]) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = o[e];
   }
   static __device__ __forceinline__ void store(float *p, const float v[8]) {
     *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);

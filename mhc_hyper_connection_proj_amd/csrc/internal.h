@@ -88,14 +88,6 @@ size_t rmsnorm_bwd_ws(int64_t N, int64_t C, bool with_dgamma);
 void launch_rmsnorm_bwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *dy, const void *x,
                         const float *gamma, float eps, void *dx, bool accumulate, float *dgamma, void *ws);
 
-// The norm's backward fused in front of the pre backward's dH_pre pass (n = 4):
-// dagg = the norm's input gradient (+ fork, agg's own gradient, if given),
-// rounded to the activation type as stored; dH_pre [N][4] from those values;
-// dgamma (may be NULL) through rmsnorm_bwd_ws(N, C, true) bytes of ws.
-void launch_h_aggregate_rmsnorm_bwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *dy, const void *x,
-                                    const float *gamma, const void *fork, const void *X, float eps, void *dagg,
-                                    float *dH_pre, float *dgamma, void *ws);
-
 // ---- projection (forward)
 size_t proj_fwd_ws(int64_t N, int64_t C, bool f32);
 // Writes H_pre, H_post, logits, saved (may be NULL); if H_res != NULL also
@@ -121,7 +113,7 @@ struct ProjBwdArgs {
   int64_t N, C;
   const void *X;
   const float *W, *alpha, *saved, *H_pre, *H_post;
-  const float *dH_pre;   // NULL in the fused pre backward (computed from g), unless already formed
+  const float *dH_pre;   // NULL in the fused pre backward (computed from g)
   const float *dH_post;
   const float *dL;       // logits gradient, or NULL when dH_res + logits are given
   const float *dH_res, *logits;

@@ -53,7 +53,7 @@ __device__ __forceinline__ void block_sum(float v[NV], float (*red)[NV]) {
 }
 
 // The norm's input gradient of one element, r (gamma dy) + coef x, as one
-// explicit fma: the fused backward and the standalone one round it alike.
+// explicit fma (the rounding does not depend on the compiler's contraction).
 __device__ __forceinline__ float norm_dx(float r, float gdy, float coef, float x) {
   return fmaf(coef, x, r * gdy);
 }
@@ -265,119 +265,6 @@ __global__ __launch_bounds__(512) void rmsnorm_bwd_kernel(
   }
 }
 
-// ============================================================ backward fused with the dH_pre pass
-// One pass per token of the pre backward with the norm's backward in front:
-// the norm's input gradient (the gradient of agg, plus the residual fork's
-// own gradient when given) is formed as rmsnorm_bwd_kernel forms it, rounded
-// to T and stored to dagg, and dH_pre[t][i] = sum_c dagg[t][c] X[t][i][c] is
-// formed from those rounded values as h_aggregate_bwd_kernel forms it: the
-// same thread geometry, the same per-thread orders and the same wave and
-// workgroup reductions, so the results equal the two-kernel composition bit
-// for bit.  TG tokens per workgroup (TG > 1 only with dgamma, whose partial
-// row of the workgroup's tokens goes to part[blockIdx.x][C]).
-template <typename T, int GPT, bool GAMMA, bool FORK, bool DGAMMA>
-__global__ __launch_bounds__(512) void h_aggregate_rmsnorm_bwd_kernel(
-    const T *__restrict__ dy, const T *__restrict__ x, const float *__restrict__ gamma, const T *__restrict__ fork,
-    const T *__restrict__ X, T *__restrict__ dagg, float *__restrict__ dHpre, float *__restrict__ part, int64_t N,
-    int64_t C, float eps, int TG) {
-  using R = typename Io8<T>::raw_t;
-  __shared__ float red[8][2];
-  __shared__ float red4[8][4];
-  const int G = (int)(C / 8);
-  float gv[GPT][8], dg[GPT][8];
-#pragma unroll
-  for (int j = 0; j < GPT; ++j) {
-    const int gc = group_of(j, G);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) { gv[j][e] = 1.f; dg[j][e] = 0.f; }
-    if (GAMMA) load_gamma(gamma, gc, gv[j]);
-  }
-  const int64_t t0 = (int64_t)blockIdx.x * TG;
-  const int64_t t1 = min(t0 + (int64_t)TG, N);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
-  for (int64_t t = t0; t < t1; ++t) {
-    R rx[GPT], rg[GPT], rf[GPT], rX[GPT][4];
-#pragma unroll
-    for (int j = 0; j < GPT; ++j) {
-      const int gc = group_of(j, G);
-      rx[j] = Io8<T>::ld_nt(x + t * C + 8 * gc);
-      rg[j] = Io8<T>::ld_nt(dy + t * C + 8 * gc);
-      if (FORK) rf[j] = Io8<T>::ld_nt(fork + t * C + 8 * gc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rX[j][i] = Io8<T>::ld_nt(X + (t * 4 + i) * C + 8 * gc);
-    }
-    float xv[GPT][8], gy[GPT][8];
-    float sums[2] = {0.f, 0.f};  // sum x^2, sum gamma dy x
-#pragma unroll
-    for (int j = 0; j < GPT; ++j) {
-      Io8<T>::cvt(rx[j], xv[j]);
-      Io8<T>::cvt(rg[j], gy[j]);
-      if ((int)threadIdx.x + j * (int)blockDim.x < G) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          sums[0] = fmaf(xv[j][e], xv[j][e], sums[0]);
-          sums[1] = fmaf(gv[j][e] * gy[j][e], xv[j][e], sums[1]);
-        }
-      }
-    }
-    block_sum<2>(sums, red);
-    const float q = sqrtf(sums[0] / (float)C);
-    const float r = 1.0f / (q + eps);
-    const float coef = q > 0.f ? -sums[1] * r * r / ((float)C * q) : 0.f;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < GPT; ++j) {
-      const int g = threadIdx.x + j * blockDim.x;
-      if (g < G) {
-        float o[8], din[8];
-        if (FORK) Io8<T>::cvt(rf[j], din);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          o[e] = norm_dx(r, gv[j][e] * gy[j][e], coef, xv[j][e]);
-          if (FORK) o[e] += din[e];
-          if (DGAMMA) dg[j][e] = fmaf(gy[j][e], r * xv[j][e], dg[j][e]);
-        }
-        Io8<T>::store(dagg + t * C + 8 * g, o);
-        // the stored (rounded) values, as the dH_pre pass would read them back
-        float dv[8], Xv[4][8];
-        Io8<T>::rounded(o, dv);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Io8<T>::cvt(rX[j][i], Xv[i]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float s2 = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) s2 = fmaf(dv[e], Xv[i][e], s2);
-          acc[i] += s2;
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float s2 = wave_sum(acc[i]);
-      if (lane == 0) red4[wave][i] = s2;
-    }
-    __syncthreads();
-    if (threadIdx.x < 4) {
-      float s2 = 0.f;
-      for (int w = 0; w < nw; ++w) s2 += red4[w][threadIdx.x];
-      dHpre[t * 4 + threadIdx.x] = s2;
-    }
-    __syncthreads();  // red4 is rewritten by the next token
-  }
-  if (DGAMMA) {
-#pragma unroll
-    for (int j = 0; j < GPT; ++j) {
-      const int g = threadIdx.x + j * blockDim.x;
-      if (g < G) {
-        float *p = part + (int64_t)blockIdx.x * C + 8 * g;
-        *reinterpret_cast<float4 *>(p) = make_float4(dg[j][0], dg[j][1], dg[j][2], dg[j][3]);
-        *reinterpret_cast<float4 *>(p + 4) = make_float4(dg[j][4], dg[j][5], dg[j][6], dg[j][7]);
-      }
-    }
-  }
-}
-
 #define MHC_NORM_GPT_DISPATCH(GPT_VAL, ...)                  \
   switch (GPT_VAL) {                                         \
     case 1: { constexpr int GPT = 1; __VA_ARGS__; } break;   \
@@ -430,46 +317,7 @@ void norm_bwd(hipStream_t s, int64_t N, int64_t C, const void *dy, const void *x
   }
 }
 
-template <typename T, bool GAMMA, bool FORK, bool DGAMMA>
-void agg_norm_bwd4(hipStream_t s, int64_t N, int64_t C, const void *dy, const void *x, const float *gamma,
-                   const void *fork, const void *X, float eps, void *dagg, float *dHpre, float *part) {
-  const StreamGeom g = stream_geom(C);
-  const int TG = DGAMMA ? kNormTG : 1;
-  const unsigned blocks = (unsigned)((N + TG - 1) / TG);
-  MHC_NORM_GPT_DISPATCH(g.gpt, hipLaunchKernelGGL((h_aggregate_rmsnorm_bwd_kernel<T, GPT, GAMMA, FORK, DGAMMA>),
-                                                  dim3(blocks), dim3(g.tpb), 0, s, (const T *)dy, (const T *)x,
-                                                  gamma, (const T *)fork, (const T *)X, (T *)dagg, dHpre, part,
-                                                  N, C, eps, TG));
-}
-
-template <typename T, bool GAMMA>
-void agg_norm_bwd(hipStream_t s, int64_t N, int64_t C, const void *dy, const void *x, const float *gamma,
-                  const void *fork, const void *X, float eps, void *dagg, float *dHpre, float *dgamma, void *ws) {
-  float *part = (float *)ws;
-  if (dgamma) {
-    if (fork) agg_norm_bwd4<T, GAMMA, true, true>(s, N, C, dy, x, gamma, fork, X, eps, dagg, dHpre, part);
-    else agg_norm_bwd4<T, GAMMA, false, true>(s, N, C, dy, x, gamma, fork, X, eps, dagg, dHpre, part);
-    const int64_t R = (N + kNormTG - 1) / kNormTG;
-    launch_rows_sum(s, part, R, C, part + R * C, dgamma, false);
-  } else if (fork) {
-    agg_norm_bwd4<T, GAMMA, true, false>(s, N, C, dy, x, gamma, fork, X, eps, dagg, dHpre, nullptr);
-  } else {
-    agg_norm_bwd4<T, GAMMA, false, false>(s, N, C, dy, x, gamma, fork, X, eps, dagg, dHpre, nullptr);
-  }
-}
-
 }  // namespace
-
-void launch_h_aggregate_rmsnorm_bwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *dy, const void *x,
-                                    const float *gamma, const void *fork, const void *X, float eps, void *dagg,
-                                    float *dH_pre, float *dgamma, void *ws) {
-  if (f32)
-    gamma ? agg_norm_bwd<float, true>(s, N, C, dy, x, gamma, fork, X, eps, dagg, dH_pre, dgamma, ws)
-          : agg_norm_bwd<float, false>(s, N, C, dy, x, gamma, fork, X, eps, dagg, dH_pre, dgamma, ws);
-  else
-    gamma ? agg_norm_bwd<bf16_t, true>(s, N, C, dy, x, gamma, fork, X, eps, dagg, dH_pre, dgamma, ws)
-          : agg_norm_bwd<bf16_t, false>(s, N, C, dy, x, gamma, fork, X, eps, dagg, dH_pre, dgamma, ws);
-}
 
 void launch_rmsnorm_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *x, const float *gamma,
                         float eps, void *y) {

@@ -1379,7 +1379,7 @@ void launch_proj_bwd(hipStream_t s, const ProjBwdArgs &a) {
   const int64_t N = a.N, K = 4 * a.C;
   const BwdWs L = bwd_layout(a.ws, N, a.C, a.f32);
   const float *dHpre = a.dH_pre;
-  if (a.g && !a.dH_pre) {  // fused pre backward: dH_pre = g . X per stream
+  if (a.g) {  // fused pre backward: dH_pre = g . X per stream
     launch_h_aggregate_bwd(s, a.f32, N, a.C, a.g, a.X, a.H_pre, nullptr, false, L.dhpre);
     dHpre = L.dhpre;
   }

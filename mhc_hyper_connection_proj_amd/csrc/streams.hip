@@ -112,7 +112,7 @@ __global__ __launch_bounds__(512) void h_aggregate_bwd_kernel(
       for (int i = 0; i < 4; ++i) {
         float s = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s = fmaf(gv[e], xv[i][e], s);  // explicit, as the fused norm backward
+        for (int e = 0; e < 8; ++e) s = fmaf(gv[e], xv[i][e], s);
         acc[i] += s;
       }
       if (WRITE_DX) {

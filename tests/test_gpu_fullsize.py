@@ -262,3 +262,81 @@ def test_rmsnorm_full_size():
     assert_act("agg", rows(f["agg"], S), ref["agg"], w.act)
     assert_rel("H_res", rows(f["H_res"], S), ref["H_res"])
     assert_normed("normed", rows(f["normed"], S), rows(f["agg"], S), ref["agg"], h64(gamma), w.rms_eps, w.act)
+
+
+# ----------------------------------------------------------------- general n at the bench's shapes
+@functools.lru_cache(maxsize=1)
+def _gn_inputs(n: int, C: int, N: int = 16384):
+    """Seeded N(0,1) bf16 residual and upstream gradient, W ~ N(0, 0.02^2): the shapes the bench's general-n
+    step runs (no workload of the pages has n != 4)."""
+    rng = np.random.Generator(np.random.PCG64(9000 + n))
+    X = synth.f32_to_bf16_bits(rng.standard_normal((N, n, C), dtype=np.float32))
+    G = synth.f32_to_bf16_bits(rng.standard_normal((N, n, C), dtype=np.float32))
+    W = (rng.standard_normal((n * C, n * n + 2 * n), dtype=np.float32) * np.float32(0.02)).astype(np.float32)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((N, C), dtype=np.float32))
+    return X, G, W, x
+
+
+@pytest.mark.parametrize("n,C", [(2, 7168), (8, 2048)])
+def test_general_n_full_size(n, C):
+    """The whole step at 16384 tokens, as the bench times it for n != 4, on sampled tokens: pre forward,
+    h_post_bda forward and backward (oracle H_res / H_post), pre backward with the h_post_bda term
+    (oracle forward state on the sample, zero upstream gradients elsewhere)."""
+    N, J, iters, eps = 16384, n * n + 2 * n, 20, 1e-6
+    log(f"general n full size: n={n} N={N} C={C}")
+    X, G, W, x = _gn_inputs(n, C)
+    S = sample_tokens(N, 100 + n)
+    Z = others(N, S, 100 + n)
+    Xd = dev(X)
+    o = B.mhc_pre_fwd(Xd, dev(W), None, None, 1e-6, iters, eps)
+    torch.cuda.synchronize()
+    ref = O.pre_fwd(h64(X[S]), h64(W), None, None, 1e-6, iters, eps)
+    assert_rel("H_pre", rows(o["H_pre"], S), ref["H_pre"])
+    assert_rel("H_post", rows(o["H_post"], S), ref["H_post"])
+    assert_mixed("logits", rows(o["H_res_logits"], S), ref["L"])
+    assert_h_res(rows(o["H_res"], S), rows(o["H_res_logits"], S), ref["H_res"], ref["L"], iters, eps,
+                 alone=B.mhc_sinkhorn_fwd(rows(o["H_res_logits"], S).contiguous(), iters, eps))
+    sv = h64(rows(o["saved"], S))
+    assert_rel("r", sv[:, 0], ref["r"])
+    assert_mixed("z", sv[:, 2:2 + J], ref["z"])
+    assert_act("agg", rows(o["agg"], S), ref["agg"], "bf16")
+    del o
+    # h_post_bda on the oracle's H_res / H_post of the sample (finite stand-ins elsewhere)
+    Hr = np.broadcast_to(np.eye(n, dtype=np.float32) * 0.5 + 0.5 / n, (N, n, n)).copy()
+    Hp = np.ones((N, n), np.float32)
+    Hr[S] = O.round_f64_to_f32(ref["H_res"]); Hp[S] = O.round_f64_to_f32(ref["H_post"])
+    Gs = only(G, S)
+    out = B.mhc_h_post_bda_fwd(Xd, dev(Hr), dev(Hp), dev(x))
+    _, dHr, dHp, dx, _ = B.mhc_h_post_bda_bwd(dev(Gs), Xd, dev(Hr), dev(Hp), dev(x), None, want_dX=False)
+    torch.cuda.synchronize()
+    XS, GS, xS = h64(X[S]), h64(Gs[S]), h64(x[S])
+    assert_act("out", rows(out, S), O.h_post_bda_fwd(XS, h64(Hr[S]), h64(Hp[S]), xS), "bf16")
+    _, odHr, odHp, odx, _ = O.h_post_bda_bwd(GS, XS, h64(Hr[S]), h64(Hp[S]), xS)
+    assert_mixed("dH_res", rows(dHr, S), odHr)
+    assert_mixed("dH_post", rows(dHp, S), odHp)
+    assert_act("dx", rows(dx, S), odx, "bf16")
+    for nm, t in (("dH_res", dHr), ("dH_post", dHp), ("dx", dx)):
+        assert not h64(rows(t, Z)).any(), f"{nm}: nonzero on tokens with zero upstream gradient"
+    del out
+    # the pre backward as the bench runs it: the h_post_bda term formed from G (all tokens)
+    saved = np.zeros((N, B.saved_stride(n)), np.float32); saved[:, 0] = 1.0; saved[:, 1] = 1.0
+    saved[S, 0] = ref["r"]; saved[S, 1] = ref["q"]; saved[S, 2:2 + J] = ref["z"]
+    H_pre = np.full((N, n), 1.0 / n, np.float32); H_pre[S] = ref["H_pre"]
+    H_post = np.ones((N, n), np.float32); H_post[S] = ref["H_post"]
+    L = np.zeros((N, n, n), np.float32); L[S] = ref["L"]
+    rng = np.random.default_rng(200 + n)
+    g = only(x, S)
+    dHq = np.zeros((N, n), np.float32); dHq[S] = rng.standard_normal((len(S), n))
+    dHR = np.zeros((N, n, n), np.float32); dHR[S] = rng.standard_normal((len(S), n, n))
+    ob = B.mhc_pre_bwd(dev(g), dev(dHq), dev(dHR), Xd, dev(W), dev(saved), dev(H_pre), dev(H_post), dev(L),
+                       iters=iters, eps=eps, post_G=dev(G), post_H_res=dev(Hr))
+    torch.cuda.synchronize()
+    rb = O.pre_bwd(h64(g[S]), h64(dHq[S]), h64(dHR[S]), XS, h64(W), None, None, 1e-6, iters, eps)
+    base_S = O.stream_mix_bwd(h64(G[S]), XS, h64(Hr[S]))[0]
+    assert_act("dX", rows(ob["dX"], S), base_S + rb["dX"], "bf16")
+    base_Z = O.stream_mix_bwd(h64(G[Z]), h64(X[Z]), h64(Hr[Z]))[0]
+    assert_act("dX (post term only)", rows(ob["dX"], Z), base_Z, "bf16")
+    aW, aa, ab = pre_bwd_abs_parts(h64(g[S]), h64(dHq[S]), h64(dHR[S]), XS, h64(W), None, None, 1e-6, iters, eps)
+    assert_tokensum("dW", ob["dW"], rb["dW"], aW, depth=sum_depth("proj", N, C, S=S, n=n))
+    assert_tokensum("dalpha", ob["dalpha"], rb["dalpha"], aa, depth=sum_depth("param", N, S=len(S), n=n))
+    assert_tokensum("dhbias", ob["dhbias"], rb["dhbias"], ab, depth=sum_depth("param", N, S=len(S), n=n))

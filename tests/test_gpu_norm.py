@@ -128,7 +128,7 @@ def test_rmsnorm_deterministic_bitwise():
 @pytest.mark.parametrize("gamma_on,fork_on,post", [(True, True, True), (False, False, False), (True, False, False),
                                                    (False, True, True)])
 def test_pre_rmsnorm_bwd(n, act, N, C, gamma_on, fork_on, post):
-    """The fused backward equals mhc_rmsnorm_bwd followed by mhc_pre_bwd bit for bit (the pre backward is
+    """mhc_pre_rmsnorm_bwd equals mhc_rmsnorm_bwd followed by mhc_pre_bwd bit for bit (the pre backward is
     held to the oracle on seeded inputs by the pre pass tests); its d_agg and dgamma against the oracle.
     Forward state, agg and H_res of the h_post_bda term come from the oracle (rounded to storage)."""
     log(f"pre rmsnorm bwd n={n} act={act} N={N} C={C} gamma={gamma_on} fork={fork_on} post={post}")
