@@ -399,7 +399,8 @@ mhc_status mhc_proj_rms_h_fma(void *stream, int64_t tokens, int32_t n, int64_t C
 // ------------------------------------------------------------------ projection bwd
 size_t mhc_proj_rms_h_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
   if (tokens <= 0 || tokens > mhc::kMaxTokens || n < 1 || n > mhc::kMaxN || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
-  return n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_bwd_ws(n, tokens, C, false);
+  return n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32)
+                : mhc::gproj_bwd_ws(n, tokens, C, false, act == MHC_F32);
 }
 
 mhc_status mhc_proj_rms_h_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
@@ -435,7 +436,9 @@ mhc_status mhc_proj_rms_h_bwd(void *stream, int64_t tokens, int32_t n, int64_t C
   v.out(dW, K * J * 4, "dW", true);
   v.out(dalpha, 12, "dalpha", true);
   v.out(dhbias, J * 4, "dhbias", true);
-  v.workspace(workspace, workspace_bytes, n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_bwd_ws(n, tokens, C, false));
+  v.workspace(workspace, workspace_bytes,
+              n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32)
+                     : mhc::gproj_bwd_ws(n, tokens, C, false, act == MHC_F32));
   if (v.finish() != MHC_OK) return v.status();
   mhc::ProjBwdArgs a{};
   a.f32 = act == MHC_F32; a.N = tokens; a.C = C; a.X = X; a.W = W; a.alpha = alpha; a.saved = saved;
@@ -872,7 +875,8 @@ struct PreNormBwdWs {
 PreNormBwdWs pre_norm_bwd_ws(int64_t tokens, int32_t n, int64_t C, mhc_dtype act, bool dgamma) {
   auto a256 = [](size_t b) { return (b + 255) / 256 * 256; };
   PreNormBwdWs w{};
-  w.pre = a256(n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_bwd_ws(n, tokens, C, true));
+  w.pre = a256(n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32)
+                      : mhc::gproj_bwd_ws(n, tokens, C, true, act == MHC_F32));
   w.dagg = a256((size_t)tokens * C * esz(act));
   w.norm = a256(mhc::rmsnorm_bwd_ws(tokens, C, dgamma));
   w.total = w.pre + w.dagg + w.norm;
@@ -965,7 +969,8 @@ mhc_status mhc_pre_rmsnorm_bwd(void *stream, int64_t tokens, int32_t n, int64_t 
 
 size_t mhc_pre_bwd_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
   if (tokens <= 0 || tokens > mhc::kMaxTokens || n < 1 || n > mhc::kMaxN || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
-  return n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_bwd_ws(n, tokens, C, true);
+  return n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32)
+                : mhc::gproj_bwd_ws(n, tokens, C, true, act == MHC_F32);
 }
 
 mhc_status mhc_pre_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
@@ -1012,7 +1017,9 @@ mhc_status mhc_pre_bwd(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_d
   v.out(dhbias, J * 4, "dhbias", true);
   v.out(dH_pre_out, tokens * n * 4, "dH_pre_out", true);
   v.out(dlogits_out, tokens * n * n * 4, "dlogits_out", true);
-  v.workspace(workspace, workspace_bytes, n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_bwd_ws(n, tokens, C, true));
+  v.workspace(workspace, workspace_bytes,
+              n == 4 ? mhc::proj_bwd_ws(tokens, C, act == MHC_F32)
+                     : mhc::gproj_bwd_ws(n, tokens, C, true, act == MHC_F32));
   if (v.finish() != MHC_OK) return v.status();
   mhc::ProjBwdArgs a{};
   a.f32 = act == MHC_F32; a.N = tokens; a.C = C; a.X = X; a.W = W; a.alpha = alpha; a.saved = saved;

@@ -14,10 +14,14 @@
 //    a per-token finalize sums the slices in order and applies RMS, gains,
 //    sigmoid and Sinkhorn;
 //  * projection backward: a per-token kernel (sigmoid / Sinkhorn backward,
-//    dp = r alpha dzh and the RMS coefficient); in the fused pre backward a
-//    per-token pass forming the aggregate and h_post_bda residual terms in
-//    an fp32 workspace; then a VALU kernel with one thread per k that owns
-//    W's row k and its dW row, walking a token block;
+//    dp = r alpha dzh and the RMS coefficient), then dX and dW.  bf16: one
+//    MFMA kernel on tiles of 32-128 channels of all n streams (so the
+//    h_post_bda gradient G, which every output stream mixes, is loaded once),
+//    dp W^T on fp32 MFMA with W's rows in registers and x^T dp on bf16 MFMA
+//    with dp split exactly into three bf16 terms, the aggregate and
+//    h_post_bda terms formed in its epilogue.  fp32: a per-token pass forming
+//    those terms in an fp32 workspace, then a VALU kernel with one thread per
+//    k that owns W's row k and its dW row, walking a token block;
 //  * Sinkhorn: one n x n matrix per thread; the backward replays the
 //    forward from checkpoints spaced ~sqrt(2 iters) half-steps apart, so it
 //    needs no storage beyond registers;
@@ -42,6 +46,13 @@ template <int NS> struct Dim {
   static constexpr int J = NS * NS + 2 * NS;   // controller outputs
   static constexpr int JT = (J + 31) / 32;     // 32-column MFMA tiles
   static constexpr int PS = J + 1;             // partial row: x @ W, then sum x^2
+  // Backward record of a token: dp[0..J), zeros up to RC, c_rms at RC, row
+  // stride RS (a multiple of 4 floats).  The fp32 MFMA of the dX kernel
+  // takes dp as two halves of JC values (lane half h holds j = h JC + c),
+  // JC a multiple of 4 so each half is read as whole 16-byte words.
+  static constexpr int JC = ((J + 1) / 2 + 3) / 4 * 4;
+  static constexpr int RC = 2 * JC;
+  static constexpr int RS = (RC + 1 + 3) / 4 * 4;
 };
 
 constexpr int kGSplitK = 8;   // k slices of the forward projection
@@ -965,8 +976,9 @@ __global__ __launch_bounds__(64) void gproj_finalize_kernel(const float *__restr
 }
 
 // ------------------------------------------------------------------ projection backward
-// Per token (one thread): dzh from the saved forward state; rec[t] =
-// {dp[0..J) = r alpha dzh, c_rms = -r sum_j dz_j z_j / (K q) (0 if q == 0)};
+// Per token (one thread): dzh from the saved forward state; rec[t] (stride
+// RS) = {dp[0..J) = r alpha dzh, zeros up to RC, c_rms = -r sum_j dz_j z_j /
+// (K q) (0 if q == 0) at RC};
 // prm[t] = {dzh[0..J) (dhbias terms), sum_seg dzh z (dalpha terms, 3)}.
 // dH_res and the logits (Sinkhorn backward) replace dL when dL == NULL.
 template <int NS, bool STORED>
@@ -1019,10 +1031,12 @@ __global__ __launch_bounds__(64) void gproj_bwd_token_kernel(
     const float dz = al[sg] * dzh;
     S += dz * z;
     da[sg] += dzh * z;
-    rec[t * (J + 1) + j] = r * dz;
+    rec[t * Dim<NS>::RS + j] = r * dz;
     prm[t * (J + 3) + j] = dzh;
   }
-  rec[t * (J + 1) + J] = q > 0.f ? -S * r / ((float)K * q) : 0.f;
+#pragma unroll
+  for (int j = J; j < Dim<NS>::RC; ++j) rec[t * Dim<NS>::RS + j] = 0.f;
+  rec[t * Dim<NS>::RS + Dim<NS>::RC] = q > 0.f ? -S * r / ((float)K * q) : 0.f;
   prm[t * (J + 3) + J] = da[0];
   prm[t * (J + 3) + J + 1] = da[1];
   prm[t * (J + 3) + J + 2] = da[2];
@@ -1104,8 +1118,10 @@ __global__ __launch_bounds__(256) void gproj_bwd_dx_kernel(
   for (int64_t ts = t0; ts < t1; ts += RT) {
     const int nt = (int)min((int64_t)RT, t1 - ts);
     __syncthreads();
-    for (int idx = threadIdx.x; idx < nt * (J + 1); idx += blockDim.x)
-      srec[idx / (J + 1)][idx % (J + 1)] = rec[(ts + idx / (J + 1)) * (J + 1) + idx % (J + 1)];
+    for (int idx = threadIdx.x; idx < nt * (J + 1); idx += blockDim.x) {
+      const int u = idx / (J + 1), j = idx % (J + 1);
+      srec[u][j] = rec[(ts + u) * Dim<NS>::RS + (j < J ? j : Dim<NS>::RC)];
+    }
     __syncthreads();
     if (kv) {
       for (int u0 = 0; u0 < nt; u0 += UB) {
@@ -1137,6 +1153,403 @@ __global__ __launch_bounds__(256) void gproj_bwd_dx_kernel(
   if (DW && kv) {
 #pragma unroll
     for (int j = 0; j < J; ++j) dwpart[((int64_t)blockIdx.y * K + k) * J + j] = dw[j];
+  }
+}
+
+// ------------------------------------------------------------------ MFMA dX / dW kernel (bf16 activations)
+// The same dX and dW as the VALU kernel above, with the aggregate and
+// h_post_bda residual terms formed in place (no fp32 term workspace):
+//   dX[t][j][c] = (dX_in) + dp[t] . W[k] + c_rms[t] x[t][j][c] + H_pre[t][j] g[t][c]
+//                 + sum_i H_res[t][j][i] G[t][i][c],      k = j C + c
+//   dW[k][.]   += x[t][k] dp[t][.]
+// Workgroup = 8 waves on one token block and one tile of CW channels of all
+// NS streams (so the G tile, needed by every output stream, is loaded once),
+// walked in 32-token sub-tiles through a 3-stage LDS ring:
+//  * waves 4..7 (loaders) fill each stage with global_load_lds_dwordx4 two
+//    sub-tiles ahead: the X tile, the G tile, the g tile and the sub-tile's
+//    32 backward records; then dW = x^T dp on bf16 MFMA (32x32x16), A = 16
+//    tokens of a k column of X (exact in bf16), B = dp split exactly into
+//    three bf16 terms (8 + 8 + 8 significant bits);
+//  * waves 0..3 own 32-k column blocks: dp W^T on fp32 MFMA (32x32x2), W's
+//    rows held in registers (a lane half holds j = h JC + c), the 32 x 32
+//    accumulator transposed through a private LDS area, then the epilogue
+//    with 16-byte row pieces and 16-byte stores; H_pre, H_res and dX_in rows
+//    are prefetched one sub-tile ahead.
+// fp32 MFMA keeps W's rows in registers: at n = 8 (J = 80) 40 values per
+// lane per block, where the six three-term bf16 products would need 240.
+// Synchronisation as in the n = 4 kernel: loaders issue no other global
+// memory operation in the loop (exact vmcnt), dX waves never issue DMA, one
+// barrier per sub-tile.
+__device__ __forceinline__ void gdma16(const void *g, void *lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+template <int n>
+__device__ __forceinline__ void gwait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// vmcnt <= n for a wave-uniform n (at most 16); otherwise waits for all.
+__device__ __forceinline__ void gwait_vmcnt_le(int n) {
+  switch (n) {
+    case 1: gwait_vmcnt<1>(); break;
+    case 2: gwait_vmcnt<2>(); break;
+    case 3: gwait_vmcnt<3>(); break;
+    case 4: gwait_vmcnt<4>(); break;
+    case 5: gwait_vmcnt<5>(); break;
+    case 6: gwait_vmcnt<6>(); break;
+    case 7: gwait_vmcnt<7>(); break;
+    case 8: gwait_vmcnt<8>(); break;
+    case 9: gwait_vmcnt<9>(); break;
+    case 10: gwait_vmcnt<10>(); break;
+    case 11: gwait_vmcnt<11>(); break;
+    case 12: gwait_vmcnt<12>(); break;
+    case 13: gwait_vmcnt<13>(); break;
+    case 14: gwait_vmcnt<14>(); break;
+    case 15: gwait_vmcnt<15>(); break;
+    case 16: gwait_vmcnt<16>(); break;
+    default: gwait_vmcnt<0>(); break;
+  }
+}
+__device__ __forceinline__ void glds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void gwave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+typedef __attribute__((ext_vector_type(4))) unsigned int gu32x4;
+
+// 32-channel blocks per stream in a channel tile of the MFMA dX kernel: as
+// wide as the 3-stage ring fits in LDS with W's rows in registers.
+constexpr int gmf_cb(int n) { return n <= 2 ? 4 : n == 3 ? 2 : 1; }
+constexpr int64_t gmf_cw(int n) { return 32 * gmf_cb(n); }
+
+template <int NS> struct GMf {
+  static constexpr int J = Dim<NS>::J, JT = Dim<NS>::JT, JC = Dim<NS>::JC, RC = Dim<NS>::RC, RS = Dim<NS>::RS;
+  static constexpr int CB = gmf_cb(NS);                     // 32-channel blocks per stream in a tile
+  static constexpr int CW = 32 * CB;                        // channels of a tile
+  static constexpr int PW = CW / 8;                         // 16-byte pieces of a tile row
+  static constexpr int NB = NS * CB;                        // 32-k column blocks of a tile
+  static constexpr int MB = (NB + 3) / 4;                   // blocks per wave (round robin over 4 waves)
+  static constexpr int XB = NS * 32 * CW * 2;               // bytes of the X tile (and of the G tile)
+  static constexpr int GB = 32 * CW * 2;                    // bytes of the g tile
+  static constexpr int RB = (RS * 32 * 4 + 1023) / 1024 * 1024;  // record tile, whole 1 KB copies
+  static constexpr int AS = 40;                             // row stride (floats) of a wave's accumulator tile
+  static constexpr int ACC = 4 * 32 * AS * 4;               // the four dX waves' accumulator tiles
+  static_assert(NB >= 4, "every dX wave owns a block (its first block waits for the prefetched rows)");
+  static_assert(3 * (2 * XB + GB + RB) + ACC <= 160 * 1024, "LDS of one workgroup");
+  // Byte offset of 16-byte piece `slot` of row (stream j, token t) in an X
+  // or G tile ([stream][token][CW], j = 0 for the g tile).  Tokens t and
+  // t + 8, which one column read takes together, land on different banks:
+  // rows of 64 bytes are permuted (t ^ bit 3 of t), wider rows have their
+  // pieces rotated by half a row.  The map is its own inverse in t.
+  static __device__ __forceinline__ int off(int j, int t, int slot) {
+    const int b3 = (t >> 3) & 1;
+    if (PW == 4) return ((j * 32 + (t ^ b3)) * PW + slot) * 16;
+    return ((j * 32 + t) * PW + (slot ^ (b3 * (PW / 2)))) * 16;
+  }
+};
+
+// flags: bit 0 g given, bit 1 h_post_bda term (G, H_res), bit 2 accumulate into dX
+template <int NS, bool DW>
+__global__ __launch_bounds__(512) void gproj_bwd_mfma_kernel(
+    const bf16_t *__restrict__ X, const float *__restrict__ W, const float *__restrict__ rec,
+    const float *__restrict__ Hpre, const bf16_t *__restrict__ gr, const bf16_t *__restrict__ Gp,
+    const float *__restrict__ Hres, bf16_t *__restrict__ dX, float *__restrict__ dwpart, int64_t N, int64_t C,
+    int64_t tbsz, int64_t ntb, int flags) {
+  using M = GMf<NS>;
+  constexpr int J = M::J, JT = M::JT, JC = M::JC, RC = M::RC, RS = M::RS, CB = M::CB, CW = M::CW, PW = M::PW;
+  constexpr int NB = M::NB, MB = M::MB;
+  extern __shared__ __attribute__((aligned(16))) char glds[];
+  const bool has_g = flags & 1, post = (flags >> 1) & 1, accum = (flags >> 2) & 1;
+  const int64_t K = (int64_t)NS * C;
+  const int64_t nct = (C + CW - 1) / CW;
+  // XCD-contiguous tile order (as the n = 4 kernel): XCD b % 8 walks tiles
+  // [x per, (x + 1) per) in order, neighbouring channel tiles of one block
+  const int64_t T = nct * ntb, per = (T + 7) / 8;
+  const int64_t tile = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (tile >= T) return;  // grid padding to a multiple of 8 (whole workgroup)
+  // token blocks from the last down: the dH_pre pass before read X and g in
+  // token order, so the first blocks here may still sit in the Infinity Cache
+  const int64_t tb = ntb - 1 - tile / nct;
+  const int64_t c0 = (tile % nct) * CW;
+  const int64_t t_begin = min(N, tb * tbsz);
+  const int64_t t_end = min(N, t_begin + tbsz);
+  const int nsub = (int)((t_end - t_begin + 31) / 32);
+
+  // stage layout: X tile, G tile (post), g tile (has_g), records
+  const int oG = M::XB, og = oG + (post ? M::XB : 0), oR = og + (has_g ? M::GB : 0), SB = oR + M::RB;
+  const int QX = M::XB / 1024, QG = post ? QX : 0, Qg = has_g ? M::GB / 1024 : 0, QR = M::RB / 1024;
+  const int Q = QX + QG + Qg + QR;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 31, h = lane >> 5;
+  const bool loader = wave >= 4;
+  const int w4 = wave & 3;
+
+  // ---- loaders: copy q of a stage (lane -> 16 bytes)
+  auto issue = [&](int i) {
+    char *st = glds + (i % 3) * SB;
+    const int64_t t0 = t_begin + 32 * (int64_t)i;
+    for (int q = w4; q < Q; q += 4) {
+      if (q < QX + QG + Qg) {
+        const bool is_g = q >= QX + QG;
+        const int qq = is_g ? q - QX - QG : q < QX ? q : q - QX;
+        const int p16 = qq * 64 + lane;  // 16-byte piece index inside the tile
+        const int row = p16 / PW, ps = p16 % PW;
+        const int j = row / 32, tp = row % 32;
+        const int b3 = (tp >> 3) & 1;
+        const int t = PW == 4 ? tp ^ b3 : tp;
+        const int slot = PW == 4 ? ps : ps ^ (b3 * (PW / 2));
+        const int64_t tt = min(t0 + t, N - 1);  // rows past N re-read row N-1 (never stored, dW-masked)
+        const int64_t ch = c0 + 8 * slot < C ? c0 + 8 * slot : c0;  // pieces past C: a real channel
+        const bf16_t *src = is_g ? gr + tt * C + ch : (q < QX ? X : Gp) + (tt * NS + j) * C + ch;
+        char *dst = st + (is_g ? og : q < QX ? 0 : oG) + qq * 1024;
+        gdma16(src, dst);
+      } else {
+        // records are contiguous; the workspace holds them up to the 32-token padding plus 1 KB
+        const int qq = q - QX - QG - Qg;
+        gdma16(reinterpret_cast<const char *>(rec + t0 * RS) + qq * 1024 + lane * 16, st + oR + qq * 1024);
+      }
+    }
+  };
+
+  // ---- dX waves: blocks b = w4 + 4 bi; stream j = b / CB, channels c0 + 32 (b % CB) + [0, 32)
+  float wf[MB][JC];
+  if (!loader) {
+#pragma unroll
+    for (int bi = 0; bi < MB; ++bi) {
+      const int b = w4 + 4 * bi;
+      const int64_t c = c0 + 32 * (b % CB) + col;
+      const bool ok = b < NB && c < C;
+      const float *wr = W + ((int64_t)(b / CB) * C + c) * J;
+#pragma unroll
+      for (int e = 0; e < JC; ++e) {
+        const int jj = h * JC + e;
+        wf[bi][e] = ok && jj < J ? wr[jj] : 0.f;
+      }
+    }
+  }
+  // prefetched per sub-tile: rows er and er + 16 of each block
+  const int er = lane >> 2, pk = lane & 3;
+  float hp[MB][2], hr[MB][2][NS];
+  gu32x4 din[MB][2];
+  auto prefetch = [&](int i) {
+    const int64_t t0 = t_begin + 32 * (int64_t)i;
+#pragma unroll
+    for (int bi = 0; bi < MB; ++bi) {
+      const int b = w4 + 4 * bi, j = b / CB;
+      const int64_t ch = c0 + 32 * (b % CB) + 8 * pk;
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int64_t t = t0 + er + 16 * rr;
+        const bool v = b < NB && t < N;
+        hp[bi][rr] = v && has_g ? Hpre[t * NS + j] : 0.f;
+#pragma unroll
+        for (int e = 0; e < NS; ++e) hr[bi][rr][e] = v && post ? Hres[(t * NS + j) * NS + e] : 0.f;
+        din[bi][rr] = v && accum && ch < C ? *reinterpret_cast<const gu32x4 *>(dX + (t * NS + j) * C + ch)
+                                           : gu32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+
+  gf32x16 accW[MB][JT];
+#pragma unroll
+  for (int bi = 0; bi < MB; ++bi)
+#pragma unroll
+    for (int u = 0; u < JT; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) accW[bi][u][r] = 0.f;
+
+  if (loader) {
+    const int nq = (Q - w4 + 3) / 4;  // this wave's copies per stage
+    if (nsub > 0) issue(0);
+    if (nsub > 1) issue(1);
+    for (int i = 0; i < nsub; ++i) {
+      if (i + 1 < nsub) gwait_vmcnt_le(nq); else gwait_vmcnt<0>();
+      glds_barrier();
+      if (i + 2 < nsub) issue(i + 2);
+      if (DW) {
+        const char *st = glds + (i % 3) * SB;
+        const float *rt = reinterpret_cast<const float *>(st + oR);
+        const int64_t t0 = t_begin + 32 * (int64_t)i;
+        // per 16-token half s: B = the three bf16 terms of dp[token][j],
+        // j = 32 u + col, for the 8 tokens 16 s + 8 h + p of the lane (tokens
+        // past N give 0); A = x[token][kk] of the same tokens for each block
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          gu32x4 bfr[JT][3];
+#pragma unroll
+          for (int u = 0; u < JT; ++u) {
+            uint32_t tw[3][4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              float v2[2];
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                const int tok = 16 * s + 8 * h + 2 * p + e;
+                const int jj = 32 * u + col;
+                v2[e] = (jj < J && t0 + tok < N) ? rt[tok * RS + jj] : 0.f;
+              }
+              float th[2], tm[2], tl[2];
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                th[e] = (float)(__bf16)v2[e];
+                const float r1 = v2[e] - th[e];
+                tm[e] = (float)(__bf16)r1;
+                tl[e] = r1 - tm[e];
+              }
+              tw[0][p] = pack_bf16x2(th[0], th[1]);
+              tw[1][p] = pack_bf16x2(tm[0], tm[1]);
+              tw[2][p] = pack_bf16x2(tl[0], tl[1]);
+            }
+#pragma unroll
+            for (int m = 0; m < 3; ++m) bfr[u][m] = gu32x4{tw[m][0], tw[m][1], tw[m][2], tw[m][3]};
+          }
+#pragma unroll
+          for (int bi = 0; bi < MB; ++bi) {
+            const int b = w4 + 4 * bi;
+            if (b >= NB) continue;
+            const int j = b / CB, kk = 32 * (b % CB) + col;  // column of the tile
+            uint32_t w4v[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const int tr0 = 16 * s + 8 * h + 2 * p;
+              const uint32_t lo = *reinterpret_cast<const uint16_t *>(st + M::off(j, tr0, kk >> 3) + 2 * (kk & 7));
+              const uint32_t hi =
+                  *reinterpret_cast<const uint16_t *>(st + M::off(j, tr0 + 1, kk >> 3) + 2 * (kk & 7));
+              w4v[p] = lo | (hi << 16);
+            }
+            const gu32x4 xa = gu32x4{w4v[0], w4v[1], w4v[2], w4v[3]};
+#pragma unroll
+            for (int m = 0; m < 3; ++m)
+#pragma unroll
+              for (int u = 0; u < JT; ++u)
+                accW[bi][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(gbf16x8, xa),
+                                                                      __builtin_bit_cast(gbf16x8, bfr[u][m]),
+                                                                      accW[bi][u], 0, 0, 0);
+          }
+        }
+      }
+    }
+  } else {
+    float *acc_t = reinterpret_cast<float *>(glds + 3 * SB) + w4 * 32 * M::AS;
+    gwait_vmcnt<0>();  // W in registers: only the prefetches are pending inside the loop
+    prefetch(0);
+    for (int i = 0; i < nsub; ++i) {
+      glds_barrier();
+      const char *st = glds + (i % 3) * SB;
+      const float *rt = reinterpret_cast<const float *>(st + oR);
+      const int64_t t0 = t_begin + 32 * (int64_t)i;
+#pragma unroll
+      for (int bi = 0; bi < MB; ++bi) {
+        const int b = w4 + 4 * bi;
+        if (b >= NB) continue;
+        const int j = b / CB, cb = b % CB;
+        // dp W^T: A = dp[token col][h JC + e], B = W[k col][h JC + e]
+        gf32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        const float *ar = rt + col * RS + h * JC;
+#pragma unroll
+        for (int e4 = 0; e4 < JC / 4; ++e4) {
+          const float4 a4 = *reinterpret_cast<const float4 *>(ar + 4 * e4);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.x, wf[bi][4 * e4], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.y, wf[bi][4 * e4 + 1], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.z, wf[bi][4 * e4 + 2], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a4.w, wf[bi][4 * e4 + 3], acc, 0, 0, 0);
+        }
+        if (bi == 0) {
+          // the prefetched rows, waited for once, after the first MFMAs
+          __builtin_amdgcn_sched_barrier(0);
+          gwait_vmcnt<0>();
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_t[(8 * (r >> 2) + 4 * h + (r & 3)) * M::AS + col] = acc[r];
+        gwave_lds_sync();
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          const int row = er + 16 * rr;
+          const int64_t t = t0 + row;
+          const int64_t ch = c0 + 32 * cb + 8 * pk;
+          if (!(t < N && ch < C)) continue;
+          const int slot = 4 * cb + pk;
+          const float4 a0 = *reinterpret_cast<const float4 *>(&acc_t[row * M::AS + 8 * pk]);
+          const float4 a1 = *reinterpret_cast<const float4 *>(&acc_t[row * M::AS + 8 * pk + 4]);
+          float o[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+          const float crms = rt[row * RS + RC];
+          const gu32x4 xv = *reinterpret_cast<const gu32x4 *>(st + M::off(j, row, slot));
+          const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            o[2 * p] += crms * bf16_lo(xw[p]);
+            o[2 * p + 1] += crms * bf16_hi(xw[p]);
+          }
+          if (has_g) {
+            const gu32x4 gv = *reinterpret_cast<const gu32x4 *>(st + og + M::off(0, row, slot));
+            const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+            const float hv = hp[bi][rr];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              o[2 * p] += hv * bf16_lo(gw[p]);
+              o[2 * p + 1] += hv * bf16_hi(gw[p]);
+            }
+          }
+          if (post) {  // sum_i H_res[t][j][i] G[t][i], i in order
+            float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < NS; ++e) {
+              const gu32x4 v = *reinterpret_cast<const gu32x4 *>(st + oG + M::off(e, row, slot));
+              const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+              const float hv = hr[bi][rr][e];
+#pragma unroll
+              for (int p = 0; p < 4; ++p) {
+                s8[2 * p] += hv * bf16_lo(vw[p]);
+                s8[2 * p + 1] += hv * bf16_hi(vw[p]);
+              }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] += s8[e];
+          }
+          if (accum) {
+            const uint32_t dw4[4] = {din[bi][rr].x, din[bi][rr].y, din[bi][rr].z, din[bi][rr].w};
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              o[2 * p] += bf16_lo(dw4[p]);
+              o[2 * p + 1] += bf16_hi(dw4[p]);
+            }
+          }
+          uint4 ow;
+          ow.x = pack_bf16x2(o[0], o[1]);
+          ow.y = pack_bf16x2(o[2], o[3]);
+          ow.z = pack_bf16x2(o[4], o[5]);
+          ow.w = pack_bf16x2(o[6], o[7]);
+          *reinterpret_cast<uint4 *>(dX + (t * NS + j) * C + ch) = ow;
+        }
+        gwave_lds_sync();  // the accumulator tile's reads precede the next block's writes
+      }
+      if (i + 1 < nsub) prefetch(i + 1);
+    }
+  }
+  if (DW && loader) {
+#pragma unroll
+    for (int bi = 0; bi < MB; ++bi) {
+      const int b = w4 + 4 * bi;
+      if (b >= NB) continue;
+      const int64_t kb = (int64_t)(b / CB) * C + c0 + 32 * (b % CB);  // k of the block's first column
+      const int64_t cb0 = c0 + 32 * (b % CB);
+#pragma unroll
+      for (int u = 0; u < JT; ++u) {
+        const int jj = 32 * u + col;
+        if (jj >= J) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int e = 8 * (r >> 2) + 4 * h + (r & 3);
+          if (cb0 + e < C) dwpart[(tb * K + kb + e) * J + jj] = accW[bi][u][r];
+        }
+      }
+    }
   }
 }
 
@@ -1174,19 +1587,38 @@ struct GBwdLay {
   size_t rec, prm, dw, dhrow, term, dl, total;
 };
 
-// terms: room for the fp32 residual-gradient terms (the fused pre backward).
-GBwdLay gbwd_layout(int64_t N, int64_t C, int n, bool terms) {
+// Backward record stride (floats) for a run-time n: Dim<n>::RS.
+static int grec_stride(int n) {
+  const int J = n * n + 2 * n, JC = ((J + 1) / 2 + 3) / 4 * 4;
+  return (2 * JC + 1 + 3) / 4 * 4;
+}
+
+// f32: the VALU dX kernel, with room for the fp32 residual-gradient terms
+// (terms: the fused pre backward).  bf16: the MFMA dX kernel, whose records
+// are copied in whole 32-token sub-tiles (padded, plus the last 1 KB copy's
+// overhang) and which reads g and G itself.
+GBwdLay gbwd_layout(int64_t N, int64_t C, int n, bool terms, bool f32) {
   const int64_t J = (int64_t)n * n + 2 * n, K = (int64_t)n * C;
   GBwdLay L;
-  // token blocks of >= 64 tokens, at most kGMaxTB, and dW partials within kGDwBudget
   const int64_t by_budget = std::max<int64_t>(1, kGDwBudget / (K * J * 4));
-  L.ntb = std::min<int64_t>(std::min<int64_t>(kGMaxTB, by_budget), std::max<int64_t>(1, (N + 63) / 64));
-  L.tb = (N + L.ntb - 1) / L.ntb;
-  L.rec = al256((size_t)N * (J + 1) * 4);
+  if (f32) {
+    // token blocks of >= 64 tokens, at most kGMaxTB, and dW partials within kGDwBudget
+    L.ntb = std::min<int64_t>(std::min<int64_t>(kGMaxTB, by_budget), std::max<int64_t>(1, (N + 63) / 64));
+    L.tb = (N + L.ntb - 1) / L.ntb;
+  } else {
+    // about 512 workgroups (two rounds of one per CU) over the channel tiles,
+    // token blocks in whole 32-token sub-tiles
+    const int64_t nct = (C + gmf_cw(n) - 1) / gmf_cw(n);
+    L.ntb = std::min<int64_t>(std::min<int64_t>(std::max<int64_t>(1, 512 / nct), by_budget),
+                              std::max<int64_t>(1, (N + 31) / 32));
+    L.tb = ((N + L.ntb - 1) / L.ntb + 31) / 32 * 32;
+  }
+  const int RS = grec_stride(n);
+  L.rec = f32 ? al256((size_t)N * RS * 4) : al256((size_t)(N + 31) / 32 * 32 * RS * 4 + 1024);
   L.prm = al256((size_t)N * (J + 3) * 4);
   L.dw = al256((size_t)L.ntb * K * J * 4);
   L.dhrow = al256((size_t)N * n * 4);
-  L.term = terms ? al256((size_t)N * K * 4) : 0;
+  L.term = terms && f32 ? al256((size_t)N * K * 4) : 0;
   L.dl = al256((size_t)N * n * n * 4);  // the logits' gradient when the row-per-lane Sinkhorn backward forms it
   L.total = L.rec + L.prm + L.dw + L.dhrow + L.term + L.dl;
   return L;
@@ -1386,7 +1818,9 @@ void glaunch_proj_fwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, cons
                                         iters, eps));
 }
 
-size_t gproj_bwd_ws(int n, int64_t N, int64_t C, bool terms) { return gbwd_layout(N, C, n, terms).total; }
+size_t gproj_bwd_ws(int n, int64_t N, int64_t C, bool terms, bool f32) {
+  return gbwd_layout(N, C, n, terms, f32).total;
+}
 
 template <typename T>
 static void gdx(hipStream_t s, int n, const ProjBwdArgs &a, const GBwdLay &L, const float *rec, const float *term,
@@ -1403,6 +1837,25 @@ static void gdx(hipStream_t s, int n, const ProjBwdArgs &a, const GBwdLay &L, co
                                           a.accumulate))
 }
 
+template <int NS>
+static void gdx_mfma(hipStream_t s, const ProjBwdArgs &a, const GBwdLay &L, const float *rec, float *dwp) {
+  using M = GMf<NS>;
+  const int64_t nct = (a.C + M::CW - 1) / M::CW, T = nct * L.ntb;
+  const unsigned blocks = (unsigned)((T + 7) / 8 * 8);
+  const bool has_g = a.g != nullptr, post = a.post_G != nullptr;
+  const int flags = (has_g ? 1 : 0) | (post ? 2 : 0) | (a.accumulate ? 4 : 0);
+  const size_t stage = (size_t)M::XB * (post ? 2 : 1) + (has_g ? M::GB : 0) + M::RB;
+  const size_t lds = 3 * stage + M::ACC;
+  if (a.dW)
+    hipLaunchKernelGGL((gproj_bwd_mfma_kernel<NS, true>), dim3(blocks), dim3(512), lds, s, (const bf16_t *)a.X, a.W,
+                       rec, a.H_pre, (const bf16_t *)a.g, (const bf16_t *)a.post_G, a.post_H_res, (bf16_t *)a.dX,
+                       dwp, a.N, a.C, L.tb, L.ntb, flags);
+  else
+    hipLaunchKernelGGL((gproj_bwd_mfma_kernel<NS, false>), dim3(blocks), dim3(512), lds, s, (const bf16_t *)a.X, a.W,
+                       rec, a.H_pre, (const bf16_t *)a.g, (const bf16_t *)a.post_G, a.post_H_res, (bf16_t *)a.dX,
+                       dwp, a.N, a.C, L.tb, L.ntb, flags);
+}
+
 template <typename T>
 static void gterms(hipStream_t s, int n, const ProjBwdArgs &a, float *term) {
   MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gpre_terms_kernel<T, NS>), dim3((unsigned)a.N), dim3(gtpb(a.C)), 0, s,
@@ -1411,7 +1864,7 @@ static void gterms(hipStream_t s, int n, const ProjBwdArgs &a, float *term) {
 
 void glaunch_proj_bwd(hipStream_t s, int n, const ProjBwdArgs &a) {
   const bool terms = a.g != nullptr || a.post_G != nullptr;
-  const GBwdLay L = gbwd_layout(a.N, a.C, n, terms);
+  const GBwdLay L = gbwd_layout(a.N, a.C, n, terms, a.f32);
   const int64_t J = (int64_t)n * n + 2 * n, K = (int64_t)n * a.C;
   char *base = (char *)a.ws;
   float *rec = (float *)base;
@@ -1448,16 +1901,12 @@ void glaunch_proj_bwd(hipStream_t s, int n, const ProjBwdArgs &a) {
     MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_bwd_token_kernel<NS, false>), dim3(tb), dim3(g.threads), 0, s,
                                           a.N, K, a.alpha, a.saved, saved_stride(n), a.H_pre, a.H_post, dHpre,
                                           a.dH_post, dLin, a.dH_res, a.logits, a.iters, a.eps, rec, prm, dLout))
-  if (terms) {
-    if (a.f32)
-      gterms<float>(s, n, a, term);
-    else
-      gterms<bf16_t>(s, n, a, term);
-  }
-  if (a.f32)
+  if (a.f32) {
+    if (terms) gterms<float>(s, n, a, term);
     gdx<float>(s, n, a, L, rec, term, dwp);
-  else
-    gdx<bf16_t>(s, n, a, L, rec, term, dwp);
+  } else {
+    MHC_NS_DISPATCH(n, gdx_mfma<NS>(s, a, L, rec, dwp));
+  }
   if (a.dW)
     hipLaunchKernelGGL(gdw_reduce_kernel, dim3((unsigned)((K * J + 255) / 256)), dim3(256), 0, s, dwp, a.dW, L.ntb,
                        K * J);

@@ -166,7 +166,7 @@ void glaunch_proj_fwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, cons
                       const float *alpha, const float *hbias, float rms_eps, float *H_pre, float *H_post,
                       float *logits, float *saved, float *H_res, int iters, float eps, void *ws);
 // terms: the fused pre backward (aggregate and h_post_bda residual terms formed first)
-size_t gproj_bwd_ws(int n, int64_t N, int64_t C, bool terms);
+size_t gproj_bwd_ws(int n, int64_t N, int64_t C, bool terms, bool f32);
 void glaunch_proj_bwd(hipStream_t s, int n, const ProjBwdArgs &a);
 
 }  // namespace mhc

@@ -127,10 +127,17 @@ def dxdw_token_block(N: int, C: int, n: int = 4, act: str = "bf16") -> int:
     """Tokens per block of the projection backward's dX / dW kernel (the partition of the token sum
     into per-block dW partials), chosen as the library chooses it."""
     K = n * C
-    if n != 4:  # blocks of >= 64 tokens, at most 32 of them, dW partials within 512 MiB
+    if n != 4:
         J = n * n + 2 * n
-        ntb = min(32, max(1, (512 << 20) // (K * J * 4)), max(1, _cdiv(N, 64)))
-        return _cdiv(N, ntb)
+        by_budget = max(1, (512 << 20) // (K * J * 4))  # dW partials within 512 MiB
+        if act == "f32":  # blocks of >= 64 tokens, at most 32 of them
+            ntb = min(32, by_budget, max(1, _cdiv(N, 64)))
+            return _cdiv(N, ntb)
+        # bf16: about 512 workgroups over the channel tiles (32, 64 or 128 channels of all n streams),
+        # blocks in whole 32-token sub-tiles
+        cw = 32 * (4 if n <= 2 else 2 if n == 3 else 1)
+        ntb = min(max(1, 512 // _cdiv(C, cw)), by_budget, max(1, _cdiv(N, 32)))
+        return _rup(_cdiv(N, ntb), 32)
     if act == "f32":  # about 2048 workgroups of 1024 k
         return _rup(max(32, _cdiv(N * _cdiv(K, 1024), 2048)), 32)
     nkt = _cdiv(K, 256)  # bf16: whole rounds of 256 workgroups, then the fewest blocks
@@ -151,9 +158,9 @@ def sum_depth(path: str, N: int, C: int = 0, S: int | None = None, n: int = 4, a
     rounds at most once per nonzero term it meets.  The leading 1 is the product forming the term.
 
       proj   dW, per token block of dxdw_token_block tokens, then the block partials summed in
-             order.  n = 4, bf16: six MFMA accumulations per 32-token sub-tile (three bf16 terms of
-             dp, two 16-token halves) and at most 15 roundings inside one MFMA.  n = 4, fp32: one fma
-             per token.  Other n: one add per token.
+             order.  bf16 (any n): six MFMA accumulations per 32-token sub-tile (three bf16 terms of
+             dp, two 16-token halves) and at most 15 roundings inside one MFMA.  fp32: one fma (n = 4)
+             or one add (other n) per token.
       param  dalpha, dhbias.  n = 4: <= 4 adds over a lane's owned columns, a 64-lane DPP tree (6),
              four waves (2), one thread's strided walk over 64-token block partials (every 32nd
              block), a 32-way tree (5).  Other n: a per-token row (<= n^2 adds in the RES segment),
@@ -171,7 +178,7 @@ def sum_depth(path: str, N: int, C: int = 0, S: int | None = None, n: int = 4, a
     if path == "proj":
         tb = dxdw_token_block(N, C, n, act)
         nb = _cdiv(N, tb)
-        bf = n == 4 and act == "bf16"
+        bf = act == "bf16"
         if idx is not None:  # per block: its nonzero tokens (fp32) or 32-token sub-tiles (bf16 MFMA)
             blocks = idx // tb
             units = np.unique(idx // 32) // (tb // 32) if bf else blocks
