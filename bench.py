@@ -211,6 +211,55 @@ def measure_norm_bwd_fusion(lib, L, sp, stream, torch, N, n, C, X, W, G, H_res, 
     return res
 
 
+def measure_reread_chunks(lib, L, sp, stream, torch, Xcopies, W, G, bufs, N, n, C, rms_eps, iters, eps) -> dict:
+    """The pre forward and the pre backward read X twice (the projection then the aggregate; the
+    dH_pre pass then dX/dW).  Run on token chunks small enough for the 256 MB Infinity Cache, the
+    second read of a chunk's X (and g) can come from there: each pass is called once per chunk
+    (pointers offset into the same tensors; dW, dalpha, dhbias overwritten per chunk, which does
+    not change the work), against one call over all tokens.  Mean of 4 event-timed passes after one
+    warm-up, the two residual copies alternated between passes."""
+    from mhc_hyper_connection_proj_amd._lib import MHC_BF16
+    P = lambda t: t.data_ptr()
+    b = bufs
+    ws_f = lib.mhc_pre_fwd_workspace_size(N, n, C, MHC_BF16)
+    ws_b = lib.mhc_pre_bwd_workspace_size(N, n, C, MHC_BF16)
+    dev = G.device
+    wsf = torch.empty(max(ws_f, 16), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(max(ws_b, 16), dtype=torch.uint8, device=dev)
+    xs, hs = n * C * 2, C * 2  # bytes per token: residual rows, one row
+
+    def fwd(X, t0, m):
+        L.check(lib.mhc_pre_fwd(sp, m, n, C, MHC_BF16, P(X) + t0 * xs, P(W), None, None, rms_eps, iters, eps,
+                                P(b["H_pre"]) + t0 * 16, P(b["H_post"]) + t0 * 16, P(b["H_res"]) + t0 * 64,
+                                P(b["L"]) + t0 * 64, P(b["saved"]) + t0 * 128, P(b["agg"]) + t0 * hs, P(wsf), ws_f))
+
+    def bwd(X, t0, m):
+        L.check(lib.mhc_pre_bwd(sp, m, n, C, MHC_BF16, P(b["g"]) + t0 * hs, P(b["dHp"]) + t0 * 16,
+                                P(b["dHr"]) + t0 * 64, P(X) + t0 * xs, P(W), None, P(b["saved"]) + t0 * 128,
+                                P(b["H_pre"]) + t0 * 16, P(b["H_post"]) + t0 * 16, P(b["L"]) + t0 * 64, iters, eps,
+                                P(G) + t0 * xs, P(b["H_res"]) + t0 * 64, P(b["dX"]) + t0 * xs, 0, P(b["dW"]),
+                                P(b["da"]), P(b["db"]), None, None, P(wsb), ws_b))
+
+    def timed(fn, chunk, reps=4):
+        def one(k):
+            X = Xcopies[k % 2]
+            for t0 in range(0, N, chunk):
+                fn(X, t0, min(chunk, N - t0))
+        one(1)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for k in range(reps):
+            one(k)
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([ev[k].elapsed_time(ev[k + 1]) for k in range(reps)]))
+
+    chunks = [N, 4096, 2048, 1024]
+    return {"chunk_tokens": chunks, "pre_fwd_ms": [timed(fwd, c) for c in chunks],
+            "pre_bwd_ms": [timed(bwd, c) for c in chunks]}
+
+
 def measure_general_n(N: int, stream, torch) -> dict:
     """One mHC step (pre fwd, post fwd, post bwd, pre bwd with the h_post_bda dX term) at stream counts
     other than 4, on the kernels templated on n: same token count as the headline workload, a width
@@ -557,6 +606,10 @@ def main():
                                               saved, H_pre, H_post, L, dHp, dHr)
     variants = measure_variants(lib, _lib, sp, N, n, C, cur["X"], Gd, H_res, H_post, x, g, out, dX, dHr, dHp, dx,
                                 stream, torch)
+    reread = measure_reread_chunks(lib, _lib, sp, stream, torch, Xcopies, Wd, Gd,
+                                   {"H_pre": H_pre, "H_post": H_post, "H_res": H_res, "L": L, "saved": saved,
+                                    "agg": agg, "g": g, "dHp": dHp, "dHr": dHr, "dX": dX, "dW": dW, "da": da,
+                                    "db": db}, N, n, C, w.rms_eps, w.iters, w.eps)
     general_n = measure_general_n(N, stream, torch)
     configs = measure_configs(stream, torch)
 
@@ -613,6 +666,7 @@ def main():
                                     "traffic": p_traffic, "algorithmic_bytes_per_launch": p_bytes,
                                     "avg_launch_ms": mean["post_bwd"]},
         "variants": variants,
+        "reread_chunks": reread,
         "general_n": general_n,
         "configs": configs,
         "cpu_baseline": None,

@@ -180,7 +180,8 @@ bool zero_act(hipStream_t s, void *p, int64_t n, mhc_dtype act) {
 
 // ---- fused pre forward: checks and launches shared by mhc_pre_fwd and mhc_pre_fwd_noalloc
 size_t pre_fwd_ws(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
-  return n == 4 ? mhc::proj_fwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_fwd_ws(n, tokens);
+  return n == 4 ? mhc::proj_fwd_ws(tokens, C, act == MHC_F32)
+                : mhc::gproj_fwd_ws(n, tokens, C, act == MHC_F32);
 }
 
 // Shapes, scalars and every tensor argument (no workspace).  False when a check failed or
@@ -337,7 +338,8 @@ mhc_status mhc_bandwidth_probe(void *stream, int32_t kind, const void *src, void
 // ------------------------------------------------------------------ projection fwd
 size_t mhc_proj_rms_h_workspace_size(int64_t tokens, int32_t n, int64_t C, mhc_dtype act) {
   if (tokens <= 0 || tokens > mhc::kMaxTokens || n < 1 || n > mhc::kMaxN || C <= 0 || C % 8 || C > mhc::kMaxC) return 0;
-  return n == 4 ? mhc::proj_fwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_fwd_ws(n, tokens);
+  return n == 4 ? mhc::proj_fwd_ws(tokens, C, act == MHC_F32)
+                : mhc::gproj_fwd_ws(n, tokens, C, act == MHC_F32);
 }
 
 mhc_status mhc_proj_rms_h(void *stream, int64_t tokens, int32_t n, int64_t C, mhc_dtype act,
@@ -359,7 +361,9 @@ mhc_status mhc_proj_rms_h(void *stream, int64_t tokens, int32_t n, int64_t C, mh
   v.out(H_post, tokens * n * 4, "H_post");
   v.out(H_res_logits, tokens * n * n * 4, "H_res_logits");
   v.out(saved, tokens * mhc::saved_stride(n) * 4, "saved", true);
-  v.workspace(workspace, workspace_bytes, n == 4 ? mhc::proj_fwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_fwd_ws(n, tokens));
+  v.workspace(workspace, workspace_bytes,
+              n == 4 ? mhc::proj_fwd_ws(tokens, C, act == MHC_F32)
+                     : mhc::gproj_fwd_ws(n, tokens, C, act == MHC_F32));
   if (v.finish() != MHC_OK) return v.status();
   if (n == 4)
     mhc::launch_proj_fwd((hipStream_t)stream, act == MHC_F32, tokens, C, X, W, alpha, hbias, rms_eps,
@@ -851,7 +855,9 @@ mhc_status mhc_pre_rmsnorm_fwd(void *stream, int64_t tokens, int32_t n, int64_t 
   v.out(saved, tokens * mhc::saved_stride(n) * 4, "saved", true);
   v.out(agg, tokens * C * esz(act), "agg");
   v.out(normed, tokens * C * esz(act), "normed");
-  v.workspace(workspace, workspace_bytes, n == 4 ? mhc::proj_fwd_ws(tokens, C, act == MHC_F32) : mhc::gproj_fwd_ws(n, tokens));
+  v.workspace(workspace, workspace_bytes,
+              n == 4 ? mhc::proj_fwd_ws(tokens, C, act == MHC_F32)
+                     : mhc::gproj_fwd_ws(n, tokens, C, act == MHC_F32));
   if (v.finish() != MHC_OK) return v.status();
   const hipStream_t s = (hipStream_t)stream;
   if (n == 4) {

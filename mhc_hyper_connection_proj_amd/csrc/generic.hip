@@ -79,6 +79,48 @@ template <> __device__ __forceinline__ void st_one<bf16_t>(bf16_t *p, float v) {
 
 __device__ __forceinline__ float sigm(float v) { return 1.0f / (1.0f + __expf(-v)); }
 
+// LDS DMA rings (the MFMA kernels below): global_load_lds_dwordx4 moves 16
+// bytes per lane to consecutive LDS addresses; each wave waits for its own
+// copies with s_waitcnt vmcnt, then a bare barrier publishes the stage.
+__device__ __forceinline__ void gdma16(const void *g, void *lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+template <int n>
+__device__ __forceinline__ void gwait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// vmcnt <= n for a wave-uniform n (at most 16); otherwise waits for all.
+__device__ __forceinline__ void gwait_vmcnt_le(int n) {
+  switch (n) {
+    case 1: gwait_vmcnt<1>(); break;
+    case 2: gwait_vmcnt<2>(); break;
+    case 3: gwait_vmcnt<3>(); break;
+    case 4: gwait_vmcnt<4>(); break;
+    case 5: gwait_vmcnt<5>(); break;
+    case 6: gwait_vmcnt<6>(); break;
+    case 7: gwait_vmcnt<7>(); break;
+    case 8: gwait_vmcnt<8>(); break;
+    case 9: gwait_vmcnt<9>(); break;
+    case 10: gwait_vmcnt<10>(); break;
+    case 11: gwait_vmcnt<11>(); break;
+    case 12: gwait_vmcnt<12>(); break;
+    case 13: gwait_vmcnt<13>(); break;
+    case 14: gwait_vmcnt<14>(); break;
+    case 15: gwait_vmcnt<15>(); break;
+    case 16: gwait_vmcnt<16>(); break;
+    default: gwait_vmcnt<0>(); break;
+  }
+}
+__device__ __forceinline__ void glds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void gwave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+typedef __attribute__((ext_vector_type(4))) unsigned int gu32x4;
+
 // Sum of NV per-thread values over a workgroup of at most 512 threads; the
 // totals go to every thread.  Fixed order: wave DPP tree, then waves in order.
 template <int NV>
@@ -796,34 +838,103 @@ __global__ __launch_bounds__(256) void gproj_partial_kernel(const T *__restrict_
   if (h == 0 && tvalid) part[((int64_t)slice * N + trow) * PS + J] = ss + ss_other;
 }
 
-// bf16 activations: the same blocking on the bf16 MFMA (32x32x16).  Each W
+// bf16 activations: the same split-K on the bf16 MFMA (32x32x16).  Each W
 // value is split exactly into three bf16 terms (hi = W rounded to bf16,
 // mid = the rest rounded, lo = what remains: 8 + 8 + 8 significant bits
 // cover fp32's 24), and bf16 x times a bf16 term is exact in the fp32
-// accumulator, so the three products give x @ W to fp32 accumulation.  The
-// chunk's terms sit in LDS as [term][column][k]; a lane's A operand is the
-// 8 x values it already holds (k = 32h + 8q .. +8 for MFMA q) and its B
-// operand the same 8 k of its column, read as one 16-byte LDS access (the k
-// order inside an MFMA is free as long as A and B agree).
+// accumulator, so the three products give x @ W to fp32 accumulation.
+// gpack_w_kernel splits W once per call into Wp[chunk][term][column][8
+// pieces of 8 k] (64 k per chunk, 32 JT columns, zero past K and J), piece p
+// of column j stored in slot p ^ (j & 7), so a chunk is one contiguous block
+// of 12 JT KB that a workgroup copies verbatim into LDS.  A workgroup is 8
+// waves x 32 tokens on one k slice; each 64-k chunk of W (shared) and of
+// every wave's X tile (4 KB, 8 lanes per 128-byte row segment, piece p of
+// row r in slot p ^ (r & 7)) goes through an LDS ring filled by
+// global_load_lds_dwordx4 (3 stages where they fit in LDS, else 2).  A
+// lane's A operand is the 8 x values of its token at k = 32h + 8q and its B
+// operand the same 8 k of its column (the k order inside an MFMA is free as
+// long as A and B agree).  Each chunk is summed from zero and then added to
+// the running sum, as in the fp32 kernel.
 typedef __attribute__((ext_vector_type(8))) __bf16 gbf16x8;
 
+template <int NS> struct GPj {
+  static constexpr int JT = Dim<NS>::JT;
+  static constexpr int WB = 3 * 32 * JT * 128;          // bytes of one packed 64-k W chunk
+  static constexpr int XT = 32 * 128;                   // bytes of one wave's X tile
+  static constexpr int SB = WB + 8 * XT;                // bytes of one stage
+  static constexpr int STAGES = 3 * SB <= 160 * 1024 ? 3 : 2;
+};
+
 template <int NS>
-__global__ __launch_bounds__(256) void gproj_partial_bf16_kernel(const bf16_t *__restrict__ X,
-                                                                const float *__restrict__ W,
-                                                                float *__restrict__ part, int64_t N, int64_t K) {
-  constexpr int J = Dim<NS>::J, JT = Dim<NS>::JT, PS = Dim<NS>::PS;
-  constexpr int SWB = 64 + 8;  // LDS row stride of a term's [column][k] rows (bf16; 144 bytes)
-  __shared__ __align__(16) uint16_t sWb[3][32 * JT][SWB];
+__global__ __launch_bounds__(256) void gpack_w_kernel(const float *__restrict__ W, bf16_t *__restrict__ Wp,
+                                                     int64_t K) {
+  constexpr int J = Dim<NS>::J, JT = Dim<NS>::JT;
+  const int64_t nch = (K + 63) / 64;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (chunk, column, piece)
+  if (i >= nch * 32 * JT * 8) return;
+  const int p = (int)(i & 7), j = (int)((i >> 3) % (32 * JT));
+  const int64_t c = (i >> 3) / (32 * JT);
+  float hi[8], mid[8], lo[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int64_t k = c * 64 + 8 * p + e;
+    const float w = (k < K && j < J) ? W[k * J + j] : 0.f;
+    hi[e] = (float)(__bf16)w;
+    const float r1 = w - hi[e];
+    mid[e] = (float)(__bf16)r1;
+    lo[e] = r1 - mid[e];
+  }
+  const int slot = p ^ (j & 7);
+  const float *terms[3] = {hi, mid, lo};
+#pragma unroll
+  for (int m = 0; m < 3; ++m) {
+    const float *v = terms[m];
+    uint4 w4;
+    w4.x = pack_bf16x2(v[0], v[1]);
+    w4.y = pack_bf16x2(v[2], v[3]);
+    w4.z = pack_bf16x2(v[4], v[5]);
+    w4.w = pack_bf16x2(v[6], v[7]);
+    *reinterpret_cast<uint4 *>(Wp + ((c * 3 + m) * 32 * JT + j) * 64 + 8 * slot) = w4;
+  }
+}
+
+constexpr int kGDmaTok = 8 * kGTok;  // tokens per bf16 forward workgroup
+
+template <int NS>
+__global__ __launch_bounds__(512) void gproj_partial_dma_kernel(const bf16_t *__restrict__ X,
+                                                               const bf16_t *__restrict__ Wp,
+                                                               float *__restrict__ part, int64_t N, int64_t K) {
+  using G = GPj<NS>;
+  constexpr int J = Dim<NS>::J, JT = G::JT, PS = Dim<NS>::PS, STG = G::STAGES;
+  extern __shared__ __attribute__((aligned(16))) char gpl[];
   const int slice = blockIdx.x % kGSplitK;
   const int64_t tb = blockIdx.x / kGSplitK;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int row = lane & 31, h = lane >> 5;
   const int64_t nch = (K + 63) / 64;
   const int64_t cps = (nch + kGSplitK - 1) / kGSplitK;
-  const int64_t c_begin = slice * cps;
-  const int64_t c_end = min(nch, c_begin + cps);
-  const int64_t trow = tb * kGTokWG + wave * kGTok + row;
-  const bool tvalid = trow < N;
+  const int64_t c_begin = min(nch, slice * cps);
+  const int nc = (int)(min(nch, c_begin + cps) - c_begin);
+  const int64_t tw = tb * kGDmaTok + kGTok * wave;  // this wave's first token
+  constexpr int QW = G::WB / 1024;                  // 1 KB copies of a W chunk, over the 8 waves
+  const int nq = (QW - wave + 7) / 8 + 4;           // this wave's copies per chunk
+
+  auto issue = [&](int i) {
+    char *st = gpl + (i % STG) * G::SB;
+    const int64_t c = c_begin + i;
+    const char *wsrc = reinterpret_cast<const char *>(Wp) + c * G::WB;
+    for (int q = wave; q < QW; q += 8) gdma16(wsrc + q * 1024 + lane * 16, st + q * 1024);
+    char *xs = st + G::WB + wave * G::XT;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rr = 8 * q + (lane >> 3);   // row within the wave's 32
+      const int p = (lane & 7) ^ (rr & 7);  // global 8-k piece for this slot
+      const int64_t t = min(tw + rr, N - 1);  // rows past N re-read row N-1 (never stored)
+      const int64_t k = c * 64 + 8 * p < K ? c * 64 + 8 * p : c * 64;  // past K: a real k (W is 0 there)
+      gdma16(X + t * K + k, xs + q * 1024);
+    }
+  };
 
   gf32x16 outer[JT];
 #pragma unroll
@@ -831,63 +942,34 @@ __global__ __launch_bounds__(256) void gproj_partial_bf16_kernel(const bf16_t *_
 #pragma unroll
     for (int r = 0; r < 16; ++r) outer[u][r] = 0.f;
   float ss = 0.f;
-
-  // W is taken as (k, k + 1) pairs of one column, so each term's pair is one
-  // 32-bit LDS store; the next chunk's pairs and x groups are loaded while
-  // the current chunk is multiplied.
-  constexpr int NPAIR = 32 * 32 * JT;            // k pairs x columns per chunk
-  constexpr int PPT = (NPAIR + 255) / 256;       // pairs per thread
-  using R = Io8<bf16_t>::raw_t;
-  float wlo[PPT], whi[PPT];
-  R xr[4];
-  bool xok[4];
-  auto fetch = [&](int64_t c) {
-    const int64_t kc = c * 64;
-#pragma unroll
-    for (int q = 0; q < PPT; ++q) {
-      const int idx = threadIdx.x + q * 256;
-      const int kp = idx / (32 * JT), j = idx % (32 * JT);
-      const int64_t k = kc + 2 * kp;
-      const bool ok = idx < NPAIR && j < J;
-      wlo[q] = (ok && k < K) ? W[k * J + j] : 0.f;
-      whi[q] = (ok && k + 1 < K) ? W[(k + 1) * J + j] : 0.f;
-    }
-    const int64_t k0 = kc + 32 * h;
+  if (nc > 0) issue(0);
+  if (STG == 3 && nc > 1) issue(1);
+  for (int i = 0; i < nc; ++i) {
+    // this wave's copies of chunk i are complete once at most those of chunk i + 1 remain
+    if (STG == 3 && i + 1 < nc) gwait_vmcnt_le(nq); else gwait_vmcnt<0>();
+    glds_barrier();
+    if (i + STG - 1 < nc) issue(i + STG - 1);  // that slot was last read in iteration i - 1
+    const char *st = gpl + (i % STG) * G::SB;
+    const char *xs = st + G::WB + wave * G::XT;
+    const int64_t k0 = (c_begin + i) * 64;
+    gu32x4 a[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      xok[q] = tvalid && k0 + 8 * q < K;
-      xr[q] = xok[q] ? Io8<bf16_t>::ld_nt(X + trow * K + k0 + 8 * q) : R{0u, 0u, 0u, 0u};
+      const int p = 4 * h + q;
+      a[q] = *reinterpret_cast<const gu32x4 *>(xs + (row * 8 + (p ^ (row & 7))) * 16);
     }
-  };
-  if (c_begin < c_end) fetch(c_begin);
-  for (int64_t c = c_begin; c < c_end; ++c) {
-    __syncthreads();  // the previous chunk's reads of sWb are done
-#pragma unroll
-    for (int q = 0; q < PPT; ++q) {
-      const int idx = threadIdx.x + q * 256;
-      if (idx < NPAIR) {
-        const int kp = idx / (32 * JT), j = idx % (32 * JT);
-        const float a0 = wlo[q], a1 = whi[q];
-        const float h0 = (float)(__bf16)a0, h1 = (float)(__bf16)a1;
-        const float r0 = a0 - h0, r1 = a1 - h1;
-        const float m0 = (float)(__bf16)r0, m1 = (float)(__bf16)r1;
-        *reinterpret_cast<uint32_t *>(&sWb[0][j][2 * kp]) = pack_bf16x2(h0, h1);
-        *reinterpret_cast<uint32_t *>(&sWb[1][j][2 * kp]) = pack_bf16x2(m0, m1);
-        *reinterpret_cast<uint32_t *>(&sWb[2][j][2 * kp]) = pack_bf16x2(r0 - m0, r1 - m1);
-      }
-    }
-    R xa[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) xa[q] = xr[q];
-    __syncthreads();
-    if (c + 1 < c_end) fetch(c + 1);
     float sq = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      float v[8];
-      Io8<bf16_t>::cvt(xa[q], v);
+      if (k0 + 32 * h + 8 * q < K) {
+        const uint32_t w4[4] = {a[q].x, a[q].y, a[q].z, a[q].w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sq = fmaf(v[e], v[e], sq);
+        for (int e = 0; e < 4; ++e) {
+          const float v0 = bf16_lo(w4[e]), v1 = bf16_hi(w4[e]);
+          sq = fmaf(v0, v0, sq);
+          sq = fmaf(v1, v1, sq);
+        }
+      }
     }
     ss += sq;
 #pragma unroll
@@ -897,31 +979,35 @@ __global__ __launch_bounds__(256) void gproj_partial_bf16_kernel(const bf16_t *_
       for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const gbf16x8 a = __builtin_bit_cast(gbf16x8, xa[q]);
+        const int p = 4 * h + q;
 #pragma unroll
-        for (int term = 0; term < 3; ++term) {
-          const uint4 bw = *reinterpret_cast<const uint4 *>(&sWb[term][32 * u + row][32 * h + 8 * q]);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(gbf16x8, bw), acc, 0, 0, 0);
+        for (int m = 0; m < 3; ++m) {
+          const gu32x4 bw =
+              *reinterpret_cast<const gu32x4 *>(st + ((m * 32 * JT + 32 * u + row) * 8 + (p ^ (row & 7))) * 16);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(gbf16x8, a[q]),
+                                                        __builtin_bit_cast(gbf16x8, bw), acc, 0, 0, 0);
         }
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) outer[u][r] += acc[r];
     }
   }
-  // accumulator layout as in the fp32 kernel above
+  // accumulator layout of a 32x32 MFMA: lane (col, h), register r holds row
+  // 8*(r/4) + 4*h + (r%4), column col.  Sum of squares: the two k halves of a
+  // token's row sit on lanes row and row + 32.
 #pragma unroll
   for (int u = 0; u < JT; ++u) {
     const int col = 32 * u + row;
     if (col < J) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t t = tb * kGTokWG + wave * kGTok + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int64_t t = tw + 8 * (r >> 2) + 4 * h + (r & 3);
         if (t < N) part[((int64_t)slice * N + t) * PS + col] = outer[u][r];
       }
     }
   }
   const float ss_other = __shfl_xor(ss, 32);
-  if (h == 0 && tvalid) part[((int64_t)slice * N + trow) * PS + J] = ss + ss_other;
+  if (h == 0 && tw + row < N) part[((int64_t)slice * N + tw + row) * PS + J] = ss + ss_other;
 }
 
 // One thread per token: slices summed in order, then RMS, gains, sigmoid;
@@ -1180,44 +1266,6 @@ __global__ __launch_bounds__(256) void gproj_bwd_dx_kernel(
 // Synchronisation as in the n = 4 kernel: loaders issue no other global
 // memory operation in the loop (exact vmcnt), dX waves never issue DMA, one
 // barrier per sub-tile.
-__device__ __forceinline__ void gdma16(const void *g, void *lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
-}
-template <int n>
-__device__ __forceinline__ void gwait_vmcnt() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-// vmcnt <= n for a wave-uniform n (at most 16); otherwise waits for all.
-__device__ __forceinline__ void gwait_vmcnt_le(int n) {
-  switch (n) {
-    case 1: gwait_vmcnt<1>(); break;
-    case 2: gwait_vmcnt<2>(); break;
-    case 3: gwait_vmcnt<3>(); break;
-    case 4: gwait_vmcnt<4>(); break;
-    case 5: gwait_vmcnt<5>(); break;
-    case 6: gwait_vmcnt<6>(); break;
-    case 7: gwait_vmcnt<7>(); break;
-    case 8: gwait_vmcnt<8>(); break;
-    case 9: gwait_vmcnt<9>(); break;
-    case 10: gwait_vmcnt<10>(); break;
-    case 11: gwait_vmcnt<11>(); break;
-    case 12: gwait_vmcnt<12>(); break;
-    case 13: gwait_vmcnt<13>(); break;
-    case 14: gwait_vmcnt<14>(); break;
-    case 15: gwait_vmcnt<15>(); break;
-    case 16: gwait_vmcnt<16>(); break;
-    default: gwait_vmcnt<0>(); break;
-  }
-}
-__device__ __forceinline__ void glds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-__device__ __forceinline__ void gwave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-typedef __attribute__((ext_vector_type(4))) unsigned int gu32x4;
 
 // 32-channel blocks per stream in a channel tile of the MFMA dX kernel: as
 // wide as the 3-stage ring fits in LDS with W's rows in registers.
@@ -1795,23 +1843,33 @@ void glaunch_stream_distribute_bwd(hipStream_t s, bool f32, int n, int64_t N, in
                                   dx, nullptr);
 }
 
-size_t gproj_fwd_ws(int n, int64_t N) {
-  const int64_t J = (int64_t)n * n + 2 * n;
-  return al256((size_t)kGSplitK * N * (J + 1) * 4);
+// split-K partials [8][N][J + 1], then (bf16) the packed W chunks
+size_t gproj_fwd_ws(int n, int64_t N, int64_t C, bool f32) {
+  const int64_t J = (int64_t)n * n + 2 * n, JT = (J + 31) / 32, nch = ((int64_t)n * C + 63) / 64;
+  return al256((size_t)kGSplitK * N * (J + 1) * 4) + (f32 ? 0 : al256((size_t)nch * 3 * 32 * JT * 128));
 }
 
 void glaunch_proj_fwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *X, const float *W,
                       const float *alpha, const float *hbias, float rms_eps, float *H_pre, float *H_post,
                       float *logits, float *saved, float *H_res, int iters, float eps, void *ws) {
-  const int64_t K = (int64_t)n * C;
+  const int64_t K = (int64_t)n * C, J = (int64_t)n * n + 2 * n;
   float *part = (float *)ws;
-  const unsigned pb = (unsigned)(((N + kGTokWG - 1) / kGTokWG) * kGSplitK);
-  if (f32)
+  if (f32) {
+    const unsigned pb = (unsigned)(((N + kGTokWG - 1) / kGTokWG) * kGSplitK);
     MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_partial_kernel<float, NS>), dim3(pb), dim3(256), 0, s,
                                           (const float *)X, W, part, N, K))
-  else
-    MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_partial_bf16_kernel<NS>), dim3(pb), dim3(256), 0, s,
-                                          (const bf16_t *)X, W, part, N, K))
+  } else {
+    bf16_t *Wp = (bf16_t *)((char *)ws + al256((size_t)kGSplitK * N * (J + 1) * 4));
+    const int64_t nch = (K + 63) / 64;
+    const unsigned pb = (unsigned)(((N + kGDmaTok - 1) / kGDmaTok) * kGSplitK);
+    MHC_NS_DISPATCH(n, {
+      using G = GPj<NS>;
+      hipLaunchKernelGGL((gpack_w_kernel<NS>), dim3((unsigned)((nch * 32 * G::JT * 8 + 255) / 256)), dim3(256), 0,
+                         s, W, Wp, K);
+      hipLaunchKernelGGL((gproj_partial_dma_kernel<NS>), dim3(pb), dim3(512), (size_t)G::STAGES * G::SB, s,
+                         (const bf16_t *)X, (const bf16_t *)Wp, part, N, K);
+    })
+  }
   const unsigned fb = (unsigned)((N + 63) / 64);
   MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_finalize_kernel<NS>), dim3(fb), dim3(64), 0, s, part, N, K, alpha,
                                         hbias, rms_eps, H_pre, H_post, logits, saved, saved_stride(n), H_res,

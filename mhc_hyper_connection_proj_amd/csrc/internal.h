@@ -161,7 +161,7 @@ void glaunch_stream_mix_bwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C
                             const float *M, void *dX, float *dM);
 void glaunch_stream_distribute_bwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *G,
                                    const void *x, const float *H_post, void *dx, float *dH_post);
-size_t gproj_fwd_ws(int n, int64_t N);
+size_t gproj_fwd_ws(int n, int64_t N, int64_t C, bool f32);
 void glaunch_proj_fwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, const void *X, const float *W,
                       const float *alpha, const float *hbias, float rms_eps, float *H_pre, float *H_post,
                       float *logits, float *saved, float *H_res, int iters, float eps, void *ws);
