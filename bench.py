@@ -157,8 +157,8 @@ def measure_norm_bwd_fusion(lib, L, sp, stream, torch, N, n, C, X, W, G, H_res, 
                             logits, dHp, dHr) -> dict:
     """The pre backward with the norm's backward in front, at the workload's shape (the h_post_bda term
     formed from G), with a gain and dgamma and without: mhc_pre_rmsnorm_bwd against mhc_rmsnorm_bwd
-    followed by mhc_pre_bwd (the same results, bit for bit).  Mean of 5 event-timed calls after one
-    warm-up."""
+    followed by mhc_pre_bwd (the same results, bit for bit).  Mean of 5 event-timed calls of each
+    after one warm-up, the two forms alternating."""
     dev = X.device
     bf = torch.bfloat16
     P = lambda t: t.data_ptr() if t is not None else None
@@ -196,18 +196,23 @@ def measure_norm_bwd_fusion(lib, L, sp, stream, torch, N, n, C, X, W, G, H_res, 
                                 P(H_pre), P(H_post), P(logits), 20, 1e-6, P(G), P(H_res), P(dX), 0, P(dW), P(da),
                                 P(db), None, None, P(wsp), wp))
 
+    # the two forms alternate call by call (back-to-back calls of this phase slow down as the GPU
+    # warms, which would otherwise favour whichever form runs first)
     res = {}
-    for name, fn in (("fused_ms", fused), ("norm_then_pre_bwd_ms", composed), ("fused_no_gain_ms", fused_nog),
-                     ("norm_then_pre_bwd_no_gain_ms", composed_nog)):
-        fn()
+    for (na, fa), (nb, fb) in ((("fused_ms", fused), ("norm_then_pre_bwd_ms", composed)),
+                               (("fused_no_gain_ms", fused_nog), ("norm_then_pre_bwd_no_gain_ms", composed_nog))):
+        fa(); fb()
         torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(11)]
         ev[0].record(stream)
         for i in range(5):
-            fn()
-            ev[i + 1].record(stream)
+            fa()
+            ev[2 * i + 1].record(stream)
+            fb()
+            ev[2 * i + 2].record(stream)
         torch.cuda.synchronize()
-        res[name] = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(5)]))
+        res[na] = float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(5)]))
+        res[nb] = float(np.mean([ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(5)]))
     return res
 
 
