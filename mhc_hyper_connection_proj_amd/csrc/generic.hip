@@ -47,11 +47,14 @@ template <int NS> struct Dim {
   static constexpr int JT = (J + 31) / 32;     // 32-column MFMA tiles
   static constexpr int PS = J + 1;             // partial row: x @ W, then sum x^2
   // Backward record of a token: dp[0..J), zeros up to RC, c_rms at RC, row
-  // stride RS (a multiple of 4 floats).  The fp32 MFMA of the dX kernel
-  // takes dp as two halves of JC values (lane half h holds j = h JC + c),
-  // JC a multiple of 4 so each half is read as whole 16-byte words.
+  // stride RS (a multiple of 4 floats).  The fp32 MFMA of the dX kernels
+  // takes dp in equal parts, one per lane group, read as whole 16-byte
+  // words: two halves of JC values (32x32x2, n <= 3: lane half h holds
+  // j = h JC + c) or four quarters of JQ values (16x16x4, n >= 5: lane group
+  // g holds j = g JQ + c).
   static constexpr int JC = ((J + 1) / 2 + 3) / 4 * 4;
-  static constexpr int RC = 2 * JC;
+  static constexpr int JQ = ((J + 3) / 4 + 3) / 4 * 4;
+  static constexpr int RC = NS >= 5 ? 4 * JQ : 2 * JC;
   static constexpr int RS = (RC + 1 + 3) / 4 * 4;
 };
 
@@ -1242,7 +1245,7 @@ __global__ __launch_bounds__(256) void gproj_bwd_dx_kernel(
   }
 }
 
-// ------------------------------------------------------------------ MFMA dX / dW kernel (bf16 activations)
+// ------------------------------------------------------------------ MFMA dX / dW kernel (bf16 activations, n <= 3)
 // The same dX and dW as the VALU kernel above, with the aggregate and
 // h_post_bda residual terms formed in place (no fp32 term workspace):
 //   dX[t][j][c] = (dX_in) + dp[t] . W[k] + c_rms[t] x[t][j][c] + H_pre[t][j] g[t][c]
@@ -1261,14 +1264,15 @@ __global__ __launch_bounds__(256) void gproj_bwd_dx_kernel(
 //    accumulator transposed through a private LDS area, then the epilogue
 //    with 16-byte row pieces and 16-byte stores; H_pre, H_res and dX_in rows
 //    are prefetched one sub-tile ahead.
-// fp32 MFMA keeps W's rows in registers: at n = 8 (J = 80) 40 values per
-// lane per block, where the six three-term bf16 products would need 240.
+// fp32 MFMA keeps W's rows in registers (J / 2 values per lane per block,
+// where the six three-term bf16 products would need 3 J).  n >= 5 uses the
+// two kernels further below.
 // Synchronisation as in the n = 4 kernel: loaders issue no other global
 // memory operation in the loop (exact vmcnt), dX waves never issue DMA, one
 // barrier per sub-tile.
 
-// 32-channel blocks per stream in a channel tile of the MFMA dX kernel: as
-// wide as the 3-stage ring fits in LDS with W's rows in registers.
+// 32-channel blocks per stream in a channel tile of the MFMA dX/dW kernel
+// (n <= 3): as wide as the 3-stage ring fits in LDS.
 constexpr int gmf_cb(int n) { return n <= 2 ? 4 : n == 3 ? 2 : 1; }
 constexpr int64_t gmf_cw(int n) { return 32 * gmf_cb(n); }
 
@@ -1601,6 +1605,360 @@ __global__ __launch_bounds__(512) void gproj_bwd_mfma_kernel(
   }
 }
 
+// ------------------------------------------------------------------ dX and dW as two kernels (bf16, n >= 5)
+// For n >= 5 W's rows and the dW accumulators of a channel tile do not both
+// fit on chip beside a ring at more than 32 channels (64-byte row pieces, one
+// DRAM page opened per 64 bytes).  There dW = x^T dp runs alone on tiles of
+// 256 consecutive k (512-byte pieces), and dX, freed of the accumulators, on
+// tiles of 64 channels of all n streams with eight dX waves.
+typedef __attribute__((ext_vector_type(4))) float gf32x4;
+
+// dp split once per call into its three exact bf16 terms, transposed per
+// 32-token sub-tile: dpT[sub][term][column (32 JT, zero past J)][32 tokens]
+// (zero for tokens past N), so a dW B fragment (8 tokens of one column) is
+// one 16-byte read.  Thread = (sub-tile, column, token), tokens fastest.
+template <int NS>
+__global__ __launch_bounds__(256) void gsplit_dp_kernel(const float *__restrict__ rec, bf16_t *__restrict__ dpT,
+                                                       int64_t N) {
+  constexpr int J = Dim<NS>::J, JT = Dim<NS>::JT, RS = Dim<NS>::RS;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nsub = (N + 31) / 32;
+  if (i >= nsub * 32 * JT * 32) return;
+  const int tok = (int)(i & 31), jj = (int)((i >> 5) % (32 * JT));
+  const int64_t sb = (i >> 5) / (32 * JT);
+  const int64_t t = sb * 32 + tok;
+  const float v = (t < N && jj < J) ? rec[t * RS + jj] : 0.f;
+  const float hi = (float)(__bf16)v, r1 = v - hi, mid = (float)(__bf16)r1, lo = r1 - mid;
+  const float terms[3] = {hi, mid, lo};
+#pragma unroll
+  for (int m = 0; m < 3; ++m) {
+    const __bf16 b = (__bf16)terms[m];
+    dpT[((sb * 3 + m) * 32 * JT + jj) * 32 + tok] = __builtin_bit_cast(uint16_t, b);
+  }
+}
+
+// dW kernel: eight waves on one token block and 256 consecutive k, walked in
+// 32-token sub-tiles through a 2-stage ring that all eight waves fill with
+// global_load_lds_dwordx4 (no other global memory operation in the loop):
+// the X tile (512-byte row pieces) and the sub-tile's block of dpT.  Two
+// stages (68 KB at n = 8) let two workgroups share a CU: 4% faster for the
+// n = 8 pre backward than three stages and one workgroup.  Wave w owns the 32 k at 32 w: bf16 MFMA
+// (32x32x16), A = 8 tokens of a k column of the X tile (exact in bf16), B =
+// one bf16 term of dp for the same 8 tokens (one 16-byte read).  Piece p of
+// X row t sits in slot p ^ (4 ((t >> 3) & 1)), so the two 8-token halves of
+// a column read fall on different banks.
+template <int NS> struct GDw {
+  static constexpr int JT = Dim<NS>::JT;
+  static constexpr int XB = 32 * 512;           // X tile: 32 tokens x 256 k
+  static constexpr int DB = 3 * 32 * JT * 64;   // dpT block of one sub-tile
+  static constexpr int SB = XB + DB;
+  static constexpr int STG = 2;
+  static_assert(DB % 1024 == 0, "whole 1 KB copies");
+  static __device__ __forceinline__ int off(int t, int slot) { return (t * 32 + (slot ^ (4 * ((t >> 3) & 1)))) * 16; }
+};
+
+template <int NS>
+__global__ __launch_bounds__(512) void gproj_dw_mfma_kernel(const bf16_t *__restrict__ X, const bf16_t *__restrict__ dpT,
+                                                           float *__restrict__ dwpart, int64_t N, int64_t K,
+                                                           int64_t tbsz, int64_t ntb) {
+  using M = GDw<NS>;
+  constexpr int J = Dim<NS>::J, JT = Dim<NS>::JT;
+  extern __shared__ __attribute__((aligned(16))) char gdl[];
+  const int64_t nkt = (K + 255) / 256;
+  const int64_t T = nkt * ntb, per = (T + 7) / 8;
+  const int64_t tile = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;  // XCD-contiguous order
+  if (tile >= T) return;  // grid padding to a multiple of 8 (whole workgroup)
+  const int64_t tb = tile / nkt;
+  const int64_t k0 = (tile % nkt) * 256;
+  const int64_t t_begin = min(N, tb * tbsz), t_end = min(N, t_begin + tbsz);
+  const int nsub = (int)((t_end - t_begin + 31) / 32);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, col = lane & 31, h = lane >> 5;
+  constexpr int QX = M::XB / 1024, QD = M::DB / 1024, Q = QX + QD;
+
+  auto issue = [&](int i) {
+    char *st = gdl + (i % M::STG) * M::SB;
+    const int64_t t0 = t_begin + 32 * (int64_t)i;  // a multiple of 32
+    for (int q = wave; q < Q; q += 8) {
+      if (q < QX) {
+        const int t = 2 * q + (lane >> 5), slot = lane & 31;
+        const int p = slot ^ (4 * ((t >> 3) & 1));
+        const int64_t tt = min(t0 + t, N - 1);  // rows past N re-read row N-1 (their dp terms are 0)
+        const int64_t k = k0 + 8 * p < K ? k0 + 8 * p : k0;
+        gdma16(X + tt * K + k, st + q * 1024);
+      } else {
+        const int qq = q - QX;
+        gdma16(reinterpret_cast<const char *>(dpT) + (t0 / 32) * M::DB + qq * 1024 + lane * 16,
+               st + M::XB + qq * 1024);
+      }
+    }
+  };
+
+  gf32x16 accW[JT];
+#pragma unroll
+  for (int u = 0; u < JT; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) accW[u][r] = 0.f;
+  const int kk = 32 * wave + col;  // this lane's column of the tile
+  // two stages: the slot refilled after the barrier of sub-tile i was read
+  // in sub-tile i - 1, so only sub-tile i's copies are outstanding at its wait
+  if (nsub > 0) issue(0);
+  for (int i = 0; i < nsub; ++i) {
+    gwait_vmcnt<0>();
+    glds_barrier();
+    if (i + 1 < nsub) issue(i + 1);
+    const char *st = gdl + (i % M::STG) * M::SB;
+    const char *dt = st + M::XB;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      uint32_t w4v[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int tr0 = 16 * s + 8 * h + 2 * p;
+        const uint32_t lo = *reinterpret_cast<const uint16_t *>(st + M::off(tr0, kk >> 3) + 2 * (kk & 7));
+        const uint32_t hi = *reinterpret_cast<const uint16_t *>(st + M::off(tr0 + 1, kk >> 3) + 2 * (kk & 7));
+        w4v[p] = lo | (hi << 16);
+      }
+      const gu32x4 xa = gu32x4{w4v[0], w4v[1], w4v[2], w4v[3]};
+#pragma unroll
+      for (int m = 0; m < 3; ++m)
+#pragma unroll
+        for (int u = 0; u < JT; ++u) {
+          const gu32x4 bw = *reinterpret_cast<const gu32x4 *>(dt + ((m * 32 * JT + 32 * u + col) * 32 + 16 * s + 8 * h) * 2);
+          accW[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(gbf16x8, xa),
+                                                            __builtin_bit_cast(gbf16x8, bw), accW[u], 0, 0, 0);
+        }
+    }
+  }
+  const int64_t kb = k0 + 32 * wave;
+#pragma unroll
+  for (int u = 0; u < JT; ++u) {
+    const int jj = 32 * u + col;
+    if (jj >= J) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t k = kb + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (k < K) dwpart[(tb * K + k) * J + jj] = accW[u][r];
+    }
+  }
+}
+
+// dX kernel: 12 waves on one token block and one tile of 64 channels of all
+// NS streams, walked in 16-token sub-tiles through a 3-stage LDS ring:
+//  * waves 8..11 (loaders) fill each stage with global_load_lds_dwordx4 two
+//    sub-tiles ahead: X and G tiles [stream][token][64 channels], the g tile
+//    and the 16 records (piece p of row t in slot p ^ (t & 7));
+//  * wave w < NS owns stream w: dp W^T on fp32 MFMA (16x16x4) over four
+//    16-column blocks, W's rows in registers (lane group g holds
+//    j = g JQ + c), the 16 x 64 result transposed through a private LDS
+//    area, then the epilogue with 16-byte row pieces (eight lanes store one
+//    token's 128-byte row piece); H_pre, H_res and dX_in rows prefetched one
+//    sub-tile ahead.  Waves NS..7 only keep the barrier sequence.
+template <int NS> struct GDx {
+  static constexpr int J = Dim<NS>::J, JQ = Dim<NS>::JQ, RC = Dim<NS>::RC, RS = Dim<NS>::RS;
+  static constexpr int XB = NS * 16 * 128;                        // X (and G) tile
+  static constexpr int GB = 16 * 128;                             // g tile
+  static constexpr int RB = (RS * 16 * 4 + 1023) / 1024 * 1024;   // records, whole 1 KB copies
+  static constexpr int AS = 68;                                   // accumulator tile row stride (floats)
+  static constexpr int ACC = 8 * 16 * AS * 4;
+  static_assert(NS >= 5 && NS <= 8, "the split kernels serve n = 5..8");
+  static_assert(3 * (2 * XB + GB + RB) + ACC <= 160 * 1024, "LDS of one workgroup");
+  static __device__ __forceinline__ int off(int j, int t, int slot) { return ((j * 16 + t) * 8 + (slot ^ (t & 7))) * 16; }
+};
+
+// flags: bit 0 g given, bit 1 h_post_bda term (G, H_res), bit 2 accumulate into dX
+template <int NS>
+__global__ __launch_bounds__(768) void gproj_dx16_mfma_kernel(
+    const bf16_t *__restrict__ X, const float *__restrict__ W, const float *__restrict__ rec,
+    const float *__restrict__ Hpre, const bf16_t *__restrict__ gr, const bf16_t *__restrict__ Gp,
+    const float *__restrict__ Hres, bf16_t *__restrict__ dX, int64_t N, int64_t C, int64_t tbsz, int64_t ntb,
+    int flags) {
+  using M = GDx<NS>;
+  constexpr int J = M::J, JQ = M::JQ, RC = M::RC, RS = M::RS;
+  extern __shared__ __attribute__((aligned(16))) char gxl[];
+  const bool has_g = flags & 1, post = (flags >> 1) & 1, accum = (flags >> 2) & 1;
+  const int64_t nct = (C + 63) / 64;
+  const int64_t T = nct * ntb, per = (T + 7) / 8;
+  const int64_t tile = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;  // XCD-contiguous order
+  if (tile >= T) return;  // grid padding to a multiple of 8 (whole workgroup)
+  const int64_t tb = tile / nct;
+  const int64_t c0 = (tile % nct) * 64;
+  const int64_t t_begin = min(N, tb * tbsz), t_end = min(N, t_begin + tbsz);
+  const int nsub = (int)((t_end - t_begin + 15) / 16);
+
+  const int oG = M::XB, og = oG + (post ? M::XB : 0), oR = og + (has_g ? M::GB : 0), SB = oR + M::RB;
+  const int QX = M::XB / 1024, QG = post ? QX : 0, Qg = has_g ? M::GB / 1024 : 0, QR = M::RB / 1024;
+  const int Q = QX + QG + Qg + QR;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const bool loader = wave >= 8;
+  const int lw = wave - 8;
+
+  auto issue = [&](int i) {
+    char *st = gxl + (i % 3) * SB;
+    const int64_t t0 = t_begin + 16 * (int64_t)i;
+    for (int q = lw; q < Q; q += 4) {
+      if (q < QX + QG + Qg) {
+        const bool is_g = q >= QX + QG;
+        const int qq = is_g ? q - QX - QG : q < QX ? q : q - QX;
+        const int row = 8 * qq + (lane >> 3);  // (stream, token) row of the tile
+        const int j = row / 16, t = row % 16;
+        const int p = (lane & 7) ^ (t & 7);
+        const int64_t tt = min(t0 + t, N - 1);  // rows past N re-read row N-1 (never stored)
+        const int64_t ch = c0 + 8 * p < C ? c0 + 8 * p : c0;  // pieces past C: a real channel
+        const bf16_t *src = is_g ? gr + tt * C + ch : (q < QX ? X : Gp) + (tt * NS + j) * C + ch;
+        gdma16(src, st + (is_g ? og : q < QX ? 0 : oG) + qq * 1024);
+      } else {
+        // records: contiguous, padded to whole 32-token sub-tiles plus 1 KB
+        const int qq = q - QX - QG - Qg;
+        gdma16(reinterpret_cast<const char *>(rec + t0 * RS) + qq * 1024 + lane * 16, st + oR + qq * 1024);
+      }
+    }
+  };
+
+  // ---- dX wave w < NS: stream j = w, columns c0 + 16 bi + (lane & 15)
+  const int j = wave;
+  const bool active = !loader && wave < NS;
+  const int gq = lane >> 4, cl = lane & 15;
+  float wf[4][JQ];
+  if (active) {
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) {
+      const int64_t c = c0 + 16 * bi + cl;
+      const float *wr = W + ((int64_t)j * C + c) * J;
+#pragma unroll
+      for (int e = 0; e < JQ; ++e) {
+        const int jj = gq * JQ + e;
+        wf[bi][e] = c < C && jj < J ? wr[jj] : 0.f;
+      }
+    }
+  }
+  const int er = lane >> 3, pk = lane & 7;  // epilogue: rows er and er + 8, channels 8 pk .. + 8
+  float hp[2], hr[2][NS];
+  gu32x4 din[2];
+  auto prefetch = [&](int i) {
+    const int64_t t0 = t_begin + 16 * (int64_t)i;
+    const int64_t ch = c0 + 8 * pk;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int64_t t = t0 + er + 8 * rr;
+      const bool v = t < N;
+      hp[rr] = v && has_g ? Hpre[t * NS + j] : 0.f;
+#pragma unroll
+      for (int e = 0; e < NS; ++e) hr[rr][e] = v && post ? Hres[(t * NS + j) * NS + e] : 0.f;
+      din[rr] = v && accum && ch < C ? *reinterpret_cast<const gu32x4 *>(dX + (t * NS + j) * C + ch)
+                                     : gu32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
+  if (loader) {
+    const int nq = (Q - lw + 3) / 4;  // this wave's copies per stage
+    if (nsub > 0) issue(0);
+    if (nsub > 1) issue(1);
+    for (int i = 0; i < nsub; ++i) {
+      if (i + 1 < nsub) gwait_vmcnt_le(nq); else gwait_vmcnt<0>();
+      glds_barrier();
+      if (i + 2 < nsub) issue(i + 2);
+    }
+  } else if (!active) {
+    for (int i = 0; i < nsub; ++i) glds_barrier();
+  } else {
+    float *acc_t = reinterpret_cast<float *>(gxl + 3 * SB) + wave * 16 * M::AS;
+    gwait_vmcnt<0>();  // W in registers: only the prefetches are pending inside the loop
+    prefetch(0);
+    for (int i = 0; i < nsub; ++i) {
+      glds_barrier();
+      const char *st = gxl + (i % 3) * SB;
+      const float *rt = reinterpret_cast<const float *>(st + oR);
+      const int64_t t0 = t_begin + 16 * (int64_t)i;
+      // the four blocks' accumulations interleaved (independent chains), each
+      // A value read once for the four blocks
+      const float *ar = rt + cl * RS + gq * JQ;
+      gf32x4 acc[4];
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) acc[bi] = gf32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e4 = 0; e4 < JQ / 4; ++e4) {
+        const float4 a4 = *reinterpret_cast<const float4 *>(ar + 4 * e4);
+        const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int bi = 0; bi < 4; ++bi)
+            acc[bi] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], wf[bi][4 * e4 + e], acc[bi], 0, 0, 0);
+      }
+      // 16x16 accumulator layout: lane (column cl, group gq), register r holds row 4 gq + r
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc_t[(4 * gq + r) * M::AS + 16 * bi + cl] = acc[bi][r];
+      // the prefetched rows, waited for once, after the MFMAs
+      __builtin_amdgcn_sched_barrier(0);
+      gwait_vmcnt<0>();
+      gwave_lds_sync();
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int row = er + 8 * rr;
+        const int64_t t = t0 + row;
+        const int64_t ch = c0 + 8 * pk;
+        if (!(t < N && ch < C)) continue;
+        const float4 a0 = *reinterpret_cast<const float4 *>(&acc_t[row * M::AS + 8 * pk]);
+        const float4 a1 = *reinterpret_cast<const float4 *>(&acc_t[row * M::AS + 8 * pk + 4]);
+        float o[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const float crms = rt[row * RS + RC];
+        const gu32x4 xv = *reinterpret_cast<const gu32x4 *>(st + M::off(j, row, pk));
+        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          o[2 * p] += crms * bf16_lo(xw[p]);
+          o[2 * p + 1] += crms * bf16_hi(xw[p]);
+        }
+        if (has_g) {
+          const gu32x4 gv = *reinterpret_cast<const gu32x4 *>(st + og + M::off(0, row, pk));
+          const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            o[2 * p] += hp[rr] * bf16_lo(gw[p]);
+            o[2 * p + 1] += hp[rr] * bf16_hi(gw[p]);
+          }
+        }
+        if (post) {  // sum_i H_res[t][j][i] G[t][i], i in order
+          float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int e = 0; e < NS; ++e) {
+            const gu32x4 v = *reinterpret_cast<const gu32x4 *>(st + oG + M::off(e, row, pk));
+            const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              s8[2 * p] += hr[rr][e] * bf16_lo(vw[p]);
+              s8[2 * p + 1] += hr[rr][e] * bf16_hi(vw[p]);
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] += s8[e];
+        }
+        if (accum) {
+          const uint32_t dw4[4] = {din[rr].x, din[rr].y, din[rr].z, din[rr].w};
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            o[2 * p] += bf16_lo(dw4[p]);
+            o[2 * p + 1] += bf16_hi(dw4[p]);
+          }
+        }
+        uint4 ow;
+        ow.x = pack_bf16x2(o[0], o[1]);
+        ow.y = pack_bf16x2(o[2], o[3]);
+        ow.z = pack_bf16x2(o[4], o[5]);
+        ow.w = pack_bf16x2(o[6], o[7]);
+        *reinterpret_cast<uint4 *>(dX + (t * NS + j) * C + ch) = ow;
+      }
+      gwave_lds_sync();  // the accumulator tile's reads precede the next sub-tile's writes
+      if (i + 1 < nsub) prefetch(i + 1);
+    }
+  }
+}
+
 // dW[k][j] = sum over token blocks in block order.
 __global__ __launch_bounds__(256) void gdw_reduce_kernel(const float *__restrict__ part, float *__restrict__ dW,
                                                         int64_t ntb, int64_t KJ) {
@@ -1632,13 +1990,13 @@ inline size_t al256(size_t b) { return (b + 255) / 256 * 256; }
 
 struct GBwdLay {
   int64_t ntb, tb;
-  size_t rec, prm, dw, dhrow, term, dl, total;
+  size_t rec, prm, dw, dhrow, term, dl, dpt, total;
 };
 
 // Backward record stride (floats) for a run-time n: Dim<n>::RS.
 static int grec_stride(int n) {
-  const int J = n * n + 2 * n, JC = ((J + 1) / 2 + 3) / 4 * 4;
-  return (2 * JC + 1 + 3) / 4 * 4;
+  const int J = n * n + 2 * n, JC = ((J + 1) / 2 + 3) / 4 * 4, JQ = ((J + 3) / 4 + 3) / 4 * 4;
+  return ((n >= 5 ? 4 * JQ : 2 * JC) + 1 + 3) / 4 * 4;
 }
 
 // f32: the VALU dX kernel, with room for the fp32 residual-gradient terms
@@ -1654,9 +2012,10 @@ GBwdLay gbwd_layout(int64_t N, int64_t C, int n, bool terms, bool f32) {
     L.ntb = std::min<int64_t>(std::min<int64_t>(kGMaxTB, by_budget), std::max<int64_t>(1, (N + 63) / 64));
     L.tb = (N + L.ntb - 1) / L.ntb;
   } else {
-    // about 512 workgroups (two rounds of one per CU) over the channel tiles,
-    // token blocks in whole 32-token sub-tiles
-    const int64_t nct = (C + gmf_cw(n) - 1) / gmf_cw(n);
+    // about 512 workgroups (two rounds of one per CU) over the tiles of the
+    // kernel that forms dW (channel tiles of all n streams for n <= 3, 256
+    // consecutive k for n >= 5), token blocks in whole 32-token sub-tiles
+    const int64_t nct = n >= 5 ? (K + 255) / 256 : (C + gmf_cw(n) - 1) / gmf_cw(n);
     L.ntb = std::min<int64_t>(std::min<int64_t>(std::max<int64_t>(1, 512 / nct), by_budget),
                               std::max<int64_t>(1, (N + 31) / 32));
     L.tb = ((N + L.ntb - 1) / L.ntb + 31) / 32 * 32;
@@ -1668,7 +2027,9 @@ GBwdLay gbwd_layout(int64_t N, int64_t C, int n, bool terms, bool f32) {
   L.dhrow = al256((size_t)N * n * 4);
   L.term = terms && f32 ? al256((size_t)N * K * 4) : 0;
   L.dl = al256((size_t)N * n * n * 4);  // the logits' gradient when the row-per-lane Sinkhorn backward forms it
-  L.total = L.rec + L.prm + L.dw + L.dhrow + L.term + L.dl;
+  // bf16, n >= 5: dp's bf16 terms transposed per 32-token sub-tile for the dW kernel
+  L.dpt = !f32 && n >= 5 ? al256((size_t)(N + 31) / 32 * 3 * 32 * ((J + 31) / 32) * 64) : 0;
+  L.total = L.rec + L.prm + L.dw + L.dhrow + L.term + L.dl + L.dpt;
   return L;
 }
 
@@ -1895,23 +2256,52 @@ static void gdx(hipStream_t s, int n, const ProjBwdArgs &a, const GBwdLay &L, co
                                           a.accumulate))
 }
 
+// n >= 5: the dX kernel (about 512 workgroups of 64 channels x a token block
+// in whole 16-token sub-tiles), then the dW kernel on the layout's token blocks.
 template <int NS>
-static void gdx_mfma(hipStream_t s, const ProjBwdArgs &a, const GBwdLay &L, const float *rec, float *dwp) {
-  using M = GMf<NS>;
-  const int64_t nct = (a.C + M::CW - 1) / M::CW, T = nct * L.ntb;
-  const unsigned blocks = (unsigned)((T + 7) / 8 * 8);
+static void gdx_split(hipStream_t s, const ProjBwdArgs &a, const GBwdLay &L, const float *rec, float *dwp,
+                      bf16_t *dpT) {
+  using M = GDx<NS>;
+  const int64_t nct = (a.C + 63) / 64;
+  const int64_t ntbx = std::min<int64_t>(std::max<int64_t>(1, 512 / nct), std::max<int64_t>(1, (a.N + 15) / 16));
+  const int64_t tbx = ((a.N + ntbx - 1) / ntbx + 15) / 16 * 16;
   const bool has_g = a.g != nullptr, post = a.post_G != nullptr;
   const int flags = (has_g ? 1 : 0) | (post ? 2 : 0) | (a.accumulate ? 4 : 0);
   const size_t stage = (size_t)M::XB * (post ? 2 : 1) + (has_g ? M::GB : 0) + M::RB;
-  const size_t lds = 3 * stage + M::ACC;
-  if (a.dW)
-    hipLaunchKernelGGL((gproj_bwd_mfma_kernel<NS, true>), dim3(blocks), dim3(512), lds, s, (const bf16_t *)a.X, a.W,
-                       rec, a.H_pre, (const bf16_t *)a.g, (const bf16_t *)a.post_G, a.post_H_res, (bf16_t *)a.dX,
-                       dwp, a.N, a.C, L.tb, L.ntb, flags);
-  else
-    hipLaunchKernelGGL((gproj_bwd_mfma_kernel<NS, false>), dim3(blocks), dim3(512), lds, s, (const bf16_t *)a.X, a.W,
-                       rec, a.H_pre, (const bf16_t *)a.g, (const bf16_t *)a.post_G, a.post_H_res, (bf16_t *)a.dX,
-                       dwp, a.N, a.C, L.tb, L.ntb, flags);
+  hipLaunchKernelGGL((gproj_dx16_mfma_kernel<NS>), dim3((unsigned)((nct * ntbx + 7) / 8 * 8)), dim3(768),
+                     3 * stage + M::ACC, s, (const bf16_t *)a.X, a.W, rec, a.H_pre, (const bf16_t *)a.g,
+                     (const bf16_t *)a.post_G, a.post_H_res, (bf16_t *)a.dX, a.N, a.C, tbx, ntbx, flags);
+  if (a.dW) {
+    const int64_t K = (int64_t)NS * a.C, nkt = (K + 255) / 256;
+    const int64_t nsp = (a.N + 31) / 32 * 32 * GDw<NS>::JT * 32;
+    hipLaunchKernelGGL((gsplit_dp_kernel<NS>), dim3((unsigned)((nsp + 255) / 256)), dim3(256), 0, s, rec, dpT, a.N);
+    hipLaunchKernelGGL((gproj_dw_mfma_kernel<NS>), dim3((unsigned)((nkt * L.ntb + 7) / 8 * 8)), dim3(512),
+                       GDw<NS>::STG * GDw<NS>::SB, s, (const bf16_t *)a.X, (const bf16_t *)dpT, dwp, a.N, K, L.tb, L.ntb);
+  }
+}
+
+template <int NS>
+static void gdx_mfma(hipStream_t s, const ProjBwdArgs &a, const GBwdLay &L, const float *rec, float *dwp,
+                     bf16_t *dpT) {
+  if constexpr (NS >= 5) {
+    gdx_split<NS>(s, a, L, rec, dwp, dpT);
+  } else {
+    using M = GMf<NS>;
+    const int64_t nct = (a.C + M::CW - 1) / M::CW, T = nct * L.ntb;
+    const unsigned blocks = (unsigned)((T + 7) / 8 * 8);
+    const bool has_g = a.g != nullptr, post = a.post_G != nullptr;
+    const int flags = (has_g ? 1 : 0) | (post ? 2 : 0) | (a.accumulate ? 4 : 0);
+    const size_t stage = (size_t)M::XB * (post ? 2 : 1) + (has_g ? M::GB : 0) + M::RB;
+    const size_t lds = 3 * stage + M::ACC;
+    if (a.dW)
+      hipLaunchKernelGGL((gproj_bwd_mfma_kernel<NS, true>), dim3(blocks), dim3(512), lds, s, (const bf16_t *)a.X,
+                         a.W, rec, a.H_pre, (const bf16_t *)a.g, (const bf16_t *)a.post_G, a.post_H_res,
+                         (bf16_t *)a.dX, dwp, a.N, a.C, L.tb, L.ntb, flags);
+    else
+      hipLaunchKernelGGL((gproj_bwd_mfma_kernel<NS, false>), dim3(blocks), dim3(512), lds, s, (const bf16_t *)a.X,
+                         a.W, rec, a.H_pre, (const bf16_t *)a.g, (const bf16_t *)a.post_G, a.post_H_res,
+                         (bf16_t *)a.dX, dwp, a.N, a.C, L.tb, L.ntb, flags);
+  }
 }
 
 template <typename T>
@@ -1963,7 +2353,8 @@ void glaunch_proj_bwd(hipStream_t s, int n, const ProjBwdArgs &a) {
     if (terms) gterms<float>(s, n, a, term);
     gdx<float>(s, n, a, L, rec, term, dwp);
   } else {
-    MHC_NS_DISPATCH(n, gdx_mfma<NS>(s, a, L, rec, dwp));
+    bf16_t *dpT = (bf16_t *)(base + L.rec + L.prm + L.dw + L.dhrow + L.term + L.dl);
+    MHC_NS_DISPATCH(n, gdx_mfma<NS>(s, a, L, rec, dwp, dpT));
   }
   if (a.dW)
     hipLaunchKernelGGL(gdw_reduce_kernel, dim3((unsigned)((K * J + 255) / 256)), dim3(256), 0, s, dwp, a.dW, L.ntb,

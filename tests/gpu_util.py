@@ -133,10 +133,10 @@ def dxdw_token_block(N: int, C: int, n: int = 4, act: str = "bf16") -> int:
         if act == "f32":  # blocks of >= 64 tokens, at most 32 of them
             ntb = min(32, by_budget, max(1, _cdiv(N, 64)))
             return _cdiv(N, ntb)
-        # bf16: about 512 workgroups over the channel tiles (32, 64 or 128 channels of all n streams),
-        # blocks in whole 32-token sub-tiles
-        cw = 32 * (4 if n <= 2 else 2 if n == 3 else 1)
-        ntb = min(max(1, 512 // _cdiv(C, cw)), by_budget, max(1, _cdiv(N, 32)))
+        # bf16: about 512 workgroups over the tiles of the kernel that forms dW (64 or 128 channels of
+        # all n streams for n <= 3, 256 consecutive k for n >= 5), blocks in whole 32-token sub-tiles
+        tiles = _cdiv(K, 256) if n >= 5 else _cdiv(C, 32 * (4 if n <= 2 else 2))
+        ntb = min(max(1, 512 // tiles), by_budget, max(1, _cdiv(N, 32)))
         return _rup(_cdiv(N, ntb), 32)
     if act == "f32":  # about 2048 workgroups of 1024 k
         return _rup(max(32, _cdiv(N * _cdiv(K, 1024), 2048)), 32)
