@@ -611,9 +611,9 @@ __global__ __launch_bounds__(256) void gpost_fwd_kernel(const T *__restrict__ X,
 // <G_i, x + bias> and dx = sum_i H_post[i] G_i (MODE != mix).  One wave per
 // token, four waves per workgroup working independently: a lane owns the
 // 8-channel groups g = lane, lane + 64, ..., and the per-token sums are wave
-// reductions (no barrier).  The rows j of X are taken JB at a time (JB = 4
-// for n > 4), each pass with its own JB * n sums, so the per-lane sums stay
-// few; G is re-read per pass (from the caches).  DBIAS: each wave walks TG
+// reductions (no barrier).  The rows j of X are taken JB at a time, each
+// pass with its own JB * n sums (all rows in one pass up to n = 7, two
+// passes of four at n = 8, G re-read per pass from the caches).  DBIAS: each wave walks TG
 // tokens and adds its lanes' dx into its own partial row part[wave][C]
 // (owned by that lane alone: no atomics).
 template <typename T, int NS, int MODE>
@@ -625,7 +625,10 @@ __global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr
                                                        float *__restrict__ part, int64_t N, int64_t C, int TG) {
   const bool HAS_BIAS = bias != nullptr, WRITE_DX = dX != nullptr, DBIAS = part != nullptr;
   constexpr bool MIX = MODE != kPostDist, DIST = MODE != kPostMix;
-  constexpr int JB = NS > 4 ? 4 : NS;
+  // all of X's rows in one pass (G read once) up to n = 7; at n = 8 the
+  // n^2 + n sums take the registers to 256 either way, and two passes of
+  // four rows measured the same
+  constexpr int JB = NS <= 7 ? NS : 4;
   constexpr int NPASS = MIX ? (NS + JB - 1) / JB : 1;
   constexpr int NR = (MIX ? JB * NS : 0) + (DIST ? NS : 0);
   const int lane = threadIdx.x & 63;
@@ -864,8 +867,13 @@ template <int NS> struct GPj {
   static constexpr int JT = Dim<NS>::JT;
   static constexpr int WB = 3 * 32 * JT * 128;          // bytes of one packed 64-k W chunk
   static constexpr int XT = 32 * 128;                   // bytes of one wave's X tile
-  static constexpr int SB = WB + 8 * XT;                // bytes of one stage
+  // waves (32 tokens each) per workgroup, and ring stages: three where they
+  // fit in LDS (one column tile), else two.  Four waves with three stages
+  // for the wider W chunks measured 40% slower (W read per token doubles).
+  static constexpr int WAVES = 8;
+  static constexpr int SB = WB + WAVES * XT;            // bytes of one stage
   static constexpr int STAGES = 3 * SB <= 160 * 1024 ? 3 : 2;
+  static constexpr int TOK = 32 * WAVES;                // tokens per workgroup
 };
 
 template <int NS>
@@ -901,8 +909,6 @@ __global__ __launch_bounds__(256) void gpack_w_kernel(const float *__restrict__ 
   }
 }
 
-constexpr int kGDmaTok = 8 * kGTok;  // tokens per bf16 forward workgroup
-
 template <int NS>
 __global__ __launch_bounds__(512) void gproj_partial_dma_kernel(const bf16_t *__restrict__ X,
                                                                const bf16_t *__restrict__ Wp,
@@ -919,15 +925,15 @@ __global__ __launch_bounds__(512) void gproj_partial_dma_kernel(const bf16_t *__
   const int64_t cps = (nch + kGSplitK - 1) / kGSplitK;
   const int64_t c_begin = min(nch, slice * cps);
   const int nc = (int)(min(nch, c_begin + cps) - c_begin);
-  const int64_t tw = tb * kGDmaTok + kGTok * wave;  // this wave's first token
-  constexpr int QW = G::WB / 1024;                  // 1 KB copies of a W chunk, over the 8 waves
-  const int nq = (QW - wave + 7) / 8 + 4;           // this wave's copies per chunk
+  const int64_t tw = tb * G::TOK + kGTok * wave;  // this wave's first token
+  constexpr int QW = G::WB / 1024;                       // 1 KB copies of a W chunk, over the waves
+  const int nq = (QW - wave + G::WAVES - 1) / G::WAVES + 4;  // this wave's copies per chunk
 
   auto issue = [&](int i) {
     char *st = gpl + (i % STG) * G::SB;
     const int64_t c = c_begin + i;
     const char *wsrc = reinterpret_cast<const char *>(Wp) + c * G::WB;
-    for (int q = wave; q < QW; q += 8) gdma16(wsrc + q * 1024 + lane * 16, st + q * 1024);
+    for (int q = wave; q < QW; q += G::WAVES) gdma16(wsrc + q * 1024 + lane * 16, st + q * 1024);
     char *xs = st + G::WB + wave * G::XT;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -1658,7 +1664,8 @@ template <int NS> struct GDw {
 };
 
 template <int NS>
-__global__ __launch_bounds__(512) void gproj_dw_mfma_kernel(const bf16_t *__restrict__ X, const bf16_t *__restrict__ dpT,
+__global__ __launch_bounds__(512) void gproj_dw_mfma_kernel(const bf16_t *__restrict__ X,
+                                                           const bf16_t *__restrict__ dpT,
                                                            float *__restrict__ dwpart, int64_t N, int64_t K,
                                                            int64_t tbsz, int64_t ntb) {
   using M = GDw<NS>;
@@ -1724,7 +1731,8 @@ __global__ __launch_bounds__(512) void gproj_dw_mfma_kernel(const bf16_t *__rest
       for (int m = 0; m < 3; ++m)
 #pragma unroll
         for (int u = 0; u < JT; ++u) {
-          const gu32x4 bw = *reinterpret_cast<const gu32x4 *>(dt + ((m * 32 * JT + 32 * u + col) * 32 + 16 * s + 8 * h) * 2);
+          const gu32x4 bw =
+              *reinterpret_cast<const gu32x4 *>(dt + ((m * 32 * JT + 32 * u + col) * 32 + 16 * s + 8 * h) * 2);
           accW[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(gbf16x8, xa),
                                                             __builtin_bit_cast(gbf16x8, bw), accW[u], 0, 0, 0);
         }
@@ -1763,7 +1771,9 @@ template <int NS> struct GDx {
   static constexpr int ACC = 8 * 16 * AS * 4;
   static_assert(NS >= 5 && NS <= 8, "the split kernels serve n = 5..8");
   static_assert(3 * (2 * XB + GB + RB) + ACC <= 160 * 1024, "LDS of one workgroup");
-  static __device__ __forceinline__ int off(int j, int t, int slot) { return ((j * 16 + t) * 8 + (slot ^ (t & 7))) * 16; }
+  static __device__ __forceinline__ int off(int j, int t, int slot) {
+    return ((j * 16 + t) * 8 + (slot ^ (t & 7))) * 16;
+  }
 };
 
 // flags: bit 0 g given, bit 1 h_post_bda term (G, H_res), bit 2 accumulate into dX
@@ -2222,13 +2232,13 @@ void glaunch_proj_fwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, cons
   } else {
     bf16_t *Wp = (bf16_t *)((char *)ws + al256((size_t)kGSplitK * N * (J + 1) * 4));
     const int64_t nch = (K + 63) / 64;
-    const unsigned pb = (unsigned)(((N + kGDmaTok - 1) / kGDmaTok) * kGSplitK);
     MHC_NS_DISPATCH(n, {
       using G = GPj<NS>;
+      const unsigned pb = (unsigned)(((N + G::TOK - 1) / G::TOK) * kGSplitK);
       hipLaunchKernelGGL((gpack_w_kernel<NS>), dim3((unsigned)((nch * 32 * G::JT * 8 + 255) / 256)), dim3(256), 0,
                          s, W, Wp, K);
-      hipLaunchKernelGGL((gproj_partial_dma_kernel<NS>), dim3(pb), dim3(512), (size_t)G::STAGES * G::SB, s,
-                         (const bf16_t *)X, (const bf16_t *)Wp, part, N, K);
+      hipLaunchKernelGGL((gproj_partial_dma_kernel<NS>), dim3(pb), dim3(64 * G::WAVES), (size_t)G::STAGES * G::SB,
+                         s, (const bf16_t *)X, (const bf16_t *)Wp, part, N, K);
     })
   }
   const unsigned fb = (unsigned)((N + 63) / 64);
@@ -2276,7 +2286,8 @@ static void gdx_split(hipStream_t s, const ProjBwdArgs &a, const GBwdLay &L, con
     const int64_t nsp = (a.N + 31) / 32 * 32 * GDw<NS>::JT * 32;
     hipLaunchKernelGGL((gsplit_dp_kernel<NS>), dim3((unsigned)((nsp + 255) / 256)), dim3(256), 0, s, rec, dpT, a.N);
     hipLaunchKernelGGL((gproj_dw_mfma_kernel<NS>), dim3((unsigned)((nkt * L.ntb + 7) / 8 * 8)), dim3(512),
-                       GDw<NS>::STG * GDw<NS>::SB, s, (const bf16_t *)a.X, (const bf16_t *)dpT, dwp, a.N, K, L.tb, L.ntb);
+                       GDw<NS>::STG * GDw<NS>::SB, s, (const bf16_t *)a.X, (const bf16_t *)dpT, dwp, a.N, K, L.tb,
+                       L.ntb);
   }
 }
 
