@@ -612,10 +612,18 @@ __global__ __launch_bounds__(256) void gpost_fwd_kernel(const T *__restrict__ X,
 // token, four waves per workgroup working independently: a lane owns the
 // 8-channel groups g = lane, lane + 64, ..., and the per-token sums are wave
 // reductions (no barrier).  The rows j of X are taken JB at a time, each
-// pass with its own JB * n sums (all rows in one pass up to n = 7, two
-// passes of four at n = 8, G re-read per pass from the caches).  DBIAS: each wave walks TG
+// pass with its own JB * n sums (GPostShape).  DBIAS: each wave walks TG
 // tokens and adds its lanes' dx into its own partial row part[wave][C]
 // (owned by that lane alone: no atomics).
+template <int NS, int MODE> struct GPostShape {
+  // all of X's rows in one pass (G read once) up to n = 7; at n = 8 the
+  // n^2 + n sums take the registers to 256 either way, so two passes of
+  // four rows, on two waves of the same token at once without dbias (the
+  // second G read then comes from L2)
+  static constexpr int JB = NS <= 7 ? NS : 4;
+  static constexpr int NPASS = MODE != kPostDist ? (NS + JB - 1) / JB : 1;
+};
+
 template <typename T, int NS, int MODE>
 __global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr, const T *__restrict__ X,
                                                        const float *__restrict__ Hr, const float *__restrict__ Hp,
@@ -625,20 +633,20 @@ __global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr
                                                        float *__restrict__ part, int64_t N, int64_t C, int TG) {
   const bool HAS_BIAS = bias != nullptr, WRITE_DX = dX != nullptr, DBIAS = part != nullptr;
   constexpr bool MIX = MODE != kPostDist, DIST = MODE != kPostMix;
-  // all of X's rows in one pass (G read once) up to n = 7; at n = 8 the
-  // n^2 + n sums take the registers to 256 either way, and two passes of
-  // four rows measured the same
-  constexpr int JB = NS <= 7 ? NS : 4;
-  constexpr int NPASS = MIX ? (NS + JB - 1) / JB : 1;
+  constexpr int JB = GPostShape<NS, MODE>::JB, NPASS = GPostShape<NS, MODE>::NPASS;
   constexpr int NR = (MIX ? JB * NS : 0) + (DIST ? NS : 0);
   const int lane = threadIdx.x & 63;
   const int64_t wv = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);  // global wave index
+  // without dbias (one token per wave) the passes of a token run on NPASS
+  // consecutive waves of one workgroup
+  const bool split = NPASS > 1 && !DBIAS;
+  const int pass_lo = split ? (int)(wv % NPASS) : 0, pass_hi = split ? pass_lo + 1 : NPASS;
   const int64_t G = C / 8;
-  const int64_t t0 = wv * TG;
+  const int64_t t0 = (split ? wv / NPASS : wv) * TG;
   const int64_t t1 = min(t0 + (int64_t)TG, N);
   for (int64_t t = t0; t < t1; ++t) {
 #pragma unroll 1
-    for (int pass = 0; pass < NPASS; ++pass) {
+    for (int pass = pass_lo; pass < pass_hi; ++pass) {
       const int j0 = pass * JB;
       const bool dist_here = DIST && pass == 0;
       float acc[NR];
@@ -2165,11 +2173,13 @@ static void gpost_bwd5(hipStream_t s, int n, int64_t N, int64_t C, const void *G
                        const float *Hp, const void *x, const void *b, void *dX, float *dHr, float *dHp, void *dx,
                        float *part) {
   const int TG = part ? kGPostTG : 1;
-  const int64_t waves = (N + TG - 1) / TG;  // one wave per TG tokens, four waves per workgroup
-  const unsigned blocks = (unsigned)((waves + 3) / 4);
-  MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gpost_bwd_kernel<T, NS, MODE>), dim3(blocks), dim3(256), 0, s,
-                                        (const T *)G, (const T *)X, Hr, Hp, (const T *)x, (const T *)b, (T *)dX,
-                                        dHr, dHp, (T *)dx, part, N, C, TG));
+  MHC_NS_DISPATCH(n, {
+    // one wave per TG tokens (per pass of a token without dbias), four waves per workgroup
+    const int64_t waves = part ? (N + TG - 1) / TG : N * GPostShape<NS, MODE>::NPASS;
+    const unsigned blocks = (unsigned)((waves + 3) / 4);
+    hipLaunchKernelGGL((gpost_bwd_kernel<T, NS, MODE>), dim3(blocks), dim3(256), 0, s, (const T *)G,
+                       (const T *)X, Hr, Hp, (const T *)x, (const T *)b, (T *)dX, dHr, dHp, (T *)dx, part, N, C, TG);
+  });
 }
 
 template <typename T>
