@@ -628,7 +628,8 @@ def main():
     k_bytes = led["dxdw_kernel"] * N
     k_gbs = k_bytes / (k_ms * 1e-3) / 1e9
     traffic = pmc_traffic("proj_bwd_mfma_full_layer_pmc.txt", ["mhc_hyper_connection_proj_amd/csrc/proj.hip",
-                                                               "mhc_hyper_connection_proj_amd/csrc/device.h"])
+                                                               "mhc_hyper_connection_proj_amd/csrc/device.h",
+                                                               "mhc_hyper_connection_proj_amd/csrc/ring.h"])
     # the h_post_bda backward (one kernel, the whole post_bwd phase), for context
     p_bytes = led["post_bwd"] * N
     p_gbs = p_bytes / (mean["post_bwd"] * 1e-3) / 1e9

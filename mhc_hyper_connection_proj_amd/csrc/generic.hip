@@ -31,6 +31,7 @@
 
 #include "device.h"
 #include "internal.h"
+#include "ring.h"
 
 namespace mhc {
 
@@ -81,46 +82,6 @@ template <> __device__ __forceinline__ void st_one<bf16_t>(bf16_t *p, float v) {
 }
 
 __device__ __forceinline__ float sigm(float v) { return 1.0f / (1.0f + __expf(-v)); }
-
-// LDS DMA rings (the MFMA kernels below): global_load_lds_dwordx4 moves 16
-// bytes per lane to consecutive LDS addresses; each wave waits for its own
-// copies with s_waitcnt vmcnt, then a bare barrier publishes the stage.
-__device__ __forceinline__ void gdma16(const void *g, void *lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
-}
-template <int n>
-__device__ __forceinline__ void gwait_vmcnt() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-// vmcnt <= n for a wave-uniform n (at most 16); otherwise waits for all.
-__device__ __forceinline__ void gwait_vmcnt_le(int n) {
-  switch (n) {
-    case 1: gwait_vmcnt<1>(); break;
-    case 2: gwait_vmcnt<2>(); break;
-    case 3: gwait_vmcnt<3>(); break;
-    case 4: gwait_vmcnt<4>(); break;
-    case 5: gwait_vmcnt<5>(); break;
-    case 6: gwait_vmcnt<6>(); break;
-    case 7: gwait_vmcnt<7>(); break;
-    case 8: gwait_vmcnt<8>(); break;
-    case 9: gwait_vmcnt<9>(); break;
-    case 10: gwait_vmcnt<10>(); break;
-    case 11: gwait_vmcnt<11>(); break;
-    case 12: gwait_vmcnt<12>(); break;
-    case 13: gwait_vmcnt<13>(); break;
-    case 14: gwait_vmcnt<14>(); break;
-    case 15: gwait_vmcnt<15>(); break;
-    case 16: gwait_vmcnt<16>(); break;
-    default: gwait_vmcnt<0>(); break;
-  }
-}
-__device__ __forceinline__ void glds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-__device__ __forceinline__ void gwave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 typedef __attribute__((ext_vector_type(4))) unsigned int gu32x4;
 
@@ -941,7 +902,7 @@ __global__ __launch_bounds__(512) void gproj_partial_dma_kernel(const bf16_t *__
     char *st = gpl + (i % STG) * G::SB;
     const int64_t c = c_begin + i;
     const char *wsrc = reinterpret_cast<const char *>(Wp) + c * G::WB;
-    for (int q = wave; q < QW; q += G::WAVES) gdma16(wsrc + q * 1024 + lane * 16, st + q * 1024);
+    for (int q = wave; q < QW; q += G::WAVES) dma16(wsrc + q * 1024 + lane * 16, st + q * 1024);
     char *xs = st + G::WB + wave * G::XT;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -949,7 +910,7 @@ __global__ __launch_bounds__(512) void gproj_partial_dma_kernel(const bf16_t *__
       const int p = (lane & 7) ^ (rr & 7);  // global 8-k piece for this slot
       const int64_t t = min(tw + rr, N - 1);  // rows past N re-read row N-1 (never stored)
       const int64_t k = c * 64 + 8 * p < K ? c * 64 + 8 * p : c * 64;  // past K: a real k (W is 0 there)
-      gdma16(X + t * K + k, xs + q * 1024);
+      dma16(X + t * K + k, xs + q * 1024);
     }
   };
 
@@ -963,8 +924,8 @@ __global__ __launch_bounds__(512) void gproj_partial_dma_kernel(const bf16_t *__
   if (STG == 3 && nc > 1) issue(1);
   for (int i = 0; i < nc; ++i) {
     // this wave's copies of chunk i are complete once at most those of chunk i + 1 remain
-    if (STG == 3 && i + 1 < nc) gwait_vmcnt_le(nq); else gwait_vmcnt<0>();
-    glds_barrier();
+    if (STG == 3 && i + 1 < nc) wait_vmcnt_le(nq); else wait_vmcnt<0>();
+    lds_barrier();
     if (i + STG - 1 < nc) issue(i + STG - 1);  // that slot was last read in iteration i - 1
     const char *st = gpl + (i % STG) * G::SB;
     const char *xs = st + G::WB + wave * G::XT;
@@ -1372,11 +1333,11 @@ __global__ __launch_bounds__(512) void gproj_bwd_mfma_kernel(
         const int64_t ch = c0 + 8 * slot < C ? c0 + 8 * slot : c0;  // pieces past C: a real channel
         const bf16_t *src = is_g ? gr + tt * C + ch : (q < QX ? X : Gp) + (tt * NS + j) * C + ch;
         char *dst = st + (is_g ? og : q < QX ? 0 : oG) + qq * 1024;
-        gdma16(src, dst);
+        dma16(src, dst);
       } else {
         // records are contiguous; the workspace holds them up to the 32-token padding plus 1 KB
         const int qq = q - QX - QG - Qg;
-        gdma16(reinterpret_cast<const char *>(rec + t0 * RS) + qq * 1024 + lane * 16, st + oR + qq * 1024);
+        dma16(reinterpret_cast<const char *>(rec + t0 * RS) + qq * 1024 + lane * 16, st + oR + qq * 1024);
       }
     }
   };
@@ -1433,8 +1394,8 @@ __global__ __launch_bounds__(512) void gproj_bwd_mfma_kernel(
     if (nsub > 0) issue(0);
     if (nsub > 1) issue(1);
     for (int i = 0; i < nsub; ++i) {
-      if (i + 1 < nsub) gwait_vmcnt_le(nq); else gwait_vmcnt<0>();
-      glds_barrier();
+      if (i + 1 < nsub) wait_vmcnt_le(nq); else wait_vmcnt<0>();
+      lds_barrier();
       if (i + 2 < nsub) issue(i + 2);
       if (DW) {
         const char *st = glds + (i % 3) * SB;
@@ -1501,10 +1462,10 @@ __global__ __launch_bounds__(512) void gproj_bwd_mfma_kernel(
     }
   } else {
     float *acc_t = reinterpret_cast<float *>(glds + 3 * SB) + w4 * 32 * M::AS;
-    gwait_vmcnt<0>();  // W in registers: only the prefetches are pending inside the loop
+    wait_vmcnt<0>();  // W in registers: only the prefetches are pending inside the loop
     prefetch(0);
     for (int i = 0; i < nsub; ++i) {
-      glds_barrier();
+      lds_barrier();
       const char *st = glds + (i % 3) * SB;
       const float *rt = reinterpret_cast<const float *>(st + oR);
       const int64_t t0 = t_begin + 32 * (int64_t)i;
@@ -1529,11 +1490,11 @@ __global__ __launch_bounds__(512) void gproj_bwd_mfma_kernel(
         if (bi == 0) {
           // the prefetched rows, waited for once, after the first MFMAs
           __builtin_amdgcn_sched_barrier(0);
-          gwait_vmcnt<0>();
+          wait_vmcnt<0>();
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_t[(8 * (r >> 2) + 4 * h + (r & 3)) * M::AS + col] = acc[r];
-        gwave_lds_sync();
+        wave_lds_sync();
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr) {
           const int row = er + 16 * rr;
@@ -1593,7 +1554,7 @@ __global__ __launch_bounds__(512) void gproj_bwd_mfma_kernel(
           ow.w = pack_bf16x2(o[6], o[7]);
           *reinterpret_cast<uint4 *>(dX + (t * NS + j) * C + ch) = ow;
         }
-        gwave_lds_sync();  // the accumulator tile's reads precede the next block's writes
+        wave_lds_sync();  // the accumulator tile's reads precede the next block's writes
       }
       if (i + 1 < nsub) prefetch(i + 1);
     }
@@ -1630,7 +1591,10 @@ typedef __attribute__((ext_vector_type(4))) float gf32x4;
 // dp split once per call into its three exact bf16 terms, transposed per
 // 32-token sub-tile: dpT[sub][term][column (32 JT, zero past J)][32 tokens]
 // (zero for tokens past N), so a dW B fragment (8 tokens of one column) is
-// one 16-byte read.  Thread = (sub-tile, column, token), tokens fastest.
+// one 16-byte read.  In each column's 64-byte row the 8-token group p sits in
+// slot p ^ ((column >> 2) & 3): the 32 columns one read takes then spread
+// over the banks (rows 64 bytes apart would put 8 of them on each bank).
+// Thread = (sub-tile, column, token), tokens fastest.
 template <int NS>
 __global__ __launch_bounds__(256) void gsplit_dp_kernel(const float *__restrict__ rec, bf16_t *__restrict__ dpT,
                                                        int64_t N) {
@@ -1647,7 +1611,8 @@ __global__ __launch_bounds__(256) void gsplit_dp_kernel(const float *__restrict_
 #pragma unroll
   for (int m = 0; m < 3; ++m) {
     const __bf16 b = (__bf16)terms[m];
-    dpT[((sb * 3 + m) * 32 * JT + jj) * 32 + tok] = __builtin_bit_cast(uint16_t, b);
+    dpT[((sb * 3 + m) * 32 * JT + jj) * 32 + 8 * ((tok >> 3) ^ ((jj >> 2) & 3)) + (tok & 7)] =
+        __builtin_bit_cast(uint16_t, b);
   }
 }
 
@@ -1700,10 +1665,10 @@ __global__ __launch_bounds__(512) void gproj_dw_mfma_kernel(const bf16_t *__rest
         const int p = slot ^ (4 * ((t >> 3) & 1));
         const int64_t tt = min(t0 + t, N - 1);  // rows past N re-read row N-1 (their dp terms are 0)
         const int64_t k = k0 + 8 * p < K ? k0 + 8 * p : k0;
-        gdma16(X + tt * K + k, st + q * 1024);
+        dma16(X + tt * K + k, st + q * 1024);
       } else {
         const int qq = q - QX;
-        gdma16(reinterpret_cast<const char *>(dpT) + (t0 / 32) * M::DB + qq * 1024 + lane * 16,
+        dma16(reinterpret_cast<const char *>(dpT) + (t0 / 32) * M::DB + qq * 1024 + lane * 16,
                st + M::XB + qq * 1024);
       }
     }
@@ -1719,8 +1684,8 @@ __global__ __launch_bounds__(512) void gproj_dw_mfma_kernel(const bf16_t *__rest
   // in sub-tile i - 1, so only sub-tile i's copies are outstanding at its wait
   if (nsub > 0) issue(0);
   for (int i = 0; i < nsub; ++i) {
-    gwait_vmcnt<0>();
-    glds_barrier();
+    wait_vmcnt<0>();
+    lds_barrier();
     if (i + 1 < nsub) issue(i + 1);
     const char *st = gdl + (i % M::STG) * M::SB;
     const char *dt = st + M::XB;
@@ -1739,8 +1704,8 @@ __global__ __launch_bounds__(512) void gproj_dw_mfma_kernel(const bf16_t *__rest
       for (int m = 0; m < 3; ++m)
 #pragma unroll
         for (int u = 0; u < JT; ++u) {
-          const gu32x4 bw =
-              *reinterpret_cast<const gu32x4 *>(dt + ((m * 32 * JT + 32 * u + col) * 32 + 16 * s + 8 * h) * 2);
+          const int slot = (2 * s + h) ^ ((col >> 2) & 3);  // token group 2s + h of column 32u + col
+          const gu32x4 bw = *reinterpret_cast<const gu32x4 *>(dt + ((m * 32 * JT + 32 * u + col) * 32 + 8 * slot) * 2);
           accW[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(gbf16x8, xa),
                                                             __builtin_bit_cast(gbf16x8, bw), accW[u], 0, 0, 0);
         }
@@ -1826,11 +1791,11 @@ __global__ __launch_bounds__(768) void gproj_dx16_mfma_kernel(
         const int64_t tt = min(t0 + t, N - 1);  // rows past N re-read row N-1 (never stored)
         const int64_t ch = c0 + 8 * p < C ? c0 + 8 * p : c0;  // pieces past C: a real channel
         const bf16_t *src = is_g ? gr + tt * C + ch : (q < QX ? X : Gp) + (tt * NS + j) * C + ch;
-        gdma16(src, st + (is_g ? og : q < QX ? 0 : oG) + qq * 1024);
+        dma16(src, st + (is_g ? og : q < QX ? 0 : oG) + qq * 1024);
       } else {
         // records: contiguous, padded to whole 32-token sub-tiles plus 1 KB
         const int qq = q - QX - QG - Qg;
-        gdma16(reinterpret_cast<const char *>(rec + t0 * RS) + qq * 1024 + lane * 16, st + oR + qq * 1024);
+        dma16(reinterpret_cast<const char *>(rec + t0 * RS) + qq * 1024 + lane * 16, st + oR + qq * 1024);
       }
     }
   };
@@ -1875,18 +1840,18 @@ __global__ __launch_bounds__(768) void gproj_dx16_mfma_kernel(
     if (nsub > 0) issue(0);
     if (nsub > 1) issue(1);
     for (int i = 0; i < nsub; ++i) {
-      if (i + 1 < nsub) gwait_vmcnt_le(nq); else gwait_vmcnt<0>();
-      glds_barrier();
+      if (i + 1 < nsub) wait_vmcnt_le(nq); else wait_vmcnt<0>();
+      lds_barrier();
       if (i + 2 < nsub) issue(i + 2);
     }
   } else if (!active) {
-    for (int i = 0; i < nsub; ++i) glds_barrier();
+    for (int i = 0; i < nsub; ++i) lds_barrier();
   } else {
     float *acc_t = reinterpret_cast<float *>(gxl + 3 * SB) + wave * 16 * M::AS;
-    gwait_vmcnt<0>();  // W in registers: only the prefetches are pending inside the loop
+    wait_vmcnt<0>();  // W in registers: only the prefetches are pending inside the loop
     prefetch(0);
     for (int i = 0; i < nsub; ++i) {
-      glds_barrier();
+      lds_barrier();
       const char *st = gxl + (i % 3) * SB;
       const float *rt = reinterpret_cast<const float *>(st + oR);
       const int64_t t0 = t_begin + 16 * (int64_t)i;
@@ -1913,8 +1878,8 @@ __global__ __launch_bounds__(768) void gproj_dx16_mfma_kernel(
         for (int r = 0; r < 4; ++r) acc_t[(4 * gq + r) * M::AS + 16 * bi + cl] = acc[bi][r];
       // the prefetched rows, waited for once, after the MFMAs
       __builtin_amdgcn_sched_barrier(0);
-      gwait_vmcnt<0>();
-      gwave_lds_sync();
+      wait_vmcnt<0>();
+      wave_lds_sync();
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
         const int row = er + 8 * rr;
@@ -1971,7 +1936,7 @@ __global__ __launch_bounds__(768) void gproj_dx16_mfma_kernel(
         ow.w = pack_bf16x2(o[6], o[7]);
         *reinterpret_cast<uint4 *>(dX + (t * NS + j) * C + ch) = ow;
       }
-      gwave_lds_sync();  // the accumulator tile's reads precede the next sub-tile's writes
+      wave_lds_sync();  // the accumulator tile's reads precede the next sub-tile's writes
       if (i + 1 < nsub) prefetch(i + 1);
     }
   }

@@ -25,6 +25,7 @@
 //    v_dot2_f32_bf16 with the same blocking.
 #include "device.h"
 #include "internal.h"
+#include "ring.h"
 #include "sinkhorn.h"
 
 namespace mhc {
@@ -240,23 +241,6 @@ constexpr int kDmaStages = 3;
 constexpr int kWChunk = 8 * 3 * kWcol * 8;   // bf16 elements per 64-k W chunk (12 KB)
 constexpr int kXTile = 32 * 64;              // bf16 elements per wave X tile (4 KB)
 constexpr int kStageElems = kWChunk + kDmaWaves * kXTile;
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ __forceinline__ void dma16(const void *g, void *lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds_base, 16, 0, 0);
-}
-// The same with the non-temporal cache policy, for a stream read once.
-__device__ __forceinline__ void dma16_nt(const void *g, void *lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds_base, 16, 0, 2);
-}
-
-// s_waitcnt with vmcnt <= n (expcnt and lgkmcnt left unconstrained).
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 __global__ __launch_bounds__(512) void proj_partial_dma_kernel(const bf16_t *__restrict__ X,
                                                                const bf16_t *__restrict__ Wp,
@@ -863,37 +847,6 @@ struct B2Lay {
 // chunk c lane half h takes the 8 j of group (2c + h) % 3 of pair (2c + h) / 3.
 __constant__ constexpr int kPairA[6] = {0, 0, 1, 0, 2, 1};  // dp term of each pair
 __constant__ constexpr int kPairB[6] = {0, 1, 0, 2, 0, 1};  // W term of each pair
-
-// vmcnt <= n for a wave-uniform n; a value outside the table waits for all.
-__device__ __forceinline__ void wait_vmcnt_le(int n) {
-  switch (n) {
-    case 1: wait_vmcnt<1>(); break;
-    case 2: wait_vmcnt<2>(); break;
-    case 3: wait_vmcnt<3>(); break;
-    case 4: wait_vmcnt<4>(); break;
-    case 5: wait_vmcnt<5>(); break;
-    case 6: wait_vmcnt<6>(); break;
-    case 7: wait_vmcnt<7>(); break;
-    case 8: wait_vmcnt<8>(); break;
-    case 9: wait_vmcnt<9>(); break;
-    case 10: wait_vmcnt<10>(); break;
-    case 11: wait_vmcnt<11>(); break;
-    case 12: wait_vmcnt<12>(); break;
-    default: wait_vmcnt<0>(); break;
-  }
-}
-
-// LDS reads done, then a workgroup barrier.  The memory clobber keeps the
-// compiler from moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Orders this wave's LDS writes before its following LDS reads (the region
-// is private to the wave, so no workgroup barrier is needed).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // Per-lane inputs of one sub-tile's dX epilogue, for rows er + 8q: dX_in,
 // H_pre and the row's H_res row.
