@@ -302,22 +302,59 @@ inline SkBwdGeom sk_bwd_geom(int n, int iters) {
   return {64, false, 0};
 }
 
-// Row per lane: the same gradient with token i's n rows on n lanes of a
-// group of GW = n rounded up to a power of two (lanes past n hold zeros and
-// only join the shuffles).  A row pass is in-lane; in a column pass each lane
-// reads column b of every row of its group by shuffles and takes the sums
-// and the half-step backward in the per-token form's order, so the result
-// is the per-token stored form's, operation for operation.  Lane a records e
-// of its row (row pass) or of column a (column pass) for every half-step, and
-// its row at every kSkCkpt-th half-step, in its own LDS slots (word w at
-// lds[w * blockDim]).
+// Row per lane (n >= 3): token i's matrix on a group of GW = n rounded up
+// to a power of two lanes, each lane holding one line rotated by its lane
+// index a: in the row layout v[c] = M[a][(a + c) % GW], in the column layout
+// v[k] = M[(a + k) % GW][a] (entries past n are zero, lanes a >= n hold
+// zeros).  A row pass sums and scales in-lane in the row layout, a column
+// pass in-lane in the column layout, and sk_rotate turns either layout into
+// the other with GW shuffles whose source register is the same on every lane
+// (lane a reads lane (a + k) % GW's v[(GW - k) % GW]).  Every line sum runs
+// in the rotated order (line a from entry a on), so every path that uses
+// these functions (the fused finalize, the batched forward) gives the same
+// bits for the same logits.
 constexpr int sk_group(int n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8; }
 
-inline size_t sk_lane_words(int n, int iters) {
-  const int H = 2 * iters;
-  return (size_t)H + (size_t)((H + kSkCkpt - 1) / kSkCkpt) * n;
+template <int GW>
+__device__ __forceinline__ void sk_rotate(float v[GW], int a, int base) {
+  float o[GW];
+#pragma unroll
+  for (int k = 0; k < GW; ++k) o[k] = __shfl(v[(GW - k) & (GW - 1)], base + ((a + k) & (GW - 1)), 64);
+#pragma unroll
+  for (int k = 0; k < GW; ++k) v[k] = o[k];
 }
 
+// 2 iters half-steps on the row layout (act: lane a < n of a real token);
+// the state ends in the row layout.
+template <int NS>
+__device__ __forceinline__ void sk_forward_lanes(float v[sk_group(NS)], int a, int base, bool act, int iters,
+                                                 float eps) {
+  constexpr int GW = sk_group(NS);
+  for (int h = 0; h < 2 * iters; ++h) {
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < GW; ++c) s += v[c];
+    const float d = act ? 1.0f / (s + eps) : 0.f;
+#pragma unroll
+    for (int c = 0; c < GW; ++c) v[c] *= d;
+    sk_rotate<GW>(v, a, base);
+  }
+}
+
+// Lanes records of the backward: e of the lane's line for every half-step,
+// and the lane's row every kSkCkpt-th half-step.
+inline size_t sk_lane_words(int n, int iters) {
+  const int H = 2 * iters;
+  return (size_t)H + (size_t)((H + kSkCkpt - 1) / kSkCkpt) * sk_group(n);
+}
+
+// The gradient on the lanes layout: the forward records each half-step's
+// line sum (+ eps) and the state every kSkCkpt half-steps in the lane's own
+// LDS slots (word w at lds[w * blockDim]); the reverse walk turns m (the
+// half-step's output) and dm into the half-step's layout, applies the
+// half-step backward in-lane with d = 1/e (the forward's reciprocal,
+// recomputed bit-identically) and rebuilds the input as m e, restarting from
+// the exact recorded state at every checkpoint.
 template <int NS>
 __global__ __launch_bounds__(256) void gsinkhorn_bwd_lanes_kernel(int64_t count, const float *__restrict__ dH,
                                                                  const float *__restrict__ L,
@@ -332,79 +369,83 @@ __global__ __launch_bounds__(256) void gsinkhorn_bwd_lanes_kernel(int64_t count,
   const bool act = a < NS && i < count;
   const int H = 2 * iters;
   float *ck = my + (size_t)H * T;
-  float m[NS], dm[NS];
+  // real[c]: entry c of the lane's line is a matrix entry (the same test in both layouts)
+  bool real[GW];
+  float m[GW], dm[GW];
 #pragma unroll
-  for (int b = 0; b < NS; ++b) {
-    m[b] = act ? __expf(L[(i * NS + a) * NS + b]) : 0.f;
-    dm[b] = act ? dH[(i * NS + a) * NS + b] : 0.f;
+  for (int c = 0; c < GW; ++c) {
+    const int col = (a + c) & (GW - 1);
+    real[c] = act && col < NS;
+    m[c] = real[c] ? __expf(L[(i * NS + a) * NS + col]) : 0.f;
+    dm[c] = real[c] ? dH[(i * NS + a) * NS + col] : 0.f;
   }
-  // forward, recording line sums (+ eps) and checkpoints
   for (int h = 0; h < H; ++h) {
     if (h % kSkCkpt == 0) {
 #pragma unroll
-      for (int b = 0; b < NS; ++b) ck[((h / kSkCkpt) * NS + b) * T] = m[b];
+      for (int c = 0; c < GW; ++c) ck[((h / kSkCkpt) * GW + c) * T] = m[c];
     }
-    if ((h & 1) == 0) {
-      float sum = 0.f;
+    float s = 0.f;
 #pragma unroll
-      for (int b = 0; b < NS; ++b) sum += m[b];
-      const float e = sum + eps;
-      my[h * T] = e;
-      const float d = act ? 1.0f / e : 0.f;
+    for (int c = 0; c < GW; ++c) s += m[c];
+    const float e = s + eps;
+    my[h * T] = e;
+    const float d = act ? 1.0f / e : 0.f;
 #pragma unroll
-      for (int b = 0; b < NS; ++b) m[b] *= d;
-    } else {
-      float mine = 0.f;
-#pragma unroll
-      for (int b = 0; b < NS; ++b) {
-        float sum = 0.f;
-#pragma unroll
-        for (int r = 0; r < NS; ++r) sum += __shfl(m[b], base + r, 64);
-        const float e = sum + eps;
-        if (b == a) mine = e;
-        m[b] *= act ? 1.0f / e : 0.f;
-      }
-      my[h * T] = mine;
-    }
+    for (int c = 0; c < GW; ++c) m[c] *= d;
+    sk_rotate<GW>(m, a, base);
   }
-  // reverse walk: m holds the output of half-step h
+  // m: the output of half-step H - 1 and dm its gradient, both in the row
+  // layout; each step below turns them into half-step h's layout first
   for (int h = H - 1; h >= 0; --h) {
-    if ((h + 1) % kSkCkpt == 0 && h + 1 < H) {
+    if ((h + 1) % kSkCkpt == 0 && h + 1 < H) {  // exact state after half-step h (row layout)
 #pragma unroll
-      for (int b = 0; b < NS; ++b) m[b] = ck[(((h + 1) / kSkCkpt) * NS + b) * T];
+      for (int c = 0; c < GW; ++c) m[c] = ck[(((h + 1) / kSkCkpt) * GW + c) * T];
     }
-    const float er = my[h * T];
-    if ((h & 1) == 0) {
-      const float d = act ? 1.0f / er : 0.f;
-      float o[NS];
+    sk_rotate<GW>(m, a, base);
+    sk_rotate<GW>(dm, a, base);
+    const float e = my[h * T];
+    const float d = act ? 1.0f / e : 0.f;
+    float o[GW];
 #pragma unroll
-      for (int b = 0; b < NS; ++b) {
-        float acc = dm[b] * (eps * d);
+    for (int c = 0; c < GW; ++c) {
+      float acc = dm[c] * (eps * d);
 #pragma unroll
-        for (int bp = 0; bp < NS; ++bp) acc += (dm[b] - dm[bp]) * m[bp];
-        o[b] = d * acc;
-      }
+      for (int cp = 0; cp < GW; ++cp) acc += (dm[c] - dm[cp]) * m[cp];
+      o[c] = real[c] ? d * acc : 0.f;
+    }
 #pragma unroll
-      for (int b = 0; b < NS; ++b) {
-        dm[b] = o[b];
-        m[b] *= act ? er : 0.f;
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < NS; ++b) {
-        const float e = __shfl(er, base + b, 64);  // column b's e, recorded by lane b of the group
-        const float d = act ? 1.0f / e : 0.f;
-        float acc = dm[b] * (eps * d);
-#pragma unroll
-        for (int r = 0; r < NS; ++r) acc += (dm[b] - __shfl(dm[b], base + r, 64)) * __shfl(m[b], base + r, 64);
-        dm[b] = d * acc;
-        m[b] *= act ? e : 0.f;
-      }
+    for (int c = 0; c < GW; ++c) {
+      dm[c] = o[c];
+      m[c] *= act ? e : 0.f;
     }
   }
-  if (act) {
 #pragma unroll
-    for (int b = 0; b < NS; ++b) dL[(i * NS + a) * NS + b] = dm[b] * __expf(L[(i * NS + a) * NS + b]);
+  for (int c = 0; c < GW; ++c) {
+    const int col = (a + c) & (GW - 1);
+    if (real[c]) dL[(i * NS + a) * NS + col] = dm[c] * __expf(L[(i * NS + a) * NS + col]);
+  }
+}
+
+// The forward on the lanes layout (n >= 3).
+template <int NS>
+__global__ __launch_bounds__(256) void gsinkhorn_fwd_lanes_kernel(int64_t count, const float *__restrict__ L,
+                                                                 float *__restrict__ H, int iters, float eps) {
+  constexpr int GW = sk_group(NS);
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) / GW;
+  const int a = threadIdx.x % GW;
+  const int base = (threadIdx.x & 63) - a;
+  const bool act = a < NS && i < count;
+  float v[GW];
+#pragma unroll
+  for (int c = 0; c < GW; ++c) {
+    const int col = (a + c) & (GW - 1);
+    v[c] = act && col < NS ? __expf(L[(i * NS + a) * NS + col]) : 0.f;
+  }
+  sk_forward_lanes<NS>(v, a, base, act, iters, eps);
+#pragma unroll
+  for (int c = 0; c < GW; ++c) {
+    const int col = (a + c) & (GW - 1);
+    if (act && col < NS) H[(i * NS + a) * NS + col] = v[c];
   }
 }
 
@@ -521,6 +562,49 @@ __global__ __launch_bounds__(256) void gcol_sum_kernel(const float *__restrict__
   for (int64_t r = threadIdx.x; r < R; r += 256) s[0] += rows[r * NC + col];
   gblock_sum<1>(s, red);
   if (threadIdx.x == 0) out[col] = s[0];
+}
+
+// Sums over tokens of the per-token parameter terms rows[R][NC] (dhbias and
+// dalpha of the projection backward), in two fixed-order stages.  Stage 1:
+// thread i adds column i % NC over rows i / NC + kGParts m, m = 0, 1, ... in
+// order, so consecutive threads read consecutive floats.
+constexpr int kGParts = 1024;
+
+__global__ __launch_bounds__(256) void gparam_part_kernel(const float *__restrict__ rows, float *__restrict__ part,
+                                                         int64_t R, int NC) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)kGParts * NC) return;
+  float s = 0.f;
+#pragma unroll 8
+  for (int64_t f = i; f < R * NC; f += (int64_t)kGParts * NC) s += rows[f];
+  part[i] = s;
+}
+
+// Stage 2: per column, 32 lanes each add every 32nd of the kGParts partials
+// in order, then a pairwise tree over the 32; columns [0, J) go to dhbias,
+// [J, J + 3) to dalpha (either may be NULL).
+__global__ __launch_bounds__(1024) void gparam_final_kernel(const float *__restrict__ part, int NC, int J,
+                                                           float *__restrict__ dhbias, float *__restrict__ dalpha) {
+  __shared__ float red[32][33];
+  const int e = threadIdx.x & 31, q = threadIdx.x >> 5;
+  const int col = blockIdx.x * 32 + e;
+  float s = 0.f;
+  if (col < NC) {
+#pragma unroll 4
+    for (int p = q; p < kGParts; p += 32) s += part[(int64_t)p * NC + col];
+  }
+  red[q][e] = s;
+  __syncthreads();
+  for (int w = 16; w > 0; w >>= 1) {
+    if (q < w) red[q][e] += red[q + w][e];
+    __syncthreads();
+  }
+  if (q != 0 || col >= NC) return;
+  if (col < J) {
+    if (dhbias) dhbias[col] = red[0][e];
+  } else if (dalpha) {
+    dalpha[col - J] = red[0][e];
+  }
 }
 
 // h_post_bda forward and its halves (modes as the n = 4 kernels).
@@ -1036,6 +1120,86 @@ __global__ __launch_bounds__(64) void gproj_finalize_kernel(const float *__restr
     sk_forward<NS>(L, m, iters, eps);
 #pragma unroll
     for (int e = 0; e < NS * NS; ++e) Hres[t * NS * NS + e] = m[e];
+  }
+}
+
+// The same for n >= 3 on GW = sk_group(n) lanes per token: lane a < n sums
+// the slices of its entries (H_pre a, H_post a, logits row a) in slice order,
+// every lane the sum of squares (so all lanes hold the same r), and the
+// Sinkhorn runs on the lanes layout, as the batched forward does.
+template <int NS>
+__global__ __launch_bounds__(256) void gproj_finalize_lanes_kernel(
+    const float *__restrict__ part, int64_t N, int64_t K, const float *__restrict__ alpha,
+    const float *__restrict__ hbias, float rms_eps, float *__restrict__ Hpre, float *__restrict__ Hpost,
+    float *__restrict__ logits, float *__restrict__ saved, int SS, float *__restrict__ Hres, int iters, float eps) {
+  constexpr int J = Dim<NS>::J, PS = Dim<NS>::PS, GW = sk_group(NS);
+  const int64_t t = ((int64_t)blockIdx.x * 256 + threadIdx.x) / GW;
+  const int a = threadIdx.x % GW;
+  const int base = (threadIdx.x & 63) - a;
+  const bool tv = t < N;
+  const bool act = tv && a < NS;
+  const int64_t tt = tv ? t : N - 1;  // lanes past N compute on a real row and store nothing
+  const int ar = a < NS ? a : 0;      // lanes a >= n likewise
+  // p[0] = H_pre column a, p[1] = H_post column a, p[2 + b] = logit (a, b)
+  float ss = 0.f, p[NS + 2];
+#pragma unroll
+  for (int e = 0; e < NS + 2; ++e) p[e] = 0.f;
+  for (int sl = 0; sl < kGSplitK; ++sl) {
+    const float *pr = part + ((int64_t)sl * N + tt) * PS;
+    ss += pr[J];
+    p[0] += pr[ar];
+    p[1] += pr[NS + ar];
+#pragma unroll
+    for (int b = 0; b < NS; ++b) p[2 + b] += pr[2 * NS + ar * NS + b];
+  }
+  const float q = sqrtf(ss / (float)K);
+  const float r = 1.0f / (q + rms_eps);
+  const float a0 = alpha ? alpha[0] : 1.f, a1 = alpha ? alpha[1] : 1.f, a2 = alpha ? alpha[2] : 1.f;
+  float L[NS];
+  {
+    const float z0 = r * p[0], z1 = r * p[1];
+    const float zh0 = a0 * z0 + (hbias ? hbias[ar] : 0.f);
+    const float zh1 = a1 * z1 + (hbias ? hbias[NS + ar] : 0.f);
+    if (act) {
+      Hpre[t * NS + a] = sigm(zh0);
+      Hpost[t * NS + a] = 2.0f * sigm(zh1);
+      if (saved) {
+        saved[t * SS + 2 + a] = z0;
+        saved[t * SS + 2 + NS + a] = z1;
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NS; ++b) {
+      const int j = 2 * NS + ar * NS + b;
+      const float z = r * p[2 + b];
+      L[b] = a2 * z + (hbias ? hbias[j] : 0.f);
+      if (act) {
+        logits[t * NS * NS + a * NS + b] = L[b];
+        if (saved) saved[t * SS + 2 + j] = z;
+      }
+    }
+  }
+  if (saved && tv && a == 0) {
+    saved[t * SS + 0] = r;
+    saved[t * SS + 1] = q;
+    for (int j = 2 + J; j < SS; ++j) saved[t * SS + j] = 0.f;
+  }
+  if (Hres) {
+    float v[GW];
+#pragma unroll
+    for (int c = 0; c < GW; ++c) {
+      const int col = (a + c) & (GW - 1);
+      float x = 0.f;
+#pragma unroll
+      for (int b = 0; b < NS; ++b) x = b == col ? L[b] : x;
+      v[c] = act && col < NS ? __expf(x) : 0.f;
+    }
+    sk_forward_lanes<NS>(v, a, base, act, iters, eps);
+#pragma unroll
+    for (int c = 0; c < GW; ++c) {
+      const int col = (a + c) & (GW - 1);
+      if (act && col < NS) Hres[(t * NS + a) * NS + col] = v[c];
+    }
   }
 }
 
@@ -1973,7 +2137,7 @@ inline size_t al256(size_t b) { return (b + 255) / 256 * 256; }
 
 struct GBwdLay {
   int64_t ntb, tb;
-  size_t rec, prm, dw, dhrow, term, dl, dpt, total;
+  size_t rec, prm, dw, dhrow, term, dl, dpt, psum, total;
 };
 
 // Backward record stride (floats) for a run-time n: Dim<n>::RS.
@@ -2012,7 +2176,8 @@ GBwdLay gbwd_layout(int64_t N, int64_t C, int n, bool terms, bool f32) {
   L.dl = al256((size_t)N * n * n * 4);  // the logits' gradient when the row-per-lane Sinkhorn backward forms it
   // bf16, n >= 5: dp's bf16 terms transposed per 32-token sub-tile for the dW kernel
   L.dpt = !f32 && n >= 5 ? al256((size_t)(N + 31) / 32 * 3 * 32 * ((J + 31) / 32) * 64) : 0;
-  L.total = L.rec + L.prm + L.dw + L.dhrow + L.term + L.dl + L.dpt;
+  L.psum = al256((size_t)kGParts * (J + 3) * 4);  // stage-1 partials of the parameter sums
+  L.total = L.rec + L.prm + L.dw + L.dhrow + L.term + L.dl + L.dpt + L.psum;
   return L;
 }
 
@@ -2025,6 +2190,12 @@ int saved_stride(int n) {
 }
 
 void glaunch_sinkhorn_fwd(hipStream_t s, int n, int64_t count, const float *L, float *H, int iters, float eps) {
+  if (n >= 3) {  // the lanes layout, as the fused finalize
+    const unsigned b = (unsigned)((count * sk_group(n) + 255) / 256);
+    MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gsinkhorn_fwd_lanes_kernel<NS>), dim3(b), dim3(256), 0, s, count, L, H,
+                                          iters, eps));
+    return;
+  }
   const unsigned b = (unsigned)((count + 63) / 64);
   MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gsinkhorn_fwd_kernel<NS>), dim3(b), dim3(64), 0, s, count, L, H, iters,
                                         eps));
@@ -2216,6 +2387,13 @@ void glaunch_proj_fwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, cons
                          s, (const bf16_t *)X, (const bf16_t *)Wp, part, N, K);
     })
   }
+  if (n >= 3) {
+    const unsigned fb = (unsigned)((N * sk_group(n) + 255) / 256);
+    MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_finalize_lanes_kernel<NS>), dim3(fb), dim3(256), 0, s, part, N, K,
+                                          alpha, hbias, rms_eps, H_pre, H_post, logits, saved, saved_stride(n),
+                                          H_res, iters, eps));
+    return;
+  }
   const unsigned fb = (unsigned)((N + 63) / 64);
   MHC_NS_DISPATCH(n, hipLaunchKernelGGL((gproj_finalize_kernel<NS>), dim3(fb), dim3(64), 0, s, part, N, K, alpha,
                                         hbias, rms_eps, H_pre, H_post, logits, saved, saved_stride(n), H_res,
@@ -2346,10 +2524,14 @@ void glaunch_proj_bwd(hipStream_t s, int n, const ProjBwdArgs &a) {
     hipLaunchKernelGGL(gdw_reduce_kernel, dim3((unsigned)((K * J + 255) / 256)), dim3(256), 0, s, dwp, a.dW, L.ntb,
                        K * J);
   // parameter sums: columns 0..J-1 of prm are dhbias terms, J..J+2 dalpha terms
-  if (a.dhbias)
-    hipLaunchKernelGGL(gcol_sum_kernel, dim3((unsigned)J), dim3(256), 0, s, prm, a.dhbias, a.N, (int)(J + 3));
-  if (a.dalpha)
-    hipLaunchKernelGGL(gcol_sum_kernel, dim3(3u), dim3(256), 0, s, prm + J, a.dalpha, a.N, (int)(J + 3));
+  if (a.dhbias || a.dalpha) {
+    const int NC = (int)(J + 3);
+    float *part = (float *)(base + L.rec + L.prm + L.dw + L.dhrow + L.term + L.dl + L.dpt);
+    hipLaunchKernelGGL(gparam_part_kernel, dim3((unsigned)((kGParts * NC + 255) / 256)), dim3(256), 0, s, prm, part,
+                       a.N, NC);
+    hipLaunchKernelGGL(gparam_final_kernel, dim3((unsigned)((NC + 31) / 32)), dim3(1024), 0, s, part, NC, (int)J,
+                       a.dhbias, a.dalpha);
+  }
 }
 
 }  // namespace mhc
