@@ -660,7 +660,7 @@ __global__ __launch_bounds__(256) void gpost_fwd_kernel(const T *__restrict__ X,
 // pass with its own JB * n sums (GPostShape).  DBIAS: each wave walks TG
 // tokens and adds its lanes' dx into its own partial row part[wave][C]
 // (owned by that lane alone: no atomics).
-template <int NS, int MODE> struct GPostShape {
+template <typename T, int NS, int MODE> struct GPostShape {
   // all of X's rows in one pass (G read once) up to n = 7; at n = 8 the
   // n^2 + n sums take the registers to 256 either way, so two passes of
   // four rows, on two waves of the same token at once without dbias (the
@@ -678,7 +678,7 @@ __global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr
                                                        float *__restrict__ part, int64_t N, int64_t C, int TG) {
   const bool HAS_BIAS = bias != nullptr, WRITE_DX = dX != nullptr, DBIAS = part != nullptr;
   constexpr bool MIX = MODE != kPostDist, DIST = MODE != kPostMix;
-  constexpr int JB = GPostShape<NS, MODE>::JB, NPASS = GPostShape<NS, MODE>::NPASS;
+  constexpr int JB = GPostShape<T, NS, MODE>::JB, NPASS = GPostShape<T, NS, MODE>::NPASS;
   constexpr int NR = (MIX ? JB * NS : 0) + (DIST ? NS : 0);
   const int lane = threadIdx.x & 63;
   const int64_t wv = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);  // global wave index
@@ -698,6 +698,78 @@ __global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr
 #pragma unroll
       for (int r = 0; r < NR; ++r) acc[r] = 0.f;
       for (int64_t g = lane; g < G; g += 64) {
+        if constexpr (sizeof(T) == 2) {
+          // bf16: G rows stay packed; dot products as bf16 pairs, other terms converted where used
+          gu32x4 gw[NS];
+#pragma unroll
+          for (int i = 0; i < NS; ++i) gw[i] = *reinterpret_cast<const gu32x4 *>(Gr + (t * NS + i) * C + 8 * g);
+          auto gval = [&](int i, int e) {
+            const uint32_t w = (e >> 1) == 0 ? gw[i].x : (e >> 1) == 1 ? gw[i].y : (e >> 1) == 2 ? gw[i].z : gw[i].w;
+            return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+          };
+          // the dwords go through plain variables: bit-casting ext-vector
+          // elements directly has been lowered with dword 0 in every position
+          typedef __attribute__((ext_vector_type(2))) __bf16 pbf16x2;
+          auto dot8 = [&](const gu32x4 &u, const gu32x4 &v, float a) {
+            const uint32_t uw[4] = {u.x, u.y, u.z, u.w}, vw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(pbf16x2, uw[q]), __builtin_bit_cast(pbf16x2, vw[q]),
+                                                  a, false);
+            return a;
+          };
+          if (MIX) {
+#pragma unroll
+            for (int jj = 0; jj < JB; ++jj) {
+              const int j = j0 + jj;
+              if (j < NS) {
+                const gu32x4 xw = *reinterpret_cast<const gu32x4 *>(X + (t * NS + j) * C + 8 * g);
+#pragma unroll
+                for (int i = 0; i < NS; ++i) acc[jj * NS + i] = dot8(xw, gw[i], acc[jj * NS + i]);
+                if (WRITE_DX) {
+                  float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                  for (int i = 0; i < NS; ++i) {
+                    const float w = Hr[t * NS * NS + j * NS + i];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) d[e] += w * gval(i, e);
+                  }
+                  Io8<T>::store(dX + (t * NS + j) * C + 8 * g, d);
+                }
+              }
+            }
+          }
+          if (DIST && dist_here) {
+            constexpr int off = MIX ? JB * NS : 0;
+            float xb[8], o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            Io8<T>::load(x + t * C + 8 * g, xb);
+            if (HAS_BIAS) {
+              float bv[8];
+              Io8<T>::load(bias + 8 * g, bv);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) xb[e] += bv[e];
+            }
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+              const float hp = Hp[t * NS + i];
+              float sdot = 0.f;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const float gvi = gval(i, e);
+                sdot += gvi * xb[e];
+                o[e] += hp * gvi;
+              }
+              acc[off + i] += sdot;
+            }
+            Io8<T>::store(dx + t * C + 8 * g, o);
+            if (DBIAS) {
+              float *p = part + wv * C + 8 * g;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) p[e] = (t == t0 ? 0.f : p[e]) + o[e];
+            }
+          }
+          continue;
+        }
         float gv[NS][8];
 #pragma unroll
         for (int i = 0; i < NS; ++i) Io8<T>::load(Gr + (t * NS + i) * C + 8 * g, gv[i]);
@@ -2311,7 +2383,7 @@ static void gpost_bwd5(hipStream_t s, int n, int64_t N, int64_t C, const void *G
   const int TG = part ? kGPostTG : 1;
   MHC_NS_DISPATCH(n, {
     // one wave per TG tokens (per pass of a token without dbias), four waves per workgroup
-    const int64_t waves = part ? (N + TG - 1) / TG : N * GPostShape<NS, MODE>::NPASS;
+    const int64_t waves = part ? (N + TG - 1) / TG : N * GPostShape<T, NS, MODE>::NPASS;
     const unsigned blocks = (unsigned)((waves + 3) / 4);
     hipLaunchKernelGGL((gpost_bwd_kernel<T, NS, MODE>), dim3(blocks), dim3(256), 0, s, (const T *)G,
                        (const T *)X, Hr, Hp, (const T *)x, (const T *)b, (T *)dX, dHr, dHp, (T *)dx, part, N, C, TG);
