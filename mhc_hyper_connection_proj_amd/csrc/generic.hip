@@ -505,7 +505,7 @@ __global__ __launch_bounds__(256) void gagg_fwd_kernel(const T *__restrict__ X, 
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       float v[8];
-      Io8<T>::load(X + (t * NS + i) * C + 8 * g, v);
+      Io8<T>::load_nt(X + (t * NS + i) * C + 8 * g, v);
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] += h[i] * v[e];
     }
@@ -527,11 +527,11 @@ __global__ __launch_bounds__(256) void gagg_bwd_kernel(const T *__restrict__ gr,
   for (int i = 0; i < NS; ++i) { h[i] = Hpre[t * hs + i]; acc[i] = 0.f; }
   for (int64_t g = threadIdx.x; g < G; g += blockDim.x) {
     float gv[8];
-    Io8<T>::load(gr + t * C + 8 * g, gv);
+    Io8<T>::load_nt(gr + t * C + 8 * g, gv);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       float v[8];
-      Io8<T>::load(X + (t * NS + i) * C + 8 * g, v);
+      Io8<T>::load_nt(X + (t * NS + i) * C + 8 * g, v);
       float s = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) s += gv[e] * v[e];
@@ -618,7 +618,7 @@ __global__ __launch_bounds__(256) void gpost_fwd_kernel(const T *__restrict__ X,
   for (int64_t g = threadIdx.x; g < G; g += blockDim.x) {
     float xb[8], xv[NS][8];
     if (MODE != kPostMix) {
-      Io8<T>::load(x + t * C + 8 * g, xb);
+      Io8<T>::load_nt(x + t * C + 8 * g, xb);
       if (HAS_BIAS) {
         float b[8];
         Io8<T>::load(bias + 8 * g, b);
@@ -628,7 +628,7 @@ __global__ __launch_bounds__(256) void gpost_fwd_kernel(const T *__restrict__ X,
     }
     if (MODE != kPostDist) {
 #pragma unroll
-      for (int j = 0; j < NS; ++j) Io8<T>::load(X + (t * NS + j) * C + 8 * g, xv[j]);
+      for (int j = 0; j < NS; ++j) Io8<T>::load_nt(X + (t * NS + j) * C + 8 * g, xv[j]);
     }
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
@@ -646,7 +646,9 @@ __global__ __launch_bounds__(256) void gpost_fwd_kernel(const T *__restrict__ X,
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] += hp * xb[e];
       }
-      Io8<T>::store(out + (t * NS + i) * C + 8 * g, o);
+      // the new residual: written non-temporally (its dirty lines otherwise
+      // land in the next kernel's reads when the caches evict them)
+      Io8<T>::store_nt(out + (t * NS + i) * C + 8 * g, o);
     }
   }
 }
@@ -702,7 +704,10 @@ __global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr
           // bf16: G rows stay packed; dot products as bf16 pairs, other terms converted where used
           gu32x4 gw[NS];
 #pragma unroll
-          for (int i = 0; i < NS; ++i) gw[i] = *reinterpret_cast<const gu32x4 *>(Gr + (t * NS + i) * C + 8 * g);
+          for (int i = 0; i < NS; ++i) {
+            const gu32x4 *gp = reinterpret_cast<const gu32x4 *>(Gr + (t * NS + i) * C + 8 * g);
+            gw[i] = NPASS > 1 ? *gp : __builtin_nontemporal_load(gp);  // two passes: G kept for the second
+          }
           auto gval = [&](int i, int e) {
             const uint32_t w = (e >> 1) == 0 ? gw[i].x : (e >> 1) == 1 ? gw[i].y : (e >> 1) == 2 ? gw[i].z : gw[i].w;
             return (e & 1) ? bf16_hi(w) : bf16_lo(w);
@@ -714,8 +719,8 @@ __global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr
             const uint32_t uw[4] = {u.x, u.y, u.z, u.w}, vw[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(pbf16x2, uw[q]), __builtin_bit_cast(pbf16x2, vw[q]),
-                                                  a, false);
+              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(pbf16x2, uw[q]),
+                                                  __builtin_bit_cast(pbf16x2, vw[q]), a, false);
             return a;
           };
           if (MIX) {
@@ -723,7 +728,8 @@ __global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr
             for (int jj = 0; jj < JB; ++jj) {
               const int j = j0 + jj;
               if (j < NS) {
-                const gu32x4 xw = *reinterpret_cast<const gu32x4 *>(X + (t * NS + j) * C + 8 * g);
+                const gu32x4 xw =
+                    __builtin_nontemporal_load(reinterpret_cast<const gu32x4 *>(X + (t * NS + j) * C + 8 * g));
 #pragma unroll
                 for (int i = 0; i < NS; ++i) acc[jj * NS + i] = dot8(xw, gw[i], acc[jj * NS + i]);
                 if (WRITE_DX) {
@@ -742,7 +748,7 @@ __global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr
           if (DIST && dist_here) {
             constexpr int off = MIX ? JB * NS : 0;
             float xb[8], o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            Io8<T>::load(x + t * C + 8 * g, xb);
+            Io8<T>::load_nt(x + t * C + 8 * g, xb);
             if (HAS_BIAS) {
               float bv[8];
               Io8<T>::load(bias + 8 * g, bv);
@@ -772,14 +778,19 @@ __global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr
         }
         float gv[NS][8];
 #pragma unroll
-        for (int i = 0; i < NS; ++i) Io8<T>::load(Gr + (t * NS + i) * C + 8 * g, gv[i]);
+        for (int i = 0; i < NS; ++i) {
+          if (NPASS > 1)
+            Io8<T>::load(Gr + (t * NS + i) * C + 8 * g, gv[i]);  // two passes: G kept for the second
+          else
+            Io8<T>::load_nt(Gr + (t * NS + i) * C + 8 * g, gv[i]);
+        }
         if (MIX) {
 #pragma unroll
           for (int jj = 0; jj < JB; ++jj) {
             const int j = j0 + jj;
             if (j < NS) {
               float xv[8];
-              Io8<T>::load(X + (t * NS + j) * C + 8 * g, xv);
+              Io8<T>::load_nt(X + (t * NS + j) * C + 8 * g, xv);
 #pragma unroll
               for (int i = 0; i < NS; ++i) {
                 float sdot = 0.f;
@@ -803,7 +814,7 @@ __global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr
         if (DIST && dist_here) {
           constexpr int off = MIX ? JB * NS : 0;
           float xb[8], o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-          Io8<T>::load(x + t * C + 8 * g, xb);
+          Io8<T>::load_nt(x + t * C + 8 * g, xb);
           if (HAS_BIAS) {
             float bv[8];
             Io8<T>::load(bias + 8 * g, bv);
