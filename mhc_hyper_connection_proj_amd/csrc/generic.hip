@@ -1077,7 +1077,7 @@ __global__ __launch_bounds__(512) void gproj_partial_dma_kernel(const bf16_t *__
       const int p = (lane & 7) ^ (rr & 7);  // global 8-k piece for this slot
       const int64_t t = min(tw + rr, N - 1);  // rows past N re-read row N-1 (never stored)
       const int64_t k = c * 64 + 8 * p < K ? c * 64 + 8 * p : c * 64;  // past K: a real k (W is 0 there)
-      dma16(X + t * K + k, xs + q * 1024);
+      dma16_nt(X + t * K + k, xs + q * 1024);  // X is streamed once
     }
   };
 
