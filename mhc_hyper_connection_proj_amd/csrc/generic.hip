@@ -8,25 +8,34 @@
 // operations are provided here for any n up to 8, with the same
 // definitions, layouts, determinism (fixed-order reductions, no atomics)
 // and boundary checks, but simpler, less tuned kernels:
-//  * projection forward: split-K over 8 slices, fp32 MFMA (32x32x2) on the
-//    activations converted exactly to fp32, each 64-k W chunk staged once per
-//    workgroup in LDS for four waves of 32 tokens, ceil(J/32) column tiles;
-//    a per-token finalize sums the slices in order and applies RMS, gains,
+//  * projection forward: split-K over 8 slices.  bf16: W split once per call
+//    into three exact bf16 terms and packed in 64-k chunks; 8 waves x 32
+//    tokens per workgroup copy each chunk and their X tiles into an LDS ring
+//    (global_load_lds) and multiply on the bf16 MFMA (32x32x16).  fp32: the
+//    fp32 MFMA (32x32x2) with each 64-k W chunk staged once per workgroup.
+//    A per-token finalize sums the slices in order and applies RMS, gains,
 //    sigmoid and Sinkhorn;
 //  * projection backward: a per-token kernel (sigmoid / Sinkhorn backward,
-//    dp = r alpha dzh and the RMS coefficient), then dX and dW.  bf16: one
-//    MFMA kernel on tiles of 32-128 channels of all n streams (so the
-//    h_post_bda gradient G, which every output stream mixes, is loaded once),
-//    dp W^T on fp32 MFMA with W's rows in registers and x^T dp on bf16 MFMA
-//    with dp split exactly into three bf16 terms, the aggregate and
-//    h_post_bda terms formed in its epilogue.  fp32: a per-token pass forming
-//    those terms in an fp32 workspace, then a VALU kernel with one thread per
-//    k that owns W's row k and its dW row, walking a token block;
-//  * Sinkhorn: one n x n matrix per thread; the backward replays the
-//    forward from checkpoints spaced ~sqrt(2 iters) half-steps apart, so it
-//    needs no storage beyond registers;
-//  * streaming ops: one workgroup per token, 8-channel groups per thread,
-//    per-token sums lane -> wave -> workgroup in fixed order.
+//    dp = r alpha dzh and the RMS coefficient), then dX and dW, with the
+//    aggregate and h_post_bda terms formed in the dX epilogue.  bf16, n <= 3:
+//    one MFMA kernel on tiles of 64-128 channels of all n streams (so the
+//    h_post_bda gradient G, which every output stream mixes, is loaded
+//    once), dp W^T on fp32 MFMA with W's rows in registers and x^T dp on
+//    bf16 MFMA with dp split exactly into three bf16 terms.  bf16, n >= 5:
+//    the same two contractions as two kernels (dX on 64-channel tiles of all
+//    n streams, dW on 256-k tiles), dp split and transposed once for dW.
+//    fp32: a per-token pass forming the epilogue terms in an fp32 workspace,
+//    then a VALU kernel with one thread per k that owns W's row k and its dW
+//    row, walking a token block;
+//  * Sinkhorn: n >= 3 on groups of 4 or 8 lanes, one rotated line per lane
+//    (row and column passes in-lane, layouts swapped by lane moves); the
+//    backward records every half-step's line sums and a checkpoint every 8
+//    half-steps.  n <= 2 (and records too large for LDS): one matrix per
+//    thread, with stored sums where they fit, else a replay of the forward
+//    from checkpoints spaced ~sqrt(2 iters) half-steps apart;
+//  * streaming ops: one workgroup (or wave) per token, 8-channel groups per
+//    thread, once-read rows loaded non-temporally, per-token sums lane ->
+//    wave -> workgroup in fixed order.
 #include <algorithm>
 
 #include "device.h"
