@@ -1186,6 +1186,335 @@ __global__ __launch_bounds__(512) void proj_bwd_mfma_kernel(
   }
 }
 
+// ------------------------------------------------------------------ MFMA dX / dW, 16-token sub-tiles
+// The fused pre backward's form (g and the h_post_bda term given) on
+// 16-token sub-tiles, so that two workgroups share a CU: each workgroup's
+// 3-stage ring (X, g, G tiles and the 16 dp records: 20,992 bytes a stage)
+// and the dX waves' accumulator tiles take 80,384 bytes of LDS, and every
+// wave stays within 128 registers.  Roles, tiles (64 channels of all four
+// streams), swizzles, the barrier sequence and the epilogue are those of
+// proj_bwd_mfma_kernel; what changes with 16 tokens:
+//  * dX: dp W^T on v_mfma_f32_16x16x32_bf16, one 16 x 16 block per 16
+//    channels; the contraction runs over j (24, padded to 32) once per kept
+//    term pair (hh, hm, mh, hl, lh, mm), A = a dp term's 8 j of one token (one
+//    16-byte record piece; lane group 3 holds zeros), B = a W term's 8 j of
+//    one channel.  Each W term is held once (3 x 4 registers per 16
+//    channels) and serves every pair it appears in;
+//  * dW: x^T dp on 32x32x16 with the 16 tokens as the contraction, A = 8
+//    tokens of an X column, B = 8 tokens of a dp term's column;
+//  * copies per sub-tile: X and G quarters two 1 KB copies per loader, g one
+//    copy on loaders 0 and 1, the records 2.5 KB on loaders 0-2 (half a copy
+//    on loader 2).
+constexpr int kB3Stages = 3;
+constexpr int kB3Quarter = 16 * 128;  // bytes of one 16 x 64 bf16 tile
+constexpr int kB3AccRow = 68;         // floats per row of a wave's 16 x 64 accumulator tile
+
+struct B3Lay {
+  static constexpr int X = 0;
+  static constexpr int G = 4 * kB3Quarter;     // g
+  static constexpr int Q = G + kB3Quarter;     // G of h_post_bda
+  static constexpr int P = Q + 4 * kB3Quarter;  // 16 dp records
+  static constexpr int stage = P + 16 * kDpaBytes;
+  static constexpr int acc = kB3Stages * stage;
+  static constexpr int total = acc + 4 * 16 * kB3AccRow * 4;
+  static_assert(2 * total <= 160 * 1024, "two workgroups' LDS on one CU");
+};
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+// Per-lane inputs of one sub-tile's dX epilogue, for rows er + 8q: dX_in,
+// H_pre and the row's H_res row.
+struct DxPre16 {
+  u32x4 d[2];
+  float hp[2];
+  float4 hr[2];
+};
+
+template <bool ACCUM, bool DW>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void proj_bwd_mfma16_kernel(
+    const bf16_t *__restrict__ X, const float *__restrict__ W, const char *__restrict__ dpA,
+    const float *__restrict__ Hpre, const bf16_t *__restrict__ gr, const bf16_t *__restrict__ Gp,
+    const float *__restrict__ Hres, bf16_t *__restrict__ dX, float *__restrict__ dWpart, int64_t N, int64_t C,
+    int64_t tbsz) {
+  using L = B3Lay;
+  extern __shared__ __attribute__((aligned(16))) char b3lds[];
+  const int64_t K = 4 * C;
+  const int64_t nkt = (C + kBwKW - 1) / kBwKW;
+  const int64_t ntb = (N + tbsz - 1) / tbsz;
+  // XCD-contiguous tile order (as in proj_bwd_mfma_kernel)
+  const int64_t T = nkt * ntb, per = (T + 7) / 8;
+  const int64_t tile = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (tile >= T) return;  // grid padding to a multiple of 8 (whole workgroup)
+  const int64_t tb = ntb - 1 - tile / nkt;  // token blocks from the last down
+  const int64_t kt = tile % nkt;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const bool loader = wave >= 4;
+  const int kq = wave & 3;  // stream of this wave
+  const int64_t c0 = kt * kBwKW;
+  const int64_t kbase = kq * C + c0;
+  const int64_t nvalid = min<int64_t>(kBwKW, C - c0);
+
+  const int64_t t_begin = tb * tbsz;
+  const int64_t t_end = min(N, t_begin + tbsz);
+  const int nsub = (int)((t_end - t_begin + 15) / 16);
+
+  // ---- loader geometry: lane -> (row in its 8-row group, 16-byte piece)
+  const int drow = lane >> 3;
+  const int dpiece = (lane & 7) ^ drow;
+  const bool dvalid = 8 * dpiece < nvalid;
+  const int64_t gcol = dvalid ? c0 + 8 * dpiece : c0;  // a real channel when the piece lies past the tile
+  const int64_t xk = kq * C + gcol;
+  const int nload = 4 + (kq < 2 ? 1 : 0) + (kq < 3 ? 1 : 0);
+
+  auto issue = [&](int i) {
+    char *st = b3lds + (i % kB3Stages) * L::stage;
+    const int64_t t0 = t_begin + 16 * (int64_t)i;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int64_t t = min(t0 + 8 * q + drow, N - 1);
+      dma16(X + t * K + xk, st + L::X + kq * kB3Quarter + q * 1024);
+      dma16(Gp + (t * 4 + kq) * C + gcol, st + L::Q + kq * kB3Quarter + q * 1024);
+    }
+    if (kq < 2) {
+      const int64_t t = min(t0 + 8 * kq + drow, N - 1);
+      dma16(gr + t * C + gcol, st + L::G + kq * 1024);
+    }
+    // the sub-tile's 16 records are contiguous (they exist up to the
+    // 32-token padding): 2.5 KB, the last half copy on lanes 0..31
+    const char *rs = dpA + t0 * kDpaBytes;
+    if (kq < 2) dma16(rs + kq * 1024 + lane * 16, st + L::P + kq * 1024);
+    if (kq == 2 && lane < 32) dma16(rs + 2048 + lane * 16, st + L::P + 2048);
+  };
+
+  // ---- dX geometry: lane -> token rows er + 8q (q = 0, 1) and 8 channels
+  // at ek of the wave's 64, so eight lanes store one row's 128-byte line
+  const int er = lane >> 3;
+  const int ek = (lane & 7) * 8;
+  const bool ekv = ek < nvalid;
+  const int64_t kx = kbase + ek;
+
+  auto prefetch = [&](DxPre16 &P, int i) {
+    const int64_t t0 = t_begin + 16 * (int64_t)i;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int64_t tt = t0 + er + 8 * q;
+      const bool v = tt < N && ekv;
+      if (ACCUM) P.d[q] = v ? *reinterpret_cast<const u32x4 *>(dX + tt * K + kx) : u32x4{0u, 0u, 0u, 0u};
+      P.hp[q] = v ? Hpre[tt * 4 + kq] : 0.f;
+      P.hr[q] = tt < N ? *reinterpret_cast<const float4 *>(Hres + tt * 16 + kq * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+
+  // 16x16x32 layout: lane (n = lane & 15, group gq = lane >> 4); A holds row
+  // n's k = 8 gq .. 8 gq + 7, B column n's same k, D rows 4 gq + r, column n
+  const int n16 = lane & 15, gq = lane >> 4;
+  // B fragments: W term m of channel 16 bi + n16, j = 8 gq .. + 7 (zero for gq = 3)
+  u32x4 wt[4][3];
+  f32x4 accX[4];
+  f32x16 accW[2];
+  if (!loader) {
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) {
+      const bool kv = 16 * bi + n16 < nvalid && gq < 3;
+      const float *wr = W + (kbase + 16 * bi + n16) * kJ + 8 * gq;
+      const float4 v0 = kv ? *reinterpret_cast<const float4 *>(wr) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 v1 = kv ? *reinterpret_cast<const float4 *>(wr + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float w8[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      float th[8], tmid[8], tl[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        th[e] = bf16_round(w8[e]);
+        const float r1 = w8[e] - th[e];
+        tmid[e] = bf16_round(r1);
+        tl[e] = r1 - tmid[e];
+      }
+      wt[bi][0] = u32x4{pack_bf16x2(th[0], th[1]), pack_bf16x2(th[2], th[3]), pack_bf16x2(th[4], th[5]),
+                        pack_bf16x2(th[6], th[7])};
+      wt[bi][1] = u32x4{pack_bf16x2(tmid[0], tmid[1]), pack_bf16x2(tmid[2], tmid[3]), pack_bf16x2(tmid[4], tmid[5]),
+                        pack_bf16x2(tmid[6], tmid[7])};
+      wt[bi][2] = u32x4{pack_bf16x2(tl[0], tl[1]), pack_bf16x2(tl[2], tl[3]), pack_bf16x2(tl[4], tl[5]),
+                        pack_bf16x2(tl[6], tl[7])};
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) accW[rt][r] = 0.f;
+
+  float *acc_t = reinterpret_cast<float *>(b3lds + L::acc) + kq * 16 * kB3AccRow;
+
+  // The two roles run separate loops with the same barrier sequence: a dX
+  // wave never issues an LDS DMA, so its LDS reads need no wait on vmcnt.
+  if (loader) {
+    const int col = lane & 31, h = lane >> 5;
+    issue(0);
+    if (nsub > 1) issue(1);
+    for (int i = 0; i < nsub; ++i) {
+      if (i + 1 < nsub) wait_vmcnt_le(nload); else wait_vmcnt<0>();
+      lds_barrier();
+      const char *st = b3lds + (i % kB3Stages) * L::stage;
+      if (i + 2 < nsub) issue(i + 2);
+      if (DW) {
+        // dW += X^T dp: A = 8 tokens (8h .. 8h + 7) of X column k = 32 rt + col,
+        // B = the same 8 tokens of dp term tm at j = col
+        const bf16_t *xs = reinterpret_cast<const bf16_t *>(st + L::X + kq * kB3Quarter);
+        u32x4 xa[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          uint32_t w4[4];
+          const int kk = 32 * rt + col;
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const int r0 = 8 * h + 2 * p;
+            const uint32_t lo16 = xs[r0 * 64 + 8 * ((kk >> 3) ^ (r0 & 7)) + (kk & 7)];
+            const uint32_t hi16 = xs[(r0 + 1) * 64 + 8 * ((kk >> 3) ^ ((r0 + 1) & 7)) + (kk & 7)];
+            w4[p] = lo16 | (hi16 << 16);
+          }
+          xa[rt] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+        }
+        const char *ps = st + L::P;
+#pragma unroll
+        for (int tm = 0; tm < 3; ++tm) {
+          uint32_t w4[4] = {0u, 0u, 0u, 0u};
+          if (col < kJ) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const int r0 = 8 * h + 2 * p;
+              const int off = (tm * 3 + (col >> 3)) * 16 + (col & 7) * 2;
+              const uint32_t lo16 = *reinterpret_cast<const uint16_t *>(ps + r0 * kDpaBytes + off);
+              const uint32_t hi16 = *reinterpret_cast<const uint16_t *>(ps + (r0 + 1) * kDpaBytes + off);
+              w4[p] = lo16 | (hi16 << 16);
+            }
+          }
+          const u32x4 bfr = u32x4{w4[0], w4[1], w4[2], w4[3]};
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+            accW[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa[rt]),
+                                                               __builtin_bit_cast(bf16x8, bfr), accW[rt], 0, 0, 0);
+        }
+      }
+    }
+    if (DW && col < kJ) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int e = 32 * rt + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (e < nvalid) dWpart[(tb * K + kbase + e) * kJ + col] = accW[rt][r];
+        }
+    }
+  } else {
+    wait_vmcnt<0>();  // W in registers: only the prefetches are pending inside the loop
+    DxPre16 cur;
+    prefetch(cur, 0);
+    for (int i = 0; i < nsub; ++i) {
+      lds_barrier();
+      const char *st = b3lds + (i % kB3Stages) * L::stage;
+      const int64_t t0 = t_begin + 16 * (int64_t)i;
+      // (a) dp W^T for 16 tokens x 64 channels: A fragments (token t0 + n16,
+      // dp term s, j = 8 gq ..) from the records, 4 blocks x 6 term pairs
+      const char *ps = st + L::P;
+      u32x4 af[3];
+#pragma unroll
+      for (int sdp = 0; sdp < 3; ++sdp)
+        af[sdp] = gq < 3 ? *reinterpret_cast<const u32x4 *>(ps + n16 * kDpaBytes + (sdp * 3 + gq) * 16)
+                         : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) {
+        f32x4 a4 = f32x4{0.f, 0.f, 0.f, 0.f};
+        // pairs (dp term, W term): hh, hm, mh, hl, lh, mm
+        a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[0]),
+                                                     __builtin_bit_cast(bf16x8, wt[bi][0]), a4, 0, 0, 0);
+        a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[0]),
+                                                     __builtin_bit_cast(bf16x8, wt[bi][1]), a4, 0, 0, 0);
+        a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[1]),
+                                                     __builtin_bit_cast(bf16x8, wt[bi][0]), a4, 0, 0, 0);
+        a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[0]),
+                                                     __builtin_bit_cast(bf16x8, wt[bi][2]), a4, 0, 0, 0);
+        a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[2]),
+                                                     __builtin_bit_cast(bf16x8, wt[bi][0]), a4, 0, 0, 0);
+        a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[1]),
+                                                     __builtin_bit_cast(bf16x8, wt[bi][1]), a4, 0, 0, 0);
+        accX[bi] = a4;
+      }
+      // (b) dX = dp W^T + c_rms x + H_pre g + sum_i H_res[j][i] G[i] + dX_in,
+      // through the wave's LDS accumulator tile as in proj_bwd_mfma_kernel
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<0>();
+      const char *xs = st + L::X + kq * kB3Quarter;
+      const char *gs = st + L::G;
+      const char *qs = st + L::Q;
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc_t[(4 * gq + r) * kB3AccRow + 16 * bi + n16] = accX[bi][r];
+      wave_lds_sync();
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int row = er + 8 * q;
+        const int64_t tt = t0 + row;
+        if (!(tt < N && ekv)) continue;
+        const int slot = (ek >> 3) ^ (row & 7);
+        const float4 a0 = *reinterpret_cast<const float4 *>(&acc_t[row * kB3AccRow + ek]);
+        const float4 a1 = *reinterpret_cast<const float4 *>(&acc_t[row * kB3AccRow + ek + 4]);
+        const float acc8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const float crms = *reinterpret_cast<const float *>(ps + row * kDpaBytes + 9 * 16);
+        const u32x4 xv = *reinterpret_cast<const u32x4 *>(xs + row * 128 + 16 * slot);
+        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+        float o[8];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          o[2 * p] = acc8[2 * p] + crms * bf16_lo(xw[p]);
+          o[2 * p + 1] = acc8[2 * p + 1] + crms * bf16_hi(xw[p]);
+        }
+        {
+          const u32x4 gv = *reinterpret_cast<const u32x4 *>(gs + row * 128 + 16 * slot);
+          const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+          const float hp = cur.hp[q];
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            o[2 * p] += hp * bf16_lo(gw[p]);
+            o[2 * p + 1] += hp * bf16_hi(gw[p]);
+          }
+        }
+        {  // h_post_bda term: sum_i H_res[j][i] G[i], j = this wave's stream
+          const float4 hr = cur.hr[q];
+          uint32_t gw[4][4];
+#pragma unroll
+          for (int si = 0; si < 4; ++si) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(qs + si * kB3Quarter + row * 128 + 16 * slot);
+            gw[si][0] = v.x; gw[si][1] = v.y; gw[si][2] = v.z; gw[si][3] = v.w;
+          }
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            o[2 * p] += (hr.x * bf16_lo(gw[0][p]) + hr.y * bf16_lo(gw[1][p])) +
+                        (hr.z * bf16_lo(gw[2][p]) + hr.w * bf16_lo(gw[3][p]));
+            o[2 * p + 1] += (hr.x * bf16_hi(gw[0][p]) + hr.y * bf16_hi(gw[1][p])) +
+                            (hr.z * bf16_hi(gw[2][p]) + hr.w * bf16_hi(gw[3][p]));
+          }
+        }
+        if (ACCUM) {
+          const uint32_t dw4[4] = {cur.d[q].x, cur.d[q].y, cur.d[q].z, cur.d[q].w};
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            o[2 * p] += bf16_lo(dw4[p]);
+            o[2 * p + 1] += bf16_hi(dw4[p]);
+          }
+        }
+        uint4 ow;
+        ow.x = pack_bf16x2(o[0], o[1]);
+        ow.y = pack_bf16x2(o[2], o[3]);
+        ow.z = pack_bf16x2(o[4], o[5]);
+        ow.w = pack_bf16x2(o[6], o[7]);
+        *reinterpret_cast<uint4 *>(dX + tt * K + kx) = ow;
+      }
+      wave_lds_sync();  // the reads of the accumulator area precede the next sub-tile's writes
+      if (i + 1 < nsub) prefetch(cur, i + 1);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ fp32 VALU dX / dW kernel
 template <bool ACCUM, bool HAS_G, bool DW>
 __global__ __launch_bounds__(256) void proj_bwd_dx_f32_kernel(
@@ -1291,9 +1620,23 @@ static void launch_b2_dw(hipStream_t s, const ProjBwdArgs &a, const BwdWs &L) {
                      (const bf16_t *)a.post_G, a.post_H_res, (bf16_t *)a.dX, L.dwpart, a.N, a.C, L.tbsz, group4);
 }
 
+template <bool ACCUM, bool DW>
+static void launch_b3(hipStream_t s, const ProjBwdArgs &a, const BwdWs &L) {
+  const int64_t nkt = (a.C + kBwKW - 1) / kBwKW;
+  const int64_t blocks = round_up(nkt * L.ntb, 8);
+  hipLaunchKernelGGL((proj_bwd_mfma16_kernel<ACCUM, DW>), dim3((unsigned)blocks), dim3(512), (size_t)B3Lay::total,
+                     s, (const bf16_t *)a.X, a.W, (const char *)L.dpA, a.H_pre, (const bf16_t *)a.g,
+                     (const bf16_t *)a.post_G, a.post_H_res, (bf16_t *)a.dX, L.dwpart, a.N, a.C, L.tbsz);
+}
+
 template <bool ACCUM, bool HAS_G>
 static void launch_b2(hipStream_t s, const ProjBwdArgs &a, const BwdWs &L) {
   const bool post = a.post_G != nullptr;
+  if (HAS_G && post) {  // the fused pre backward with the h_post_bda term: 16-token sub-tiles
+    if (a.dW) launch_b3<ACCUM, true>(s, a, L);
+    else launch_b3<ACCUM, false>(s, a, L);
+    return;
+  }
   if (a.dW) {
     if (post) launch_b2_dw<ACCUM, HAS_G, true, true>(s, a, L);
     else launch_b2_dw<ACCUM, HAS_G, true, false>(s, a, L);
