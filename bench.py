@@ -623,11 +623,11 @@ def main():
     gbs = tot_bytes / (mhc_ms * 1e-3) / 1e9
 
     # dominant kernel: the dX / dW kernel of the pre backward, timed alone
-    kname = "proj_bwd_mfma_kernel"
+    kname = "proj_bwd_mfma16_kernel"
     k_ms = float(np.mean([kev[st][0].elapsed_time(kev[st][1]) for st in range(args.steps)]))
     k_bytes = led["dxdw_kernel"] * N
     k_gbs = k_bytes / (k_ms * 1e-3) / 1e9
-    traffic = pmc_traffic("proj_bwd_mfma_full_layer_pmc.txt", ["mhc_hyper_connection_proj_amd/csrc/proj.hip",
+    traffic = pmc_traffic("proj_bwd_dxdw_full_layer_pmc.txt", ["mhc_hyper_connection_proj_amd/csrc/proj.hip",
                                                                "mhc_hyper_connection_proj_amd/csrc/device.h",
                                                                "mhc_hyper_connection_proj_amd/csrc/ring.h"])
     # the h_post_bda backward (one kernel, the whole post_bwd phase), for context
