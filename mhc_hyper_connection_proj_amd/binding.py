@@ -339,8 +339,9 @@ def mhc_pre_rmsnorm_fwd(X, W, gamma=None, alpha=None, hbias=None, rms_eps=1e-6, 
 
 
 def mhc_pre_bwd(g, dH_post, dH_res, X, W, saved, H_pre, H_post, H_res_logits, alpha=None, iters=20, eps=1e-6,
-                dX=None, accumulate_dX=False, want_intermediates=False, post_G=None, post_H_res=None):
-    """Fused pre pass backward.  Returns dict(dX, dW, dalpha, dhbias[, dH_pre, dlogits]).
+                dX=None, accumulate_dX=False, want_intermediates=False, post_G=None, post_H_res=None, want_dW=True):
+    """Fused pre pass backward.  Returns dict(dX, dW, dalpha, dhbias[, dH_pre, dlogits]); dW is None
+    when want_dW is False.
 
     post_G / post_H_res: the h_post_bda upstream gradient and H_res; when given,
     the h_post_bda dX term is added here (call mhc_h_post_bda_bwd with want_dX=False).
@@ -359,8 +360,8 @@ def mhc_pre_bwd(g, dH_post, dH_res, X, W, saved, H_pre, H_post, H_res_logits, al
             raise ValueError("accumulate_dX needs dX")
         dX = torch.empty_like(X)
     _need(dX, "dX", X.dtype, X.numel())
-    o = dict(dX=dX, dW=torch.empty(n * C, J, dtype=f32, device=d), dalpha=torch.empty(3, dtype=f32, device=d),
-             dhbias=torch.empty(J, dtype=f32, device=d))
+    o = dict(dX=dX, dW=torch.empty(n * C, J, dtype=f32, device=d) if want_dW else None,
+             dalpha=torch.empty(3, dtype=f32, device=d), dhbias=torch.empty(J, dtype=f32, device=d))
     if want_intermediates:
         o["dH_pre"] = torch.empty(*X.shape[:-2], n, dtype=f32, device=d)
         o["dlogits"] = torch.empty(*X.shape[:-2], n, n, dtype=f32, device=d)

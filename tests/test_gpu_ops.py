@@ -342,6 +342,36 @@ def test_pre_fwd_bwd(act, N, C, mode):
     assert_tokensum("dhbias", ob["dhbias"], rb["dhbias"], ab, depth=sum_depth("param", N))
 
 
+@pytest.mark.parametrize("act,N,C", [("bf16", 37, 296), ("bf16", 66, 7168), ("bf16", 130, 4096)])
+def test_pre_bwd_post_term_accumulate_no_dw(act, N, C):
+    # the h_post_bda dX term formed in the pass and the result added onto a given dX, with dW not
+    # requested: the remaining variants of the fused dX/dW kernel (the other tests write dX fresh
+    # and always take dW)
+    log(f"pre bwd post term + accumulate, no dW act={act} N={N} C={C}")
+    X, W, alpha, hb = _proj_inputs(act, N, C)
+    ref = O.pre_fwd(h64(X), h64(W), h64(alpha), h64(hb), 1e-6, 20, 1e-6)
+    saved = np.zeros((N, 32), np.float32)
+    saved[:, 0] = ref["r"]; saved[:, 1] = ref["q"]; saved[:, 2:26] = ref["z"]
+    g = store(RNG.standard_normal((N, C)), act)
+    dHq = f32(RNG.standard_normal((N, 4)))
+    dHr = f32(RNG.standard_normal((N, 4, 4)))
+    dX0 = store(RNG.standard_normal((N, 4, C)), act)
+    Gp = store(RNG.standard_normal((N, 4, C)), act)
+    Hrp = f32(O.sinkhorn_fwd(RNG.standard_normal((N, 4, 4)), 20, 1e-6))
+    ob = B.mhc_pre_bwd(dev(g), dev(dHq), dev(dHr), dev(X), dev(W), dev(saved), dev(f32(ref["H_pre"])),
+                       dev(f32(ref["H_post"])), dev(f32(ref["L"])), alpha=dev(alpha), iters=20, eps=1e-6,
+                       dX=dev(dX0), accumulate_dX=True, post_G=dev(Gp), post_H_res=dev(Hrp), want_dW=False)
+    torch.cuda.synchronize()
+    assert ob["dW"] is None
+    zeros = np.zeros((N, 4)); zc = np.zeros((N, C))
+    post = O.h_post_bda_bwd(h64(Gp), h64(X), h64(Hrp), zeros, zc)[0]
+    rb = O.pre_bwd(h64(g), h64(dHq), h64(dHr), h64(X), h64(W), h64(alpha), h64(hb), 1e-6, 20, 1e-6)
+    assert_act("dX", ob["dX"], h64(dX0) + post + rb["dX"], act)
+    _, aa, ab = pre_bwd_abs_parts(h64(g), h64(dHq), h64(dHr), h64(X), h64(W), h64(alpha), h64(hb), 1e-6, 20, 1e-6)
+    assert_tokensum("dalpha", ob["dalpha"], rb["dalpha"], aa, depth=sum_depth("param", N))
+    assert_tokensum("dhbias", ob["dhbias"], rb["dhbias"], ab, depth=sum_depth("param", N))
+
+
 @pytest.mark.parametrize("iters,eps", [(100, 1e-6), (200, 1e-6), (150, 0.25)])
 def test_pre_fwd_bwd_long_iterations(iters, eps):
     """The fused pre pass runs its Sinkhorn in the quad layout (finalize forward, per-token backward):
