@@ -409,22 +409,32 @@ __global__ __launch_bounds__(256) void h_post_bda_bwd_kernel(
 // neither stores nor sums it), so the wait for one set counts only the loads
 // issued after it.  Results per token and the dbias partial rows follow the
 // same arithmetic as above with one group per thread.
+// The rows loaded a token ahead are G and x (20 registers a set); X, used
+// last (dH_res), is loaded when its token's turn comes, before the next
+// token's G and x, so its latency is covered by the dX, dx and dH_post work
+// (and its wait leaves the next token's loads in flight), and the two sets
+// plus the working values stay within the 128 registers of a 1024-thread
+// workgroup (holding X a token ahead too had spilled).
 struct PostRowsBf16 {
-  nt_u32x4 g[4], X[4], x;
+  nt_u32x4 g[4], x;
 };
 
 __device__ __forceinline__ void post_rows_issue(PostRowsBf16 &r, const bf16_t *__restrict__ Gr,
-                                                const bf16_t *__restrict__ X, const bf16_t *__restrict__ x,
-                                                int64_t t, int64_t C, int c8) {
+                                                const bf16_t *__restrict__ x, int64_t t, int64_t C, int c8) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) r.g[i] = Io8<bf16_t>::ld_nt(Gr + (t * 4 + i) * C + c8);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r.X[i] = Io8<bf16_t>::ld_nt(X + (t * 4 + i) * C + c8);
   r.x = Io8<bf16_t>::ld_nt(x + t * C + c8);
 }
 
+__device__ __forceinline__ void post_x_issue(nt_u32x4 xr[4], const bf16_t *__restrict__ X, int64_t t, int64_t C,
+                                             int c8) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xr[i] = Io8<bf16_t>::ld_nt(X + (t * 4 + i) * C + c8);
+}
+
 template <bool DXO>
-__device__ __forceinline__ void post_rows_compute(const PostRowsBf16 &r, const float *__restrict__ Hres,
+__device__ __forceinline__ void post_rows_compute(const PostRowsBf16 &r, const nt_u32x4 xr[4],
+                                                  const float *__restrict__ Hres,
                                                   const float *__restrict__ Hpost, nt_u32x4 braw,
                                                   bf16_t *__restrict__ dX, bf16_t *__restrict__ dx, float dbp[8],
                                                   float *__restrict__ red, int64_t t, int tt, int64_t C, int c8,
@@ -465,7 +475,7 @@ __device__ __forceinline__ void post_rows_compute(const PostRowsBf16 &r, const f
 #pragma unroll
   for (int js = 0; js < 4; ++js) {
     float xv[8];
-    Io8<bf16_t>::cvt(r.X[js], xv);
+    Io8<bf16_t>::cvt(xr[js], xv);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float a = 0.f;
@@ -502,21 +512,27 @@ __global__ __launch_bounds__(1024) void h_post_bda_bwd_dbias_bf16_kernel(
 #pragma unroll
   for (int e = 0; e < 8; ++e) dbp[e] = 0.f;
   PostRowsBf16 ra, rb;
-  post_rows_issue(ra, Gr, X, x, t0, C, c8);
+  nt_u32x4 xr[4];
+  post_rows_issue(ra, Gr, x, t0, C, c8);
   int tt = 0;
   // two tokens per trip, both prefetches unconditional inside the loop
   for (; tt + 2 < ntok; tt += 2) {
-    post_rows_issue(rb, Gr, X, x, t0 + tt + 1, C, c8);
-    post_rows_compute<DXO>(ra, Hres, Hpost, braw, dX, dx, dbp, red, t0 + tt, tt, C, c8, live);
-    post_rows_issue(ra, Gr, X, x, t0 + tt + 2, C, c8);
-    post_rows_compute<DXO>(rb, Hres, Hpost, braw, dX, dx, dbp, red, t0 + tt + 1, tt + 1, C, c8, live);
+    post_x_issue(xr, X, t0 + tt, C, c8);
+    post_rows_issue(rb, Gr, x, t0 + tt + 1, C, c8);
+    post_rows_compute<DXO>(ra, xr, Hres, Hpost, braw, dX, dx, dbp, red, t0 + tt, tt, C, c8, live);
+    post_x_issue(xr, X, t0 + tt + 1, C, c8);
+    post_rows_issue(ra, Gr, x, t0 + tt + 2, C, c8);
+    post_rows_compute<DXO>(rb, xr, Hres, Hpost, braw, dX, dx, dbp, red, t0 + tt + 1, tt + 1, C, c8, live);
   }
   if (tt + 1 < ntok) {
-    post_rows_issue(rb, Gr, X, x, t0 + tt + 1, C, c8);
-    post_rows_compute<DXO>(ra, Hres, Hpost, braw, dX, dx, dbp, red, t0 + tt, tt, C, c8, live);
-    post_rows_compute<DXO>(rb, Hres, Hpost, braw, dX, dx, dbp, red, t0 + tt + 1, tt + 1, C, c8, live);
+    post_x_issue(xr, X, t0 + tt, C, c8);
+    post_rows_issue(rb, Gr, x, t0 + tt + 1, C, c8);
+    post_rows_compute<DXO>(ra, xr, Hres, Hpost, braw, dX, dx, dbp, red, t0 + tt, tt, C, c8, live);
+    post_x_issue(xr, X, t0 + tt + 1, C, c8);
+    post_rows_compute<DXO>(rb, xr, Hres, Hpost, braw, dX, dx, dbp, red, t0 + tt + 1, tt + 1, C, c8, live);
   } else {
-    post_rows_compute<DXO>(ra, Hres, Hpost, braw, dX, dx, dbp, red, t0 + tt, tt, C, c8, live);
+    post_x_issue(xr, X, t0 + tt, C, c8);
+    post_rows_compute<DXO>(ra, xr, Hres, Hpost, braw, dX, dx, dbp, red, t0 + tt, tt, C, c8, live);
   }
   __syncthreads();
   const int nw = blockDim.x >> 6;
