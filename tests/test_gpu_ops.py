@@ -298,7 +298,7 @@ def test_proj_rms_h_bwd(act, N, C):
 # ----------------------------------------------------------------- fused pre pass
 @pytest.mark.parametrize("mode", ["accumulate", "post"])
 @pytest.mark.parametrize("act,N,C", [("f32", 64, 256), ("bf16", 37, 296), ("bf16", 66, 7168), ("bf16", 130, 4096),
-                                     ("bf16", 1000, 2048), ("bf16", 33, 16384)])
+                                     ("bf16", 1000, 2048), ("bf16", 33, 16384), ("bf16", 1, 8), ("bf16", 17, 72)])
 def test_pre_fwd_bwd(act, N, C, mode):
     log(f"pre fwd/bwd act={act} N={N} C={C} mode={mode}")
     X, W, alpha, hb = _proj_inputs(act, N, C)
