@@ -798,422 +798,55 @@ __global__ __launch_bounds__(1024) void param_final_kernel(const float *__restri
 }
 
 // ------------------------------------------------------------------ MFMA dX / dW kernel
-// Workgroup = 8 waves on one token block and one k tile of four 64-k quarters,
-// walked in 32-token sub-tiles through a 3-stage LDS ring:
+// Workgroup = 8 waves on one token block and one k tile of four 64-k
+// quarters, walked in 16-token sub-tiles through a 3-stage LDS ring:
 //  * waves 4..7 (loaders) fill each stage with global_load_lds_dwordx4: the X
-//    tile, the g tile, the h_post_bda upstream gradient G (POST) and the 32
-//    per-token dp records of the sub-tile, two sub-tiles ahead.  With
-//    dW they then run x^T dp on MFMA (loader w-4 owns quarter w-4; A
-//    fragments are 8-token X columns read from LDS, B fragments the dp terms);
-//  * waves 0..3 own one quarter each: dp W^T on bf16 MFMA (W's three terms
-//    held in registers), each 32 x 32 half of the accumulator transposed through a
-//    private LDS area, then the dX epilogue with dX_in, H_pre and H_res rows
-//    loaded one sub-tile ahead into registers.
+//    tile, the g tile, the h_post_bda upstream gradient G (POST) and the 16
+//    per-token dp records of the sub-tile, two sub-tiles ahead.  With dW they
+//    then run x^T dp on MFMA (32x32x16 with the 16 tokens as the
+//    contraction; loader w-4 owns quarter w-4; A = 8 tokens of an X column
+//    read from LDS, B = the same 8 tokens of a dp term's column);
+//  * waves 0..3 own one quarter each: dp W^T on v_mfma_f32_16x16x32_bf16,
+//    one 16 x 16 block per 16 channels; the contraction runs over j (24,
+//    padded to 32) once per kept pair of exact bf16 terms (hh, hm, mh, hl,
+//    lh, mm: the products above 2^-24 relative), A = a dp term's 8 j of one
+//    token (one 16-byte record piece; lane group 3 holds zeros), B = a W
+//    term's 8 j of one channel.  Each W term is held once in registers (3 x 4
+//    per 16 channels) and serves every pair it appears in.  The 16 x 64
+//    result goes through a private LDS area, then the dX epilogue with dX_in,
+//    H_pre and H_res rows loaded one sub-tile ahead into registers.
+// The ring (20,992 bytes a stage with the h_post_bda term) and the
+// accumulator tiles take at most 80,384 bytes and every wave stays within
+// 128 registers, so two workgroups share a CU.
 // One barrier per sub-tile: loaders first wait for their own loads of the
 // sub-tile (s_waitcnt vmcnt), so the barrier both publishes the stage and
 // guarantees that the slot refilled next has been read by every wave.  The
 // loaders issue no other global memory instructions inside the loop, which
-// keeps their vmcnt arithmetic exact.
+// keeps their vmcnt arithmetic exact; dX waves never issue DMA, so their LDS
+// reads need no wait on vmcnt.
 // In every 128-byte LDS row (64 bf16 of X, g or G) the 16-byte piece p of
 // row r sits in slot p ^ (r & 7): the DMA lanes of an instruction cover 8
 // rows x 8 slots, and the row-wise and column-wise reads below spread over
-// the banks.  The 32 dp records (160 bytes each) are copied as they are.
+// the banks.  The 16 dp records (160 bytes each) are copied as they are
+// (2.5 KB: loaders 0-2, half a copy on loader 2).
 // Channel tiles: without the h_post_bda term, 256 consecutive k (g pieces
 // addressed per piece; when C is a multiple of 256 the four tiles that read
 // the same g tile run back to back on one XCD).  With it (POST), one
 // 64-channel range c0 for all 4 streams (quarter i = stream i): the g tile
-// (32 x 64) and the G tile (4 x 32 x 64) are then loaded once and shared by
-// the four dX waves, which each need all four streams of G.
-constexpr int kB2Stages = 3;
-constexpr int kB2Quarter = 32 * 128;  // bytes of one 32 x 64 bf16 tile
-constexpr int kB2AccRow = 68;         // floats per row of a wave's 32 x 64 accumulator tile
-
-template <bool HAS_G, bool POST>
-struct B2Lay {
-  static constexpr int X = 0;
-  static constexpr int G = 4 * kB2Quarter;                               // g
-  static constexpr int Q = G + (HAS_G ? (POST ? 1 : 4) * kB2Quarter : 0);  // G of h_post_bda
-  static constexpr int P = Q + (POST ? 4 * kB2Quarter : 0);              // 32 dp records
-  static constexpr int stage = P + 32 * kDpaBytes;
-  static constexpr int acc = kB2Stages * stage;
-  static constexpr int total = acc + 4 * 32 * kB2AccRow * 4;
-  static_assert(total <= 160 * 1024, "LDS of one workgroup");
-};
-
-// dp W^T runs on bf16 MFMA with dp and W both split exactly into three bf16
-// terms (hi, mid, lo); of the nine term products the six above 2^-24 relative
-// are kept: (hi,hi) (hi,mid) (mid,hi) (hi,lo) (lo,hi) (mid,mid).  The
-// contraction runs over (pair, j): 6 x 24 = 144 = 9 chunks of 16, and in
-// chunk c lane half h takes the 8 j of group (2c + h) % 3 of pair (2c + h) / 3.
-__constant__ constexpr int kPairA[6] = {0, 0, 1, 0, 2, 1};  // dp term of each pair
-__constant__ constexpr int kPairB[6] = {0, 1, 0, 2, 0, 1};  // W term of each pair
-
-// Per-lane inputs of one sub-tile's dX epilogue, for rows er + 8q: dX_in,
-// H_pre and the row's H_res row.
-struct DxPre {
-  u32x4 d[4];
-  float hp[4];
-  float4 hr[4];
-};
-
-template <bool ACCUM, bool HAS_G, bool DW, bool POST>
-__global__ __launch_bounds__(512) void proj_bwd_mfma_kernel(
-    const bf16_t *__restrict__ X, const float *__restrict__ W, const char *__restrict__ dpA,
-    const float *__restrict__ Hpre, const bf16_t *__restrict__ gr, const bf16_t *__restrict__ Gp,
-    const float *__restrict__ Hres, bf16_t *__restrict__ dX, float *__restrict__ dWpart, int64_t N, int64_t C,
-    int64_t tbsz, int group4) {
-  constexpr bool SPW = POST;  // stream-per-wave channel tiles
-  using L = B2Lay<HAS_G, POST>;
-  extern __shared__ __attribute__((aligned(16))) char b2lds[];
-  const int64_t K = 4 * C;
-  const int64_t nkt = SPW ? (C + kBwKW - 1) / kBwKW : (K + 4 * kBwKW - 1) / (4 * kBwKW);
-  const int64_t ntb = (N + tbsz - 1) / tbsz;
-  int64_t kt, tbi;
-  if (SPW) {
-    // XCD-contiguous order: workgroups are dispatched round-robin over the 8
-    // XCDs, so XCD b % 8 takes tiles [x * per, (x + 1) * per) in order and its
-    // CUs read neighbouring 128-byte row pieces of the same tokens together
-    const int64_t T = nkt * ntb, per = (T + 7) / 8;
-    const int64_t tile = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
-    if (tile >= T) return;  // grid padding to a multiple of 8 (whole workgroup)
-    tbi = tile / nkt;
-    kt = tile % nkt;
-  } else if (group4) {
-    const int64_t b = blockIdx.x, nct = C / (4 * kBwKW);
-    const int64_t pidx = (b / 32) * 8 + (b % 8);
-    if (pidx >= ntb * nct) return;  // grid padding to a multiple of 32 (whole workgroup)
-    tbi = pidx / nct;
-    kt = ((b / 8) % 4) * nct + pidx % nct;
-  } else {
-    tbi = blockIdx.x / nkt;
-    kt = blockIdx.x % nkt;
-  }
-  // token blocks from the last down: the preceding dH_pre pass read X and g
-  // in token order, so the first blocks here still sit in the Infinity Cache
-  const int64_t tb = ntb - 1 - tbi;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int col = lane & 31, h = lane >> 5;
-  const bool loader = wave >= 4;
-  const int kq = wave & 3;  // quarter of this wave
-  // k of the quarter's first column and the number of its real columns
-  const int64_t c0 = SPW ? kt * kBwKW : 0;
-  const int64_t kbase = SPW ? kq * C + c0 : kt * 4 * kBwKW + kq * kBwKW;
-  const int64_t nvalid = SPW ? min<int64_t>(kBwKW, C - c0) : max<int64_t>(0, min<int64_t>(kBwKW, K - kbase));
-  const int64_t ksafe = SPW ? kbase : kt * 4 * kBwKW;  // a real k of the tile (redirect target)
-
-  const int64_t t_begin = tb * tbsz;
-  const int64_t t_end = min(N, t_begin + tbsz);
-  const int nsub = (int)((t_end - t_begin + 31) / 32);
-
-  // ---- loader geometry: lane -> (row in its 8-row group, 16-byte piece)
-  const int drow = lane >> 3;
-  const int dpiece = (lane & 7) ^ drow;
-  const bool dvalid = 8 * dpiece < nvalid;
-  const int64_t xk = dvalid ? kbase + 8 * dpiece : ksafe;
-  // channel of the lane's piece (g and G tiles); a real channel when the
-  // piece lies past the tile
-  const int64_t gcol = SPW ? (dvalid ? c0 + 8 * dpiece : c0) : xk - (xk / C) * C;
-  const int nload = 4 + (HAS_G ? (SPW ? 1 : 4) : 0) + (POST ? 4 : 0) + (kq == 0 ? 2 : 1);
-
-  auto issue = [&](int i) {
-    char *st = b2lds + (i % kB2Stages) * L::stage;
-    const int64_t t0 = t_begin + 32 * (int64_t)i;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t t = min(t0 + 8 * q + drow, N - 1);
-      dma16(X + t * K + xk, st + L::X + kq * kB2Quarter + q * 1024);
-      if (HAS_G && !SPW) dma16(gr + t * C + gcol, st + L::G + kq * kB2Quarter + q * 1024);
-      if (POST) dma16(Gp + (t * 4 + kq) * C + gcol, st + L::Q + kq * kB2Quarter + q * 1024);
-    }
-    if (HAS_G && SPW) {
-      const int64_t t = min(t0 + 8 * kq + drow, N - 1);
-      dma16(gr + t * C + gcol, st + L::G + kq * 1024);
-    }
-    // the sub-tile's 32 dp records are contiguous (records exist up to the
-    // 32-token padding, zero past N): 5 KB in five 1 KB copies
-    const char *rs = dpA + t0 * kDpaBytes;
-    dma16(rs + kq * 1024 + lane * 16, st + L::P + kq * 1024);
-    if (kq == 0) dma16(rs + 4096 + lane * 16, st + L::P + 4096);
-  };
-
-  // ---- dX geometry: lane -> token rows er + 8q (q = 0..3) and 8 k at ek of
-  // the quarter's 64, so eight lanes store one row's whole 128-byte line
-  const int er = lane >> 3;
-  const int ek = (lane & 7) * 8;
-  const bool ekv = ek < nvalid;
-  const int64_t kx = kbase + ek;
-  const int si_x = SPW ? kq : (int)(min<int64_t>(kx, K - 1) / C);
-
-  auto prefetch = [&](DxPre &P, int i) {
-    const int64_t t0 = t_begin + 32 * (int64_t)i;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t tt = t0 + er + 8 * q;
-      const bool v = tt < N && ekv;
-      if (ACCUM) P.d[q] = v ? *reinterpret_cast<const u32x4 *>(dX + tt * K + kx) : u32x4{0u, 0u, 0u, 0u};
-      if (HAS_G) P.hp[q] = v ? Hpre[tt * 4 + si_x] : 0.f;
-      if (POST)
-        P.hr[q] = tt < N ? *reinterpret_cast<const float4 *>(Hres + tt * 16 + kq * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  };
-
-  // B fragments of dp W^T: W[k][*] of this lane's column k split into its
-  // three terms, arranged by chunk (see kPairB)
-  u32x4 wb[2][9];
-  f32x16 accW[2];
-  if (!loader) {
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const bool kv = 32 * ct + col < nvalid;
-      uint32_t tw[3][kJ / 2];  // [term][j pair]
-#pragma unroll
-      for (int s4 = 0; s4 < kJ / 4; ++s4) {
-        const float4 v = kv ? *reinterpret_cast<const float4 *>(W + (kbase + 32 * ct + col) * kJ + 4 * s4)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
-        const float w4[4] = {v.x, v.y, v.z, v.w};
-        float th[4], tmid[4], tl[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          th[e] = bf16_round(w4[e]);
-          const float r1 = w4[e] - th[e];
-          tmid[e] = bf16_round(r1);
-          tl[e] = r1 - tmid[e];
-        }
-        tw[0][2 * s4] = pack_bf16x2(th[0], th[1]); tw[0][2 * s4 + 1] = pack_bf16x2(th[2], th[3]);
-        tw[1][2 * s4] = pack_bf16x2(tmid[0], tmid[1]); tw[1][2 * s4 + 1] = pack_bf16x2(tmid[2], tmid[3]);
-        tw[2][2 * s4] = pack_bf16x2(tl[0], tl[1]); tw[2][2 * s4 + 1] = pack_bf16x2(tl[2], tl[3]);
-      }
-#pragma unroll
-      for (int c = 0; c < 9; ++c) {
-        const int g0 = 2 * c, g1 = 2 * c + 1;
-        const int b0 = kPairB[g0 / 3], m0 = g0 % 3, b1 = kPairB[g1 / 3], m1 = g1 % 3;
-        const u32x4 v0 = {tw[b0][4 * m0], tw[b0][4 * m0 + 1], tw[b0][4 * m0 + 2], tw[b0][4 * m0 + 3]};
-        const u32x4 v1 = {tw[b1][4 * m1], tw[b1][4 * m1 + 1], tw[b1][4 * m1 + 2], tw[b1][4 * m1 + 3]};
-        wb[ct][c] = h ? v1 : v0;
-      }
-    }
-  }
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) accW[rt][r] = 0.f;
-
-  float *acc_t = reinterpret_cast<float *>(b2lds + L::acc) + kq * 32 * kB2AccRow;
-
-  // The two roles run separate loops with the same barrier sequence: a dX
-  // wave never issues an LDS DMA, so its LDS reads need no wait on vmcnt.
-  if (loader) {
-    issue(0);
-    if (nsub > 1) issue(1);
-    for (int i = 0; i < nsub; ++i) {
-      if (i + 1 < nsub) wait_vmcnt_le(nload); else wait_vmcnt<0>();
-      lds_barrier();
-      const char *st = b2lds + (i % kB2Stages) * L::stage;
-      if (i + 2 < nsub) issue(i + 2);
-      if (DW) {
-        // dW += X^T dp: A = 8-token X columns (k = 32 rt + col), B = dp terms
-        const bf16_t *xs = reinterpret_cast<const bf16_t *>(st + L::X + kq * kB2Quarter);
-        u32x4 xa[2][2];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            uint32_t w4[4];
-            const int kk = 32 * rt + col;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-              const int r0 = 16 * s + 8 * h + 2 * p;
-              const uint32_t lo16 = xs[r0 * 64 + 8 * ((kk >> 3) ^ (r0 & 7)) + (kk & 7)];
-              const uint32_t hi16 = xs[(r0 + 1) * 64 + 8 * ((kk >> 3) ^ ((r0 + 1) & 7)) + (kk & 7)];
-              w4[p] = lo16 | (hi16 << 16);
-            }
-            xa[rt][s] = u32x4{w4[0], w4[1], w4[2], w4[3]};
-          }
-        // B = dp term tm at j = col for the same 8 tokens, gathered from the
-        // sub-tile's dp records
-        const char *ps = st + L::P;
-        u32x4 bfr[2][3];
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-          for (int tm = 0; tm < 3; ++tm) {
-            uint32_t w4[4] = {0u, 0u, 0u, 0u};
-            if (col < kJ) {
-#pragma unroll
-              for (int p = 0; p < 4; ++p) {
-                const int r0 = 16 * s + 8 * h + 2 * p;
-                const int off = (tm * 3 + (col >> 3)) * 16 + (col & 7) * 2;
-                const uint32_t lo16 = *reinterpret_cast<const uint16_t *>(ps + r0 * kDpaBytes + off);
-                const uint32_t hi16 = *reinterpret_cast<const uint16_t *>(ps + (r0 + 1) * kDpaBytes + off);
-                w4[p] = lo16 | (hi16 << 16);
-              }
-            }
-            bfr[s][tm] = u32x4{w4[0], w4[1], w4[2], w4[3]};
-          }
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-          for (int tm = 0; tm < 3; ++tm)
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-              accW[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa[rt][s]),
-                                                                 __builtin_bit_cast(bf16x8, bfr[s][tm]),
-                                                                 accW[rt], 0, 0, 0);
-      }
-    }
-  } else {
-    // W in registers before the loop, so the only loads pending inside it
-    // are the prefetches (otherwise every sub-tile waits for all of them)
-    wait_vmcnt<0>();
-    DxPre cur;
-    prefetch(cur, 0);
-    for (int i = 0; i < nsub; ++i) {
-      lds_barrier();
-      const char *st = b2lds + (i % kB2Stages) * L::stage;
-      const int64_t t0 = t_begin + 32 * (int64_t)i;
-      // (a) dp W^T for 32 tokens x 64 k: A fragments (token t0 + col) from
-      // the dp records, 2 x 9 bf16 MFMAs
-      const char *ps = st + L::P;
-      u32x4 af[9];
-#pragma unroll
-      for (int c = 0; c < 9; ++c) {
-        const int g0 = 2 * c, g1 = 2 * c + 1;
-        const int p0 = kPairA[g0 / 3] * 3 + g0 % 3, p1 = kPairA[g1 / 3] * 3 + g1 % 3;
-        af[c] = *reinterpret_cast<const u32x4 *>(ps + col * kDpaBytes + (h ? p1 : p0) * 16);
-      }
-      f32x16 accX[2];
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) accX[ct][r] = 0.f;
-#pragma unroll
-        for (int c = 0; c < 9; ++c)
-          accX[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[c]),
-                                                            __builtin_bit_cast(bf16x8, wb[ct][c]), accX[ct], 0, 0, 0);
-      }
-      // (b) dX = dp W^T + c_rms x + H_pre g + sum_i H_res[j][i] G[i] + dX_in:
-      // the 32 x 64 accumulators are transposed through the wave's LDS area,
-      // then each row is stored as one 128-byte line by eight lanes.  The
-      // prefetched inputs are waited for here, once: a wait left to their
-      // first use inside the (branchy) row loop would also wait for the
-      // previous rows' stores.  The scheduling fence keeps the MFMAs above
-      // the wait, so they cover its latency.
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<0>();
-      const char *xs = st + L::X + kq * kB2Quarter;
-      const char *gs = st + L::G + (SPW ? 0 : kq * kB2Quarter);
-      const char *qs = st + L::Q;
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          acc_t[(8 * (r >> 2) + 4 * h + (r & 3)) * kB2AccRow + 32 * ct + col] = accX[ct][r];
-      wave_lds_sync();
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = er + 8 * q;
-        const int64_t tt = t0 + row;
-        if (!(tt < N && ekv)) continue;
-        const int slot = (ek >> 3) ^ (row & 7);
-        const float4 a0 = *reinterpret_cast<const float4 *>(&acc_t[row * kB2AccRow + ek]);
-        const float4 a1 = *reinterpret_cast<const float4 *>(&acc_t[row * kB2AccRow + ek + 4]);
-        const float acc8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        const float crms = *reinterpret_cast<const float *>(ps + row * kDpaBytes + 9 * 16);
-        const u32x4 xv = *reinterpret_cast<const u32x4 *>(xs + row * 128 + 16 * slot);
-        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-        float o[8];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          o[2 * p] = acc8[2 * p] + crms * bf16_lo(xw[p]);
-          o[2 * p + 1] = acc8[2 * p + 1] + crms * bf16_hi(xw[p]);
-        }
-        if (HAS_G) {
-          const u32x4 gv = *reinterpret_cast<const u32x4 *>(gs + row * 128 + 16 * slot);
-          const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-          const float hp = cur.hp[q];
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            o[2 * p] += hp * bf16_lo(gw[p]);
-            o[2 * p + 1] += hp * bf16_hi(gw[p]);
-          }
-        }
-        if (POST) {  // h_post_bda term: sum_i H_res[j][i] G[i], j = this wave's stream
-          const float4 hr = cur.hr[q];
-          uint32_t gw[4][4];
-#pragma unroll
-          for (int si = 0; si < 4; ++si) {
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(qs + si * kB2Quarter + row * 128 + 16 * slot);
-            gw[si][0] = v.x; gw[si][1] = v.y; gw[si][2] = v.z; gw[si][3] = v.w;
-          }
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            o[2 * p] += (hr.x * bf16_lo(gw[0][p]) + hr.y * bf16_lo(gw[1][p])) +
-                        (hr.z * bf16_lo(gw[2][p]) + hr.w * bf16_lo(gw[3][p]));
-            o[2 * p + 1] += (hr.x * bf16_hi(gw[0][p]) + hr.y * bf16_hi(gw[1][p])) +
-                            (hr.z * bf16_hi(gw[2][p]) + hr.w * bf16_hi(gw[3][p]));
-          }
-        }
-        if (ACCUM) {
-          const uint32_t dw4[4] = {cur.d[q].x, cur.d[q].y, cur.d[q].z, cur.d[q].w};
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            o[2 * p] += bf16_lo(dw4[p]);
-            o[2 * p + 1] += bf16_hi(dw4[p]);
-          }
-        }
-        uint4 ow;
-        ow.x = pack_bf16x2(o[0], o[1]);
-        ow.y = pack_bf16x2(o[2], o[3]);
-        ow.z = pack_bf16x2(o[4], o[5]);
-        ow.w = pack_bf16x2(o[6], o[7]);
-        *reinterpret_cast<uint4 *>(dX + tt * K + kx) = ow;
-      }
-      wave_lds_sync();  // the reads of the accumulator area precede the next sub-tile's writes
-      // the next sub-tile's dX_in, H_pre and H_res, in flight across the
-      // barrier and the next sub-tile's MFMAs
-      if (i + 1 < nsub) prefetch(cur, i + 1);
-    }
-  }
-  if (DW && loader && col < kJ) {
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int e = 32 * rt + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (e < nvalid) dWpart[(tb * K + kbase + e) * kJ + col] = accW[rt][r];
-      }
-  }
-}
-
-// ------------------------------------------------------------------ MFMA dX / dW, 16-token sub-tiles
-// The fused pre backward's form (g and the h_post_bda term given) on
-// 16-token sub-tiles, so that two workgroups share a CU: each workgroup's
-// 3-stage ring (X, g, G tiles and the 16 dp records: 20,992 bytes a stage)
-// and the dX waves' accumulator tiles take 80,384 bytes of LDS, and every
-// wave stays within 128 registers.  Roles, tiles (64 channels of all four
-// streams), swizzles, the barrier sequence and the epilogue are those of
-// proj_bwd_mfma_kernel; what changes with 16 tokens:
-//  * dX: dp W^T on v_mfma_f32_16x16x32_bf16, one 16 x 16 block per 16
-//    channels; the contraction runs over j (24, padded to 32) once per kept
-//    term pair (hh, hm, mh, hl, lh, mm), A = a dp term's 8 j of one token (one
-//    16-byte record piece; lane group 3 holds zeros), B = a W term's 8 j of
-//    one channel.  Each W term is held once (3 x 4 registers per 16
-//    channels) and serves every pair it appears in;
-//  * dW: x^T dp on 32x32x16 with the 16 tokens as the contraction, A = 8
-//    tokens of an X column, B = 8 tokens of a dp term's column;
-//  * copies per sub-tile: X and G quarters two 1 KB copies per loader, g one
-//    copy on loaders 0 and 1, the records 2.5 KB on loaders 0-2 (half a copy
-//    on loader 2).
+// (16 x 64) and the G tile (4 x 16 x 64) are then loaded once and shared by
+// the four dX waves, which each need all four streams of G; these tiles are
+// walked in XCD-contiguous order, so an XCD's CUs read neighbouring row
+// pieces of the same tokens together.
 constexpr int kB3Stages = 3;
 constexpr int kB3Quarter = 16 * 128;  // bytes of one 16 x 64 bf16 tile
 constexpr int kB3AccRow = 68;         // floats per row of a wave's 16 x 64 accumulator tile
 
+template <bool HAS_G, bool POST>
 struct B3Lay {
   static constexpr int X = 0;
-  static constexpr int G = 4 * kB3Quarter;     // g
-  static constexpr int Q = G + kB3Quarter;     // G of h_post_bda
-  static constexpr int P = Q + 4 * kB3Quarter;  // 16 dp records
+  static constexpr int G = 4 * kB3Quarter;                               // g
+  static constexpr int Q = G + (HAS_G ? (POST ? 1 : 4) * kB3Quarter : 0);  // G of h_post_bda
+  static constexpr int P = Q + (POST ? 4 * kB3Quarter : 0);              // 16 dp records
   static constexpr int stage = P + 16 * kDpaBytes;
   static constexpr int acc = kB3Stages * stage;
   static constexpr int total = acc + 4 * 16 * kB3AccRow * 4;
@@ -1230,30 +863,45 @@ struct DxPre16 {
   float4 hr[2];
 };
 
-template <bool ACCUM, bool DW>
+template <bool ACCUM, bool HAS_G, bool DW, bool POST>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void proj_bwd_mfma16_kernel(
     const bf16_t *__restrict__ X, const float *__restrict__ W, const char *__restrict__ dpA,
     const float *__restrict__ Hpre, const bf16_t *__restrict__ gr, const bf16_t *__restrict__ Gp,
     const float *__restrict__ Hres, bf16_t *__restrict__ dX, float *__restrict__ dWpart, int64_t N, int64_t C,
-    int64_t tbsz) {
-  using L = B3Lay;
+    int64_t tbsz, int group4) {
+  constexpr bool SPW = POST;  // stream-per-wave channel tiles
+  using L = B3Lay<HAS_G, POST>;
   extern __shared__ __attribute__((aligned(16))) char b3lds[];
   const int64_t K = 4 * C;
-  const int64_t nkt = (C + kBwKW - 1) / kBwKW;
+  const int64_t nkt = SPW ? (C + kBwKW - 1) / kBwKW : (K + 4 * kBwKW - 1) / (4 * kBwKW);
   const int64_t ntb = (N + tbsz - 1) / tbsz;
-  // XCD-contiguous tile order (as in proj_bwd_mfma_kernel)
-  const int64_t T = nkt * ntb, per = (T + 7) / 8;
-  const int64_t tile = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
-  if (tile >= T) return;  // grid padding to a multiple of 8 (whole workgroup)
-  const int64_t tb = ntb - 1 - tile / nkt;  // token blocks from the last down
-  const int64_t kt = tile % nkt;
+  int64_t kt, tbi;
+  if (SPW) {  // XCD-contiguous tile order
+    const int64_t T = nkt * ntb, per = (T + 7) / 8;
+    const int64_t tile = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+    if (tile >= T) return;  // grid padding to a multiple of 8 (whole workgroup)
+    tbi = tile / nkt;
+    kt = tile % nkt;
+  } else if (group4) {  // the four k tiles that read the same g tile on one XCD, back to back
+    const int64_t b = blockIdx.x, nct = C / (4 * kBwKW);
+    const int64_t pidx = (b / 32) * 8 + (b % 8);
+    if (pidx >= ntb * nct) return;  // grid padding to a multiple of 32 (whole workgroup)
+    tbi = pidx / nct;
+    kt = ((b / 8) % 4) * nct + pidx % nct;
+  } else {
+    tbi = blockIdx.x / nkt;
+    kt = blockIdx.x % nkt;
+  }
+  const int64_t tb = ntb - 1 - tbi;  // token blocks from the last down
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const bool loader = wave >= 4;
-  const int kq = wave & 3;  // stream of this wave
-  const int64_t c0 = kt * kBwKW;
-  const int64_t kbase = kq * C + c0;
-  const int64_t nvalid = min<int64_t>(kBwKW, C - c0);
+  const int kq = wave & 3;  // quarter of this wave
+  // k of the quarter's first column and the number of its real columns
+  const int64_t c0 = SPW ? kt * kBwKW : 0;
+  const int64_t kbase = SPW ? kq * C + c0 : kt * 4 * kBwKW + kq * kBwKW;
+  const int64_t nvalid = SPW ? min<int64_t>(kBwKW, C - c0) : max<int64_t>(0, min<int64_t>(kBwKW, K - kbase));
+  const int64_t ksafe = SPW ? kbase : kt * 4 * kBwKW;  // a real k of the tile (redirect target)
 
   const int64_t t_begin = tb * tbsz;
   const int64_t t_end = min(N, t_begin + tbsz);
@@ -1263,9 +911,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int drow = lane >> 3;
   const int dpiece = (lane & 7) ^ drow;
   const bool dvalid = 8 * dpiece < nvalid;
-  const int64_t gcol = dvalid ? c0 + 8 * dpiece : c0;  // a real channel when the piece lies past the tile
-  const int64_t xk = kq * C + gcol;
-  const int nload = 4 + (kq < 2 ? 1 : 0) + (kq < 3 ? 1 : 0);
+  const int64_t xk = dvalid ? kbase + 8 * dpiece : ksafe;
+  // channel of the lane's piece (g and G tiles); a real channel when the
+  // piece lies past the tile
+  const int64_t gcol = SPW ? (dvalid ? c0 + 8 * dpiece : c0) : xk - (xk / C) * C;
+  const int nload = 2 + (HAS_G ? (SPW ? (kq < 2 ? 1 : 0) : 2) : 0) + (POST ? 2 : 0) + (kq < 3 ? 1 : 0);
 
   auto issue = [&](int i) {
     char *st = b3lds + (i % kB3Stages) * L::stage;
@@ -1274,9 +924,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     for (int q = 0; q < 2; ++q) {
       const int64_t t = min(t0 + 8 * q + drow, N - 1);
       dma16(X + t * K + xk, st + L::X + kq * kB3Quarter + q * 1024);
-      dma16(Gp + (t * 4 + kq) * C + gcol, st + L::Q + kq * kB3Quarter + q * 1024);
+      if (HAS_G && !SPW) dma16(gr + t * C + gcol, st + L::G + kq * kB3Quarter + q * 1024);
+      if (POST) dma16(Gp + (t * 4 + kq) * C + gcol, st + L::Q + kq * kB3Quarter + q * 1024);
     }
-    if (kq < 2) {
+    if (HAS_G && SPW && kq < 2) {
       const int64_t t = min(t0 + 8 * kq + drow, N - 1);
       dma16(gr + t * C + gcol, st + L::G + kq * 1024);
     }
@@ -1293,6 +944,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int ek = (lane & 7) * 8;
   const bool ekv = ek < nvalid;
   const int64_t kx = kbase + ek;
+  const int si_x = SPW ? kq : (int)(min<int64_t>(kx, K - 1) / C);  // stream of the lane's k
 
   auto prefetch = [&](DxPre16 &P, int i) {
     const int64_t t0 = t_begin + 16 * (int64_t)i;
@@ -1301,8 +953,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       const int64_t tt = t0 + er + 8 * q;
       const bool v = tt < N && ekv;
       if (ACCUM) P.d[q] = v ? *reinterpret_cast<const u32x4 *>(dX + tt * K + kx) : u32x4{0u, 0u, 0u, 0u};
-      P.hp[q] = v ? Hpre[tt * 4 + kq] : 0.f;
-      P.hr[q] = tt < N ? *reinterpret_cast<const float4 *>(Hres + tt * 16 + kq * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (HAS_G) P.hp[q] = v ? Hpre[tt * 4 + si_x] : 0.f;
+      if (POST)
+        P.hr[q] = tt < N ? *reinterpret_cast<const float4 *>(Hres + tt * 16 + kq * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
 
@@ -1439,11 +1092,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         accX[bi] = a4;
       }
       // (b) dX = dp W^T + c_rms x + H_pre g + sum_i H_res[j][i] G[i] + dX_in,
-      // through the wave's LDS accumulator tile as in proj_bwd_mfma_kernel
+      // through the wave's LDS accumulator tile
       __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<0>();
       const char *xs = st + L::X + kq * kB3Quarter;
-      const char *gs = st + L::G;
+      const char *gs = st + L::G + (SPW ? 0 : kq * kB3Quarter);
       const char *qs = st + L::Q;
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi)
@@ -1468,7 +1121,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
           o[2 * p] = acc8[2 * p] + crms * bf16_lo(xw[p]);
           o[2 * p + 1] = acc8[2 * p + 1] + crms * bf16_hi(xw[p]);
         }
-        {
+        if (HAS_G) {
           const u32x4 gv = *reinterpret_cast<const u32x4 *>(gs + row * 128 + 16 * slot);
           const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
           const float hp = cur.hp[q];
@@ -1478,7 +1131,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
             o[2 * p + 1] += hp * bf16_hi(gw[p]);
           }
         }
-        {  // h_post_bda term: sum_i H_res[j][i] G[i], j = this wave's stream
+        if (POST) {  // h_post_bda term: sum_i H_res[j][i] G[i], j = this wave's stream
           const float4 hr = cur.hr[q];
           uint32_t gw[4][4];
 #pragma unroll
@@ -1609,40 +1262,25 @@ __global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict_
 }
 
 template <bool ACCUM, bool HAS_G, bool DW, bool POST>
-static void launch_b2_dw(hipStream_t s, const ProjBwdArgs &a, const BwdWs &L) {
+static void launch_b3(hipStream_t s, const ProjBwdArgs &a, const BwdWs &L) {
   const int64_t K = 4 * a.C;
   const int64_t nkt = POST ? (a.C + kBwKW - 1) / kBwKW : (K + 4 * kBwKW - 1) / (4 * kBwKW);
   const int group4 = (!POST && a.C % (4 * kBwKW) == 0) ? 1 : 0;
   const int64_t blocks = POST ? round_up(nkt * L.ntb, 8) : group4 ? round_up(nkt * L.ntb, 32) : nkt * L.ntb;
-  const size_t lds = (size_t)B2Lay<HAS_G, POST>::total;
-  hipLaunchKernelGGL((proj_bwd_mfma_kernel<ACCUM, HAS_G, DW, POST>), dim3((unsigned)blocks), dim3(512), lds, s,
+  const size_t lds = (size_t)B3Lay<HAS_G, POST>::total;
+  hipLaunchKernelGGL((proj_bwd_mfma16_kernel<ACCUM, HAS_G, DW, POST>), dim3((unsigned)blocks), dim3(512), lds, s,
                      (const bf16_t *)a.X, a.W, (const char *)L.dpA, a.H_pre, (const bf16_t *)a.g,
                      (const bf16_t *)a.post_G, a.post_H_res, (bf16_t *)a.dX, L.dwpart, a.N, a.C, L.tbsz, group4);
 }
 
-template <bool ACCUM, bool DW>
-static void launch_b3(hipStream_t s, const ProjBwdArgs &a, const BwdWs &L) {
-  const int64_t nkt = (a.C + kBwKW - 1) / kBwKW;
-  const int64_t blocks = round_up(nkt * L.ntb, 8);
-  hipLaunchKernelGGL((proj_bwd_mfma16_kernel<ACCUM, DW>), dim3((unsigned)blocks), dim3(512), (size_t)B3Lay::total,
-                     s, (const bf16_t *)a.X, a.W, (const char *)L.dpA, a.H_pre, (const bf16_t *)a.g,
-                     (const bf16_t *)a.post_G, a.post_H_res, (bf16_t *)a.dX, L.dwpart, a.N, a.C, L.tbsz);
-}
-
 template <bool ACCUM, bool HAS_G>
 static void launch_b2(hipStream_t s, const ProjBwdArgs &a, const BwdWs &L) {
-  const bool post = a.post_G != nullptr;
-  if (HAS_G && post) {  // the fused pre backward with the h_post_bda term: 16-token sub-tiles
-    if (a.dW) launch_b3<ACCUM, true>(s, a, L);
-    else launch_b3<ACCUM, false>(s, a, L);
-    return;
-  }
-  if (a.dW) {
-    if (post) launch_b2_dw<ACCUM, HAS_G, true, true>(s, a, L);
-    else launch_b2_dw<ACCUM, HAS_G, true, false>(s, a, L);
+  if (HAS_G && a.post_G) {  // the fused pre backward with the h_post_bda term
+    if (a.dW) launch_b3<ACCUM, true, true, true>(s, a, L);
+    else launch_b3<ACCUM, true, false, true>(s, a, L);
   } else {
-    if (post) launch_b2_dw<ACCUM, HAS_G, false, true>(s, a, L);
-    else launch_b2_dw<ACCUM, HAS_G, false, false>(s, a, L);
+    if (a.dW) launch_b3<ACCUM, HAS_G, true, false>(s, a, L);
+    else launch_b3<ACCUM, HAS_G, false, false>(s, a, L);
   }
 }
 

@@ -158,8 +158,9 @@ def sum_depth(path: str, N: int, C: int = 0, S: int | None = None, n: int = 4, a
     rounds at most once per nonzero term it meets.  The leading 1 is the product forming the term.
 
       proj   dW, per token block of dxdw_token_block tokens, then the block partials summed in
-             order.  bf16 (any n): six MFMA accumulations per 32-token sub-tile (three bf16 terms of
-             dp, two 16-token halves) and at most 15 roundings inside one MFMA.  fp32: one fma (n = 4)
+             order.  bf16 (any n): at most six MFMA accumulations per 32 tokens (three bf16 terms of
+             dp on each 16 tokens, one MFMA contracting 16 tokens) and at most 15 roundings
+             inside one MFMA.  fp32: one fma (n = 4)
              or one add (other n) per token.
       param  dalpha, dhbias.  n = 4: <= 4 adds over a lane's owned columns, a 64-lane DPP tree (6),
              four waves (2), one thread's strided walk over 64-token block partials (every 32nd
