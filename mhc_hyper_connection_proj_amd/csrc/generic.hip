@@ -1005,7 +1005,12 @@ __global__ __launch_bounds__(256) void gproj_partial_kernel(const T *__restrict_
 // lane's A operand is the 8 x values of its token at k = 32h + 8q and its B
 // operand the same 8 k of its column (the k order inside an MFMA is free as
 // long as A and B agree).  Each chunk is summed from zero and then added to
-// the running sum, as in the fp32 kernel.
+// the running sum, as in the fp32 kernel.  With NSUB > 1 the slice's chunks
+// form NSUB sub-slices, each with its own running sum, and workgroup tb starts
+// its walk at sub-slice tb % NSUB (wrapping around); the sub-slice sums are
+// added in sub-slice order at the end, so a token's result still depends on K
+// alone.  Rows whose stride is a multiple of 16 KB otherwise put the same k
+// offsets of all tokens in flight at once, which reads slower.
 typedef __attribute__((ext_vector_type(8))) __bf16 gbf16x8;
 
 template <int NS> struct GPj {
@@ -1054,7 +1059,7 @@ __global__ __launch_bounds__(256) void gpack_w_kernel(const float *__restrict__ 
   }
 }
 
-template <int NS>
+template <int NS, int NSUB>
 __global__ __launch_bounds__(512) void gproj_partial_dma_kernel(const bf16_t *__restrict__ X,
                                                                const bf16_t *__restrict__ Wp,
                                                                float *__restrict__ part, int64_t N, int64_t K) {
@@ -1073,10 +1078,15 @@ __global__ __launch_bounds__(512) void gproj_partial_dma_kernel(const bf16_t *__
   const int64_t tw = tb * G::TOK + kGTok * wave;  // this wave's first token
   constexpr int QW = G::WB / 1024;                       // 1 KB copies of a W chunk, over the waves
   const int nq = (QW - wave + G::WAVES - 1) / G::WAVES + 4;  // this wave's copies per chunk
+  // the slice's chunks fall into NSUB sub-slices of sps chunks; the walk
+  // starts at sub-slice tb % NSUB and wraps around
+  const int sps = (nc + NSUB - 1) / NSUB;
+  const int cstart = sps * (int)(tb % NSUB) < nc ? sps * (int)(tb % NSUB) : 0;
+  auto chunk = [&](int v) { return cstart + v < nc ? cstart + v : cstart + v - nc; };
 
-  auto issue = [&](int i) {
-    char *st = gpl + (i % STG) * G::SB;
-    const int64_t c = c_begin + i;
+  auto issue = [&](int v) {  // the copies of walk position v
+    char *st = gpl + (v % STG) * G::SB;
+    const int64_t c = c_begin + chunk(v);
     const char *wsrc = reinterpret_cast<const char *>(Wp) + c * G::WB;
     for (int q = wave; q < QW; q += G::WAVES) dma16(wsrc + q * 1024 + lane * 16, st + q * 1024);
     char *xs = st + G::WB + wave * G::XT;
@@ -1090,22 +1100,28 @@ __global__ __launch_bounds__(512) void gproj_partial_dma_kernel(const bf16_t *__
     }
   };
 
-  gf32x16 outer[JT];
+  gf32x16 outer[NSUB][JT];  // one running sum per sub-slice
+  float ss[NSUB];
 #pragma unroll
-  for (int u = 0; u < JT; ++u)
+  for (int q = 0; q < NSUB; ++q) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) outer[u][r] = 0.f;
-  float ss = 0.f;
+    for (int u = 0; u < JT; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) outer[q][u][r] = 0.f;
+    ss[q] = 0.f;
+  }
   if (nc > 0) issue(0);
   if (STG == 3 && nc > 1) issue(1);
-  for (int i = 0; i < nc; ++i) {
-    // this wave's copies of chunk i are complete once at most those of chunk i + 1 remain
-    if (STG == 3 && i + 1 < nc) wait_vmcnt_le(nq); else wait_vmcnt<0>();
+  for (int v = 0; v < nc; ++v) {
+    // this wave's copies of position v are complete once at most those of v + 1 remain
+    if (STG == 3 && v + 1 < nc) wait_vmcnt_le(nq); else wait_vmcnt<0>();
     lds_barrier();
-    if (i + STG - 1 < nc) issue(i + STG - 1);  // that slot was last read in iteration i - 1
-    const char *st = gpl + (i % STG) * G::SB;
+    if (v + STG - 1 < nc) issue(v + STG - 1);  // that slot was last read in iteration v - 1
+    const char *st = gpl + (v % STG) * G::SB;
     const char *xs = st + G::WB + wave * G::XT;
-    const int64_t k0 = (c_begin + i) * 64;
+    const int ci = chunk(v);
+    const int sub = NSUB == 1 ? 0 : ci / sps;  // workgroup-uniform
+    const int64_t k0 = (c_begin + ci) * 64;
     gu32x4 a[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -1125,7 +1141,9 @@ __global__ __launch_bounds__(512) void gproj_partial_dma_kernel(const bf16_t *__
         }
       }
     }
-    ss += sq;
+#pragma unroll
+    for (int q = 0; q < NSUB; ++q)
+      if (sub == q) ss[q] += sq;
 #pragma unroll
     for (int u = 0; u < JT; ++u) {
       gf32x16 acc;
@@ -1143,8 +1161,22 @@ __global__ __launch_bounds__(512) void gproj_partial_dma_kernel(const bf16_t *__
         }
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) outer[u][r] += acc[r];
+      for (int q = 0; q < NSUB; ++q)
+        if (sub == q) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) outer[q][u][r] += acc[r];
+        }
     }
+  }
+  // the sub-slice sums in sub-slice order: a token's summation order depends
+  // on K alone, not on where the walk started
+#pragma unroll
+  for (int q = 1; q < NSUB; ++q) {
+#pragma unroll
+    for (int u = 0; u < JT; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) outer[0][u][r] += outer[q][u][r];
+    ss[0] += ss[q];
   }
   // accumulator layout of a 32x32 MFMA: lane (col, h), register r holds row
   // 8*(r/4) + 4*h + (r%4), column col.  Sum of squares: the two k halves of a
@@ -1156,12 +1188,12 @@ __global__ __launch_bounds__(512) void gproj_partial_dma_kernel(const bf16_t *__
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t t = tw + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (t < N) part[((int64_t)slice * N + t) * PS + col] = outer[u][r];
+        if (t < N) part[((int64_t)slice * N + t) * PS + col] = outer[0][u][r];
       }
     }
   }
-  const float ss_other = __shfl_xor(ss, 32);
-  if (h == 0 && tw + row < N) part[((int64_t)slice * N + tw + row) * PS + J] = ss + ss_other;
+  const float ss_other = __shfl_xor(ss[0], 32);
+  if (h == 0 && tw + row < N) part[((int64_t)slice * N + tw + row) * PS + J] = ss[0] + ss_other;
 }
 
 // One thread per token: slices summed in order, then RMS, gains, sigmoid;
@@ -2475,8 +2507,16 @@ void glaunch_proj_fwd(hipStream_t s, bool f32, int n, int64_t N, int64_t C, cons
       const unsigned pb = (unsigned)(((N + G::TOK - 1) / G::TOK) * kGSplitK);
       hipLaunchKernelGGL((gpack_w_kernel<NS>), dim3((unsigned)((nch * 32 * G::JT * 8 + 255) / 256)), dim3(256), 0,
                          s, W, Wp, K);
-      hipLaunchKernelGGL((gproj_partial_dma_kernel<NS>), dim3(pb), dim3(64 * G::WAVES), (size_t)G::STAGES * G::SB,
-                         s, (const bf16_t *)X, (const bf16_t *)Wp, part, N, K);
+      // rows a multiple of 16 KB apart, 32 KB or more: staggered walk starts
+      // over 4 sub-slices where one column tile is summed (n <= 3; with more
+      // columns the kernel waits on its MFMAs, and the extra sums slowed it)
+      constexpr int NSUB = G::JT == 1 ? 4 : 1;
+      if (NSUB > 1 && (2 * K) % 16384 == 0 && 2 * K >= 32768)
+        hipLaunchKernelGGL((gproj_partial_dma_kernel<NS, NSUB>), dim3(pb), dim3(64 * G::WAVES),
+                           (size_t)G::STAGES * G::SB, s, (const bf16_t *)X, (const bf16_t *)Wp, part, N, K);
+      else
+        hipLaunchKernelGGL((gproj_partial_dma_kernel<NS, 1>), dim3(pb), dim3(64 * G::WAVES),
+                           (size_t)G::STAGES * G::SB, s, (const bf16_t *)X, (const bf16_t *)Wp, part, N, K);
     })
   }
   if (n >= 3) {

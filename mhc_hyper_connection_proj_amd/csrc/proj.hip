@@ -235,6 +235,12 @@ __global__ __launch_bounds__(256) void proj_partial_f32_kernel(const void *__res
 // loads visible and guarantees the slot refilled next was read by everyone.
 // A wave owns its 32 tokens over the whole slice, so its accumulators are
 // the workgroup's output (no cross-wave reduction).
+// With NSUB > 1 the slice's chunks form NSUB sub-slices, each with its own
+// running sum, and workgroup tb starts its walk at sub-slice tb % NSUB
+// (wrapping around); the sub-slice sums are added in sub-slice order at the
+// end, so a token's result depends on K alone.  Where the rows are a multiple
+// of 16 KB apart (C = 4096, 8192) the unstaggered walk puts the same k offset
+// of every token in flight at once, which reads 15-20% slower.
 constexpr int kDmaWaves = 8;
 constexpr int kDmaTok = 32 * kDmaWaves;      // 256 tokens per workgroup
 constexpr int kDmaStages = 3;
@@ -242,6 +248,7 @@ constexpr int kWChunk = 8 * 3 * kWcol * 8;   // bf16 elements per 64-k W chunk (
 constexpr int kXTile = 32 * 64;              // bf16 elements per wave X tile (4 KB)
 constexpr int kStageElems = kWChunk + kDmaWaves * kXTile;
 
+template <int NSUB>
 __global__ __launch_bounds__(512) void proj_partial_dma_kernel(const bf16_t *__restrict__ X,
                                                                const bf16_t *__restrict__ Wp,
                                                                float *__restrict__ part, int64_t N,
@@ -256,11 +263,16 @@ __global__ __launch_bounds__(512) void proj_partial_dma_kernel(const bf16_t *__r
   const int64_t c_begin = min(nch, slice * cps);
   const int nc = (int)(min(nch, c_begin + cps) - c_begin);
   const int64_t tw = tb * kDmaTok + 32 * wave;  // this wave's first token
+  // the slice's chunks fall into NSUB sub-slices of sps chunks; the walk
+  // starts at sub-slice tb % NSUB and wraps around
+  const int sps = (nc + NSUB - 1) / NSUB;
+  const int cstart = sps * (int)(tb % NSUB) < nc ? sps * (int)(tb % NSUB) : 0;
+  auto chunk = [&](int v) { return cstart + v < nc ? cstart + v : cstart + v - nc; };
 
-  // issue the loads of chunk index i (0-based within the slice) into its slot
-  auto issue = [&](int i) {
-    bf16_t *st = ring + (i % kDmaStages) * kStageElems;
-    const int64_t k0 = (c_begin + i) * 64;
+  // issue the loads of walk position v into its slot
+  auto issue = [&](int v) {
+    bf16_t *st = ring + (v % kDmaStages) * kStageElems;
+    const int64_t k0 = (c_begin + chunk(v)) * 64;
     if (wave < 6) {
       const bf16_t *wsrc = Wp + (k0 / 8) * 3 * kWcol * 8;
 #pragma unroll
@@ -281,16 +293,20 @@ __global__ __launch_bounds__(512) void proj_partial_dma_kernel(const bf16_t *__r
     }
   };
 
-  f32x16 outer;
+  f32x16 outer[NSUB];  // one running sum per sub-slice
+  float ss[NSUB];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) outer[r] = 0.f;
-  float ss = 0.f;
+  for (int q = 0; q < NSUB; ++q) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) outer[q][r] = 0.f;
+    ss[q] = 0.f;
+  }
   if (nc > 0) issue(0);
   if (nc > 1) issue(1);
-  for (int i = 0; i < nc; ++i) {
-    // this wave's loads of chunk i are complete once at most those of chunk
-    // i+1 remain outstanding
-    if (i + 1 < nc) {
+  for (int v = 0; v < nc; ++v) {
+    // this wave's loads of position v are complete once at most those of
+    // position v+1 remain outstanding
+    if (v + 1 < nc) {
       if (wave < 6) wait_vmcnt<6>(); else wait_vmcnt<4>();
     } else {
       wait_vmcnt<0>();
@@ -298,10 +314,11 @@ __global__ __launch_bounds__(512) void proj_partial_dma_kernel(const bf16_t *__r
     // a bare barrier: __syncthreads' fence would also wait for the chunk
     // still in flight.  The memory clobber keeps LDS reads below it.
     asm volatile("s_barrier" ::: "memory");
-    if (i + 2 < nc) issue(i + 2);  // slot (i+2) % 3 was last read in iteration i-1
-    const bf16_t *st = ring + (i % kDmaStages) * kStageElems;
+    if (v + 2 < nc) issue(v + 2);  // slot (v+2) % 3 was last read in iteration v-1
+    const bf16_t *st = ring + (v % kDmaStages) * kStageElems;
     const bf16_t *xs = st + kWChunk + wave * kXTile;
-    const int64_t k0 = (c_begin + i) * 64;
+    const int ci = chunk(v);
+    const int64_t k0 = (c_begin + ci) * 64;
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
@@ -336,20 +353,36 @@ __global__ __launch_bounds__(512) void proj_partial_dma_kernel(const bf16_t *__r
         }
       }
     }
+    // into the running sum of the chunk's sub-slice (workgroup-uniform branch)
+    const int sub = NSUB == 1 ? 0 : ci / sps;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) outer[r] += acc[r];
-    ss += s;
+    for (int q = 0; q < NSUB; ++q)
+      if (sub == q) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) outer[q][r] += acc[r];
+        ss[q] += s;
+      }
+  }
+  // the sub-slice sums in sub-slice order, so a token's summation order
+  // depends on K alone, not on where the walk started
+  f32x16 tot = outer[0];
+  float sst = ss[0];
+#pragma unroll
+  for (int q = 1; q < NSUB; ++q) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tot[r] += outer[q][r];
+    sst += ss[q];
   }
   // sum of squares: the two lane halves hold the two 32-k halves of each row
-  ss += __shfl_xor(ss, 32);
+  sst += __shfl_xor(sst, 32);
   if (row < kJ) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t t = tw + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (t < N) part[((int64_t)slice * N + t) * kPartStride + row] = outer[r];
+      if (t < N) part[((int64_t)slice * N + t) * kPartStride + row] = tot[r];
     }
   }
-  if (h == 0 && tw + row < N) part[((int64_t)slice * N + tw + row) * kPartStride + kJ] = ss;
+  if (h == 0 && tw + row < N) part[((int64_t)slice * N + tw + row) * kPartStride + kJ] = sst;
 }
 
 // ------------------------------------------------------------------ partial projection, bf16 on the VALU
@@ -533,8 +566,14 @@ void launch_proj_fwd(hipStream_t s, bool f32, int64_t N, int64_t C, const void *
     const unsigned pblocks = (unsigned)(((N + kDmaTok - 1) / kDmaTok) * kSplitK);
     const size_t lds = (size_t)kDmaStages * kStageElems * sizeof(bf16_t);
     hipLaunchKernelGGL((pack_w_kernel<false>), dim3(pack_blocks), dim3(256), 0, s, W, wpk, K, Kp);
-    hipLaunchKernelGGL(proj_partial_dma_kernel, dim3(pblocks), dim3(kDmaWaves * 64), lds, s,
-                       (const bf16_t *)X, (const bf16_t *)wpk, part, N, K);
+    // rows a multiple of 16 KB apart, 32 KB or more: staggered walk starts
+    // over 4 sub-slices
+    if ((2 * K) % 16384 == 0 && 2 * K >= 32768)
+      hipLaunchKernelGGL(proj_partial_dma_kernel<4>, dim3(pblocks), dim3(kDmaWaves * 64), lds, s,
+                         (const bf16_t *)X, (const bf16_t *)wpk, part, N, K);
+    else
+      hipLaunchKernelGGL(proj_partial_dma_kernel<1>, dim3(pblocks), dim3(kDmaWaves * 64), lds, s,
+                         (const bf16_t *)X, (const bf16_t *)wpk, part, N, K);
   }
   hipLaunchKernelGGL(proj_finalize_kernel, dim3((unsigned)((N + 15) / 16)), dim3(64), 0, s, part,
                      alpha, hbias, rms_eps, H_pre, H_post, logits, saved, H_res, iters, eps, N, K);
