@@ -12,12 +12,13 @@ typedef uint16_t bf16_t;  // bf16 storage: the upper half of an fp32 bit pattern
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Two fp32 -> two bf16 (round to nearest even) packed low|high: v_cvt_pk_bf16_f32.
+// Two fp32 -> two bf16 (round to nearest even) packed low|high.  Converted as
+// one two-element vector, so the pair is a single v_cvt_pk_bf16_f32 (two
+// scalar conversions compile to two of them plus a shift and an or).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const __bf16 ha = (__bf16)a;
-  const __bf16 hb = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+  typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 // ---------------------------------------------------------------- 8-wide activation I/O
