@@ -994,10 +994,11 @@ __global__ __launch_bounds__(256) void gproj_partial_kernel(const T *__restrict_
 // mid = the rest rounded, lo = what remains: 8 + 8 + 8 significant bits
 // cover fp32's 24), and bf16 x times a bf16 term is exact in the fp32
 // accumulator, so the three products give x @ W to fp32 accumulation.
-// gpack_w_kernel splits W once per call into Wp[chunk][term][column][8
-// pieces of 8 k] (64 k per chunk, 32 JT columns, zero past K and J), piece p
-// of column j stored in slot p ^ (j & 7), so a chunk is one contiguous block
-// of 12 JT KB that a workgroup copies verbatim into LDS.  A workgroup is 8
+// gpack_w_kernel splits W once per call into Wp[chunk][piece of 8 k][term]
+// [column][8 k] (64 k per chunk, 32 JT columns, zero past K and J), so a
+// chunk is one contiguous block of 12 JT KB that a workgroup copies verbatim
+// into LDS, and the 32 columns of one piece and term (a B fragment for each
+// lane of a half-wave) are 512 contiguous bytes, read without bank conflicts.  A workgroup is 8
 // waves x 32 tokens on one k slice; each 64-k chunk of W (shared) and of
 // every wave's X tile (4 KB, 8 lanes per 128-byte row segment, piece p of
 // row r in slot p ^ (r & 7)) goes through an LDS ring filled by
@@ -1031,10 +1032,10 @@ __global__ __launch_bounds__(256) void gpack_w_kernel(const float *__restrict__ 
                                                      int64_t K) {
   constexpr int J = Dim<NS>::J, JT = Dim<NS>::JT;
   const int64_t nch = (K + 63) / 64;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (chunk, column, piece)
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (chunk, piece, column)
   if (i >= nch * 32 * JT * 8) return;
-  const int p = (int)(i & 7), j = (int)((i >> 3) % (32 * JT));
-  const int64_t c = (i >> 3) / (32 * JT);
+  const int j = (int)(i % (32 * JT)), p = (int)((i / (32 * JT)) & 7);
+  const int64_t c = i / (32 * JT * 8);
   float hi[8], mid[8], lo[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -1045,7 +1046,6 @@ __global__ __launch_bounds__(256) void gpack_w_kernel(const float *__restrict__ 
     mid[e] = (float)(__bf16)r1;
     lo[e] = r1 - mid[e];
   }
-  const int slot = p ^ (j & 7);
   const float *terms[3] = {hi, mid, lo};
 #pragma unroll
   for (int m = 0; m < 3; ++m) {
@@ -1055,7 +1055,7 @@ __global__ __launch_bounds__(256) void gpack_w_kernel(const float *__restrict__ 
     w4.y = pack_bf16x2(v[2], v[3]);
     w4.z = pack_bf16x2(v[4], v[5]);
     w4.w = pack_bf16x2(v[6], v[7]);
-    *reinterpret_cast<uint4 *>(Wp + ((c * 3 + m) * 32 * JT + j) * 64 + 8 * slot) = w4;
+    *reinterpret_cast<uint4 *>(Wp + (((c * 8 + p) * 3 + m) * 32 * JT + j) * 8) = w4;
   }
 }
 
@@ -1154,8 +1154,7 @@ __global__ __launch_bounds__(512) void gproj_partial_dma_kernel(const bf16_t *__
         const int p = 4 * h + q;
 #pragma unroll
         for (int m = 0; m < 3; ++m) {
-          const gu32x4 bw =
-              *reinterpret_cast<const gu32x4 *>(st + ((m * 32 * JT + 32 * u + row) * 8 + (p ^ (row & 7))) * 16);
+          const gu32x4 bw = *reinterpret_cast<const gu32x4 *>(st + ((p * 3 + m) * 32 * JT + 32 * u + row) * 16);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(gbf16x8, a[q]),
                                                         __builtin_bit_cast(gbf16x8, bw), acc, 0, 0, 0);
         }
