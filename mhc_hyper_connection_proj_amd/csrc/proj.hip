@@ -22,7 +22,10 @@
 //  * Accuracy: each 64-k chunk accumulates in a fresh MFMA accumulator and is
 //    then added into an fp32 running sum (two-level blocking), the 4 waves of a
 //    workgroup and the 8 slices are summed in a fixed order; sum x^2 uses
-//    v_dot2_f32_bf16 with the same blocking.
+//    v_dot2_f32_bf16 with the same blocking.  Where the rows are a multiple of
+//    16 KB apart, each quarter of a slice keeps its own running sum (so the
+//    workgroups can start their walks at different quarters) and the quarters
+//    are added in order: the summation order still depends on K alone.
 #include "device.h"
 #include "internal.h"
 #include "ring.h"
