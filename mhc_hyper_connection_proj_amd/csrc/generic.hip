@@ -680,14 +680,17 @@ template <typename T, int NS, int MODE> struct GPostShape {
   static constexpr int NPASS = MODE != kPostDist ? (NS + JB - 1) / JB : 1;
 };
 
-template <typename T, int NS, int MODE>
+template <typename T, int NS, int MODE, bool WDX>
 __global__ __launch_bounds__(256) void gpost_bwd_kernel(const T *__restrict__ Gr, const T *__restrict__ X,
                                                        const float *__restrict__ Hr, const float *__restrict__ Hp,
                                                        const T *__restrict__ x, const T *__restrict__ bias,
                                                        T *__restrict__ dX, float *__restrict__ dHr,
                                                        float *__restrict__ dHp, T *__restrict__ dx,
                                                        float *__restrict__ part, int64_t N, int64_t C, int TG) {
-  const bool HAS_BIAS = bias != nullptr, WRITE_DX = dX != nullptr, DBIAS = part != nullptr;
+  // WDX = false compiles the dX rows out (fewer registers).  With WDX the
+  // test is a compile-time one up to n = 6 and a run-time one at n = 7, 8,
+  // where that register allocation measured faster
+  const bool HAS_BIAS = bias != nullptr, DBIAS = part != nullptr, WRITE_DX = WDX && (NS <= 6 || dX != nullptr);
   constexpr bool MIX = MODE != kPostDist, DIST = MODE != kPostMix;
   constexpr int JB = GPostShape<T, NS, MODE>::JB, NPASS = GPostShape<T, NS, MODE>::NPASS;
   constexpr int NR = (MIX ? JB * NS : 0) + (DIST ? NS : 0);
@@ -2436,8 +2439,12 @@ static void gpost_bwd5(hipStream_t s, int n, int64_t N, int64_t C, const void *G
     // one wave per TG tokens (per pass of a token without dbias), four waves per workgroup
     const int64_t waves = part ? (N + TG - 1) / TG : N * GPostShape<T, NS, MODE>::NPASS;
     const unsigned blocks = (unsigned)((waves + 3) / 4);
-    hipLaunchKernelGGL((gpost_bwd_kernel<T, NS, MODE>), dim3(blocks), dim3(256), 0, s, (const T *)G,
-                       (const T *)X, Hr, Hp, (const T *)x, (const T *)b, (T *)dX, dHr, dHp, (T *)dx, part, N, C, TG);
+    if (dX)
+      hipLaunchKernelGGL((gpost_bwd_kernel<T, NS, MODE, true>), dim3(blocks), dim3(256), 0, s, (const T *)G,
+                         (const T *)X, Hr, Hp, (const T *)x, (const T *)b, (T *)dX, dHr, dHp, (T *)dx, part, N, C, TG);
+    else
+      hipLaunchKernelGGL((gpost_bwd_kernel<T, NS, MODE, false>), dim3(blocks), dim3(256), 0, s, (const T *)G,
+                         (const T *)X, Hr, Hp, (const T *)x, (const T *)b, (T *)dX, dHr, dHp, (T *)dx, part, N, C, TG);
   });
 }
 
