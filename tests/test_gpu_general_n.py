@@ -178,6 +178,26 @@ def test_proj_rms_h_general_n(n, act, N, C):
     assert_tokensum("dhbias", db, odb, ab, depth=sum_depth("param", N, n=n))
 
 
+@pytest.mark.parametrize("n,C", [(1, 16384), (2, 8192), (3, 8192)])
+def test_proj_staggered_walk_general_n(n, C):
+    """Rows a multiple of 16 KB apart (and at least 32 KB) take the staggered projection walk; 1030
+    tokens make five token blocks, so the walk starts at every one of its four sub-slices."""
+    N, act = 1030, "bf16"
+    log(f"proj staggered n={n} N={N} C={C}")
+    X, W, alpha, hb = _proj_inputs(n, act, N, C, zero_row=True)
+    J = n * n + 2 * n
+    Hp, Hq, L, saved = B.mhc_proj_rms_h(dev(X), dev(W), dev(alpha), dev(hb), 1e-6)
+    torch.cuda.synchronize()
+    p = O.proj_rms_h(h64(X), h64(W), h64(alpha), h64(hb), 1e-6)
+    s = h64(saved)
+    assert_rel("q", s[:, 1], p.q)
+    assert_rel("r", s[:, 0], p.r)
+    assert_mixed("z", s[:, 2:2 + J], p.z)
+    assert_mixed("logits", L, p.L)
+    assert_rel("H_pre", Hp, p.H_pre)
+    assert_rel("H_post", Hq, p.H_post)
+
+
 @pytest.mark.parametrize("n", NS)
 @pytest.mark.parametrize("mode", ["accumulate", "post"])
 @pytest.mark.parametrize("act,N,C", [("bf16", 37, 296), ("f32", 20, 256), ("bf16", 66, 2048)])

@@ -220,8 +220,11 @@ def test_h_post_bda_identity_h_res_exact_bf16():
 
 
 # ----------------------------------------------------------------- projection
+# 1030 tokens at C = 4096 and 8192: five token blocks, so the staggered projection walk (rows a multiple of
+# 16 KB apart) starts at every one of its four sub-slices
 PROJ = [("f32", 64, 256), ("bf16", 37, 296), ("bf16", 70, 4096), ("bf16", 67, 7168),
-        ("bf16", 5, 8), ("f32", 33, 1032), ("bf16", 129, 1024), ("bf16", 33, 16384)]
+        ("bf16", 5, 8), ("f32", 33, 1032), ("bf16", 129, 1024), ("bf16", 33, 16384),
+        ("bf16", 1030, 4096), ("bf16", 1030, 8192)]
 
 
 def _proj_inputs(act, N, C, zero_row=True):
