@@ -268,40 +268,69 @@ def measure_reread_chunks(lib, L, sp, stream, torch, Xcopies, W, G, bufs, N, n, 
 def measure_general_n(N: int, stream, torch) -> dict:
     """One mHC step (pre fwd, post fwd, post bwd, pre bwd with the h_post_bda dX term) at stream counts
     other than 4, on the kernels templated on n: same token count as the headline workload, a width
-    that keeps the residual near 0.5 GB, synthetic N(0,1) bf16 inputs, W ~ N(0, 0.02).  Mean of 3
-    event-timed steps after one warm-up; GB/s on each boundary tensor once per phase,
-    (16 n + 10) C bytes per token."""
+    that keeps the residual near 0.5 GB, synthetic N(0,1) bf16 inputs, W ~ N(0, 0.02), the same
+    per-channel scale as the layer stand-in.  As for the headline: two copies of the residual
+    alternate between steps, HIP events bracket every phase, and the mHC time is the sum of the four
+    mHC phases (ms_per_step; ms_per_step_incl_layer adds the layer stand-in's two scale kernels).
+    Mean of 5 event-timed steps after one warm-up; GB/s on each boundary tensor once per phase,
+    (16 n + 10) C bytes per token, over the mHC time."""
     from mhc_hyper_connection_proj_amd import binding as B
     dev = torch.device("cuda", 0)
     gen = torch.Generator(device=dev).manual_seed(5)
     res = {}
     for n, C in ((2, 7168), (8, 2048)):
-        X = torch.randn(N, n, C, device=dev, generator=gen).to(torch.bfloat16)
+        Xs = [torch.randn(N, n, C, device=dev, generator=gen).to(torch.bfloat16)]
+        Xs.append(Xs[0].clone())
         G = torch.randn(N, n, C, device=dev, generator=gen).to(torch.bfloat16)
         W = torch.randn(n * C, n * n + 2 * n, device=dev, generator=gen) * 0.02
         s = torch.rand(C, device=dev, generator=gen).to(torch.bfloat16) + 0.5
+        st = {}
 
-        def step():
-            f = B.mhc_pre_fwd(X, W)
-            x = f["agg"] * s
-            B.mhc_h_post_bda_fwd(X, f["H_res"], f["H_post"], x)
-            _, dHr, dHp, dx, _ = B.mhc_h_post_bda_bwd(G, X, f["H_res"], f["H_post"], x, want_dX=False)
-            B.mhc_pre_bwd(dx * s, dHp, dHr, X, W, f["saved"], f["H_pre"], f["H_post"], f["H_res_logits"],
-                          post_G=G, post_H_res=f["H_res"])
+        def pre_fwd():
+            st["f"] = B.mhc_pre_fwd(st["X"], W)
 
-        step()
+        def layer():
+            st["x"] = st["f"]["agg"] * s
+
+        def post_fwd():
+            B.mhc_h_post_bda_fwd(st["X"], st["f"]["H_res"], st["f"]["H_post"], st["x"])
+
+        def post_bwd():
+            f = st["f"]
+            _, st["dHr"], st["dHp"], st["dx"], _ = B.mhc_h_post_bda_bwd(G, st["X"], f["H_res"], f["H_post"],
+                                                                         st["x"], want_dX=False)
+
+        def layer_bwd():
+            st["g"] = st["dx"] * s
+
+        def pre_bwd():
+            f = st["f"]
+            B.mhc_pre_bwd(st["g"], st["dHp"], st["dHr"], st["X"], W, f["saved"], f["H_pre"], f["H_post"],
+                          f["H_res_logits"], post_G=G, post_H_res=f["H_res"])
+
+        seq = [("pre_fwd", pre_fwd, True), ("layer", layer, False), ("post_fwd", post_fwd, True),
+               ("post_bwd", post_bwd, True), ("layer_bwd", layer_bwd, False), ("pre_bwd", pre_bwd, True)]
+        st["X"] = Xs[0]
+        for _, fn, _ in seq:
+            fn()
         torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        ev[0].record(stream)
-        for i in range(3):
-            step()
-            ev[i + 1].record(stream)
+        steps = 5
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 1)] for _ in range(steps)]
+        for k in range(steps):
+            st["X"] = Xs[(k + 1) % 2]
+            evs[k][0].record(stream)
+            for i, (_, fn, _) in enumerate(seq):
+                fn()
+                evs[k][i + 1].record(stream)
         torch.cuda.synchronize()
-        ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(3)]))
+        ph = {name: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)]))
+              for i, (name, _, _) in enumerate(seq)}
+        ms = sum(ph[name] for name, _, m in seq if m)
         gbs = (16 * n + 10) * C * N / (ms * 1e-3) / 1e9
-        res[f"n{n}_C{C}"] = {"ms_per_step_incl_layer": ms, "tokens_per_s": N / (ms * 1e-3), "achieved_gbs": gbs,
+        res[f"n{n}_C{C}"] = {"ms_per_step": ms, "ms_per_step_incl_layer": sum(ph.values()),
+                             "phases_ms": ph, "tokens_per_s": N / (ms * 1e-3), "achieved_gbs": gbs,
                              "frac": gbs / HBM_PEAK_GBS}
-        del X, G, W
+        del Xs, G, W, st
     return res
 
 
